@@ -1,0 +1,466 @@
+"""Pins for the fp64 oracle: brute force, closed forms, textbook routines, invariants.
+
+None of these tests re-types the oracle's own formula; each checks it against
+something the pages or the mathematics fix independently, chosen so that a
+dropped term, a wrong sign, a wrong index or a transposed operand fails.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _bf16(x):
+    """Round float64 values to bf16 and widen back (inputs hold bf16 values exactly)."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _tiny_inputs(seed=0, B=2, H=2, G=2, Q=3, NB=9, d=8, lens=(137, 100)):
+    r = _rng(seed)
+    q = _bf16(r.standard_normal((B, H, G, Q, d)))
+    k = _bf16(r.standard_normal((B, H, NB, 16, d)))
+    v = _bf16(r.standard_normal((B, H, NB, 16, d)))
+    return q, k, v, np.array(lens[:B])
+
+
+# ---------------------------------------------------------------------------
+# O0 summaries
+# ---------------------------------------------------------------------------
+
+def test_summaries_aligned_equal_library_reduction():
+    r = _rng(1)
+    k = _bf16(r.standard_normal((2, 3, 5, 16, 8)))
+    lens = np.array([80, 80])
+    s = ref.build_summaries(k, lens)
+    np.testing.assert_array_equal(s[:, :, :, 0, :], np.amin(k, axis=3))
+    np.testing.assert_array_equal(s[:, :, :, 1, :], np.amax(k, axis=3))
+
+
+def test_summaries_ignore_tokens_past_length():
+    r = _rng(2)
+    k = _bf16(r.standard_normal((1, 1, 3, 16, 4)))
+    k[0, 0, 2, 5:, :] = 1e6            # tokens 37.. are past the length
+    k[0, 0, 2, 5:, 1] = -1e6
+    lens = np.array([37])
+    s = ref.build_summaries(k, lens)
+    # brute force over the valid tokens only
+    for d in range(4):
+        vals = [k[0, 0, 2, t, d] for t in range(16) if 32 + t < 37]
+        assert s[0, 0, 2, 0, d] == min(vals)
+        assert s[0, 0, 2, 1, d] == max(vals)
+    assert np.all(np.abs(s) < 1e5)
+
+
+def test_summaries_bracket_and_attain():
+    q, k, v, lens = _tiny_inputs(3)
+    s = ref.build_summaries(k, lens)
+    B, H, NB = k.shape[:3]
+    for b in range(B):
+        for j in range(NB):
+            n = min(16, int(lens[b]) - 16 * j)
+            if n <= 0:
+                assert np.all(s[b, :, j] == 0)
+                continue
+            toks = k[b, :, j, :n, :]
+            assert np.all(s[b, :, j, 0][:, None, :] <= toks)
+            assert np.all(s[b, :, j, 1][:, None, :] >= toks)
+            assert np.all(np.any(toks == s[b, :, j, 0][:, None, :], axis=1))
+            assert np.all(np.any(toks == s[b, :, j, 1][:, None, :], axis=1))
+
+
+def test_summary_is_one_sixteenth_of_kv():
+    # [xllm] section three component table: the compressed key cache is 1/16 of the full KV.
+    d, block = 128, 16
+    summary_elems = 2 * d            # min and max per block
+    kv_elems = 2 * block * d         # keys and values per block
+    assert summary_elems * 16 == kv_elems
+
+
+# ---------------------------------------------------------------------------
+# O1 scores
+# ---------------------------------------------------------------------------
+
+def test_score_bounds_every_true_dot_product():
+    q, k, v, lens = _tiny_inputs(4)
+    W = 16
+    summ = ref.build_summaries(k, lens)
+    s = ref.score_blocks(q, summ, lens, W)
+    B, H, G, Q, d = q.shape
+    for b in range(B):
+        n_cand = ref.first_window_block(lens[b], W)
+        for h in range(H):
+            for j in range(n_cand):
+                n = min(16, int(lens[b]) - 16 * j)
+                dots = q[b, h].reshape(-1, d) @ k[b, h, j, :n].T   # every row x every valid token
+                assert s[b, h, j] >= dots.max() - 1e-12
+
+
+def test_score_closed_forms():
+    r = _rng(5)
+    d = 8
+    # 16 identical keys: the bound is tight, score = max over rows of q . k.
+    key = _bf16(r.standard_normal(d))
+    k = np.broadcast_to(key, (1, 1, 2, 16, d)).copy()
+    q = _bf16(r.standard_normal((1, 1, 2, 2, d)))
+    lens = np.array([32])
+    s = ref.score_blocks(q, ref.build_summaries(k, lens), lens, window=0)
+    assert s[0, 0, 0] == pytest.approx(max(float(row @ key) for row in q[0, 0].reshape(-1, d)), abs=1e-12)
+    # non-negative queries read the max summary; non-positive queries the min summary
+    k = _bf16(r.standard_normal((1, 1, 2, 16, d)))
+    summ = ref.build_summaries(k, lens)
+    qp = np.abs(q)
+    s = ref.score_blocks(qp, summ, lens, window=0)
+    assert s[0, 0, 1] == pytest.approx(max(float(row @ summ[0, 0, 1, 1]) for row in qp[0, 0].reshape(-1, d)), abs=1e-12)
+    qn = -np.abs(q)
+    s = ref.score_blocks(qn, summ, lens, window=0)
+    assert s[0, 0, 1] == pytest.approx(max(float(row @ summ[0, 0, 1, 0]) for row in qn[0, 0].reshape(-1, d)), abs=1e-12)
+
+
+def test_score_sign_split_identity_matmul():
+    # max(q*a, q*b) = q+ * b + q- * a for a <= b, evaluated as one library matmul.
+    q, k, v, lens = _tiny_inputs(6)
+    W = 16
+    summ = ref.build_summaries(k, lens)
+    s = ref.score_blocks(q, summ, lens, W)
+    B, H, G, Q, d = q.shape
+    for b in range(B):
+        n_cand = ref.first_window_block(lens[b], W)
+        for h in range(H):
+            rows = q[b, h].reshape(-1, d)
+            A = np.concatenate([np.maximum(rows, 0), np.minimum(rows, 0)], axis=1)      # [R, 2d]
+            Bm = np.concatenate([summ[b, h, :n_cand, 1], summ[b, h, :n_cand, 0]], axis=1)  # [n, 2d]
+            alt = np.matmul(A, Bm.T).max(axis=0)
+            np.testing.assert_allclose(s[b, h, :n_cand], alt, rtol=0, atol=1e-12)
+            assert np.all(np.isneginf(s[b, h, n_cand:]))
+
+
+def test_score_max_aggregation_pure_python():
+    q, k, v, lens = _tiny_inputs(7, B=1, H=1, G=2, Q=2, NB=4, d=4, lens=(64,))
+    summ = ref.build_summaries(k, lens)
+    s = ref.score_blocks(q, summ, lens, window=16)
+    for j in range(3):
+        best = -math.inf
+        for g in range(2):
+            for i in range(2):
+                tot = 0.0
+                for dd in range(4):
+                    a = q[0, 0, g, i, dd] * summ[0, 0, j, 0, dd]
+                    c = q[0, 0, g, i, dd] * summ[0, 0, j, 1, dd]
+                    tot += a if a > c else c
+                best = max(best, tot)
+        assert s[0, 0, j] == pytest.approx(best, abs=1e-12)
+    assert s[0, 0, 3] == -math.inf
+
+
+# ---------------------------------------------------------------------------
+# O2 top-K
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("distinct", [True, False])
+def test_topk_equals_full_sort(distinct):
+    r = _rng(8)
+    B, H, NB = 2, 3, 40
+    scores = r.standard_normal((B, H, NB)) if distinct else r.integers(-2, 3, (B, H, NB)).astype(float)
+    lens = np.array([16 * 40, 16 * 10 + 3])
+    W, K = 16, 12
+    sel = ref.topk_blocks(scores, lens, K, W)
+    for b in range(B):
+        n_cand = ref.first_window_block(lens[b], W)
+        for h in range(H):
+            full = sorted(range(n_cand), key=lambda j: (-scores[b, h, j], j))
+            expect = (full + [-1] * K)[:K]
+            assert list(sel[b, h]) == expect
+
+
+def test_topk_fewer_candidates_than_k_pads():
+    scores = np.array([[[3.0, 1.0, 2.0, 9.0, 9.0]]])
+    lens = np.array([16 * 3 + 64])        # W = 64 -> candidates 0..2
+    sel = ref.topk_blocks(scores, lens, 5, 64)
+    assert list(sel[0, 0]) == [0, 2, 1, -1, -1]
+
+
+def test_topk_brute_force_subsets():
+    # The selected set maximises the score sum among all K-subsets (distinct scores).
+    r = _rng(9)
+    s = r.standard_normal(9)
+    lens = np.array([16 * 9])
+    sel = ref.topk_blocks(s[None, None], lens, 3, 0)[0, 0]
+    best = max(itertools.combinations(range(9), 3), key=lambda c: sum(s[list(c)]))
+    assert set(sel) == set(best)
+
+
+# ---------------------------------------------------------------------------
+# O3 plan
+# ---------------------------------------------------------------------------
+
+def test_plan_worked_example():
+    with open(os.path.join(GOLDEN, "plan_worked_example.json")) as f:
+        ex = json.load(f)
+    NB = ex["num_blocks"]
+    scores = np.full((1, 1, NB), -np.inf)
+    sc = np.array(ex["scores_candidates"], dtype=float)
+    scores[0, 0, : sc.size] = sc
+    lens = np.array([ex["seq_len"]])
+    K, W = ex["top_k"], ex["window"]
+    sel = ref.topk_blocks(scores, lens, K, W)
+    assert list(sel[0, 0]) == ex["expected_topk"]
+    res = np.array([[ex["resident"]]])
+    for case in ex["cases"]:
+        p = ref.build_plan(scores, sel, res, lens, case["cap"], W)
+        n = case["plan_count"]
+        assert p["plan_count"][0, 0] == n
+        assert p["plan"][0, 0, :n].tolist() == case["plan"]
+        assert np.all(p["plan"][0, 0, n:] == -1)
+        assert p["resident"][0, 0].tolist() == case["resident_after"]
+        tc = int(p["table_count"][0, 0])
+        assert p["table"][0, 0, :tc].tolist() == case["table"]
+        assert np.all(p["table"][0, 0, tc:] == -1)
+
+
+def _check_plan_invariants(s, S, R, cap, p, n_cand):
+    S_set = set(int(x) for x in S if x >= 0)
+    R_list = [int(x) for x in R]
+    R_set = set(x for x in R_list if x >= 0)
+    Rn = [int(x) for x in p["resident"]]
+    n = int(p["plan_count"])
+    A = [x for x in S if x >= 0 and int(x) not in R_set]
+    assert n == min(cap, len(A))
+    changed = [i for i in range(len(R_list)) if R_list[i] != Rn[i]]
+    assert len(changed) == n
+    assert set(x for x in Rn if x >= 0) <= R_set | S_set
+    assert len(set(Rn) & S_set) == len(R_set & S_set) + n
+    assert len([x for x in Rn if x >= 0]) == len(set(x for x in Rn if x >= 0))      # distinct
+    assert all(x < n_cand for x in Rn if x >= 0)                                      # no window block
+    # admitted blocks beat every new block left out; evicted stale blocks score no higher
+    admitted = set(int(r[1]) for r in p["plan"][:n])
+    left = [x for x in A if int(x) not in admitted]
+    for a in admitted:
+        for o in left:
+            assert (s[a], -a) > (s[o], -o)
+    evicted = [int(r[2]) for r in p["plan"][:n] if r[2] >= 0]
+    kept_stale = [x for x in Rn if x >= 0 and x in R_set and x not in S_set]
+    if evicted:
+        for e in evicted:
+            for kst in kept_stale:
+                assert (s[e], -e) <= (s[kst], -kst)
+    # empty slots are filled before any stale slot is evicted
+    n_empty = sum(1 for x in R_list if x < 0)
+    assert len(evicted) == max(0, n - n_empty)
+    # the plan lists slots in ascending order and pairs them with ascending new blocks
+    slots = [int(r[0]) for r in p["plan"][:n]]
+    news = [int(r[1]) for r in p["plan"][:n]]
+    assert slots == sorted(slots) and news == sorted(news)
+
+
+def test_plan_invariants_random():
+    r = _rng(10)
+    for trial in range(300):
+        K = int(r.integers(1, 9))
+        n_cand = int(r.integers(1, 20))
+        W = 32
+        L = 16 * n_cand + W
+        NB = n_cand + 3
+        s = np.full(NB, -np.inf)
+        s[:n_cand] = r.integers(-4, 5, n_cand) if trial % 2 else r.standard_normal(n_cand)
+        S = ref.topk_blocks(s[None, None], np.array([L]), K, W)[0, 0]
+        n_fill = min(K, n_cand, int(r.integers(0, K + 1)))
+        R = np.full(K, -1)
+        R[:n_fill] = r.choice(n_cand, n_fill, replace=False)
+        r.shuffle(R)
+        cap = int(r.integers(0, K + 2))
+        p = ref.build_plan(s[None, None], S[None, None], R[None, None], np.array([L]), cap, W)
+        one = {k: v[0, 0] for k, v in p.items()}
+        _check_plan_invariants(s, S, R, cap, one, n_cand)
+        # table = updated residents in slot order, then the window blocks
+        tc = int(one["table_count"])
+        entries = [int(x) for x in one["resident"] if x >= 0] + list(range(n_cand, ref.num_blocks(L)))
+        assert one["table"][:tc].tolist() == entries
+
+
+def test_plan_special_cases():
+    r = _rng(11)
+    K, n_cand, W = 8, 30, 64
+    L = 16 * n_cand + W
+    s = np.full(n_cand + 5, -np.inf)
+    s[:n_cand] = r.standard_normal(n_cand)
+    S = ref.topk_blocks(s[None, None], np.array([L]), K, W)
+    R_full = np.array(r.choice(n_cand, K, replace=False))[None, None]
+    # cap >= K with a full resident set: the resident set becomes the selection
+    p = ref.build_plan(s[None, None], S, R_full, np.array([L]), K, W)
+    assert set(p["resident"][0, 0].tolist()) == set(S[0, 0].tolist())
+    # cap = 0: nothing changes
+    p = ref.build_plan(s[None, None], S, R_full, np.array([L]), 0, W)
+    assert p["plan_count"][0, 0] == 0 and np.array_equal(p["resident"], R_full)
+    # resident == selection: empty plan whatever the cap
+    p = ref.build_plan(s[None, None], S, S[:, :, ::-1].copy(), np.array([L]), K, W)
+    assert p["plan_count"][0, 0] == 0
+
+
+def test_plan_exhaustive_tiny():
+    # Every resident set of K = 3 slots over 6 candidates (with empties), every cap:
+    # the result equals the rule stated in words, evaluated by enumeration of
+    # all slot assignments and picking the unique one the rule allows.
+    s = np.array([0.5, 2.0, -1.0, 3.0, 1.0, 0.0, -np.inf, -np.inf])
+    L, W, K = 16 * 6 + 32, 32, 3
+    S = ref.topk_blocks(s[None, None], np.array([L]), K, W)[0, 0]       # [3, 1, 4]
+    assert S.tolist() == [3, 1, 4]
+    vals = [-1] + list(range(6))
+    for R in itertools.product(vals, repeat=K):
+        filled = [x for x in R if x >= 0]
+        if len(filled) != len(set(filled)):
+            continue
+        for cap in range(0, 4):
+            p = ref.build_plan(s[None, None], S[None, None], np.array(R)[None, None], np.array([L]), cap, W)
+            newR = p["resident"][0, 0].tolist()
+            # enumerate all outcomes: choose which slots change and to what
+            new_blocks = [x for x in S if x not in R]
+            n = min(cap, len(new_blocks))
+            want_new = set(new_blocks[:n])                       # best n by selection order
+            empties = [i for i in range(K) if R[i] < 0]
+            stale = sorted([i for i in range(K) if R[i] >= 0 and R[i] not in S],
+                           key=lambda i: (s[R[i]], -R[i]))
+            want_slots = sorted((empties + stale)[:n])
+            candidates = []
+            for slots in itertools.combinations(range(K), n):
+                for perm in itertools.permutations(sorted(want_new)):
+                    out = list(R)
+                    for sl, bl in zip(slots, perm):
+                        out[sl] = bl
+                    ok = (list(slots) == want_slots and list(perm) == sorted(want_new))
+                    if ok:
+                        candidates.append(out)
+            assert len(candidates) == 1
+            assert newR == candidates[0]
+
+
+# ---------------------------------------------------------------------------
+# O4 attention
+# ---------------------------------------------------------------------------
+
+def test_attention_all_blocks_equals_dense_sdpa():
+    q, k, v, lens = _tiny_inputs(12, B=2, H=2, G=3, Q=2, NB=6, d=16, lens=(96, 77))
+    B, H, G, Q, d = q.shape
+    NB = k.shape[2]
+    table = np.tile(np.arange(NB), (B, H, 1))
+    tc = np.full((B, H), NB)
+    scale = 1 / math.sqrt(d)
+    out, lse = ref.sparse_attention(q, k, v, table, tc, lens, scale)
+    for b in range(B):
+        L = int(lens[b])
+        kk = torch.from_numpy(k[b].reshape(H, NB * 16, d)[:, :L])
+        vv = torch.from_numpy(v[b].reshape(H, NB * 16, d)[:, :L])
+        qq = torch.from_numpy(q[b, :, :, 0, :])                              # [H, G, d]
+        dense = torch.nn.functional.scaled_dot_product_attention(
+            qq[:, :, None, :], kk[:, None].expand(H, G, L, d), vv[:, None].expand(H, G, L, d), scale=scale)
+        np.testing.assert_allclose(out[b], dense[:, :, 0, :].numpy(), rtol=0, atol=1e-12)
+        z = torch.einsum("hgd,htd->hgt", qq, kk) * scale
+        np.testing.assert_allclose(lse[b], torch.logsumexp(z, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_attention_special_cases():
+    q, k, v, lens = _tiny_inputs(13, B=1, H=1, G=2, Q=2, NB=5, d=8, lens=(70,))
+    scale = 0.3
+    # constant values: output equals that value
+    vc = np.broadcast_to(np.arange(8.0), v.shape).copy()
+    table = np.array([[[4, 0, 2, -1, -1]]])
+    tc = np.array([[3]])
+    out, _ = ref.sparse_attention(q, k, vc, table, tc, lens, scale)
+    np.testing.assert_allclose(out[0, 0], np.broadcast_to(np.arange(8.0), (2, 8)), atol=1e-12)
+    # permutation invariance
+    o1, l1 = ref.sparse_attention(q, k, v, table, tc, lens, scale)
+    o2, l2 = ref.sparse_attention(q, k, v, np.array([[[2, 4, 0, -1, -1]]]), tc, lens, scale)
+    np.testing.assert_allclose(o1, o2, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, atol=1e-12)
+    # one partial block (block 4 holds tokens 64..69): closed-form softmax over 6 tokens
+    o, l = ref.sparse_attention(q, k, v, np.array([[[4, -1, -1, -1, -1]]]), np.array([[1]]), lens, scale)
+    for g in range(2):
+        z = [float(q[0, 0, g, 0] @ k[0, 0, 4, t]) * scale for t in range(6)]
+        m = max(z)
+        w = [math.exp(x - m) for x in z]
+        expect = sum(wi * v[0, 0, 4, t] for t, wi in enumerate(w)) / sum(w)
+        np.testing.assert_allclose(o[0, 0, g], expect, atol=1e-12)
+        assert l[0, 0, g] == pytest.approx(m + math.log(sum(w)), abs=1e-12)
+    # no token at all: zeros and -inf
+    o, l = ref.sparse_attention(q, k, v, np.full((1, 1, 5), -1), np.array([[0]]), lens, scale)
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+
+
+def test_attention_uses_target_query_only():
+    q, k, v, lens = _tiny_inputs(14, B=1, H=1, G=1, Q=3, NB=3, d=8, lens=(48,))
+    table, tc = np.array([[[0, 1, 2]]]), np.array([[3]])
+    o1, _ = ref.sparse_attention(q, k, v, table, tc, lens, 0.35)
+    q2 = q.copy()
+    q2[:, :, :, 1:, :] = 0.0
+    o2, _ = ref.sparse_attention(q2, k, v, table, tc, lens, 0.35)
+    np.testing.assert_array_equal(o1, o2)
+
+
+# ---------------------------------------------------------------------------
+# geometry, cap, budget
+# ---------------------------------------------------------------------------
+
+def test_window_geometry():
+    # the window blocks overlap the last W tokens; count <= ceil(W/16) + 1
+    for L in range(1, 400):
+        for W in (0, 1, 15, 16, 17, 64, 128):
+            w0, nb = ref.first_window_block(L, W), ref.num_blocks(L)
+            toks = set(range(max(0, L - W), L))
+            covered = set(t for j in range(w0, nb) for t in range(16 * j, min(16 * j + 16, L)))
+            assert toks <= covered
+            if w0 > 0:
+                assert 16 * w0 <= L - W          # block w0 - 1 lies wholly before the window
+            assert nb - w0 <= -(-W // 16) + 1
+
+
+def test_fetch_cap_values():
+    assert ref.fetch_cap(0.05, 128) == 6          # default ratio at K = 128
+    assert ref.fetch_cap(0.05, 16) == 0
+    assert ref.fetch_cap(0.29, 100) == 29
+    assert [ref.fetch_cap(x, 128) for x in (0.01, 0.02, 0.05, 0.10, 0.20)] == [1, 2, 6, 12, 25]
+    assert ref.fetch_cap(1.0, 128) == 128
+
+
+def test_token_budget():
+    # [lode] and [xllm] section six: K = 128 blocks of 16 tokens is the 2,048-token budget.
+    assert 128 * 16 == 2048
+
+
+# ---------------------------------------------------------------------------
+# the whole step on the small synthetic workload
+# ---------------------------------------------------------------------------
+
+def test_decode_step_tiny_workload():
+    import synth
+    w = synth.WORKLOADS["tiny_4k"]
+    inp = synth.generate(w, "cpu")
+    f64 = lambda t: t.to(torch.float64).numpy()
+    q, k, v = f64(inp["q"]), f64(inp["k"]), f64(inp["v"])
+    lens = inp["seq_lens"].numpy()
+    summ = ref.build_summaries(k, lens)
+    s = ref.score_blocks(q, summ, lens, w.window)
+    sel = ref.topk_blocks(s, lens, w.top_k, w.window)
+    R = synth.resident_from_selection(w, torch.from_numpy(sel), inp["seq_lens"]).numpy()
+    res = ref.decode_step(q, summ, k, v, lens, R, w.top_k, w.window, w.cap, 1 / math.sqrt(128))
+    assert w.cap == 0
+    assert np.all(res["plan_count"] == 0) and np.array_equal(res["resident"], R)
+    # planted blocks carry a +2|q| shift along one target direction, several standard
+    # deviations of the bound's spread: most of them make the top-K
+    planted = inp["planted"].numpy()
+    for h in range(w.num_kv_heads):
+        hot = set(np.nonzero(planted[0, h])[0].tolist())
+        assert len(hot) == w.planted
+        assert len(hot & set(sel[0, h].tolist())) >= w.planted // 2
+    assert np.all(res["table_count"] == w.top_k + 4)
+    assert np.all(np.isfinite(res["out"]))

@@ -1,0 +1,67 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that the pins catch each.
+
+Each mutation edits one line of the oracle's source, loads the edited copy as a
+separate module, points the pin tests at it and expects at least one of them
+to fail.  The oracle file itself is never modified.
+"""
+import inspect
+import types
+
+import pytest
+
+import oracle.ref as ref_mod
+from tests import test_oracle as pins
+
+MUTATIONS = {
+    "score_swaps_min_and_max": ("kmin = summ[b, h, :n_cand, 0, :]", "kmin = summ[b, h, :n_cand, 1, :]"),
+    "score_takes_min_of_products": ("bound = np.maximum(lo, hi).sum(axis=-1)", "bound = np.minimum(lo, hi).sum(axis=-1)"),
+    "score_averages_rows": ("s[b, h, :n_cand] = bound.max(axis=0)", "s[b, h, :n_cand] = bound.mean(axis=0)"),
+    "topk_ties_prefer_high_index": ("order = np.lexsort((idx, -s))", "order = np.lexsort((-idx, -s))"),
+    "window_one_block_late": ("return max(0, (int(seq_len) - int(window)) // block)",
+                              "return max(0, (int(seq_len) - int(window)) // block + 1)"),
+    "plan_admits_worst_first": ("admit = admit[:n]", "admit = admit[::-1][:n]"),
+    "plan_stale_tie_low_index": ("stale.sort(key=lambda i: (s[int(res[i])], -int(res[i])))",
+                                 "stale.sort(key=lambda i: (s[int(res[i])], int(res[i])))"),
+    "plan_evicts_best_stale": ("stale.sort(key=lambda i: (s[int(res[i])], -int(res[i])))",
+                               "stale.sort(key=lambda i: (-s[int(res[i])], -int(res[i])))"),
+    "plan_pairs_unsorted": ("zip(sorted(victims), sorted(admit))", "zip(victims, admit)"),
+    "summaries_read_past_length": ("n_valid = min(bs, L - j * bs)", "n_valid = bs"),
+    "attention_drops_scale": ("z = (kt @ q[b, h, g, 0, :]) * scale", "z = (kt @ q[b, h, g, 0, :])"),
+    "attention_uses_a_draft": ("z = (kt @ q[b, h, g, 0, :]) * scale", "z = (kt @ q[b, h, g, 1, :]) * scale"),
+    "attention_ignores_length": ("if j * block + t < L]", "if True]"),
+    "table_drops_window": ("entries = [int(x) for x in r if x >= 0] + list(range(w0, nb))",
+                           "entries = [int(x) for x in r if x >= 0]"),
+    "cap_rounds_to_nearest": ("return int(math.floor(float(fetch_ratio) * int(top_k) + 1e-9))",
+                              "return int(round(float(fetch_ratio) * int(top_k)))"),
+}
+
+PIN_TESTS = [getattr(pins, n) for n in dir(pins)
+             if n.startswith("test_") and n != "test_decode_step_tiny_workload"]
+
+
+def _run_pins(mutant, monkeypatch) -> bool:
+    """True if some pin fails against ``mutant``."""
+    monkeypatch.setattr(pins, "ref", mutant)
+    for t in PIN_TESTS:
+        params = inspect.signature(t).parameters
+        variants = [{"distinct": True}, {"distinct": False}] if "distinct" in params else [{}]
+        for kw in variants:
+            try:
+                t(**kw)
+            except Exception:
+                return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, monkeypatch):
+    src = inspect.getsource(ref_mod)
+    old, new = MUTATIONS[name]
+    assert src.count(old) >= 1, name
+    mutant = types.ModuleType("oracle_mutant_" + name)
+    exec(compile(src.replace(old, new), "<mutant " + name + ">", "exec"), mutant.__dict__)
+    assert _run_pins(mutant, monkeypatch), f"mutation {name} went unnoticed"
+
+
+def test_unmutated_oracle_passes(monkeypatch):
+    assert not _run_pins(ref_mod, monkeypatch)
