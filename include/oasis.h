@@ -1,0 +1,219 @@
+/*
+ * oasis.h -- C ABI of liboasis: one decode step of one attention layer of
+ * OasisKV's look-ahead sparse attention, on AMD Instinct MI355X (gfx950).
+ *
+ * The step has four parts (xllm-io paper review of OasisKV, section three,
+ * training flow step 3): the draft and target queries scan per-block min/max
+ * key summaries, a top-K of blocks is predicted per KV head, the prediction is
+ * compared with the resident set to build a capped transfer plan, and the
+ * target queries attend over the resulting head-wise block table.
+ *
+ * Conventions for every entry point below:
+ *   - Pointers named as device pointers must point to GPU memory that stays
+ *     valid until the work queued on `stream` has finished; `dims` is a host
+ *     pointer read during the call only.  The library keeps no pointer after
+ *     it returns, allocates no memory and holds no state apart from a
+ *     thread-local error string.
+ *   - Tensors are dense and row-major in the layouts stated per argument.
+ *     bf16 data is IEEE bfloat16 stored in 16 bits.
+ *   - Work is queued on `stream` (NULL = the default stream) and is
+ *     asynchronous: a status of OASIS_OK means the launches were queued.
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Host-side argument checks run before anything is queued.  On an error
+ *     status nothing is queued and no output is touched; the reason is in
+ *     oasis_last_error().
+ *   - Values that live in device memory (sequence lengths, selections,
+ *     resident sets, tables) cannot be checked on the host.  Their stated
+ *     ranges are preconditions; out-of-range entries are skipped or treated
+ *     as empty by the kernels so that no access leaves the buffers, but the
+ *     results for such entries are unspecified.
+ *   - Calls that write the same buffers must not run concurrently.
+ *
+ * Notation: B sequences, H = num_kv_heads, G = group (query heads per KV
+ * head), Q = num_queries (index 0 is the target query, 1..Q-1 the drafts),
+ * d = head_dim = 128, bs = block_size = 16, NB = max_blocks, K = top_k,
+ * W = window_tokens, C = oasis_fetch_cap(), T = oasis_table_stride().
+ * For sequence b with length len_b (1 <= len_b <= 16 * NB):
+ *   nblk_b = ceil(len_b / 16)            blocks holding a token,
+ *   w0_b   = max(0, floor((len_b - W) / 16))   first local-window block.
+ * Blocks [0, w0_b) are the scoring candidates; blocks [w0_b, nblk_b) form the
+ * local window, which is always attended and never scored or evicted.
+ */
+#ifndef OASIS_H_
+#define OASIS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OASIS_ABI_VERSION 1
+
+typedef enum {
+  OASIS_OK = 0,
+  OASIS_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad ratio, ... */
+  OASIS_ERR_UNSUPPORTED = 2,   /* valid request outside what the kernels implement */
+  OASIS_ERR_WORKSPACE = 3,     /* workspace missing or smaller than oasis_workspace_bytes() */
+  OASIS_ERR_HIP = 4            /* a HIP runtime call failed; text in oasis_last_error() */
+} oasis_status;
+
+/* Problem sizes of one decode step of one layer.  Host struct, read during the
+ * call only.  Supported: head_dim == 128, block_size == 16, 1 <= top_k <= 1024,
+ * top_k <= max_blocks <= 32768, group * num_queries <= 128, group <= 16,
+ * window_tokens >= 0, 0 <= fetch_ratio <= 1. */
+typedef struct {
+  int32_t batch;           /* B */
+  int32_t num_kv_heads;    /* H */
+  int32_t group;           /* G query heads per KV head (GQA group) */
+  int32_t head_dim;        /* d, must be 128 */
+  int32_t block_size;      /* tokens per block, must be 16 */
+  int32_t max_blocks;      /* NB: block stride of every per-block tensor */
+  int32_t num_queries;     /* Q = 1 + drafts per query head */
+  int32_t top_k;           /* K blocks selected per KV head */
+  int32_t window_tokens;   /* W local-window tokens kept resident */
+  double fetch_ratio;      /* cap C = floor(fetch_ratio * K) new blocks per KV head per step */
+} oasis_dims;
+
+/* Version of this ABI (OASIS_ABI_VERSION of the header the library was built with). */
+int oasis_abi_version(void);
+
+/* Static text for a status code. */
+const char* oasis_status_string(oasis_status status);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* oasis_last_error(void);
+
+/* The capped-eviction cap C = floor(fetch_ratio * top_k), taken in double
+ * precision with a 1e-9 guard (xllm-io review, section three component table,
+ * Capped Eviction Policy: fetch ratio 0.05 by default; legiblepapers.com FAQ
+ * Q7).  Returns -1 if dims is invalid. */
+int32_t oasis_fetch_cap(const oasis_dims* dims);
+
+/* Row length T of the attention table: K resident slots plus the most local-
+ * window blocks any length can produce, ceil(W / 16) + 1.  -1 if invalid. */
+int32_t oasis_table_stride(const oasis_dims* dims);
+
+/* Device workspace that oasis_decode_step needs (and oasis_sparse_decode_attn
+ * with table_stride == oasis_table_stride(dims)), in bytes, a multiple of 256.
+ * It holds the per-split attention partials.  0 if dims is invalid. */
+size_t oasis_workspace_bytes(const oasis_dims* dims);
+
+/* Device workspace that oasis_sparse_decode_attn needs for a given table
+ * stride, in bytes, a multiple of 256.  0 if an argument is invalid. */
+size_t oasis_attn_workspace_bytes(const oasis_dims* dims, int32_t table_stride);
+
+/* Per-block min/max key summaries ("compressed keys"): for every block j of
+ * every (b, h), summ[b,h,j,0,:] = min and summ[b,h,j,1,:] = max over the valid
+ * tokens t (16*j + t < len_b) of k[b,h,j,t,:].  Blocks without a valid token
+ * get zeros.  Exact (bf16 min/max).
+ * xllm-io review, section three component table (Compressed Key Cache:
+ * per-dimension min/max of every logical block, 1/16 of the KV size) and
+ * section two (Quest-style min/max pooling).
+ *   k        device, bf16 [B, H, NB, 16, 128]
+ *   seq_lens device, int32 [B]
+ *   summ     device, bf16 [B, H, NB, 2, 128]   (output) */
+oasis_status oasis_build_summaries(const oasis_dims* dims, const void* k, const int32_t* seq_lens,
+                                   void* summ, hipStream_t stream);
+
+/* Look-ahead block scores: for every candidate block j < w0_b,
+ *   scores[b,h,j] = max over g < G, i < Q of
+ *                   sum_d max(q[b,h,g,i,d] * kmin[b,h,j,d], q[b,h,g,i,d] * kmax[b,h,j,d]),
+ * the Quest upper bound of q.k over the block, aggregated by max over the GQA
+ * group and the target and draft queries.  Blocks j >= w0_b get -inf.
+ * bf16 inputs, fp32 accumulation.
+ * xllm-io review, section two (the draft queries scan the compressed key
+ * summary to predict next step's important blocks) and section three
+ * component table (Look-ahead Attention).
+ *   q        device, bf16 [B, H, G, Q, 128]
+ *   summ     device, bf16 [B, H, NB, 2, 128]  (oasis_build_summaries layout)
+ *   seq_lens device, int32 [B]
+ *   scores   device, fp32 [B, H, NB]          (output) */
+oasis_status oasis_score_summaries(const oasis_dims* dims, const void* q, const void* summ,
+                                   const int32_t* seq_lens, float* scores, hipStream_t stream);
+
+/* Head-wise top-K block selection: topk[b,h,:] lists the min(K, w0_b) best
+ * candidate blocks, best first, under the order "higher fp32 score first,
+ * equal scores: lower block index first" (-0.0 counts as +0.0); remaining
+ * entries are -1.  Scores must not be NaN.
+ * xllm-io review, section three component table (top-K = 128 blocks per head)
+ * and section six (block size 16, K = 128 blocks per KV head).
+ *   scores   device, fp32 [B, H, NB]
+ *   seq_lens device, int32 [B]
+ *   topk     device, int32 [B, H, K]          (output) */
+oasis_status oasis_topk_blocks(const oasis_dims* dims, const float* scores, const int32_t* seq_lens,
+                               int32_t* topk, hipStream_t stream);
+
+/* Capped-eviction transfer plan against the resident set, and the attention
+ * table.  Per (b, h), with S = topk[b,h,:] and R = resident[b,h,:]:
+ *   A = entries of S not in R, in S order; n = min(C, |A|); the first n of A
+ *   are admitted.  Victim slots: empty slots (-1) by ascending slot, then
+ *   slots whose block is not in S by ascending score (equal scores: higher
+ *   block index first); the first n are freed.  Freed slots in ascending slot
+ *   order receive the admitted blocks in ascending block order.
+ *   plan[b,h,r,:] = (slot, new block, old block or -1) for r < n by ascending
+ *   slot, rows r >= n are -1; plan_count[b,h] = n; resident is updated in
+ *   place.  table[b,h,:] = the updated resident entries != -1 in slot order,
+ *   then the window blocks w0_b .. nblk_b - 1, then -1 up to T entries;
+ *   table_count[b,h] = number of entries.
+ * xllm-io review, section three training flow step 3 (compare with the
+ * resident set, build the transfer plan) and component table (Capped
+ * Eviction Policy; Head-wise Mapping), legiblepapers.com FAQ Q7 (the cap
+ * bounds newly admitted blocks at the selection stage).  The admission,
+ * victim and pairing orders are this library's readings; the pages leave
+ * them open.
+ *   scores      device, fp32 [B, H, NB]  (ranks stale slots)
+ *   topk        device, int32 [B, H, K]  (oasis_topk_blocks output)
+ *   seq_lens    device, int32 [B]
+ *   resident    device, int32 [B, H, K]  in/out; entries distinct, in [0, w0_b) or -1
+ *   plan        device, int32 [B, H, C, 3] (output; may be NULL when C == 0)
+ *   plan_count  device, int32 [B, H]       (output)
+ *   table       device, int32 [B, H, T]    (output)
+ *   table_count device, int32 [B, H]       (output) */
+oasis_status oasis_build_plan(const oasis_dims* dims, const float* scores, const int32_t* topk,
+                              const int32_t* seq_lens, int32_t* resident, int32_t* plan,
+                              int32_t* plan_count, int32_t* table, int32_t* table_count,
+                              hipStream_t stream);
+
+/* Sparse decode attention of the target queries over the head-wise table:
+ *   out[b,h,g,:] = sum_t softmax_t(scale * q[b,h,g,0,:] . k_t) v_t
+ * over the tokens t of the blocks table[b,h,0 .. table_count[b,h]-1] whose
+ * index is below len_b; lse[b,h,g] = log(sum_t exp(scale * q.k_t)).  With no
+ * token, out = 0 and lse = -inf.  bf16 inputs, fp32 softmax and accumulation.
+ * xllm-io review, section three training flow step 3 (foreground attention
+ * over the sparse working set) and architecture figure (sparse working set
+ * in HBM: selected blocks plus the local window).
+ *   q            device, bf16 [B, H, G, Q, 128] (row 0 of each query head is used)
+ *   k, v         device, bf16 [B, H, NB, 16, 128]
+ *   table        device, int32 [B, H, table_stride]; entries distinct, in [0, NB)
+ *   table_count  device, int32 [B, H], each in [0, table_stride]
+ *   table_stride host, 1 <= table_stride <= 4096
+ *   seq_lens     device, int32 [B]
+ *   scale        host, finite
+ *   out          device, fp32 [B, H, G, 128]   (output)
+ *   lse          device, fp32 [B, H, G]        (output; may be NULL)
+ *   ws, ws_bytes device workspace, at least oasis_attn_workspace_bytes(dims, table_stride) */
+oasis_status oasis_sparse_decode_attn(const oasis_dims* dims, const void* q, const void* k,
+                                      const void* v, const int32_t* table,
+                                      const int32_t* table_count, int32_t table_stride,
+                                      const int32_t* seq_lens, float scale, float* out, float* lse,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole step on one stream: oasis_score_summaries, oasis_topk_blocks,
+ * oasis_build_plan, then oasis_sparse_decode_attn over the updated table
+ * (table_stride = oasis_table_stride(dims)).  Arguments as above. */
+oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void* summ,
+                               const void* k, const void* v, const int32_t* seq_lens,
+                               float* scores, int32_t* topk, int32_t* resident, int32_t* plan,
+                               int32_t* plan_count, int32_t* table, int32_t* table_count,
+                               float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OASIS_H_ */

@@ -1,0 +1,328 @@
+"""ctypes binding of liboasis (see include/oasis.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of liboasis.so.  PyTorch provides device memory and the current HIP
+stream.  Shapes, dtypes, devices and contiguity are checked here before any
+pointer reaches the library, so that a kernel never sees a buffer smaller
+than its grid assumes.  There is no fallback: without the built library every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Dict, Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liboasis.so")
+
+OASIS_OK = 0
+STATUS_NAMES = {0: "OASIS_OK", 1: "OASIS_ERR_INVALID_ARG", 2: "OASIS_ERR_UNSUPPORTED",
+                3: "OASIS_ERR_WORKSPACE", 4: "OASIS_ERR_HIP"}
+
+
+class OasisDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("num_queries", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("window_tokens", ctypes.c_int32),
+        ("fetch_ratio", ctypes.c_double),
+    ]
+
+    def __repr__(self):
+        return "OasisDims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class OasisError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_DIMS = ctypes.POINTER(OasisDims)
+_SIGNATURES = {
+    "oasis_abi_version": (ctypes.c_int, []),
+    "oasis_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "oasis_last_error": (ctypes.c_char_p, []),
+    "oasis_fetch_cap": (ctypes.c_int32, [_DIMS]),
+    "oasis_table_stride": (ctypes.c_int32, [_DIMS]),
+    "oasis_workspace_bytes": (ctypes.c_size_t, [_DIMS]),
+    "oasis_attn_workspace_bytes": (ctypes.c_size_t, [_DIMS, ctypes.c_int32]),
+    "oasis_build_summaries": (ctypes.c_int, [_DIMS, _P, _P, _P, _P]),
+    "oasis_score_summaries": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P]),
+    "oasis_topk_blocks": (ctypes.c_int, [_DIMS, _P, _P, _P, _P]),
+    "oasis_build_plan": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "oasis_sparse_decode_attn": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
+                                                ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "oasis_decode_step": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liboasis.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it first (python -m oasis_score_summaries_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols() -> Tuple[str, ...]:
+    return tuple(_SIGNATURES)
+
+
+def _check(status: int, where: str) -> None:
+    if status != OASIS_OK:
+        msg = load().oasis_last_error().decode(errors="replace")
+        raise OasisError(status, where, msg)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...], device=None,
+          align: int = 4):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.data_ptr() % align != 0:
+        raise ValueError(f"{name} must be {align}-byte aligned")
+
+
+def make_dims(batch: int, num_kv_heads: int, group: int, max_blocks: int, num_queries: int,
+              top_k: int, window_tokens: int, fetch_ratio: float, head_dim: int = 128,
+              block_size: int = 16) -> OasisDims:
+    return OasisDims(batch, num_kv_heads, group, head_dim, block_size, max_blocks, num_queries,
+                     top_k, window_tokens, float(fetch_ratio))
+
+
+def dims_for(workload) -> OasisDims:
+    """Dims of a synthetic workload (any object with the Workload fields)."""
+    return make_dims(workload.batch, workload.num_kv_heads, workload.group, workload.max_blocks,
+                     workload.queries, workload.top_k, workload.window, workload.fetch_ratio)
+
+
+def fetch_cap(dims: OasisDims) -> int:
+    c = load().oasis_fetch_cap(ctypes.byref(dims))
+    if c < 0:
+        _check(1, "oasis_fetch_cap")
+    return c
+
+
+def table_stride(dims: OasisDims) -> int:
+    t = load().oasis_table_stride(ctypes.byref(dims))
+    if t < 0:
+        _check(1, "oasis_table_stride")
+    return t
+
+
+def workspace_bytes(dims: OasisDims, stride: Optional[int] = None) -> int:
+    lib = load()
+    n = (lib.oasis_workspace_bytes(ctypes.byref(dims)) if stride is None
+         else lib.oasis_attn_workspace_bytes(ctypes.byref(dims), int(stride)))
+    if n == 0:
+        _check(1, "oasis_workspace_bytes")
+    return n
+
+
+def _shapes(d: OasisDims):
+    B, H, G, Q, NB, K = d.batch, d.num_kv_heads, d.group, d.num_queries, d.max_blocks, d.top_k
+    return {
+        "q": (B, H, G, Q, 128), "kv": (B, H, NB, 16, 128), "summ": (B, H, NB, 2, 128),
+        "lens": (B,), "scores": (B, H, NB), "topk": (B, H, K), "resident": (B, H, K),
+        "bh": (B, H), "out": (B, H, G, 128), "lse": (B, H, G),
+    }
+
+
+def build_summaries(dims: OasisDims, k: torch.Tensor, seq_lens: torch.Tensor,
+                    summ: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    s = _shapes(dims)
+    _need(k, "k", torch.bfloat16, s["kv"], align=16)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], k.device)
+    if summ is None:
+        summ = torch.empty(s["summ"], dtype=torch.bfloat16, device=k.device)
+    _need(summ, "summ", torch.bfloat16, s["summ"], k.device, align=16)
+    _check(load().oasis_build_summaries(ctypes.byref(dims), _ptr(k), _ptr(seq_lens), _ptr(summ),
+                                        _stream(stream)), "oasis_build_summaries")
+    return summ
+
+
+def score_summaries(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor, seq_lens: torch.Tensor,
+                    scores: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    s = _shapes(dims)
+    _need(q, "q", torch.bfloat16, s["q"], align=16)
+    _need(summ, "summ", torch.bfloat16, s["summ"], q.device, align=16)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], q.device)
+    if scores is None:
+        scores = torch.empty(s["scores"], dtype=torch.float32, device=q.device)
+    _need(scores, "scores", torch.float32, s["scores"], q.device)
+    _check(load().oasis_score_summaries(ctypes.byref(dims), _ptr(q), _ptr(summ), _ptr(seq_lens),
+                                        _ptr(scores), _stream(stream)), "oasis_score_summaries")
+    return scores
+
+
+def topk_blocks(dims: OasisDims, scores: torch.Tensor, seq_lens: torch.Tensor,
+                topk: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    s = _shapes(dims)
+    _need(scores, "scores", torch.float32, s["scores"])
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], scores.device)
+    if topk is None:
+        topk = torch.empty(s["topk"], dtype=torch.int32, device=scores.device)
+    _need(topk, "topk", torch.int32, s["topk"], scores.device)
+    _check(load().oasis_topk_blocks(ctypes.byref(dims), _ptr(scores), _ptr(seq_lens), _ptr(topk),
+                                    _stream(stream)), "oasis_topk_blocks")
+    return topk
+
+
+def _plan_outputs(dims: OasisDims, device, plan, plan_count, table, table_count):
+    s = _shapes(dims)
+    C, T = fetch_cap(dims), table_stride(dims)
+    if plan is None:
+        plan = torch.empty((dims.batch, dims.num_kv_heads, C, 3), dtype=torch.int32, device=device)
+    if plan_count is None:
+        plan_count = torch.empty(s["bh"], dtype=torch.int32, device=device)
+    if table is None:
+        table = torch.empty((dims.batch, dims.num_kv_heads, T), dtype=torch.int32, device=device)
+    if table_count is None:
+        table_count = torch.empty(s["bh"], dtype=torch.int32, device=device)
+    _need(plan, "plan", torch.int32, (dims.batch, dims.num_kv_heads, C, 3), device)
+    _need(plan_count, "plan_count", torch.int32, s["bh"], device)
+    _need(table, "table", torch.int32, (dims.batch, dims.num_kv_heads, T), device)
+    _need(table_count, "table_count", torch.int32, s["bh"], device)
+    return plan, plan_count, table, table_count
+
+
+def build_plan(dims: OasisDims, scores: torch.Tensor, topk: torch.Tensor, seq_lens: torch.Tensor,
+               resident: torch.Tensor, plan=None, plan_count=None, table=None, table_count=None,
+               stream=None) -> Dict[str, torch.Tensor]:
+    """Applies the capped plan; ``resident`` is updated in place."""
+    s = _shapes(dims)
+    _need(scores, "scores", torch.float32, s["scores"])
+    dev = scores.device
+    _need(topk, "topk", torch.int32, s["topk"], dev)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+    _need(resident, "resident", torch.int32, s["resident"], dev)
+    plan, plan_count, table, table_count = _plan_outputs(dims, dev, plan, plan_count, table, table_count)
+    _check(load().oasis_build_plan(ctypes.byref(dims), _ptr(scores), _ptr(topk), _ptr(seq_lens),
+                                   _ptr(resident), _ptr(plan if plan.numel() else None),
+                                   _ptr(plan_count), _ptr(table), _ptr(table_count), _stream(stream)),
+           "oasis_build_plan")
+    return {"plan": plan, "plan_count": plan_count, "resident": resident, "table": table,
+            "table_count": table_count}
+
+
+def sparse_decode_attn(dims: OasisDims, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       table: torch.Tensor, table_count: torch.Tensor, seq_lens: torch.Tensor,
+                       scale: Optional[float] = None, out=None, lse=None, ws=None,
+                       stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    s = _shapes(dims)
+    _need(q, "q", torch.bfloat16, s["q"], align=16)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, s["kv"], dev, align=16)
+    _need(v, "v", torch.bfloat16, s["kv"], dev, align=16)
+    if table.dim() != 3:
+        raise ValueError("table must be [B, H, table_stride]")
+    stride = int(table.shape[2])
+    _need(table, "table", torch.int32, (dims.batch, dims.num_kv_heads, stride), dev)
+    _need(table_count, "table_count", torch.int32, s["bh"], dev)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(128)
+    if out is None:
+        out = torch.empty(s["out"], dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(s["lse"], dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, s["out"], dev)
+    _need(lse, "lse", torch.float32, s["lse"], dev)
+    need = workspace_bytes(dims, stride)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if ws.device != dev or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous uint8 GPU tensor on the inputs' device")
+    _check(load().oasis_sparse_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(table),
+                                           _ptr(table_count), stride, _ptr(seq_lens), float(scale),
+                                           _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)),
+           "oasis_sparse_decode_attn")
+    return out, lse
+
+
+class StepBuffers:
+    """Outputs and workspace of oasis_decode_step, allocated once and reused."""
+
+    def __init__(self, dims: OasisDims, device):
+        s = _shapes(dims)
+        dev = torch.device(device)
+        self.scores = torch.empty(s["scores"], dtype=torch.float32, device=dev)
+        self.topk = torch.empty(s["topk"], dtype=torch.int32, device=dev)
+        self.plan, self.plan_count, self.table, self.table_count = _plan_outputs(
+            dims, dev, None, None, None, None)
+        self.out = torch.empty(s["out"], dtype=torch.float32, device=dev)
+        self.lse = torch.empty(s["lse"], dtype=torch.float32, device=dev)
+        self.ws = torch.empty(workspace_bytes(dims), dtype=torch.uint8, device=dev)
+
+    def as_dict(self) -> Dict[str, torch.Tensor]:
+        return {n: getattr(self, n) for n in ("scores", "topk", "plan", "plan_count", "table",
+                                              "table_count", "out", "lse")}
+
+
+def decode_step(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor, k: torch.Tensor,
+                v: torch.Tensor, seq_lens: torch.Tensor, resident: torch.Tensor,
+                scale: Optional[float] = None, buffers: Optional[StepBuffers] = None,
+                stream=None) -> Dict[str, torch.Tensor]:
+    """score -> top-K -> capped plan (``resident`` updated in place) -> attention."""
+    s = _shapes(dims)
+    _need(q, "q", torch.bfloat16, s["q"], align=16)
+    dev = q.device
+    _need(summ, "summ", torch.bfloat16, s["summ"], dev, align=16)
+    _need(k, "k", torch.bfloat16, s["kv"], dev, align=16)
+    _need(v, "v", torch.bfloat16, s["kv"], dev, align=16)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+    _need(resident, "resident", torch.int32, s["resident"], dev)
+    if buffers is None:
+        buffers = StepBuffers(dims, dev)
+    b = buffers
+    if scale is None:
+        scale = 1.0 / math.sqrt(128)
+    _check(load().oasis_decode_step(
+        ctypes.byref(dims), _ptr(q), _ptr(summ), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(b.scores),
+        _ptr(b.topk), _ptr(resident), _ptr(b.plan if b.plan.numel() else None), _ptr(b.plan_count),
+        _ptr(b.table), _ptr(b.table_count), float(scale), _ptr(b.out), _ptr(b.lse), _ptr(b.ws),
+        b.ws.numel(), _stream(stream)), "oasis_decode_step")
+    res = b.as_dict()
+    res["resident"] = resident
+    return res

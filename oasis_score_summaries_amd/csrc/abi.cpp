@@ -1,0 +1,244 @@
+// C ABI of liboasis: host-side argument checks and launches (see include/oasis.h).
+#include "oasis.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+oasis_status fail(oasis_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+oasis_status hip_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return OASIS_OK;
+  return fail(OASIS_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+// Checks `in` and fills `out`.  Returns OASIS_OK or the error (text set).
+oasis_status check_dims(const oasis_dims* in, oasis::Dims* out) {
+  using namespace oasis;
+  if (in == nullptr) return fail(OASIS_ERR_INVALID_ARG, "dims is NULL");
+  if (in->head_dim != kHeadDim)
+    return fail(OASIS_ERR_UNSUPPORTED, "head_dim %d: only %d is implemented", in->head_dim, kHeadDim);
+  if (in->block_size != kBlock)
+    return fail(OASIS_ERR_UNSUPPORTED, "block_size %d: only %d is implemented", in->block_size, kBlock);
+  if (in->batch < 1 || in->num_kv_heads < 1 || in->group < 1 || in->num_queries < 1)
+    return fail(OASIS_ERR_INVALID_ARG, "batch, num_kv_heads, group and num_queries must be >= 1");
+  if (in->max_blocks < 1) return fail(OASIS_ERR_INVALID_ARG, "max_blocks must be >= 1");
+  if (in->top_k < 1) return fail(OASIS_ERR_INVALID_ARG, "top_k must be >= 1");
+  if (in->top_k > in->max_blocks)
+    return fail(OASIS_ERR_INVALID_ARG, "top_k %d exceeds max_blocks %d", in->top_k, in->max_blocks);
+  if (in->window_tokens < 0) return fail(OASIS_ERR_INVALID_ARG, "window_tokens must be >= 0");
+  if (!(in->fetch_ratio >= 0.0 && in->fetch_ratio <= 1.0))
+    return fail(OASIS_ERR_INVALID_ARG, "fetch_ratio must lie in [0, 1]");
+  if (in->max_blocks > kMaxBlocks)
+    return fail(OASIS_ERR_UNSUPPORTED, "max_blocks %d exceeds %d", in->max_blocks, kMaxBlocks);
+  if (in->top_k > kMaxTopK) return fail(OASIS_ERR_UNSUPPORTED, "top_k %d exceeds %d", in->top_k, kMaxTopK);
+  if ((int64_t)in->group * in->num_queries > kMaxRows)
+    return fail(OASIS_ERR_UNSUPPORTED, "group * num_queries exceeds %d", kMaxRows);
+  if (in->group > kMaxGroup) return fail(OASIS_ERR_UNSUPPORTED, "group %d exceeds %d", in->group, kMaxGroup);
+  if ((int64_t)in->batch * in->num_kv_heads > 65535)
+    return fail(OASIS_ERR_UNSUPPORTED, "batch * num_kv_heads exceeds 65535");
+  if (in->window_tokens > kMaxBlocks * kBlock)
+    return fail(OASIS_ERR_UNSUPPORTED, "window_tokens exceeds %d", kMaxBlocks * kBlock);
+  out->batch = in->batch;
+  out->heads = in->num_kv_heads;
+  out->group = in->group;
+  out->max_blocks = in->max_blocks;
+  out->queries = in->num_queries;
+  out->top_k = in->top_k;
+  out->window = in->window_tokens;
+  out->cap = (int)floor(in->fetch_ratio * (double)in->top_k + 1e-9);
+  out->table_stride = in->top_k + (in->window_tokens + kBlock - 1) / kBlock + 1;
+  return OASIS_OK;
+}
+
+#define OASIS_REQUIRE(ptr)                                                      \
+  do {                                                                          \
+    if ((ptr) == nullptr) return fail(OASIS_ERR_INVALID_ARG, "%s is NULL", #ptr); \
+  } while (0)
+
+oasis_status check_table_stride(const oasis::Dims& d, int32_t table_stride) {
+  if (table_stride < 1 || table_stride > oasis::kMaxTableStride)
+    return fail(OASIS_ERR_INVALID_ARG, "table_stride %d outside [1, %d]", table_stride,
+                oasis::kMaxTableStride);
+  (void)d;
+  return OASIS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oasis_abi_version(void) { return OASIS_ABI_VERSION; }
+
+const char* oasis_status_string(oasis_status status) {
+  switch (status) {
+    case OASIS_OK: return "ok";
+    case OASIS_ERR_INVALID_ARG: return "invalid argument";
+    case OASIS_ERR_UNSUPPORTED: return "unsupported";
+    case OASIS_ERR_WORKSPACE: return "workspace too small";
+    case OASIS_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* oasis_last_error(void) { return g_last_error; }
+
+int32_t oasis_fetch_cap(const oasis_dims* dims) {
+  oasis::Dims d;
+  if (check_dims(dims, &d) != OASIS_OK) return -1;
+  return d.cap;
+}
+
+int32_t oasis_table_stride(const oasis_dims* dims) {
+  oasis::Dims d;
+  if (check_dims(dims, &d) != OASIS_OK) return -1;
+  return d.table_stride;
+}
+
+size_t oasis_workspace_bytes(const oasis_dims* dims) {
+  oasis::Dims d;
+  if (check_dims(dims, &d) != OASIS_OK) return 0;
+  return oasis::attn_workspace_bytes(d, d.table_stride);
+}
+
+size_t oasis_attn_workspace_bytes(const oasis_dims* dims, int32_t table_stride) {
+  oasis::Dims d;
+  if (check_dims(dims, &d) != OASIS_OK) return 0;
+  if (check_table_stride(d, table_stride) != OASIS_OK) return 0;
+  return oasis::attn_workspace_bytes(d, table_stride);
+}
+
+oasis_status oasis_build_summaries(const oasis_dims* dims, const void* k, const int32_t* seq_lens,
+                                   void* summ, hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  OASIS_REQUIRE(k);
+  OASIS_REQUIRE(seq_lens);
+  OASIS_REQUIRE(summ);
+  return hip_status(oasis::launch_build_summaries(d, k, seq_lens, summ, stream), "build_summaries");
+}
+
+oasis_status oasis_score_summaries(const oasis_dims* dims, const void* q, const void* summ,
+                                   const int32_t* seq_lens, float* scores, hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  OASIS_REQUIRE(q);
+  OASIS_REQUIRE(summ);
+  OASIS_REQUIRE(seq_lens);
+  OASIS_REQUIRE(scores);
+  return hip_status(oasis::launch_score(d, q, summ, seq_lens, scores, stream), "score_summaries");
+}
+
+oasis_status oasis_topk_blocks(const oasis_dims* dims, const float* scores, const int32_t* seq_lens,
+                               int32_t* topk, hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  OASIS_REQUIRE(scores);
+  OASIS_REQUIRE(seq_lens);
+  OASIS_REQUIRE(topk);
+  return hip_status(oasis::launch_topk(d, scores, seq_lens, topk, stream), "topk_blocks");
+}
+
+oasis_status oasis_build_plan(const oasis_dims* dims, const float* scores, const int32_t* topk,
+                              const int32_t* seq_lens, int32_t* resident, int32_t* plan,
+                              int32_t* plan_count, int32_t* table, int32_t* table_count,
+                              hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  OASIS_REQUIRE(scores);
+  OASIS_REQUIRE(topk);
+  OASIS_REQUIRE(seq_lens);
+  OASIS_REQUIRE(resident);
+  if (d.cap > 0) OASIS_REQUIRE(plan);
+  OASIS_REQUIRE(plan_count);
+  OASIS_REQUIRE(table);
+  OASIS_REQUIRE(table_count);
+  return hip_status(oasis::launch_plan(d, scores, topk, seq_lens, resident, plan, plan_count, table,
+                                       table_count, stream),
+                    "build_plan");
+}
+
+oasis_status oasis_sparse_decode_attn(const oasis_dims* dims, const void* q, const void* k,
+                                      const void* v, const int32_t* table,
+                                      const int32_t* table_count, int32_t table_stride,
+                                      const int32_t* seq_lens, float scale, float* out, float* lse,
+                                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  OASIS_REQUIRE(q);
+  OASIS_REQUIRE(k);
+  OASIS_REQUIRE(v);
+  OASIS_REQUIRE(table);
+  OASIS_REQUIRE(table_count);
+  OASIS_REQUIRE(seq_lens);
+  OASIS_REQUIRE(out);
+  st = check_table_stride(d, table_stride);
+  if (st != OASIS_OK) return st;
+  if (!isfinite(scale)) return fail(OASIS_ERR_INVALID_ARG, "scale must be finite");
+  const size_t need = oasis::attn_workspace_bytes(d, table_stride);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(OASIS_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need,
+                ws == nullptr ? (size_t)0 : ws_bytes);
+  return hip_status(oasis::launch_attention(d, q, k, v, table, table_count, table_stride, seq_lens,
+                                            scale, out, lse, ws, stream),
+                    "sparse_decode_attn");
+}
+
+oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void* summ,
+                               const void* k, const void* v, const int32_t* seq_lens,
+                               float* scores, int32_t* topk, int32_t* resident, int32_t* plan,
+                               int32_t* plan_count, int32_t* table, int32_t* table_count,
+                               float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  OASIS_REQUIRE(q);
+  OASIS_REQUIRE(summ);
+  OASIS_REQUIRE(k);
+  OASIS_REQUIRE(v);
+  OASIS_REQUIRE(seq_lens);
+  OASIS_REQUIRE(scores);
+  OASIS_REQUIRE(topk);
+  OASIS_REQUIRE(resident);
+  if (d.cap > 0) OASIS_REQUIRE(plan);
+  OASIS_REQUIRE(plan_count);
+  OASIS_REQUIRE(table);
+  OASIS_REQUIRE(table_count);
+  OASIS_REQUIRE(out);
+  if (!isfinite(scale)) return fail(OASIS_ERR_INVALID_ARG, "scale must be finite");
+  const size_t need = oasis::attn_workspace_bytes(d, d.table_stride);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(OASIS_ERR_WORKSPACE, "decode step needs %zu workspace bytes, got %zu", need,
+                ws == nullptr ? (size_t)0 : ws_bytes);
+  st = hip_status(oasis::launch_score(d, q, summ, seq_lens, scores, stream), "decode_step/score");
+  if (st != OASIS_OK) return st;
+  st = hip_status(oasis::launch_topk_plan(d, scores, seq_lens, topk, resident, plan, plan_count,
+                                          table, table_count, stream),
+                  "decode_step/select");
+  if (st != OASIS_OK) return st;
+  return hip_status(oasis::launch_attention(d, q, k, v, table, table_count, d.table_stride, seq_lens,
+                                            scale, out, lse, ws, stream),
+                    "decode_step/attention");
+}
+
+}  // extern "C"

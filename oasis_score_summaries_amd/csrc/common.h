@@ -1,0 +1,97 @@
+// Internal helpers shared by the gfx950 kernels of liboasis (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oasis {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 16;
+constexpr int kMaxBlocks = 32768;   // NB limit (top-K keeps one register slice per thread)
+constexpr int kMaxTopK = 1024;
+constexpr int kMaxRows = 128;       // G * Q limit of the score kernel (8 row tiles of 16)
+constexpr int kMaxGroup = 16;       // query heads per KV head in the attention kernel
+constexpr int kMaxTableStride = 4096;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- sequence geometry (identical on host and device) ----------------------------
+__host__ __device__ inline int clamp_len(int len, int max_blocks) {
+  const int cap = max_blocks * kBlock;
+  return len < 0 ? 0 : (len > cap ? cap : len);
+}
+// Blocks that hold at least one token.
+__host__ __device__ inline int num_blocks(int len) { return (len + kBlock - 1) / kBlock; }
+// First block overlapping the last `window` tokens; earlier blocks are scoring candidates.
+__host__ __device__ inline int first_window_block(int len, int window) {
+  const int x = len - window;
+  return x > 0 ? x / kBlock : 0;
+}
+
+// ---- bf16 bit helpers -------------------------------------------------------------
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Keep the lanes of a packed bf16 pair whose sign bit is set (x < 0), zero the others.
+__device__ inline uint32_t bf16x2_neg_part(uint32_t w) {
+  const uint32_t lo = (w & 0x00008000u) ? (w & 0x0000ffffu) : 0u;
+  const uint32_t hi = (w & 0x80000000u) ? (w & 0xffff0000u) : 0u;
+  return lo | hi;
+}
+// Keep the lanes whose sign bit is clear (x >= 0), zero the others.
+__device__ inline uint32_t bf16x2_pos_part(uint32_t w) {
+  const uint32_t lo = (w & 0x00008000u) ? 0u : (w & 0x0000ffffu);
+  const uint32_t hi = (w & 0x80000000u) ? 0u : (w & 0xffff0000u);
+  return lo | hi;
+}
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Order-preserving map of a non-NaN fp32 value to uint32 (-0.0 maps like +0.0).
+__device__ inline uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---- wave64 / workgroup scans -----------------------------------------------------
+__device__ inline int wave_inclusive_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum over the threads of a workgroup (in thread order).
+// `scratch` needs blockDim.x / 64 + 1 ints of LDS.  Returns the prefix, stores
+// the total in *total.  Must be reached by every thread of the workgroup.
+__device__ inline int block_exclusive_scan(int x, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = (blockDim.x + 63) >> 6;
+  const int inc = wave_inclusive_scan(x);
+  if (lane == 63 || threadIdx.x == blockDim.x - 1) scratch[wave] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int t = scratch[w];
+      scratch[w] = run;
+      run += t;
+    }
+    scratch[nw] = run;
+  }
+  __syncthreads();
+  const int r = scratch[wave] + inc - x;
+  *total = scratch[nw];
+  __syncthreads();
+  return r;
+}
+
+}  // namespace oasis

@@ -1,0 +1,42 @@
+// Internal launcher interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oasis {
+
+// Validated problem sizes (see oasis_dims in include/oasis.h).
+struct Dims {
+  int batch, heads, group, max_blocks, queries, top_k, window, cap, table_stride;
+};
+
+// Attention split geometry: table entries handled by one workgroup, and the
+// workspace layout that the split kernel and the combine kernel share.
+struct AttnSplit {
+  int blocks_per_split;  // table entries per workgroup
+  int num_splits;        // ceil(table_stride / blocks_per_split)
+};
+AttnSplit attn_split(int table_stride);
+size_t attn_workspace_bytes(const Dims& d, int table_stride);
+
+hipError_t launch_build_summaries(const Dims& d, const void* k, const int32_t* seq_lens, void* summ,
+                                  hipStream_t stream);
+hipError_t launch_score(const Dims& d, const void* q, const void* summ, const int32_t* seq_lens,
+                        float* scores, hipStream_t stream);
+hipError_t launch_topk(const Dims& d, const float* scores, const int32_t* seq_lens, int32_t* topk,
+                       hipStream_t stream);
+hipError_t launch_plan(const Dims& d, const float* scores, const int32_t* topk,
+                       const int32_t* seq_lens, int32_t* resident, int32_t* plan,
+                       int32_t* plan_count, int32_t* table, int32_t* table_count,
+                       hipStream_t stream);
+hipError_t launch_topk_plan(const Dims& d, const float* scores, const int32_t* seq_lens,
+                            int32_t* topk, int32_t* resident, int32_t* plan, int32_t* plan_count,
+                            int32_t* table, int32_t* table_count, hipStream_t stream);
+hipError_t launch_attention(const Dims& d, const void* q, const void* k, const void* v,
+                            const int32_t* table, const int32_t* table_count, int table_stride,
+                            const int32_t* seq_lens, float scale, float* out, float* lse, void* ws,
+                            hipStream_t stream);
+
+}  // namespace oasis

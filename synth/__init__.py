@@ -214,33 +214,40 @@ def generate(w: Workload, device="cpu", layer: int = 0, with_kv: bool = True) ->
     return out
 
 
+def resident_for_head(w: Workload, selection_row, n_cand: int, b: int, h: int, layer: int = 0):
+    """Resident slot row for one (sequence, KV head) from its block selection.
+
+    The slots hold the selected blocks in ascending block order, empty slots
+    (-1) last.  For the "swap" recipe ``resident_swaps`` random members are then
+    replaced, slot for slot, by random candidate blocks outside the selection.
+    The random draws depend only on (b, h, layer), not on other heads.
+    """
+    sel = np.asarray(selection_row, dtype=np.int64)
+    K = sel.shape[0]
+    res = np.full(K, -1, dtype=np.int64)
+    s = np.sort(sel[sel >= 0])
+    res[: s.size] = s
+    n = min(w.resident_swaps, s.size) if w.resident == "swap" else 0
+    if n > 0:
+        outside = np.setdiff1d(np.arange(n_cand), s)
+        n = min(n, outside.size)
+        if n > 0:
+            rng = np.random.default_rng(_seed(w, "resident", layer, b, h))
+            slots = rng.choice(s.size, size=n, replace=False)
+            res[slots] = rng.choice(outside, size=n, replace=False)
+    return res
+
+
 def resident_from_selection(w: Workload, selection: torch.Tensor, lens: torch.Tensor,
                             layer: int = 0) -> torch.Tensor:
-    """Turn a per-head block selection into a resident slot table.
-
-    ``selection``: int [B, N_kv, K], -1 = pad.  The slots hold the selected
-    blocks in ascending block order (empty slots, -1, last).  For the "swap"
-    recipe ``resident_swaps`` random members are then replaced, slot for slot,
-    by random candidate blocks outside the selection.  Returns int32 on CPU.
-    """
+    """Resident slot tables [B, N_kv, K] (int32, CPU) from per-head selections."""
     sel = selection.detach().to("cpu", torch.int64).numpy()
     B, H, K = sel.shape
     res = np.full((B, H, K), -1, dtype=np.int64)
-    rng = np.random.default_rng(_seed(w, "resident", layer))
     for b in range(B):
         n_cand = first_window_block(int(lens[b]), w.window, w.block)
         for h in range(H):
-            s = np.sort(sel[b, h][sel[b, h] >= 0])
-            res[b, h, : s.size] = s
-            n = min(w.resident_swaps, s.size) if w.resident == "swap" else 0
-            if n == 0:
-                continue
-            outside = np.setdiff1d(np.arange(n_cand), s)
-            n = min(n, outside.size)
-            if n == 0:
-                continue
-            slots = rng.choice(s.size, size=n, replace=False)
-            res[b, h, slots] = rng.choice(outside, size=n, replace=False)
+            res[b, h] = resident_for_head(w, sel[b, h], n_cand, b, h, layer)
     return torch.from_numpy(res.astype(np.int32))
 
 

@@ -1,0 +1,137 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects bad arguments before anything is queued (no kernel runs here)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import oasis_score_summaries_amd as oa
+from oasis_score_summaries_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "oasis.h")
+
+INVALID_ARG, UNSUPPORTED, WORKSPACE = 1, 2, 3
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+# Calls with fake pointers run only where no GPU exists: should a check ever let
+# one through, the launch then fails in the runtime instead of touching memory.
+cpu_only = pytest.mark.skipif(torch.cuda.is_available(),
+                              reason="fake-pointer validation tests run on CPU-only hosts")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oasis_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return oa.load()
+
+
+def _dims(**kw):
+    base = dict(batch=2, num_kv_heads=2, group=4, max_blocks=64, num_queries=5, top_k=16,
+                window_tokens=64, fetch_ratio=0.05)
+    base.update(kw)
+    head_dim = base.pop("head_dim", 128)
+    block = base.pop("block_size", 16)
+    return oa.make_dims(**base, head_dim=head_dim, block_size=block)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) == 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.exported_symbols())
+
+
+def test_version_and_status_strings(lib):
+    text = open(HEADER).read()
+    assert lib.oasis_abi_version() == int(re.search(r"#define OASIS_ABI_VERSION (\d+)", text).group(1))
+    for code in range(5):
+        assert lib.oasis_status_string(code)
+    assert lib.oasis_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, UNSUPPORTED), ("block_size", 32, UNSUPPORTED), ("batch", 0, INVALID_ARG),
+    ("num_kv_heads", 0, INVALID_ARG), ("group", 0, INVALID_ARG), ("num_queries", 0, INVALID_ARG),
+    ("max_blocks", 0, INVALID_ARG), ("top_k", 0, INVALID_ARG), ("top_k", 65, INVALID_ARG),
+    ("window_tokens", -1, INVALID_ARG), ("fetch_ratio", -0.1, INVALID_ARG),
+    ("fetch_ratio", 1.5, INVALID_ARG), ("fetch_ratio", float("nan"), INVALID_ARG),
+    ("max_blocks", 40000, UNSUPPORTED), ("group", 17, UNSUPPORTED), ("num_queries", 40, UNSUPPORTED),
+])
+@cpu_only
+def test_dims_validation(lib, field, value, status):
+    d = _dims(**{field: value})
+    assert lib.oasis_fetch_cap(ctypes.byref(d)) == -1
+    assert lib.oasis_table_stride(ctypes.byref(d)) == -1
+    assert lib.oasis_workspace_bytes(ctypes.byref(d)) == 0
+    st = lib.oasis_score_summaries(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None)
+    assert st == status
+    assert lib.oasis_last_error()
+    st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == status
+
+
+@cpu_only
+def test_null_pointers_rejected(lib):
+    d = _dims()
+    args = [FAKE] * 4
+    for i in range(4):
+        a = list(args)
+        a[i] = None
+        assert lib.oasis_score_summaries(ctypes.byref(d), *a, None) == INVALID_ARG
+        assert b"NULL" in lib.oasis_last_error()
+    assert lib.oasis_score_summaries(None, FAKE, FAKE, FAKE, FAKE, None) == INVALID_ARG
+    assert lib.oasis_build_summaries(ctypes.byref(d), None, FAKE, FAKE, None) == INVALID_ARG
+    assert lib.oasis_topk_blocks(ctypes.byref(d), FAKE, FAKE, None, None) == INVALID_ARG
+    d4 = _dims(fetch_ratio=0.25)                                # cap 4: the plan is required
+    assert lib.oasis_fetch_cap(ctypes.byref(d4)) == 4
+    assert lib.oasis_build_plan(ctypes.byref(d4), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                None) == INVALID_ARG
+    d0 = _dims(fetch_ratio=0.01)                                # cap 0: plan may be NULL
+    assert lib.oasis_fetch_cap(ctypes.byref(d0)) == 0
+    assert lib.oasis_build_plan(ctypes.byref(d0), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                None) == INVALID_ARG          # plan_count is still required
+
+
+@cpu_only
+def test_workspace_and_table_stride_checks(lib):
+    d = _dims()
+    need = lib.oasis_workspace_bytes(ctypes.byref(d))
+    assert need > 0 and need % 256 == 0
+    T = lib.oasis_table_stride(ctypes.byref(d))
+    assert T == 16 + 4 + 1
+    assert lib.oasis_attn_workspace_bytes(ctypes.byref(d), T) == need
+    assert lib.oasis_attn_workspace_bytes(ctypes.byref(d), 0) == 0
+    st = lib.oasis_sparse_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, T, FAKE, 0.1,
+                                      FAKE, None, FAKE, need - 1, None)
+    assert st == WORKSPACE
+    st = lib.oasis_sparse_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 5000, FAKE, 0.1,
+                                      FAKE, None, FAKE, need, None)
+    assert st == INVALID_ARG
+    st = lib.oasis_sparse_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, T, FAKE,
+                                      float("inf"), FAKE, None, FAKE, need, None)
+    assert st == INVALID_ARG
+    st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, FAKE, FAKE, 0.1, FAKE, None, None, need, None)
+    assert st == WORKSPACE
+
+
+def test_fetch_cap_rounding(lib):
+    assert lib.oasis_fetch_cap(ctypes.byref(_dims(max_blocks=2048, top_k=128))) == 6
+    assert lib.oasis_fetch_cap(ctypes.byref(_dims(max_blocks=2048, top_k=100, fetch_ratio=0.29))) == 29
+    assert lib.oasis_fetch_cap(ctypes.byref(_dims(max_blocks=2048, top_k=128, fetch_ratio=1.0))) == 128
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    d = _dims()
+    with pytest.raises(ValueError):   # CPU tensors never reach the library
+        oa.topk_blocks(d, torch.zeros((2, 2, 64)), torch.zeros(2, dtype=torch.int32))

@@ -1,0 +1,365 @@
+"""GPU parity: every liboasis entry point against the fp64 oracle (tolerances in _helpers).
+
+All calls go through the C ABI (ctypes binding).  Inputs are seeded synthetic
+tensors; no expected value comes from the GPU.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ref
+from tests._helpers import (OUT_ATOL, check_scores, default_scale, f64, i64, oracle_head,
+                            oracle_selection_head, plan_robust, score_floor, selection_equivalent)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import oasis_score_summaries_amd as oa
+    oa.load()
+    return oa
+
+
+def _dims(oa, B, H, G, NB, Q, K, W, ratio):
+    return oa.make_dims(B, H, G, NB, Q, K, W, ratio)
+
+
+def _small_inputs(seed, B, H, G, Q, NB, lens, integer=False):
+    g = torch.Generator().manual_seed(seed)
+    if integer:
+        q = torch.randint(-3, 4, (B, H, G, Q, 128), generator=g).to(torch.bfloat16)
+        k = torch.randint(-4, 5, (B, H, NB, 16, 128), generator=g).to(torch.bfloat16)
+    else:
+        q = torch.randn((B, H, G, Q, 128), generator=g).to(torch.bfloat16)
+        k = torch.randn((B, H, NB, 16, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, NB, 16, 128), generator=g).to(torch.bfloat16)
+    return q, k, v, torch.tensor(lens, dtype=torch.int32)
+
+
+# ---------------------------------------------------------------------------
+# S0 summaries and S1 scores
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,H,G,Q,NB,lens", [
+    (1, 2, 4, 4, 256, [4096]),
+    (3, 2, 1, 1, 37, [592, 1, 300]),            # ragged tail, single-token sequence
+    (2, 1, 16, 8, 70, [1100, 17]),              # 128 query rows
+    (2, 3, 16, 5, 129, [2064, 2049]),           # 80 query rows, partial last tile
+])
+def test_summaries_and_scores(lib, B, H, G, Q, NB, lens):
+    _say(f"summaries+scores B={B} H={H} G={G} Q={Q} NB={NB} lens={lens}")
+    q, k, v, L = _small_inputs(11 + NB, B, H, G, Q, NB, lens)
+    W = 64
+    d = _dims(lib, B, H, G, NB, Q, min(8, NB), W, 0.05)
+    summ = lib.build_summaries(d, k.to(DEV), L.to(DEV))
+    scores = lib.score_summaries(d, q.to(DEV), summ, L.to(DEV))
+    torch.cuda.synchronize()
+    ref_summ = ref.build_summaries(f64(k), L.numpy())
+    np.testing.assert_array_equal(f64(summ), ref_summ)
+    ref_s = ref.score_blocks(f64(q), ref_summ, L.numpy(), W)
+    check_scores(f64(scores), ref_s, score_floor(f64(q), ref_summ), "scores")
+
+
+# ---------------------------------------------------------------------------
+# S2 top-K and S3 plan on given fp32 scores: decisions in the same precision, bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("NB,K,lens,distinct", [
+    (2048, 128, [32768, 32768 - 77, 900, 100], True),
+    (2048, 128, [32768, 5000], False),          # many exact ties
+    (8192, 128, [131072], True),
+    (32768, 1024, [524288, 300000], True),      # largest supported NB and K
+    (300, 1, [4800, 16], True),                 # K = 1; a sequence with no candidate
+    (40, 40, [640, 200], False),                # K = NB
+])
+def test_topk_on_given_scores(lib, NB, K, lens, distinct):
+    _say(f"topk NB={NB} K={K} lens={lens} distinct={distinct}")
+    B, H, W = len(lens), 3, 128
+    scores = synth.random_scores((B, H, NB), seed=NB + K, distinct=distinct)
+    L = torch.tensor(lens, dtype=torch.int32)
+    d = _dims(lib, B, H, 4, NB, 5, K, W, 0.05)
+    got = lib.topk_blocks(d, scores.to(DEV), L.to(DEV))
+    torch.cuda.synchronize()
+    expect = ref.topk_blocks(scores.numpy(), L.numpy(), K, W)
+    np.testing.assert_array_equal(i64(got), expect)
+
+
+@pytest.mark.parametrize("cap_ratio", [0.0, 1 / 128, 4 / 128, 0.05, 1.0])
+@pytest.mark.parametrize("distinct", [True, False])
+def test_plan_on_given_scores(lib, cap_ratio, distinct):
+    B, H, NB, K, W = 3, 4, 2048, 128, 128
+    lens = [32768, 20000 + 5, 3000]
+    _say(f"plan ratio={cap_ratio} distinct={distinct}")
+    scores = synth.random_scores((B, H, NB), seed=7, distinct=distinct)
+    L = torch.tensor(lens, dtype=torch.int32)
+    sel = ref.topk_blocks(scores.numpy(), L.numpy(), K, W)
+    res = torch.empty((B, H, K), dtype=torch.int32)
+    for b in range(B):
+        n_cand = ref.first_window_block(lens[b], W)
+        for h in range(H):
+            n_empty = [0, 5, K // 2, K][h]
+            r = synth.random_resident(K, n_cand, n_empty, seed=100 * b + h).numpy()
+            if h == 1:  # mostly the selection, a few strangers, five empty slots
+                rng = np.random.default_rng(b)
+                s = sel[b, h][sel[b, h] >= 0]
+                keep = s[: K - n_empty - 10]
+                others = rng.choice(np.setdiff1d(np.arange(n_cand), s), K - n_empty - keep.size,
+                                    replace=False)
+                r = np.concatenate([keep, others, -np.ones(n_empty, dtype=np.int64)])
+                rng.shuffle(r)
+            res[b, h] = torch.from_numpy(r.astype(np.int32))
+    d = _dims(lib, B, H, 4, NB, 5, K, W, cap_ratio)
+    cap = lib.fetch_cap(d)
+    assert cap == ref.fetch_cap(cap_ratio, K)
+    res_dev = res.to(DEV)
+    out = lib.build_plan(d, scores.to(DEV), torch.from_numpy(sel.astype(np.int32)).to(DEV), L.to(DEV), res_dev)
+    torch.cuda.synchronize()
+    expect = ref.build_plan(scores.numpy(), sel, res.numpy(), L.numpy(), cap, W)
+    for key in ("plan", "plan_count", "resident", "table", "table_count"):
+        np.testing.assert_array_equal(i64(out[key]), expect[key], err_msg=key)
+
+
+# ---------------------------------------------------------------------------
+# S4 attention on given tables
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G,lens,NB", [(4, [4096, 1000], 256), (1, [77], 5), (16, [2048, 33], 128),
+                                       (8, [513, 16], 40)])
+def test_attention_on_given_tables(lib, G, lens, NB):
+    _say(f"attention G={G} lens={lens} NB={NB}")
+    B, H, Q, K, W = len(lens), 2, 2, min(16, NB), 64
+    q, k, v, L = _small_inputs(5 + G, B, H, G, Q, NB, lens)
+    d = _dims(lib, B, H, G, NB, Q, K, W, 0.05)
+    T = lib.table_stride(d)
+    rng = np.random.default_rng(G)
+    table = np.full((B, H, T), -1, dtype=np.int64)
+    tc = np.zeros((B, H), dtype=np.int64)
+    for b in range(B):
+        nb = ref.num_blocks(lens[b])
+        for h in range(H):
+            n = [min(T, nb), min(3, nb), 0][(b + h) % 3] if (b, h) != (0, 0) else min(T, nb)
+            ids = rng.choice(nb, size=n, replace=False) if n else np.array([], dtype=np.int64)
+            if n and (b, h) == (0, 0) and nb - 1 not in ids:
+                ids[0] = nb - 1        # the partial last block
+            table[b, h, :n] = ids
+            tc[b, h] = n
+    scale = default_scale()
+    out, lse = lib.sparse_decode_attn(d, q.to(DEV), k.to(DEV), v.to(DEV),
+                                      torch.from_numpy(table.astype(np.int32)).to(DEV),
+                                      torch.from_numpy(tc.astype(np.int32)).to(DEV), L.to(DEV), scale)
+    torch.cuda.synchronize()
+    eo, el = ref.sparse_attention(f64(q), f64(k), f64(v), table, tc, L.numpy(), scale)
+    np.testing.assert_allclose(f64(out), eo, rtol=0, atol=OUT_ATOL)
+    fin = np.isfinite(el)
+    assert np.array_equal(np.isneginf(f64(lse)), ~fin)
+    np.testing.assert_allclose(f64(lse)[fin], el[fin], rtol=0, atol=OUT_ATOL)
+
+
+def test_attention_all_blocks_matches_dense(lib):
+    """Table = every block: the sparse path reduces to dense decode attention."""
+    B, H, G, Q, NB = 2, 2, 4, 1, 64
+    lens = [1024, 1000]
+    q, k, v, L = _small_inputs(3, B, H, G, Q, NB, lens)
+    d = _dims(lib, B, H, G, NB, Q, 8, 0, 0.05)
+    T = NB
+    table = torch.arange(NB, dtype=torch.int32).repeat(B, H, 1)
+    tc = torch.tensor([[ref.num_blocks(x)] * H for x in lens], dtype=torch.int32)
+    out, _ = lib.sparse_decode_attn(d, q.to(DEV), k.to(DEV), v.to(DEV), table.to(DEV), tc.to(DEV),
+                                    L.to(DEV), default_scale())
+    torch.cuda.synchronize()
+    for b in range(B):
+        kk = k[b].float().reshape(H, NB * 16, 128)[:, : lens[b]].double()
+        vv = v[b].float().reshape(H, NB * 16, 128)[:, : lens[b]].double()
+        qq = q[b, :, :, 0].double()
+        dense = torch.nn.functional.scaled_dot_product_attention(
+            qq[:, :, None], kk[:, None].expand(H, G, -1, -1), vv[:, None].expand(H, G, -1, -1),
+            scale=default_scale())[:, :, 0]
+        np.testing.assert_allclose(f64(out[b]), dense.numpy(), rtol=0, atol=OUT_ATOL)
+    assert T == NB
+
+
+# ---------------------------------------------------------------------------
+# The fused step
+# ---------------------------------------------------------------------------
+
+def _run_step(lib, w, inp_dev, resident_cpu):
+    d = lib.dims_for(w)
+    summ = lib.build_summaries(d, inp_dev["k"], inp_dev["seq_lens"])
+    res_dev = resident_cpu.to(DEV)
+    out = lib.decode_step(d, inp_dev["q"], summ, inp_dev["k"], inp_dev["v"], inp_dev["seq_lens"],
+                          res_dev, default_scale())
+    torch.cuda.synchronize()
+    return {key: val.detach().cpu() for key, val in out.items()}, summ
+
+
+def _compare_head(w, got, exp, b, h, exact_plan: bool):
+    floor = score_floor(exp["q64"][None, None], exp["summ"][None, None])[0, 0]
+    check_scores(f64(got["scores"][b, h]), exp["scores"], floor, f"scores b={b} h={h}")
+    gsel, esel = i64(got["topk"][b, h]), exp["topk"]
+    assert selection_equivalent(gsel, esel, exp["scores"]), f"selection b={b} h={h}"
+    if not exact_plan:
+        return False
+    for key in ("topk", "plan", "plan_count", "resident", "table", "table_count"):
+        np.testing.assert_array_equal(i64(got[key][b, h]), exp[key], err_msg=f"{key} b={b} h={h}")
+    np.testing.assert_allclose(f64(got["out"][b, h]), exp["out"], rtol=0, atol=OUT_ATOL)
+    fin = np.isfinite(exp["lse"])
+    np.testing.assert_allclose(f64(got["lse"][b, h])[fin], exp["lse"][fin], rtol=0, atol=OUT_ATOL)
+    return True
+
+
+def test_decode_step_tiny_workload(lib):
+    w = synth.WORKLOADS["tiny_4k"]
+    _say(f"decode_step {w.name}")
+    inp = synth.generate(w, "cpu")
+    lens = inp["seq_lens"]
+    sel = np.stack([np.stack([oracle_selection_head(inp["q"], inp["k"], lens, w.top_k, w.window, b, h)
+                              for h in range(w.num_kv_heads)]) for b in range(w.batch)])
+    resident = synth.resident_from_selection(w, torch.from_numpy(sel), lens)
+    got, _ = _run_step(lib, w, {k: v.to(DEV) for k, v in inp.items()}, resident)
+    for b in range(w.batch):
+        for h in range(w.num_kv_heads):
+            exp = oracle_head(inp["q"], inp["k"], inp["v"], lens, resident[b, h].numpy(), w.top_k,
+                              w.window, w.cap, default_scale(), b, h)
+            exp["q64"] = f64(inp["q"][b, h])
+            robust = plan_robust(exp["scores"], exp["topk"], resident[b, h].numpy(), w.cap,
+                                 ref.first_window_block(int(lens[b]), w.window))
+            assert robust
+            _compare_head(w, got, exp, b, h, exact_plan=True)
+
+
+@pytest.mark.parametrize("ratio,W,lens", [(0.05, 64, [4096, 1000, 70]), (0.25, 0, [4096, 1024, 16]),
+                                          (1.0, 128, [4000, 2222, 130])])
+def test_decode_step_integer_inputs(lib, ratio, W, lens):
+    """Small-integer q and k make every score exact in fp32 and fp64, so every
+    selection and plan decision (exact ties included) must agree bit for bit."""
+    _say(f"decode_step integer ratio={ratio} W={W} lens={lens}")
+    B, H, G, Q, NB, K = len(lens), 3, 4, 5, 256, 24
+    q, k, v, L = _small_inputs(21, B, H, G, Q, NB, lens, integer=True)
+    w = synth.Workload(name="int", batch=B, num_kv_heads=H, group=G, ctx=NB * 16, num_drafts=Q - 1,
+                       top_k=K, window=W, fetch_ratio=ratio, planted=0)
+    resident = torch.empty((B, H, K), dtype=torch.int32)
+    for b in range(B):
+        for h in range(H):
+            resident[b, h] = synth.random_resident(K, ref.first_window_block(lens[b], W), [0, 3, K][h], 50 * b + h)
+    inp_dev = {"q": q.to(DEV), "k": k.to(DEV), "v": v.to(DEV), "seq_lens": L.to(DEV)}
+    got, _ = _run_step(lib, w, inp_dev, resident)
+    for b in range(B):
+        for h in range(H):
+            exp = oracle_head(q, k, v, L, resident[b, h].numpy(), K, W, w.cap, default_scale(), b, h)
+            exp["q64"] = f64(q[b, h])
+            np.testing.assert_array_equal(f64(got["scores"][b, h]), exp["scores"])
+            _compare_head(w, got, exp, b, h, exact_plan=True)
+
+
+def test_decode_step_deterministic(lib):
+    w = synth.WORKLOADS["tiny_4k"].with_(batch=2, fetch_ratio=0.25)
+    inp = {k: v.to(DEV) for k, v in synth.generate(w, "cpu").items()}
+    resident = synth.random_resident(w.top_k, 200, 2, 9).repeat(w.batch, w.num_kv_heads, 1)
+    a, _ = _run_step(lib, w, inp, resident)
+    b, _ = _run_step(lib, w, inp, resident)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled heads, in the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+
+def _sample_heads(w, n=4):
+    heads = [(0, 0), (w.batch - 1, w.num_kv_heads - 1), (w.batch // 2, w.num_kv_heads // 2),
+             (min(1, w.batch - 1), w.num_kv_heads - 1)]
+    return list(dict.fromkeys(heads))[:n]
+
+
+def _full_size_case(lib, w, layer=0):
+    _say(f"full-size {w.name} layer={layer}: generating")
+    inp = synth.generate(w, DEV, layer=layer)
+    d = lib.dims_for(w)
+    summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
+    lens = inp["seq_lens"].cpu()
+    # Resident sets: the GPU's own selection for every head (as the benchmark builds
+    # them), then the oracle's for the sampled heads, which are the ones compared.
+    q_sel = inp["q_prev"] if w.resident == "prev" else inp["q"]
+    sc = lib.score_summaries(d, q_sel, summ, inp["seq_lens"])
+    sel = lib.topk_blocks(d, sc, inp["seq_lens"])
+    resident = synth.resident_from_selection(w, sel, lens, layer=layer)
+    heads = _sample_heads(w)
+    cpu = {}
+    for (b, h) in heads:
+        for key in ("q", "k", "v"):
+            cpu.setdefault(key, {})[(b, h)] = inp[key][b:b + 1, h:h + 1].cpu()
+        if w.resident == "prev":
+            cpu.setdefault("q_prev", {})[(b, h)] = inp["q_prev"][b:b + 1, h:h + 1].cpu()
+        qs = cpu["q_prev" if w.resident == "prev" else "q"][(b, h)]
+        osel = oracle_selection_head(qs, cpu["k"][(b, h)], lens[b:b + 1], w.top_k, w.window, 0, 0)
+        n_cand = ref.first_window_block(int(lens[b]), w.window)
+        resident[b, h] = torch.from_numpy(synth.resident_for_head(w, osel, n_cand, b, h, layer).astype(np.int32))
+    _say(f"full-size {w.name} layer={layer}: decode_step")
+    res_dev = resident.to(DEV)
+    out = lib.decode_step(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res_dev, default_scale())
+    torch.cuda.synchronize()
+    got = {key: val.detach().cpu() for key, val in out.items()}
+    # summaries of the sampled heads are checked bit-exactly too
+    n_exact = 0
+    for (b, h) in heads:
+        _say(f"full-size {w.name} layer={layer}: oracle b={b} h={h}")
+        exp = oracle_head(cpu["q"][(b, h)], cpu["k"][(b, h)], cpu["v"][(b, h)], lens[b:b + 1],
+                          resident[b, h].numpy(), w.top_k, w.window, w.cap, default_scale(), 0, 0)
+        np.testing.assert_array_equal(f64(summ[b, h]), exp["summ"])
+        exp["q64"] = f64(cpu["q"][(b, h)][0, 0])
+        robust = plan_robust(exp["scores"], exp["topk"], resident[b, h].numpy(), w.cap,
+                             ref.first_window_block(int(lens[b]), w.window))
+        n_exact += _compare_head(w, got, exp, b, h, exact_plan=robust)
+        # whatever the robustness, the GPU's own outputs must be self-consistent
+        tc = int(got["table_count"][b, h])
+        assert int(got["plan_count"][b, h]) <= w.cap
+        assert tc == int((got["resident"][b, h] >= 0).sum()) + ref.num_blocks(int(lens[b])) - \
+            ref.first_window_block(int(lens[b]), w.window)
+        assert torch.isfinite(got["out"][b, h]).all()
+    assert n_exact >= len(heads) - 1, f"only {n_exact} of {len(heads)} sampled heads were comparable"
+    del inp, summ, out
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_32k", "long_128k", "qwen3_235b_32k"])
+def test_full_size_workload(lib, name):
+    _full_size_case(lib, synth.WORKLOADS[name])
+
+
+@pytest.mark.parametrize("layer", [0, 35])
+def test_full_size_reasoning_layer(lib, layer):
+    _full_size_case(lib, synth.WORKLOADS["reasoning_36l"], layer=layer)
+
+
+# ---------------------------------------------------------------------------
+# Degenerate cases
+# ---------------------------------------------------------------------------
+
+def test_no_candidates_and_short_sequences(lib):
+    """len < W: nothing to score or select; the table is the window alone."""
+    B, H, G, Q, NB, K, W = 3, 2, 4, 2, 16, 4, 128
+    lens = [100, 1, 128]
+    q, k, v, L = _small_inputs(2, B, H, G, Q, NB, lens)
+    w = synth.Workload(name="short", batch=B, num_kv_heads=H, group=G, ctx=NB * 16, num_drafts=Q - 1,
+                       top_k=K, window=W, fetch_ratio=1.0, planted=0)
+    resident = torch.full((B, H, K), -1, dtype=torch.int32)
+    got, _ = _run_step(lib, w, {"q": q.to(DEV), "k": k.to(DEV), "v": v.to(DEV), "seq_lens": L.to(DEV)},
+                       resident)
+    assert torch.all(got["topk"] == -1) and torch.all(got["plan_count"] == 0)
+    for b in range(B):
+        for h in range(H):
+            exp = oracle_head(q, k, v, L, resident[b, h].numpy(), K, W, w.cap, default_scale(), b, h)
+            np.testing.assert_array_equal(i64(got["table"][b, h]), exp["table"])
+            np.testing.assert_allclose(f64(got["out"][b, h]), exp["out"], rtol=0, atol=OUT_ATOL)
