@@ -1,0 +1,254 @@
+#!/usr/bin/env python
+"""Throughput of one OasisKV look-ahead sparse-attention decode step of one layer on one MI355X.
+
+A step is the whole path on one batch: score every candidate block against the
+min/max key summaries, select the top-K blocks per KV head, build the capped
+transfer plan against the resident set, and run sparse attention over the
+updated head-wise table (oasis_decode_step).  Inputs are seeded synthetic
+tensors already resident in HBM.  Several independent input sets are rotated
+step to step so that the 256 MB last-level cache cannot serve a step from the
+previous one; each step reads its set's resident table and writes the update
+to a scratch table, so every step does the same work.
+
+Prints one JSON line.  Default workload: the Qwen3-8B attention-layer shape at
+32K context (batch 8, 8 KV heads x group 4, K = 128, 128-token window, fetch
+ratio 0.05, 1 target + 4 drafts per query head).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode steps/s per layer + achieved HBM GB/s (% peak), Qwen3-8B 32K"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
+BLOCK_KV_BYTES = 16 * 128 * 2 * 2   # K and V of one 16-token block of one KV head, bf16
+SUMMARY_BYTES = 2 * 128 * 2         # min and max of one block, bf16
+
+
+def kv_cache_bytes(batch: int, ctx: int, layers: int, kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """KV capacity M_KV(B, L) = B * L * N_layer * 2 * N_kv * d_h * s (xllm-io review, Eq. (1))."""
+    return batch * ctx * layers * 2 * kv_heads * head_dim * elem_bytes
+
+
+def algorithmic_bytes(w, lens, table_count) -> dict:
+    """Bytes one step must move: candidate summaries, the K/V blocks of every table entry,
+    the queries and the output.  Per kernel as well (inputs plus outputs)."""
+    import synth
+    H, G, Q = w.num_kv_heads, w.group, w.queries
+    cand = sum(synth.first_window_block(int(x), w.window) for x in lens) * H
+    blocks = int(table_count.sum())
+    q_all = w.batch * H * G * Q * 128 * 2
+    q_target = w.batch * H * G * 128 * 2
+    out = w.batch * H * G * (128 + 1) * 4
+    scores = w.batch * H * w.max_blocks * 4
+    step = cand * SUMMARY_BYTES + blocks * BLOCK_KV_BYTES + q_all + out
+    return {
+        "step": step,
+        "score": cand * SUMMARY_BYTES + q_all + scores,
+        "attn_split": blocks * BLOCK_KV_BYTES + q_target,
+        "summaries": cand * SUMMARY_BYTES,
+        "kv": blocks * BLOCK_KV_BYTES,
+        "units": {"candidate_block_heads": cand, "table_blocks": blocks},
+    }
+
+
+def cpu_baseline(w, sets, budget_s: float) -> dict:
+    """The fp64 oracle on the host: the same step (score, top-K, plan, attention) for
+    (sequence, KV head) units of input set 0, until ``budget_s`` seconds have run."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import ref
+
+    s0 = sets[0]
+    lens = s0["seq_lens"].cpu()
+    res = s0["resident"].cpu()
+    units = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    f64 = lambda t: t.to(torch.float64).numpy()
+    done, elapsed = 0, 0.0
+    scale = 1.0 / math.sqrt(128)
+    with threadpool_limits(1):
+        for (b, h) in units:
+            qh = f64(s0["q"][b:b + 1, h:h + 1].cpu())
+            kh = f64(s0["k"][b:b + 1, h:h + 1].cpu())
+            vh = f64(s0["v"][b:b + 1, h:h + 1].cpu())
+            sh = f64(s0["summ"][b:b + 1, h:h + 1].cpu())
+            L = lens[b:b + 1].numpy()
+            t = time.perf_counter()
+            ref.decode_step(qh, sh, kh, vh, L, res[b:b + 1, h:h + 1].numpy().astype(np.int64),
+                            w.top_k, w.window, w.cap, scale)
+            elapsed += time.perf_counter() - t
+            done += 1
+            if elapsed >= budget_s:
+                break
+    per_step = elapsed / done * len(units)
+    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(units)} (sequence, KV head) units of one step, fp64 numpy, "
+                      f"{elapsed:.1f} s, scaled to a whole step",
+            "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="qwen3_8b_32k")
+    ap.add_argument("--sets", type=int, default=6, help="independent input sets rotated per step")
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--stage-steps", type=int, default=300, help="evented steps for per-kernel times")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the decode step of one layer is measured on a single "
+              "MI355X and no multi-GPU path is built", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import oasis_score_summaries_amd as oa
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    d = oa.dims_for(w)
+    n_sets = w.layers if w.layers > 1 else args.sets
+
+    # ---- set-up (untimed): inputs, summaries, resident sets ------------------------
+    t_setup = time.perf_counter()
+    sets = []
+    for i in range(n_sets):
+        inp = synth.generate(w, dev, layer=i)
+        summ = oa.build_summaries(d, inp["k"], inp["seq_lens"])
+        q_sel = inp["q_prev"] if w.resident == "prev" else inp["q"]
+        sel = oa.topk_blocks(d, oa.score_summaries(d, q_sel, summ, inp["seq_lens"]), inp["seq_lens"])
+        resident = synth.resident_from_selection(w, sel, inp["seq_lens"].cpu(), layer=i).to(dev)
+        sets.append({"q": inp["q"], "k": inp["k"], "v": inp["v"], "seq_lens": inp["seq_lens"],
+                     "summ": summ, "resident": resident})
+        del inp, q_sel, sel
+    buffers = oa.StepBuffers(d, dev)
+    res_next = torch.empty_like(sets[0]["resident"])
+    steps = [oa.PreparedStep(d, s["q"], s["summ"], s["k"], s["v"], s["seq_lens"], s["resident"],
+                             buffers, resident_next=res_next) for s in sets]
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    # ---- warm-up, then the timed region ---------------------------------------------
+    for i in range(args.warmup):
+        steps[i % n_sets]()
+    torch.cuda.synchronize()
+    graph = None
+    if args.mode == "graph":
+        # One graph holds one step per input set; replaying it walks the rotation.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            steps[0]()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for st in steps:
+                st()
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup // n_sets)):
+            graph.replay()
+        torch.cuda.synchronize()
+    reps = max(1, args.steps // n_sets) if graph is not None else None
+    n_timed = reps * n_sets if graph is not None else args.steps
+
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    if graph is not None:
+        for _ in range(reps):
+            graph.replay()
+    else:
+        for i in range(n_timed):
+            steps[i % n_sets]()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / n_timed
+
+    # The graph's last step ran set n_sets-1; an eager run of it must give the same bits.
+    check = {}
+    if graph is not None:
+        out_graph = buffers.out.clone()
+        steps[-1]()
+        torch.cuda.synchronize()
+        check["graph_matches_eager"] = bool(torch.equal(out_graph, buffers.out))
+
+    # ---- per-kernel times: evented steps (HIP events on the launch stream) ---------------
+    stage = {k: [] for k in oa.StageEvents.STAGES}
+    evs = oa.StageEvents()
+    for i in range(args.stage_steps):
+        steps[i % n_sets](events=evs)
+        for k, v in evs.elapsed_ms().items():
+            stage[k].append(v)
+    stage_us = {k: 1e3 * statistics.mean(v) for k, v in stage.items()}
+
+    # ---- bytes and roofline ------------------------------------------------------------------
+    torch.cuda.synchronize()
+    nb = {}
+    for s in sets[:1]:
+        steps[0]()
+        torch.cuda.synchronize()
+        nb = algorithmic_bytes(w, s["seq_lens"].cpu(), buffers.table_count.cpu())
+    step_gbps = nb["step"] / (ms_per_step * 1e-3) / 1e9
+    dominant = max(("score", "attn_split"), key=lambda k: stage_us[k])
+    dom_gbps = nb[dominant] / (stage_us[dominant] * 1e-6) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_per_step, 2),   # one step = one layer
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": n_timed,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.num_kv_heads, "group": w.group,
+                   "context": w.ctx, "queries_per_head": w.queries, "top_k": w.top_k,
+                   "window_tokens": w.window, "fetch_ratio": w.fetch_ratio, "cap": w.cap,
+                   "input_sets": n_sets, "mode": args.mode},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": nb[dominant],
+                     "avg_launch_us": round(stage_us[dominant], 3)},
+        "step_hbm": {"achieved": round(step_gbps, 1), "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+                     "bytes_per_step": nb["step"], "units": nb["units"]},
+        "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "wall_s": round(wall_s, 3),
+        "setup_s": round(setup_s, 1),
+        "checks": check,
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(w, sets, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -202,15 +202,34 @@ oasis_status oasis_sparse_decode_attn(const oasis_dims* dims, const void* q, con
                                       const int32_t* seq_lens, float scale, float* out, float* lse,
                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* The whole step on one stream: oasis_score_summaries, oasis_topk_blocks,
- * oasis_build_plan, then oasis_sparse_decode_attn over the updated table
- * (table_stride = oasis_table_stride(dims)).  Arguments as above. */
+/* The whole step on one stream: oasis_score_summaries, then the selection and
+ * the plan (one kernel doing oasis_topk_blocks and oasis_build_plan), then
+ * oasis_sparse_decode_attn over the updated table (table_stride =
+ * oasis_table_stride(dims)).  Arguments as above, except:
+ *   resident_next  device, int32 [B, H, K] or NULL.  NULL: `resident` is
+ *                  updated in place.  Otherwise `resident` is only read and the
+ *                  updated slot table is written here (a double-buffered slot
+ *                  table: step t reads one buffer and writes the other); the
+ *                  two buffers must not overlap. */
 oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void* summ,
                                const void* k, const void* v, const int32_t* seq_lens,
-                               float* scores, int32_t* topk, int32_t* resident, int32_t* plan,
-                               int32_t* plan_count, int32_t* table, int32_t* table_count,
-                               float scale, float* out, float* lse, void* ws, size_t ws_bytes,
-                               hipStream_t stream);
+                               float* scores, int32_t* topk, int32_t* resident,
+                               int32_t* resident_next, int32_t* plan, int32_t* plan_count,
+                               int32_t* table, int32_t* table_count, float scale, float* out,
+                               float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* oasis_decode_step with timing markers, for measurement: events[0..4]
+ * (created by the caller with hipEventCreate) are recorded on `stream` before
+ * the scoring kernel, after it, after the selection-and-plan kernel, after the
+ * attention split kernel and after the attention merge kernel.  The kernels
+ * queued are the same as oasis_decode_step's. */
+oasis_status oasis_decode_step_timed(const oasis_dims* dims, const void* q, const void* summ,
+                                     const void* k, const void* v, const int32_t* seq_lens,
+                                     float* scores, int32_t* topk, int32_t* resident,
+                                     int32_t* resident_next, int32_t* plan, int32_t* plan_count,
+                                     int32_t* table, int32_t* table_count, float scale, float* out,
+                                     float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
+                                     hipEvent_t* events);
 
 #ifdef __cplusplus
 }

@@ -6,7 +6,8 @@ attention over the head-wise block table.  The work runs in the HIP kernels of
 liboasis.so (C ABI in include/oasis.h); this package is its Python binding.
 Every call raises if the library has not been built.
 """
-from ._lib import (LIB_PATH, OasisDims, OasisError, StepBuffers, build_plan,  # noqa: F401
+from ._lib import (LIB_PATH, OasisDims, OasisError, PreparedStep, StageEvents,  # noqa: F401
+                   StepBuffers, build_plan,
                    build_summaries, decode_step, dims_for, exported_symbols, fetch_cap, load,
                    make_dims, score_summaries, sparse_decode_attn, table_stride, topk_blocks,
                    workspace_bytes)

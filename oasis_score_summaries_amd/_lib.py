@@ -63,8 +63,11 @@ _SIGNATURES = {
     "oasis_build_plan": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "oasis_sparse_decode_attn": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
                                                 ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
-    "oasis_decode_step": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+    "oasis_decode_step": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P]),
+    "oasis_decode_step_timed": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                               _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P,
+                                               ctypes.POINTER(ctypes.c_void_p)]),
 }
 
 _lib = None
@@ -303,8 +306,9 @@ class StepBuffers:
 def decode_step(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor, k: torch.Tensor,
                 v: torch.Tensor, seq_lens: torch.Tensor, resident: torch.Tensor,
                 scale: Optional[float] = None, buffers: Optional[StepBuffers] = None,
-                stream=None) -> Dict[str, torch.Tensor]:
-    """score -> top-K -> capped plan (``resident`` updated in place) -> attention."""
+                resident_next: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """score -> top-K -> capped plan -> attention.  The updated resident set goes to
+    ``resident_next`` if given (``resident`` is then only read), else in place."""
     s = _shapes(dims)
     _need(q, "q", torch.bfloat16, s["q"], align=16)
     dev = q.device
@@ -313,6 +317,8 @@ def decode_step(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor, k: torch.T
     _need(v, "v", torch.bfloat16, s["kv"], dev, align=16)
     _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
     _need(resident, "resident", torch.int32, s["resident"], dev)
+    if resident_next is not None:
+        _need(resident_next, "resident_next", torch.int32, s["resident"], dev)
     if buffers is None:
         buffers = StepBuffers(dims, dev)
     b = buffers
@@ -320,9 +326,115 @@ def decode_step(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor, k: torch.T
         scale = 1.0 / math.sqrt(128)
     _check(load().oasis_decode_step(
         ctypes.byref(dims), _ptr(q), _ptr(summ), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(b.scores),
-        _ptr(b.topk), _ptr(resident), _ptr(b.plan if b.plan.numel() else None), _ptr(b.plan_count),
+        _ptr(b.topk), _ptr(resident), _ptr(resident_next),
+        _ptr(b.plan if b.plan.numel() else None), _ptr(b.plan_count),
         _ptr(b.table), _ptr(b.table_count), float(scale), _ptr(b.out), _ptr(b.lse), _ptr(b.ws),
         b.ws.numel(), _stream(stream)), "oasis_decode_step")
     res = b.as_dict()
-    res["resident"] = resident
+    res["resident"] = resident if resident_next is None else resident_next
     return res
+
+
+# ---------------------------------------------------------------------------
+# Repeated steps: arguments marshalled once, HIP events for stage timing
+# ---------------------------------------------------------------------------
+
+_hip = None
+
+
+def _hip_runtime() -> ctypes.CDLL:
+    global _hip
+    if _hip is None:
+        h = ctypes.CDLL("libamdhip64.so")
+        h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        h.hipEventCreate.restype = ctypes.c_int
+        h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h.hipEventDestroy.restype = ctypes.c_int
+        h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        h.hipEventSynchronize.restype = ctypes.c_int
+        h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        h.hipEventElapsedTime.restype = ctypes.c_int
+        _hip = h
+    return _hip
+
+
+class StageEvents:
+    """Five HIP events bracketing the kernels of one fused step (see oasis_decode_step_timed)."""
+
+    STAGES = ("score", "select_plan", "attn_split", "attn_merge")
+
+    def __init__(self):
+        h = _hip_runtime()
+        self.handles = (ctypes.c_void_p * 5)()
+        for i in range(5):
+            ev = ctypes.c_void_p()
+            if h.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles[i] = ev.value
+
+    def elapsed_ms(self) -> Dict[str, float]:
+        h = _hip_runtime()
+        if h.hipEventSynchronize(self.handles[4]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        out = {}
+        for i, name in enumerate(self.STAGES):
+            ms = ctypes.c_float()
+            if h.hipEventElapsedTime(ctypes.byref(ms), self.handles[i], self.handles[i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out[name] = float(ms.value)
+        return out
+
+    def __del__(self):
+        try:
+            h = _hip_runtime()
+            for i in range(5):
+                if self.handles[i]:
+                    h.hipEventDestroy(self.handles[i])
+        except Exception:
+            pass
+
+
+class PreparedStep:
+    """One fused decode step whose arguments are checked and marshalled once.
+
+    Calling it queues oasis_decode_step on the current stream (or, with
+    ``events``, oasis_decode_step_timed).  The tensors must stay alive and keep
+    their storage while the object is used.
+    """
+
+    def __init__(self, dims: OasisDims, q, summ, k, v, seq_lens, resident, buffers: StepBuffers,
+                 resident_next=None, scale: Optional[float] = None):
+        s = _shapes(dims)
+        _need(q, "q", torch.bfloat16, s["q"], align=16)
+        dev = q.device
+        _need(summ, "summ", torch.bfloat16, s["summ"], dev, align=16)
+        _need(k, "k", torch.bfloat16, s["kv"], dev, align=16)
+        _need(v, "v", torch.bfloat16, s["kv"], dev, align=16)
+        _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+        _need(resident, "resident", torch.int32, s["resident"], dev)
+        if resident_next is not None:
+            _need(resident_next, "resident_next", torch.int32, s["resident"], dev)
+        b = buffers
+        for name, t in b.as_dict().items():
+            if t.device != dev:
+                raise ValueError(f"buffer {name} is on {t.device}, expected {dev}")
+        if b.ws.numel() < workspace_bytes(dims):
+            raise ValueError("workspace too small")
+        self.dims = dims
+        self.buffers = b
+        self.keep = (q, summ, k, v, seq_lens, resident, resident_next)
+        scale = 1.0 / math.sqrt(128) if scale is None else float(scale)
+        self.args = [ctypes.byref(dims), _ptr(q), _ptr(summ), _ptr(k), _ptr(v), _ptr(seq_lens),
+                     _ptr(b.scores), _ptr(b.topk), _ptr(resident), _ptr(resident_next),
+                     _ptr(b.plan if b.plan.numel() else None), _ptr(b.plan_count), _ptr(b.table),
+                     _ptr(b.table_count), ctypes.c_float(scale), _ptr(b.out), _ptr(b.lse), _ptr(b.ws),
+                     ctypes.c_size_t(b.ws.numel())]
+        self.lib = load()
+
+    def __call__(self, stream=None, events: Optional[StageEvents] = None) -> None:
+        st = _stream(stream)
+        if events is None:
+            _check(self.lib.oasis_decode_step(*self.args, st), "oasis_decode_step")
+        else:
+            _check(self.lib.oasis_decode_step_timed(*self.args, st, events.handles),
+                   "oasis_decode_step_timed")

@@ -203,12 +203,14 @@ oasis_status oasis_sparse_decode_attn(const oasis_dims* dims, const void* q, con
                     "sparse_decode_attn");
 }
 
-oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void* summ,
-                               const void* k, const void* v, const int32_t* seq_lens,
-                               float* scores, int32_t* topk, int32_t* resident, int32_t* plan,
-                               int32_t* plan_count, int32_t* table, int32_t* table_count,
-                               float scale, float* out, float* lse, void* ws, size_t ws_bytes,
-                               hipStream_t stream) {
+// The fused step; with `events` non-NULL, markers are recorded between its kernels.
+static oasis_status decode_step_impl(const oasis_dims* dims, const void* q, const void* summ,
+                                     const void* k, const void* v, const int32_t* seq_lens,
+                                     float* scores, int32_t* topk, int32_t* resident,
+                                     int32_t* resident_next, int32_t* plan, int32_t* plan_count,
+                                     int32_t* table, int32_t* table_count, float scale, float* out,
+                                     float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
+                                     hipEvent_t* events) {
   oasis::Dims d;
   oasis_status st = check_dims(dims, &d);
   if (st != OASIS_OK) return st;
@@ -230,15 +232,59 @@ oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void
   if (ws == nullptr || ws_bytes < need)
     return fail(OASIS_ERR_WORKSPACE, "decode step needs %zu workspace bytes, got %zu", need,
                 ws == nullptr ? (size_t)0 : ws_bytes);
+  if (resident_next != nullptr && resident_next != resident) {
+    const size_t n = (size_t)d.batch * d.heads * d.top_k;
+    if (resident_next < resident + n && resident < resident_next + n)
+      return fail(OASIS_ERR_INVALID_ARG, "resident and resident_next overlap");
+  } else {
+    resident_next = resident;
+  }
+  if (events != nullptr) {
+    for (int i = 0; i < 5; ++i) OASIS_REQUIRE(events[i]);
+  }
+  auto mark = [&](int i) -> oasis_status {
+    if (events == nullptr) return OASIS_OK;
+    return hip_status(hipEventRecord(events[i], stream), "decode_step/event");
+  };
+  if ((st = mark(0)) != OASIS_OK) return st;
   st = hip_status(oasis::launch_score(d, q, summ, seq_lens, scores, stream), "decode_step/score");
-  if (st != OASIS_OK) return st;
-  st = hip_status(oasis::launch_topk_plan(d, scores, seq_lens, topk, resident, plan, plan_count,
-                                          table, table_count, stream),
+  if (st != OASIS_OK || (st = mark(1)) != OASIS_OK) return st;
+  st = hip_status(oasis::launch_topk_plan(d, scores, seq_lens, topk, resident, resident_next, plan,
+                                          plan_count, table, table_count, stream),
                   "decode_step/select");
+  if (st != OASIS_OK || (st = mark(2)) != OASIS_OK) return st;
+  st = hip_status(oasis::launch_attention_split(d, q, k, v, table, table_count, d.table_stride,
+                                                seq_lens, scale, ws, stream),
+                  "decode_step/attention");
+  if (st != OASIS_OK || (st = mark(3)) != OASIS_OK) return st;
+  st = hip_status(oasis::launch_attention_merge(d, table_count, d.table_stride, out, lse, ws, stream),
+                  "decode_step/attention-merge");
   if (st != OASIS_OK) return st;
-  return hip_status(oasis::launch_attention(d, q, k, v, table, table_count, d.table_stride, seq_lens,
-                                            scale, out, lse, ws, stream),
-                    "decode_step/attention");
+  return mark(4);
+}
+
+oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void* summ,
+                               const void* k, const void* v, const int32_t* seq_lens,
+                               float* scores, int32_t* topk, int32_t* resident,
+                               int32_t* resident_next, int32_t* plan, int32_t* plan_count,
+                               int32_t* table, int32_t* table_count, float scale, float* out,
+                               float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_step_impl(dims, q, summ, k, v, seq_lens, scores, topk, resident, resident_next, plan,
+                          plan_count, table, table_count, scale, out, lse, ws, ws_bytes, stream,
+                          nullptr);
+}
+
+oasis_status oasis_decode_step_timed(const oasis_dims* dims, const void* q, const void* summ,
+                                     const void* k, const void* v, const int32_t* seq_lens,
+                                     float* scores, int32_t* topk, int32_t* resident,
+                                     int32_t* resident_next, int32_t* plan, int32_t* plan_count,
+                                     int32_t* table, int32_t* table_count, float scale, float* out,
+                                     float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
+                                     hipEvent_t* events) {
+  if (events == nullptr) return fail(OASIS_ERR_INVALID_ARG, "events is NULL");
+  return decode_step_impl(dims, q, summ, k, v, seq_lens, scores, topk, resident, resident_next, plan,
+                          plan_count, table, table_count, scale, out, lse, ws, ws_bytes, stream,
+                          events);
 }
 
 }  // extern "C"

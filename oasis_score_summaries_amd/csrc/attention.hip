@@ -208,10 +208,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   }
 }
 
-hipError_t launch_attention(const Dims& d, const void* q, const void* k, const void* v,
-                            const int32_t* table, const int32_t* table_count, int table_stride,
-                            const int32_t* seq_lens, float scale, float* out, float* lse, void* ws,
-                            hipStream_t stream) {
+hipError_t launch_attention_split(const Dims& d, const void* q, const void* k, const void* v,
+                                  const int32_t* table, const int32_t* table_count,
+                                  int table_stride, const int32_t* seq_lens, float scale, void* ws,
+                                  hipStream_t stream) {
   const AttnSplit s = attn_split(table_stride);
   const size_t parts = (size_t)d.batch * d.heads * s.num_splits * d.group;
   float* part_o = (float*)ws;
@@ -219,11 +219,28 @@ hipError_t launch_attention(const Dims& d, const void* q, const void* k, const v
   attn_split_kernel<<<dim3(s.num_splits, d.batch * d.heads), dim3(64 * kAttnWaves), 0, stream>>>(
       (const u32x4*)q, (const u32x4*)k, (const u32x4*)v, table, table_count, table_stride, seq_lens,
       scale * kLog2e, part_o, part_ml, d.heads, d.group, d.queries, d.max_blocks, s.num_splits);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_merge(const Dims& d, const int32_t* table_count, int table_stride,
+                                  float* out, float* lse, const void* ws, hipStream_t stream) {
+  const AttnSplit s = attn_split(table_stride);
+  const size_t parts = (size_t)d.batch * d.heads * s.num_splits * d.group;
+  const float* part_o = (const float*)ws;
+  const float* part_ml = part_o + parts * kHeadDim;
   attn_merge_kernel<<<dim3(d.batch * d.heads), dim3(256), 0, stream>>>(
       part_o, part_ml, table_count, table_stride, d.group, s.num_splits, s.blocks_per_split, out, lse);
   return hipGetLastError();
+}
+
+hipError_t launch_attention(const Dims& d, const void* q, const void* k, const void* v,
+                            const int32_t* table, const int32_t* table_count, int table_stride,
+                            const int32_t* seq_lens, float scale, float* out, float* lse, void* ws,
+                            hipStream_t stream) {
+  hipError_t err = launch_attention_split(d, q, k, v, table, table_count, table_stride, seq_lens,
+                                          scale, ws, stream);
+  if (err != hipSuccess) return err;
+  return launch_attention_merge(d, table_count, table_stride, out, lse, ws, stream);
 }
 
 }  // namespace oasis

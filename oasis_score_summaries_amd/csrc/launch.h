@@ -32,8 +32,15 @@ hipError_t launch_plan(const Dims& d, const float* scores, const int32_t* topk,
                        int32_t* plan_count, int32_t* table, int32_t* table_count,
                        hipStream_t stream);
 hipError_t launch_topk_plan(const Dims& d, const float* scores, const int32_t* seq_lens,
-                            int32_t* topk, int32_t* resident, int32_t* plan, int32_t* plan_count,
-                            int32_t* table, int32_t* table_count, hipStream_t stream);
+                            int32_t* topk, const int32_t* resident, int32_t* resident_next,
+                            int32_t* plan, int32_t* plan_count, int32_t* table,
+                            int32_t* table_count, hipStream_t stream);
+hipError_t launch_attention_split(const Dims& d, const void* q, const void* k, const void* v,
+                                  const int32_t* table, const int32_t* table_count,
+                                  int table_stride, const int32_t* seq_lens, float scale, void* ws,
+                                  hipStream_t stream);
+hipError_t launch_attention_merge(const Dims& d, const int32_t* table_count, int table_stride,
+                                  float* out, float* lse, const void* ws, hipStream_t stream);
 hipError_t launch_attention(const Dims& d, const void* q, const void* k, const void* v,
                             const int32_t* table, const int32_t* table_count, int table_stride,
                             const int32_t* seq_lens, float scale, float* out, float* lse, void* ws,

@@ -148,10 +148,10 @@ __device__ int topk_select(const float* __restrict__ row, int n_cand, int K, Top
 // Applies the capped-eviction rule for one (sequence, KV head).  `sel` holds the
 // K selection entries (-1 = none), best first.  Every thread must call it, with
 // blockDim.x >= K.
-__device__ void plan_apply(const float* __restrict__ srow, const int* sel, int32_t* res,
-                           int32_t* plan_row, int32_t* plan_count, int32_t* table_row,
-                           int32_t* table_count, int K, int C, int NB, int w0, int nblk, int T,
-                           PlanShared& sh) {
+__device__ void plan_apply(const float* __restrict__ srow, const int* sel, const int32_t* res,
+                           int32_t* res_next, int32_t* plan_row, int32_t* plan_count,
+                           int32_t* table_row, int32_t* table_count, int K, int C, int NB, int w0,
+                           int nblk, int T, PlanShared& sh) {
   const int tid = threadIdx.x;
   const int nwords = (NB + 31) >> 5;
   for (int w = tid; w < nwords; w += blockDim.x) {
@@ -220,8 +220,10 @@ __device__ void plan_apply(const float* __restrict__ srow, const int* sel, int32
     plan_row[3 * pos_vict + 0] = tid;
     plan_row[3 * pos_vict + 1] = new_r;
     plan_row[3 * pos_vict + 2] = r_i;
-    res[tid] = new_r;
   }
+  // Every slot is written so that res_next may be a different buffer; when it
+  // is `res` itself, each thread rewrites only the slot it read above.
+  if (tid < K) res_next[tid] = new_r;
   for (int r = n_placed + tid; r < C; r += blockDim.x) {
     plan_row[3 * r + 0] = -1;
     plan_row[3 * r + 1] = -1;
@@ -261,15 +263,16 @@ __global__ __launch_bounds__(kSelectThreads) void plan_kernel(
   const int bh = blockIdx.x;
   const int len = clamp_len(seq_lens[bh / heads], NB);
   plan_apply(scores + (size_t)bh * NB, topk + (size_t)bh * K, resident + (size_t)bh * K,
-             plan + (size_t)bh * C * 3, plan_count + bh, table + (size_t)bh * T, table_count + bh,
-             K, C, NB, first_window_block(len, window), num_blocks(len), T, sh);
+             resident + (size_t)bh * K, plan + (size_t)bh * C * 3, plan_count + bh,
+             table + (size_t)bh * T, table_count + bh, K, C, NB, first_window_block(len, window),
+             num_blocks(len), T, sh);
 }
 
 template <int ITEMS>
 __global__ __launch_bounds__(kSelectThreads) void topk_plan_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int32_t* topk,
-    int32_t* resident, int32_t* plan, int32_t* plan_count, int32_t* table, int32_t* table_count,
-    int heads, int NB, int K, int C, int window, int T) {
+    const int32_t* resident, int32_t* resident_next, int32_t* plan, int32_t* plan_count,
+    int32_t* table, int32_t* table_count, int heads, int NB, int K, int C, int window, int T) {
   __shared__ TopkShared tsh;
   __shared__ PlanShared psh;
   const int bh = blockIdx.x;
@@ -283,9 +286,9 @@ __global__ __launch_bounds__(kSelectThreads) void topk_plan_kernel(
     topk[(size_t)bh * K + t] = v;
   }
   __syncthreads();
-  plan_apply(srow, tsh.sorted_idx, resident + (size_t)bh * K, plan + (size_t)bh * C * 3,
-             plan_count + bh, table + (size_t)bh * T, table_count + bh, K, C, NB, n_cand,
-             num_blocks(len), T, psh);
+  plan_apply(srow, tsh.sorted_idx, resident + (size_t)bh * K, resident_next + (size_t)bh * K,
+             plan + (size_t)bh * C * 3, plan_count + bh, table + (size_t)bh * T, table_count + bh,
+             K, C, NB, n_cand, num_blocks(len), T, psh);
 }
 
 static int items_for(int NB) {
@@ -328,16 +331,17 @@ hipError_t launch_plan(const Dims& d, const float* scores, const int32_t* topk,
 }
 
 hipError_t launch_topk_plan(const Dims& d, const float* scores, const int32_t* seq_lens,
-                            int32_t* topk, int32_t* resident, int32_t* plan, int32_t* plan_count,
-                            int32_t* table, int32_t* table_count, hipStream_t stream) {
+                            int32_t* topk, const int32_t* resident, int32_t* resident_next,
+                            int32_t* plan, int32_t* plan_count, int32_t* table,
+                            int32_t* table_count, hipStream_t stream) {
   const dim3 grid(d.batch * d.heads), block(kSelectThreads);
   switch (items_for(d.max_blocks)) {
 #define OASIS_TP_CASE(I)                                                                          \
   case I:                                                                                         \
-    topk_plan_kernel<I><<<grid, block, 0, stream>>>(scores, seq_lens, topk, resident, plan,       \
-                                                    plan_count, table, table_count, d.heads,      \
-                                                    d.max_blocks, d.top_k, d.cap, d.window,       \
-                                                    d.table_stride);                              \
+    topk_plan_kernel<I><<<grid, block, 0, stream>>>(scores, seq_lens, topk, resident,             \
+                                                    resident_next, plan, plan_count, table,       \
+                                                    table_count, d.heads, d.max_blocks, d.top_k,  \
+                                                    d.cap, d.window, d.table_stride);             \
     break;
     OASIS_TP_CASE(1)
     OASIS_TP_CASE(2)

@@ -44,7 +44,7 @@ def _dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.exported_symbols())
@@ -75,8 +75,8 @@ def test_dims_validation(lib, field, value, status):
     st = lib.oasis_score_summaries(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None)
     assert st == status
     assert lib.oasis_last_error()
-    st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                               FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30, None)
+    st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30, None)
     assert st == status
 
 
@@ -120,9 +120,15 @@ def test_workspace_and_table_stride_checks(lib):
     st = lib.oasis_sparse_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, T, FAKE,
                                       float("inf"), FAKE, None, FAKE, need, None)
     assert st == INVALID_ARG
-    st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                               FAKE, FAKE, FAKE, 0.1, FAKE, None, None, need, None)
+    st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, None, need, None)
     assert st == WORKSPACE
+    # overlapping double-buffered slot tables are rejected
+    res = ctypes.c_void_p(0x10000)
+    st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, res,
+                               ctypes.c_void_p(0x10000 + 64), FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None,
+                               FAKE, need, None)
+    assert st == INVALID_ARG and b"overlap" in lib.oasis_last_error()
 
 
 def test_fetch_cap_rounding(lib):

@@ -204,15 +204,57 @@ def _run_step(lib, w, inp_dev, resident_cpu):
     return {key: val.detach().cpu() for key, val in out.items()}, summ
 
 
-def _compare_head(w, got, exp, b, h, exact_plan: bool):
+PLAN_KEYS = ("topk", "plan", "plan_count", "resident", "table", "table_count")
+
+
+def _plan_valid(got, exp, b, h, resident_row, cap, tol):
+    """The GPU's plan for one head obeys the capped-eviction rule up to near-ties
+    (score differences within ``tol``) in the oracle's scores."""
+    s = exp["scores"]
+    S = [int(x) for x in i64(got["topk"][b, h]) if x >= 0]
+    R = [int(x) for x in resident_row]
+    Rset = set(x for x in R if x >= 0)
+    new = [x for x in S if x not in Rset]
+    n = int(got["plan_count"][b, h])
+    assert n == min(cap, len(new))
+    plan = i64(got["plan"][b, h])[:n]
+    admitted = [int(r[1]) for r in plan]
+    assert set(admitted) <= set(new)
+    for a in admitted:
+        for o in set(new) - set(admitted):
+            assert s[a] >= s[o] - tol
+    slots = [int(r[0]) for r in plan]
+    assert slots == sorted(slots) and admitted == sorted(admitted)
+    n_empty = sum(1 for x in R if x < 0)
+    evicted = [R[i] for i in slots if R[i] >= 0]
+    assert len(evicted) == max(0, n - n_empty)
+    kept_stale = [x for i, x in enumerate(R) if x >= 0 and x not in set(S) and i not in slots]
+    for e in evicted:
+        assert e not in set(S)
+        for k in kept_stale:
+            assert s[e] <= s[k] + tol
+    Rn = list(R)
+    for r in plan:
+        assert int(r[2]) == R[int(r[0])]
+        Rn[int(r[0])] = int(r[1])
+    assert Rn == [int(x) for x in i64(got["resident"][b, h])]
+
+
+def _compare_head(w, got, exp, b, h, resident_row, robust: bool) -> bool:
+    """Scores within tolerance and the selection equal up to near-ties, always.  If the
+    GPU's selection, plan and table equal the oracle's, the attention output is
+    compared too (returns True); otherwise the head must have a near-tie in a
+    deciding comparison and its plan must still obey the rule (returns False)."""
     floor = score_floor(exp["q64"][None, None], exp["summ"][None, None])[0, 0]
     check_scores(f64(got["scores"][b, h]), exp["scores"], floor, f"scores b={b} h={h}")
     gsel, esel = i64(got["topk"][b, h]), exp["topk"]
     assert selection_equivalent(gsel, esel, exp["scores"]), f"selection b={b} h={h}"
-    if not exact_plan:
+    same = all(np.array_equal(i64(got[key][b, h]), exp[key]) for key in PLAN_KEYS)
+    if not same:
+        assert not robust, f"b={b} h={h}: the plan differs although no decision is a near-tie"
+        fin = exp["scores"][np.isfinite(exp["scores"])]
+        _plan_valid(got, exp, b, h, resident_row, w.cap, 1e-5 * float(np.abs(fin).max()))
         return False
-    for key in ("topk", "plan", "plan_count", "resident", "table", "table_count"):
-        np.testing.assert_array_equal(i64(got[key][b, h]), exp[key], err_msg=f"{key} b={b} h={h}")
     np.testing.assert_allclose(f64(got["out"][b, h]), exp["out"], rtol=0, atol=OUT_ATOL)
     fin = np.isfinite(exp["lse"])
     np.testing.assert_allclose(f64(got["lse"][b, h])[fin], exp["lse"][fin], rtol=0, atol=OUT_ATOL)
@@ -233,10 +275,7 @@ def test_decode_step_tiny_workload(lib):
             exp = oracle_head(inp["q"], inp["k"], inp["v"], lens, resident[b, h].numpy(), w.top_k,
                               w.window, w.cap, default_scale(), b, h)
             exp["q64"] = f64(inp["q"][b, h])
-            robust = plan_robust(exp["scores"], exp["topk"], resident[b, h].numpy(), w.cap,
-                                 ref.first_window_block(int(lens[b]), w.window))
-            assert robust
-            _compare_head(w, got, exp, b, h, exact_plan=True)
+            assert _compare_head(w, got, exp, b, h, resident[b, h].numpy(), robust=True)
 
 
 @pytest.mark.parametrize("ratio,W,lens", [(0.05, 64, [4096, 1000, 70]), (0.25, 0, [4096, 1024, 16]),
@@ -260,7 +299,7 @@ def test_decode_step_integer_inputs(lib, ratio, W, lens):
             exp = oracle_head(q, k, v, L, resident[b, h].numpy(), K, W, w.cap, default_scale(), b, h)
             exp["q64"] = f64(q[b, h])
             np.testing.assert_array_equal(f64(got["scores"][b, h]), exp["scores"])
-            _compare_head(w, got, exp, b, h, exact_plan=True)
+            assert _compare_head(w, got, exp, b, h, resident[b, h].numpy(), robust=True)
 
 
 def test_decode_step_deterministic(lib):
@@ -277,10 +316,13 @@ def test_decode_step_deterministic(lib):
 # Full-size workloads, sampled heads, in the benchmark's launch configuration
 # ---------------------------------------------------------------------------
 
-def _sample_heads(w, n=4):
-    heads = [(0, 0), (w.batch - 1, w.num_kv_heads - 1), (w.batch // 2, w.num_kv_heads // 2),
-             (min(1, w.batch - 1), w.num_kv_heads - 1)]
-    return list(dict.fromkeys(heads))[:n]
+def _sample_heads(w, n=6):
+    rng = np.random.default_rng(1234)
+    heads = [(0, 0), (w.batch - 1, w.num_kv_heads - 1)]
+    while len(heads) < n:
+        heads.append((int(rng.integers(w.batch)), int(rng.integers(w.num_kv_heads))))
+        heads = list(dict.fromkeys(heads))
+    return heads
 
 
 def _full_size_case(lib, w, layer=0):
@@ -321,14 +363,16 @@ def _full_size_case(lib, w, layer=0):
         exp["q64"] = f64(cpu["q"][(b, h)][0, 0])
         robust = plan_robust(exp["scores"], exp["topk"], resident[b, h].numpy(), w.cap,
                              ref.first_window_block(int(lens[b]), w.window))
-        n_exact += _compare_head(w, got, exp, b, h, exact_plan=robust)
+        n_exact += _compare_head(w, got, exp, b, h, resident[b, h].numpy(), robust)
         # whatever the robustness, the GPU's own outputs must be self-consistent
         tc = int(got["table_count"][b, h])
         assert int(got["plan_count"][b, h]) <= w.cap
         assert tc == int((got["resident"][b, h] >= 0).sum()) + ref.num_blocks(int(lens[b])) - \
             ref.first_window_block(int(lens[b]), w.window)
         assert torch.isfinite(got["out"][b, h]).all()
-    assert n_exact >= len(heads) - 1, f"only {n_exact} of {len(heads)} sampled heads were comparable"
+    # fp32 scoring error (~1e-7 relative) is far below the 1e-5 tolerance, so nearly
+    # every sampled head must reproduce the oracle's plan and table exactly
+    assert n_exact >= len(heads) - 1, f"only {n_exact} of {len(heads)} sampled heads matched exactly"
     del inp, summ, out
     torch.cuda.empty_cache()
 
