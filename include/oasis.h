@@ -193,7 +193,7 @@ oasis_status oasis_build_plan(const oasis_dims* dims, const float* scores, const
  *   table_stride host, 1 <= table_stride <= 4096
  *   seq_lens     device, int32 [B]
  *   scale        host, finite
- *   out          device, fp32 [B, H, G, 128]   (output)
+ *   out          device, fp32 [B, H, G, 128]   (output, 16-byte aligned)
  *   lse          device, fp32 [B, H, G]        (output; may be NULL)
  *   ws, ws_bytes device workspace, at least oasis_attn_workspace_bytes(dims, table_stride) */
 oasis_status oasis_sparse_decode_attn(const oasis_dims* dims, const void* q, const void* k,

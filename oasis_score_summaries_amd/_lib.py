@@ -270,7 +270,7 @@ def sparse_decode_attn(dims: OasisDims, q: torch.Tensor, k: torch.Tensor, v: tor
         out = torch.empty(s["out"], dtype=torch.float32, device=dev)
     if lse is None:
         lse = torch.empty(s["lse"], dtype=torch.float32, device=dev)
-    _need(out, "out", torch.float32, s["out"], dev)
+    _need(out, "out", torch.float32, s["out"], dev, align=16)
     _need(lse, "lse", torch.float32, s["lse"], dev)
     need = workspace_bytes(dims, stride)
     if ws is None:
@@ -362,11 +362,12 @@ class StageEvents:
     """Five HIP events bracketing the kernels of one fused step (see oasis_decode_step_timed)."""
 
     STAGES = ("score", "select_plan", "attn_split", "attn_merge")
+    N = 5
 
     def __init__(self):
         h = _hip_runtime()
-        self.handles = (ctypes.c_void_p * 5)()
-        for i in range(5):
+        self.handles = (ctypes.c_void_p * self.N)()
+        for i in range(self.N):
             ev = ctypes.c_void_p()
             if h.hipEventCreate(ctypes.byref(ev)) != 0:
                 raise RuntimeError("hipEventCreate failed")
@@ -374,7 +375,7 @@ class StageEvents:
 
     def elapsed_ms(self) -> Dict[str, float]:
         h = _hip_runtime()
-        if h.hipEventSynchronize(self.handles[4]) != 0:
+        if h.hipEventSynchronize(self.handles[self.N - 1]) != 0:
             raise RuntimeError("hipEventSynchronize failed")
         out = {}
         for i, name in enumerate(self.STAGES):
@@ -387,7 +388,7 @@ class StageEvents:
     def __del__(self):
         try:
             h = _hip_runtime()
-            for i in range(5):
+            for i in range(self.N):
                 if self.handles[i]:
                     h.hipEventDestroy(self.handles[i])
         except Exception:

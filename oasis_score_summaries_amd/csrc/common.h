@@ -58,6 +58,88 @@ __device__ inline uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---- wave64 cross-lane primitives on DPP (no LDS traffic) ---------------------------
+// DPP controls: row_shr:n = 0x110 + n, quad_perm [1,0,3,2] = 0xb1, [2,3,0,1] = 0x4e,
+// row_half_mirror = 0x141, row_mirror = 0x140.  Lanes without a source keep `old` (0).
+template <int CTRL>
+__device__ inline int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active).
+__device__ inline int wave_scan_incl(int x) {
+  x += dpp_i32<0x111>(x);
+  x += dpp_i32<0x112>(x);
+  x += dpp_i32<0x114>(x);
+  x += dpp_i32<0x118>(x);  // inclusive within each row of 16 lanes
+  const int t0 = __builtin_amdgcn_readlane(x, 15);
+  const int t1 = __builtin_amdgcn_readlane(x, 31);
+  const int t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
+}
+
+// Max / min of a uint32 over the 64 lanes of a wave; the result is wave-uniform.
+__device__ inline uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<0xb1>(x));
+  x = max(x, dpp_u32<0x4e>(x));
+  x = max(x, dpp_u32<0x141>(x));
+  x = max(x, dpp_u32<0x140>(x));  // every lane holds its row's max
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+  return max(a, b);
+}
+__device__ inline uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_u32<0xb1>(x));
+  x = min(x, dpp_u32<0x4e>(x));
+  x = min(x, dpp_u32<0x141>(x));
+  x = min(x, dpp_u32<0x140>(x));
+  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+  return min(a, b);
+}
+
+// Max and sum of a float over the 64 lanes of a wave; the result is wave-uniform.
+template <int CTRL>
+__device__ inline float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ inline float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<0xb1>(x));
+  x = fmaxf(x, dpp_f32<0x4e>(x));
+  x = fmaxf(x, dpp_f32<0x141>(x));
+  x = fmaxf(x, dpp_f32<0x140>(x));
+  const float a = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16)));
+  const float b = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
+  return fmaxf(a, b);
+}
+__device__ inline float wave_sum_f32(float x) {
+  x += dpp_f32<0xb1>(x);
+  x += dpp_f32<0x4e>(x);
+  x += dpp_f32<0x141>(x);
+  x += dpp_f32<0x140>(x);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
+                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return a + b;
+}
+
+// Exclusive rank of this lane among the lanes whose flag is set, and their count.
+__device__ inline int wave_flag_rank(bool flag, int* count) {
+  const uint64_t m = __ballot(flag);
+  *count = __popcll(m);
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = lane == 0 ? 0ull : (m & ((~0ull) >> (64 - lane)));
+  return __popcll(below);
+}
+
 // ---- wave64 / workgroup scans -----------------------------------------------------
 __device__ inline int wave_inclusive_scan(int x) {
   const int lane = threadIdx.x & 63;

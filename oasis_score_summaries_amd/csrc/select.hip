@@ -15,203 +15,318 @@
 // slots with the lowest scores (equal scores: higher block index first), and
 // pairs freed slots in slot order with admitted blocks in block order.
 //
-// One workgroup per (sequence, KV head).  Selection is an exact radix select
-// over order-preserving 32-bit keys (four 8-bit digit passes with an LDS
-// histogram), then the lowest-index ties of the threshold key, then a rank
-// sort of the K winners in LDS.  The plan uses LDS bitmaps for set membership
-// and workgroup prefix sums for every compaction, so every output position is
-// a pure function of the inputs (no atomics decide an order).
+// One workgroup per (sequence, KV head); the work is latency bound, so the
+// design minimises dependent steps and barriers:
+//   * scores sit in registers, element e = i * THREADS + tid (coalesced loads);
+//   * exact radix select over order-preserving 32-bit keys, starting below the
+//     bits that all keys share (found with two DPP wave reductions), 8 bits per
+//     pass, per-wave LDS histograms (no cross-wave atomic contention), a DPP
+//     prefix sum over the 256 digits, and an early exit once the threshold
+//     digit holds exactly the keys still needed;
+//   * the ties of the threshold key are taken in index order with ballot ranks;
+//   * the K winners are rank-sorted in LDS;
+//   * the plan uses LDS bitmaps for set membership and ballot ranks for every
+//     compaction, so every output position is a pure function of the inputs.
 #include "common.h"
 #include "launch.h"
 
 namespace oasis {
 
-constexpr int kSelectThreads = 1024;
-
-struct TopkShared {
-  uint32_t hist[256];
-  int scan[kSelectThreads / 64 + 1];
-  uint32_t cand_key[kMaxTopK];
-  int cand_idx[kMaxTopK];
+template <int THREADS, int ITEMS>
+struct SelectShared {
+  static constexpr int NW = THREADS / 64;
+  uint32_t hist[2][NW][256];
+  int scan[2][NW];
+  uint32_t rmax[NW], rmin[NW];
+  int cnt[ITEMS * NW];          // packed (> threshold) << 16 | (== threshold) counts per (item, wave)
+  alignas(16) uint64_t cand[kMaxTopK];  // (key << 32) | ~index: larger is better, all distinct
   int sorted_idx[kMaxTopK];
-  uint32_t digit;
-  int above;
+  uint32_t sel_digit;
+  int sel_above, sel_count, n_gt;
 };
 
+template <int THREADS>
 struct PlanShared {
+  static constexpr int NW = THREADS / 64;
   uint32_t bm_sel[kMaxBlocks / 32];
   uint32_t bm_res[kMaxBlocks / 32];
-  float st_score[kMaxTopK];
-  int st_blk[kMaxTopK];
-  int adm_list[kMaxTopK];
-  int adm_sorted[kMaxTopK];
-  int scan[kSelectThreads / 64 + 1];
+  alignas(16) uint64_t st[THREADS];  // stale slots: (order_key(score) << 32) | ~block, others all ones
+  int adm_list[THREADS];
+  int adm_sorted[THREADS];
+  int w_new[NW], w_empty[NW], w_vict[NW], w_tab[NW];
 };
 
+// Inclusive prefix sum over the threads of the workgroup; `scratch` holds NW ints
+// and is not reused by the caller before the next barrier.  Contains one barrier.
+template <int NW>
+__device__ inline int block_scan_incl(int x, int* scratch, int* total) {
+  const int inc = wave_scan_incl(x);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 63) scratch[wave] = inc;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = scratch[w];
+    before += (w < wave) ? c : 0;
+    tot += c;
+  }
+  *total = tot;
+  return before + inc;
+}
+
+// Sum of per-wave counts `wcount` (NW entries) over the waves before this one, and in total.
+template <int NW>
+__device__ inline int waves_before(const int* wcount, int* total) {
+  const int wave = threadIdx.x >> 6;
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = wcount[w];
+    before += (w < wave) ? c : 0;
+    tot += c;
+  }
+  *total = tot;
+  return before;
+}
+
+// Number of entries of v[0 .. n) greater than x (n even or odd; v 16-byte aligned).
+__device__ inline int rank_above(const uint64_t* v, int n, uint64_t x) {
+  int rank = 0;
+  const int n2 = n & ~1;
+  int u = 0;
+  for (; u + 8 <= n2; u += 8) {
+    uint64_t a[8];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const u32x4 w = *(const u32x4*)(v + u + j);
+      a[j] = ((uint64_t)w.y << 32) | w.x;
+      a[j + 1] = ((uint64_t)w.w << 32) | w.z;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rank += a[j] > x;
+  }
+  for (; u < n; ++u) rank += v[u] > x;
+  return rank;
+}
+// Number of entries of v[0 .. n) smaller than x.
+__device__ inline int rank_below(const uint64_t* v, int n, uint64_t x) {
+  int rank = 0;
+  const int n2 = n & ~1;
+  int u = 0;
+  for (; u + 8 <= n2; u += 8) {
+    uint64_t a[8];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const u32x4 w = *(const u32x4*)(v + u + j);
+      a[j] = ((uint64_t)w.y << 32) | w.x;
+      a[j + 1] = ((uint64_t)w.w << 32) | w.z;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rank += a[j] < x;
+  }
+  for (; u < n; ++u) rank += v[u] < x;
+  return rank;
+}
+
 // Selects the min(K, n_cand) best of row[0 .. n_cand) into sh.sorted_idx, best
-// first; returns that count.  Thread t owns elements [t*ITEMS, (t+1)*ITEMS), so
-// thread order is index order for the tie scans.  Every thread must call it.
-template <int ITEMS>
-__device__ int topk_select(const float* __restrict__ row, int n_cand, int K, TopkShared& sh) {
-  const int tid = threadIdx.x;
+// first, and returns that count.  Every thread of the workgroup must call it.
+template <int THREADS, int ITEMS>
+__device__ int topk_select(const float* __restrict__ row, int n_cand, int K,
+                           SelectShared<THREADS, ITEMS>& sh) {
+  constexpr int NW = THREADS / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = n_cand < K ? n_cand : K;
   if (m <= 0) return 0;  // uniform across the workgroup
+
   uint32_t key[ITEMS];
-  const int base = tid * ITEMS;
+  uint32_t lmax = 0u, lmin = 0xffffffffu;
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
-    const int e = base + i;
+    const int e = i * THREADS + tid;
     key[i] = (e < n_cand) ? order_key(row[e]) : 0u;
-  }
-
-  uint32_t prefix = 0u, mask = 0u;
-  int krem = m;  // how many of the elements matching `prefix` are still to be taken
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += blockDim.x) sh.hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < ITEMS; ++i) {
-      if (base + i < n_cand && (key[i] & mask) == prefix) atomicAdd(&sh.hist[(key[i] >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // Lane l owns digits 255-4l .. 252-4l, i.e. the histogram read from the top.
-      int c[4];
-      int local = 0;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        c[u] = (int)sh.hist[255 - 4 * tid - u];
-        local += c[u];
-      }
-      int run = wave_inclusive_scan(local) - local;  // elements in larger digits
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (run < krem && krem <= run + c[u]) {
-          sh.digit = (uint32_t)(255 - 4 * tid - u);
-          sh.above = run;
-        }
-        run += c[u];
-      }
-    }
-    __syncthreads();
-    prefix |= sh.digit << shift;
-    mask |= 0xffu << shift;
-    krem -= sh.above;
-    __syncthreads();
-  }
-
-  // Threshold key `prefix`: every larger key is taken, plus the krem lowest-
-  // index elements equal to it.
-  int n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    if (base + i < n_cand) {
-      n_gt += key[i] > prefix;
-      n_eq += key[i] == prefix;
+    if (e < n_cand) {
+      lmax = max(lmax, key[i]);
+      lmin = min(lmin, key[i]);
     }
   }
-  int tot_gt, tot_eq;
-  int off_gt = block_exclusive_scan(n_gt, sh.scan, &tot_gt);
-  int off_eq = block_exclusive_scan(n_eq, sh.scan, &tot_eq);
-#pragma unroll
-  for (int i = 0; i < ITEMS; ++i) {
-    const int e = base + i;
-    if (e >= n_cand) continue;
-    if (key[i] > prefix) {
-      sh.cand_key[off_gt] = key[i];
-      sh.cand_idx[off_gt] = e;
-      ++off_gt;
-    } else if (key[i] == prefix) {
-      if (off_eq < krem) {
-        sh.cand_key[tot_gt + off_eq] = key[i];
-        sh.cand_idx[tot_gt + off_eq] = e;
-      }
-      ++off_eq;
-    }
+  lmax = wave_max_u32(lmax);
+  lmin = wave_min_u32(lmin);
+  if (lane == 0) {
+    sh.rmax[wave] = lmax;
+    sh.rmin[wave] = lmin;
   }
   __syncthreads();
-  // Rank sort of the m winners: all keys differ in (key, -index).
-  for (int t = tid; t < m; t += blockDim.x) {
-    const uint32_t kt = sh.cand_key[t];
-    const int it = sh.cand_idx[t];
-    int rank = 0;
-    for (int u = 0; u < m; ++u) {
-      const uint32_t ku = sh.cand_key[u];
-      rank += (ku > kt) || (ku == kt && sh.cand_idx[u] < it);
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    kmax = max(kmax, sh.rmax[w]);
+    kmin = min(kmin, sh.rmin[w]);
+  }
+
+  // Radix select below the common high bits.  Invariant: `prefix` holds the
+  // threshold key's bits at positions > top (and zeros below); krem of the keys
+  // that match it there are still to be taken.
+  uint32_t prefix = kmax;
+  int krem = m;
+  int lo = 32;  // keys are compared on key >> lo
+  const uint32_t diff = kmax ^ kmin;
+  if (diff != 0u) {
+    int top = 31 - __clz(diff);
+    prefix = (uint32_t)(((uint64_t)kmax >> (top + 1)) << (top + 1));
+    for (int pass = 0;; ++pass) {
+      lo = top >= 7 ? top - 7 : 0;
+      const uint32_t dmask = (1u << (top - lo + 1)) - 1u;
+      const uint64_t hi_match = (uint64_t)prefix >> (top + 1);
+      uint32_t* hist = sh.hist[pass & 1][wave];
+      for (int dd = lane; dd < 256; dd += 64) hist[dd] = 0u;  // this wave's own histogram
+#pragma unroll
+      for (int i = 0; i < ITEMS; ++i) {
+        const int e = i * THREADS + tid;
+        if (e < n_cand && ((uint64_t)key[i] >> (top + 1)) == hi_match)
+          atomicAdd(&hist[(key[i] >> lo) & dmask], 1u);
+      }
+      __syncthreads();
+      // Thread t owns digit 255 - t: the prefix sum runs from the largest digit down.
+      const int digit = 255 - tid;
+      int cnt = 0;
+      if (tid < 256) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) cnt += (int)sh.hist[pass & 1][w][digit];
+      }
+      int tot;
+      const int incl = block_scan_incl<NW>(cnt, sh.scan[pass & 1], &tot);
+      const int excl = incl - cnt;
+      if (cnt > 0 && excl < krem && krem <= incl) {
+        sh.sel_digit = (uint32_t)digit;
+        sh.sel_above = excl;
+        sh.sel_count = cnt;
+      }
+      __syncthreads();
+      prefix |= sh.sel_digit << lo;
+      krem -= sh.sel_above;
+      const int count = sh.sel_count;
+      if (lo == 0 || count == krem) break;  // every key matching the prefix is taken
+      top = lo - 1;
     }
-    sh.sorted_idx[rank] = it;
+  }
+
+  // Collect: keys above the threshold (on key >> lo) all go; of the keys equal to
+  // it, the krem with the lowest indices.  Index order is (item, wave, lane).
+  const uint64_t thr = (uint64_t)prefix >> lo;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int e = i * THREADS + tid;
+    const uint64_t kk = (uint64_t)key[i] >> lo;
+    const int cg = __popcll(__ballot(e < n_cand && kk > thr));
+    const int ce = __popcll(__ballot(e < n_cand && kk == thr));
+    if (lane == 0) sh.cnt[i * NW + wave] = ce | (cg << 16);
+  }
+  __syncthreads();
+  {
+    const int v = (tid < ITEMS * NW) ? sh.cnt[tid] : 0;
+    int tot;
+    const int incl = block_scan_incl<NW>(v, sh.scan[0], &tot);
+    if (tid < ITEMS * NW) sh.cnt[tid] = incl - v;  // exclusive, packed
+    if (tid == 0) sh.n_gt = (int)((uint32_t)tot >> 16);
+  }
+  __syncthreads();
+  const int n_gt = sh.n_gt;  // == m - krem
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int e = i * THREADS + tid;
+    const uint64_t kk = (uint64_t)key[i] >> lo;
+    const bool gt = e < n_cand && kk > thr;
+    const bool eq = e < n_cand && kk == thr;
+    int unused;
+    const int rg = wave_flag_rank(gt, &unused);
+    const int re = wave_flag_rank(eq, &unused);
+    const int base = sh.cnt[i * NW + wave];
+    const uint64_t comp = ((uint64_t)key[i] << 32) | (uint32_t)(~(uint32_t)e);
+    if (gt) sh.cand[(int)((uint32_t)base >> 16) + rg] = comp;
+    const int r = (base & 0xffff) + re;
+    if (eq && r < krem) sh.cand[n_gt + r] = comp;
+  }
+  __syncthreads();
+  // Rank sort of the m winners: rank = number of larger composites.  The loop reads
+  // LDS 16 bytes at a time, several reads in flight.
+  for (int t = tid; t < m; t += THREADS) {
+    const uint64_t ct = sh.cand[t];
+    sh.sorted_idx[rank_above(sh.cand, m, ct)] = (int)(~(uint32_t)ct);
   }
   __syncthreads();
   return m;
 }
 
-// Applies the capped-eviction rule for one (sequence, KV head).  `sel` holds the
-// K selection entries (-1 = none), best first.  Every thread must call it, with
-// blockDim.x >= K.
-__device__ void plan_apply(const float* __restrict__ srow, const int* sel, const int32_t* res,
+// Applies the capped-eviction rule for one (sequence, KV head).  Thread t < K passes
+// selection entry t as `s_i` (-1 = none; the entries are best first); `res` holds the
+// resident slots; the updated slots go to `res_next` (may equal `res`).  Needs
+// K <= THREADS; every thread calls it.
+template <int THREADS>
+__device__ void plan_apply(const float* __restrict__ srow, int s_i, const int32_t* res,
                            int32_t* res_next, int32_t* plan_row, int32_t* plan_count,
                            int32_t* table_row, int32_t* table_count, int K, int C, int NB, int w0,
-                           int nblk, int T, PlanShared& sh) {
-  const int tid = threadIdx.x;
+                           int nblk, int T, PlanShared<THREADS>& sh) {
+  constexpr int NW = THREADS / 64;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nwords = (NB + 31) >> 5;
-  for (int w = tid; w < nwords; w += blockDim.x) {
+  for (int w = tid; w < nwords; w += THREADS) {
     sh.bm_sel[w] = 0u;
     sh.bm_res[w] = 0u;
   }
+  int r_i = -1;
+  if (tid < K) r_i = res[tid];
+  else s_i = -1;
   __syncthreads();
-  int s_i = -1, r_i = -1;
-  if (tid < K) {
-    s_i = sel[tid];
-    r_i = res[tid];
-  }
   const bool s_ok = s_i >= 0 && s_i < NB;
   const bool r_ok = r_i >= 0 && r_i < NB;
   if (s_ok) atomicOr(&sh.bm_sel[s_i >> 5], 1u << (s_i & 31));
   if (r_ok) atomicOr(&sh.bm_res[r_i >> 5], 1u << (r_i & 31));
   __syncthreads();
 
-  // Admission: selected, not resident, in selection order; the first n are admitted.
-  const int is_new = (s_ok && !((sh.bm_res[s_i >> 5] >> (s_i & 31)) & 1u)) ? 1 : 0;
-  int n_new;
-  const int pos_new = block_exclusive_scan(is_new, sh.scan, &n_new);
-  const int n = C < n_new ? C : n_new;
-  const bool admitted = is_new && pos_new < n;
-
-  // Victims: empty slots by slot, then stale slots by (score asc, block desc).
+  // New blocks (selection order) and empty slots (slot order): ballot ranks.
+  const bool is_new = s_ok && !((sh.bm_res[s_i >> 5] >> (s_i & 31)) & 1u);
   const bool empty = tid < K && r_i < 0;
   const bool stale = tid < K && r_i >= 0 && !(r_ok && ((sh.bm_sel[r_i >> 5] >> (r_i & 31)) & 1u));
-  int n_empty;
-  const int pos_empty = block_exclusive_scan(empty ? 1 : 0, sh.scan, &n_empty);
-  const float sc = stale ? (r_ok ? srow[r_i] : -INFINITY) : 0.f;
-  if (tid < K) {
-    sh.st_score[tid] = sc;
-    sh.st_blk[tid] = stale ? r_i : -1;
+  int c_new, c_empty;
+  const int rk_new = wave_flag_rank(is_new, &c_new);
+  const int rk_empty = wave_flag_rank(empty, &c_empty);
+  if (lane == 0) {
+    sh.w_new[wave] = c_new;
+    sh.w_empty[wave] = c_empty;
   }
+  // Worst-first order of stale slots: ascending score, equal scores higher block first.
+  const uint64_t st_me =
+      stale ? (((uint64_t)order_key(r_ok ? srow[r_i] : -INFINITY) << 32) | (uint32_t)(~(uint32_t)r_i))
+            : ~0ull;
+  if (tid < K) sh.st[tid] = st_me;
+  __syncthreads();
+  int n_new, n_empty;
+  const int pos_new = waves_before<NW>(sh.w_new, &n_new) + rk_new;
+  const int pos_empty = waves_before<NW>(sh.w_empty, &n_empty) + rk_empty;
+  const int n = C < n_new ? C : n_new;
+  const bool admitted = is_new && pos_new < n;
   if (admitted) sh.adm_list[pos_new] = s_i;
   __syncthreads();
+
+  // Victims: the first n of (empty slots by slot, stale slots by score asc, block desc).
   bool victim = false;
   if (empty) {
     victim = pos_empty < n;
-  } else if (stale) {
-    const int m_stale = n - n_empty;
-    if (m_stale > 0) {
-      int rank = 0;
-      for (int u = 0; u < K; ++u) {
-        const int bu = sh.st_blk[u];
-        if (bu < 0) continue;
-        const float su = sh.st_score[u];
-        rank += (su < sc) || (su == sc && bu > r_i);
-      }
-      victim = rank < m_stale;
-    }
+  } else if (stale && n > n_empty) {
+    victim = rank_below(sh.st, K, st_me) < n - n_empty;
   }
   if (admitted) {
     int rank = 0;
     for (int u = 0; u < n; ++u) rank += sh.adm_list[u] < s_i;
     sh.adm_sorted[rank] = s_i;
   }
+  int c_vict;
+  const int rk_vict = wave_flag_rank(victim, &c_vict);
+  if (lane == 0) sh.w_vict[wave] = c_vict;
+  __syncthreads();
   int n_vict;
-  const int pos_vict = block_exclusive_scan(victim ? 1 : 0, sh.scan, &n_vict);  // syncs
+  const int pos_vict = waves_before<NW>(sh.w_vict, &n_vict) + rk_vict;
   const int n_placed = n < n_vict ? n : n_vict;
 
   int new_r = r_i;
@@ -221,10 +336,10 @@ __device__ void plan_apply(const float* __restrict__ srow, const int* sel, const
     plan_row[3 * pos_vict + 1] = new_r;
     plan_row[3 * pos_vict + 2] = r_i;
   }
-  // Every slot is written so that res_next may be a different buffer; when it
-  // is `res` itself, each thread rewrites only the slot it read above.
+  // Every slot is written so that res_next may be another buffer; when it is `res`
+  // itself each thread rewrites only the slot it read above.
   if (tid < K) res_next[tid] = new_r;
-  for (int r = n_placed + tid; r < C; r += blockDim.x) {
+  for (int r = n_placed + tid; r < C; r += THREADS) {
     plan_row[3 * r + 0] = -1;
     plan_row[3 * r + 1] = -1;
     plan_row[3 * r + 2] = -1;
@@ -233,89 +348,109 @@ __device__ void plan_apply(const float* __restrict__ srow, const int* sel, const
 
   // Table: updated resident entries in slot order, then the window blocks.
   const bool keep = tid < K && new_r >= 0 && new_r < NB;
+  int c_tab;
+  const int rk_tab = wave_flag_rank(keep, &c_tab);
+  if (lane == 0) sh.w_tab[wave] = c_tab;
+  __syncthreads();
   int n_res;
-  const int pos_t = block_exclusive_scan(keep ? 1 : 0, sh.scan, &n_res);
+  const int pos_t = waves_before<NW>(sh.w_tab, &n_res) + rk_tab;
   if (keep) table_row[pos_t] = new_r;
   const int nwin = nblk - w0;
-  for (int i = tid; i < nwin; i += blockDim.x) table_row[n_res + i] = w0 + i;
-  for (int i = n_res + nwin + tid; i < T; i += blockDim.x) table_row[i] = -1;
+  for (int i = tid; i < nwin; i += THREADS) table_row[n_res + i] = w0 + i;
+  for (int i = n_res + nwin + tid; i < T; i += THREADS) table_row[i] = -1;
   if (tid == 0) *table_count = n_res + nwin;
 }
 
-template <int ITEMS>
-__global__ __launch_bounds__(kSelectThreads) void topk_kernel(const float* __restrict__ scores,
-                                                              const int32_t* __restrict__ seq_lens,
-                                                              int32_t* __restrict__ topk, int heads,
-                                                              int NB, int K, int window) {
-  __shared__ TopkShared sh;
+template <int THREADS, int ITEMS>
+__global__ __launch_bounds__(THREADS) void topk_kernel(const float* __restrict__ scores,
+                                                       const int32_t* __restrict__ seq_lens,
+                                                       int32_t* __restrict__ topk, int heads, int NB,
+                                                       int K, int window) {
+  __shared__ SelectShared<THREADS, ITEMS> sh;
   const int bh = blockIdx.x;
   const int len = clamp_len(seq_lens[bh / heads], NB);
   const int n_cand = first_window_block(len, window);
-  const int m = topk_select<ITEMS>(scores + (size_t)bh * NB, n_cand, K, sh);
-  for (int t = threadIdx.x; t < K; t += blockDim.x) topk[(size_t)bh * K + t] = t < m ? sh.sorted_idx[t] : -1;
+  const int m = topk_select<THREADS, ITEMS>(scores + (size_t)bh * NB, n_cand, K, sh);
+  for (int t = threadIdx.x; t < K; t += THREADS) topk[(size_t)bh * K + t] = t < m ? sh.sorted_idx[t] : -1;
 }
 
-__global__ __launch_bounds__(kSelectThreads) void plan_kernel(
+template <int THREADS>
+__global__ __launch_bounds__(THREADS) void plan_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ topk,
     const int32_t* __restrict__ seq_lens, int32_t* resident, int32_t* plan, int32_t* plan_count,
     int32_t* table, int32_t* table_count, int heads, int NB, int K, int C, int window, int T) {
-  __shared__ PlanShared sh;
+  __shared__ PlanShared<THREADS> sh;
   const int bh = blockIdx.x;
   const int len = clamp_len(seq_lens[bh / heads], NB);
-  plan_apply(scores + (size_t)bh * NB, topk + (size_t)bh * K, resident + (size_t)bh * K,
-             resident + (size_t)bh * K, plan + (size_t)bh * C * 3, plan_count + bh,
-             table + (size_t)bh * T, table_count + bh, K, C, NB, first_window_block(len, window),
-             num_blocks(len), T, sh);
+  const int s_i = threadIdx.x < K ? topk[(size_t)bh * K + threadIdx.x] : -1;
+  plan_apply<THREADS>(scores + (size_t)bh * NB, s_i, resident + (size_t)bh * K,
+                      resident + (size_t)bh * K, plan + (size_t)bh * C * 3, plan_count + bh,
+                      table + (size_t)bh * T, table_count + bh, K, C, NB,
+                      first_window_block(len, window), num_blocks(len), T, sh);
 }
 
-template <int ITEMS>
-__global__ __launch_bounds__(kSelectThreads) void topk_plan_kernel(
+// Selection and plan in one workgroup.
+template <int THREADS, int ITEMS>
+__global__ __launch_bounds__(THREADS) void topk_plan_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int32_t* topk,
     const int32_t* resident, int32_t* resident_next, int32_t* plan, int32_t* plan_count,
     int32_t* table, int32_t* table_count, int heads, int NB, int K, int C, int window, int T) {
-  __shared__ TopkShared tsh;
-  __shared__ PlanShared psh;
+  // The selection's LDS is dead once each thread holds its entry, so the plan reuses it.
+  __shared__ union {
+    SelectShared<THREADS, ITEMS> t;
+    PlanShared<THREADS> p;
+  } sh;
   const int bh = blockIdx.x;
   const int len = clamp_len(seq_lens[bh / heads], NB);
   const int n_cand = first_window_block(len, window);
   const float* srow = scores + (size_t)bh * NB;
-  const int m = topk_select<ITEMS>(srow, n_cand, K, tsh);
-  for (int t = threadIdx.x; t < K; t += blockDim.x) {
-    const int v = t < m ? tsh.sorted_idx[t] : -1;
-    tsh.sorted_idx[t] = v;
-    topk[(size_t)bh * K + t] = v;
-  }
+  const int m = topk_select<THREADS, ITEMS>(srow, n_cand, K, sh.t);
+  for (int t = threadIdx.x; t < K; t += THREADS) topk[(size_t)bh * K + t] = t < m ? sh.t.sorted_idx[t] : -1;
+  const int s_i = (threadIdx.x < m) ? sh.t.sorted_idx[threadIdx.x] : -1;
   __syncthreads();
-  plan_apply(srow, tsh.sorted_idx, resident + (size_t)bh * K, resident_next + (size_t)bh * K,
-             plan + (size_t)bh * C * 3, plan_count + bh, table + (size_t)bh * T, table_count + bh,
-             K, C, NB, n_cand, num_blocks(len), T, psh);
+  plan_apply<THREADS>(srow, s_i, resident + (size_t)bh * K, resident_next + (size_t)bh * K,
+                      plan + (size_t)bh * C * 3, plan_count + bh, table + (size_t)bh * T,
+                      table_count + bh, K, C, NB, n_cand, num_blocks(len), T, sh.p);
 }
 
-static int items_for(int NB) {
+// Workgroup size and scores per thread for a problem: 256 threads while K <= 256
+// and the scores fit 8 per thread, else 1024 (up to 32 per thread).
+static int select_threads(const Dims& d) {
+  return (d.top_k <= 256 && d.max_blocks <= 256 * 8) ? 256 : 1024;
+}
+static int select_items(const Dims& d, int threads) {
   int items = 1;
-  while (items * kSelectThreads < NB) items <<= 1;
+  while (items * threads < d.max_blocks) items <<= 1;
   return items;
 }
 
+#define OASIS_SELECT_DISPATCH(CASE)                      \
+  do {                                                   \
+    const int threads_ = select_threads(d);              \
+    const int items_ = select_items(d, threads_);        \
+    if (threads_ == 256) {                               \
+      switch (items_) {                                  \
+        CASE(256, 1) CASE(256, 2) CASE(256, 4) CASE(256, 8) \
+        default: return hipErrorInvalidValue;            \
+      }                                                  \
+    } else {                                             \
+      switch (items_) {                                  \
+        CASE(1024, 1) CASE(1024, 2) CASE(1024, 4) CASE(1024, 8) CASE(1024, 16) CASE(1024, 32) \
+        default: return hipErrorInvalidValue;            \
+      }                                                  \
+    }                                                    \
+  } while (0)
+
 hipError_t launch_topk(const Dims& d, const float* scores, const int32_t* seq_lens, int32_t* topk,
                        hipStream_t stream) {
-  const dim3 grid(d.batch * d.heads), block(kSelectThreads);
-  switch (items_for(d.max_blocks)) {
-#define OASIS_TOPK_CASE(I)                                                                        \
-  case I:                                                                                         \
-    topk_kernel<I><<<grid, block, 0, stream>>>(scores, seq_lens, topk, d.heads, d.max_blocks,     \
-                                               d.top_k, d.window);                                \
+#define OASIS_TOPK_CASE(T, I)                                                                       \
+  case I:                                                                                           \
+    topk_kernel<T, I><<<dim3(d.batch * d.heads), dim3(T), 0, stream>>>(scores, seq_lens, topk,      \
+                                                                       d.heads, d.max_blocks,       \
+                                                                       d.top_k, d.window);          \
     break;
-    OASIS_TOPK_CASE(1)
-    OASIS_TOPK_CASE(2)
-    OASIS_TOPK_CASE(4)
-    OASIS_TOPK_CASE(8)
-    OASIS_TOPK_CASE(16)
-    OASIS_TOPK_CASE(32)
+  OASIS_SELECT_DISPATCH(OASIS_TOPK_CASE);
 #undef OASIS_TOPK_CASE
-    default:
-      return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 
@@ -323,10 +458,15 @@ hipError_t launch_plan(const Dims& d, const float* scores, const int32_t* topk,
                        const int32_t* seq_lens, int32_t* resident, int32_t* plan,
                        int32_t* plan_count, int32_t* table, int32_t* table_count,
                        hipStream_t stream) {
-  const int threads = ((d.top_k + 63) / 64) * 64;
-  plan_kernel<<<dim3(d.batch * d.heads), dim3(threads), 0, stream>>>(
-      scores, topk, seq_lens, resident, plan, plan_count, table, table_count, d.heads,
-      d.max_blocks, d.top_k, d.cap, d.window, d.table_stride);
+  if (d.top_k <= 256) {
+    plan_kernel<256><<<dim3(d.batch * d.heads), dim3(256), 0, stream>>>(
+        scores, topk, seq_lens, resident, plan, plan_count, table, table_count, d.heads,
+        d.max_blocks, d.top_k, d.cap, d.window, d.table_stride);
+  } else {
+    plan_kernel<1024><<<dim3(d.batch * d.heads), dim3(1024), 0, stream>>>(
+        scores, topk, seq_lens, resident, plan, plan_count, table, table_count, d.heads,
+        d.max_blocks, d.top_k, d.cap, d.window, d.table_stride);
+  }
   return hipGetLastError();
 }
 
@@ -334,25 +474,14 @@ hipError_t launch_topk_plan(const Dims& d, const float* scores, const int32_t* s
                             int32_t* topk, const int32_t* resident, int32_t* resident_next,
                             int32_t* plan, int32_t* plan_count, int32_t* table,
                             int32_t* table_count, hipStream_t stream) {
-  const dim3 grid(d.batch * d.heads), block(kSelectThreads);
-  switch (items_for(d.max_blocks)) {
-#define OASIS_TP_CASE(I)                                                                          \
-  case I:                                                                                         \
-    topk_plan_kernel<I><<<grid, block, 0, stream>>>(scores, seq_lens, topk, resident,             \
-                                                    resident_next, plan, plan_count, table,       \
-                                                    table_count, d.heads, d.max_blocks, d.top_k,  \
-                                                    d.cap, d.window, d.table_stride);             \
+#define OASIS_TP_CASE(T, I)                                                                        \
+  case I:                                                                                          \
+    topk_plan_kernel<T, I><<<dim3(d.batch * d.heads), dim3(T), 0, stream>>>(                       \
+        scores, seq_lens, topk, resident, resident_next, plan, plan_count, table, table_count,     \
+        d.heads, d.max_blocks, d.top_k, d.cap, d.window, d.table_stride);                          \
     break;
-    OASIS_TP_CASE(1)
-    OASIS_TP_CASE(2)
-    OASIS_TP_CASE(4)
-    OASIS_TP_CASE(8)
-    OASIS_TP_CASE(16)
-    OASIS_TP_CASE(32)
+  OASIS_SELECT_DISPATCH(OASIS_TP_CASE);
 #undef OASIS_TP_CASE
-    default:
-      return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 
