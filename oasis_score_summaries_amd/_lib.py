@@ -109,13 +109,20 @@ def _ptr(t: Optional[torch.Tensor]) -> ctypes.c_void_p:
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
+def _norm_device(dev) -> torch.device:
+    dev = torch.device(dev)
+    if dev.type == "cuda" and dev.index is None:
+        return torch.device("cuda", torch.cuda.current_device())
+    return dev
+
+
 def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: Tuple[int, ...], device=None,
           align: int = 4):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
-    if device is not None and t.device != device:
+    if device is not None and _norm_device(t.device) != _norm_device(device):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -289,7 +296,7 @@ class StepBuffers:
 
     def __init__(self, dims: OasisDims, device):
         s = _shapes(dims)
-        dev = torch.device(device)
+        dev = _norm_device(device)
         self.scores = torch.empty(s["scores"], dtype=torch.float32, device=dev)
         self.topk = torch.empty(s["topk"], dtype=torch.int32, device=dev)
         self.plan, self.plan_count, self.table, self.table_count = _plan_outputs(
@@ -417,7 +424,7 @@ class PreparedStep:
             _need(resident_next, "resident_next", torch.int32, s["resident"], dev)
         b = buffers
         for name, t in b.as_dict().items():
-            if t.device != dev:
+            if _norm_device(t.device) != _norm_device(dev):
                 raise ValueError(f"buffer {name} is on {t.device}, expected {dev}")
         if b.ws.numel() < workspace_bytes(dims):
             raise ValueError("workspace too small")

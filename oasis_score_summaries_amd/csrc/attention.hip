@@ -15,32 +15,47 @@
 // visible (on this multi-XCD part a device-scope fence writes back and
 // invalidates the whole L2).
 //
-// Per block, per wave (G <= 16 query heads padded to 16 MFMA columns):
-//   S^T = K (16 tokens x 128) . q^T          4 x v_mfma_f32_16x16x32_bf16
-//   O^T += V^T (128 x 16 tokens) . P^T        32 x v_mfma_f32_16x16x4_f32
-// bf16 K and q multiply exactly; P stays fp32 and V widens exactly to fp32, so
-// the result carries only fp32 accumulation rounding.  The token order inside
-// the PV contraction is chosen so that each lane feeds the probabilities it
-// computed itself (no cross-lane exchange), and the head-dim order inside an
-// output tile is interleaved so that each lane feeds one element of a 16-byte
-// V load it already holds.  Lane l ends up owning query head l%16 and head
-// dims [32*(l/16), 32*(l/16)+32), i.e. 128 contiguous output bytes.
+// Per pair of blocks, per wave (G <= 16 query heads padded to 16 MFMA columns):
+//   S^T = K (16 tokens x 128) . q^T           2 x 4 x v_mfma_f32_16x16x32_bf16
+//   O^T += V^T (128 x 32 tokens) . P^T        2 x 8 x v_mfma_f32_16x16x32_bf16
+// bf16 K and q multiply exactly.  Each fp32 probability p enters the PV product
+// as two bf16 terms, bf16(p) and bf16(p - bf16(p)), which carry p to about 2^-17
+// relative at twice the (small) cost of one bf16 product.  (Built with
+// OASIS_ATTN_PV_BF16=0, PV runs as 32 fp32 v_mfma_f32_16x16x4_f32 per block
+// instead.)  The token
+// order inside the PV contraction is chosen so that each lane feeds the
+// probabilities it computed itself (no cross-lane exchange), and the head-dim
+// order inside an output tile is interleaved so that each lane feeds one element
+// of a 16-byte V load it already holds.  Lane l ends up owning query head l%16
+// and head dims [32*(l/16), 32*(l/16)+32), i.e. 128 contiguous output bytes.
 #include "common.h"
 #include "launch.h"
 
 namespace oasis {
 
+#ifndef OASIS_ATTN_BLOCKS_PER_WAVE
+#define OASIS_ATTN_BLOCKS_PER_WAVE 2
+#endif
+#ifndef OASIS_ATTN_MIN_ROUNDS
+#define OASIS_ATTN_MIN_ROUNDS 1
+#endif
+#ifndef OASIS_ATTN_PV_BF16
+#define OASIS_ATTN_PV_BF16 1
+#endif
 constexpr int kAttnWaves = 4;
-constexpr int kAttnBlocksPerWave = 2;                          // blocks in flight per wave
+constexpr int kAttnBlocksPerWave = OASIS_ATTN_BLOCKS_PER_WAVE;  // blocks in flight per wave
 constexpr int kAttnBlocksPerRound = kAttnWaves * kAttnBlocksPerWave;
 constexpr int kAttnMaxSplits = 64;                             // partials per head
+static_assert(!OASIS_ATTN_PV_BF16 || kAttnBlocksPerWave % 2 == 0,
+              "the bf16 PV product takes blocks in pairs");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 AttnSplit attn_split(int table_stride) {
   // Enough rounds per workgroup that no head has more than kAttnMaxSplits partials.
   const int rounds_needed = (table_stride + kAttnBlocksPerRound - 1) / kAttnBlocksPerRound;
-  const int rounds = (rounds_needed + kAttnMaxSplits - 1) / kAttnMaxSplits;
+  int rounds = (rounds_needed + kAttnMaxSplits - 1) / kAttnMaxSplits;
+  if (rounds < OASIS_ATTN_MIN_ROUNDS) rounds = OASIS_ATTN_MIN_ROUNDS;
   AttnSplit s;
   s.blocks_per_split = rounds * kAttnBlocksPerRound;
   s.num_splits = (table_stride + s.blocks_per_split - 1) / s.blocks_per_split;
@@ -62,6 +77,16 @@ __device__ inline float bf16_elem(const u32x4& v, int e) {
 }
 
 // One workgroup: `rounds` rounds of kAttnBlocksPerRound table entries of one head.
+//
+// K and V blocks are read with fully contiguous 1 KB wave loads (instruction s of
+// a block covers tokens 4s..4s+3): lane l holds token 4s + l/16, 16-byte chunk
+// l%16.  That is already the layout the PV product wants for V.  For QK, lane l
+// must supply one token's chunks, so K goes through LDS (rows padded to 272
+// bytes, conflict-free) and is read back with MFMA row i holding token
+// 4*(i%4) + i/4; the scores then come out with lane l owning exactly the tokens
+// 4r + l/16 whose V rows it loaded.
+constexpr int kKRow = kHeadDim * 2 / 16 + 1;  // padded LDS row of one K token, in 16-byte chunks
+
 __global__ __launch_bounds__(256) void attn_split_kernel(
     const u32x4* __restrict__ q, const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const int32_t* __restrict__ table, const int32_t* __restrict__ table_count, int T,
@@ -69,7 +94,11 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     float* __restrict__ part_ml, int heads, int group, int queries, int NB, int nsplit, int rounds) {
   __shared__ float sm_m[kAttnWaves][16];
   __shared__ float sm_l[kAttnWaves][16];
-  __shared__ float sm_o[kAttnWaves][16][kHeadDim + 4];
+  // K staging during the rounds, then the cross-wave merge of the outputs.
+  __shared__ union {
+    u32x4 kst[kAttnWaves][kAttnBlocksPerWave][kBlock * kKRow];
+    float o[kAttnWaves][16][kHeadDim + 4];
+  } sm;
 
   const int bh = blockIdx.y, sp = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -80,68 +109,183 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
   const int split_blocks = rounds * kAttnBlocksPerRound;
   if (sp * split_blocks >= tc) return;  // the merge reads only splits below ceil(tc / split_blocks)
 
-  u32x4 qf[4];
+  // Loads are unconditional (clamped addresses, results masked) so that no branch
+  // splits them.  The first round's table entries go first: they head the
+  // dependent chain table -> K/V.
+  int ent[kAttnBlocksPerWave];
+  {
+    const int e0 = sp * split_blocks + wave * kAttnBlocksPerWave;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    qf[s] = (col < group) ? q[((size_t)(bh * group + col) * queries) * 16 + 4 * s + grp]
-                          : u32x4{0u, 0u, 0u, 0u};
+    for (int a = 0; a < kAttnBlocksPerWave; ++a) {
+      const int e = e0 + a;
+      ent[a] = table[(size_t)bh * T + (e < tc ? e : tc - 1)];
+    }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // Columns past the group repeat the last query head; their results are never read.
+  u32x4 qf[4];
+  const int gq = col < group ? col : group - 1;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qf[s] = q[((size_t)(bh * group + gq) * queries) * 16 + 4 * s + grp];
+
   float m_run = -INFINITY;  // running max of scale*log2(e)*q.k for query head `col`
   float l_run = 0.f;        // this lane's share of the running sum
   floatx4 o[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) o[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int krow = 4 * (col & 3) + (col >> 2);  // token this lane feeds as an MFMA row
 
   for (int rd = 0; rd < rounds; ++rd) {
     const int e0 = sp * split_blocks + rd * kAttnBlocksPerRound + wave * kAttnBlocksPerWave;
     if (e0 >= tc) break;  // uniform across the wave
-    u32x4 kf[kAttnBlocksPerWave][4], vf[kAttnBlocksPerWave][4];
+    u32x4 kr[kAttnBlocksPerWave][4], vf[kAttnBlocksPerWave][4];
     int blk[kAttnBlocksPerWave];
+    if (rd > 0) {
 #pragma unroll
-    for (int a = 0; a < kAttnBlocksPerWave; ++a) {
-      const int e = e0 + a;
-      int id = (e < tc) ? table[(size_t)bh * T + e] : -1;
-      if (id < 0 || id >= NB || id * kBlock >= len) id = -1;
-      blk[a] = id;
-      const size_t base = ((size_t)bh * NB + (id < 0 ? 0 : id)) * (kBlock * 16);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        // K: token `col`, 16-byte chunk 4s + grp.  V: token 4*grp + s, chunk `col`.
-        kf[a][s] = (id >= 0) ? k[base + col * 16 + 4 * s + grp] : u32x4{0u, 0u, 0u, 0u};
-        vf[a][s] = (id >= 0) ? v[base + (4 * grp + s) * 16 + col] : u32x4{0u, 0u, 0u, 0u};
+      for (int a = 0; a < kAttnBlocksPerWave; ++a) {
+        const int e = e0 + a;
+        ent[a] = table[(size_t)bh * T + (e < tc ? e : tc - 1)];
       }
     }
 #pragma unroll
     for (int a = 0; a < kAttnBlocksPerWave; ++a) {
-      if (blk[a] < 0) continue;  // uniform across the wave
-      floatx4 st = {0.f, 0.f, 0.f, 0.f};
+      const int e = e0 + a;
+      int id = ent[a];
+      if (e >= tc || id < 0 || id >= NB || id * kBlock >= len) id = -1;
+      blk[a] = id;
+      const size_t base = ((size_t)bh * NB + (id < 0 ? 0 : id)) * (kBlock * 16) + lane;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[a][s]), as_bf16x8(qf[s]), st, 0, 0, 0);
+        kr[a][s] = __builtin_nontemporal_load(k + base + 64 * s);
+        vf[a][s] = __builtin_nontemporal_load(v + base + 64 * s);
       }
-      // st[i] = q[col] . k[token 4*grp + i]
-      const int tok0 = blk[a] * kBlock + 4 * grp;
-      float p[4];
+    }
+    // Keep every load of the round ahead of the arithmetic that consumes them.
+    __builtin_amdgcn_sched_barrier(0);
+    // Stage K: token 4s + grp, chunk col.
+#pragma unroll
+    for (int a = 0; a < kAttnBlocksPerWave; ++a) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        sm.kst[wave][a][(4 * s + grp) * kKRow + col] = kr[a][s];
+    }
+    __builtin_amdgcn_wave_barrier();
+    u32x4 kf[kAttnBlocksPerWave][4];
+#pragma unroll
+    for (int a = 0; a < kAttnBlocksPerWave; ++a) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        kf[a][s] = sm.kst[wave][a][krow * kKRow + 4 * s + grp];
+    }
+    __builtin_amdgcn_wave_barrier();
+    // V rows of tokens past the sequence (or of a skipped block) are zeroed: their
+    // probability is 0, but the memory behind them need not hold finite values.
+#pragma unroll
+    for (int a = 0; a < kAttnBlocksPerWave; ++a) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (blk[a] < 0 || blk[a] * kBlock + 4 * s + grp >= len) vf[a][s] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#if OASIS_ATTN_PV_BF16
+#pragma unroll
+    for (int a = 0; a < kAttnBlocksPerWave; a += 2) {
+      float p[2][4];
       float bm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = (tok0 + i < len) ? st[i] * scale_log2 : -INFINITY;
-        bm = fmaxf(bm, p[i]);
+      for (int h = 0; h < 2; ++h) {
+        floatx4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[a + h][s]), as_bf16x8(qf[s]), st,
+                                                       0, 0, 0);
+        }
+        // st[r] = q[col] . k[token 4r + grp]
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = blk[a + h] >= 0 && blk[a + h] * kBlock + 4 * r + grp < len;
+          p[h][r] = ok ? st[r] * scale_log2 : -INFINITY;
+          bm = fmaxf(bm, p[h][r]);
+        }
       }
       bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
       bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-      const float m_new = fmaxf(m_run, bm);  // finite: the block holds a valid token
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_new = fmaxf(m_run, bm);
+      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;  // no valid token yet: all weights 0
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+      // Each probability enters the bf16 PV product as two bf16 terms, hi = bf16(p)
+      // and lo = bf16(p - hi), so p is carried to about 2^-17 relative; the
+      // running sum adds the fp32 values.
+      uint32_t hw[4], lw[4];
       float psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(p[i] - m_new);
-        psum += p[i];
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(p[h][r] - m_ref);
+          const float p1 = __builtin_amdgcn_exp2f(p[h][r + 1] - m_ref);
+          psum += p0 + p1;
+          const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+          const __bf16 l0 = (__bf16)(p0 - (float)h0), l1 = (__bf16)(p1 - (float)h1);
+          hw[2 * h + r / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+          lw[2 * h + r / 2] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+        }
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
 #pragma unroll
       for (int t = 0; t < 8; ++t) o[t] *= alpha;
+      const u32x4 pb_hi = {hw[0], hw[1], hw[2], hw[3]};
+      const u32x4 pb_lo = {lw[0], lw[1], lw[2], lw[3]};
+      // Tile t: lane supplies head dim 8*col + t of tokens 4s + grp of both blocks.
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int w = t >> 1;
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+        u32x4 va;
+        va[0] = __builtin_amdgcn_perm(vf[a][1][w], vf[a][0][w], sel);
+        va[1] = __builtin_amdgcn_perm(vf[a][3][w], vf[a][2][w], sel);
+        va[2] = __builtin_amdgcn_perm(vf[a + 1][1][w], vf[a + 1][0][w], sel);
+        va[3] = __builtin_amdgcn_perm(vf[a + 1][3][w], vf[a + 1][2][w], sel);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb_hi), o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(pb_lo), o[t], 0, 0, 0);
+      }
+    }
+#else
+#pragma unroll
+    for (int a = 0; a < kAttnBlocksPerWave; ++a) {
+      floatx4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[a][s]), as_bf16x8(qf[s]), st, 0, 0, 0);
+      }
+      // st[r] = q[col] . k[token 4r + grp]
+      float p[4];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = blk[a] >= 0 && blk[a] * kBlock + 4 * r + grp < len;
+        p[r] = ok ? st[r] * scale_log2 : -INFINITY;
+        bm = fmaxf(bm, p[r]);
+      }
+      bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+      bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+      const float m_new = fmaxf(m_run, bm);
+      const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;  // no valid token yet: all weights 0
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_ref);
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(p[r] - m_ref);
+        psum += p[r];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[t] *= alpha;
+      // Step s contracts tokens 4s + (lane group): V element t of this lane's row, own p[s].
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -150,7 +294,9 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
         }
       }
     }
+#endif
   }
+  __syncthreads();  // the K staging area becomes the merge area
 
   // Merge the four waves in LDS.  o[t][r] holds head dim 32*grp + 8r + t of query head col.
   l_run += __shfl_xor(l_run, 16, 64);
@@ -162,7 +308,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) sm_o[wave][col][32 * grp + 8 * r + t] = o[t][r];
+    for (int t = 0; t < 8; ++t) sm.o[wave][col][32 * grp + 8 * r + t] = o[t][r];
   }
   __syncthreads();
   const size_t part = (size_t)bh * nsplit + sp;
@@ -176,7 +322,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w) {
         const float f = __builtin_amdgcn_exp2f(sm_m[w][g] - mx);
-        acc += f * sm_o[w][g][dd];
+        acc += f * sm.o[w][g][dd];
         lsum += f * sm_l[w][g];
       }
     }

@@ -26,63 +26,81 @@
 
 namespace oasis {
 
-constexpr int kScoreWaves = 4;          // waves per workgroup
-constexpr int kScoreBlocksPerWave = 32; // two 16-block MFMA tiles per wave
+#ifndef OASIS_SCORE_TILES_PER_WAVE
+#define OASIS_SCORE_TILES_PER_WAVE 2
+#endif
+constexpr int kScoreWaves = 4;                                   // waves per workgroup
+constexpr int kScoreTilesPerWave = OASIS_SCORE_TILES_PER_WAVE;   // 16-block MFMA tiles per wave
+constexpr int kScoreBlocksPerWG = kScoreWaves * kScoreTilesPerWave * 16;
 
+// The query fragments do not depend on the block, so the workgroup builds them once
+// in LDS (sign-split, in MFMA lane order) and every wave reads them from there.
 template <int RT>
 __global__ __launch_bounds__(256) void score_kernel(const u32x4* __restrict__ q,
                                                     const u32x4* __restrict__ summ,
                                                     const int32_t* __restrict__ seq_lens,
                                                     float* __restrict__ scores, int heads,
                                                     int max_blocks, int rows, int window) {
+  __shared__ u32x4 afrag[RT][8][64];
   const int bh = blockIdx.y;
   const int b = bh / heads;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int j0 = (blockIdx.x * kScoreWaves + wave) * kScoreBlocksPerWave;
-  if (j0 >= max_blocks) return;
+  const int jw = blockIdx.x * kScoreBlocksPerWG + wave * kScoreTilesPerWave * 16;  // this wave's first block
   const int len = clamp_len(seq_lens[b], max_blocks);
   const int n_cand = first_window_block(len, window);
   float* out = scores + (size_t)bh * max_blocks;
-  if (j0 >= n_cand) {  // no candidate in this wave's range
-    if (lane < kScoreBlocksPerWave && j0 + lane < max_blocks) out[j0 + lane] = -INFINITY;
+  if ((int)blockIdx.x * kScoreBlocksPerWG >= n_cand) {  // no candidate in this workgroup's range
+    for (int j = threadIdx.x; j < kScoreBlocksPerWG; j += blockDim.x) {
+      const int jb = blockIdx.x * kScoreBlocksPerWG + j;
+      if (jb < max_blocks) out[jb] = -INFINITY;
+    }
     return;
   }
 
-  // Summary fragments of both tiles first, so all 16 loads are in flight together.
-  u32x4 bv[2][8];
+  // Loads are issued unconditionally (clamped to valid addresses, results masked
+  // later) so that no branch or wait splits them: first this thread's query chunks,
+  // then the wave's summary fragments; the query fragments can then be built while
+  // the summaries are still in flight.
+  constexpr int kQPerThread = RT * 8 * 64 / 256;
+  const u32x4* qb = q + (size_t)bh * rows * 16;
+  u32x4 qv[kQPerThread];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int jb = j0 + 16 * t + col;
+  for (int u = 0; u < kQPerThread; ++u) {
+    const int f = u * 256 + threadIdx.x;
+    const int row = 16 * (f / 512) + (f & 15);
+    const int c = 4 * ((f / 64) % 8) + ((f & 63) >> 4);
+    qv[u] = qb[(row < rows ? row : rows - 1) * 16 + (c & 15)];
+  }
+  u32x4 bv[kScoreTilesPerWave][8];
+#pragma unroll
+  for (int t = 0; t < kScoreTilesPerWave; ++t) {
+    int jb = jw + 16 * t + col;
+    jb = jb < n_cand ? jb : n_cand - 1;  // n_cand >= 1 here; columns past it are masked below
     const size_t base = ((size_t)bh * max_blocks + jb) * 32 + grp;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      bv[t][s] = (jb < n_cand) ? summ[base + 4 * s] : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int s = 0; s < 8; ++s) bv[t][s] = summ[base + 4 * s];
   }
 
-  // Query fragments: row 16r + col, features of chunk 4s + grp, sign-split so
-  // that kmin chunks meet min(q,0) and kmax chunks meet max(q,0).
-  u32x4 av[RT][8];
-  const u32x4* qb = q + (size_t)bh * rows * 16;
+  // Query fragments: (row tile r, step s, lane) holds row 16r + lane%16, features of
+  // chunk 4s + lane/16, sign-split so that kmin chunks (s < 4) meet min(q,0) and kmax
+  // chunks meet max(q,0); rows past the real ones are zero.
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int row = 16 * r + col;
+  for (int u = 0; u < kQPerThread; ++u) {
+    const int f = u * 256 + threadIdx.x;
+    const int r = f / 512, st = (f / 64) % 8, l = f & 63;
+    u32x4 x = qv[u];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int c = 4 * s + grp;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < rows) {
-        x = qb[row * 16 + (c & 15)];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = (s < 4) ? bf16x2_neg_part(x[e]) : bf16x2_pos_part(x[e]);
-      }
-      av[r][s] = x;
-    }
+    for (int e = 0; e < 4; ++e) x[e] = (st < 4) ? bf16x2_neg_part(x[e]) : bf16x2_pos_part(x[e]);
+    if (16 * r + (l & 15) >= rows) x = u32x4{0u, 0u, 0u, 0u};
+    afrag[r][st][l] = x;
   }
+  __syncthreads();
 
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kScoreTilesPerWave; ++t) {
+    const int jb = jw + 16 * t + col;
+    if (jw + 16 * t >= max_blocks) break;  // uniform across the wave
     floatx4 acc[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -90,12 +108,12 @@ __global__ __launch_bounds__(256) void score_kernel(const u32x4* __restrict__ q,
     for (int s = 0; s < 8; ++s) {
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[r][s]), as_bf16x8(bv[t][s]),
-                                                         acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(afrag[r][s][lane]),
+                                                         as_bf16x8(bv[t][s]), acc[r], 0, 0, 0);
       }
     }
-    // Lane l holds rows 16r + 4*(l/16) + i of block column l%16: max over its
-    // real rows, then across the four lane groups of the column.
+    // Lane l holds rows 16r + 4*(l/16) + i of block column l%16: max over its real
+    // rows, then across the four lane groups of the column.
     float m = -INFINITY;
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
@@ -106,7 +124,6 @@ __global__ __launch_bounds__(256) void score_kernel(const u32x4* __restrict__ q,
     }
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
-    const int jb = j0 + 16 * t + col;
     if (grp == 0 && jb < max_blocks) out[jb] = (jb < n_cand) ? m : -INFINITY;
   }
 }
@@ -114,8 +131,7 @@ __global__ __launch_bounds__(256) void score_kernel(const u32x4* __restrict__ q,
 hipError_t launch_score(const Dims& d, const void* q, const void* summ, const int32_t* seq_lens,
                         float* scores, hipStream_t stream) {
   const int rows = d.group * d.queries;
-  const int per_wg = kScoreWaves * kScoreBlocksPerWave;
-  const dim3 grid((d.max_blocks + per_wg - 1) / per_wg, d.batch * d.heads);
+  const dim3 grid((d.max_blocks + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG, d.batch * d.heads);
   const dim3 block(64 * kScoreWaves);
   const u32x4* qq = (const u32x4*)q;
   const u32x4* ss = (const u32x4*)summ;
