@@ -1,0 +1,40 @@
+"""Byte accounting of the benchmark, pinned to the pages' worked capacity example."""
+import json
+import math
+import os
+
+import torch
+
+import bench
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_kv_capacity_worked_example():
+    with open(os.path.join(GOLDEN, "eq1_kv_capacity.json")) as f:
+        ex = json.load(f)
+    per_request = bench.kv_cache_bytes(1, ex["context_tokens"], ex["layers"], ex["kv_heads"],
+                                       ex["head_dim"], ex["bytes_per_elem"])
+    assert round(per_request / 1e9, 1) == ex["printed_gb_per_request"]
+    assert math.floor(ex["hbm_bytes_for_kv"] / per_request) == ex["printed_b_max"]
+
+
+def test_per_block_units_are_one_instance_of_the_capacity_formula():
+    # one 16-token block of one KV head of one layer: the capacity formula with B = 1,
+    # L = 16, N_layer = 1, N_kv = 1, d_h = 128, s = 2
+    assert bench.BLOCK_KV_BYTES == bench.kv_cache_bytes(1, 16, 1, 1, 128, 2)
+    # the summary of a block is 1/16 of its K+V bytes
+    assert bench.SUMMARY_BYTES * 16 == bench.BLOCK_KV_BYTES
+
+
+def test_algorithmic_bytes_by_hand():
+    w = synth.WORKLOADS["tiny_4k"]
+    lens = torch.tensor([4096])
+    tc = torch.tensor([[20, 20]])
+    nb = bench.algorithmic_bytes(w, lens, tc)
+    cand = (4096 - 64) // 16 * 2                           # 252 candidate blocks x 2 heads
+    assert nb["units"] == {"candidate_block_heads": cand, "table_blocks": 40}
+    q_all = 1 * 2 * 4 * 4 * 256
+    out = 1 * 2 * 4 * 129 * 4
+    assert nb["step"] == cand * 512 + 40 * 8192 + q_all + out
