@@ -109,6 +109,8 @@ def main(argv=None) -> int:
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--stage-steps", type=int, default=300, help="evented steps for per-kernel times")
+    ap.add_argument("--chunks", type=int, default=1,
+                    help="runs of sequences issued on separate streams (oasis_decode_step_pipelined)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -145,7 +147,7 @@ def main(argv=None) -> int:
     buffers = oa.StepBuffers(d, dev)
     res_next = torch.empty_like(sets[0]["resident"])
     steps = [oa.PreparedStep(d, s["q"], s["summ"], s["k"], s["v"], s["seq_lens"], s["resident"],
-                             buffers, resident_next=res_next) for s in sets]
+                             buffers, resident_next=res_next, chunks=args.chunks) for s in sets]
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -232,7 +234,7 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.num_kv_heads, "group": w.group,
                    "context": w.ctx, "queries_per_head": w.queries, "top_k": w.top_k,
                    "window_tokens": w.window, "fetch_ratio": w.fetch_ratio, "cap": w.cap,
-                   "input_sets": n_sets, "mode": args.mode},
+                   "input_sets": n_sets, "mode": args.mode, "chunks": args.chunks},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "bytes_per_launch": nb[dominant],

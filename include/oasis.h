@@ -218,6 +218,27 @@ oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void
                                int32_t* table, int32_t* table_count, float scale, float* out,
                                float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* oasis_decode_step with the batch cut into n_chunks runs of sequences whose
+ * kernels go to different streams, so that one run's latency-bound selection and
+ * merge overlap another run's HBM-bound scoring and attention.  Run 0 uses
+ * `stream`; run c > 0 uses aux_streams[(c - 1) % n_aux].  The auxiliary streams
+ * first wait for the work already queued on `stream` (events[0]) and `stream`
+ * finally waits for all of them (events[1 .. n_aux]), so to the caller the call
+ * behaves like oasis_decode_step on `stream` (also under HIP graph capture).
+ * Streams and events are the caller's (hipStreamCreate / hipEventCreate, default
+ * priority); none is created or destroyed here.  n_chunks is clamped to B; with
+ * n_chunks == 1 the auxiliary arguments are ignored.  Results are identical to
+ * oasis_decode_step's. */
+oasis_status oasis_decode_step_pipelined(const oasis_dims* dims, const void* q, const void* summ,
+                                         const void* k, const void* v, const int32_t* seq_lens,
+                                         float* scores, int32_t* topk, int32_t* resident,
+                                         int32_t* resident_next, int32_t* plan,
+                                         int32_t* plan_count, int32_t* table,
+                                         int32_t* table_count, float scale, float* out, float* lse,
+                                         void* ws, size_t ws_bytes, hipStream_t stream,
+                                         int32_t n_chunks, hipStream_t* aux_streams, int32_t n_aux,
+                                         hipEvent_t* events, int32_t n_events);
+
 /* oasis_decode_step with timing markers, for measurement: events[0..4]
  * (created by the caller with hipEventCreate) are recorded on `stream` before
  * the scoring kernel, after it, after the selection-and-plan kernel, after the

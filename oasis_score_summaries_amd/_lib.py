@@ -68,6 +68,11 @@ _SIGNATURES = {
     "oasis_decode_step_timed": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P,
                                                ctypes.POINTER(ctypes.c_void_p)]),
+    "oasis_decode_step_pipelined": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                   _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t,
+                                                   _P, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                                   ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                                   ctypes.c_int32]),
 }
 
 _lib = None
@@ -361,6 +366,8 @@ def _hip_runtime() -> ctypes.CDLL:
         h.hipEventSynchronize.restype = ctypes.c_int
         h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         h.hipEventElapsedTime.restype = ctypes.c_int
+        h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        h.hipEventCreateWithFlags.restype = ctypes.c_int
         _hip = h
     return _hip
 
@@ -402,16 +409,40 @@ class StageEvents:
             pass
 
 
+class SyncEvents:
+    """HIP events without timing, for fork/join ordering between streams."""
+
+    def __init__(self, n: int):
+        h = _hip_runtime()
+        self.n = n
+        self.handles = (ctypes.c_void_p * max(1, n))()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if h.hipEventCreateWithFlags(ctypes.byref(ev), 0x2) != 0:  # hipEventDisableTiming
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.handles[i] = ev.value
+
+    def __del__(self):
+        try:
+            h = _hip_runtime()
+            for i in range(self.n):
+                if self.handles[i]:
+                    h.hipEventDestroy(self.handles[i])
+        except Exception:
+            pass
+
+
 class PreparedStep:
     """One fused decode step whose arguments are checked and marshalled once.
 
-    Calling it queues oasis_decode_step on the current stream (or, with
-    ``events``, oasis_decode_step_timed).  The tensors must stay alive and keep
-    their storage while the object is used.
+    Calling it queues oasis_decode_step on the current stream (with ``events``,
+    oasis_decode_step_timed; with ``chunks`` > 1, oasis_decode_step_pipelined on
+    ``chunks`` - 1 auxiliary streams owned by this object).  The tensors must stay
+    alive and keep their storage while the object is used.
     """
 
     def __init__(self, dims: OasisDims, q, summ, k, v, seq_lens, resident, buffers: StepBuffers,
-                 resident_next=None, scale: Optional[float] = None):
+                 resident_next=None, scale: Optional[float] = None, chunks: int = 1):
         s = _shapes(dims)
         _need(q, "q", torch.bfloat16, s["q"], align=16)
         dev = q.device
@@ -438,11 +469,19 @@ class PreparedStep:
                      _ptr(b.table_count), ctypes.c_float(scale), _ptr(b.out), _ptr(b.lse), _ptr(b.ws),
                      ctypes.c_size_t(b.ws.numel())]
         self.lib = load()
+        self.chunks = max(1, min(int(chunks), dims.batch))
+        self.aux = [torch.cuda.Stream(device=dev) for _ in range(self.chunks - 1)]
+        self.aux_handles = (ctypes.c_void_p * max(1, len(self.aux)))(*[s.cuda_stream for s in self.aux])
+        self.sync = SyncEvents(len(self.aux) + 1 if self.aux else 0)
 
     def __call__(self, stream=None, events: Optional[StageEvents] = None) -> None:
         st = _stream(stream)
-        if events is None:
-            _check(self.lib.oasis_decode_step(*self.args, st), "oasis_decode_step")
-        else:
+        if events is not None:
             _check(self.lib.oasis_decode_step_timed(*self.args, st, events.handles),
                    "oasis_decode_step_timed")
+        elif self.chunks > 1:
+            _check(self.lib.oasis_decode_step_pipelined(
+                *self.args, st, self.chunks, self.aux_handles, len(self.aux), self.sync.handles,
+                self.sync.n), "oasis_decode_step_pipelined")
+        else:
+            _check(self.lib.oasis_decode_step(*self.args, st), "oasis_decode_step")

@@ -62,13 +62,21 @@ AttnSplit attn_split(int table_stride) {
   return s;
 }
 
-// Workspace: the partial outputs, then (max, sum) pairs.
+// Workspace: one record per (sequence, KV head, split, query head): the unnormalised
+// output (128 floats), the running max (log2 units), the sum, and padding to 16
+// bytes.  Records of one (sequence, KV head) are contiguous, so a run of sequences
+// owns a contiguous slice of the workspace.
+constexpr int kRec = kHeadDim + 4;
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t attn_workspace_bytes(const Dims& d, int table_stride) {
   const AttnSplit s = attn_split(table_stride);
-  const size_t parts = (size_t)d.batch * d.heads * s.num_splits * d.group;
-  return align256(parts * (kHeadDim + 2) * sizeof(float));
+  return align256((size_t)d.batch * d.heads * s.num_splits * d.group * kRec * sizeof(float));
+}
+
+size_t attn_workspace_bytes_per_sequence(const Dims& d, int table_stride) {
+  const AttnSplit s = attn_split(table_stride);
+  return (size_t)d.heads * s.num_splits * d.group * kRec * sizeof(float);
 }
 
 __device__ inline float bf16_elem(const u32x4& v, int e) {
@@ -90,8 +98,8 @@ constexpr int kKRow = kHeadDim * 2 / 16 + 1;  // padded LDS row of one K token, 
 __global__ __launch_bounds__(256) void attn_split_kernel(
     const u32x4* __restrict__ q, const u32x4* __restrict__ k, const u32x4* __restrict__ v,
     const int32_t* __restrict__ table, const int32_t* __restrict__ table_count, int T,
-    const int32_t* __restrict__ seq_lens, float scale_log2, float* __restrict__ part_o,
-    float* __restrict__ part_ml, int heads, int group, int queries, int NB, int nsplit, int rounds) {
+    const int32_t* __restrict__ seq_lens, float scale_log2, float* __restrict__ part,
+    int heads, int group, int queries, int NB, int nsplit, int rounds) {
   __shared__ float sm_m[kAttnWaves][16];
   __shared__ float sm_l[kAttnWaves][16];
   // K staging during the rounds, then the cross-wave merge of the outputs.
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
     for (int t = 0; t < 8; ++t) sm.o[wave][col][32 * grp + 8 * r + t] = o[t][r];
   }
   __syncthreads();
-  const size_t part = (size_t)bh * nsplit + sp;
+  float* rec0 = part + ((size_t)bh * nsplit + sp) * group * kRec;
   for (int idx = threadIdx.x; idx < group * kHeadDim; idx += blockDim.x) {
     const int g = idx / kHeadDim, dd = idx % kHeadDim;
     float mx = -INFINITY;
@@ -326,10 +334,11 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
         lsum += f * sm_l[w][g];
       }
     }
-    part_o[(part * group + g) * kHeadDim + dd] = acc;
+    float* rec = rec0 + g * kRec;
+    rec[dd] = acc;
     if (dd == 0) {
-      part_ml[(part * group + g) * 2 + 0] = mx;
-      part_ml[(part * group + g) * 2 + 1] = lsum;
+      rec[kHeadDim + 0] = mx;
+      rec[kHeadDim + 1] = lsum;
     }
   }
 }
@@ -338,8 +347,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(
 // split s's (max, sum) so the weights come from two DPP wave reductions; then
 // every thread sums its float4 of the output over the splits with all loads issued
 // before the first add.
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_ml,
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part,
                                                          const int32_t* __restrict__ table_count,
                                                          int T, int group, int nsplit,
                                                          int split_blocks, float* __restrict__ out,
@@ -351,12 +359,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   int tc = table_count[bh];
   tc = tc < 0 ? 0 : (tc > T ? T : tc);
   const int nvalid = (tc + split_blocks - 1) / split_blocks;  // <= nsplit <= kAttnMaxSplits
-  const size_t part0 = (size_t)bh * nsplit;
+  const float* head = part + (size_t)bh * nsplit * group * kRec;
   for (int g = wave; g < group; g += kAttnWaves) {
     float m = -INFINITY, l = 0.f;
     if (lane < nvalid) {
-      m = part_ml[((part0 + lane) * group + g) * 2 + 0];
-      l = part_ml[((part0 + lane) * group + g) * 2 + 1];
+      m = head[((size_t)lane * group + g) * kRec + kHeadDim + 0];
+      l = head[((size_t)lane * group + g) * kRec + kHeadDim + 1];
     }
     const float mx = wave_max_f32(m);
     const float w = (mx == -INFINITY || lane >= nvalid) ? 0.f : __builtin_amdgcn_exp2f(m - mx);
@@ -368,19 +376,20 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
     }
   }
   __syncthreads();
-  const floatx4* po = (const floatx4*)part_o;
   for (int idx = threadIdx.x; idx < group * (kHeadDim / 4); idx += blockDim.x) {
     const int g = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
+    const floatx4* po = (const floatx4*)(head + (size_t)g * kRec) + d4;
+    const size_t stride4 = (size_t)group * kRec / 4;  // records of consecutive splits
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
     int s = 0;
     for (; s + 8 <= nvalid; s += 8) {
       floatx4 x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = po[((part0 + s + u) * group + g) * (kHeadDim / 4) + d4];
+      for (int u = 0; u < 8; ++u) x[u] = po[(size_t)(s + u) * stride4];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc += sm_w[s + u][g] * x[u];
     }
-    for (; s < nvalid; ++s) acc += sm_w[s][g] * po[((part0 + s) * group + g) * (kHeadDim / 4) + d4];
+    for (; s < nvalid; ++s) acc += sm_w[s][g] * po[(size_t)s * stride4];
     const float sum = sm_sum[g];
     const bool any = sm_mx[g] != -INFINITY && sum > 0.f;
     floatx4* o4 = (floatx4*)(out + ((size_t)bh * group + g) * kHeadDim);
@@ -396,12 +405,9 @@ hipError_t launch_attention_split(const Dims& d, const void* q, const void* k, c
                                   int table_stride, const int32_t* seq_lens, float scale, void* ws,
                                   hipStream_t stream) {
   const AttnSplit s = attn_split(table_stride);
-  const size_t parts = (size_t)d.batch * d.heads * s.num_splits * d.group;
-  float* part_o = (float*)ws;
-  float* part_ml = part_o + parts * kHeadDim;
   attn_split_kernel<<<dim3(s.num_splits, d.batch * d.heads), dim3(64 * kAttnWaves), 0, stream>>>(
       (const u32x4*)q, (const u32x4*)k, (const u32x4*)v, table, table_count, table_stride, seq_lens,
-      scale * kLog2e, part_o, part_ml, d.heads, d.group, d.queries, d.max_blocks, s.num_splits,
+      scale * kLog2e, (float*)ws, d.heads, d.group, d.queries, d.max_blocks, s.num_splits,
       s.blocks_per_split / kAttnBlocksPerRound);
   return hipGetLastError();
 }
@@ -409,11 +415,8 @@ hipError_t launch_attention_split(const Dims& d, const void* q, const void* k, c
 hipError_t launch_attention_merge(const Dims& d, const int32_t* table_count, int table_stride,
                                   float* out, float* lse, const void* ws, hipStream_t stream) {
   const AttnSplit s = attn_split(table_stride);
-  const size_t parts = (size_t)d.batch * d.heads * s.num_splits * d.group;
-  const float* part_o = (const float*)ws;
-  const float* part_ml = part_o + parts * kHeadDim;
   attn_merge_kernel<<<dim3(d.batch * d.heads), dim3(64 * kAttnWaves), 0, stream>>>(
-      part_o, part_ml, table_count, table_stride, d.group, s.num_splits, s.blocks_per_split, out, lse);
+      (const float*)ws, table_count, table_stride, d.group, s.num_splits, s.blocks_per_split, out, lse);
   return hipGetLastError();
 }
 

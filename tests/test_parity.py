@@ -407,3 +407,70 @@ def test_no_candidates_and_short_sequences(lib):
             exp = oracle_head(q, k, v, L, resident[b, h].numpy(), K, W, w.cap, default_scale(), b, h)
             np.testing.assert_array_equal(i64(got["table"][b, h]), exp["table"])
             np.testing.assert_allclose(f64(got["out"][b, h]), exp["out"], rtol=0, atol=OUT_ATOL)
+
+
+# ---------------------------------------------------------------------------
+# Pipelined (multi-stream) step and HIP graph replay
+# ---------------------------------------------------------------------------
+
+def _prepared_inputs(lib, w, seed_layer=0):
+    inp = {k: v.to(DEV) for k, v in synth.generate(w, "cpu", layer=seed_layer).items()}
+    d = lib.dims_for(w)
+    summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
+    n_cand = [ref.first_window_block(int(x), w.window) for x in inp["seq_lens"].cpu()]
+    res = torch.stack([torch.stack([synth.random_resident(w.top_k, n_cand[b], 3, 10 * b + h)
+                                    for h in range(w.num_kv_heads)]) for b in range(w.batch)]).to(DEV)
+    return d, inp, summ, res
+
+
+@pytest.mark.parametrize("chunks", [2, 3, 8])
+def test_pipelined_step_matches_plain_step(lib, chunks):
+    w = synth.WORKLOADS["tiny_4k"].with_(batch=5, num_kv_heads=3, fetch_ratio=0.25, ctx=4096 + 40,
+                                         min_len=1000)
+    _say(f"pipelined chunks={chunks}")
+    d, inp, summ, res = _prepared_inputs(lib, w)
+    outs = []
+    for c in (1, chunks):
+        bufs = lib.StepBuffers(d, DEV)
+        rn = torch.empty_like(res)
+        st = lib.PreparedStep(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, bufs,
+                              resident_next=rn, chunks=c)
+        st()
+        torch.cuda.synchronize()
+        outs.append({**{k: v.clone() for k, v in bufs.as_dict().items()}, "resident": rn.clone()})
+    for key in outs[0]:
+        assert torch.equal(outs[0][key], outs[1][key]), key
+
+
+@pytest.mark.parametrize("chunks", [1, 4])
+def test_graph_replay_matches_eager(lib, chunks):
+    """Every replay of a captured step, with eager work and syncs between replays,
+    gives the eager result bit for bit."""
+    w = synth.WORKLOADS["tiny_4k"].with_(batch=4, fetch_ratio=0.25)
+    _say(f"graph replay chunks={chunks}")
+    d, inp, summ, res = _prepared_inputs(lib, w, seed_layer=3)
+    bufs = lib.StepBuffers(d, DEV)
+    rn = torch.empty_like(res)
+    st = lib.PreparedStep(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, bufs,
+                          resident_next=rn, chunks=chunks)
+    st()
+    torch.cuda.synchronize()
+    eager = {**{k: v.clone() for k, v in bufs.as_dict().items()}, "resident": rn.clone()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st()
+    for rep in range(4):
+        for t in list(bufs.as_dict().values()) + [rn]:
+            t.fill_(-7 if t.dtype == torch.int32 else float("nan"))   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = {**bufs.as_dict(), "resident": rn}
+        for key in eager:
+            assert torch.equal(eager[key], got[key]), f"replay {rep}: {key}"
