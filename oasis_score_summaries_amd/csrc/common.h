@@ -135,9 +135,7 @@ __device__ inline float wave_sum_f32(float x) {
 __device__ inline int wave_flag_rank(bool flag, int* count) {
   const uint64_t m = __ballot(flag);
   *count = __popcll(m);
-  const int lane = threadIdx.x & 63;
-  const uint64_t below = lane == 0 ? 0ull : (m & ((~0ull) >> (64 - lane)));
-  return __popcll(below);
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // ---- wave64 / workgroup scans -----------------------------------------------------

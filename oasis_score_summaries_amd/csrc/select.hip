@@ -23,8 +23,11 @@
 //     pass, per-wave LDS histograms (no cross-wave atomic contention), a DPP
 //     prefix sum over the 256 digits, and an early exit once the threshold
 //     digit holds exactly the keys still needed;
-//   * the ties of the threshold key are taken in index order with ballot ranks;
-//   * the K winners are rank-sorted in LDS;
+//   * fast path: when the first pass's threshold digit holds few keys, the keys at
+//     or above it are dropped into per-digit buckets and ranked inside their bucket
+//     only, which yields the sorted selection at once;
+//   * otherwise the ties of the threshold key are taken in index order with ballot
+//     ranks and the K winners are rank-sorted in LDS;
 //   * the plan uses LDS bitmaps for set membership and ballot ranks for every
 //     compaction, so every output position is a pure function of the inputs.
 #include "common.h"
@@ -32,28 +35,51 @@
 
 namespace oasis {
 
+// Bucket-placement fast path: taken when the threshold digit of the first radix
+// pass holds at most this many keys.
+constexpr int kBucketMax = 256;
+
 template <int THREADS, int ITEMS>
 struct SelectShared {
   static constexpr int NW = THREADS / 64;
   uint32_t hist[2][NW][256];
   int scan[2][NW];
   uint32_t rmax[NW], rmin[NW];
+  int start[256];                           // keys with a larger first-pass digit
+  int fill[256];                            // per-digit placement counters
   int cnt[ITEMS * NW];          // packed (> threshold) << 16 | (== threshold) counts per (item, wave)
-  alignas(16) uint64_t cand[kMaxTopK];  // (key << 32) | ~index: larger is better, all distinct
+  // The fast path uses `bucket` (+32: reads past a bucket's end stay inside), the
+  // radix path `cand`: (key << 32) | ~index, larger is better, all distinct.
+  union {
+    alignas(16) uint64_t bucket[kMaxTopK + kBucketMax + 32];
+    alignas(16) uint64_t cand[kMaxTopK + 32];
+  };
   int sorted_idx[kMaxTopK];
   uint32_t sel_digit;
   int sel_above, sel_count, n_gt;
 };
 
+// Set-membership bitmaps of the plan (bit j of word j / 32: block j is selected /
+// resident).  Kept outside the selection's LDS so that they can be cleared while the
+// selection runs.
+struct PlanBitmaps {
+  uint32_t sel[kMaxBlocks / 32];
+  uint32_t res[kMaxBlocks / 32];
+};
+__device__ inline void clear_bitmaps(PlanBitmaps& bm, int NB) {
+  for (int w = threadIdx.x; w < (NB + 31) >> 5; w += blockDim.x) {
+    bm.sel[w] = 0u;
+    bm.res[w] = 0u;
+  }
+}
+
 template <int THREADS>
 struct PlanShared {
   static constexpr int NW = THREADS / 64;
-  uint32_t bm_sel[kMaxBlocks / 32];
-  uint32_t bm_res[kMaxBlocks / 32];
-  alignas(16) uint64_t st[THREADS];  // stale slots: (order_key(score) << 32) | ~block, others all ones
-  int adm_list[THREADS];
+  alignas(16) uint64_t st[THREADS + 32];  // stale slots, compacted: (order_key(score) << 32) | ~block
+  alignas(16) int adm_list[THREADS + 16];
   int adm_sorted[THREADS];
-  int w_new[NW], w_empty[NW], w_vict[NW], w_tab[NW];
+  int w_new[NW], w_empty[NW], w_stale[NW], w_vict[NW], w_tab[NW];
 };
 
 // Inclusive prefix sum over the threads of the workgroup; `scratch` holds NW ints
@@ -90,49 +116,32 @@ __device__ inline int waves_before(const int* wcount, int* total) {
   return before;
 }
 
-// Number of entries of v[0 .. n) greater than x (n even or odd; v 16-byte aligned).
-__device__ inline int rank_above(const uint64_t* v, int n, uint64_t x) {
+// Number of entries of v[0 .. n) greater (ABOVE) or smaller (!ABOVE) than x.  v is
+// 16-byte aligned and holds, from n up to the next multiple of 32, entries that never
+// count (0 when counting larger ones, all ones when counting smaller ones), so the
+// loop needs no per-entry bound; 32 entries are read per wait.
+template <bool ABOVE>
+__device__ inline int count_cmp(const uint64_t* v, int n, uint64_t x) {
   int rank = 0;
-  const int n2 = n & ~1;
-  int u = 0;
-  for (; u + 8 <= n2; u += 8) {
-    uint64_t a[8];
+  for (int u = 0; u < n; u += 32) {
+    u32x4 w[16];
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      const u32x4 w = *(const u32x4*)(v + u + j);
-      a[j] = ((uint64_t)w.y << 32) | w.x;
-      a[j + 1] = ((uint64_t)w.w << 32) | w.z;
+    for (int j = 0; j < 16; ++j) w[j] = *(const u32x4*)(v + u + 2 * j);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint64_t a = ((uint64_t)w[j].y << 32) | w[j].x;
+      const uint64_t b = ((uint64_t)w[j].w << 32) | w[j].z;
+      rank += ABOVE ? (a > x) : (a < x);
+      rank += ABOVE ? (b > x) : (b < x);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) rank += a[j] > x;
   }
-  for (; u < n; ++u) rank += v[u] > x;
-  return rank;
-}
-// Number of entries of v[0 .. n) smaller than x.
-__device__ inline int rank_below(const uint64_t* v, int n, uint64_t x) {
-  int rank = 0;
-  const int n2 = n & ~1;
-  int u = 0;
-  for (; u + 8 <= n2; u += 8) {
-    uint64_t a[8];
-#pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      const u32x4 w = *(const u32x4*)(v + u + j);
-      a[j] = ((uint64_t)w.y << 32) | w.x;
-      a[j + 1] = ((uint64_t)w.w << 32) | w.z;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) rank += a[j] < x;
-  }
-  for (; u < n; ++u) rank += v[u] < x;
   return rank;
 }
 
 // Selects the min(K, n_cand) best of row[0 .. n_cand) into sh.sorted_idx, best
 // first, and returns that count.  Every thread of the workgroup must call it.
 template <int THREADS, int ITEMS>
-__device__ int topk_select(const float* __restrict__ row, int n_cand, int K,
+__device__ __attribute__((always_inline)) int topk_select(const float* __restrict__ row, int n_cand, int K,
                            SelectShared<THREADS, ITEMS>& sh) {
   constexpr int NW = THREADS / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -202,7 +211,50 @@ __device__ int topk_select(const float* __restrict__ row, int n_cand, int K,
         sh.sel_above = excl;
         sh.sel_count = cnt;
       }
+      if (pass == 0 && tid < 256) {
+        sh.start[digit] = excl;
+        sh.fill[digit] = 0;
+      }
       __syncthreads();
+      if (pass == 0 && sh.sel_count <= kBucketMax) {
+        // Fast path.  Every key whose first-pass digit is at least the threshold digit
+        // d0 goes to its digit's bucket; buckets are laid out from the largest digit
+        // down, bucket d starting at start[d], so the placed keys occupy
+        // [0, above + count(d0)).  A key's rank among the larger composites of its own
+        // bucket then gives its final position; of the threshold bucket the keys with
+        // rank below the number still needed are taken.
+        const uint32_t d0 = sh.sel_digit;
+#pragma unroll
+        for (int i = 0; i < ITEMS; ++i) {
+          const int e = i * THREADS + tid;
+          const uint32_t dg = (key[i] >> lo) & dmask;
+          if (e < n_cand && dg >= d0) {
+            const int slot = (int)atomicAdd((uint32_t*)&sh.fill[dg], 1u);
+            sh.bucket[sh.start[dg] + slot] = ((uint64_t)key[i] << 32) | (uint32_t)(~(uint32_t)e);
+          }
+        }
+        __syncthreads();
+        const int above = sh.sel_above;
+        const int need = krem - above;
+        const int placed = above + sh.sel_count;
+        for (int t = tid; t < placed; t += THREADS) {
+          const uint64_t c = sh.bucket[t];
+          const uint32_t dg = ((uint32_t)(c >> 32) >> lo) & dmask;
+          const int b0 = sh.start[dg], nb = sh.fill[dg];
+          int r = 0;
+          for (int u = 0; u < nb; u += 16) {  // 16 reads in flight per wait
+            uint64_t a[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) a[j] = sh.bucket[b0 + u + j];  // padded: stays in the array
+#pragma unroll
+            for (int j = 0; j < 16; ++j) r += (u + j < nb) && a[j] > c;
+          }
+          const int pos = dg > d0 ? b0 + r : (r < need ? above + r : -1);
+          if (pos >= 0) sh.sorted_idx[pos] = (int)(~(uint32_t)c);
+        }
+        __syncthreads();
+        return m;
+      }
       prefix |= sh.sel_digit << lo;
       krem -= sh.sel_above;
       const int count = sh.sel_count;
@@ -247,66 +299,80 @@ __device__ int topk_select(const float* __restrict__ row, int n_cand, int K,
     const int r = (base & 0xffff) + re;
     if (eq && r < krem) sh.cand[n_gt + r] = comp;
   }
+  if (tid >= m && tid < ((m + 31) & ~31)) sh.cand[tid] = 0ull;  // never larger than a key
   __syncthreads();
   // Rank sort of the m winners: rank = number of larger composites.  The loop reads
   // LDS 16 bytes at a time, several reads in flight.
   for (int t = tid; t < m; t += THREADS) {
     const uint64_t ct = sh.cand[t];
-    sh.sorted_idx[rank_above(sh.cand, m, ct)] = (int)(~(uint32_t)ct);
+    sh.sorted_idx[count_cmp<true>(sh.cand, m, ct)] = (int)(~(uint32_t)ct);
   }
   __syncthreads();
   return m;
 }
 
+// The resident slot a thread t < K owns (-1 for the other threads) and that block's
+// score (-inf when the block is out of range).  Loaded by the caller before the
+// selection so that the latency overlaps it.
+struct ResidentSlot {
+  int block;
+  float score;
+};
+__device__ inline ResidentSlot load_resident_slot(const int32_t* res, const float* __restrict__ srow,
+                                                  int K, int NB) {
+  const int tid = threadIdx.x;
+  const int r = tid < K ? res[tid] : -1;
+  const bool ok = r >= 0 && r < NB;
+  return ResidentSlot{r, srow[ok ? r : 0]};
+}
+
 // Applies the capped-eviction rule for one (sequence, KV head).  Thread t < K passes
-// selection entry t as `s_i` (-1 = none; the entries are best first); `res` holds the
-// resident slots; the updated slots go to `res_next` (may equal `res`).  Needs
-// K <= THREADS; every thread calls it.
+// selection entry t as `s_i` (-1 = none; the entries are best first) and resident slot
+// t as `rs`; the updated slots go to `res_next`.  `bm` must have been cleared, with a
+// barrier since.  Needs K <= THREADS; every thread calls it.
 template <int THREADS>
-__device__ void plan_apply(const float* __restrict__ srow, int s_i, const int32_t* res,
-                           int32_t* res_next, int32_t* plan_row, int32_t* plan_count,
-                           int32_t* table_row, int32_t* table_count, int K, int C, int NB, int w0,
-                           int nblk, int T, PlanShared<THREADS>& sh) {
+__device__ __attribute__((always_inline)) void plan_apply(
+    int s_i, ResidentSlot rs, int32_t* res_next, int32_t* plan_row, int32_t* plan_count,
+    int32_t* table_row, int32_t* table_count, int K, int C, int NB, int w0, int nblk, int T,
+    PlanBitmaps& bm, PlanShared<THREADS>& sh) {
   constexpr int NW = THREADS / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int nwords = (NB + 31) >> 5;
-  for (int w = tid; w < nwords; w += THREADS) {
-    sh.bm_sel[w] = 0u;
-    sh.bm_res[w] = 0u;
-  }
-  int r_i = -1;
-  if (tid < K) r_i = res[tid];
-  else s_i = -1;
-  __syncthreads();
+  const int r_i = rs.block;
+  if (tid >= K) s_i = -1;
   const bool s_ok = s_i >= 0 && s_i < NB;
   const bool r_ok = r_i >= 0 && r_i < NB;
-  if (s_ok) atomicOr(&sh.bm_sel[s_i >> 5], 1u << (s_i & 31));
-  if (r_ok) atomicOr(&sh.bm_res[r_i >> 5], 1u << (r_i & 31));
+  if (s_ok) atomicOr(&bm.sel[s_i >> 5], 1u << (s_i & 31));
+  if (r_ok) atomicOr(&bm.res[r_i >> 5], 1u << (r_i & 31));
   __syncthreads();
 
   // New blocks (selection order) and empty slots (slot order): ballot ranks.
-  const bool is_new = s_ok && !((sh.bm_res[s_i >> 5] >> (s_i & 31)) & 1u);
+  const bool is_new = s_ok && !((bm.res[s_i >> 5] >> (s_i & 31)) & 1u);
   const bool empty = tid < K && r_i < 0;
-  const bool stale = tid < K && r_i >= 0 && !(r_ok && ((sh.bm_sel[r_i >> 5] >> (r_i & 31)) & 1u));
-  int c_new, c_empty;
+  const bool stale = tid < K && r_i >= 0 && !(r_ok && ((bm.sel[r_i >> 5] >> (r_i & 31)) & 1u));
+  int c_new, c_empty, c_stale;
   const int rk_new = wave_flag_rank(is_new, &c_new);
   const int rk_empty = wave_flag_rank(empty, &c_empty);
+  const int rk_stale = wave_flag_rank(stale, &c_stale);
   if (lane == 0) {
     sh.w_new[wave] = c_new;
     sh.w_empty[wave] = c_empty;
+    sh.w_stale[wave] = c_stale;
   }
   // Worst-first order of stale slots: ascending score, equal scores higher block first.
   const uint64_t st_me =
-      stale ? (((uint64_t)order_key(r_ok ? srow[r_i] : -INFINITY) << 32) | (uint32_t)(~(uint32_t)r_i))
+      stale ? (((uint64_t)order_key(r_ok ? rs.score : -INFINITY) << 32) | (uint32_t)(~(uint32_t)r_i))
             : ~0ull;
-  if (tid < K) sh.st[tid] = st_me;
   __syncthreads();
-  int n_new, n_empty;
+  int n_new, n_empty, n_stale;
   const int pos_new = waves_before<NW>(sh.w_new, &n_new) + rk_new;
   const int pos_empty = waves_before<NW>(sh.w_empty, &n_empty) + rk_empty;
+  const int pos_stale = waves_before<NW>(sh.w_stale, &n_stale) + rk_stale;
   const int n = C < n_new ? C : n_new;
   const bool admitted = is_new && pos_new < n;
   if (admitted) sh.adm_list[pos_new] = s_i;
+  if (stale) sh.st[pos_stale] = st_me;  // only the stale slots are ranked
+  if (tid >= n_stale && tid < ((n_stale + 31) & ~31)) sh.st[tid] = ~0ull;  // never smaller
+  if (tid >= n && tid < ((n + 15) & ~15)) sh.adm_list[tid] = 0x7fffffff;   // never smaller
   __syncthreads();
 
   // Victims: the first n of (empty slots by slot, stale slots by score asc, block desc).
@@ -314,11 +380,17 @@ __device__ void plan_apply(const float* __restrict__ srow, int s_i, const int32_
   if (empty) {
     victim = pos_empty < n;
   } else if (stale && n > n_empty) {
-    victim = rank_below(sh.st, K, st_me) < n - n_empty;
+    victim = count_cmp<false>(sh.st, n_stale, st_me) < n - n_empty;
   }
   if (admitted) {
     int rank = 0;
-    for (int u = 0; u < n; ++u) rank += sh.adm_list[u] < s_i;
+    for (int u = 0; u < n; u += 16) {
+      u32x4 w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = *(const u32x4*)(sh.adm_list + u + 4 * j);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) rank += (int)w[j >> 2][j & 3] < s_i;
+    }
     sh.adm_sorted[rank] = s_i;
   }
   int c_vict;
@@ -380,13 +452,16 @@ __global__ __launch_bounds__(THREADS) void plan_kernel(
     const int32_t* __restrict__ seq_lens, int32_t* resident, int32_t* plan, int32_t* plan_count,
     int32_t* table, int32_t* table_count, int heads, int NB, int K, int C, int window, int T) {
   __shared__ PlanShared<THREADS> sh;
+  __shared__ PlanBitmaps bm;
   const int bh = blockIdx.x;
   const int len = clamp_len(seq_lens[bh / heads], NB);
   const int s_i = threadIdx.x < K ? topk[(size_t)bh * K + threadIdx.x] : -1;
-  plan_apply<THREADS>(scores + (size_t)bh * NB, s_i, resident + (size_t)bh * K,
-                      resident + (size_t)bh * K, plan + (size_t)bh * C * 3, plan_count + bh,
-                      table + (size_t)bh * T, table_count + bh, K, C, NB,
-                      first_window_block(len, window), num_blocks(len), T, sh);
+  const ResidentSlot rs = load_resident_slot(resident + (size_t)bh * K, scores + (size_t)bh * NB, K, NB);
+  clear_bitmaps(bm, NB);
+  __syncthreads();
+  plan_apply<THREADS>(s_i, rs, resident + (size_t)bh * K, plan + (size_t)bh * C * 3,
+                      plan_count + bh, table + (size_t)bh * T, table_count + bh, K, C, NB,
+                      first_window_block(len, window), num_blocks(len), T, bm, sh);
 }
 
 // Selection and plan in one workgroup.
@@ -395,28 +470,38 @@ __global__ __launch_bounds__(THREADS) void topk_plan_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ seq_lens, int32_t* topk,
     const int32_t* resident, int32_t* resident_next, int32_t* plan, int32_t* plan_count,
     int32_t* table, int32_t* table_count, int heads, int NB, int K, int C, int window, int T) {
-  // The selection's LDS is dead once each thread holds its entry, so the plan reuses it.
+  // The selection's LDS is dead once each thread holds its entry, so the plan reuses
+  // it (the plan's first write to it follows a barrier that comes after every read of
+  // the selection).  The bitmaps are cleared while the selection runs.
   __shared__ union {
     SelectShared<THREADS, ITEMS> t;
     PlanShared<THREADS> p;
   } sh;
+  __shared__ PlanBitmaps bm;
   const int bh = blockIdx.x;
   const int len = clamp_len(seq_lens[bh / heads], NB);
   const int n_cand = first_window_block(len, window);
   const float* srow = scores + (size_t)bh * NB;
+  const ResidentSlot rs = load_resident_slot(resident + (size_t)bh * K, srow, K, NB);
+  clear_bitmaps(bm, NB);
   const int m = topk_select<THREADS, ITEMS>(srow, n_cand, K, sh.t);
+  if (m == 0) __syncthreads();  // the selection had no barrier after the clear
   for (int t = threadIdx.x; t < K; t += THREADS) topk[(size_t)bh * K + t] = t < m ? sh.t.sorted_idx[t] : -1;
   const int s_i = (threadIdx.x < m) ? sh.t.sorted_idx[threadIdx.x] : -1;
-  __syncthreads();
-  plan_apply<THREADS>(srow, s_i, resident + (size_t)bh * K, resident_next + (size_t)bh * K,
-                      plan + (size_t)bh * C * 3, plan_count + bh, table + (size_t)bh * T,
-                      table_count + bh, K, C, NB, n_cand, num_blocks(len), T, sh.p);
+  plan_apply<THREADS>(s_i, rs, resident_next + (size_t)bh * K, plan + (size_t)bh * C * 3,
+                      plan_count + bh, table + (size_t)bh * T, table_count + bh, K, C, NB, n_cand,
+                      num_blocks(len), T, bm, sh.p);
 }
 
-// Workgroup size and scores per thread for a problem: 256 threads while K <= 256
-// and the scores fit 8 per thread, else 1024 (up to 32 per thread).
+// Workgroup size and scores per thread for a problem: 512 threads while K <= 512
+// and the scores fit 8 per thread (measured fastest for 2048 blocks, K = 128: fewer
+// serial loads and LDS atomics per thread than 256, fewer waves per barrier than
+// 1024), else 1024 (up to 32 per thread).
+#ifndef OASIS_SELECT_SMALL
+#define OASIS_SELECT_SMALL 512
+#endif
 static int select_threads(const Dims& d) {
-  return (d.top_k <= 256 && d.max_blocks <= 256 * 8) ? 256 : 1024;
+  return (d.top_k <= OASIS_SELECT_SMALL && d.max_blocks <= OASIS_SELECT_SMALL * 8) ? OASIS_SELECT_SMALL : 1024;
 }
 static int select_items(const Dims& d, int threads) {
   int items = 1;
@@ -428,9 +513,10 @@ static int select_items(const Dims& d, int threads) {
   do {                                                   \
     const int threads_ = select_threads(d);              \
     const int items_ = select_items(d, threads_);        \
-    if (threads_ == 256) {                               \
+    if (threads_ == OASIS_SELECT_SMALL) {                \
       switch (items_) {                                  \
-        CASE(256, 1) CASE(256, 2) CASE(256, 4) CASE(256, 8) \
+        CASE(OASIS_SELECT_SMALL, 1) CASE(OASIS_SELECT_SMALL, 2) \
+        CASE(OASIS_SELECT_SMALL, 4) CASE(OASIS_SELECT_SMALL, 8) \
         default: return hipErrorInvalidValue;            \
       }                                                  \
     } else {                                             \

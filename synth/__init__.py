@@ -251,12 +251,13 @@ def resident_from_selection(w: Workload, selection: torch.Tensor, lens: torch.Te
     return torch.from_numpy(res.astype(np.int32))
 
 
-def random_scores(shape, seed: int, distinct: bool = True) -> torch.Tensor:
+def random_scores(shape, seed: int, distinct: bool = True, levels: int = 7) -> torch.Tensor:
     """fp32 test scores for exercising selection and planning on their own.
 
     With ``distinct`` the values are a random permutation of a spaced grid, so
-    every comparison has one answer; otherwise values are drawn from a small
-    set so that exact ties are common.
+    every comparison has one answer; otherwise values are drawn uniformly from
+    ``levels`` equally spaced values, so that exact ties are common (few levels:
+    large groups of equal scores; many levels: small groups spread over the range).
     """
     g = torch.Generator().manual_seed(seed)
     n = int(np.prod(shape))
@@ -264,7 +265,8 @@ def random_scores(shape, seed: int, distinct: bool = True) -> torch.Tensor:
         perm = torch.randperm(n, generator=g)
         vals = (perm.to(torch.float64) * 0.37 - 0.11 * n).to(torch.float32)
     else:
-        vals = torch.randint(-3, 4, (n,), generator=g).to(torch.float32) * 0.5
+        lo = -(levels // 2)
+        vals = torch.randint(lo, lo + levels, (n,), generator=g).to(torch.float32) * 0.5
     return vals.reshape(shape)
 
 

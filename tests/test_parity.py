@@ -76,18 +76,21 @@ def test_summaries_and_scores(lib, B, H, G, Q, NB, lens):
 # S2 top-K and S3 plan on given fp32 scores: decisions in the same precision, bit-exact
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("NB,K,lens,distinct", [
-    (2048, 128, [32768, 32768 - 77, 900, 100], True),
-    (2048, 128, [32768, 5000], False),          # many exact ties
-    (8192, 128, [131072], True),
-    (32768, 1024, [524288, 300000], True),      # largest supported NB and K
-    (300, 1, [4800, 16], True),                 # K = 1; a sequence with no candidate
-    (40, 40, [640, 200], False),                # K = NB
+@pytest.mark.parametrize("NB,K,lens,distinct,levels", [
+    (2048, 128, [32768, 32768 - 77, 900, 100], True, 0),
+    (2048, 128, [32768, 5000], False, 7),        # large groups of exact ties
+    (2048, 128, [32768, 20000], False, 512),     # small tie groups in every digit
+    (4096, 256, [65536, 4000], False, 1500),
+    (8192, 128, [131072], True, 0),
+    (8192, 128, [131072, 70000], False, 3000),
+    (32768, 1024, [524288, 300000], True, 0),    # largest supported NB and K
+    (300, 1, [4800, 16], True, 0),               # K = 1; a sequence with no candidate
+    (40, 40, [640, 200], False, 7),              # K = NB
 ])
-def test_topk_on_given_scores(lib, NB, K, lens, distinct):
-    _say(f"topk NB={NB} K={K} lens={lens} distinct={distinct}")
+def test_topk_on_given_scores(lib, NB, K, lens, distinct, levels):
+    _say(f"topk NB={NB} K={K} lens={lens} distinct={distinct} levels={levels}")
     B, H, W = len(lens), 3, 128
-    scores = synth.random_scores((B, H, NB), seed=NB + K, distinct=distinct)
+    scores = synth.random_scores((B, H, NB), seed=NB + K, distinct=distinct, levels=levels)
     L = torch.tensor(lens, dtype=torch.int32)
     d = _dims(lib, B, H, 4, NB, 5, K, W, 0.05)
     got = lib.topk_blocks(d, scores.to(DEV), L.to(DEV))
