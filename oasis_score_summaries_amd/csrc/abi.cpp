@@ -253,11 +253,13 @@ static oasis_status decode_step_impl(const oasis_dims* dims, const void* q, cons
                                           plan_count, table, table_count, stream),
                   "decode_step/select");
   if (st != OASIS_OK || (st = mark(2)) != OASIS_OK) return st;
-  st = hip_status(oasis::launch_attention_split(d, q, k, v, table, table_count, d.table_stride,
-                                                seq_lens, scale, ws, stream),
+  const oasis::AttnSplit split = oasis::attn_split(d, d.table_stride);
+  st = hip_status(oasis::launch_attention_split(d, split, q, k, v, table, table_count,
+                                                d.table_stride, seq_lens, scale, ws, stream),
                   "decode_step/attention");
   if (st != OASIS_OK || (st = mark(3)) != OASIS_OK) return st;
-  st = hip_status(oasis::launch_attention_merge(d, table_count, d.table_stride, out, lse, ws, stream),
+  st = hip_status(oasis::launch_attention_merge(d, split, table_count, d.table_stride, out, lse, ws,
+                                                stream),
                   "decode_step/attention-merge");
   if (st != OASIS_OK) return st;
   return mark(4);
@@ -290,11 +292,13 @@ static oasis_status decode_step_chunk(const oasis::Dims& full, int b0, int nb, c
                                           stream),
                   "decode_step/select");
   if (st != OASIS_OK) return st;
-  st = hip_status(oasis::launch_attention_split(d, qb, kb, vb, table + bh0 * T, table_count + bh0,
+  // The split geometry of the whole batch, so that the run's records fit its slice.
+  const oasis::AttnSplit split = oasis::attn_split(full, full.table_stride);
+  st = hip_status(oasis::launch_attention_split(d, split, qb, kb, vb, table + bh0 * T, table_count + bh0,
                                                 full.table_stride, seq_lens + b0, scale, wsb, stream),
                   "decode_step/attention");
   if (st != OASIS_OK) return st;
-  return hip_status(oasis::launch_attention_merge(d, table_count + bh0, full.table_stride,
+  return hip_status(oasis::launch_attention_merge(d, split, table_count + bh0, full.table_stride,
                                                   out + bh0 * G * 128,
                                                   lse == nullptr ? nullptr : lse + bh0 * G, wsb,
                                                   stream),

@@ -12,13 +12,14 @@ struct Dims {
   int batch, heads, group, max_blocks, queries, top_k, window, cap, table_stride;
 };
 
-// Attention split geometry: table entries handled by one workgroup, and the
-// workspace layout that the split kernel and the combine kernel share.
+// Attention split geometry shared by the split kernel, the merge kernel and the
+// workspace layout: workgroup s of a head takes table entries
+// [4 * rounds * s, 4 * rounds * (s + 1)), one per wave and round.
 struct AttnSplit {
-  int blocks_per_split;  // table entries per workgroup
-  int num_splits;        // ceil(table_stride / blocks_per_split)
+  int rounds;      // table entries per wave
+  int num_splits;  // ceil(table_stride / (4 * rounds))
 };
-AttnSplit attn_split(int table_stride);
+AttnSplit attn_split(const Dims& d, int table_stride);
 size_t attn_workspace_bytes(const Dims& d, int table_stride);
 // Workspace bytes owned by one sequence (a run of sequences owns a contiguous slice).
 size_t attn_workspace_bytes_per_sequence(const Dims& d, int table_stride);
@@ -37,12 +38,13 @@ hipError_t launch_topk_plan(const Dims& d, const float* scores, const int32_t* s
                             int32_t* topk, const int32_t* resident, int32_t* resident_next,
                             int32_t* plan, int32_t* plan_count, int32_t* table,
                             int32_t* table_count, hipStream_t stream);
-hipError_t launch_attention_split(const Dims& d, const void* q, const void* k, const void* v,
-                                  const int32_t* table, const int32_t* table_count,
+hipError_t launch_attention_split(const Dims& d, const AttnSplit& s, const void* q, const void* k,
+                                  const void* v, const int32_t* table, const int32_t* table_count,
                                   int table_stride, const int32_t* seq_lens, float scale, void* ws,
                                   hipStream_t stream);
-hipError_t launch_attention_merge(const Dims& d, const int32_t* table_count, int table_stride,
-                                  float* out, float* lse, const void* ws, hipStream_t stream);
+hipError_t launch_attention_merge(const Dims& d, const AttnSplit& s, const int32_t* table_count,
+                                  int table_stride, float* out, float* lse, const void* ws,
+                                  hipStream_t stream);
 hipError_t launch_attention(const Dims& d, const void* q, const void* k, const void* v,
                             const int32_t* table, const int32_t* table_count, int table_stride,
                             const int32_t* seq_lens, float scale, float* out, float* lse, void* ws,
