@@ -3,12 +3,18 @@
 
 A step is the whole path on one batch: score every candidate block against the
 min/max key summaries, select the top-K blocks per KV head, build the capped
-transfer plan against the resident set, and run sparse attention over the
-updated head-wise table (oasis_decode_step).  Inputs are seeded synthetic
-tensors already resident in HBM.  Several independent input sets are rotated
-step to step so that the 256 MB last-level cache cannot serve a step from the
-previous one; each step reads its set's resident table and writes the update
-to a scratch table, so every step does the same work.
+transfer plan against the resident set, and run sparse attention of the target
+queries over the head-wise working set.  By default the step is the pipeline
+the OasisKV pages describe (oasis_decode_step_overlapped): the foreground
+attention over the blocks resident now runs on one stream while the background
+look-ahead (scoring, top-K, plan for the next step) runs on another.  With
+--order serial it is oasis_decode_step: plan first, then attention over the
+updated table, all on one stream; the JSON line reports that time as well.
+Inputs are seeded synthetic tensors already resident in HBM.  Several
+independent input sets are rotated step to step so that the 256 MB last-level
+cache cannot serve a step from the previous one; each step reads its set's
+resident table and writes the update to a scratch table, so every step does
+the same work.
 
 Prints one JSON line.  Default workload: the Qwen3-8B attention-layer shape at
 32K context (batch 8, 8 KV heads x group 4, K = 128, 128-token window, fetch
@@ -40,13 +46,26 @@ def kv_cache_bytes(batch: int, ctx: int, layers: int, kv_heads: int, head_dim: i
     return batch * ctx * layers * 2 * kv_heads * head_dim * elem_bytes
 
 
+def working_set_blocks(w, lens, resident) -> int:
+    """Blocks the overlapped step's attention reads: per (sequence, KV head) the
+    resident blocks before the first window block plus the window blocks."""
+    total = 0
+    for b in range(w.batch):
+        L = int(lens[b])
+        w0 = max(0, (L - w.window) // 16)
+        nblk = (L + 15) // 16
+        r = resident[b]
+        total += int(((r >= 0) & (r < w0)).sum()) + w.num_kv_heads * (nblk - w0)
+    return total
+
+
 def algorithmic_bytes(w, lens, table_count) -> dict:
     """Bytes one step must move: candidate summaries, the K/V blocks of every table entry,
     the queries and the output.  Per kernel as well (inputs plus outputs)."""
     import synth
     H, G, Q = w.num_kv_heads, w.group, w.queries
     cand = sum(synth.first_window_block(int(x), w.window) for x in lens) * H
-    blocks = int(table_count.sum())
+    blocks = int(table_count) if isinstance(table_count, int) else int(table_count.sum())
     q_all = w.batch * H * G * Q * 128 * 2
     q_target = w.batch * H * G * 128 * 2
     out = w.batch * H * G * (128 + 1) * 4
@@ -62,7 +81,7 @@ def algorithmic_bytes(w, lens, table_count) -> dict:
     }
 
 
-def cpu_baseline(w, sets, budget_s: float) -> dict:
+def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     """The fp64 oracle on the host: the same step (score, top-K, plan, attention) for
     (sequence, KV head) units of input set 0, until ``budget_s`` seconds have run."""
     import numpy as np
@@ -86,8 +105,9 @@ def cpu_baseline(w, sets, budget_s: float) -> dict:
             sh = f64(s0["summ"][b:b + 1, h:h + 1].cpu())
             L = lens[b:b + 1].numpy()
             t = time.perf_counter()
-            ref.decode_step(qh, sh, kh, vh, L, res[b:b + 1, h:h + 1].numpy().astype(np.int64),
-                            w.top_k, w.window, w.cap, scale)
+            step = ref.decode_step_overlapped if overlapped else ref.decode_step
+            step(qh, sh, kh, vh, L, res[b:b + 1, h:h + 1].numpy().astype(np.int64),
+                 w.top_k, w.window, w.cap, scale)
             elapsed += time.perf_counter() - t
             done += 1
             if elapsed >= budget_s:
@@ -109,8 +129,10 @@ def main(argv=None) -> int:
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--stage-steps", type=int, default=300, help="evented steps for per-kernel times")
-    ap.add_argument("--chunks", type=int, default=1,
-                    help="runs of sequences issued on separate streams (oasis_decode_step_pipelined)")
+    ap.add_argument("--order", choices=("overlapped", "serial"), default="overlapped",
+                    help="overlapped: attention over the resident set on one stream while the "
+                         "look-ahead plans the next step on another; serial: plan, then attention "
+                         "over the updated table on one stream")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -146,74 +168,85 @@ def main(argv=None) -> int:
         del inp, q_sel, sel
     buffers = oa.StepBuffers(d, dev)
     res_next = torch.empty_like(sets[0]["resident"])
-    steps = [oa.PreparedStep(d, s["q"], s["summ"], s["k"], s["v"], s["seq_lens"], s["resident"],
-                             buffers, resident_next=res_next, chunks=args.chunks) for s in sets]
+    serial_steps = [oa.PreparedStep(d, s["q"], s["summ"], s["k"], s["v"], s["seq_lens"], s["resident"],
+                                    buffers, resident_next=res_next) for s in sets]
+    over_steps = [oa.PreparedStep(d, s["q"], s["summ"], s["k"], s["v"], s["seq_lens"], s["resident"],
+                                  buffers, resident_next=res_next, overlapped=True) for s in sets]
+    steps = over_steps if args.order == "overlapped" else serial_steps
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
-    # ---- warm-up, then the timed region ---------------------------------------------
-    for i in range(args.warmup):
-        steps[i % n_sets]()
-    torch.cuda.synchronize()
-    graph = None
-    if args.mode == "graph":
-        # One graph holds one step per input set; replaying it walks the rotation.
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            steps[0]()
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for st in steps:
-                st()
+    def timed(step_list):
+        """Warm-up, then exactly the timed steps; returns (ms per step, steps, wall s,
+        graph or None)."""
+        for i in range(args.warmup):
+            step_list[i % n_sets]()
         torch.cuda.synchronize()
-        for _ in range(max(1, args.warmup // n_sets)):
-            graph.replay()
+        graph = None
+        if args.mode == "graph":
+            # One graph holds one step per input set; replaying it walks the rotation.
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step_list[0]()
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for st in step_list:
+                    st()
+            torch.cuda.synchronize()
+            for _ in range(max(1, args.warmup // n_sets)):
+                graph.replay()
+            torch.cuda.synchronize()
+        reps = max(1, args.steps // n_sets)
+        n = reps * n_sets if graph is not None else args.steps
         torch.cuda.synchronize()
-    reps = max(1, args.steps // n_sets) if graph is not None else None
-    n_timed = reps * n_sets if graph is not None else args.steps
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record()
+        if graph is not None:
+            for _ in range(reps):
+                graph.replay()
+        else:
+            for i in range(n):
+                step_list[i % n_sets]()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n, n, time.perf_counter() - t0, graph
 
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    if graph is not None:
-        for _ in range(reps):
-            graph.replay()
-    else:
-        for i in range(n_timed):
-            steps[i % n_sets]()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = gpu_ms / n_timed
-
-    # The graph's last step ran set n_sets-1; an eager run of it must give the same bits.
+    # ---- the timed region (the chosen order), then the other order for reference ------
+    ms_per_step, n_timed, wall_s, graph = timed(steps)
     check = {}
     if graph is not None:
-        out_graph = buffers.out.clone()
+        # The graph's last step ran set n_sets-1; an eager run of it must give the same bits.
+        out_graph, res_graph = buffers.out.clone(), res_next.clone()
         steps[-1]()
         torch.cuda.synchronize()
-        check["graph_matches_eager"] = bool(torch.equal(out_graph, buffers.out))
+        check["graph_matches_eager"] = bool(torch.equal(out_graph, buffers.out) and
+                                            torch.equal(res_graph, res_next))
+    other = "serial" if args.order == "overlapped" else "overlapped"
+    ms_other, _, _, _ = timed(serial_steps if other == "serial" else over_steps)
+    del graph
 
-    # ---- per-kernel times: evented steps (HIP events on the launch stream) ---------------
+    # ---- per-kernel times: evented serial steps (HIP events on the launch stream) -----
     stage = {k: [] for k in oa.StageEvents.STAGES}
     evs = oa.StageEvents()
     for i in range(args.stage_steps):
-        steps[i % n_sets](events=evs)
+        serial_steps[i % n_sets](events=evs)
         for k, v in evs.elapsed_ms().items():
             stage[k].append(v)
     stage_us = {k: 1e3 * statistics.mean(v) for k, v in stage.items()}
 
     # ---- bytes and roofline ------------------------------------------------------------------
     torch.cuda.synchronize()
-    nb = {}
-    for s in sets[:1]:
-        steps[0]()
+    s0 = sets[0]
+    if args.order == "overlapped":
+        blocks = working_set_blocks(w, s0["seq_lens"].cpu(), s0["resident"].cpu())
+    else:
+        serial_steps[0]()
         torch.cuda.synchronize()
-        nb = algorithmic_bytes(w, s["seq_lens"].cpu(), buffers.table_count.cpu())
+        blocks = int(buffers.table_count.sum())
+    nb = algorithmic_bytes(w, s0["seq_lens"].cpu(), blocks)
     step_gbps = nb["step"] / (ms_per_step * 1e-3) / 1e9
     dominant = max(("score", "attn_split"), key=lambda k: stage_us[k])
     dom_gbps = nb[dominant] / (stage_us[dominant] * 1e-6) / 1e9
@@ -234,7 +267,7 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.num_kv_heads, "group": w.group,
                    "context": w.ctx, "queries_per_head": w.queries, "top_k": w.top_k,
                    "window_tokens": w.window, "fetch_ratio": w.fetch_ratio, "cap": w.cap,
-                   "input_sets": n_sets, "mode": args.mode, "chunks": args.chunks},
+                   "input_sets": n_sets, "mode": args.mode, "order": args.order},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None, "bytes_per_launch": nb[dominant],
@@ -242,12 +275,13 @@ def main(argv=None) -> int:
         "step_hbm": {"achieved": round(step_gbps, 1), "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
                      "bytes_per_step": nb["step"], "units": nb["units"]},
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
+        f"{other}_ms_per_step": round(ms_other, 6),
         "wall_s": round(wall_s, 3),
         "setup_s": round(setup_s, 1),
         "checks": check,
     }
     if args.cpu_budget > 0:
-        result["cpu_baseline"] = cpu_baseline(w, sets, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(w, sets, args.cpu_budget, args.order == "overlapped")
     print(json.dumps(result), flush=True)
     return 0
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define OASIS_ABI_VERSION 1
+#define OASIS_ABI_VERSION 2
 
 typedef enum {
   OASIS_OK = 0,
@@ -202,6 +202,23 @@ oasis_status oasis_sparse_decode_attn(const oasis_dims* dims, const void* q, con
                                       const int32_t* seq_lens, float scale, float* out, float* lse,
                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* oasis_sparse_decode_attn over the working set held as resident slots: the
+ * tokens attended are those of the blocks resident[b,h,s] (s < K, -1 = empty
+ * slot) that lie before the first window block w0_b, followed by the window
+ * blocks w0_b .. nblk_b - 1, i.e. the same set as the table that
+ * oasis_build_plan would write for this slot table (a resident block at or
+ * past w0_b is attended once, as a window block).  No compacted table is
+ * needed, so the attention can start from the slot table of the previous
+ * step.  Same sources as oasis_sparse_decode_attn.
+ *   resident     device, int32 [B, H, K]; entries distinct, or -1
+ *   ws, ws_bytes device workspace, at least oasis_workspace_bytes(dims)
+ *   other arguments as for oasis_sparse_decode_attn */
+oasis_status oasis_sparse_decode_attn_resident(const oasis_dims* dims, const void* q, const void* k,
+                                               const void* v, const int32_t* resident,
+                                               const int32_t* seq_lens, float scale, float* out,
+                                               float* lse, void* ws, size_t ws_bytes,
+                                               hipStream_t stream);
+
 /* The whole step on one stream: oasis_score_summaries, then the selection and
  * the plan (one kernel doing oasis_topk_blocks and oasis_build_plan), then
  * oasis_sparse_decode_attn over the updated table (table_stride =
@@ -218,26 +235,32 @@ oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void
                                int32_t* table, int32_t* table_count, float scale, float* out,
                                float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* oasis_decode_step with the batch cut into n_chunks runs of sequences whose
- * kernels go to different streams, so that one run's latency-bound selection and
- * merge overlap another run's HBM-bound scoring and attention.  Run 0 uses
- * `stream`; run c > 0 uses aux_streams[(c - 1) % n_aux].  The auxiliary streams
- * first wait for the work already queued on `stream` (events[0]) and `stream`
- * finally waits for all of them (events[1 .. n_aux]), so to the caller the call
- * behaves like oasis_decode_step on `stream` (also under HIP graph capture).
- * Streams and events are the caller's (hipStreamCreate / hipEventCreate, default
- * priority); none is created or destroyed here.  n_chunks is clamped to B; with
- * n_chunks == 1 the auxiliary arguments are ignored.  Results are identical to
- * oasis_decode_step's. */
-oasis_status oasis_decode_step_pipelined(const oasis_dims* dims, const void* q, const void* summ,
-                                         const void* k, const void* v, const int32_t* seq_lens,
-                                         float* scores, int32_t* topk, int32_t* resident,
-                                         int32_t* resident_next, int32_t* plan,
-                                         int32_t* plan_count, int32_t* table,
-                                         int32_t* table_count, float scale, float* out, float* lse,
-                                         void* ws, size_t ws_bytes, hipStream_t stream,
-                                         int32_t n_chunks, hipStream_t* aux_streams, int32_t n_aux,
-                                         hipEvent_t* events, int32_t n_events);
+/* The step as a foreground and a background half: while the target queries
+ * attend over the blocks resident now, the look-ahead scoring, the selection
+ * and the plan produce the resident set of the next step (lode.cx summary,
+ * point 3: background prefetch while the GPU computes the current attention;
+ * legiblepapers.com summary: foreground attention over the entries currently
+ * resident, background look-ahead for future blocks; xllm-io review, section
+ * three, training flow step 3).
+ *   foreground: exactly oasis_sparse_decode_attn_resident(dims, q, k, v,
+ *     resident, seq_lens, scale, out, lse, ws, ws_bytes).
+ *   background: oasis_score_summaries, then the selection and the plan, reading
+ *     `resident` and writing the next slot table to `resident_next` (and plan,
+ *     table, table_count for it), as oasis_decode_step does.
+ * The halves share only inputs; they are queued on `stream` as two launches that
+ * each hold work of both halves (scoring with the attention's block gathering,
+ * then the selection and plan with the attention's merge), so the
+ * latency-bound parts of one half run under the other's streaming.
+ * resident_next is required and must not overlap `resident`; the caller swaps
+ * the two between steps.  Other arguments as for oasis_decode_step. */
+oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q, const void* summ,
+                                          const void* k, const void* v, const int32_t* seq_lens,
+                                          float* scores, int32_t* topk, const int32_t* resident,
+                                          int32_t* resident_next, int32_t* plan,
+                                          int32_t* plan_count, int32_t* table,
+                                          int32_t* table_count, float scale, float* out,
+                                          float* lse, void* ws, size_t ws_bytes,
+                                          hipStream_t stream);
 
 /* oasis_decode_step with timing markers, for measurement: events[0..4]
  * (created by the caller with hipEventCreate) are recorded on `stream` before

@@ -8,6 +8,7 @@ Every call raises if the library has not been built.
 """
 from ._lib import (LIB_PATH, OasisDims, OasisError, PreparedStep, StageEvents,  # noqa: F401
                    StepBuffers, build_plan,
-                   build_summaries, decode_step, dims_for, exported_symbols, fetch_cap, load,
-                   make_dims, score_summaries, sparse_decode_attn, table_stride, topk_blocks,
+                   build_summaries, decode_step, decode_step_overlapped, dims_for,
+                   exported_symbols, fetch_cap, load, make_dims, score_summaries,
+                   sparse_decode_attn, sparse_decode_attn_resident, table_stride, topk_blocks,
                    workspace_bytes)

@@ -68,11 +68,11 @@ _SIGNATURES = {
     "oasis_decode_step_timed": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t, _P,
                                                ctypes.POINTER(ctypes.c_void_p)]),
-    "oasis_decode_step_pipelined": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                                   _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t,
-                                                   _P, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
-                                                   ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
-                                                   ctypes.c_int32]),
+    "oasis_sparse_decode_attn_resident": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, ctypes.c_float,
+                                                         _P, _P, _P, ctypes.c_size_t, _P]),
+    "oasis_decode_step_overlapped": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                    _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t,
+                                                    _P]),
 }
 
 _lib = None
@@ -296,6 +296,38 @@ def sparse_decode_attn(dims: OasisDims, q: torch.Tensor, k: torch.Tensor, v: tor
     return out, lse
 
 
+def sparse_decode_attn_resident(dims: OasisDims, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                resident: torch.Tensor, seq_lens: torch.Tensor,
+                                scale: Optional[float] = None, out=None, lse=None, ws=None,
+                                stream=None):
+    """Attention of the target queries over the resident slots plus the window
+    (oasis_sparse_decode_attn_resident).  Returns (out, lse)."""
+    s = _shapes(dims)
+    _need(q, "q", torch.bfloat16, s["q"], align=16)
+    dev = q.device
+    _need(k, "k", torch.bfloat16, s["kv"], dev, align=16)
+    _need(v, "v", torch.bfloat16, s["kv"], dev, align=16)
+    _need(resident, "resident", torch.int32, s["resident"], dev)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(128)
+    if out is None:
+        out = torch.empty(s["out"], dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty(s["lse"], dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, s["out"], dev, align=16)
+    _need(lse, "lse", torch.float32, s["lse"], dev)
+    need = workspace_bytes(dims)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if ws.device != dev or ws.dtype != torch.uint8 or not ws.is_contiguous():
+        raise ValueError("ws must be a contiguous uint8 GPU tensor on the inputs' device")
+    _check(load().oasis_sparse_decode_attn_resident(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(resident), _ptr(seq_lens), float(scale),
+        _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "oasis_sparse_decode_attn_resident")
+    return out, lse
+
+
 class StepBuffers:
     """Outputs and workspace of oasis_decode_step, allocated once and reused."""
 
@@ -344,6 +376,38 @@ def decode_step(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor, k: torch.T
         b.ws.numel(), _stream(stream)), "oasis_decode_step")
     res = b.as_dict()
     res["resident"] = resident if resident_next is None else resident_next
+    return res
+
+
+def decode_step_overlapped(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor, k: torch.Tensor,
+                           v: torch.Tensor, seq_lens: torch.Tensor, resident: torch.Tensor,
+                           resident_next: torch.Tensor, scale: Optional[float] = None,
+                           buffers: Optional[StepBuffers] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """Attention over ``resident`` (plus the window) and, alongside it, score ->
+    top-K -> capped plan writing the next slot table to ``resident_next``
+    (oasis_decode_step_overlapped)."""
+    s = _shapes(dims)
+    _need(q, "q", torch.bfloat16, s["q"], align=16)
+    dev = q.device
+    _need(summ, "summ", torch.bfloat16, s["summ"], dev, align=16)
+    _need(k, "k", torch.bfloat16, s["kv"], dev, align=16)
+    _need(v, "v", torch.bfloat16, s["kv"], dev, align=16)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+    _need(resident, "resident", torch.int32, s["resident"], dev)
+    _need(resident_next, "resident_next", torch.int32, s["resident"], dev)
+    if buffers is None:
+        buffers = StepBuffers(dims, dev)
+    b = buffers
+    if scale is None:
+        scale = 1.0 / math.sqrt(128)
+    _check(load().oasis_decode_step_overlapped(
+        ctypes.byref(dims), _ptr(q), _ptr(summ), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(b.scores),
+        _ptr(b.topk), _ptr(resident), _ptr(resident_next),
+        _ptr(b.plan if b.plan.numel() else None), _ptr(b.plan_count),
+        _ptr(b.table), _ptr(b.table_count), float(scale), _ptr(b.out), _ptr(b.lse), _ptr(b.ws),
+        b.ws.numel(), _stream(stream)), "oasis_decode_step_overlapped")
+    res = b.as_dict()
+    res["resident"] = resident_next
     return res
 
 
@@ -409,40 +473,18 @@ class StageEvents:
             pass
 
 
-class SyncEvents:
-    """HIP events without timing, for fork/join ordering between streams."""
-
-    def __init__(self, n: int):
-        h = _hip_runtime()
-        self.n = n
-        self.handles = (ctypes.c_void_p * max(1, n))()
-        for i in range(n):
-            ev = ctypes.c_void_p()
-            if h.hipEventCreateWithFlags(ctypes.byref(ev), 0x2) != 0:  # hipEventDisableTiming
-                raise RuntimeError("hipEventCreateWithFlags failed")
-            self.handles[i] = ev.value
-
-    def __del__(self):
-        try:
-            h = _hip_runtime()
-            for i in range(self.n):
-                if self.handles[i]:
-                    h.hipEventDestroy(self.handles[i])
-        except Exception:
-            pass
-
-
 class PreparedStep:
     """One fused decode step whose arguments are checked and marshalled once.
 
     Calling it queues oasis_decode_step on the current stream (with ``events``,
-    oasis_decode_step_timed; with ``chunks`` > 1, oasis_decode_step_pipelined on
-    ``chunks`` - 1 auxiliary streams owned by this object).  The tensors must stay
-    alive and keep their storage while the object is used.
+    oasis_decode_step_timed).  With ``overlapped``, it queues
+    oasis_decode_step_overlapped instead: attention over ``resident`` alongside
+    the scoring, selection and plan into ``resident_next`` (required).  The
+    tensors must stay alive and keep their storage while the object is used.
     """
 
     def __init__(self, dims: OasisDims, q, summ, k, v, seq_lens, resident, buffers: StepBuffers,
-                 resident_next=None, scale: Optional[float] = None, chunks: int = 1):
+                 resident_next=None, scale: Optional[float] = None, overlapped: bool = False):
         s = _shapes(dims)
         _need(q, "q", torch.bfloat16, s["q"], align=16)
         dev = q.device
@@ -469,19 +511,18 @@ class PreparedStep:
                      _ptr(b.table_count), ctypes.c_float(scale), _ptr(b.out), _ptr(b.lse), _ptr(b.ws),
                      ctypes.c_size_t(b.ws.numel())]
         self.lib = load()
-        self.chunks = max(1, min(int(chunks), dims.batch))
-        self.aux = [torch.cuda.Stream(device=dev) for _ in range(self.chunks - 1)]
-        self.aux_handles = (ctypes.c_void_p * max(1, len(self.aux)))(*[s.cuda_stream for s in self.aux])
-        self.sync = SyncEvents(len(self.aux) + 1 if self.aux else 0)
+        self.overlapped = bool(overlapped)
+        if self.overlapped and resident_next is None:
+            raise ValueError("the overlapped step needs resident_next (the attention reads resident)")
 
     def __call__(self, stream=None, events: Optional[StageEvents] = None) -> None:
         st = _stream(stream)
-        if events is not None:
+        if self.overlapped:
+            if events is not None:
+                raise ValueError("stage events time the serial step only")
+            _check(self.lib.oasis_decode_step_overlapped(*self.args, st), "oasis_decode_step_overlapped")
+        elif events is not None:
             _check(self.lib.oasis_decode_step_timed(*self.args, st, events.handles),
                    "oasis_decode_step_timed")
-        elif self.chunks > 1:
-            _check(self.lib.oasis_decode_step_pipelined(
-                *self.args, st, self.chunks, self.aux_handles, len(self.aux), self.sync.handles,
-                self.sync.n), "oasis_decode_step_pipelined")
         else:
             _check(self.lib.oasis_decode_step(*self.args, st), "oasis_decode_step")

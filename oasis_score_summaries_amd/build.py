@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liboasis.so")
-SOURCES = ["abi.cpp", "summaries.hip", "score.hip", "select.hip", "attention.hip"]
+SOURCES = ["abi.cpp", "summaries.hip", "score.hip", "select.hip", "attention.hip", "fused.hip"]
 ARCH = os.environ.get("OASIS_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions are kept out of the device code: ordinary float code

@@ -203,15 +203,40 @@ oasis_status oasis_sparse_decode_attn(const oasis_dims* dims, const void* q, con
                     "sparse_decode_attn");
 }
 
-// The fused step; with `events` non-NULL, markers are recorded between its kernels.
-static oasis_status decode_step_impl(const oasis_dims* dims, const void* q, const void* summ,
-                                     const void* k, const void* v, const int32_t* seq_lens,
-                                     float* scores, int32_t* topk, int32_t* resident,
-                                     int32_t* resident_next, int32_t* plan, int32_t* plan_count,
-                                     int32_t* table, int32_t* table_count, float scale, float* out,
-                                     float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
-                                     hipEvent_t* events) {
+oasis_status oasis_sparse_decode_attn_resident(const oasis_dims* dims, const void* q, const void* k,
+                                               const void* v, const int32_t* resident,
+                                               const int32_t* seq_lens, float scale, float* out,
+                                               float* lse, void* ws, size_t ws_bytes,
+                                               hipStream_t stream) {
   oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  OASIS_REQUIRE(q);
+  OASIS_REQUIRE(k);
+  OASIS_REQUIRE(v);
+  OASIS_REQUIRE(resident);
+  OASIS_REQUIRE(seq_lens);
+  OASIS_REQUIRE(out);
+  if (!isfinite(scale)) return fail(OASIS_ERR_INVALID_ARG, "scale must be finite");
+  const size_t need = oasis::attn_workspace_bytes(d, d.table_stride);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(OASIS_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need,
+                ws == nullptr ? (size_t)0 : ws_bytes);
+  return hip_status(oasis::launch_attention(d, q, k, v, resident, nullptr, d.table_stride, seq_lens,
+                                            scale, out, lse, ws, stream, true),
+                    "sparse_decode_attn_resident");
+}
+
+// Argument checks shared by the fused-step entry points.  On success `d` is filled
+// and *resident_next is resolved (NULL or equal to `resident`: in place).
+static oasis_status check_step_args(const oasis_dims* dims, oasis::Dims& d, const void* q,
+                                    const void* summ, const void* k, const void* v,
+                                    const int32_t* seq_lens, const float* scores,
+                                    const int32_t* topk, const int32_t* resident,
+                                    int32_t** resident_next, const int32_t* plan,
+                                    const int32_t* plan_count, const int32_t* table,
+                                    const int32_t* table_count, float scale, const float* out,
+                                    const void* ws, size_t ws_bytes) {
   oasis_status st = check_dims(dims, &d);
   if (st != OASIS_OK) return st;
   OASIS_REQUIRE(q);
@@ -232,13 +257,29 @@ static oasis_status decode_step_impl(const oasis_dims* dims, const void* q, cons
   if (ws == nullptr || ws_bytes < need)
     return fail(OASIS_ERR_WORKSPACE, "decode step needs %zu workspace bytes, got %zu", need,
                 ws == nullptr ? (size_t)0 : ws_bytes);
-  if (resident_next != nullptr && resident_next != resident) {
+  if (*resident_next != nullptr && *resident_next != resident) {
     const size_t n = (size_t)d.batch * d.heads * d.top_k;
-    if (resident_next < resident + n && resident < resident_next + n)
+    if (*resident_next < resident + n && resident < *resident_next + n)
       return fail(OASIS_ERR_INVALID_ARG, "resident and resident_next overlap");
   } else {
-    resident_next = resident;
+    *resident_next = const_cast<int32_t*>(resident);
   }
+  return OASIS_OK;
+}
+
+// The fused step; with `events` non-NULL, markers are recorded between its kernels.
+static oasis_status decode_step_impl(const oasis_dims* dims, const void* q, const void* summ,
+                                     const void* k, const void* v, const int32_t* seq_lens,
+                                     float* scores, int32_t* topk, int32_t* resident,
+                                     int32_t* resident_next, int32_t* plan, int32_t* plan_count,
+                                     int32_t* table, int32_t* table_count, float scale, float* out,
+                                     float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
+                                     hipEvent_t* events) {
+  oasis::Dims d;
+  oasis_status st = check_step_args(dims, d, q, summ, k, v, seq_lens, scores, topk, resident,
+                                    &resident_next, plan, plan_count, table, table_count, scale,
+                                    out, ws, ws_bytes);
+  if (st != OASIS_OK) return st;
   if (events != nullptr) {
     for (int i = 0; i < 5; ++i) OASIS_REQUIRE(events[i]);
   }
@@ -258,125 +299,33 @@ static oasis_status decode_step_impl(const oasis_dims* dims, const void* q, cons
                                                 d.table_stride, seq_lens, scale, ws, stream),
                   "decode_step/attention");
   if (st != OASIS_OK || (st = mark(3)) != OASIS_OK) return st;
-  st = hip_status(oasis::launch_attention_merge(d, split, table_count, d.table_stride, out, lse, ws,
-                                                stream),
+  st = hip_status(oasis::launch_attention_merge(d, split, out, lse, ws, stream),
                   "decode_step/attention-merge");
   if (st != OASIS_OK) return st;
   return mark(4);
 }
 
-// The step's kernels for sequences [b0, b0 + d.batch) of a problem with `full` sizes.
-static oasis_status decode_step_chunk(const oasis::Dims& full, int b0, int nb, const void* q,
-                                      const void* summ, const void* k, const void* v,
-                                      const int32_t* seq_lens, float* scores, int32_t* topk,
-                                      int32_t* resident, int32_t* resident_next, int32_t* plan,
-                                      int32_t* plan_count, int32_t* table, int32_t* table_count,
-                                      float scale, float* out, float* lse, void* ws,
-                                      hipStream_t stream) {
-  oasis::Dims d = full;
-  d.batch = nb;
-  const size_t H = full.heads, G = full.group, Q = full.queries, NB = full.max_blocks;
-  const size_t K = full.top_k, C = full.cap, T = full.table_stride, bh0 = (size_t)b0 * H;
-  const char* qb = (const char*)q + bh0 * G * Q * 256;
-  const char* sb = (const char*)summ + bh0 * NB * 512;
-  const char* kb = (const char*)k + bh0 * NB * 4096;
-  const char* vb = (const char*)v + bh0 * NB * 4096;
-  char* wsb = (char*)ws + (size_t)b0 * oasis::attn_workspace_bytes_per_sequence(full, full.table_stride);
-  oasis_status st = hip_status(oasis::launch_score(d, qb, sb, seq_lens + b0, scores + bh0 * NB, stream),
-                               "decode_step/score");
-  if (st != OASIS_OK) return st;
-  st = hip_status(oasis::launch_topk_plan(d, scores + bh0 * NB, seq_lens + b0, topk + bh0 * K,
-                                          resident + bh0 * K, resident_next + bh0 * K,
-                                          plan == nullptr ? nullptr : plan + bh0 * C * 3,
-                                          plan_count + bh0, table + bh0 * T, table_count + bh0,
-                                          stream),
-                  "decode_step/select");
-  if (st != OASIS_OK) return st;
-  // The split geometry of the whole batch, so that the run's records fit its slice.
-  const oasis::AttnSplit split = oasis::attn_split(full, full.table_stride);
-  st = hip_status(oasis::launch_attention_split(d, split, qb, kb, vb, table + bh0 * T, table_count + bh0,
-                                                full.table_stride, seq_lens + b0, scale, wsb, stream),
-                  "decode_step/attention");
-  if (st != OASIS_OK) return st;
-  return hip_status(oasis::launch_attention_merge(d, split, table_count + bh0, full.table_stride,
-                                                  out + bh0 * G * 128,
-                                                  lse == nullptr ? nullptr : lse + bh0 * G, wsb,
-                                                  stream),
-                    "decode_step/attention-merge");
-}
-
-oasis_status oasis_decode_step_pipelined(const oasis_dims* dims, const void* q, const void* summ,
-                                         const void* k, const void* v, const int32_t* seq_lens,
-                                         float* scores, int32_t* topk, int32_t* resident,
-                                         int32_t* resident_next, int32_t* plan,
-                                         int32_t* plan_count, int32_t* table,
-                                         int32_t* table_count, float scale, float* out, float* lse,
-                                         void* ws, size_t ws_bytes, hipStream_t stream,
-                                         int32_t n_chunks, hipStream_t* aux_streams, int32_t n_aux,
-                                         hipEvent_t* events, int32_t n_events) {
+oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q, const void* summ,
+                                          const void* k, const void* v, const int32_t* seq_lens,
+                                          float* scores, int32_t* topk, const int32_t* resident,
+                                          int32_t* resident_next, int32_t* plan,
+                                          int32_t* plan_count, int32_t* table,
+                                          int32_t* table_count, float scale, float* out,
+                                          float* lse, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
   oasis::Dims d;
-  oasis_status st = check_dims(dims, &d);
+  OASIS_REQUIRE(resident_next);
+  oasis_status st = check_step_args(dims, d, q, summ, k, v, seq_lens, scores, topk, resident,
+                                    &resident_next, plan, plan_count, table, table_count, scale,
+                                    out, ws, ws_bytes);
   if (st != OASIS_OK) return st;
-  OASIS_REQUIRE(q);
-  OASIS_REQUIRE(summ);
-  OASIS_REQUIRE(k);
-  OASIS_REQUIRE(v);
-  OASIS_REQUIRE(seq_lens);
-  OASIS_REQUIRE(scores);
-  OASIS_REQUIRE(topk);
-  OASIS_REQUIRE(resident);
-  if (d.cap > 0) OASIS_REQUIRE(plan);
-  OASIS_REQUIRE(plan_count);
-  OASIS_REQUIRE(table);
-  OASIS_REQUIRE(table_count);
-  OASIS_REQUIRE(out);
-  if (!isfinite(scale)) return fail(OASIS_ERR_INVALID_ARG, "scale must be finite");
-  const size_t need = oasis::attn_workspace_bytes(d, d.table_stride);
-  if (ws == nullptr || ws_bytes < need)
-    return fail(OASIS_ERR_WORKSPACE, "decode step needs %zu workspace bytes, got %zu", need,
-                ws == nullptr ? (size_t)0 : ws_bytes);
-  if (resident_next != nullptr && resident_next != resident) {
-    const size_t n = (size_t)d.batch * d.heads * d.top_k;
-    if (resident_next < resident + n && resident < resident_next + n)
-      return fail(OASIS_ERR_INVALID_ARG, "resident and resident_next overlap");
-  } else {
-    resident_next = resident;
-  }
-  if (n_chunks < 1) return fail(OASIS_ERR_INVALID_ARG, "n_chunks must be >= 1");
-  if (n_chunks > d.batch) n_chunks = d.batch;
-  if (n_chunks > 1) {
-    if (n_aux < 1 || aux_streams == nullptr)
-      return fail(OASIS_ERR_INVALID_ARG, "more than one chunk needs at least one auxiliary stream");
-    for (int i = 0; i < n_aux; ++i)
-      if (aux_streams[i] == nullptr) return fail(OASIS_ERR_INVALID_ARG, "aux_streams[%d] is NULL", i);
-    if (events == nullptr || n_events < 1 + n_aux)
-      return fail(OASIS_ERR_INVALID_ARG, "need 1 + n_aux events, got %d", n_events);
-    for (int i = 0; i < 1 + n_aux; ++i)
-      if (events[i] == nullptr) return fail(OASIS_ERR_INVALID_ARG, "events[%d] is NULL", i);
-  }
-  const int used_aux = n_chunks > 1 ? (n_aux < n_chunks - 1 ? n_aux : n_chunks - 1) : 0;
-  if (used_aux > 0) {
-    if ((st = hip_status(hipEventRecord(events[0], stream), "pipelined/fork")) != OASIS_OK) return st;
-    for (int i = 0; i < used_aux; ++i)
-      if ((st = hip_status(hipStreamWaitEvent(aux_streams[i], events[0], 0), "pipelined/fork")) != OASIS_OK)
-        return st;
-  }
-  for (int c = 0; c < n_chunks; ++c) {
-    const int b0 = (int)((int64_t)d.batch * c / n_chunks);
-    const int b1 = (int)((int64_t)d.batch * (c + 1) / n_chunks);
-    hipStream_t sc = (c == 0) ? stream : aux_streams[(c - 1) % used_aux];
-    st = decode_step_chunk(d, b0, b1 - b0, q, summ, k, v, seq_lens, scores, topk, resident,
-                           resident_next, plan, plan_count, table, table_count, scale, out, lse,
-                           ws, sc);
-    if (st != OASIS_OK) return st;
-  }
-  for (int i = 0; i < used_aux; ++i) {
-    if ((st = hip_status(hipEventRecord(events[1 + i], aux_streams[i]), "pipelined/join")) != OASIS_OK)
-      return st;
-    if ((st = hip_status(hipStreamWaitEvent(stream, events[1 + i], 0), "pipelined/join")) != OASIS_OK)
-      return st;
-  }
-  return OASIS_OK;
+  if (resident_next == resident)
+    return fail(OASIS_ERR_INVALID_ARG,
+                "resident_next must be its own buffer: the attention reads resident meanwhile");
+  return hip_status(oasis::launch_overlapped_step(d, q, summ, k, v, seq_lens, scores, topk, resident,
+                                                  resident_next, plan, plan_count, table,
+                                                  table_count, scale, out, lse, ws, stream),
+                    "decode_step_overlapped");
 }
 
 oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void* summ,

@@ -1,0 +1,117 @@
+// The overlapped decode step as two fused launches on gfx950.
+//
+// The OasisKV pages split a decode step into a foreground half, attention of the
+// current token over the blocks resident in HBM now, and a background half, the
+// look-ahead that scores the block summaries with the draft queries, predicts the
+// top-K blocks and plans the transfers for the next step (lode.cx summary, point
+// 3; legiblepapers.com summary; xllm-io review, section three, training flow
+// step 3).  The two halves share only inputs, so their work items can sit in
+// the same grids:
+//   launch 1: the scoring workgroups and the attention split workgroups (both
+//             stream HBM: summaries on one side, K/V blocks on the other);
+//   launch 2: the selection-and-plan workgroups and the attention merge
+//             workgroups (both latency bound).
+// One grid per phase needs no second stream and no cross-stream event, and the
+// ramp-up and tail of each phase are paid once instead of twice.  (With more than
+// 32 query rows per KV head the scoring workgroup needs more registers than the
+// attention's four waves per SIMD allow; launch 1 is then the two kernels back to
+// back.)  A workgroup's
+// role follows from its index; the scoring and selection workgroups, which run
+// longest, come first so that they start first.
+#include "attention_impl.h"
+#include "score_impl.h"
+#include "select_impl.h"
+
+namespace oasis {
+
+template <int RT, int GP>
+__global__ __launch_bounds__(256, OASIS_ATTN_MIN_WAVES) void score_attn_kernel(ScoreArgs sa, AttnArgs aa,
+                                                                             int n_score, int score_gx,
+                                                                             int attn_gx) {
+  __shared__ union {
+    ScoreShared<RT> s;
+    AttnShared<GP> a;
+  } sh;
+  const int b = blockIdx.x;
+  if (b < n_score) {
+    score_wg<RT>(b % score_gx, b / score_gx, sh.s, sa);
+  } else {
+    const int i = b - n_score;
+    attn_split_wg<GP, true>(i % attn_gx, i / attn_gx, sh.a, aa);
+  }
+}
+
+template <int THREADS, int ITEMS>
+__global__ __launch_bounds__(THREADS) void select_merge_kernel(TopkPlanArgs ta, const float* part,
+                                                               int group, int nsplit, float* out,
+                                                               float* lse, int n_select) {
+  __shared__ union {
+    TopkPlanShared<THREADS, ITEMS> t;
+    MergeShared<THREADS / 64> m;
+  } sh;
+  __shared__ PlanBitmaps bm;
+  if ((int)blockIdx.x < n_select) {
+    topk_plan_wg<THREADS, ITEMS>(blockIdx.x, sh.t, bm, ta);
+  } else {
+    attn_merge_wg<THREADS / 64>(blockIdx.x - n_select, sh.m, part, group, nsplit, out, lse);
+  }
+}
+
+hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ, const void* k,
+                                  const void* v, const int32_t* seq_lens, float* scores,
+                                  int32_t* topk, const int32_t* resident, int32_t* resident_next,
+                                  int32_t* plan, int32_t* plan_count, int32_t* table,
+                                  int32_t* table_count, float scale, float* out, float* lse,
+                                  void* ws, hipStream_t stream) {
+  const int heads = d.batch * d.heads;
+  const AttnSplit s = attn_split(d, d.table_stride);
+  const ScoreArgs sa = score_args(d, q, summ, seq_lens, scores);
+  const AttnArgs aa = attn_args(d, s, q, k, v, resident, nullptr, d.table_stride, seq_lens, scale, ws);
+  const int score_gx = score_grid_x(d);
+  const int n_score = score_gx * heads;
+  const int attn_gx = s.num_splits;
+  const int grid1 = n_score + attn_gx * heads;
+  const int rt = (d.group * d.queries + 15) / 16;
+  const int gp = d.group <= 4 ? 4 : (d.group <= 8 ? 8 : 16);
+  // Up to two row tiles the scoring work fits the attention's register budget (four
+  // waves per SIMD); with more query rows the two kinds of workgroup keep their own
+  // kernels, back to back.
+  switch (rt <= 2 ? rt * 100 + gp : 0) {
+#define OASIS_SA_CASE(RT, GP)                                                                  \
+  case RT * 100 + GP:                                                                          \
+    score_attn_kernel<RT, GP><<<dim3(grid1), dim3(256), 0, stream>>>(sa, aa, n_score, score_gx, \
+                                                                     attn_gx);                 \
+    break;
+    OASIS_SA_CASE(1, 4)
+    OASIS_SA_CASE(1, 8)
+    OASIS_SA_CASE(1, 16)
+    OASIS_SA_CASE(2, 4)
+    OASIS_SA_CASE(2, 8)
+    OASIS_SA_CASE(2, 16)
+#undef OASIS_SA_CASE
+    default: {
+      hipError_t e = launch_score(d, q, summ, seq_lens, scores, stream);
+      if (e != hipSuccess) return e;
+      e = launch_attention_split(d, s, q, k, v, resident, nullptr, d.table_stride, seq_lens, scale, ws,
+                                 stream, true);
+      if (e != hipSuccess) return e;
+    }
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  const TopkPlanArgs ta = topk_plan_args(d, scores, seq_lens, topk, resident, resident_next, plan,
+                                         plan_count, table, table_count);
+  const int grid2 = heads + heads * d.group;
+#define OASIS_SM_CASE(T, I)                                                                    \
+  case I:                                                                                      \
+    select_merge_kernel<T, I><<<dim3(grid2), dim3(T), 0, stream>>>(ta, (const float*)ws,       \
+                                                                   d.group, s.num_splits, out, \
+                                                                   lse, heads);                \
+    break;
+  OASIS_SELECT_DISPATCH(OASIS_SM_CASE);
+#undef OASIS_SM_CASE
+  return hipGetLastError();
+}
+
+}  // namespace oasis

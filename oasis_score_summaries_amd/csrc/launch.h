@@ -38,16 +38,28 @@ hipError_t launch_topk_plan(const Dims& d, const float* scores, const int32_t* s
                             int32_t* topk, const int32_t* resident, int32_t* resident_next,
                             int32_t* plan, int32_t* plan_count, int32_t* table,
                             int32_t* table_count, hipStream_t stream);
+// from_resident: `table` holds the resident slots ([B*H, top_k], -1 = empty) and the
+// window blocks are appended implicitly (table_count unused, table_stride = top_k +
+// the most window blocks); otherwise `table` is a compacted table of table_stride
+// columns with table_count valid entries.
 hipError_t launch_attention_split(const Dims& d, const AttnSplit& s, const void* q, const void* k,
                                   const void* v, const int32_t* table, const int32_t* table_count,
                                   int table_stride, const int32_t* seq_lens, float scale, void* ws,
-                                  hipStream_t stream);
-hipError_t launch_attention_merge(const Dims& d, const AttnSplit& s, const int32_t* table_count,
-                                  int table_stride, float* out, float* lse, const void* ws,
-                                  hipStream_t stream);
+                                  hipStream_t stream, bool from_resident = false);
+hipError_t launch_attention_merge(const Dims& d, const AttnSplit& s, float* out, float* lse,
+                                  const void* ws, hipStream_t stream);
 hipError_t launch_attention(const Dims& d, const void* q, const void* k, const void* v,
                             const int32_t* table, const int32_t* table_count, int table_stride,
                             const int32_t* seq_lens, float scale, float* out, float* lse, void* ws,
-                            hipStream_t stream);
+                            hipStream_t stream, bool from_resident = false);
+
+// The overlapped step (attention over `resident` and the window; scoring, selection
+// and plan into `resident_next`) as two fused launches on `stream`.
+hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ, const void* k,
+                                  const void* v, const int32_t* seq_lens, float* scores,
+                                  int32_t* topk, const int32_t* resident, int32_t* resident_next,
+                                  int32_t* plan, int32_t* plan_count, int32_t* table,
+                                  int32_t* table_count, float scale, float* out, float* lse,
+                                  void* ws, hipStream_t stream);
 
 }  // namespace oasis

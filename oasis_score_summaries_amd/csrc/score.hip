@@ -21,125 +21,26 @@
 // instruction fetches 64 contiguous bytes from each of 16 blocks and a wave's
 // 8 steps consume every byte of its 16 blocks once.  The query features are
 // permuted the same way, so the contraction is unchanged.
-#include "common.h"
-#include "launch.h"
+#include "score_impl.h"
 
 namespace oasis {
 
-#ifndef OASIS_SCORE_TILES_PER_WAVE
-#define OASIS_SCORE_TILES_PER_WAVE 2
-#endif
-constexpr int kScoreWaves = 4;                                   // waves per workgroup
-constexpr int kScoreTilesPerWave = OASIS_SCORE_TILES_PER_WAVE;   // 16-block MFMA tiles per wave
-constexpr int kScoreBlocksPerWG = kScoreWaves * kScoreTilesPerWave * 16;
-
-// The query fragments do not depend on the block, so the workgroup builds them once
-// in LDS (sign-split, in MFMA lane order) and every wave reads them from there.
 template <int RT>
-__global__ __launch_bounds__(256) void score_kernel(const u32x4* __restrict__ q,
-                                                    const u32x4* __restrict__ summ,
-                                                    const int32_t* __restrict__ seq_lens,
-                                                    float* __restrict__ scores, int heads,
-                                                    int max_blocks, int rows, int window) {
-  __shared__ u32x4 afrag[RT][8][64];
-  const int bh = blockIdx.y;
-  const int b = bh / heads;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = lane & 15, grp = lane >> 4;
-  const int jw = blockIdx.x * kScoreBlocksPerWG + wave * kScoreTilesPerWave * 16;  // this wave's first block
-  const int len = clamp_len(seq_lens[b], max_blocks);
-  const int n_cand = first_window_block(len, window);
-  float* out = scores + (size_t)bh * max_blocks;
-  if ((int)blockIdx.x * kScoreBlocksPerWG >= n_cand) {  // no candidate in this workgroup's range
-    for (int j = threadIdx.x; j < kScoreBlocksPerWG; j += blockDim.x) {
-      const int jb = blockIdx.x * kScoreBlocksPerWG + j;
-      if (jb < max_blocks) out[jb] = -INFINITY;
-    }
-    return;
-  }
-
-  // Loads are issued unconditionally (clamped to valid addresses, results masked
-  // later) so that no branch or wait splits them: first this thread's query chunks,
-  // then the wave's summary fragments; the query fragments can then be built while
-  // the summaries are still in flight.
-  constexpr int kQPerThread = RT * 8 * 64 / 256;
-  const u32x4* qb = q + (size_t)bh * rows * 16;
-  u32x4 qv[kQPerThread];
-#pragma unroll
-  for (int u = 0; u < kQPerThread; ++u) {
-    const int f = u * 256 + threadIdx.x;
-    const int row = 16 * (f / 512) + (f & 15);
-    const int c = 4 * ((f / 64) % 8) + ((f & 63) >> 4);
-    qv[u] = qb[(row < rows ? row : rows - 1) * 16 + (c & 15)];
-  }
-  u32x4 bv[kScoreTilesPerWave][8];
-#pragma unroll
-  for (int t = 0; t < kScoreTilesPerWave; ++t) {
-    int jb = jw + 16 * t + col;
-    jb = jb < n_cand ? jb : n_cand - 1;  // n_cand >= 1 here; columns past it are masked below
-    const size_t base = ((size_t)bh * max_blocks + jb) * 32 + grp;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) bv[t][s] = summ[base + 4 * s];
-  }
-
-  // Query fragments: (row tile r, step s, lane) holds row 16r + lane%16, features of
-  // chunk 4s + lane/16, sign-split so that kmin chunks (s < 4) meet min(q,0) and kmax
-  // chunks meet max(q,0); rows past the real ones are zero.
-#pragma unroll
-  for (int u = 0; u < kQPerThread; ++u) {
-    const int f = u * 256 + threadIdx.x;
-    const int r = f / 512, st = (f / 64) % 8, l = f & 63;
-    u32x4 x = qv[u];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = (st < 4) ? bf16x2_neg_part(x[e]) : bf16x2_pos_part(x[e]);
-    if (16 * r + (l & 15) >= rows) x = u32x4{0u, 0u, 0u, 0u};
-    afrag[r][st][l] = x;
-  }
-  __syncthreads();
-
-#pragma unroll
-  for (int t = 0; t < kScoreTilesPerWave; ++t) {
-    const int jb = jw + 16 * t + col;
-    if (jw + 16 * t >= max_blocks) break;  // uniform across the wave
-    floatx4 acc[RT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(afrag[r][s][lane]),
-                                                         as_bf16x8(bv[t][s]), acc[r], 0, 0, 0);
-      }
-    }
-    // Lane l holds rows 16r + 4*(l/16) + i of block column l%16: max over its real
-    // rows, then across the four lane groups of the column.
-    float m = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (16 * r + 4 * grp + i < rows) m = fmaxf(m, acc[r][i]);
-      }
-    }
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    if (grp == 0 && jb < max_blocks) out[jb] = (jb < n_cand) ? m : -INFINITY;
-  }
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  __shared__ ScoreShared<RT> sh;
+  score_wg<RT>(blockIdx.x, blockIdx.y, sh, a);
 }
 
 hipError_t launch_score(const Dims& d, const void* q, const void* summ, const int32_t* seq_lens,
                         float* scores, hipStream_t stream) {
   const int rows = d.group * d.queries;
-  const dim3 grid((d.max_blocks + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG, d.batch * d.heads);
+  const dim3 grid(score_grid_x(d), d.batch * d.heads);
   const dim3 block(64 * kScoreWaves);
-  const u32x4* qq = (const u32x4*)q;
-  const u32x4* ss = (const u32x4*)summ;
+  const ScoreArgs a = score_args(d, q, summ, seq_lens, scores);
   switch ((rows + 15) / 16) {
-#define OASIS_SCORE_CASE(RT)                                                                     \
-  case RT:                                                                                       \
-    score_kernel<RT><<<grid, block, 0, stream>>>(qq, ss, seq_lens, scores, d.heads, d.max_blocks, \
-                                                 rows, d.window);                                \
+#define OASIS_SCORE_CASE(RT)                                 \
+  case RT:                                                   \
+    score_kernel<RT><<<grid, block, 0, stream>>>(a);         \
     break;
     OASIS_SCORE_CASE(1)
     OASIS_SCORE_CASE(2)

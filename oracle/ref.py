@@ -236,6 +236,35 @@ def build_plan(scores: np.ndarray, topk: np.ndarray, resident: np.ndarray, seq_l
             "table": table, "table_count": table_count}
 
 
+def resident_table(resident: np.ndarray, seq_lens: np.ndarray, window: int,
+                   block: int = 16) -> Tuple[np.ndarray, np.ndarray]:
+    """The working set held as a resident slot table, written out as a table.
+
+    [legible] summary (the foreground attends over the entries resident in
+    HBM now); [xllm] section three, training flow step 2 (selected historical
+    blocks plus the local window).  The entries are the resident blocks in
+    slot order, empty slots skipped, then the window blocks
+    [first_window_block, num_blocks).  Reading: a resident block at or past
+    the first window block is listed once, as a window block (the window can
+    move past a block that was selected when the sequence was shorter).
+
+    resident: [B, H, K] (-1 = empty).  Returns table [B, H, K + ceil(W/16) + 1]
+    (-1 padded) and table_count [B, H].
+    """
+    B, H, K = resident.shape
+    T = K + -(-window // block) + 1
+    table = np.full((B, H, T), -1, dtype=np.int64)
+    table_count = np.zeros((B, H), dtype=np.int64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        w0, nb = first_window_block(L, window, block), num_blocks(L, block)
+        for h in range(H):
+            entries = [int(x) for x in resident[b, h] if 0 <= x < w0] + list(range(w0, nb))
+            table[b, h, : len(entries)] = entries
+            table_count[b, h] = len(entries)
+    return table, table_count
+
+
 # ---------------------------------------------------------------------------
 # O4  sparse decode attention over the head-wise block table
 # ---------------------------------------------------------------------------
@@ -299,3 +328,26 @@ def decode_step(q, summ, k, v, seq_lens, resident, top_k: int, window: int, cap:
     p = build_plan(s, sel, resident, seq_lens, cap, window, block)
     out, lse = sparse_attention(q, k, v, p["table"], p["table_count"], seq_lens, scale, block)
     return {"scores": s, "topk": sel, **p, "out": out, "lse": lse}
+
+
+def decode_step_overlapped(q, summ, k, v, seq_lens, resident, top_k: int, window: int, cap: int,
+                           scale: float, block: int = 16) -> Dict[str, np.ndarray]:
+    """Foreground attention over the blocks resident now, and the background
+    look-ahead that produces the resident set of the next step.
+
+    [lode] point 3 (while the current token's attention runs over the hot KV
+    entries, a background pipeline finds and stages the blocks needed next);
+    [legible] summary (foreground attention over the resident entries,
+    background look-ahead attention predicting future blocks); [xllm] section
+    three, training flow step 3.  The two parts share only their inputs: the
+    attention uses ``resident_table(resident)``; the plan is ``build_plan`` on
+    the look-ahead scores and selection.  The returned ``resident`` is the
+    next step's slot table.
+    """
+    table, tcount = resident_table(resident, seq_lens, window, block)
+    out, lse = sparse_attention(q, k, v, table, tcount, seq_lens, scale, block)
+    s = score_blocks(q, summ, seq_lens, window, block)
+    sel = topk_blocks(s, seq_lens, top_k, window, block)
+    p = build_plan(s, sel, resident, seq_lens, cap, window, block)
+    return {"scores": s, "topk": sel, **p, "out": out, "lse": lse,
+            "attn_table": table, "attn_table_count": tcount}

@@ -44,7 +44,7 @@ def _dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.exported_symbols())
@@ -141,3 +141,29 @@ def test_binding_rejects_bad_tensors_before_the_library():
     d = _dims()
     with pytest.raises(ValueError):   # CPU tensors never reach the library
         oa.topk_blocks(d, torch.zeros((2, 2, 64)), torch.zeros(2, dtype=torch.int32))
+
+
+def test_overlapped_step_argument_checks(lib):
+    """The overlapped step needs its own resident_next buffer; checked before anything
+    is queued."""
+    d = _dims()
+    need = lib.oasis_workspace_bytes(ctypes.byref(d))
+    res = ctypes.c_void_p(0x10000)
+
+    def call(res_next, ws_bytes=need):
+        return lib.oasis_decode_step_overlapped(
+            ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, res, res_next, FAKE, FAKE,
+            FAKE, FAKE, 0.1, FAKE, None, FAKE, ws_bytes, None)
+
+    assert call(None) == INVALID_ARG
+    assert call(res) == INVALID_ARG
+    assert b"own buffer" in lib.oasis_last_error()
+    assert call(ctypes.c_void_p(0x10000 + 64)) == INVALID_ARG   # overlaps
+    assert b"overlap" in lib.oasis_last_error()
+    assert call(ctypes.c_void_p(0x20000), need - 1) == WORKSPACE
+    st = lib.oasis_sparse_decode_attn_resident(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, 0.1,
+                                               FAKE, None, FAKE, need, None)
+    assert st == INVALID_ARG
+    st = lib.oasis_sparse_decode_attn_resident(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1,
+                                               FAKE, None, FAKE, need - 1, None)
+    assert st == WORKSPACE

@@ -464,3 +464,61 @@ def test_decode_step_tiny_workload():
         assert len(hot & set(sel[0, h].tolist())) >= w.planted // 2
     assert np.all(res["table_count"] == w.top_k + 4)
     assert np.all(np.isfinite(res["out"]))
+
+
+# ---------------------------------------------------------------------------
+# The working set as resident slots (foreground attention of the overlapped step)
+# ---------------------------------------------------------------------------
+
+def test_resident_table_hand_example():
+    # len 700, W 64: first window block floor(636 / 16) = 39, blocks ceil(700 / 16) = 44.
+    # Slot 1 is empty; block 40 lies in the window and is listed once, as a window block.
+    R = np.array([[[5, -1, 40, 2]]])
+    table, count = ref.resident_table(R, np.array([700]), 64)
+    assert count.tolist() == [[7]]
+    assert table[0, 0, :7].tolist() == [5, 2, 39, 40, 41, 42, 43]
+    assert np.all(table[0, 0, 7:] == -1) and table.shape[-1] == 4 + 4 + 1
+
+
+def test_resident_table_of_planned_set_is_the_plan_table():
+    r = _rng(11)
+    B, H, NB, K, W = 2, 3, 64, 12, 40
+    lens = np.array([1000, 611])
+    for trial in range(5):
+        scores = r.standard_normal((B, H, NB))
+        sel = ref.topk_blocks(scores, lens, K, W)
+        res = np.full((B, H, K), -1)
+        for b in range(B):
+            n_cand = ref.first_window_block(int(lens[b]), W)
+            for h in range(H):
+                m = min(K - trial, n_cand)
+                res[b, h, :m] = r.choice(n_cand, size=m, replace=False)
+                r.shuffle(res[b, h])
+        p = ref.build_plan(scores, sel, res, lens, 3, W)
+        table, count = ref.resident_table(p["resident"], lens, W)
+        np.testing.assert_array_equal(table, p["table"])
+        np.testing.assert_array_equal(count, p["table_count"])
+
+
+@pytest.mark.parametrize("cap", [0, 4])
+def test_overlapped_step_agrees_with_serial_when_the_plan_changes_nothing(cap):
+    """The two step orders attend over the same blocks exactly when the plan leaves
+    the slot table unchanged: cap 0, or a resident set equal to the selection."""
+    q, k, v, lens = _tiny_inputs(seed=3, NB=12, lens=(190, 150))
+    summ = ref.build_summaries(k, lens)
+    K, W = 5, 32
+    s = ref.score_blocks(q, summ, lens, W)
+    sel = ref.topk_blocks(s, lens, K, W)
+    R = sel.copy() if cap else sel[:, :, ::-1].copy()     # the selected set, in some slot order
+    a = ref.decode_step(q, summ, k, v, lens, R, K, W, cap, 0.125)
+    o = ref.decode_step_overlapped(q, summ, k, v, lens, R, K, W, cap, 0.125)
+    assert np.all(a["plan_count"] == 0) and np.all(o["plan_count"] == 0)
+    np.testing.assert_array_equal(o["resident"], R)
+    np.testing.assert_allclose(o["out"], a["out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o["lse"], a["lse"], rtol=0, atol=1e-12)
+    # and the attention differs once the plan does change the set
+    R2 = np.where(np.arange(K) < 2, -1, sel)              # two empty slots to fill
+    a2 = ref.decode_step(q, summ, k, v, lens, R2, K, W, 4, 0.125)
+    o2 = ref.decode_step_overlapped(q, summ, k, v, lens, R2, K, W, 4, 0.125)
+    assert np.all(a2["plan_count"] == 2)
+    assert np.abs(o2["out"] - a2["out"]).max() > 1e-6

@@ -33,6 +33,14 @@ MUTATIONS = {
                            "entries = [int(x) for x in r if x >= 0]"),
     "cap_rounds_to_nearest": ("return int(math.floor(float(fetch_ratio) * int(top_k) + 1e-9))",
                               "return int(round(float(fetch_ratio) * int(top_k)))"),
+    "resident_table_keeps_window_blocks": (
+        "entries = [int(x) for x in resident[b, h] if 0 <= x < w0] + list(range(w0, nb))",
+        "entries = [int(x) for x in resident[b, h] if x >= 0] + list(range(w0, nb))"),
+    "overlapped_attends_next_set": (
+        "table, tcount = resident_table(resident, seq_lens, window, block)",
+        "table, tcount = resident_table(build_plan(score_blocks(q, summ, seq_lens, window, block), "
+        "topk_blocks(score_blocks(q, summ, seq_lens, window, block), seq_lens, top_k, window, block), "
+        "resident, seq_lens, cap, window, block)['resident'], seq_lens, window, block)"),
 }
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins)
@@ -44,7 +52,12 @@ def _run_pins(mutant, monkeypatch) -> bool:
     monkeypatch.setattr(pins, "ref", mutant)
     for t in PIN_TESTS:
         params = inspect.signature(t).parameters
-        variants = [{"distinct": True}, {"distinct": False}] if "distinct" in params else [{}]
+        if "distinct" in params:
+            variants = [{"distinct": True}, {"distinct": False}]
+        elif "cap" in params:
+            variants = [{"cap": 0}, {"cap": 4}]
+        else:
+            variants = [{}]
         for kw in variants:
             try:
                 t(**kw)

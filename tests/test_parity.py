@@ -376,7 +376,25 @@ def _full_size_case(lib, w, layer=0):
     # fp32 scoring error (~1e-7 relative) is far below the 1e-5 tolerance, so nearly
     # every sampled head must reproduce the oracle's plan and table exactly
     assert n_exact >= len(heads) - 1, f"only {n_exact} of {len(heads)} sampled heads matched exactly"
-    del inp, summ, out
+    # The overlapped step on the same inputs (the benchmark's configuration): the same
+    # plan outputs, and attention over the slot table as it was before the plan.
+    _say(f"full-size {w.name} layer={layer}: overlapped step")
+    res0 = resident.to(DEV)
+    rn = torch.empty_like(res0)
+    ov = lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res0, rn,
+                                    default_scale())
+    torch.cuda.synchronize()
+    for key in ("scores", "topk", "plan", "plan_count", "table", "table_count"):
+        assert torch.equal(ov[key].cpu(), got[key]), key
+    assert torch.equal(rn.cpu(), got["resident"])
+    for (b, h) in heads:
+        lb = lens[b:b + 1].numpy()
+        table, tc = ref.resident_table(i64(resident[b:b + 1, h:h + 1]), lb, w.window)
+        eo, el = ref.sparse_attention(f64(cpu["q"][(b, h)]), f64(cpu["k"][(b, h)]),
+                                      f64(cpu["v"][(b, h)]), table, tc, lb, default_scale())
+        np.testing.assert_allclose(f64(ov["out"][b, h].cpu()), eo[0, 0], rtol=0, atol=OUT_ATOL)
+        np.testing.assert_allclose(f64(ov["lse"][b, h].cpu()), el[0, 0], rtol=0, atol=OUT_ATOL)
+    del inp, summ, out, ov
     torch.cuda.empty_cache()
 
 
@@ -413,7 +431,7 @@ def test_no_candidates_and_short_sequences(lib):
 
 
 # ---------------------------------------------------------------------------
-# Pipelined (multi-stream) step and HIP graph replay
+# Overlapped (foreground / background) step, resident-slot attention, HIP graphs
 # ---------------------------------------------------------------------------
 
 def _prepared_inputs(lib, w, seed_layer=0):
@@ -426,36 +444,87 @@ def _prepared_inputs(lib, w, seed_layer=0):
     return d, inp, summ, res
 
 
-@pytest.mark.parametrize("chunks", [2, 3, 8])
-def test_pipelined_step_matches_plain_step(lib, chunks):
+def _step_outputs(bufs, rn):
+    return {**{k: v.clone() for k, v in bufs.as_dict().items()}, "resident": rn.clone()}
+
+
+def test_overlapped_step_matches_its_parts(lib):
+    """The overlapped step is the serial step's background half plus the attention
+    over the current slot table: its plan outputs equal the serial step's bit for
+    bit, its attention equals oasis_sparse_decode_attn_resident's up to the order of
+    the merge's additions, and the attention matches the oracle's over the
+    resident table."""
     w = synth.WORKLOADS["tiny_4k"].with_(batch=5, num_kv_heads=3, fetch_ratio=0.25, ctx=4096 + 40,
                                          min_len=1000)
-    _say(f"pipelined chunks={chunks}")
+    _say("overlapped step vs its parts")
     d, inp, summ, res = _prepared_inputs(lib, w)
-    outs = []
-    for c in (1, chunks):
-        bufs = lib.StepBuffers(d, DEV)
-        rn = torch.empty_like(res)
-        st = lib.PreparedStep(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, bufs,
-                              resident_next=rn, chunks=c)
-        st()
-        torch.cuda.synchronize()
-        outs.append({**{k: v.clone() for k, v in bufs.as_dict().items()}, "resident": rn.clone()})
-    for key in outs[0]:
-        assert torch.equal(outs[0][key], outs[1][key]), key
+    scale = default_scale()
+    serial_bufs, over_bufs = lib.StepBuffers(d, DEV), lib.StepBuffers(d, DEV)
+    rn_serial, rn_over = torch.empty_like(res), torch.empty_like(res)
+    lib.decode_step(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, scale,
+                    buffers=serial_bufs, resident_next=rn_serial)
+    lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, rn_over,
+                               scale, buffers=over_bufs)
+    alone, alone_lse = lib.sparse_decode_attn_resident(d, inp["q"], inp["k"], inp["v"], res,
+                                                       inp["seq_lens"], scale)
+    torch.cuda.synchronize()
+    a, o = _step_outputs(serial_bufs, rn_serial), _step_outputs(over_bufs, rn_over)
+    for key in ("scores", "topk", "plan", "plan_count", "table", "table_count", "resident"):
+        assert torch.equal(a[key], o[key]), key
+    # Same split records; the fused merge spreads the splits over more waves, so only
+    # the order of the final fp32 additions differs.
+    np.testing.assert_allclose(f64(o["out"].cpu()), f64(alone.cpu()), rtol=0, atol=1e-6)
+    np.testing.assert_allclose(f64(o["lse"].cpu()), f64(alone_lse.cpu()), rtol=0, atol=1e-6)
+    assert not torch.equal(o["out"], a["out"])   # the plan changed the set: a different attention
+    lens = inp["seq_lens"].cpu().numpy()
+    table, tc = ref.resident_table(i64(res.cpu()), lens, w.window)
+    eo, el = ref.sparse_attention(f64(inp["q"].cpu()), f64(inp["k"].cpu()), f64(inp["v"].cpu()),
+                                  table, tc, lens, scale)
+    np.testing.assert_allclose(f64(o["out"].cpu()), eo, rtol=0, atol=OUT_ATOL)
+    np.testing.assert_allclose(f64(o["lse"].cpu()), el, rtol=0, atol=OUT_ATOL)
 
 
-@pytest.mark.parametrize("chunks", [1, 4])
-def test_graph_replay_matches_eager(lib, chunks):
-    """Every replay of a captured step, with eager work and syncs between replays,
-    gives the eager result bit for bit."""
+@pytest.mark.parametrize("G,lens,NB,K", [(4, [4096, 1000, 300], 256, 16), (1, [77, 700], 48, 5),
+                                         (16, [2048, 33], 128, 8), (8, [513, 16, 4000], 250, 40)])
+def test_attention_over_resident_slots(lib, G, lens, NB, K):
+    """Slot tables with empty slots and with blocks that the window has reached."""
+    _say(f"attention resident G={G} lens={lens} NB={NB} K={K}")
+    B, H, Q, W = len(lens), 3, 2, 64
+    q, k, v, L = _small_inputs(40 + G, B, H, G, Q, NB, lens)
+    d = _dims(lib, B, H, G, NB, Q, K, W, 0.05)
+    rng = np.random.default_rng(G + K)
+    R = np.full((B, H, K), -1, dtype=np.int64)
+    for b in range(B):
+        nb = ref.num_blocks(lens[b])
+        for h in range(H):
+            n = min(K - h, nb)                         # h empty slots (at least)
+            R[b, h, :n] = rng.choice(nb, size=n, replace=False)   # window blocks included
+            rng.shuffle(R[b, h])
+    scale = default_scale()
+    out, lse = lib.sparse_decode_attn_resident(d, q.to(DEV), k.to(DEV), v.to(DEV),
+                                               torch.from_numpy(R.astype(np.int32)).to(DEV),
+                                               L.to(DEV), scale)
+    torch.cuda.synchronize()
+    table, tc = ref.resident_table(R, L.numpy(), W)
+    eo, el = ref.sparse_attention(f64(q), f64(k), f64(v), table, tc, L.numpy(), scale)
+    np.testing.assert_allclose(f64(out), eo, rtol=0, atol=OUT_ATOL)
+    fin = np.isfinite(el)
+    assert np.array_equal(np.isneginf(f64(lse)), ~fin)
+    np.testing.assert_allclose(f64(lse)[fin], el[fin], rtol=0, atol=OUT_ATOL)
+
+
+@pytest.mark.parametrize("overlapped", [False, True])
+def test_graph_replay_matches_eager(lib, overlapped):
+    """Every replay of a captured step (the overlapped one forks a second stream
+    inside the capture), with eager work and syncs between replays, gives the
+    eager result bit for bit."""
     w = synth.WORKLOADS["tiny_4k"].with_(batch=4, fetch_ratio=0.25)
-    _say(f"graph replay chunks={chunks}")
+    _say(f"graph replay overlapped={overlapped}")
     d, inp, summ, res = _prepared_inputs(lib, w, seed_layer=3)
     bufs = lib.StepBuffers(d, DEV)
     rn = torch.empty_like(res)
     st = lib.PreparedStep(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, bufs,
-                          resident_next=rn, chunks=chunks)
+                          resident_next=rn, overlapped=overlapped)
     st()
     torch.cuda.synchronize()
     eager = {**{k: v.clone() for k, v in bufs.as_dict().items()}, "resident": rn.clone()}
