@@ -262,6 +262,18 @@ oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q,
                                           float* lse, void* ws, size_t ws_bytes,
                                           hipStream_t stream);
 
+/* oasis_decode_step_overlapped with timing markers, for measurement:
+ * events[0..2] (created by the caller with hipEventCreate) are recorded on
+ * `stream` before the first launch (scoring with the attention's block
+ * gathering), between the two launches, and after the second (selection and
+ * plan with the attention merge).  The kernels queued are the same. */
+oasis_status oasis_decode_step_overlapped_timed(
+    const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
+    const int32_t* seq_lens, float* scores, int32_t* topk, const int32_t* resident,
+    int32_t* resident_next, int32_t* plan, int32_t* plan_count, int32_t* table,
+    int32_t* table_count, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+    hipStream_t stream, hipEvent_t* events);
+
 /* oasis_decode_step with timing markers, for measurement: events[0..4]
  * (created by the caller with hipEventCreate) are recorded on `stream` before
  * the scoring kernel, after it, after the selection-and-plan kernel, after the

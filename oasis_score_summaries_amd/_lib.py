@@ -73,6 +73,10 @@ _SIGNATURES = {
     "oasis_decode_step_overlapped": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                     _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t,
                                                     _P]),
+    "oasis_decode_step_overlapped_timed": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                          _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                                                          ctypes.c_size_t, _P,
+                                                          ctypes.POINTER(ctypes.c_void_p)]),
 }
 
 _lib = None
@@ -437,12 +441,16 @@ def _hip_runtime() -> ctypes.CDLL:
 
 
 class StageEvents:
-    """Five HIP events bracketing the kernels of one fused step (see oasis_decode_step_timed)."""
+    """HIP events bracketing the kernels of one step: five for the serial step
+    (oasis_decode_step_timed), three for the overlapped one
+    (oasis_decode_step_overlapped_timed)."""
 
-    STAGES = ("score", "select_plan", "attn_split", "attn_merge")
-    N = 5
+    SERIAL_STAGES = ("score", "select_plan", "attn_split", "attn_merge")
+    OVERLAPPED_STAGES = ("score_attn_split", "select_plan_merge")
 
-    def __init__(self):
+    def __init__(self, overlapped: bool = False):
+        self.STAGES = self.OVERLAPPED_STAGES if overlapped else self.SERIAL_STAGES
+        self.N = len(self.STAGES) + 1
         h = _hip_runtime()
         self.handles = (ctypes.c_void_p * self.N)()
         for i in range(self.N):
@@ -519,8 +527,10 @@ class PreparedStep:
         st = _stream(stream)
         if self.overlapped:
             if events is not None:
-                raise ValueError("stage events time the serial step only")
-            _check(self.lib.oasis_decode_step_overlapped(*self.args, st), "oasis_decode_step_overlapped")
+                _check(self.lib.oasis_decode_step_overlapped_timed(*self.args, st, events.handles),
+                       "oasis_decode_step_overlapped_timed")
+            else:
+                _check(self.lib.oasis_decode_step_overlapped(*self.args, st), "oasis_decode_step_overlapped")
         elif events is not None:
             _check(self.lib.oasis_decode_step_timed(*self.args, st, events.handles),
                    "oasis_decode_step_timed")

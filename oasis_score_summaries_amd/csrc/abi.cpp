@@ -29,6 +29,9 @@ oasis_status hip_status(hipError_t err, const char* what) {
 // Checks `in` and fills `out`.  Returns OASIS_OK or the error (text set).
 oasis_status check_dims(const oasis_dims* in, oasis::Dims* out) {
   using namespace oasis;
+  // Launch errors are read back with hipGetLastError; drop an error left by an
+  // earlier, unrelated HIP call of the caller so that it is not reported as ours.
+  (void)hipGetLastError();
   if (in == nullptr) return fail(OASIS_ERR_INVALID_ARG, "dims is NULL");
   if (in->head_dim != kHeadDim)
     return fail(OASIS_ERR_UNSUPPORTED, "head_dim %d: only %d is implemented", in->head_dim, kHeadDim);
@@ -305,14 +308,12 @@ static oasis_status decode_step_impl(const oasis_dims* dims, const void* q, cons
   return mark(4);
 }
 
-oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q, const void* summ,
-                                          const void* k, const void* v, const int32_t* seq_lens,
-                                          float* scores, int32_t* topk, const int32_t* resident,
-                                          int32_t* resident_next, int32_t* plan,
-                                          int32_t* plan_count, int32_t* table,
-                                          int32_t* table_count, float scale, float* out,
-                                          float* lse, void* ws, size_t ws_bytes,
-                                          hipStream_t stream) {
+static oasis_status decode_step_overlapped_impl(
+    const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
+    const int32_t* seq_lens, float* scores, int32_t* topk, const int32_t* resident,
+    int32_t* resident_next, int32_t* plan, int32_t* plan_count, int32_t* table,
+    int32_t* table_count, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+    hipStream_t stream, hipEvent_t* events) {
   oasis::Dims d;
   OASIS_REQUIRE(resident_next);
   oasis_status st = check_step_args(dims, d, q, summ, k, v, seq_lens, scores, topk, resident,
@@ -322,10 +323,43 @@ oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q,
   if (resident_next == resident)
     return fail(OASIS_ERR_INVALID_ARG,
                 "resident_next must be its own buffer: the attention reads resident meanwhile");
-  return hip_status(oasis::launch_overlapped_step(d, q, summ, k, v, seq_lens, scores, topk, resident,
-                                                  resident_next, plan, plan_count, table,
-                                                  table_count, scale, out, lse, ws, stream),
-                    "decode_step_overlapped");
+  if (events != nullptr) {
+    for (int i = 0; i < 3; ++i) OASIS_REQUIRE(events[i]);
+    if ((st = hip_status(hipEventRecord(events[0], stream), "decode_step_overlapped/event")) != OASIS_OK)
+      return st;
+  }
+  st = hip_status(oasis::launch_overlapped_step(d, q, summ, k, v, seq_lens, scores, topk, resident,
+                                                resident_next, plan, plan_count, table, table_count,
+                                                scale, out, lse, ws, stream,
+                                                events == nullptr ? nullptr : events[1]),
+                  "decode_step_overlapped");
+  if (st != OASIS_OK || events == nullptr) return st;
+  return hip_status(hipEventRecord(events[2], stream), "decode_step_overlapped/event");
+}
+
+oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q, const void* summ,
+                                          const void* k, const void* v, const int32_t* seq_lens,
+                                          float* scores, int32_t* topk, const int32_t* resident,
+                                          int32_t* resident_next, int32_t* plan,
+                                          int32_t* plan_count, int32_t* table,
+                                          int32_t* table_count, float scale, float* out,
+                                          float* lse, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+  return decode_step_overlapped_impl(dims, q, summ, k, v, seq_lens, scores, topk, resident,
+                                     resident_next, plan, plan_count, table, table_count, scale,
+                                     out, lse, ws, ws_bytes, stream, nullptr);
+}
+
+oasis_status oasis_decode_step_overlapped_timed(
+    const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
+    const int32_t* seq_lens, float* scores, int32_t* topk, const int32_t* resident,
+    int32_t* resident_next, int32_t* plan, int32_t* plan_count, int32_t* table,
+    int32_t* table_count, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+    hipStream_t stream, hipEvent_t* events) {
+  OASIS_REQUIRE(events);
+  return decode_step_overlapped_impl(dims, q, summ, k, v, seq_lens, scores, topk, resident,
+                                     resident_next, plan, plan_count, table, table_count, scale,
+                                     out, lse, ws, ws_bytes, stream, events);
 }
 
 oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void* summ,

@@ -62,7 +62,7 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
                                   int32_t* topk, const int32_t* resident, int32_t* resident_next,
                                   int32_t* plan, int32_t* plan_count, int32_t* table,
                                   int32_t* table_count, float scale, float* out, float* lse,
-                                  void* ws, hipStream_t stream) {
+                                  void* ws, hipStream_t stream, hipEvent_t after_first) {
   const int heads = d.batch * d.heads;
   const AttnSplit s = attn_split(d, d.table_stride);
   const ScoreArgs sa = score_args(d, q, summ, seq_lens, scores);
@@ -99,6 +99,7 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (after_first != nullptr && (err = hipEventRecord(after_first, stream)) != hipSuccess) return err;
 
   const TopkPlanArgs ta = topk_plan_args(d, scores, seq_lens, topk, resident, resident_next, plan,
                                          plan_count, table, table_count);

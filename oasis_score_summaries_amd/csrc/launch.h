@@ -60,6 +60,6 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
                                   int32_t* topk, const int32_t* resident, int32_t* resident_next,
                                   int32_t* plan, int32_t* plan_count, int32_t* table,
                                   int32_t* table_count, float scale, float* out, float* lse,
-                                  void* ws, hipStream_t stream);
+                                  void* ws, hipStream_t stream, hipEvent_t after_first = nullptr);
 
 }  // namespace oasis
