@@ -83,6 +83,78 @@ def algorithmic_bytes(w, lens, table_count) -> dict:
     }
 
 
+# HBM traffic of the dominant kernel, measured offline with rocprofv3 byte counters
+# (FETCH_SIZE and WRITE_SIZE, one run each, scaled by what they read for the
+# --calibrate copy) and kept under profiles/ with a hash of the kernel's sources.
+# bench.py reports it only while those sources are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_attn_kernel_qwen3_8b_32k_traffic.txt")
+KERNEL_SOURCES = ("fused.hip", "score_impl.h", "attention_impl.h", "select_impl.h", "common.h", "launch.h")
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "oasis_score_summaries_amd", "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """Bytes per launch from the traffic file, or None if absent, for another
+    workload, or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split("=", 1) for line in f.read().splitlines()
+                      if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("workload") != workload or kv.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str) -> str:
+    """Traffic file text from the counter-collection CSVs of a FETCH_SIZE run and a
+    WRITE_SIZE run of ``bench.py --calibrate``."""
+    import csv
+
+    def per_kernel(d, counter):
+        vals = {}
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = []
+    scale = {}
+    mean = {}
+    for counter, d, direction in (("FETCH_SIZE", fetch_dir, "read"), ("WRITE_SIZE", write_dir, "written")):
+        vals = per_kernel(d, counter)
+        copy = [v for v in vals.get("__amd_rocclr_copyBuffer", []) if v > CALIBRATION_BYTES / 1024 / 8]
+        if not copy:
+            raise SystemExit(f"no calibration copy found in {d}")
+        scale[counter] = (CALIBRATION_BYTES / 1024) / statistics.mean(copy[:3])
+        fused = [v for k, v in vals.items() if k.startswith("void oasis::score_attn_kernel")]
+        if not fused:
+            raise SystemExit(f"no score_attn_kernel dispatch in {d}")
+        mean[counter] = statistics.mean(fused[0])
+        out.append(f"# {counter}: {statistics.mean(copy[:3]):.1f} KiB for the calibration copy "
+                   f"({CALIBRATION_BYTES >> 20} MiB {direction}) -> scale {scale[counter]:.4f}; "
+                   f"score_attn_kernel: {mean[counter]:.1f} KiB per launch over {len(fused[0])} launches")
+    fetch = mean["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
+    write = mean["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
+    head = ["# HBM traffic per launch of the fused scoring + attention-gather kernel",
+            f"# command (one run per counter): {command}"]
+    body = [f"workload = {workload}",
+            f"sources_sha256 = {kernel_sources_sha256()}",
+            f"fetch_bytes_per_launch = {int(round(fetch))}",
+            f"write_bytes_per_launch = {int(round(write))}",
+            f"traffic_bytes_per_launch = {int(round(fetch + write))}"]
+    return "\n".join(head + out + body) + "\n"
+
+
 def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     """The fp64 oracle on the host: the same step (score, top-K, plan, attention) for
     (sequence, KV head) units of input set 0, until ``budget_s`` seconds have run."""
@@ -138,7 +210,17 @@ def main(argv=None) -> int:
                     help="overlapped: attention over the resident set on one stream while the "
                          "look-ahead plans the next step on another; serial: plan, then attention "
                          "over the updated table on one stream")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic file from two rocprofv3 --pmc runs of "
+                         "'bench.py --calibrate' (FETCH_SIZE, then WRITE_SIZE) and exit")
+    ap.add_argument("--counter-command", default="", help="the command recorded in the traffic file")
     args = ap.parse_args(argv)
+    if args.summarize_counters:
+        text = summarize_counters(*args.summarize_counters, args.workload, args.counter_command)
+        with open(TRAFFIC_FILE, "w") as f:
+            f.write(text)
+        print(text, end="")
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the decode step of one layer is measured on a single "
@@ -300,7 +382,8 @@ def main(argv=None) -> int:
                    "input_sets": n_sets, "mode": args.mode, "order": args.order},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "bytes_per_launch": nb[dominant],
+                     "traffic": measured_traffic(w.name) if dominant == "score_attn_split" else None,
+                     "bytes_per_launch": nb[dominant],
                      "avg_launch_us": round(stage_us[dominant], 3)},
         "step_hbm": {"achieved": round(step_gbps, 1), "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
                      "bytes_per_step": nb["step"], "units": nb["units"]},
