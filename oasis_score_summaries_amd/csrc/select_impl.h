@@ -39,6 +39,10 @@ struct SelectShared {
 struct PlanBitmaps {
   uint32_t sel[kMaxBlocks / 32];
   uint32_t res[kMaxBlocks / 32];
+  // Per-wave counts of the plan's compactions (up to 16 waves).  Outside the LDS the
+  // plan shares with the selection, so the plan can write them before its first
+  // barrier while other waves still read the selection's output.
+  int w_new[16], w_empty[16], w_stale[16], w_vict[16];
 };
 __device__ inline void clear_bitmaps(PlanBitmaps& bm, int NB) {
   for (int w = threadIdx.x; w < (NB + 31) >> 5; w += blockDim.x) {
@@ -53,7 +57,6 @@ struct PlanShared {
   alignas(16) uint64_t st[THREADS + 32];  // stale slots, compacted: (order_key(score) << 32) | ~block
   alignas(16) int adm_list[THREADS + 16];
   int adm_sorted[THREADS];
-  int w_new[NW], w_empty[NW], w_stale[NW], w_vict[NW], w_tab[NW];
 };
 
 // Inclusive prefix sum over the threads of the workgroup; `scratch` holds NW ints
@@ -114,9 +117,13 @@ __device__ inline int count_cmp(const uint64_t* v, int n, uint64_t x) {
 
 // Selects the min(K, n_cand) best of row[0 .. n_cand) into sh.sorted_idx, best
 // first, and returns that count.  Every thread of the workgroup must call it.
+// With `bm` (cleared before the call), the selected blocks are marked in bm->sel and
+// this thread's resident block `res_block` (if in [0, NB)) in bm->res, both complete
+// when the call returns a count above zero.
 template <int THREADS, int ITEMS>
 __device__ __attribute__((always_inline)) int topk_select(const float* __restrict__ row, int n_cand, int K,
-                           SelectShared<THREADS, ITEMS>& sh) {
+                           SelectShared<THREADS, ITEMS>& sh, PlanBitmaps* bm = nullptr,
+                           int res_block = -1, int NB = 0) {
   constexpr int NW = THREADS / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m = n_cand < K ? n_cand : K;
@@ -140,6 +147,8 @@ __device__ __attribute__((always_inline)) int topk_select(const float* __restric
     sh.rmin[wave] = lmin;
   }
   __syncthreads();
+  if (bm != nullptr && res_block >= 0 && res_block < NB)   // after the clear, before the last barrier
+    atomicOr(&bm->res[res_block >> 5], 1u << (res_block & 31));
   uint32_t kmax = 0u, kmin = 0xffffffffu;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -224,7 +233,11 @@ __device__ __attribute__((always_inline)) int topk_select(const float* __restric
             for (int j = 0; j < 16; ++j) r += (u + j < nb) && a[j] > c;
           }
           const int pos = dg > d0 ? b0 + r : (r < need ? above + r : -1);
-          if (pos >= 0) sh.sorted_idx[pos] = (int)(~(uint32_t)c);
+          if (pos >= 0) {
+            const int e = (int)(~(uint32_t)c);
+            sh.sorted_idx[pos] = e;
+            if (bm != nullptr) atomicOr(&bm->sel[e >> 5], 1u << (e & 31));
+          }
         }
         __syncthreads();
         return m;
@@ -279,7 +292,9 @@ __device__ __attribute__((always_inline)) int topk_select(const float* __restric
   // LDS 16 bytes at a time, several reads in flight.
   for (int t = tid; t < m; t += THREADS) {
     const uint64_t ct = sh.cand[t];
-    sh.sorted_idx[count_cmp<true>(sh.cand, m, ct)] = (int)(~(uint32_t)ct);
+    const int e = (int)(~(uint32_t)ct);
+    sh.sorted_idx[count_cmp<true>(sh.cand, m, ct)] = e;
+    if (bm != nullptr) atomicOr(&bm->sel[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
   return m;
@@ -303,8 +318,9 @@ __device__ inline ResidentSlot load_resident_slot(const int32_t* res, const floa
 // Applies the capped-eviction rule for one (sequence, KV head).  Thread t < K passes
 // selection entry t as `s_i` (-1 = none; the entries are best first) and resident slot
 // t as `rs`; the updated slots go to `res_next`.  `bm` must have been cleared, with a
-// barrier since.  Needs K <= THREADS; every thread calls it.
-template <int THREADS>
+// barrier since; with MARKED it already holds both sets (the selection marked them).
+// Needs K <= THREADS; every thread calls it.
+template <int THREADS, bool MARKED = false>
 __device__ __attribute__((always_inline)) void plan_apply(
     int s_i, ResidentSlot rs, int32_t* res_next, int32_t* plan_row, int32_t* plan_count,
     int32_t* table_row, int32_t* table_count, int K, int C, int NB, int w0, int nblk, int T,
@@ -315,9 +331,11 @@ __device__ __attribute__((always_inline)) void plan_apply(
   if (tid >= K) s_i = -1;
   const bool s_ok = s_i >= 0 && s_i < NB;
   const bool r_ok = r_i >= 0 && r_i < NB;
-  if (s_ok) atomicOr(&bm.sel[s_i >> 5], 1u << (s_i & 31));
-  if (r_ok) atomicOr(&bm.res[r_i >> 5], 1u << (r_i & 31));
-  __syncthreads();
+  if (!MARKED) {
+    if (s_ok) atomicOr(&bm.sel[s_i >> 5], 1u << (s_i & 31));
+    if (r_ok) atomicOr(&bm.res[r_i >> 5], 1u << (r_i & 31));
+    __syncthreads();
+  }
 
   // New blocks (selection order) and empty slots (slot order): ballot ranks.
   const bool is_new = s_ok && !((bm.res[s_i >> 5] >> (s_i & 31)) & 1u);
@@ -328,9 +346,9 @@ __device__ __attribute__((always_inline)) void plan_apply(
   const int rk_empty = wave_flag_rank(empty, &c_empty);
   const int rk_stale = wave_flag_rank(stale, &c_stale);
   if (lane == 0) {
-    sh.w_new[wave] = c_new;
-    sh.w_empty[wave] = c_empty;
-    sh.w_stale[wave] = c_stale;
+    bm.w_new[wave] = c_new;
+    bm.w_empty[wave] = c_empty;
+    bm.w_stale[wave] = c_stale;
   }
   // Worst-first order of stale slots: ascending score, equal scores higher block first.
   const uint64_t st_me =
@@ -338,9 +356,9 @@ __device__ __attribute__((always_inline)) void plan_apply(
             : ~0ull;
   __syncthreads();
   int n_new, n_empty, n_stale;
-  const int pos_new = waves_before<NW>(sh.w_new, &n_new) + rk_new;
-  const int pos_empty = waves_before<NW>(sh.w_empty, &n_empty) + rk_empty;
-  const int pos_stale = waves_before<NW>(sh.w_stale, &n_stale) + rk_stale;
+  const int pos_new = waves_before<NW>(bm.w_new, &n_new) + rk_new;
+  const int pos_empty = waves_before<NW>(bm.w_empty, &n_empty) + rk_empty;
+  const int pos_stale = waves_before<NW>(bm.w_stale, &n_stale) + rk_stale;
   const int n = C < n_new ? C : n_new;
   const bool admitted = is_new && pos_new < n;
   if (admitted) sh.adm_list[pos_new] = s_i;
@@ -369,10 +387,12 @@ __device__ __attribute__((always_inline)) void plan_apply(
   }
   int c_vict;
   const int rk_vict = wave_flag_rank(victim, &c_vict);
-  if (lane == 0) sh.w_vict[wave] = c_vict;
+  if (lane == 0) bm.w_vict[wave] = c_vict;
   __syncthreads();
   int n_vict;
-  const int pos_vict = waves_before<NW>(sh.w_vict, &n_vict) + rk_vict;
+  const int pos_vict = waves_before<NW>(bm.w_vict, &n_vict) + rk_vict;
+  // Empty plus stale slots number K - |R and S| >= |S without R| >= n, so every one
+  // of the n victims takes an admitted block.
   const int n_placed = n < n_vict ? n : n_vict;
 
   int new_r = r_i;
@@ -392,15 +412,14 @@ __device__ __attribute__((always_inline)) void plan_apply(
   }
   if (tid == 0) *plan_count = n_placed;
 
-  // Table: updated resident entries in slot order, then the window blocks.
-  const bool keep = tid < K && new_r >= 0 && new_r < NB;
-  int c_tab;
-  const int rk_tab = wave_flag_rank(keep, &c_tab);
-  if (lane == 0) sh.w_tab[wave] = c_tab;
-  __syncthreads();
-  int n_res;
-  const int pos_t = waves_before<NW>(sh.w_tab, &n_res) + rk_tab;
-  if (keep) table_row[pos_t] = new_r;
+  // Table: updated resident entries in slot order, then the window blocks.  The
+  // updated set is empty exactly at the empty slots that were not filled, which
+  // are the empty slots of rank n and above (empty slots are filled in slot order);
+  // so slot t moves forward by the unfilled empty slots before it (pos_empty is the
+  // number of empty slots before t, for every thread).
+  const int unfilled_before = pos_empty > n_placed ? pos_empty - n_placed : 0;
+  const int n_res = K - (n_empty > n_placed ? n_empty - n_placed : 0);
+  if (tid < K && new_r >= 0) table_row[tid - unfilled_before] = new_r;
   const int nwin = nblk - w0;
   for (int i = tid; i < nwin; i += THREADS) table_row[n_res + i] = w0 + i;
   for (int i = n_res + nwin + tid; i < T; i += THREADS) table_row[i] = -1;
@@ -441,11 +460,15 @@ __device__ __attribute__((always_inline)) void topk_plan_wg(int bh, TopkPlanShar
   const float* srow = a.scores + (size_t)bh * NB;
   const ResidentSlot rs = load_resident_slot(a.resident + (size_t)bh * K, srow, K, NB);
   clear_bitmaps(bm, NB);
-  const int m = topk_select<THREADS, ITEMS>(srow, n_cand, K, sh.t);
-  if (m == 0) __syncthreads();  // the selection had no barrier after the clear
+  const int m = topk_select<THREADS, ITEMS>(srow, n_cand, K, sh.t, &bm, rs.block, NB);
+  if (m == 0) {  // the selection returned at once: mark the resident set here
+    __syncthreads();
+    if (rs.block >= 0 && rs.block < NB) atomicOr(&bm.res[rs.block >> 5], 1u << (rs.block & 31));
+    __syncthreads();
+  }
   for (int t = threadIdx.x; t < K; t += THREADS) a.topk[(size_t)bh * K + t] = t < m ? sh.t.sorted_idx[t] : -1;
   const int s_i = (threadIdx.x < m) ? sh.t.sorted_idx[threadIdx.x] : -1;
-  plan_apply<THREADS>(s_i, rs, a.resident_next + (size_t)bh * K,
+  plan_apply<THREADS, true>(s_i, rs, a.resident_next + (size_t)bh * K,
                       a.plan == nullptr ? nullptr : a.plan + (size_t)bh * C * 3, a.plan_count + bh,
                       a.table + (size_t)bh * T, a.table_count + bh, K, C, NB, n_cand,
                       num_blocks(len), T, bm, sh.p);

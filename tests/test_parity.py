@@ -484,6 +484,43 @@ def test_overlapped_step_matches_its_parts(lib):
     np.testing.assert_allclose(f64(o["lse"].cpu()), el, rtol=0, atol=OUT_ATOL)
 
 
+def test_overlapped_step_repeated_over_rotating_inputs(lib):
+    """Steps queued back to back over rotating input sets, sharing one workspace:
+    every step must give its own set's results (the scores handed from the scoring
+    workgroups to the selection inside one launch must never be another step's)."""
+    w = synth.WORKLOADS["qwen3_8b_32k"].with_(batch=2, num_kv_heads=4)
+    _say("overlapped step repeated over rotating inputs")
+    n_sets, n_steps = 3, 24
+    sets = []
+    for i in range(n_sets):
+        d, inp, summ, res = _prepared_inputs(lib, w, seed_layer=i)
+        bufs = lib.StepBuffers(d, DEV)
+        rn = torch.empty_like(res)
+        lib.decode_step(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, default_scale(),
+                        buffers=bufs, resident_next=rn)
+        alone, _ = lib.sparse_decode_attn_resident(d, inp["q"], inp["k"], inp["v"], res,
+                                                   inp["seq_lens"], default_scale())
+        torch.cuda.synchronize()
+        sets.append((d, inp, summ, res, _step_outputs(bufs, rn), alone.clone()))
+    shared_ws = lib.StepBuffers(sets[0][0], DEV).ws
+    runs = []
+    for i in range(n_steps):
+        d, inp, summ, res, _, _ = sets[i % n_sets]
+        bufs = lib.StepBuffers(d, DEV)
+        bufs.ws = shared_ws
+        rn = torch.empty_like(res)
+        lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, rn,
+                                   default_scale(), buffers=bufs)
+        runs.append((bufs, rn))
+    torch.cuda.synchronize()
+    for i, (bufs, rn) in enumerate(runs):
+        _, _, _, _, ref_out, alone = sets[i % n_sets]
+        got = _step_outputs(bufs, rn)
+        for key in ("scores", "topk", "plan", "plan_count", "table", "table_count", "resident"):
+            assert torch.equal(got[key], ref_out[key]), f"step {i}: {key}"
+        assert (got["out"] - alone).abs().max().item() <= 1e-6, f"step {i}: out"
+
+
 @pytest.mark.parametrize("G,lens,NB,K", [(4, [4096, 1000, 300], 256, 16), (1, [77, 700], 48, 5),
                                          (16, [2048, 33], 128, 8), (8, [513, 16, 4000], 250, 40)])
 def test_attention_over_resident_slots(lib, G, lens, NB, K):
