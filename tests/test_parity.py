@@ -408,6 +408,64 @@ def test_full_size_reasoning_layer(lib, layer):
     _full_size_case(lib, synth.WORKLOADS["reasoning_36l"], layer=layer)
 
 
+def test_largest_supported_sizes(lib):
+    """max_blocks = 32768 (a 512K-token context), K = 1024, a 4096-token window, 16
+    query heads and a cap of 512, a ragged last block: both step orders.  Scores are
+    checked on sampled blocks (the oracle's product over every block would not fit
+    the host), selection, plan and attention on the GPU's own scores and tables."""
+    B, H, G, Q, NB, K, W, ratio = 1, 1, 16, 2, 32768, 1024, 4096, 0.5
+    L = NB * 16 - 5
+    _say("largest sizes: generating")
+    g = torch.Generator().manual_seed(77)
+    q = torch.randn((B, H, G, Q, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((B, H, NB, 16, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, NB, 16, 128), generator=g).to(torch.bfloat16)
+    lens = torch.tensor([L], dtype=torch.int32)
+    d = _dims(lib, B, H, G, NB, Q, K, W, ratio)
+    C = lib.fetch_cap(d)
+    assert C == 512
+    n_cand = ref.first_window_block(L, W)
+    res = synth.random_resident(K, n_cand, 100, 5).reshape(1, 1, K)
+    qd, kd, vd, ld = q.to(DEV), k.to(DEV), v.to(DEV), lens.to(DEV)
+    summ = lib.build_summaries(d, kd, ld)
+    _say("largest sizes: serial and overlapped steps")
+    ser = lib.decode_step(d, qd, summ, kd, vd, ld, res.to(DEV).clone(), default_scale())
+    ser = {key: val.cpu() for key, val in ser.items()}
+    rn = torch.empty_like(res).to(DEV)
+    ov = lib.decode_step_overlapped(d, qd, summ, kd, vd, ld, res.to(DEV), rn, default_scale())
+    ov = {key: val.cpu() for key, val in ov.items()}
+    torch.cuda.synchronize()
+    # scores of sampled blocks against the oracle on those blocks alone
+    rng = np.random.default_rng(3)
+    blocks = np.sort(rng.choice(n_cand, size=256, replace=False))
+    summ_s = f64(summ[:, :, blocks].cpu())
+    exp_s = ref.score_blocks(f64(q), summ_s, np.array([len(blocks) * 16]), 0)
+    floor = score_floor(f64(q), summ_s)
+    check_scores(f64(ser["scores"][:, :, blocks]), exp_s, floor, "sampled scores")
+    np.testing.assert_array_equal(f64(summ[:, :, blocks[:8]].cpu()),
+                                  ref.build_summaries(f64(k[:, :, blocks[:8]]),
+                                                      np.array([8 * 16]))[:, :, :8])
+    # selection and plan on the GPU's own scores (both orders share them)
+    sc = f64(ser["scores"])
+    np.testing.assert_array_equal(f64(ov["scores"]), sc)
+    sel = ref.topk_blocks(sc, lens.numpy(), K, W)
+    np.testing.assert_array_equal(i64(ser["topk"]), sel)
+    plan = ref.build_plan(sc, sel, i64(res), lens.numpy(), C, W)
+    for key in ("plan", "plan_count", "resident", "table", "table_count"):
+        np.testing.assert_array_equal(i64(ser[key]), plan[key], err_msg=key)
+        np.testing.assert_array_equal(i64(ov[key]), plan[key], err_msg=key)
+    assert int(ser["plan_count"][0, 0]) == C
+    # attention: serial over the updated table, overlapped over the slot table as it was
+    _say("largest sizes: oracle attention")
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    eo, _ = ref.sparse_attention(qf, kf, vf, plan["table"], plan["table_count"], lens.numpy(),
+                                 default_scale())
+    np.testing.assert_allclose(f64(ser["out"]), eo, rtol=0, atol=OUT_ATOL)
+    table, tc = ref.resident_table(i64(res), lens.numpy(), W)
+    eo2, _ = ref.sparse_attention(qf, kf, vf, table, tc, lens.numpy(), default_scale())
+    np.testing.assert_allclose(f64(ov["out"]), eo2, rtol=0, atol=OUT_ATOL)
+
+
 # ---------------------------------------------------------------------------
 # Degenerate cases
 # ---------------------------------------------------------------------------
