@@ -58,14 +58,9 @@ size_t attn_workspace_bytes(const Dims& d, int table_stride) {
   return align256((size_t)d.batch * d.heads * s.num_splits * d.group * kRec * sizeof(float));
 }
 
-size_t attn_workspace_bytes_per_sequence(const Dims& d, int table_stride) {
-  const AttnSplit s = attn_split(d, table_stride);
-  return (size_t)d.heads * s.num_splits * d.group * kRec * sizeof(float);
-}
-
 // Kernels: one workgroup per (split, sequence x KV head), and one per query head.
 template <int GP, bool RES>
-__global__ __launch_bounds__(256, OASIS_ATTN_MIN_WAVES) void attn_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void attn_split_kernel(AttnArgs a) {
   __shared__ AttnShared<GP> sh;
   attn_split_wg<GP, RES>(blockIdx.x, blockIdx.y, sh, a);
 }

@@ -8,7 +8,7 @@
 
 namespace oasis {
 
-constexpr int kAttnWaves = 4;                 // one table entry per wave and round
+constexpr int kAttnWaves = kWavesPerWG;                 // one table entry per wave and round
 constexpr int kAttnMaxSplits = 256;           // partials per head
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;

@@ -14,6 +14,12 @@ constexpr int kMaxTopK = 1024;
 constexpr int kMaxRows = 128;       // G * Q limit of the score kernel (8 row tiles of 16)
 constexpr int kMaxGroup = 16;       // query heads per KV head in the attention kernel
 constexpr int kMaxTableStride = 4096;
+// Waves per workgroup of the scoring and attention-gather kernels (one value for
+// both, so that the fused kernel of the overlapped step can hold either role).
+#ifndef OASIS_WAVES_PER_WG
+#define OASIS_WAVES_PER_WG 4
+#endif
+constexpr int kWavesPerWG = OASIS_WAVES_PER_WG;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));

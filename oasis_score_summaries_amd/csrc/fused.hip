@@ -24,8 +24,10 @@
 
 namespace oasis {
 
+static_assert(kScoreWaves == kAttnWaves, "one workgroup size for both roles");
+
 template <int RT, int GP>
-__global__ __launch_bounds__(256, OASIS_ATTN_MIN_WAVES) void score_attn_kernel(ScoreArgs sa, AttnArgs aa,
+__global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void score_attn_kernel(ScoreArgs sa, AttnArgs aa,
                                                                              int n_score, int score_gx,
                                                                              int attn_gx) {
   __shared__ union {
@@ -79,7 +81,7 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
   switch (rt <= 2 ? rt * 100 + gp : 0) {
 #define OASIS_SA_CASE(RT, GP)                                                                  \
   case RT * 100 + GP:                                                                          \
-    score_attn_kernel<RT, GP><<<dim3(grid1), dim3(256), 0, stream>>>(sa, aa, n_score, score_gx, \
+    score_attn_kernel<RT, GP><<<dim3(grid1), dim3(64 * kAttnWaves), 0, stream>>>(sa, aa, n_score, score_gx, \
                                                                      attn_gx);                 \
     break;
     OASIS_SA_CASE(1, 4)

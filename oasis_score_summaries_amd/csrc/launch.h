@@ -21,8 +21,6 @@ struct AttnSplit {
 };
 AttnSplit attn_split(const Dims& d, int table_stride);
 size_t attn_workspace_bytes(const Dims& d, int table_stride);
-// Workspace bytes owned by one sequence (a run of sequences owns a contiguous slice).
-size_t attn_workspace_bytes_per_sequence(const Dims& d, int table_stride);
 
 hipError_t launch_build_summaries(const Dims& d, const void* k, const int32_t* seq_lens, void* summ,
                                   hipStream_t stream);

@@ -26,7 +26,7 @@
 namespace oasis {
 
 template <int RT>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreArgs a) {
   __shared__ ScoreShared<RT> sh;
   score_wg<RT>(blockIdx.x, blockIdx.y, sh, a);
 }

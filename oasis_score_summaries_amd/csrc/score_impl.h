@@ -11,7 +11,8 @@ namespace oasis {
 #ifndef OASIS_SCORE_TILES_PER_WAVE
 #define OASIS_SCORE_TILES_PER_WAVE 2
 #endif
-constexpr int kScoreWaves = 4;                                   // waves per workgroup
+constexpr int kScoreWaves = kWavesPerWG;                         // waves per workgroup
+constexpr int kScoreThreads = 64 * kScoreWaves;
 constexpr int kScoreTilesPerWave = OASIS_SCORE_TILES_PER_WAVE;   // 16-block MFMA tiles per wave
 constexpr int kScoreBlocksPerWG = kScoreWaves * kScoreTilesPerWave * 16;
 
@@ -59,12 +60,12 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
   // later) so that no branch or wait splits them: first this thread's query chunks,
   // then the wave's summary fragments; the query fragments can then be built while
   // the summaries are still in flight.
-  constexpr int kQPerThread = RT * 8 * 64 / 256;
+  constexpr int kQPerThread = RT * 8 * 64 / kScoreThreads;
   const u32x4* qb = q + (size_t)bh * rows * 16;
   u32x4 qv[kQPerThread];
 #pragma unroll
   for (int u = 0; u < kQPerThread; ++u) {
-    const int f = u * 256 + threadIdx.x;
+    const int f = u * kScoreThreads + threadIdx.x;
     const int row = 16 * (f / 512) + (f & 15);
     const int c = 4 * ((f / 64) % 8) + ((f & 63) >> 4);
     qv[u] = qb[(row < rows ? row : rows - 1) * 16 + (c & 15)];
@@ -84,7 +85,7 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
   // chunks meet max(q,0); rows past the real ones are zero.
 #pragma unroll
   for (int u = 0; u < kQPerThread; ++u) {
-    const int f = u * 256 + threadIdx.x;
+    const int f = u * kScoreThreads + threadIdx.x;
     const int r = f / 512, st = (f / 64) % 8, l = f & 63;
     u32x4 x = qv[u];
 #pragma unroll
