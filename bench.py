@@ -6,8 +6,9 @@ min/max key summaries, select the top-K blocks per KV head, build the capped
 transfer plan against the resident set, and run sparse attention of the target
 queries over the head-wise working set.  By default the step is the pipeline
 the OasisKV pages describe (oasis_decode_step_overlapped): the foreground
-attention over the blocks resident now runs on one stream while the background
-look-ahead (scoring, top-K, plan for the next step) runs on another.  With
+attention over the blocks resident now runs beside the background look-ahead
+(scoring, top-K, plan for the next step), as workgroups of the same two
+launches on one stream.  With
 --order serial it is oasis_decode_step: plan first, then attention over the
 updated table, all on one stream; the JSON line reports that time as well.
 Inputs are seeded synthetic tensors already resident in HBM.  Several
@@ -83,11 +84,46 @@ def algorithmic_bytes(w, lens, table_count) -> dict:
     }
 
 
+def percentiles(xs) -> dict:
+    """p10, median and p90 of a sample (nearest-rank on the sorted values)."""
+    v = sorted(xs)
+    pick = lambda p: v[min(len(v) - 1, max(0, math.ceil(p * len(v)) - 1))]
+    return {"p10": pick(0.10), "p50": statistics.median(v), "p90": pick(0.90), "n": len(v)}
+
+
+def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 20) -> float:
+    """Achievable HBM GB/s of a plain device-to-device copy: two buffers of nbytes
+    each (four times the 256 MB last-level cache), bytes read plus bytes written
+    per copy, over reps back-to-back copies timed with events."""
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
+
+
 # HBM traffic of the dominant kernel, measured offline with rocprofv3 byte counters
 # (FETCH_SIZE and WRITE_SIZE, one run each, scaled by what they read for the
 # --calibrate copy) and kept under profiles/ with a hash of the kernel's sources.
-# bench.py reports it only while those sources are unchanged.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_attn_kernel_qwen3_8b_32k_traffic.txt")
+# bench.py reports it only while those sources are unchanged.  The dominant kernel
+# is the overlapped step's first launch, scoring with attention gathering.
+LAUNCH1_KERNELS = ("score_attn_kernel",)
+
+
+def traffic_file(kernel: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+
+
 KERNEL_SOURCES = ("fused.hip", "score_impl.h", "attention_impl.h", "select_impl.h", "common.h", "launch.h")
 
 
@@ -100,11 +136,11 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(kernel: str, workload: str):
     """Bytes per launch from the traffic file, or None if absent, for another
     workload, or taken on other kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(kernel, workload)) as f:
             kv = dict(line.split("=", 1) for line in f.read().splitlines()
                       if "=" in line and not line.startswith("#"))
     except OSError:
@@ -115,9 +151,9 @@ def measured_traffic(workload: str):
     return int(kv["traffic_bytes_per_launch"])
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str) -> str:
-    """Traffic file text from the counter-collection CSVs of a FETCH_SIZE run and a
-    WRITE_SIZE run of ``bench.py --calibrate``."""
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str):
+    """(kernel, traffic file text) from the counter-collection CSVs of a FETCH_SIZE
+    run and a WRITE_SIZE run of ``bench.py --calibrate``."""
     import csv
 
     def per_kernel(d, counter):
@@ -136,28 +172,39 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
         if not copy:
             raise SystemExit(f"no calibration copy found in {d}")
         scale[counter] = (CALIBRATION_BYTES / 1024) / statistics.mean(copy[:3])
-        fused = [v for k, v in vals.items() if k.startswith("void oasis::score_attn_kernel")]
+        kernel, fused = None, []
+        for name in LAUNCH1_KERNELS:
+            fused = [v for k, v in vals.items() if k.startswith(f"void oasis::{name}<")]
+            if fused:
+                kernel = name
+                break
         if not fused:
-            raise SystemExit(f"no score_attn_kernel dispatch in {d}")
+            raise SystemExit(f"no dispatch of {' or '.join(LAUNCH1_KERNELS)} in {d}")
         mean[counter] = statistics.mean(fused[0])
         out.append(f"# {counter}: {statistics.mean(copy[:3]):.1f} KiB for the calibration copy "
                    f"({CALIBRATION_BYTES >> 20} MiB {direction}) -> scale {scale[counter]:.4f}; "
-                   f"score_attn_kernel: {mean[counter]:.1f} KiB per launch over {len(fused[0])} launches")
+                   f"{kernel}: {mean[counter]:.1f} KiB per launch over {len(fused[0])} launches")
     fetch = mean["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
     write = mean["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
-    head = ["# HBM traffic per launch of the fused scoring + attention-gather kernel",
+    head = [f"# HBM traffic per launch of {kernel} (the fused scoring + attention-gather launch)",
             f"# command (one run per counter): {command}"]
-    body = [f"workload = {workload}",
+    body = [f"kernel = {kernel}", f"workload = {workload}",
             f"sources_sha256 = {kernel_sources_sha256()}",
             f"fetch_bytes_per_launch = {int(round(fetch))}",
             f"write_bytes_per_launch = {int(round(write))}",
             f"traffic_bytes_per_launch = {int(round(fetch + write))}"]
-    return "\n".join(head + out + body) + "\n"
+    return kernel, "\n".join(head + out + body) + "\n"
 
 
 def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     """The fp64 oracle on the host: the same step (score, top-K, plan, attention) for
-    (sequence, KV head) units of input set 0, until ``budget_s`` seconds have run."""
+    (sequence, KV head) units of input set 0, until ``budget_s`` seconds have run,
+    in two modes: as written, one unit after another on one core; then the same
+    oracle mapped over the units by a pool of worker threads, one per core up to
+    16 (numpy leaves the interpreter lock while it works on arrays), for at most
+    ``budget_s`` seconds more."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
@@ -169,28 +216,50 @@ def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     res = s0["resident"].cpu()
     units = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
     f64 = lambda t: t.to(torch.float64).numpy()
-    done, elapsed = 0, 0.0
     scale = 1.0 / math.sqrt(128)
+    step = ref.decode_step_overlapped if overlapped else ref.decode_step
+
+    def unit_inputs(b, h):
+        return (f64(s0["q"][b:b + 1, h:h + 1].cpu()), f64(s0["summ"][b:b + 1, h:h + 1].cpu()),
+                f64(s0["k"][b:b + 1, h:h + 1].cpu()), f64(s0["v"][b:b + 1, h:h + 1].cpu()),
+                lens[b:b + 1].numpy(), res[b:b + 1, h:h + 1].numpy().astype(np.int64))
+
+    def run(x):
+        step(*x, w.top_k, w.window, w.cap, scale)
+
+    done, elapsed = 0, 0.0
     with threadpool_limits(1):
         for (b, h) in units:
-            qh = f64(s0["q"][b:b + 1, h:h + 1].cpu())
-            kh = f64(s0["k"][b:b + 1, h:h + 1].cpu())
-            vh = f64(s0["v"][b:b + 1, h:h + 1].cpu())
-            sh = f64(s0["summ"][b:b + 1, h:h + 1].cpu())
-            L = lens[b:b + 1].numpy()
+            x = unit_inputs(b, h)              # conversion to fp64 is not timed
             t = time.perf_counter()
-            step = ref.decode_step_overlapped if overlapped else ref.decode_step
-            step(qh, sh, kh, vh, L, res[b:b + 1, h:h + 1].numpy().astype(np.int64),
-                 w.top_k, w.window, w.cap, scale)
+            run(x)
             elapsed += time.perf_counter() - t
             done += 1
             if elapsed >= budget_s:
                 break
     per_step = elapsed / done * len(units)
-    return {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {len(units)} (sequence, KV head) units of one step, fp64 numpy, "
-                      f"{elapsed:.1f} s, scaled to a whole step",
-            "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+    out = {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done} of {len(units)} (sequence, KV head) units of one step, fp64 numpy, "
+                     f"{elapsed:.1f} s, scaled to a whole step",
+           "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    done_p, elapsed_p = 0, 0.0
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as pool:
+        for c in range(0, len(units), workers):
+            chunk = [unit_inputs(b, h) for (b, h) in units[c:c + workers]]
+            t = time.perf_counter()
+            list(pool.map(run, chunk))
+            elapsed_p += time.perf_counter() - t
+            done_p += len(chunk)
+            del chunk
+            if elapsed_p >= budget_s:
+                break
+    out["pool"] = {"value": done_p / elapsed_p / len(units), "unit": "steps/s", "cores": workers,
+                   "kind": "oracle",
+                   "sample": f"{done_p} of {len(units)} units of one step over a pool of {workers} "
+                             f"threads, {workers} units at a time, {elapsed_p:.1f} s of wall time"}
+    return out
 
 
 def main(argv=None) -> int:
@@ -216,8 +285,8 @@ def main(argv=None) -> int:
     ap.add_argument("--counter-command", default="", help="the command recorded in the traffic file")
     args = ap.parse_args(argv)
     if args.summarize_counters:
-        text = summarize_counters(*args.summarize_counters, args.workload, args.counter_command)
-        with open(TRAFFIC_FILE, "w") as f:
+        kernel, text = summarize_counters(*args.summarize_counters, args.workload, args.counter_command)
+        with open(traffic_file(kernel, args.workload), "w") as f:
             f.write(text)
         print(text, end="")
         return 0
@@ -306,10 +375,26 @@ def main(argv=None) -> int:
                 step_list[i % n_sets]()
         ev1.record()
         torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / n, n, time.perf_counter() - t0, graph
+        ms = ev0.elapsed_time(ev1) / n
+        wall = time.perf_counter() - t0
+        # Spread: the same work again with an event after every graph replay (one
+        # rotation through the input sets) or every eager step; per-step ms of each.
+        n_samples = min(reps if graph is not None else n, 300)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_samples + 1)]
+        evs[0].record()
+        for i in range(n_samples):
+            if graph is not None:
+                graph.replay()
+            else:
+                step_list[i % n_sets]()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        per = n_sets if graph is not None else 1
+        spread = [evs[i].elapsed_time(evs[i + 1]) / per for i in range(n_samples)]
+        return ms, n, wall, graph, spread
 
     # ---- the timed region (the chosen order), then the other order for reference ------
-    ms_per_step, n_timed, wall_s, graph = timed(steps)
+    ms_per_step, n_timed, wall_s, graph, spread = timed(steps)
     check = {}
     if graph is not None:
         # The graph's last step ran set n_sets-1; an eager run of it must give the same bits.
@@ -319,7 +404,8 @@ def main(argv=None) -> int:
         check["graph_matches_eager"] = bool(torch.equal(out_graph, buffers.out) and
                                             torch.equal(res_graph, res_next))
     other = "serial" if args.order == "overlapped" else "overlapped"
-    ms_other, _, _, _ = timed(serial_steps if other == "serial" else over_steps)
+    ms_other, _, _, _, _ = timed(serial_steps if other == "serial" else over_steps)
+    graph_mode = graph is not None
     del graph
 
     # ---- per-launch times: HIP events around each launch, on the launch stream --------
@@ -340,11 +426,13 @@ def main(argv=None) -> int:
                 for k, v in evs[i].elapsed_ms().items():
                     acc[k].append(v)
             done += n
-        return {k: 1e3 * statistics.mean(v) for k, v in acc.items()}, "eager, queued in batches of 30"
+        return {k: [1e3 * x for x in v] for k, v in acc.items()}
 
-    stage_us, stage_method = evented(serial_steps, False)
-    over_us, _ = evented(over_steps, True)
-    stage_us.update(over_us)
+    stage_samples = evented(serial_steps, False)
+    stage_samples.update(evented(over_steps, True))
+    stage_us = {k: statistics.mean(v) for k, v in stage_samples.items()}
+    stage_method = "eager, queued in batches of 30"
+    copy_gbps = copy_bandwidth(torch, dev)
 
     # ---- bytes and roofline ------------------------------------------------------------------
     torch.cuda.synchronize()
@@ -358,10 +446,16 @@ def main(argv=None) -> int:
     nb = algorithmic_bytes(w, s0["seq_lens"].cpu(), blocks)
     step_gbps = nb["step"] / (ms_per_step * 1e-3) / 1e9
     if args.order == "overlapped":
-        dominant = "score_attn_split"     # the fused first launch: summaries and K/V blocks
+        # The first launch: the scoring with the attention gathering (summaries,
+        # scores, K/V blocks); two kernels back to back above 32 query rows per head.
+        dominant = "score_attn_split"
+        kernel = "score_attn_kernel" if w.group * w.queries <= 32 else "score_kernel+attn_split_kernel"
+        dom_bytes = nb["score_attn_split"]
     else:
         dominant = max(("score", "attn_split"), key=lambda k: stage_us[k])
-    dom_gbps = nb[dominant] / (stage_us[dominant] * 1e-6) / 1e9
+        kernel = {"score": "score_kernel", "attn_split": "attn_split_kernel"}[dominant]
+        dom_bytes = nb[dominant]
+    dom_gbps = dom_bytes / (stage_us[dominant] * 1e-6) / 1e9
 
     result = {
         "metric": METRIC,
@@ -380,11 +474,18 @@ def main(argv=None) -> int:
                    "context": w.ctx, "queries_per_head": w.queries, "top_k": w.top_k,
                    "window_tokens": w.window, "fetch_ratio": w.fetch_ratio, "cap": w.cap,
                    "input_sets": n_sets, "mode": args.mode, "order": args.order},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(dom_gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(dom_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name) if dominant == "score_attn_split" else None,
-                     "bytes_per_launch": nb[dominant],
-                     "avg_launch_us": round(stage_us[dominant], 3)},
+                     "traffic": measured_traffic(kernel, w.name),
+                     "bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(stage_us[dominant], 3),
+                     "launch_us": {k: round(v, 3) if isinstance(v, float) else v
+                                   for k, v in percentiles(stage_samples[dominant]).items()},
+                     "copy_gbps": round(copy_gbps, 1),
+                     "frac_of_copy": round(dom_gbps / copy_gbps, 4)},
+        "step_ms": {k: round(v, 6) if isinstance(v, float) else v for k, v in percentiles(spread).items()},
+        "step_ms_sample": ("per graph replay (one step of each input set), divided by the sets"
+                           if graph_mode else "per eager step"),
         "step_hbm": {"achieved": round(step_gbps, 1), "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
                      "bytes_per_step": nb["step"], "units": nb["units"]},
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},

@@ -38,3 +38,28 @@ def test_algorithmic_bytes_by_hand():
     q_all = 1 * 2 * 4 * 4 * 256
     out = 1 * 2 * 4 * 129 * 4
     assert nb["step"] == cand * 512 + 40 * 8192 + q_all + out
+
+
+def test_percentiles_nearest_rank():
+    p = bench.percentiles(list(range(1, 11)))           # 1..10
+    assert (p["p10"], p["p50"], p["p90"], p["n"]) == (1, 5.5, 9, 10)
+    assert bench.percentiles([3.0])["p90"] == 3.0
+
+
+def test_cpu_baseline_both_modes_on_the_tiny_workload():
+    """The oracle timing leg runs on CPU tensors: one core, then the worker pool."""
+    import numpy as np
+
+    from oracle import ref
+    w = synth.WORKLOADS["tiny_4k"]
+    inp = synth.generate(w, "cpu")
+    f64 = lambda t: t.to(torch.float64).numpy()
+    lens = inp["seq_lens"].numpy()
+    summ = ref.build_summaries(f64(inp["k"]), lens)
+    resident = torch.full((w.batch, w.num_kv_heads, w.top_k), -1, dtype=torch.int32)
+    sets = [{"q": inp["q"], "k": inp["k"], "v": inp["v"], "seq_lens": inp["seq_lens"],
+             "summ": torch.from_numpy(summ).to(torch.bfloat16), "resident": resident}]
+    out = bench.cpu_baseline(w, sets, budget_s=5.0, overlapped=True)
+    assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
+    assert out["pool"]["value"] > 0 and 1 <= out["pool"]["cores"] <= 16
+    assert np.isfinite(out["pool"]["value"])

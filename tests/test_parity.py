@@ -506,15 +506,22 @@ def _step_outputs(bufs, rn):
     return {**{k: v.clone() for k, v in bufs.as_dict().items()}, "resident": rn.clone()}
 
 
-def test_overlapped_step_matches_its_parts(lib):
+@pytest.mark.parametrize("shape", [
+    {},                                                # 259 blocks, K = 16
+    {"group": 8, "num_drafts": 1},                     # 8 query heads per KV head
+    {"top_k": 300, "ctx": 8192 + 40},                  # K above 256 (1024-thread selection)
+    {"ctx": 2048 * 16 + 40, "min_len": 30000, "top_k": 64},   # 2051 blocks
+    {"group": 8, "num_drafts": 4},                     # 40 query rows: scoring in its own kernel
+])
+def test_overlapped_step_matches_its_parts(lib, shape):
     """The overlapped step is the serial step's background half plus the attention
     over the current slot table: its plan outputs equal the serial step's bit for
     bit, its attention equals oasis_sparse_decode_attn_resident's up to the order of
     the merge's additions, and the attention matches the oracle's over the
-    resident table."""
-    w = synth.WORKLOADS["tiny_4k"].with_(batch=5, num_kv_heads=3, fetch_ratio=0.25, ctx=4096 + 40,
-                                         min_len=1000)
-    _say("overlapped step vs its parts")
+    resident table.  Shapes on both sides of the fused kernels' limits."""
+    base = dict(batch=5, num_kv_heads=3, fetch_ratio=0.25, ctx=4096 + 40, min_len=1000)
+    w = synth.WORKLOADS["tiny_4k"].with_(**{**base, **shape})
+    _say(f"overlapped step vs its parts {shape}")
     d, inp, summ, res = _prepared_inputs(lib, w)
     scale = default_scale()
     serial_bufs, over_bufs = lib.StepBuffers(d, DEV), lib.StepBuffers(d, DEV)
