@@ -3,6 +3,7 @@
 Test infrastructure only: imported by the tests, the package smoke check and
 the benchmark's CPU-baseline leg, never by the HIP library or its binding.
 """
-from .ref import (build_plan, build_summaries, decode_step, decode_step_overlapped,  # noqa: F401
-                  fetch_cap, first_window_block, num_blocks, resident_table, score_blocks,
-                  sparse_attention, topk_blocks)
+from .ref import (append_token, build_plan, build_summaries, decode_step,  # noqa: F401
+                  decode_step_overlapped, execute_plan, fetch_cap, fill_working_set,
+                  first_window_block, num_blocks, pool_attention, resident_table, score_blocks,
+                  sparse_attention, topk_blocks, window_ring_slots)

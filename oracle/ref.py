@@ -311,6 +311,155 @@ def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, table: np.ndar
 
 
 # ---------------------------------------------------------------------------
+# Executing the plan: the working set in HBM
+# ---------------------------------------------------------------------------
+#
+# The full K/V of every sequence stays in its tier (host memory, or HBM when it
+# fits), addressed as before by (sequence, KV head, logical block): that page
+# table never changes.  HBM holds each KV head's working set: a pool of K block
+# slots that the head's resident slot table maps to logical blocks (the
+# head-wise logical-to-logical map), and a ring of window blocks.  Sources:
+# [xllm] section three, component table (head-wise mapping: a logical-to-logical
+# layer above the paged cache, a different sparse block set per KV head) and
+# training flow step 2 (after the sparsification conversion the full cache sits
+# in CPU memory and the GPU keeps only the selected historical blocks and the
+# local window); [xllm] section four, innovations table (the page table stays,
+# only head-wise mapping entries change); [legible] FAQ Q4; [lode] points 1 and 3
+# (hot entries in HBM, needed blocks pulled in from the larger tier).
+# Readings: a pool slot holds one whole block (16 tokens of K and of V) and slot s
+# of the pool is slot s of the slot table; logical block j of the window lives in
+# ring slot j mod (ceil(W/16) + 1), the most window blocks a length can have.
+
+def window_ring_slots(window: int, block: int = 16) -> int:
+    """Ring slots per KV head: the most blocks the last ``window`` tokens can touch."""
+    return -(-int(window) // block) + 1
+
+
+def fill_working_set(k: np.ndarray, v: np.ndarray, resident: np.ndarray, seq_lens: np.ndarray,
+                     window: int, block: int = 16):
+    """The working set of a slot table, gathered from the full cache.
+
+    Pool slot s of (b, h) holds logical block resident[b, h, s] (zeros for an
+    empty slot); ring slot j mod WB holds window block j for every j in
+    [first_window_block, num_blocks) (zeros elsewhere).
+    k, v: [B, H, NB, block, d]; resident: [B, H, K].  Returns pool_k, pool_v
+    [B, H, K, block, d] and ring_k, ring_v [B, H, WB, block, d].
+    """
+    B, H, NB, bs, d = k.shape
+    K = resident.shape[2]
+    WB = window_ring_slots(window, block)
+    pool_k = np.zeros((B, H, K, bs, d))
+    pool_v = np.zeros((B, H, K, bs, d))
+    ring_k = np.zeros((B, H, WB, bs, d))
+    ring_v = np.zeros((B, H, WB, bs, d))
+    for b in range(B):
+        L = int(seq_lens[b])
+        w0, nb = first_window_block(L, window, block), num_blocks(L, block)
+        for h in range(H):
+            for s in range(K):
+                j = int(resident[b, h, s])
+                if 0 <= j < NB:
+                    pool_k[b, h, s] = k[b, h, j]
+                    pool_v[b, h, s] = v[b, h, j]
+            for j in range(w0, nb):
+                ring_k[b, h, j % WB] = k[b, h, j]
+                ring_v[b, h, j % WB] = v[b, h, j]
+    return pool_k, pool_v, ring_k, ring_v
+
+
+def execute_plan(pool_k: np.ndarray, pool_v: np.ndarray, plan: np.ndarray, plan_count: np.ndarray,
+                 k: np.ndarray, v: np.ndarray):
+    """Moves the admitted blocks into their slots: every plan row (slot, new,
+    old) of (b, h), rows below plan_count, copies logical block ``new`` of the
+    full cache into pool slot ``slot``; the evicted block ``old`` needs no
+    transfer (the full tier keeps every block).  [xllm] section three, training
+    flow step 3 (the transfer plan goes out as an asynchronous host-link
+    transfer) and section five (KV transfer).  Returns new pool arrays.
+    """
+    pk, pv = pool_k.copy(), pool_v.copy()
+    B, H = plan_count.shape
+    for b in range(B):
+        for h in range(H):
+            for i in range(int(plan_count[b, h])):
+                slot, new = int(plan[b, h, i, 0]), int(plan[b, h, i, 1])
+                pk[b, h, slot] = k[b, h, new]
+                pv[b, h, slot] = v[b, h, new]
+    return pk, pv
+
+
+def append_token(k: np.ndarray, v: np.ndarray, summ: np.ndarray, ring_k: np.ndarray,
+                 ring_v: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, seq_lens: np.ndarray,
+                 window: int, block: int = 16):
+    """Appends one decoded token per sequence: its key and value go to position
+    L = seq_lens[b] of the full cache and of the window ring, and the summary of
+    its block L // 16 is updated in place of a rebuild: the token's key itself
+    when it opens the block, else the elementwise min and max with the summary so
+    far.  [xllm] section three, component table (per-block per-dimension min/max
+    summaries) and section five (compressed-key update).  The caller then counts
+    the token into seq_lens.  Requires L < NB * block.
+
+    k_new, v_new: [B, H, d].  Returns updated copies of k, v, summ, ring_k, ring_v.
+    """
+    k, v, summ = k.copy(), v.copy(), summ.copy()
+    ring_k, ring_v = ring_k.copy(), ring_v.copy()
+    B, H = k.shape[:2]
+    WB = ring_k.shape[2]
+    for b in range(B):
+        L = int(seq_lens[b])
+        j, t = divmod(L, block)
+        for h in range(H):
+            k[b, h, j, t] = k_new[b, h]
+            v[b, h, j, t] = v_new[b, h]
+            ring_k[b, h, j % WB, t] = k_new[b, h]
+            ring_v[b, h, j % WB, t] = v_new[b, h]
+            if t == 0:
+                summ[b, h, j, 0] = k_new[b, h]
+                summ[b, h, j, 1] = k_new[b, h]
+            else:
+                summ[b, h, j, 0] = np.minimum(summ[b, h, j, 0], k_new[b, h])
+                summ[b, h, j, 1] = np.maximum(summ[b, h, j, 1], k_new[b, h])
+    return k, v, summ, ring_k, ring_v
+
+
+def pool_attention(q: np.ndarray, pool_k: np.ndarray, pool_v: np.ndarray, ring_k: np.ndarray,
+                   ring_v: np.ndarray, resident: np.ndarray, seq_lens: np.ndarray, window: int,
+                   scale: float, block: int = 16) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention of each target query over its head's working set as stored in
+    HBM: the pool slots whose block is historical (0 <= resident < first window
+    block; every token of such a block is inside the length) and the window
+    blocks, read from their ring slots with tokens past the length dropped.
+    Same softmax as ``sparse_attention``.  Returns out [B, H, G, d], lse [B, H, G].
+    """
+    B, H, G, Q, d = q.shape
+    WB = ring_k.shape[2]
+    out = np.zeros((B, H, G, d))
+    lse = np.full((B, H, G), NEG_INF)
+    for b in range(B):
+        L = int(seq_lens[b])
+        w0, nb = first_window_block(L, window, block), num_blocks(L, block)
+        for h in range(H):
+            ks, vs = [], []
+            for s in range(resident.shape[2]):
+                if 0 <= int(resident[b, h, s]) < w0:
+                    ks.append(pool_k[b, h, s])
+                    vs.append(pool_v[b, h, s])
+            for j in range(w0, nb):
+                n = min(block, L - j * block)
+                ks.append(ring_k[b, h, j % WB, :n])
+                vs.append(ring_v[b, h, j % WB, :n])
+            if not ks:
+                continue
+            kt, vt = np.concatenate(ks), np.concatenate(vs)
+            for g in range(G):
+                z = (kt @ q[b, h, g, 0]) * scale
+                m = z.max()
+                e = np.exp(z - m)
+                out[b, h, g] = (e[:, None] * vt).sum(axis=0) / e.sum()
+                lse[b, h, g] = m + math.log(e.sum())
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
 # The whole step
 # ---------------------------------------------------------------------------
 

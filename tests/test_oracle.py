@@ -522,3 +522,118 @@ def test_overlapped_step_agrees_with_serial_when_the_plan_changes_nothing(cap):
     o2 = ref.decode_step_overlapped(q, summ, k, v, lens, R2, K, W, 4, 0.125)
     assert np.all(a2["plan_count"] == 2)
     assert np.abs(o2["out"] - a2["out"]).max() > 1e-6
+
+
+# ---------------------------------------------------------------------------
+# The working set in HBM: pool, window ring, plan execution, appended tokens
+# ---------------------------------------------------------------------------
+
+def _marked_cache(B, H, NB, d=4):
+    """K and V whose every token row holds (b, h, block, token) codes: a copy's origin
+    can be read off the values."""
+    k = np.zeros((B, H, NB, 16, d))
+    for b, h, j, t in itertools.product(range(B), range(H), range(NB), range(16)):
+        k[b, h, j, t] = [b, h, j, t][:d] + [0] * max(0, d - 4)
+    return k, -k
+
+
+def test_ring_slot_hand_example():
+    """W = 32: ring of ceil(32/16) + 1 = 3 slots.  Length 100: blocks 0..6, first
+    window block (100 - 32) // 16 = 4, so blocks 4, 5, 6 sit in ring slots 1, 2, 0."""
+    assert ref.window_ring_slots(32) == 3 and ref.window_ring_slots(0) == 1
+    assert ref.window_ring_slots(128) == 9 and ref.window_ring_slots(64) == 5
+    k, v = _marked_cache(1, 1, 8)
+    R = np.array([[[2, -1, 0]]])
+    pk, pv, rk, rv = ref.fill_working_set(k, v, R, np.array([100]), 32)
+    assert rk.shape == (1, 1, 3, 16, 4)
+    assert [int(rk[0, 0, s, 0, 2]) for s in range(3)] == [6, 4, 5]
+    assert np.array_equal(rv[0, 0, 1], -k[0, 0, 4])
+    assert np.array_equal(pk[0, 0, 0], k[0, 0, 2]) and np.array_equal(pk[0, 0, 2], k[0, 0, 0])
+    assert not pk[0, 0, 1].any() and not pv[0, 0, 1].any()      # the empty slot stays empty
+
+
+def test_ring_of_zero_window_holds_the_partial_last_block():
+    k, v = _marked_cache(1, 1, 4)
+    _, _, rk, _ = ref.fill_working_set(k, v, np.full((1, 1, 2), -1), np.array([37]), 0)
+    assert rk.shape[2] == 1 and int(rk[0, 0, 0, 0, 2]) == 2      # block 2 holds tokens 32..36
+    _, _, rk, _ = ref.fill_working_set(k, v, np.full((1, 1, 2), -1), np.array([48]), 0)
+    assert not rk.any()                                           # aligned: no window block
+
+
+@pytest.mark.parametrize("window", [0, 40, 64])
+def test_pool_attention_equals_table_attention(window):
+    """Attention over the working set as stored (pool slots + ring) equals attention
+    over the slot table written out as a table, read from the full cache."""
+    q, k, v, lens = _tiny_inputs(seed=21, NB=12, lens=(187, 100))
+    r = _rng(22)
+    B, H, K = 2, 2, 5
+    R = np.full((B, H, K), -1)
+    for b, h in itertools.product(range(B), range(H)):
+        nb = ref.num_blocks(int(lens[b]))
+        picks = r.choice(nb, size=K - 1, replace=False)           # may reach into the window
+        R[b, h, : K - 1] = picks
+        r.shuffle(R[b, h])
+    scale = 1 / math.sqrt(8)
+    pk, pv, rk, rv = ref.fill_working_set(k, v, R, lens, window)
+    out, lse = ref.pool_attention(q, pk, pv, rk, rv, R, lens, window, scale)
+    table, tc = ref.resident_table(R, lens, window)
+    eo, el = ref.sparse_attention(q, k, v, table, tc, lens, scale)
+    np.testing.assert_allclose(out, eo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, el, rtol=0, atol=1e-12)
+
+
+def test_execute_plan_gives_the_gather_of_the_next_slot_table():
+    """After the plan's copies the pool is exactly what gathering the updated slot
+    table from the full cache gives: admitted blocks in their slots, the rest
+    untouched."""
+    q, k, v, lens = _tiny_inputs(seed=23, NB=14, lens=(220, 150))
+    summ = ref.build_summaries(k, lens)
+    W, K, cap = 32, 6, 3
+    s = ref.score_blocks(q, summ, lens, W)
+    sel = ref.topk_blocks(s, lens, K, W)
+    r = _rng(24)
+    R = np.full((2, 2, K), -1)
+    for b, h in itertools.product(range(2), range(2)):
+        nc = ref.first_window_block(int(lens[b]), W)
+        R[b, h, :4] = r.choice(nc, size=4, replace=False)
+    p = ref.build_plan(s, sel, R, lens, cap, W)
+    assert p["plan_count"].sum() > 0
+    pk, pv, _, _ = ref.fill_working_set(k, v, R, lens, W)
+    nk, nv = ref.execute_plan(pk, pv, p["plan"], p["plan_count"], k, v)
+    ek, ev, _, _ = ref.fill_working_set(k, v, p["resident"], lens, W)
+    np.testing.assert_array_equal(nk, ek)
+    np.testing.assert_array_equal(nv, ev)
+    np.testing.assert_array_equal(pk, ref.fill_working_set(k, v, R, lens, W)[0])   # inputs untouched
+
+
+def test_append_token_matches_a_rebuild():
+    """Tokens appended one at a time (across block boundaries, from a partial block):
+    after each, the summaries equal a rebuild from the full cache, the ring equals
+    a fresh gather of the window, and the full cache holds the token."""
+    r = _rng(25)
+    B, H, NB, d, W = 2, 2, 6, 8, 24
+    k = _bf16(r.standard_normal((B, H, NB, 16, d)))
+    v = _bf16(r.standard_normal((B, H, NB, 16, d)))
+    lens = np.array([13, 30])
+    summ = ref.build_summaries(k, lens)
+    R = np.full((B, H, 2), -1)
+    _, _, rk, rv = ref.fill_working_set(k, v, R, lens, W)
+    for step in range(40):
+        kn = _bf16(r.standard_normal((B, H, d)) * (1 + step % 3))
+        vn = _bf16(r.standard_normal((B, H, d)))
+        k, v, summ, rk, rv = ref.append_token(k, v, summ, rk, rv, kn, vn, lens, W)
+        for b in range(B):
+            j, t = divmod(int(lens[b]), 16)
+            assert np.array_equal(k[b, :, j, t], kn[b]) and np.array_equal(v[b, :, j, t], vn[b])
+        lens = lens + 1
+        rebuilt = ref.build_summaries(k, lens)
+        for b in range(B):
+            nb = ref.num_blocks(int(lens[b]))
+            np.testing.assert_array_equal(summ[b, :, :nb], rebuilt[b, :, :nb])
+        _, _, ek, ev = ref.fill_working_set(k, v, R, lens, W)
+        for b in range(B):
+            L = int(lens[b])
+            for j in range(ref.first_window_block(L, W), ref.num_blocks(L)):
+                n = min(16, L - 16 * j)
+                np.testing.assert_array_equal(rk[b, :, j % 3, :n], ek[b, :, j % 3, :n])
+                np.testing.assert_array_equal(rv[b, :, j % 3, :n], ev[b, :, j % 3, :n])

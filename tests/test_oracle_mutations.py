@@ -41,6 +41,17 @@ MUTATIONS = {
         "table, tcount = resident_table(build_plan(score_blocks(q, summ, seq_lens, window, block), "
         "topk_blocks(score_blocks(q, summ, seq_lens, window, block), seq_lens, top_k, window, block), "
         "resident, seq_lens, cap, window, block)['resident'], seq_lens, window, block)"),
+    "ring_slot_shifted": ("ring_k[b, h, j % WB] = k[b, h, j]", "ring_k[b, h, (j + 1) % WB] = k[b, h, j]"),
+    "ring_one_slot_short": ("return -(-int(window) // block) + 1", "return -(-int(window) // block)"),
+    "plan_copies_evicted_block": ("slot, new = int(plan[b, h, i, 0]), int(plan[b, h, i, 1])",
+                                  "slot, new = int(plan[b, h, i, 0]), int(plan[b, h, i, 2])"),
+    "append_never_reopens_block": ("            if t == 0:\n                summ[b, h, j, 0] = k_new[b, h]",
+                                   "            if False:\n                summ[b, h, j, 0] = k_new[b, h]"),
+    "append_writes_wrong_ring_slot": ("ring_k[b, h, j % WB, t] = k_new[b, h]",
+                                      "ring_k[b, h, (j + 1) % WB, t] = k_new[b, h]"),
+    "pool_attention_keeps_window_slots": ("if 0 <= int(resident[b, h, s]) < w0:",
+                                          "if 0 <= int(resident[b, h, s]):"),
+    "pool_attention_reads_whole_last_block": ("n = min(block, L - j * block)", "n = block"),
 }
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins)
@@ -56,6 +67,8 @@ def _run_pins(mutant, monkeypatch) -> bool:
             variants = [{"distinct": True}, {"distinct": False}]
         elif "cap" in params:
             variants = [{"cap": 0}, {"cap": 4}]
+        elif "window" in params:
+            variants = [{"window": 0}, {"window": 40}, {"window": 64}]
         else:
             variants = [{}]
         for kw in variants:
