@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define OASIS_ABI_VERSION 2
+#define OASIS_ABI_VERSION 3
 
 typedef enum {
   OASIS_OK = 0,
@@ -286,6 +286,88 @@ oasis_status oasis_decode_step_timed(const oasis_dims* dims, const void* q, cons
                                      int32_t* table, int32_t* table_count, float scale, float* out,
                                      float* lse, void* ws, size_t ws_bytes, hipStream_t stream,
                                      hipEvent_t* events);
+
+/* ---- Executing the plan: the working set in HBM -----------------------------
+ *
+ * The full K/V cache keeps its layout and place ([B, H, max_blocks, 16, 128]
+ * bf16, in HBM or in pinned host memory that the device can address): that is
+ * the page table, and it never changes.  HBM holds each KV head's working set:
+ * a pool of K block slots, slot s holding the block the resident slot table
+ * names in slot s (the head-wise logical-to-logical map), and a ring of
+ * WB = oasis_window_ring_slots(dims) window blocks, window block j in ring slot
+ * j % WB.  (xllm-io review, section three: component table, head-wise mapping
+ * above the paged cache; training flow steps 2 and 3: the GPU keeps the
+ * selected historical blocks and the local window, the plan is carried out as
+ * an asynchronous transfer; section four, innovations table: only head-wise
+ * mapping entries change; section five: compressed-key update and KV
+ * transfer.  legiblepapers.com FAQ Q4; lode.cx points 1 and 3.)
+ *   pool_k, pool_v  device, bf16 [B, H, K, 16, 128]
+ *   ring_k, ring_v  device, bf16 [B, H, WB, 16, 128]
+ *   k, v            the full cache, bf16 [B, H, max_blocks, 16, 128]: device
+ *                   memory, or pinned host memory given by its device address
+ *                   (hipHostGetDevicePointer); read (and, by append, written)
+ *                   by the kernels directly.
+ * Buffers are caller-owned and must be pairwise disjoint (checked on the
+ * address ranges).  Errors as for the calls above. */
+
+/* Ring slots per KV head, ceil(W / 16) + 1 (== oasis_table_stride - top_k).
+ * -1 if dims is invalid. */
+int32_t oasis_window_ring_slots(const oasis_dims* dims);
+
+/* Gathers the working set of slot table `resident` ([B, H, K], -1 = empty) from
+ * the full cache: pool slot s <- block resident[b,h,s] (empty slots are left as
+ * they are), ring slot j % WB <- window block j for j in [first window block,
+ * number of blocks) of seq_lens[b].  For admission, or to rebuild. */
+oasis_status oasis_fill_working_set(const oasis_dims* dims, const int32_t* resident,
+                                    const int32_t* seq_lens, const void* k, const void* v,
+                                    void* pool_k, void* pool_v, void* ring_k, void* ring_v,
+                                    hipStream_t stream);
+
+/* Executes a plan of oasis_build_plan: for every row i < plan_count[b,h] of
+ * plan[b,h] (slot, new, old), copies block `new` of the full cache into pool
+ * slot `slot`.  The evicted block needs no transfer (the full cache keeps every
+ * block).  Rows out of range are skipped.  plan may be NULL when the cap is 0. */
+oasis_status oasis_execute_plan(const oasis_dims* dims, const int32_t* plan,
+                                const int32_t* plan_count, const void* k, const void* v,
+                                void* pool_k, void* pool_v, hipStream_t stream);
+
+/* Appends one decoded token per sequence at position L = seq_lens[b]:
+ *   k_new, v_new  device, bf16 [B, H, 128]
+ *   k, v          the full cache (both NULL: not written)
+ *   ring_k/v      token L % 16 of ring slot (L / 16) % WB
+ *   summ          the summary of block L / 16: the new key itself when L % 16
+ *                 == 0 (the token opens the block), else the elementwise min
+ *                 and max with the summary so far (exact in bf16).
+ * seq_lens is not changed: the caller counts the token in afterwards.  A
+ * sequence with L >= 16 * max_blocks has no room and is skipped. */
+oasis_status oasis_append_token(const oasis_dims* dims, const void* k_new, const void* v_new,
+                                const int32_t* seq_lens, void* summ, void* k, void* v,
+                                void* ring_k, void* ring_v, hipStream_t stream);
+
+/* oasis_sparse_decode_attn_resident over the working set: resident slot s is
+ * read from pool slot s, window block j from ring slot j % WB.  Equal to the
+ * full-cache form when the working set holds the slot table's blocks. */
+oasis_status oasis_sparse_decode_attn_pool(const oasis_dims* dims, const void* q, const void* pool_k,
+                                           const void* pool_v, const void* ring_k,
+                                           const void* ring_v, const int32_t* resident,
+                                           const int32_t* seq_lens, float scale, float* out,
+                                           float* lse, void* ws, size_t ws_bytes,
+                                           hipStream_t stream);
+
+/* oasis_decode_step_overlapped with the foreground attention over the working
+ * set (oasis_sparse_decode_attn_pool), followed by oasis_execute_plan of the
+ * plan just built, copying the admitted blocks from the full cache k, v into
+ * the pool: after the call the pool holds resident_next's blocks.  Three
+ * launches on `stream`; the copies start after the attention has read the
+ * pool.  Other arguments as for oasis_decode_step_overlapped. */
+oasis_status oasis_decode_step_pool(const oasis_dims* dims, const void* q, const void* summ,
+                                    const void* k, const void* v, void* pool_k, void* pool_v,
+                                    const void* ring_k, const void* ring_v,
+                                    const int32_t* seq_lens, float* scores, int32_t* topk,
+                                    const int32_t* resident, int32_t* resident_next,
+                                    int32_t* plan, int32_t* plan_count, int32_t* table,
+                                    int32_t* table_count, float scale, float* out, float* lse,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

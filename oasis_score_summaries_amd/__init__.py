@@ -7,7 +7,8 @@ liboasis.so (C ABI in include/oasis.h); this package is its Python binding.
 Every call raises if the library has not been built.
 """
 from ._lib import (LIB_PATH, OasisDims, OasisError, PreparedStep, StageEvents,  # noqa: F401
-                   StepBuffers, build_plan,
+                   StepBuffers, WorkingSet, append_token, build_plan, decode_step_pool,
+                   execute_plan, fill_working_set, sparse_decode_attn_pool, window_ring_slots,
                    build_summaries, decode_step, decode_step_overlapped, dims_for,
                    exported_symbols, fetch_cap, load, make_dims, score_summaries,
                    sparse_decode_attn, sparse_decode_attn_resident, table_stride, topk_blocks,

@@ -77,6 +77,15 @@ _SIGNATURES = {
                                                           _P, _P, _P, ctypes.c_float, _P, _P, _P,
                                                           ctypes.c_size_t, _P,
                                                           ctypes.POINTER(ctypes.c_void_p)]),
+    "oasis_window_ring_slots": (ctypes.c_int32, [_DIMS]),
+    "oasis_fill_working_set": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "oasis_execute_plan": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P]),
+    "oasis_append_token": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "oasis_sparse_decode_attn_pool": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float,
+                                                     _P, _P, _P, ctypes.c_size_t, _P]),
+    "oasis_decode_step_pool": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                                              ctypes.c_size_t, _P]),
 }
 
 _lib = None
@@ -422,6 +431,160 @@ def decode_step_overlapped(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor,
 _hip = None
 
 
+# ---- executing the plan: the working set in HBM -----------------------------------
+
+def window_ring_slots(dims: OasisDims) -> int:
+    n = load().oasis_window_ring_slots(ctypes.byref(dims))
+    if n < 0:
+        _check(1, "oasis_window_ring_slots")
+    return n
+
+
+class WorkingSet:
+    """The working set of every KV head in HBM: a pool of K block slots (slot s holds
+    the block of resident slot s) and a ring of window blocks (window block j in
+    ring slot j % window_ring_slots(dims)), K and V, bf16."""
+
+    def __init__(self, dims: OasisDims, device):
+        dev = _norm_device(device)
+        B, H, K, WB = dims.batch, dims.num_kv_heads, dims.top_k, window_ring_slots(dims)
+        self.dims = dims
+        self.pool_k = torch.zeros((B, H, K, 16, 128), dtype=torch.bfloat16, device=dev)
+        self.pool_v = torch.zeros_like(self.pool_k)
+        self.ring_k = torch.zeros((B, H, WB, 16, 128), dtype=torch.bfloat16, device=dev)
+        self.ring_v = torch.zeros_like(self.ring_k)
+
+    def check(self, device):
+        B, H, K = self.dims.batch, self.dims.num_kv_heads, self.dims.top_k
+        WB = window_ring_slots(self.dims)
+        for n in ("pool_k", "pool_v"):
+            _need(getattr(self, n), n, torch.bfloat16, (B, H, K, 16, 128), device, align=16)
+        for n in ("ring_k", "ring_v"):
+            _need(getattr(self, n), n, torch.bfloat16, (B, H, WB, 16, 128), device, align=16)
+
+
+def _cache_ptr(t: torch.Tensor, name: str, shape, device) -> ctypes.c_void_p:
+    """Device address of a full-cache tensor: a GPU tensor on ``device``, or a pinned
+    host tensor (its mapped address, read by the kernels over the host link)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or tuple(t.shape) != tuple(shape) \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bf16 tensor of shape {tuple(shape)}")
+    if t.device.type == "cuda":
+        _need(t, name, torch.bfloat16, shape, device, align=16)
+        return _ptr(t)
+    if not t.is_pinned():
+        raise ValueError(f"{name} must be a GPU tensor or a pinned host tensor")
+    h = _hip_runtime()
+    dptr = ctypes.c_void_p()
+    if h.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0) != 0:
+        raise RuntimeError(f"hipHostGetDevicePointer failed for {name}")
+    return dptr
+
+
+def fill_working_set(dims: OasisDims, resident: torch.Tensor, seq_lens: torch.Tensor, k: torch.Tensor,
+                     v: torch.Tensor, wset: Optional[WorkingSet] = None, stream=None) -> WorkingSet:
+    """Gathers the working set of slot table ``resident`` from the full cache k, v
+    (GPU or pinned host tensors) into ``wset`` (new if None)."""
+    s = _shapes(dims)
+    _need(resident, "resident", torch.int32, s["resident"])
+    dev = resident.device
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+    kp, vp = _cache_ptr(k, "k", s["kv"], dev), _cache_ptr(v, "v", s["kv"], dev)
+    if wset is None:
+        wset = WorkingSet(dims, dev)
+    wset.check(dev)
+    _check(load().oasis_fill_working_set(ctypes.byref(dims), _ptr(resident), _ptr(seq_lens), kp, vp,
+                                         _ptr(wset.pool_k), _ptr(wset.pool_v), _ptr(wset.ring_k),
+                                         _ptr(wset.ring_v), _stream(stream)), "oasis_fill_working_set")
+    return wset
+
+
+def execute_plan(dims: OasisDims, plan: torch.Tensor, plan_count: torch.Tensor, k: torch.Tensor,
+                 v: torch.Tensor, wset: WorkingSet, stream=None) -> None:
+    """Copies every plan row's admitted block from the full cache into its pool slot."""
+    s = _shapes(dims)
+    _need(plan_count, "plan_count", torch.int32, s["bh"])
+    dev = plan_count.device
+    _need(plan, "plan", torch.int32, (dims.batch, dims.num_kv_heads, fetch_cap(dims), 3), dev)
+    kp, vp = _cache_ptr(k, "k", s["kv"], dev), _cache_ptr(v, "v", s["kv"], dev)
+    wset.check(dev)
+    _check(load().oasis_execute_plan(ctypes.byref(dims), _ptr(plan if plan.numel() else None),
+                                     _ptr(plan_count), kp, vp, _ptr(wset.pool_k), _ptr(wset.pool_v),
+                                     _stream(stream)), "oasis_execute_plan")
+
+
+def append_token(dims: OasisDims, k_new: torch.Tensor, v_new: torch.Tensor, seq_lens: torch.Tensor,
+                 summ: torch.Tensor, wset: WorkingSet, k: Optional[torch.Tensor] = None,
+                 v: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Writes one token per sequence at position seq_lens[b] into the ring, the full
+    cache (if given) and its block's summary; seq_lens is left to the caller."""
+    s = _shapes(dims)
+    _need(k_new, "k_new", torch.bfloat16, (dims.batch, dims.num_kv_heads, 128), align=16)
+    dev = k_new.device
+    _need(v_new, "v_new", torch.bfloat16, (dims.batch, dims.num_kv_heads, 128), dev, align=16)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+    _need(summ, "summ", torch.bfloat16, s["summ"], dev, align=16)
+    wset.check(dev)
+    if (k is None) != (v is None):
+        raise ValueError("k and v must both be given or both be None")
+    kp = _cache_ptr(k, "k", s["kv"], dev) if k is not None else _ptr(None)
+    vp = _cache_ptr(v, "v", s["kv"], dev) if v is not None else _ptr(None)
+    _check(load().oasis_append_token(ctypes.byref(dims), _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
+                                     _ptr(summ), kp, vp, _ptr(wset.ring_k), _ptr(wset.ring_v),
+                                     _stream(stream)), "oasis_append_token")
+
+
+def sparse_decode_attn_pool(dims: OasisDims, q: torch.Tensor, wset: WorkingSet, resident: torch.Tensor,
+                            seq_lens: torch.Tensor, scale: Optional[float] = None, out=None, lse=None,
+                            ws=None, stream=None):
+    """Attention of the target queries over the working set (oasis_sparse_decode_attn_pool).
+    Returns (out, lse)."""
+    s = _shapes(dims)
+    _need(q, "q", torch.bfloat16, s["q"], align=16)
+    dev = q.device
+    wset.check(dev)
+    _need(resident, "resident", torch.int32, s["resident"], dev)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+    scale = 1.0 / math.sqrt(128) if scale is None else scale
+    out = torch.empty(s["out"], dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty(s["lse"], dtype=torch.float32, device=dev) if lse is None else lse
+    _need(out, "out", torch.float32, s["out"], dev, align=16)
+    _need(lse, "lse", torch.float32, s["lse"], dev)
+    ws = torch.empty(workspace_bytes(dims), dtype=torch.uint8, device=dev) if ws is None else ws
+    _check(load().oasis_sparse_decode_attn_pool(
+        ctypes.byref(dims), _ptr(q), _ptr(wset.pool_k), _ptr(wset.pool_v), _ptr(wset.ring_k),
+        _ptr(wset.ring_v), _ptr(resident), _ptr(seq_lens), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
+        ws.numel(), _stream(stream)), "oasis_sparse_decode_attn_pool")
+    return out, lse
+
+
+def decode_step_pool(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor, k: torch.Tensor,
+                     v: torch.Tensor, wset: WorkingSet, seq_lens: torch.Tensor, resident: torch.Tensor,
+                     resident_next: torch.Tensor, scale: Optional[float] = None,
+                     buffers: Optional["StepBuffers"] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """The overlapped step with the attention over the working set, then the plan's
+    block copies from the full cache k, v (GPU or pinned host tensors) into the pool
+    (oasis_decode_step_pool)."""
+    s = _shapes(dims)
+    _need(q, "q", torch.bfloat16, s["q"], align=16)
+    dev = q.device
+    _need(summ, "summ", torch.bfloat16, s["summ"], dev, align=16)
+    kp, vp = _cache_ptr(k, "k", s["kv"], dev), _cache_ptr(v, "v", s["kv"], dev)
+    wset.check(dev)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+    _need(resident, "resident", torch.int32, s["resident"], dev)
+    _need(resident_next, "resident_next", torch.int32, s["resident"], dev)
+    b = StepBuffers(dims, dev) if buffers is None else buffers
+    scale = 1.0 / math.sqrt(128) if scale is None else scale
+    _check(load().oasis_decode_step_pool(
+        ctypes.byref(dims), _ptr(q), _ptr(summ), kp, vp, _ptr(wset.pool_k), _ptr(wset.pool_v),
+        _ptr(wset.ring_k), _ptr(wset.ring_v), _ptr(seq_lens), _ptr(b.scores), _ptr(b.topk),
+        _ptr(resident), _ptr(resident_next), _ptr(b.plan if b.plan.numel() else None),
+        _ptr(b.plan_count), _ptr(b.table), _ptr(b.table_count), float(scale), _ptr(b.out), _ptr(b.lse),
+        _ptr(b.ws), b.ws.numel(), _stream(stream)), "oasis_decode_step_pool")
+    return {**b.as_dict(), "resident": resident_next}
+
+
 def _hip_runtime() -> ctypes.CDLL:
     global _hip
     if _hip is None:
@@ -436,6 +599,8 @@ def _hip_runtime() -> ctypes.CDLL:
         h.hipEventElapsedTime.restype = ctypes.c_int
         h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         h.hipEventCreateWithFlags.restype = ctypes.c_int
+        h.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+        h.hipHostGetDevicePointer.restype = ctypes.c_int
         _hip = h
     return _hip
 

@@ -387,3 +387,162 @@ oasis_status oasis_decode_step_timed(const oasis_dims* dims, const void* q, cons
 }
 
 }  // extern "C"
+
+// ---- the working set in HBM -------------------------------------------------------
+
+namespace {
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const char* x = (const char*)a;
+  const char* y = (const char*)b;
+  return x < y + nb && y < x + na;
+}
+
+// Pool, ring and (if given) full-cache buffers must be pairwise disjoint.
+oasis_status check_working_set(const oasis::Dims& d, const void* k, const void* v,
+                               const void* pool_k, const void* pool_v, const void* ring_k,
+                               const void* ring_v) {
+  const size_t blk = (size_t)oasis::kBlock * oasis::kHeadDim * 2;
+  const size_t heads = (size_t)d.batch * d.heads;
+  const size_t full = heads * d.max_blocks * blk, pool = heads * d.top_k * blk;
+  const size_t ring = heads * (size_t)(d.table_stride - d.top_k) * blk;
+  const struct {
+    const void* p;
+    size_t n;
+    const char* name;
+  } bufs[] = {{k, full, "k"},           {v, full, "v"},           {pool_k, pool, "pool_k"},
+              {pool_v, pool, "pool_v"}, {ring_k, ring, "ring_k"}, {ring_v, ring, "ring_v"}};
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (bufs[i].p != nullptr && bufs[j].p != nullptr &&
+          ranges_overlap(bufs[i].p, bufs[i].n, bufs[j].p, bufs[j].n))
+        return fail(OASIS_ERR_INVALID_ARG, "%s and %s overlap", bufs[i].name, bufs[j].name);
+  return OASIS_OK;
+}
+
+}  // namespace
+
+int32_t oasis_window_ring_slots(const oasis_dims* dims) {
+  oasis::Dims d;
+  if (check_dims(dims, &d) != OASIS_OK) return -1;
+  return d.table_stride - d.top_k;
+}
+
+oasis_status oasis_fill_working_set(const oasis_dims* dims, const int32_t* resident,
+                                    const int32_t* seq_lens, const void* k, const void* v,
+                                    void* pool_k, void* pool_v, void* ring_k, void* ring_v,
+                                    hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  OASIS_REQUIRE(resident);
+  OASIS_REQUIRE(seq_lens);
+  OASIS_REQUIRE(k);
+  OASIS_REQUIRE(v);
+  OASIS_REQUIRE(pool_k);
+  OASIS_REQUIRE(pool_v);
+  OASIS_REQUIRE(ring_k);
+  OASIS_REQUIRE(ring_v);
+  if ((st = check_working_set(d, k, v, pool_k, pool_v, ring_k, ring_v)) != OASIS_OK) return st;
+  const oasis::WorkingSet w{pool_k, pool_v, ring_k, ring_v};
+  return hip_status(oasis::launch_fill_working_set(d, resident, seq_lens, k, v, w, stream),
+                    "fill_working_set");
+}
+
+oasis_status oasis_execute_plan(const oasis_dims* dims, const int32_t* plan,
+                                const int32_t* plan_count, const void* k, const void* v,
+                                void* pool_k, void* pool_v, hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  if (d.cap > 0) OASIS_REQUIRE(plan);
+  OASIS_REQUIRE(plan_count);
+  OASIS_REQUIRE(k);
+  OASIS_REQUIRE(v);
+  OASIS_REQUIRE(pool_k);
+  OASIS_REQUIRE(pool_v);
+  if ((st = check_working_set(d, k, v, pool_k, pool_v, nullptr, nullptr)) != OASIS_OK) return st;
+  return hip_status(oasis::launch_execute_plan(d, plan, plan_count, k, v, pool_k, pool_v, stream),
+                    "execute_plan");
+}
+
+oasis_status oasis_append_token(const oasis_dims* dims, const void* k_new, const void* v_new,
+                                const int32_t* seq_lens, void* summ, void* k, void* v,
+                                void* ring_k, void* ring_v, hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  OASIS_REQUIRE(k_new);
+  OASIS_REQUIRE(v_new);
+  OASIS_REQUIRE(seq_lens);
+  OASIS_REQUIRE(summ);
+  OASIS_REQUIRE(ring_k);
+  OASIS_REQUIRE(ring_v);
+  if ((k == nullptr) != (v == nullptr))
+    return fail(OASIS_ERR_INVALID_ARG, "k and v must both be given or both be NULL");
+  if ((st = check_working_set(d, k, v, nullptr, nullptr, ring_k, ring_v)) != OASIS_OK) return st;
+  return hip_status(oasis::launch_append_token(d, k_new, v_new, seq_lens, summ, k, v, ring_k, ring_v,
+                                               stream),
+                    "append_token");
+}
+
+oasis_status oasis_sparse_decode_attn_pool(const oasis_dims* dims, const void* q, const void* pool_k,
+                                           const void* pool_v, const void* ring_k,
+                                           const void* ring_v, const int32_t* resident,
+                                           const int32_t* seq_lens, float scale, float* out,
+                                           float* lse, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  OASIS_REQUIRE(q);
+  OASIS_REQUIRE(pool_k);
+  OASIS_REQUIRE(pool_v);
+  OASIS_REQUIRE(ring_k);
+  OASIS_REQUIRE(ring_v);
+  OASIS_REQUIRE(resident);
+  OASIS_REQUIRE(seq_lens);
+  OASIS_REQUIRE(out);
+  if (!isfinite(scale)) return fail(OASIS_ERR_INVALID_ARG, "scale must be finite");
+  const size_t need = oasis::attn_workspace_bytes(d, d.table_stride);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(OASIS_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", need,
+                ws == nullptr ? (size_t)0 : ws_bytes);
+  const oasis::AttnSplit split = oasis::attn_split(d, d.table_stride);
+  st = hip_status(oasis::launch_attention_split_pool(d, split, q, pool_k, pool_v, ring_k, ring_v,
+                                                     resident, seq_lens, scale, ws, stream),
+                  "sparse_decode_attn_pool");
+  if (st != OASIS_OK) return st;
+  return hip_status(oasis::launch_attention_merge(d, split, out, lse, ws, stream),
+                    "sparse_decode_attn_pool/merge");
+}
+
+oasis_status oasis_decode_step_pool(const oasis_dims* dims, const void* q, const void* summ,
+                                    const void* k, const void* v, void* pool_k, void* pool_v,
+                                    const void* ring_k, const void* ring_v,
+                                    const int32_t* seq_lens, float* scores, int32_t* topk,
+                                    const int32_t* resident, int32_t* resident_next,
+                                    int32_t* plan, int32_t* plan_count, int32_t* table,
+                                    int32_t* table_count, float scale, float* out, float* lse,
+                                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  oasis::Dims d;
+  OASIS_REQUIRE(resident_next);
+  oasis_status st = check_step_args(dims, d, q, summ, k, v, seq_lens, scores, topk, resident,
+                                    &resident_next, plan, plan_count, table, table_count, scale,
+                                    out, ws, ws_bytes);
+  if (st != OASIS_OK) return st;
+  if (resident_next == resident)
+    return fail(OASIS_ERR_INVALID_ARG,
+                "resident_next must be its own buffer: the attention reads resident meanwhile");
+  OASIS_REQUIRE(pool_k);
+  OASIS_REQUIRE(pool_v);
+  OASIS_REQUIRE(ring_k);
+  OASIS_REQUIRE(ring_v);
+  if ((st = check_working_set(d, k, v, pool_k, pool_v, ring_k, ring_v)) != OASIS_OK) return st;
+  const oasis::WorkingSet w{pool_k, pool_v, const_cast<void*>(ring_k), const_cast<void*>(ring_v)};
+  return hip_status(oasis::launch_overlapped_step(d, q, summ, k, v, seq_lens, scores, topk, resident,
+                                                  resident_next, plan, plan_count, table,
+                                                  table_count, scale, out, lse, ws, stream, nullptr,
+                                                  &w),
+                    "decode_step_pool");
+}

@@ -59,10 +59,10 @@ size_t attn_workspace_bytes(const Dims& d, int table_stride) {
 }
 
 // Kernels: one workgroup per (split, sequence x KV head), and one per query head.
-template <int GP, bool RES>
+template <int GP, bool RES, bool POOL = false>
 __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void attn_split_kernel(AttnArgs a) {
   __shared__ AttnShared<GP> sh;
-  attn_split_wg<GP, RES>(blockIdx.x, blockIdx.y, sh, a);
+  attn_split_wg<GP, RES, POOL>(blockIdx.x, blockIdx.y, sh, a);
 }
 
 constexpr int kMergeWaves = 4;
@@ -91,6 +91,25 @@ hipError_t launch_attention_split(const Dims& d, const AttnSplit& s, const void*
     OASIS_ATTN_LAUNCH(16)
   }
 #undef OASIS_ATTN_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_split_pool(const Dims& d, const AttnSplit& s, const void* q,
+                                       const void* pool_k, const void* pool_v, const void* ring_k,
+                                       const void* ring_v, const int32_t* resident,
+                                       const int32_t* seq_lens, float scale, void* ws,
+                                       hipStream_t stream) {
+  const dim3 grid(s.num_splits, d.batch * d.heads), block(64 * kAttnWaves);
+  AttnArgs a = attn_args(d, s, q, pool_k, pool_v, resident, nullptr, d.table_stride, seq_lens, scale, ws);
+  a.ring_k = (const char*)ring_k;
+  a.ring_v = (const char*)ring_v;
+  if (d.group <= 4) {
+    attn_split_kernel<4, true, true><<<grid, block, 0, stream>>>(a);
+  } else if (d.group <= 8) {
+    attn_split_kernel<8, true, true><<<grid, block, 0, stream>>>(a);
+  } else {
+    attn_split_kernel<16, true, true><<<grid, block, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -67,13 +67,21 @@ struct AttnArgs {
   float scale_log2;
   float* part;
   int heads, group, queries, NB, nsplit, rounds, K, window;
+  // POOL only: the window ring (`k` and `v` are then the pool) and its slots per head.
+  const char* ring_k;
+  const char* ring_v;
+  int WB;
 };
 
 // One workgroup of split `sp` of (sequence, KV head) `bh`; a wave that does not
 // finish last returns early.  Every thread of the workgroup calls it.
-template <int GP, bool RES>
+// POOL (with RES): the blocks are read from the working set in HBM instead of the
+// full cache: resident slot e from pool slot e (`k`, `v`: [B, H, K, 16, 128]),
+// window block j from ring slot j % WB (`ring_k`, `ring_v`: [B, H, WB, 16, 128]).
+template <int GP, bool RES, bool POOL = false>
 __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, AttnShared<GP>& sh,
                                                              const AttnArgs& a) {
+  static_assert(RES || !POOL, "the pool is addressed through the resident slots");
   const u32x4* __restrict__ q = a.q;
   const char* __restrict__ k = a.k;
   const char* __restrict__ v = a.v;
@@ -116,10 +124,17 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
   const int tc = tc_raw < 0 ? 0 : (tc_raw > T ? T : tc_raw);
   const int w0 = first_window_block(len, window), nblk = num_blocks(len);
 
-  const uint32_t head_bytes = (uint32_t)NB * (kBlock * kHeadDim * 2);
+  constexpr uint32_t kBlockBytes = kBlock * kHeadDim * 2;
+  const uint32_t head_bytes = (uint32_t)(POOL ? K : NB) * kBlockBytes;
   const size_t head_off = (size_t)bh * head_bytes;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(v + head_off, head_bytes);
+  __amdgpu_buffer_rsrc_t rk_ring = rk, rv_ring = rv;
+  if (POOL) {
+    const uint32_t ring_bytes = (uint32_t)a.WB * kBlockBytes;
+    rk_ring = head_rsrc(a.ring_k + (size_t)bh * ring_bytes, ring_bytes);
+    rv_ring = head_rsrc(a.ring_v + (size_t)bh * ring_bytes, ring_bytes);
+  }
 
   float m_run = -INFINITY;  // running max of scale*log2(e)*q.k for query head `col`
   float l_run = 0.f;        // this lane's share of the running sum
@@ -146,14 +161,25 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
       id = -1;
     }
     if (id < 0 || id >= NB || id * kBlock >= len) id = -1;
-    const uint32_t off = id < 0 ? kOffMasked : (uint32_t)id * (kBlock * kHeadDim * 2) + lane * 16;
+    __amdgpu_buffer_rsrc_t rk_e = rk, rv_e = rv;
+    int phys = id;  // where the block sits: its logical index in the full cache
+    if (POOL) {     // ... or its pool slot, or its ring slot (all wave-uniform)
+      id = __builtin_amdgcn_readfirstlane(id);
+      const bool in_pool = __builtin_amdgcn_readfirstlane(e) < K;
+      phys = in_pool ? e : id % a.WB;
+      if (!in_pool) {
+        rk_e = rk_ring;
+        rv_e = rv_ring;
+      }
+    }
+    const uint32_t off = id < 0 ? kOffMasked : (uint32_t)phys * kBlockBytes + lane * 16;
     u32x4 kr[4], vf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      kr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off + 1024 * s, 0, kNtAux));
+      kr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk_e, off + 1024 * s, 0, kNtAux));
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      vf[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off + 1024 * s, 0, kNtAux));
+      vf[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv_e, off + 1024 * s, 0, kNtAux));
     // Stage K: token 4s + grp, chunk col.
 #pragma unroll
     for (int s = 0; s < 4; ++s) kst[wave][(4 * s + grp) * kKRow + col] = kr[s];
@@ -383,6 +409,9 @@ inline AttnArgs attn_args(const Dims& d, const AttnSplit& s, const void* q, cons
   a.rounds = s.rounds;
   a.K = d.top_k;
   a.window = d.window;
+  a.ring_k = nullptr;
+  a.ring_v = nullptr;
+  a.WB = d.table_stride - d.top_k;
   return a;
 }
 

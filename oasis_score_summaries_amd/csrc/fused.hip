@@ -1,4 +1,5 @@
-// The overlapped decode step as two fused launches on gfx950.
+// The overlapped decode step as two fused launches on gfx950 (a third when the
+// attention reads the working set in HBM: the plan's block copies).
 //
 // The OasisKV pages split a decode step into a foreground half, attention of the
 // current token over the blocks resident in HBM now, and a background half, the
@@ -26,7 +27,7 @@ namespace oasis {
 
 static_assert(kScoreWaves == kAttnWaves, "one workgroup size for both roles");
 
-template <int RT, int GP>
+template <int RT, int GP, bool POOL = false>
 __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void score_attn_kernel(ScoreArgs sa, AttnArgs aa,
                                                                              int n_score, int score_gx,
                                                                              int attn_gx) {
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void score_a
     score_wg<RT>(b % score_gx, b / score_gx, sh.s, sa);
   } else {
     const int i = b - n_score;
-    attn_split_wg<GP, true>(i % attn_gx, i / attn_gx, sh.a, aa);
+    attn_split_wg<GP, true, POOL>(i % attn_gx, i / attn_gx, sh.a, aa);
   }
 }
 
@@ -64,11 +65,17 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
                                   int32_t* topk, const int32_t* resident, int32_t* resident_next,
                                   int32_t* plan, int32_t* plan_count, int32_t* table,
                                   int32_t* table_count, float scale, float* out, float* lse,
-                                  void* ws, hipStream_t stream, hipEvent_t after_first) {
+                                  void* ws, hipStream_t stream, hipEvent_t after_first,
+                                  const WorkingSet* pool) {
   const int heads = d.batch * d.heads;
   const AttnSplit s = attn_split(d, d.table_stride);
   const ScoreArgs sa = score_args(d, q, summ, seq_lens, scores);
-  const AttnArgs aa = attn_args(d, s, q, k, v, resident, nullptr, d.table_stride, seq_lens, scale, ws);
+  AttnArgs aa = attn_args(d, s, q, pool ? pool->pool_k : k, pool ? pool->pool_v : v, resident,
+                          nullptr, d.table_stride, seq_lens, scale, ws);
+  if (pool) {
+    aa.ring_k = (const char*)pool->ring_k;
+    aa.ring_v = (const char*)pool->ring_v;
+  }
   const int score_gx = score_grid_x(d);
   const int n_score = score_gx * heads;
   const int attn_gx = s.num_splits;
@@ -81,8 +88,12 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
   switch (rt <= 2 ? rt * 100 + gp : 0) {
 #define OASIS_SA_CASE(RT, GP)                                                                  \
   case RT * 100 + GP:                                                                          \
-    score_attn_kernel<RT, GP><<<dim3(grid1), dim3(64 * kAttnWaves), 0, stream>>>(sa, aa, n_score, score_gx, \
-                                                                     attn_gx);                 \
+    if (pool)                                                                                  \
+      score_attn_kernel<RT, GP, true><<<dim3(grid1), dim3(64 * kAttnWaves), 0, stream>>>(     \
+          sa, aa, n_score, score_gx, attn_gx);                                                 \
+    else                                                                                       \
+      score_attn_kernel<RT, GP><<<dim3(grid1), dim3(64 * kAttnWaves), 0, stream>>>(           \
+          sa, aa, n_score, score_gx, attn_gx);                                                 \
     break;
     OASIS_SA_CASE(1, 4)
     OASIS_SA_CASE(1, 8)
@@ -94,8 +105,12 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
     default: {
       hipError_t e = launch_score(d, q, summ, seq_lens, scores, stream);
       if (e != hipSuccess) return e;
-      e = launch_attention_split(d, s, q, k, v, resident, nullptr, d.table_stride, seq_lens, scale, ws,
-                                 stream, true);
+      if (pool)
+        e = launch_attention_split_pool(d, s, q, pool->pool_k, pool->pool_v, pool->ring_k,
+                                        pool->ring_v, resident, seq_lens, scale, ws, stream);
+      else
+        e = launch_attention_split(d, s, q, k, v, resident, nullptr, d.table_stride, seq_lens, scale,
+                                   ws, stream, true);
       if (e != hipSuccess) return e;
     }
   }
@@ -114,7 +129,11 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
     break;
   OASIS_SELECT_DISPATCH(OASIS_SM_CASE);
 #undef OASIS_SM_CASE
-  return hipGetLastError();
+  hipError_t err2 = hipGetLastError();
+  if (err2 != hipSuccess || pool == nullptr) return err2;
+  // The attention has read the pool (launch 1), so the admitted blocks can take
+  // their slots now.
+  return launch_execute_plan(d, plan, plan_count, k, v, pool->pool_k, pool->pool_v, stream);
 }
 
 }  // namespace oasis

@@ -44,6 +44,13 @@ hipError_t launch_attention_split(const Dims& d, const AttnSplit& s, const void*
                                   const void* v, const int32_t* table, const int32_t* table_count,
                                   int table_stride, const int32_t* seq_lens, float scale, void* ws,
                                   hipStream_t stream, bool from_resident = false);
+// The same over the working set: resident slot e read from pool slot e, window
+// block j from ring slot j % (table_stride - top_k).
+hipError_t launch_attention_split_pool(const Dims& d, const AttnSplit& s, const void* q,
+                                       const void* pool_k, const void* pool_v, const void* ring_k,
+                                       const void* ring_v, const int32_t* resident,
+                                       const int32_t* seq_lens, float scale, void* ws,
+                                       hipStream_t stream);
 hipError_t launch_attention_merge(const Dims& d, const AttnSplit& s, float* out, float* lse,
                                   const void* ws, hipStream_t stream);
 hipError_t launch_attention(const Dims& d, const void* q, const void* k, const void* v,
@@ -51,13 +58,39 @@ hipError_t launch_attention(const Dims& d, const void* q, const void* k, const v
                             const int32_t* seq_lens, float scale, float* out, float* lse, void* ws,
                             hipStream_t stream, bool from_resident = false);
 
+// The working set in HBM: per (sequence, KV head) a pool of top_k block slots and a
+// ring of WB = table_stride - top_k window block slots, each slot 16 tokens of K
+// (or V) bf16.
+struct WorkingSet {
+  void* pool_k;
+  void* pool_v;
+  void* ring_k;
+  void* ring_v;
+};
+// Gathers the working set of the slot table `resident` from the full cache k, v.
+hipError_t launch_fill_working_set(const Dims& d, const int32_t* resident, const int32_t* seq_lens,
+                                   const void* k, const void* v, const WorkingSet& w,
+                                   hipStream_t stream);
+// Copies each plan row's admitted block from the full cache into its pool slot.
+hipError_t launch_execute_plan(const Dims& d, const int32_t* plan, const int32_t* plan_count,
+                               const void* k, const void* v, void* pool_k, void* pool_v,
+                               hipStream_t stream);
+// Appends one token per sequence at position seq_lens[b]: full cache (if k is not
+// NULL), ring, and the summary of its block.
+hipError_t launch_append_token(const Dims& d, const void* k_new, const void* v_new,
+                               const int32_t* seq_lens, void* summ, void* k, void* v,
+                               void* ring_k, void* ring_v, hipStream_t stream);
+
 // The overlapped step (attention over `resident` and the window; scoring, selection
-// and plan into `resident_next`) as two fused launches on `stream`.
+// and plan into `resident_next`) as two fused launches on `stream`.  With `pool`, the
+// attention reads the working set and a third launch then executes the plan, copying
+// the admitted blocks from k, v into the pool.
 hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ, const void* k,
                                   const void* v, const int32_t* seq_lens, float* scores,
                                   int32_t* topk, const int32_t* resident, int32_t* resident_next,
                                   int32_t* plan, int32_t* plan_count, int32_t* table,
                                   int32_t* table_count, float scale, float* out, float* lse,
-                                  void* ws, hipStream_t stream, hipEvent_t after_first = nullptr);
+                                  void* ws, hipStream_t stream, hipEvent_t after_first = nullptr,
+                                  const WorkingSet* pool = nullptr);
 
 }  // namespace oasis

@@ -1,0 +1,151 @@
+// Executing the plan: the working set of every KV head in HBM, on gfx950.
+//
+// The full K/V cache stays where it is (host memory, or HBM when it fits) and
+// keeps its layout: that is the page table, which never changes.  HBM holds, per
+// (sequence, KV head), a pool of K block slots, which the head's resident slot
+// table maps to logical blocks (the head-wise logical-to-logical map), and a ring
+// of window blocks (xllm-io review, section three: component table, head-wise
+// mapping above the paged cache, and training flow steps 2 and 3: the GPU keeps
+// the selected historical blocks and the local window, and the plan is carried
+// out as an asynchronous transfer; section four, innovations table: only
+// head-wise mapping entries change; legiblepapers.com FAQ Q4; lode.cx points 1
+// and 3).  Pool slot s holds the block of slot s; window block j sits in ring
+// slot j % WB, WB = ceil(W/16) + 1 being the most window blocks a length has.
+//
+// Kernels:
+//   fill_working_set_kernel  gathers a slot table's pool and the window ring from
+//                            the full cache (admission, or a rebuild);
+//   execute_plan_kernel      copies each plan row's admitted block into its slot
+//                            (the evicted block needs no transfer: the full tier
+//                            keeps every block);
+//   append_token_kernel      writes a decoded token's K and V into the full cache
+//                            and the ring and updates its block's min/max summary
+//                            in place (the compressed-key update, xllm-io review,
+//                            section five).
+// A block copy is one 256-thread workgroup moving 4 KB of K and 4 KB of V, one 16-byte
+// load and store per thread and tensor, so that copies from host memory (a mapped
+// pinned buffer read over the host link) and from HBM take the same code.
+#include "common.h"
+#include "launch.h"
+
+namespace oasis {
+
+constexpr int kChunksPerBlock = kBlock * kHeadDim * 2 / 16;  // 16-byte chunks of one block (256)
+
+__device__ inline void copy_block(const u32x4* __restrict__ sk, const u32x4* __restrict__ sv,
+                                  u32x4* __restrict__ dk, u32x4* __restrict__ dv) {
+  const int t = threadIdx.x;
+  const u32x4 a = sk[t], b = sv[t];
+  dk[t] = a;
+  dv[t] = b;
+}
+
+// Workgroup (s, bh): pool slot s < K, else ring slot s - K, of (sequence, KV head) bh.
+__global__ __launch_bounds__(kChunksPerBlock) void fill_working_set_kernel(
+    const int32_t* __restrict__ resident, const int32_t* __restrict__ seq_lens,
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v, u32x4* __restrict__ pool_k,
+    u32x4* __restrict__ pool_v, u32x4* __restrict__ ring_k, u32x4* __restrict__ ring_v,
+    int heads, int NB, int K, int WB, int window) {
+  const int s = blockIdx.x, bh = blockIdx.y;
+  int j;
+  size_t dst;
+  u32x4 *dk, *dv;
+  if (s < K) {
+    j = resident[(size_t)bh * K + s];
+    if (j < 0 || j >= NB) return;  // empty slot: left as it is
+    dst = ((size_t)bh * K + s) * kChunksPerBlock;
+    dk = pool_k;
+    dv = pool_v;
+  } else {
+    const int r = s - K;
+    const int len = clamp_len(seq_lens[bh / heads], NB);
+    const int w0 = first_window_block(len, window), nb = num_blocks(len);
+    j = w0 + ((r - w0 % WB) % WB + WB) % WB;  // the window block of ring slot r, if any
+    if (j >= nb) return;
+    dst = ((size_t)bh * WB + r) * kChunksPerBlock;
+    dk = ring_k;
+    dv = ring_v;
+  }
+  const size_t src = ((size_t)bh * NB + j) * kChunksPerBlock;
+  copy_block(k + src, v + src, dk + dst, dv + dst);
+}
+
+// Workgroup (i, bh): plan row i of (sequence, KV head) bh, if below its count.
+__global__ __launch_bounds__(kChunksPerBlock) void execute_plan_kernel(
+    const int32_t* __restrict__ plan, const int32_t* __restrict__ plan_count,
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v, u32x4* __restrict__ pool_k,
+    u32x4* __restrict__ pool_v, int NB, int K, int C) {
+  const int i = blockIdx.x, bh = blockIdx.y;
+  if (i >= plan_count[bh]) return;
+  const int32_t* row = plan + ((size_t)bh * C + i) * 3;
+  const int slot = row[0], blk = row[1];
+  if (slot < 0 || slot >= K || blk < 0 || blk >= NB) return;
+  const size_t src = ((size_t)bh * NB + blk) * kChunksPerBlock;
+  const size_t dst = ((size_t)bh * K + slot) * kChunksPerBlock;
+  copy_block(k + src, v + src, pool_k + dst, pool_v + dst);
+}
+
+// Workgroup bh, one wave: lane l owns head dims 2l and 2l + 1 (one packed bf16 pair).
+__global__ __launch_bounds__(64) void append_token_kernel(
+    const uint32_t* __restrict__ k_new, const uint32_t* __restrict__ v_new,
+    const int32_t* __restrict__ seq_lens, uint32_t* __restrict__ summ, uint32_t* __restrict__ k,
+    uint32_t* __restrict__ v, uint32_t* __restrict__ ring_k, uint32_t* __restrict__ ring_v,
+    int heads, int NB, int WB) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  const int L = seq_lens[bh / heads];
+  if (L < 0 || L >= NB * kBlock) return;  // no room: the sequence is skipped
+  const int j = L / kBlock, t = L % kBlock;
+  const uint32_t kn = k_new[(size_t)bh * 64 + lane], vn = v_new[(size_t)bh * 64 + lane];
+  const size_t tok = (((size_t)bh * NB + j) * kBlock + t) * 64 + lane;
+  if (k != nullptr) {
+    k[tok] = kn;
+    v[tok] = vn;
+  }
+  const size_t rtok = (((size_t)bh * WB + j % WB) * kBlock + t) * 64 + lane;
+  ring_k[rtok] = kn;
+  ring_v[rtok] = vn;
+  uint32_t* su = summ + ((size_t)bh * NB + j) * 128 + lane;  // min at [0], max at [64]
+  if (t == 0) {  // the token opens its block
+    su[0] = kn;
+    su[64] = kn;
+  } else {
+    const uint32_t lo = su[0], hi = su[64];
+    const float mn0 = fminf(bf16_lo(lo), bf16_lo(kn)), mn1 = fminf(bf16_hi(lo), bf16_hi(kn));
+    const float mx0 = fmaxf(bf16_lo(hi), bf16_lo(kn)), mx1 = fmaxf(bf16_hi(hi), bf16_hi(kn));
+    // Each result is one of two bf16 values, so keeping its top 16 bits is exact.
+    su[0] = (__float_as_uint(mn0) >> 16) | (__float_as_uint(mn1) & 0xffff0000u);
+    su[64] = (__float_as_uint(mx0) >> 16) | (__float_as_uint(mx1) & 0xffff0000u);
+  }
+}
+
+hipError_t launch_fill_working_set(const Dims& d, const int32_t* resident, const int32_t* seq_lens,
+                                   const void* k, const void* v, const WorkingSet& w,
+                                   hipStream_t stream) {
+  const int WB = d.table_stride - d.top_k;
+  fill_working_set_kernel<<<dim3(d.top_k + WB, d.batch * d.heads), dim3(kChunksPerBlock), 0, stream>>>(
+      resident, seq_lens, (const u32x4*)k, (const u32x4*)v, (u32x4*)w.pool_k, (u32x4*)w.pool_v,
+      (u32x4*)w.ring_k, (u32x4*)w.ring_v, d.heads, d.max_blocks, d.top_k, WB, d.window);
+  return hipGetLastError();
+}
+
+hipError_t launch_execute_plan(const Dims& d, const int32_t* plan, const int32_t* plan_count,
+                               const void* k, const void* v, void* pool_k, void* pool_v,
+                               hipStream_t stream) {
+  if (d.cap <= 0 || plan == nullptr) return hipSuccess;  // nothing can be admitted
+  execute_plan_kernel<<<dim3(d.cap, d.batch * d.heads), dim3(kChunksPerBlock), 0, stream>>>(
+      plan, plan_count, (const u32x4*)k, (const u32x4*)v, (u32x4*)pool_k, (u32x4*)pool_v,
+      d.max_blocks, d.top_k, d.cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_token(const Dims& d, const void* k_new, const void* v_new,
+                               const int32_t* seq_lens, void* summ, void* k, void* v,
+                               void* ring_k, void* ring_v, hipStream_t stream) {
+  append_token_kernel<<<dim3(d.batch * d.heads), dim3(64), 0, stream>>>(
+      (const uint32_t*)k_new, (const uint32_t*)v_new, seq_lens, (uint32_t*)summ, (uint32_t*)k,
+      (uint32_t*)v, (uint32_t*)ring_k, (uint32_t*)ring_v, d.heads, d.max_blocks,
+      d.table_stride - d.top_k);
+  return hipGetLastError();
+}
+
+}  // namespace oasis

@@ -44,7 +44,7 @@ def _dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.exported_symbols())
@@ -167,3 +167,41 @@ def test_overlapped_step_argument_checks(lib):
     st = lib.oasis_sparse_decode_attn_resident(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1,
                                                FAKE, None, FAKE, need - 1, None)
     assert st == WORKSPACE
+
+
+@cpu_only
+def test_working_set_argument_checks(lib):
+    """NULL and overlapping working-set buffers are rejected before any launch."""
+    d = _dims()
+    assert lib.oasis_window_ring_slots(ctypes.byref(d)) == lib.oasis_table_stride(ctypes.byref(d)) - 16
+    assert lib.oasis_window_ring_slots(ctypes.byref(_dims(window_tokens=0))) == 1
+    assert lib.oasis_window_ring_slots(ctypes.byref(_dims(batch=0))) == -1
+    blk = 16 * 128 * 2
+    full = 2 * 2 * 64 * blk
+    k, v = 0x100000, 0x100000 + full
+    pk, pv = 0x10000000, 0x10000000 + 2 * 2 * 16 * blk
+    rk, rv = 0x20000000, 0x20000000 + 2 * 2 * 5 * blk
+    P = ctypes.c_void_p
+
+    def fill(*ptrs):
+        return lib.oasis_fill_working_set(ctypes.byref(d), FAKE, FAKE, *[P(x) if x else None for x in ptrs], None)
+
+    assert fill(k, v, pk, pv, rk, None) == INVALID_ARG and b"NULL" in lib.oasis_last_error()
+    assert fill(k, k + 64, pk, pv, rk, rv) == INVALID_ARG and b"overlap" in lib.oasis_last_error()
+    assert fill(k, v, pk, pk + blk, rk, rv) == INVALID_ARG                       # pool_k / pool_v
+    assert fill(k, v, pk, pv, pv + 64, rv) == INVALID_ARG                        # pool_v / ring_k
+    d4 = _dims(fetch_ratio=0.25)
+    assert lib.oasis_execute_plan(ctypes.byref(d4), None, FAKE, P(k), P(v), P(pk), P(pv), None) \
+        == INVALID_ARG                                                           # cap 4: plan needed
+    d0 = _dims(fetch_ratio=0.01)
+    assert lib.oasis_execute_plan(ctypes.byref(d0), None, None, P(k), P(v), P(pk), P(pv), None) \
+        == INVALID_ARG                                                           # plan_count needed
+    assert lib.oasis_append_token(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, P(k), None, P(rk), P(rv),
+                                  None) == INVALID_ARG                            # k without v
+    need = lib.oasis_workspace_bytes(ctypes.byref(d))
+    assert lib.oasis_sparse_decode_attn_pool(ctypes.byref(d), FAKE, P(pk), P(pv), P(rk), P(rv), FAKE,
+                                             FAKE, 0.1, FAKE, None, FAKE, need - 1, None) == WORKSPACE
+    st = lib.oasis_decode_step_pool(ctypes.byref(d), FAKE, FAKE, P(k), P(v), P(pk), P(pv), P(rk),
+                                    P(rv), FAKE, FAKE, FAKE, P(0x30000000), P(0x30000000), FAKE, FAKE,
+                                    FAKE, FAKE, 0.1, FAKE, None, FAKE, need, None)
+    assert st == INVALID_ARG and b"own buffer" in lib.oasis_last_error()
