@@ -262,6 +262,104 @@ def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     return out
 
 
+def plan_execution(w, d, sets, buffers, res_next, ms_step: float, stage_us: dict, torch, oa,
+                   host_sets: int = 2, reps: int = 40) -> dict:
+    """The step over the working set in HBM (attention from the pool and the window
+    ring, then the plan's block copies into the pool), with the full cache in HBM
+    and in pinned host memory; the copy launch alone; the bulk host-to-device rate;
+    and the per-step transfer budget of the pages' Eq. (3) and stage bound of
+    Eq. (4).  Repeated steps re-run the same plan, so every step moves the same
+    blocks (correctness is the parity tests' business)."""
+    dev = torch.device("cuda:0")
+
+    def graph_ms(step_list):
+        for i in range(3 * len(step_list)):
+            step_list[i % len(step_list)]()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_list[0]()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for st in step_list:
+                st()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(step_list))
+
+    def launch_us(fn, n=60):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for i in range(n):
+            evs[2 * i].record()
+            fn()
+            evs[2 * i + 1].record()
+        torch.cuda.synchronize()
+        return 1e3 * statistics.mean(evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(n))
+
+    wsets = [oa.fill_working_set(d, s["resident"], s["seq_lens"], s["k"], s["v"]) for s in sets]
+    dev_steps = [oa.PreparedPoolStep(d, s["q"], s["summ"], s["k"], s["v"], ws, s["seq_lens"],
+                                     s["resident"], buffers, res_next) for s, ws in zip(sets, wsets)]
+    out = {"device_tier_ms_per_step": round(graph_ms(dev_steps), 6)}
+    # One step of set 0 leaves its plan in the buffers: the copies alone, from HBM.
+    dev_steps[0]()
+    torch.cuda.synchronize()
+    moved = int(buffers.plan_count.sum()) * BLOCK_KV_BYTES
+    plan = buffers.plan.clone()
+    count = buffers.plan_count.clone()
+    copy_dev = oa.PreparedPlanCopy(d, plan, count, sets[0]["k"], sets[0]["v"], wsets[0])
+    us_dev = launch_us(copy_dev)
+    out["plan_bytes_per_step"] = moved
+    out["plan_bytes_cap"] = w.batch * w.num_kv_heads * w.cap * BLOCK_KV_BYTES
+    out["copy_device_tier_us"] = round(us_dev, 3)
+    out["copy_device_tier_gbps"] = round(moved / (us_dev * 1e-6) / 1e9, 1)
+    # The full cache in pinned host memory (first host_sets input sets).
+    hosts = [(s["k"].cpu().pin_memory(), s["v"].cpu().pin_memory()) for s in sets[:host_sets]]
+    host_steps = [oa.PreparedPoolStep(d, s["q"], s["summ"], hk, hv, ws, s["seq_lens"], s["resident"],
+                                      buffers, res_next)
+                  for s, ws, (hk, hv) in zip(sets, wsets, hosts)]
+    out["host_tier_ms_per_step"] = round(graph_ms(host_steps), 6)
+    out["host_tier_input_sets"] = host_sets
+    copy_host = oa.PreparedPlanCopy(d, plan, count, hosts[0][0], hosts[0][1], wsets[0])
+    us_host = launch_us(copy_host)
+    link_gbps = moved / (us_host * 1e-6) / 1e9
+    out["copy_host_tier_us"] = round(us_host, 3)
+    out["copy_host_tier_gbps"] = round(link_gbps, 2)
+    # Bulk host-to-device copy of 1 GiB of pinned memory (the link's streaming rate).
+    src = torch.empty(1 << 29, dtype=torch.bfloat16).pin_memory()
+    dst = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(4):
+        dst.copy_(src, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    bulk = 4 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    out["bulk_h2d_gbps"] = round(bulk, 2)
+    del src, dst, hosts, host_steps
+    # Eq. (3): bytes the link can move while one layer's step computes, at the rate the
+    # plan's copies reach; Eq. (4): the slowest background stage against that step.
+    t_step = ms_step * 1e-3
+    out["eq3"] = {"link_gbps": round(link_gbps, 2), "t_step_us": round(ms_step * 1e3, 3),
+                  "c_token_bytes": int(link_gbps * 1e9 * t_step),
+                  "plan_bytes_per_step": moved,
+                  "fits": bool(moved <= link_gbps * 1e9 * t_step)}
+    t_pipe = max(stage_us["score"], stage_us["select_plan"], us_host)
+    out["eq4"] = {"t_pred_us": round(stage_us["score"], 3), "t_select_us": round(stage_us["select_plan"], 3),
+                  "t_transfer_us": round(us_host, 3), "t_pipe_us": round(t_pipe, 3),
+                  "delta_prefetch_us": round(ms_step * 1e3, 3)}
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +381,8 @@ def main(argv=None) -> int:
                     help="write the traffic file from two rocprofv3 --pmc runs of "
                          "'bench.py --calibrate' (FETCH_SIZE, then WRITE_SIZE) and exit")
     ap.add_argument("--counter-command", default="", help="the command recorded in the traffic file")
+    ap.add_argument("--no-plan-exec", action="store_true",
+                    help="skip the working-set measurements (step over the pool, plan copies, host tier)")
     args = ap.parse_args(argv)
     if args.summarize_counters:
         kernel, text = summarize_counters(*args.summarize_counters, args.workload, args.counter_command)
@@ -495,6 +595,9 @@ def main(argv=None) -> int:
         "setup_s": round(setup_s, 1),
         "checks": check,
     }
+    if not args.no_plan_exec:
+        result["plan_execution"] = plan_execution(w, d, sets, buffers, res_next, ms_per_step, stage_us,
+                                                  torch, oa)
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(w, sets, args.cpu_budget, args.order == "overlapped")
     print(json.dumps(result), flush=True)

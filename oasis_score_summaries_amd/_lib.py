@@ -701,3 +701,54 @@ class PreparedStep:
                    "oasis_decode_step_timed")
         else:
             _check(self.lib.oasis_decode_step(*self.args, st), "oasis_decode_step")
+
+
+class PreparedPoolStep:
+    """oasis_decode_step_pool with its arguments checked and marshalled once (the
+    full cache k, v may be pinned host tensors).  The tensors must stay alive and
+    keep their storage while the object is used."""
+
+    def __init__(self, dims: OasisDims, q, summ, k, v, wset: WorkingSet, seq_lens, resident,
+                 buffers: StepBuffers, resident_next, scale: Optional[float] = None):
+        s = _shapes(dims)
+        _need(q, "q", torch.bfloat16, s["q"], align=16)
+        dev = q.device
+        _need(summ, "summ", torch.bfloat16, s["summ"], dev, align=16)
+        kp, vp = _cache_ptr(k, "k", s["kv"], dev), _cache_ptr(v, "v", s["kv"], dev)
+        wset.check(dev)
+        _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+        _need(resident, "resident", torch.int32, s["resident"], dev)
+        _need(resident_next, "resident_next", torch.int32, s["resident"], dev)
+        b = buffers
+        if b.ws.numel() < workspace_bytes(dims):
+            raise ValueError("workspace too small")
+        self.keep = (q, summ, k, v, wset, seq_lens, resident, resident_next, b)
+        scale = 1.0 / math.sqrt(128) if scale is None else float(scale)
+        self.args = [ctypes.byref(dims), _ptr(q), _ptr(summ), kp, vp, _ptr(wset.pool_k),
+                     _ptr(wset.pool_v), _ptr(wset.ring_k), _ptr(wset.ring_v), _ptr(seq_lens),
+                     _ptr(b.scores), _ptr(b.topk), _ptr(resident), _ptr(resident_next),
+                     _ptr(b.plan if b.plan.numel() else None), _ptr(b.plan_count), _ptr(b.table),
+                     _ptr(b.table_count), ctypes.c_float(scale), _ptr(b.out), _ptr(b.lse), _ptr(b.ws),
+                     ctypes.c_size_t(b.ws.numel())]
+        self.lib = load()
+
+    def __call__(self, stream=None) -> None:
+        _check(self.lib.oasis_decode_step_pool(*self.args, _stream(stream)), "oasis_decode_step_pool")
+
+
+class PreparedPlanCopy:
+    """oasis_execute_plan with its arguments marshalled once."""
+
+    def __init__(self, dims: OasisDims, plan, plan_count, k, v, wset: WorkingSet):
+        s = _shapes(dims)
+        _need(plan_count, "plan_count", torch.int32, s["bh"])
+        dev = plan_count.device
+        kp, vp = _cache_ptr(k, "k", s["kv"], dev), _cache_ptr(v, "v", s["kv"], dev)
+        wset.check(dev)
+        self.keep = (plan, plan_count, k, v, wset)
+        self.args = [ctypes.byref(dims), _ptr(plan if plan.numel() else None), _ptr(plan_count), kp, vp,
+                     _ptr(wset.pool_k), _ptr(wset.pool_v)]
+        self.lib = load()
+
+    def __call__(self, stream=None) -> None:
+        _check(self.lib.oasis_execute_plan(*self.args, _stream(stream)), "oasis_execute_plan")
