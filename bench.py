@@ -360,6 +360,98 @@ def plan_execution(w, d, sets, buffers, res_next, ms_step: float, stage_us: dict
     return out
 
 
+SWEEP = [(64, 0.05), (128, 0.05), (192, 0.05),
+         (128, 0.01), (128, 0.02), (128, 0.10), (128, 0.20), (128, 1.0)]
+
+
+def run_sweep(args) -> dict:
+    """The pages' ablations at kernel level (K and the fetch ratio) on one workload's
+    inputs: per variant the overlapped step from the full cache in HBM, the step over
+    the working set with the full cache in HBM and in pinned host memory (where the
+    fetch ratio sets the bytes crossing the host link), and the plan's bytes."""
+    import torch
+
+    import oasis_score_summaries_amd as oa
+    import synth
+
+    dev = torch.device("cuda:0")
+    base = synth.WORKLOADS[args.workload]
+    n_sets = args.sets
+    sets = []
+    for i in range(n_sets):
+        inp = synth.generate(base, dev, layer=i)
+        d0 = oa.dims_for(base)
+        sets.append({"q": inp["q"], "q_sel": inp["q_prev"] if base.resident == "prev" else inp["q"],
+                     "k": inp["k"], "v": inp["v"], "seq_lens": inp["seq_lens"],
+                     "summ": oa.build_summaries(d0, inp["k"], inp["seq_lens"])})
+        del inp
+    hosts = [(s["k"].cpu().pin_memory(), s["v"].cpu().pin_memory()) for s in sets[:2]]
+
+    def graph_ms(step_list, reps=30):
+        for i in range(3 * len(step_list)):
+            step_list[i % len(step_list)]()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_list[0]()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for st in step_list:
+                st()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(step_list))
+
+    rows = []
+    for top_k, ratio in SWEEP:
+        w = base.with_(top_k=top_k, fetch_ratio=ratio)
+        d = oa.dims_for(w)
+        residents = []
+        for i, st in enumerate(sets):
+            sel = oa.topk_blocks(d, oa.score_summaries(d, st["q_sel"], st["summ"], st["seq_lens"]),
+                                 st["seq_lens"])
+            residents.append(synth.resident_from_selection(w, sel, st["seq_lens"].cpu(), layer=i).to(dev))
+        bufs = oa.StepBuffers(d, dev)
+        rn = torch.empty_like(residents[0])
+        over = [oa.PreparedStep(d, st["q"], st["summ"], st["k"], st["v"], st["seq_lens"], r, bufs,
+                                resident_next=rn, overlapped=True) for st, r in zip(sets, residents)]
+        ms_over = graph_ms(over)
+        wsets = [oa.fill_working_set(d, r, st["seq_lens"], st["k"], st["v"]) for st, r in zip(sets, residents)]
+        pool_dev = [oa.PreparedPoolStep(d, st["q"], st["summ"], st["k"], st["v"], ws, st["seq_lens"], r,
+                                        bufs, rn) for st, r, ws in zip(sets, residents, wsets)]
+        ms_pool_dev = graph_ms(pool_dev)
+        pool_host = [oa.PreparedPoolStep(d, st["q"], st["summ"], hk, hv, ws, st["seq_lens"], r, bufs, rn)
+                     for st, r, ws, (hk, hv) in zip(sets, residents, wsets, hosts)]
+        ms_pool_host = graph_ms(pool_host, reps=max(3, int(30 * 0.1 / max(ratio, 0.01))))
+        moved = 0
+        for st, r in zip(sets, residents):   # the plan bytes of every set's step
+            oa.decode_step_overlapped(d, st["q"], st["summ"], st["k"], st["v"], st["seq_lens"], r, rn,
+                                      buffers=bufs)
+            moved += int(bufs.plan_count.sum()) * BLOCK_KV_BYTES
+        torch.cuda.synchronize()
+        rows.append({"top_k": top_k, "fetch_ratio": ratio, "cap": w.cap,
+                     "overlapped_ms_per_step": round(ms_over, 6),
+                     "overlapped_steps_per_s": round(1e3 / ms_over, 1),
+                     "pool_device_tier_ms_per_step": round(ms_pool_dev, 6),
+                     "pool_host_tier_ms_per_step": round(ms_pool_host, 6),
+                     "plan_bytes_per_step": moved // n_sets,
+                     "table_blocks_per_head": top_k + (w.window + 15) // 16})
+        del over, pool_dev, pool_host, wsets, bufs, residents
+        torch.cuda.empty_cache()
+    return {"metric": "variant sweep: step time against top-K and fetch ratio", "workload": base.name,
+            "input_sets": n_sets, "host_tier_input_sets": len(hosts), "block_size": 16,
+            "rows": rows, "data": "synthetic",
+            "note": "block sizes other than 16 are not built (the kernels fix 16-token blocks)"}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -381,6 +473,8 @@ def main(argv=None) -> int:
                     help="write the traffic file from two rocprofv3 --pmc runs of "
                          "'bench.py --calibrate' (FETCH_SIZE, then WRITE_SIZE) and exit")
     ap.add_argument("--counter-command", default="", help="the command recorded in the traffic file")
+    ap.add_argument("--sweep", action="store_true",
+                    help="print one JSON line with the K and fetch-ratio sweep instead of the benchmark")
     ap.add_argument("--no-plan-exec", action="store_true",
                     help="skip the working-set measurements (step over the pool, plan copies, host tier)")
     args = ap.parse_args(argv)
@@ -406,6 +500,9 @@ def main(argv=None) -> int:
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        print(json.dumps(run_sweep(args)), flush=True)
+        return 0
     w = synth.WORKLOADS[args.workload]
     d = oa.dims_for(w)
     n_sets = w.layers if w.layers > 1 else args.sets

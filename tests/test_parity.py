@@ -321,7 +321,8 @@ def test_decode_step_deterministic(lib):
 
 def _sample_heads(w, n=6):
     rng = np.random.default_rng(1234)
-    heads = [(0, 0), (w.batch - 1, w.num_kv_heads - 1)]
+    heads = list(dict.fromkeys([(0, 0), (w.batch - 1, w.num_kv_heads - 1)]))
+    n = min(n, w.batch * w.num_kv_heads)
     while len(heads) < n:
         heads.append((int(rng.integers(w.batch)), int(rng.integers(w.num_kv_heads))))
         heads = list(dict.fromkeys(heads))
@@ -401,6 +402,15 @@ def _full_size_case(lib, w, layer=0):
 @pytest.mark.parametrize("name", ["qwen3_8b_32k", "long_128k", "qwen3_235b_32k"])
 def test_full_size_workload(lib, name):
     _full_size_case(lib, synth.WORKLOADS[name])
+
+
+@pytest.mark.parametrize("top_k,ratio", [(64, 0.05), (192, 0.05), (128, 0.01), (128, 0.02),
+                                         (128, 0.10), (128, 0.20), (128, 1.0)])
+def test_variant_sweep_shapes(lib, top_k, ratio):
+    """The shapes of the K and fetch-ratio sweep (the pages' ablations) at the
+    Qwen3-8B 32K shape, two sequences and two KV heads."""
+    w = synth.WORKLOADS["qwen3_8b_32k"].with_(batch=2, num_kv_heads=2, top_k=top_k, fetch_ratio=ratio)
+    _full_size_case(lib, w)
 
 
 @pytest.mark.parametrize("layer", [0, 35])
