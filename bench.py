@@ -262,6 +262,56 @@ def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     return out
 
 
+def layer_pipeline(d, sets, wsets, hosts, torch, oa, steps: int = 20) -> dict:
+    """The input sets as the layers of one decode step, the full cache in pinned host
+    memory: every layer's step over its working set with the plan's copies on the
+    same stream, against the copies on a transfer stream that each layer's next step
+    waits for (the pages' per-layer background transfer), and the foreground alone
+    (no copies).  Eager launches; per-layer buffers; layer i copies from host buffer
+    i mod 2 (the same bytes)."""
+    dev = torch.device("cuda:0")
+    L = len(sets)
+    per = []
+    for i, (st, ws) in enumerate(zip(sets, wsets)):
+        bufs = oa.StepBuffers(d, dev)
+        rn = torch.empty_like(st["resident"])
+        hk, hv = hosts[i % len(hosts)]
+        per.append((oa.PreparedPoolStep(d, st["q"], st["summ"], hk, hv, ws, st["seq_lens"],
+                                        st["resident"], bufs, rn),
+                    oa.PreparedStep(d, st["q"], st["summ"], st["k"], st["v"], st["seq_lens"],
+                                    st["resident"], bufs, resident_next=rn, overlapped=True)))
+    fg, tr = torch.cuda.Stream(), torch.cuda.Stream()
+    done = [torch.cuda.Event() for _ in range(L)]
+
+    def run(mode):
+        for t in range(steps + 2):                     # two warm-up steps
+            if t == 2:
+                fg.wait_stream(tr)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(fg)
+            for i, (pool_step, fg_step) in enumerate(per):
+                if mode == "serial":
+                    pool_step(stream=fg)
+                elif mode == "pipelined":
+                    fg.wait_event(done[i])
+                    pool_step(stream=fg, transfer_stream=tr)
+                    done[i].record(tr)
+                else:
+                    fg_step(stream=fg)
+        fg.wait_stream(tr)
+        e1.record(fg)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (steps * L)
+
+    for ev in done:
+        ev.record(tr)
+    res = {"layers": L, "decode_steps": steps}
+    for mode in ("foreground_only", "serial", "pipelined"):
+        res[f"{mode}_us_per_layer"] = round(run(mode), 3)
+    return res
+
+
 def plan_execution(w, d, sets, buffers, res_next, ms_step: float, stage_us: dict, torch, oa,
                    host_sets: int = 2, reps: int = 40) -> dict:
     """The step over the working set in HBM (attention from the pool and the window
@@ -345,6 +395,7 @@ def plan_execution(w, d, sets, buffers, res_next, ms_step: float, stage_us: dict
     torch.cuda.synchronize()
     bulk = 4 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     out["bulk_h2d_gbps"] = round(bulk, 2)
+    out["layer_pipeline"] = layer_pipeline(d, sets, wsets, hosts, torch, oa)
     del src, dst, hosts, host_steps
     # Eq. (3): bytes the link can move while one layer's step computes, at the rate the
     # plan's copies reach; Eq. (4): the slowest background stage against that step.
@@ -437,7 +488,11 @@ def run_sweep(args) -> dict:
                                       buffers=bufs)
             moved += int(bufs.plan_count.sum()) * BLOCK_KV_BYTES
         torch.cuda.synchronize()
+        pipe = layer_pipeline(d, [{**st, "resident": r} for st, r in zip(sets, residents)], wsets, hosts,
+                              torch, oa, steps=10)
         rows.append({"top_k": top_k, "fetch_ratio": ratio, "cap": w.cap,
+                     "layer_pipeline_us_per_layer": {k.replace("_us_per_layer", ""): v
+                                                     for k, v in pipe.items() if k.endswith("_us_per_layer")},
                      "overlapped_ms_per_step": round(ms_over, 6),
                      "overlapped_steps_per_s": round(1e3 / ms_over, 1),
                      "pool_device_tier_ms_per_step": round(ms_pool_dev, 6),

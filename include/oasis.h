@@ -369,6 +369,25 @@ oasis_status oasis_decode_step_pool(const oasis_dims* dims, const void* q, const
                                     int32_t* table_count, float scale, float* out, float* lse,
                                     void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* oasis_decode_step_pool with the plan's copies on a background stream, for a
+ * layer-pipelined decode (xllm-io review, section three: component table,
+ * asynchronous pipeline of per-layer background workers on their own streams;
+ * section five: stream events order the work of each layer; Eq. (4)): the two
+ * launches of the step go to `stream`, `plan_ready` (a caller-created event) is
+ * recorded on it after them, and `transfer_stream` waits for that event and then
+ * runs the copies.  The caller must make the next reader of the pool (this
+ * layer's next step) wait for `transfer_stream`, and must not overwrite `plan`
+ * and `plan_count` before the copies have run (per-layer buffers).
+ * transfer_stream must differ from stream.  Other arguments as for
+ * oasis_decode_step_pool. */
+oasis_status oasis_decode_step_pool_async(
+    const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
+    void* pool_k, void* pool_v, const void* ring_k, const void* ring_v, const int32_t* seq_lens,
+    float* scores, int32_t* topk, const int32_t* resident, int32_t* resident_next, int32_t* plan,
+    int32_t* plan_count, int32_t* table, int32_t* table_count, float scale, float* out, float* lse,
+    void* ws, size_t ws_bytes, hipStream_t stream, hipStream_t transfer_stream,
+    hipEvent_t plan_ready);
+
 #ifdef __cplusplus
 }
 #endif

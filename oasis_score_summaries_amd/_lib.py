@@ -86,6 +86,9 @@ _SIGNATURES = {
     "oasis_decode_step_pool": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                               _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                                               ctypes.c_size_t, _P]),
+    "oasis_decode_step_pool_async": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                    _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
+                                                    ctypes.c_size_t, _P, _P, _P]),
 }
 
 _lib = None
@@ -703,10 +706,31 @@ class PreparedStep:
             _check(self.lib.oasis_decode_step(*self.args, st), "oasis_decode_step")
 
 
+class HipEvent:
+    """A HIP event without timing, for ordering work between streams."""
+
+    def __init__(self):
+        h = _hip_runtime()
+        ev = ctypes.c_void_p()
+        if h.hipEventCreateWithFlags(ctypes.byref(ev), 2) != 0:   # hipEventDisableTiming
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.handle = ev
+
+    def __del__(self):
+        try:
+            if self.handle:
+                _hip_runtime().hipEventDestroy(self.handle)
+        except Exception:
+            pass
+
+
 class PreparedPoolStep:
     """oasis_decode_step_pool with its arguments checked and marshalled once (the
     full cache k, v may be pinned host tensors).  The tensors must stay alive and
-    keep their storage while the object is used."""
+    keep their storage while the object is used.  Called with ``transfer_stream``,
+    it queues oasis_decode_step_pool_async instead: the plan's copies go to that
+    stream after the plan is built (the caller orders this layer's next step after
+    them)."""
 
     def __init__(self, dims: OasisDims, q, summ, k, v, wset: WorkingSet, seq_lens, resident,
                  buffers: StepBuffers, resident_next, scale: Optional[float] = None):
@@ -731,9 +755,17 @@ class PreparedPoolStep:
                      _ptr(b.table_count), ctypes.c_float(scale), _ptr(b.out), _ptr(b.lse), _ptr(b.ws),
                      ctypes.c_size_t(b.ws.numel())]
         self.lib = load()
+        self.plan_ready = None
 
-    def __call__(self, stream=None) -> None:
-        _check(self.lib.oasis_decode_step_pool(*self.args, _stream(stream)), "oasis_decode_step_pool")
+    def __call__(self, stream=None, transfer_stream=None) -> None:
+        if transfer_stream is None:
+            _check(self.lib.oasis_decode_step_pool(*self.args, _stream(stream)), "oasis_decode_step_pool")
+            return
+        if self.plan_ready is None:
+            self.plan_ready = HipEvent()
+        _check(self.lib.oasis_decode_step_pool_async(*self.args, _stream(stream), _stream(transfer_stream),
+                                                     self.plan_ready.handle),
+               "oasis_decode_step_pool_async")
 
 
 class PreparedPlanCopy:

@@ -517,14 +517,13 @@ oasis_status oasis_sparse_decode_attn_pool(const oasis_dims* dims, const void* q
                     "sparse_decode_attn_pool/merge");
 }
 
-oasis_status oasis_decode_step_pool(const oasis_dims* dims, const void* q, const void* summ,
-                                    const void* k, const void* v, void* pool_k, void* pool_v,
-                                    const void* ring_k, const void* ring_v,
-                                    const int32_t* seq_lens, float* scores, int32_t* topk,
-                                    const int32_t* resident, int32_t* resident_next,
-                                    int32_t* plan, int32_t* plan_count, int32_t* table,
-                                    int32_t* table_count, float scale, float* out, float* lse,
-                                    void* ws, size_t ws_bytes, hipStream_t stream) {
+static oasis_status decode_step_pool_impl(
+    const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
+    void* pool_k, void* pool_v, const void* ring_k, const void* ring_v, const int32_t* seq_lens,
+    float* scores, int32_t* topk, const int32_t* resident, int32_t* resident_next, int32_t* plan,
+    int32_t* plan_count, int32_t* table, int32_t* table_count, float scale, float* out, float* lse,
+    void* ws, size_t ws_bytes, hipStream_t stream, bool async, hipStream_t transfer_stream,
+    hipEvent_t plan_ready) {
   oasis::Dims d;
   OASIS_REQUIRE(resident_next);
   oasis_status st = check_step_args(dims, d, q, summ, k, v, seq_lens, scores, topk, resident,
@@ -539,10 +538,51 @@ oasis_status oasis_decode_step_pool(const oasis_dims* dims, const void* q, const
   OASIS_REQUIRE(ring_k);
   OASIS_REQUIRE(ring_v);
   if ((st = check_working_set(d, k, v, pool_k, pool_v, ring_k, ring_v)) != OASIS_OK) return st;
+  if (async) {
+    OASIS_REQUIRE(plan_ready);
+    if (transfer_stream == stream)
+      return fail(OASIS_ERR_INVALID_ARG, "transfer_stream must differ from stream");
+  }
   const oasis::WorkingSet w{pool_k, pool_v, const_cast<void*>(ring_k), const_cast<void*>(ring_v)};
-  return hip_status(oasis::launch_overlapped_step(d, q, summ, k, v, seq_lens, scores, topk, resident,
-                                                  resident_next, plan, plan_count, table,
-                                                  table_count, scale, out, lse, ws, stream, nullptr,
-                                                  &w),
-                    "decode_step_pool");
+  st = hip_status(oasis::launch_overlapped_step(d, q, summ, k, v, seq_lens, scores, topk, resident,
+                                                resident_next, plan, plan_count, table, table_count,
+                                                scale, out, lse, ws, stream, nullptr, &w, !async),
+                  "decode_step_pool");
+  if (st != OASIS_OK || !async) return st;
+  // The copies wait for the plan on the transfer stream; the caller orders the next
+  // read of the pool after them.
+  if ((st = hip_status(hipEventRecord(plan_ready, stream), "decode_step_pool_async/event")) != OASIS_OK)
+    return st;
+  if ((st = hip_status(hipStreamWaitEvent(transfer_stream, plan_ready, 0),
+                       "decode_step_pool_async/wait")) != OASIS_OK)
+    return st;
+  return hip_status(oasis::launch_execute_plan(d, plan, plan_count, k, v, pool_k, pool_v,
+                                               transfer_stream),
+                    "decode_step_pool_async/execute_plan");
+}
+
+oasis_status oasis_decode_step_pool(const oasis_dims* dims, const void* q, const void* summ,
+                                    const void* k, const void* v, void* pool_k, void* pool_v,
+                                    const void* ring_k, const void* ring_v,
+                                    const int32_t* seq_lens, float* scores, int32_t* topk,
+                                    const int32_t* resident, int32_t* resident_next,
+                                    int32_t* plan, int32_t* plan_count, int32_t* table,
+                                    int32_t* table_count, float scale, float* out, float* lse,
+                                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  return decode_step_pool_impl(dims, q, summ, k, v, pool_k, pool_v, ring_k, ring_v, seq_lens, scores,
+                               topk, resident, resident_next, plan, plan_count, table, table_count,
+                               scale, out, lse, ws, ws_bytes, stream, false, nullptr, nullptr);
+}
+
+oasis_status oasis_decode_step_pool_async(
+    const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
+    void* pool_k, void* pool_v, const void* ring_k, const void* ring_v, const int32_t* seq_lens,
+    float* scores, int32_t* topk, const int32_t* resident, int32_t* resident_next, int32_t* plan,
+    int32_t* plan_count, int32_t* table, int32_t* table_count, float scale, float* out, float* lse,
+    void* ws, size_t ws_bytes, hipStream_t stream, hipStream_t transfer_stream,
+    hipEvent_t plan_ready) {
+  return decode_step_pool_impl(dims, q, summ, k, v, pool_k, pool_v, ring_k, ring_v, seq_lens, scores,
+                               topk, resident, resident_next, plan, plan_count, table, table_count,
+                               scale, out, lse, ws, ws_bytes, stream, true, transfer_stream,
+                               plan_ready);
 }

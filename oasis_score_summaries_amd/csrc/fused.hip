@@ -66,7 +66,7 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
                                   int32_t* plan, int32_t* plan_count, int32_t* table,
                                   int32_t* table_count, float scale, float* out, float* lse,
                                   void* ws, hipStream_t stream, hipEvent_t after_first,
-                                  const WorkingSet* pool) {
+                                  const WorkingSet* pool, bool execute_plan) {
   const int heads = d.batch * d.heads;
   const AttnSplit s = attn_split(d, d.table_stride);
   const ScoreArgs sa = score_args(d, q, summ, seq_lens, scores);
@@ -130,7 +130,7 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
   OASIS_SELECT_DISPATCH(OASIS_SM_CASE);
 #undef OASIS_SM_CASE
   hipError_t err2 = hipGetLastError();
-  if (err2 != hipSuccess || pool == nullptr) return err2;
+  if (err2 != hipSuccess || pool == nullptr || !execute_plan) return err2;
   // The attention has read the pool (launch 1), so the admitted blocks can take
   // their slots now.
   return launch_execute_plan(d, plan, plan_count, k, v, pool->pool_k, pool->pool_v, stream);

@@ -83,14 +83,14 @@ hipError_t launch_append_token(const Dims& d, const void* k_new, const void* v_n
 
 // The overlapped step (attention over `resident` and the window; scoring, selection
 // and plan into `resident_next`) as two fused launches on `stream`.  With `pool`, the
-// attention reads the working set and a third launch then executes the plan, copying
-// the admitted blocks from k, v into the pool.
+// attention reads the working set and (with execute_plan) a third launch then executes
+// the plan, copying the admitted blocks from k, v into the pool.
 hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ, const void* k,
                                   const void* v, const int32_t* seq_lens, float* scores,
                                   int32_t* topk, const int32_t* resident, int32_t* resident_next,
                                   int32_t* plan, int32_t* plan_count, int32_t* table,
                                   int32_t* table_count, float scale, float* out, float* lse,
                                   void* ws, hipStream_t stream, hipEvent_t after_first = nullptr,
-                                  const WorkingSet* pool = nullptr);
+                                  const WorkingSet* pool = nullptr, bool execute_plan = true);
 
 }  // namespace oasis

@@ -22,9 +22,9 @@
 //                            and the ring and updates its block's min/max summary
 //                            in place (the compressed-key update, xllm-io review,
 //                            section five).
-// A block copy is one 256-thread workgroup moving 4 KB of K and 4 KB of V, one 16-byte
-// load and store per thread and tensor, so that copies from host memory (a mapped
-// pinned buffer read over the host link) and from HBM take the same code.
+// A block copy moves 4 KB of K and 4 KB of V with 256 threads, one 16-byte load and
+// store per thread and tensor, so that copies from host memory (a mapped pinned
+// buffer read over the host link) and from HBM take the same code.
 #include "common.h"
 #include "launch.h"
 
@@ -70,19 +70,52 @@ __global__ __launch_bounds__(kChunksPerBlock) void fill_working_set_kernel(
   copy_block(k + src, v + src, dk + dst, dv + dst);
 }
 
-// Workgroup (i, bh): plan row i of (sequence, KV head) bh, if below its count.
+// A few workgroups walk all plan rows (row r = bh * C + i), kCopyRows rows per round
+// with every load of the round in flight before the first store: enough bytes in
+// flight to fill the host link or HBM, while holding few CU slots, so that the
+// copies can run beside another stream's kernels.
+constexpr int kCopyRows = 4;
+constexpr int kCopyGrid = 64;
 __global__ __launch_bounds__(kChunksPerBlock) void execute_plan_kernel(
     const int32_t* __restrict__ plan, const int32_t* __restrict__ plan_count,
     const u32x4* __restrict__ k, const u32x4* __restrict__ v, u32x4* __restrict__ pool_k,
-    u32x4* __restrict__ pool_v, int NB, int K, int C) {
-  const int i = blockIdx.x, bh = blockIdx.y;
-  if (i >= plan_count[bh]) return;
-  const int32_t* row = plan + ((size_t)bh * C + i) * 3;
-  const int slot = row[0], blk = row[1];
-  if (slot < 0 || slot >= K || blk < 0 || blk >= NB) return;
-  const size_t src = ((size_t)bh * NB + blk) * kChunksPerBlock;
-  const size_t dst = ((size_t)bh * K + slot) * kChunksPerBlock;
-  copy_block(k + src, v + src, pool_k + dst, pool_v + dst);
+    u32x4* __restrict__ pool_v, int NB, int K, int C, int rows) {
+  const int t = threadIdx.x;
+  for (int r0 = blockIdx.x * kCopyRows; r0 < rows; r0 += gridDim.x * kCopyRows) {
+    size_t src[kCopyRows], dst[kCopyRows];
+    bool ok[kCopyRows];
+#pragma unroll
+    for (int u = 0; u < kCopyRows; ++u) {
+      const int r = r0 + u;
+      ok[u] = false;
+      src[u] = dst[u] = 0;
+      if (r < rows) {
+        const int bh = r / C, i = r % C;
+        if (i < plan_count[bh]) {
+          const int32_t* row = plan + (size_t)r * 3;
+          const int slot = row[0], blk = row[1];
+          ok[u] = slot >= 0 && slot < K && blk >= 0 && blk < NB;
+          src[u] = ((size_t)bh * NB + (ok[u] ? blk : 0)) * kChunksPerBlock;
+          dst[u] = ((size_t)bh * K + (ok[u] ? slot : 0)) * kChunksPerBlock;
+        }
+      }
+    }
+    u32x4 a[kCopyRows], b[kCopyRows];
+#pragma unroll
+    for (int u = 0; u < kCopyRows; ++u) {
+      if (ok[u]) {
+        a[u] = k[src[u] + t];
+        b[u] = v[src[u] + t];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyRows; ++u) {
+      if (ok[u]) {
+        pool_k[dst[u] + t] = a[u];
+        pool_v[dst[u] + t] = b[u];
+      }
+    }
+  }
 }
 
 // Workgroup bh, one wave: lane l owns head dims 2l and 2l + 1 (one packed bf16 pair).
@@ -132,9 +165,13 @@ hipError_t launch_execute_plan(const Dims& d, const int32_t* plan, const int32_t
                                const void* k, const void* v, void* pool_k, void* pool_v,
                                hipStream_t stream) {
   if (d.cap <= 0 || plan == nullptr) return hipSuccess;  // nothing can be admitted
-  execute_plan_kernel<<<dim3(d.cap, d.batch * d.heads), dim3(kChunksPerBlock), 0, stream>>>(
+  const int rows = d.batch * d.heads * d.cap;
+  const int per_round = kCopyRows;
+  int grid = (rows + per_round - 1) / per_round;
+  if (grid > kCopyGrid) grid = kCopyGrid;
+  execute_plan_kernel<<<dim3(grid), dim3(kChunksPerBlock), 0, stream>>>(
       plan, plan_count, (const u32x4*)k, (const u32x4*)v, (u32x4*)pool_k, (u32x4*)pool_v,
-      d.max_blocks, d.top_k, d.cap);
+      d.max_blocks, d.top_k, d.cap, rows);
   return hipGetLastError();
 }
 

@@ -196,3 +196,58 @@ def test_decode_loop_over_the_working_set(lib, tier):
         inp["q"] = torch.randn(inp["q"].shape, generator=g).to(torch.bfloat16).to(DEV)
     if tier == "host":
         assert torch.equal(hk, kd.cpu()) and torch.equal(hv, vd.cpu())
+
+
+def test_layer_pipelined_copies_match_the_serial_steps(lib):
+    """Three layers, three decode steps, the full cache in pinned host memory: with
+    the plan's copies on a transfer stream (each layer's next step ordered after its
+    copies) every output and every pool equals the one-stream schedule's."""
+    w = synth.WORKLOADS["tiny_4k"].with_(batch=2, num_kv_heads=2, fetch_ratio=0.25, ctx=4096 + 40,
+                                         min_len=1000)
+    _say("layer-pipelined copies vs one stream")
+    d = lib.dims_for(w)
+    layers = []
+    for layer in range(3):
+        inp = {kk: t.to(DEV) for kk, t in synth.generate(w, "cpu", layer=layer).items()}
+        summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
+        n_cand = [ref.first_window_block(int(x), w.window) for x in inp["seq_lens"].cpu()]
+        R = torch.stack([torch.stack([synth.random_resident(w.top_k, n_cand[b], 2, 3 * b + h + layer)
+                                      for h in range(w.num_kv_heads)])
+                         for b in range(w.batch)]).to(DEV)
+        layers.append((inp, summ, R, inp["k"].cpu().pin_memory(), inp["v"].cpu().pin_memory()))
+
+    def run(pipelined):
+        fg = torch.cuda.Stream()
+        tr = torch.cuda.Stream() if pipelined else None
+        steps, done, outs = [], [], []
+        with torch.cuda.stream(fg):
+            for (inp, summ, R, hk, hv) in layers:
+                ws = lib.fill_working_set(d, R, inp["seq_lens"], hk, hv)
+                bufs = lib.StepBuffers(d, DEV)
+                rn = torch.empty_like(R)
+                steps.append((lib.PreparedPoolStep(d, inp["q"], summ, hk, hv, ws, inp["seq_lens"], R,
+                                                   bufs, rn), ws, bufs, rn))
+                done.append(torch.cuda.Event())
+        for t in range(3):
+            for li, (st, ws, bufs, rn) in enumerate(steps):
+                if pipelined:
+                    if t > 0:
+                        fg.wait_event(done[li])
+                    st(stream=fg, transfer_stream=tr)
+                    done[li].record(tr)
+                else:
+                    st(stream=fg)
+                with torch.cuda.stream(fg):
+                    outs.append({k: v.clone() for k, v in bufs.as_dict().items()})
+        fg.wait_stream(tr) if pipelined else None
+        torch.cuda.synchronize()
+        pools = [(ws.pool_k.clone(), ws.pool_v.clone()) for (_, ws, _, _) in steps]
+        return outs, pools
+
+    serial_outs, serial_pools = run(False)
+    pipe_outs, pipe_pools = run(True)
+    for i, (a, b) in enumerate(zip(serial_outs, pipe_outs)):
+        for key in a:
+            assert torch.equal(a[key], b[key]), f"step {i // 3} layer {i % 3}: {key}"
+    for (ak, av), (bk, bv) in zip(serial_pools, pipe_pools):
+        assert torch.equal(ak, bk) and torch.equal(av, bv)
