@@ -70,12 +70,13 @@ __global__ __launch_bounds__(kChunksPerBlock) void fill_working_set_kernel(
   copy_block(k + src, v + src, dk + dst, dv + dst);
 }
 
-// A few workgroups walk all plan rows (row r = bh * C + i), kCopyRows rows per round
-// with every load of the round in flight before the first store: enough bytes in
-// flight to fill the host link or HBM, while holding few CU slots, so that the
-// copies can run beside another stream's kernels.
+// At most kCopyGrid workgroups walk all plan rows (row r = bh * C + i), kCopyRows
+// rows per round with every load of the round in flight before the first store: a
+// plan of up to 1024 rows (6 per head at 8 x 8 heads is 384) goes out in one round
+// from HBM, larger plans fill the host link in several, and the copies hold at most
+// one workgroup's slots per CU, so that they can run beside another stream's kernels.
 constexpr int kCopyRows = 4;
-constexpr int kCopyGrid = 64;
+constexpr int kCopyGrid = 256;
 __global__ __launch_bounds__(kChunksPerBlock) void execute_plan_kernel(
     const int32_t* __restrict__ plan, const int32_t* __restrict__ plan_count,
     const u32x4* __restrict__ k, const u32x4* __restrict__ v, u32x4* __restrict__ pool_k,
@@ -166,8 +167,7 @@ hipError_t launch_execute_plan(const Dims& d, const int32_t* plan, const int32_t
                                hipStream_t stream) {
   if (d.cap <= 0 || plan == nullptr) return hipSuccess;  // nothing can be admitted
   const int rows = d.batch * d.heads * d.cap;
-  const int per_round = kCopyRows;
-  int grid = (rows + per_round - 1) / per_round;
+  int grid = (rows + kCopyRows - 1) / kCopyRows;
   if (grid > kCopyGrid) grid = kCopyGrid;
   execute_plan_kernel<<<dim3(grid), dim3(kChunksPerBlock), 0, stream>>>(
       plan, plan_count, (const u32x4*)k, (const u32x4*)v, (u32x4*)pool_k, (u32x4*)pool_v,
