@@ -311,6 +311,56 @@ def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, table: np.ndar
 
 
 # ---------------------------------------------------------------------------
+# Prediction quality: which blocks the true next query attends to
+# ---------------------------------------------------------------------------
+
+def block_attention_mass(q_true: np.ndarray, k: np.ndarray, seq_lens: np.ndarray, window: int,
+                         scale: float, block: int = 16) -> np.ndarray:
+    """Share of each candidate block in the true query's attention, per KV head.
+
+    For query head g of (b, h), the softmax of scale * q_true[b,h,g] . k_t over
+    every valid token t (candidates and window), summed over the tokens of block
+    j; the head-wise figure is the largest share over the group, as the
+    selection aggregates over the group.  Candidate blocks only (the window is
+    always resident); -inf elsewhere.  This is the set the look-ahead predicts:
+    [xllm] section four, Figure 4 (top-20 block prediction accuracy of the draft
+    query against a previous-token proxy) and Figure 6 (agreement of the draft
+    query's top-K set with the true next-token query's).  Reading: "the blocks
+    the true next query needs" is the top of this share.
+
+    q_true: [B, H, G, d]; k: [B, H, NB, block, d].  Returns [B, H, NB].
+    """
+    B, H, NB, bs, d = k.shape
+    G = q_true.shape[2]
+    out = np.full((B, H, NB), NEG_INF)
+    for b in range(B):
+        L = int(seq_lens[b])
+        n_cand = first_window_block(L, window, block)
+        if L <= 0:
+            continue
+        flat = k[b].reshape(H, NB * bs, d)[:, :L]            # [H, L, d]
+        for h in range(H):
+            best = np.full(n_cand, NEG_INF)
+            for g in range(G):
+                z = flat[h] @ q_true[b, h, g] * scale        # [L]
+                p = np.exp(z - z.max())
+                p /= p.sum()
+                per_block = np.add.reduceat(p, np.arange(0, L, bs))[:n_cand]
+                best = np.maximum(best, per_block)
+            out[b, h, :n_cand] = best
+    return out
+
+
+def top_overlap(pred: np.ndarray, true: np.ndarray, n: int) -> float:
+    """|first n of pred & first n of true| / n for two rankings (block ids, best
+    first, -1 padded); 1.0 when both are empty."""
+    a = {int(x) for x in pred[:n] if x >= 0}
+    b = {int(x) for x in true[:n] if x >= 0}
+    m = max(len(a), len(b))
+    return 1.0 if m == 0 else len(a & b) / m
+
+
+# ---------------------------------------------------------------------------
 # Executing the plan: the working set in HBM
 # ---------------------------------------------------------------------------
 #

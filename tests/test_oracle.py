@@ -637,3 +637,57 @@ def test_append_token_matches_a_rebuild():
                 n = min(16, L - 16 * j)
                 np.testing.assert_array_equal(rk[b, :, j % 3, :n], ek[b, :, j % 3, :n])
                 np.testing.assert_array_equal(rv[b, :, j % 3, :n], ev[b, :, j % 3, :n])
+
+
+# ---------------------------------------------------------------------------
+# Prediction quality: attention share per block, ranking overlap
+# ---------------------------------------------------------------------------
+
+def test_block_mass_through_per_block_log_sum_exp():
+    """A block's share is exp(lse over the block alone - lse over every token), the
+    log-sum-exps coming from the (separately pinned) attention oracle; the group
+    takes the largest share."""
+    q, k, v, lens = _tiny_inputs(seed=51, NB=10, lens=(150, 77))
+    W, scale = 32, 1 / math.sqrt(8)
+    qt = q[:, :, :, 0, :]
+    mass = ref.block_attention_mass(qt, k, lens, W, scale)
+    B, H, G = qt.shape[:3]
+    for b, h in itertools.product(range(B), range(H)):
+        L = int(lens[b])
+        nb, nc = ref.num_blocks(L), ref.first_window_block(L, W)
+        sub = (q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1])
+        all_t = np.arange(nb)[None, None]
+        _, lse_all = ref.sparse_attention(*sub, all_t, np.array([[nb]]), lens[b:b + 1], scale)
+        for j in range(10):
+            if j >= nc:
+                assert mass[b, h, j] == -np.inf
+                continue
+            _, lse_j = ref.sparse_attention(*sub, np.array([[[j]]]), np.array([[1]]), lens[b:b + 1], scale)
+            expect = np.exp(lse_j[0, 0] - lse_all[0, 0]).max()
+            np.testing.assert_allclose(mass[b, h, j], expect, rtol=1e-12)
+
+
+def test_block_mass_closed_forms():
+    """Identical keys: every token weighs 1/L, so a full block holds 16/L; shares of
+    the candidates plus the window's add up to 1 for a single query head."""
+    B, H, NB, d = 1, 1, 8, 4
+    k = np.ones((B, H, NB, 16, d))
+    q = np.array([[[[0.3, -1.0, 2.0, 0.5]]]])
+    m = ref.block_attention_mass(q, k, np.array([100]), 20, 0.5)
+    nc = ref.first_window_block(100, 20)                      # 5 candidate blocks
+    np.testing.assert_allclose(m[0, 0, :nc], 16 / 100, rtol=1e-13)
+    assert np.all(m[0, 0, nc:] == -np.inf)
+    q2, k2, _, lens = _tiny_inputs(seed=52, B=1, H=1, G=1, NB=9, lens=(137,))
+    m2 = ref.block_attention_mass(q2[:, :, :, 0, :], k2, lens, 0, 0.7)
+    z = k2[0, 0].reshape(-1, 8)[:137] @ q2[0, 0, 0, 0] * 0.7
+    p = np.exp(z - z.max()) / np.exp(z - z.max()).sum()
+    window_share = p[ref.first_window_block(137, 0) * 16:].sum()
+    np.testing.assert_allclose(m2[0, 0, :8].sum() + window_share, 1.0, rtol=1e-12)
+
+
+def test_top_overlap_by_hand():
+    assert ref.top_overlap(np.array([3, 1, 2, 9]), np.array([1, 3, 5, 9]), 2) == 1.0
+    assert ref.top_overlap(np.array([3, 1, 2, 9]), np.array([1, 5, 3, 9]), 2) == 0.5
+    assert ref.top_overlap(np.array([3, 1, 2, 9]), np.array([7, 5, 3, 9]), 4) == 0.5
+    assert ref.top_overlap(np.array([4, -1, -1]), np.array([4, -1, -1]), 3) == 1.0
+    assert ref.top_overlap(np.array([-1, -1]), np.array([-1, -1]), 2) == 1.0

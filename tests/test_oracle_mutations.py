@@ -52,6 +52,12 @@ MUTATIONS = {
     "pool_attention_keeps_window_slots": ("if 0 <= int(resident[b, h, s]) < w0:",
                                           "if 0 <= int(resident[b, h, s]):"),
     "pool_attention_reads_whole_last_block": ("n = min(block, L - j * block)", "n = block"),
+    "mass_omits_scale": ("z = flat[h] @ q_true[b, h, g] * scale", "z = flat[h] @ q_true[b, h, g]"),
+    "mass_normalised_over_candidates_only": ("p /= p.sum()", "p /= p[: n_cand * bs].sum()"),
+    "mass_sums_over_the_group": ("best = np.maximum(best, per_block)",
+                                 "best = np.where(np.isinf(best), per_block, best + per_block)"),
+    "overlap_divides_by_union": ("return 1.0 if m == 0 else len(a & b) / m",
+                                 "return 1.0 if m == 0 else len(a & b) / len(a | b)"),
 }
 
 PIN_TESTS = [getattr(pins, n) for n in dir(pins)
