@@ -507,6 +507,116 @@ def run_sweep(args) -> dict:
             "note": "block sizes other than 16 are not built (the kernels fix 16-token blocks)"}
 
 
+def block_mass_gpu(q_true, k, seq_lens, window: int, scale: float, torch):
+    """Analysis, not the decode path: each candidate block's share of the true
+    query's softmax over all valid tokens, largest over the group ([B, H, NB] fp32,
+    -inf outside the candidates); the definition of the oracle's block_attention_mass,
+    in fp32 torch on the device."""
+    B, H, NB = k.shape[:3]
+    T = NB * 16
+    lens = seq_lens.to(torch.int64)
+    tok = torch.arange(T, device=k.device)
+    blk = torch.arange(NB, device=k.device)
+    out = torch.empty((B, H, NB), dtype=torch.float32, device=k.device)
+    for b in range(B):
+        kf = k[b].reshape(H, T, 128).float()                                # [H, T, d]
+        qt = q_true[b].float().transpose(-1, -2).contiguous()               # [H, d, G]
+        z = torch.matmul(kf, qt).transpose(-1, -2) * scale                  # [H, G, T]
+        z = z.masked_fill(tok >= lens[b], float("-inf"))
+        p = torch.softmax(z, dim=-1)
+        share = p.reshape(H, -1, NB, 16).sum(-1).amax(1)                    # [H, NB]
+        n_cand = max(0, (int(lens[b]) - window) // 16)
+        out[b] = share.masked_fill(blk >= n_cand, float("-inf"))
+    return out
+
+
+QUALITY_NOISE = (0.1, 0.3, 0.6, 1.0)
+
+
+def prediction_quality(args) -> dict:
+    """Synthetic analogue of the pages' Figures 4 and 6: how well the look-ahead
+    selection finds the blocks the true next query attends to most.  The true next
+    query is the workload's target row; a predictor is a set of query rows scored
+    and selected by the library (min/max summaries, max over rows and the group,
+    top-K): four drafts bf16(q + s*N(0,1)) ("lookahead"), one such row ("proxy",
+    standing in for the previous token's query), both together (the rows the step
+    scores), and the true query itself (s = 0: what the summary bound alone loses).
+    Reported per noise level s: top-20 accuracy against the 20 largest attention
+    shares, top-K agreement with the K largest, and top-K agreement with the set the
+    true query itself selects (the same selection fed the true query), averaged over
+    heads and layers (the input sets)."""
+    import torch
+
+    import oasis_score_summaries_amd as oa
+    import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    scale = 1.0 / math.sqrt(128)
+    K, D = w.top_k, 4
+    gen = torch.Generator(device=dev).manual_seed(20260)
+    acc = {}
+
+    def predict(rows, inp, summ):
+        Q = rows.shape[3]
+        dq = oa.make_dims(w.batch, w.num_kv_heads, w.group, w.max_blocks, Q, K, w.window, w.fetch_ratio)
+        sc = oa.score_summaries(dq, rows.contiguous(), summ, inp["seq_lens"])
+        return oa.topk_blocks(dq, sc, inp["seq_lens"])
+
+    layers = min(args.sets, w.layers if w.layers > 1 else args.sets)
+    for layer in range(layers):
+        inp = synth.generate(w, dev, layer=layer)
+        d = oa.dims_for(w)
+        summ = oa.build_summaries(d, inp["k"], inp["seq_lens"])
+        q_true = inp["q"][:, :, :, 0, :]                                    # [B, H, G, d]
+        mass = block_mass_gpu(q_true, inp["k"], inp["seq_lens"], w.window, scale, torch)
+        true_rank = torch.topk(mass, K, dim=-1).indices.to(torch.int32)
+        valid = torch.isfinite(torch.gather(mass, -1, true_rank.long()))
+        true_rank = torch.where(valid, true_rank, torch.full_like(true_rank, -1)).cpu().numpy()
+
+        def noisy(n, s):
+            x = q_true.float().unsqueeze(3).expand(-1, -1, -1, n, -1)
+            return (x + s * torch.randn(x.shape, generator=gen, device=dev)).to(torch.bfloat16)
+
+        preds = {"exact": predict(q_true.unsqueeze(3), inp, summ)}
+        for s in QUALITY_NOISE:
+            drafts, proxy = noisy(D, s), noisy(1, s)
+            preds[f"lookahead@{s}"] = predict(drafts, inp, summ)
+            preds[f"proxy@{s}"] = predict(proxy, inp, summ)
+            preds[f"proxy+lookahead@{s}"] = predict(torch.cat([proxy, drafts], dim=3), inp, summ)
+        exact_sel = preds["exact"].cpu().numpy()
+        for name, sel in preds.items():
+            sel = sel.cpu().numpy()
+            heads = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+            t20 = [top_overlap_rows(sel[b, h], true_rank[b, h], 20) for b, h in heads]
+            tk = [top_overlap_rows(sel[b, h], true_rank[b, h], K) for b, h in heads]
+            ts = [top_overlap_rows(sel[b, h], exact_sel[b, h], K) for b, h in heads]
+            a = acc.setdefault(name, {"top20": [], "topk": [], "sel": []})
+            a["top20"].append(statistics.mean(t20))
+            a["topk"].append(statistics.mean(tk))
+            a["sel"].append(statistics.mean(ts))
+        del inp, summ, mass
+        torch.cuda.empty_cache()
+    rows = {name: {"top20_accuracy": round(statistics.mean(v["top20"]), 4),
+                   "top20_min_layer": round(min(v["top20"]), 4),
+                   "topk_agreement": round(statistics.mean(v["topk"]), 4),
+                   "topk_min_layer": round(min(v["topk"]), 4),
+                   "agreement_with_true_query_selection": round(statistics.mean(v["sel"]), 4),
+                   "selection_min_layer": round(min(v["sel"]), 4)} for name, v in acc.items()}
+    return {"metric": "look-ahead prediction quality (synthetic analogue)", "workload": w.name,
+            "layers": layers, "top_k": K, "drafts": D, "noise_levels": list(QUALITY_NOISE),
+            "predictors": rows, "data": "synthetic"}
+
+
+def top_overlap_rows(pred, true, n: int) -> float:
+    """|first n of pred & first n of true| / (the larger of the two counts); rankings
+    are block ids, best first, -1 padded."""
+    a = {int(x) for x in pred[:n] if x >= 0}
+    b = {int(x) for x in true[:n] if x >= 0}
+    m = max(len(a), len(b))
+    return 1.0 if m == 0 else len(a & b) / m
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -528,6 +638,8 @@ def main(argv=None) -> int:
                     help="write the traffic file from two rocprofv3 --pmc runs of "
                          "'bench.py --calibrate' (FETCH_SIZE, then WRITE_SIZE) and exit")
     ap.add_argument("--counter-command", default="", help="the command recorded in the traffic file")
+    ap.add_argument("--quality", action="store_true",
+                    help="print one JSON line with the prediction-quality analogue instead of the benchmark")
     ap.add_argument("--sweep", action="store_true",
                     help="print one JSON line with the K and fetch-ratio sweep instead of the benchmark")
     ap.add_argument("--no-plan-exec", action="store_true",
@@ -557,6 +669,9 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     if args.sweep:
         print(json.dumps(run_sweep(args)), flush=True)
+        return 0
+    if args.quality:
+        print(json.dumps(prediction_quality(args)), flush=True)
         return 0
     w = synth.WORKLOADS[args.workload]
     d = oa.dims_for(w)

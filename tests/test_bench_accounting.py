@@ -63,3 +63,17 @@ def test_cpu_baseline_both_modes_on_the_tiny_workload():
     assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
     assert out["pool"]["value"] > 0 and 1 <= out["pool"]["cores"] <= 16
     assert np.isfinite(out["pool"]["value"])
+
+
+def test_analysis_overlap_matches_the_oracle_definition():
+    import numpy as np
+
+    from oracle import ref
+    r = np.random.default_rng(3)
+    for _ in range(200):
+        n = int(r.integers(1, 12))
+        a = r.permutation(30)[: int(r.integers(0, 12))]
+        b = r.permutation(30)[: int(r.integers(0, 12))]
+        a = np.concatenate([a, -np.ones(3, dtype=int)])
+        b = np.concatenate([b, -np.ones(3, dtype=int)])
+        assert bench.top_overlap_rows(a, b, n) == ref.top_overlap(a, b, n)

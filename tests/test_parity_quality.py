@@ -1,0 +1,60 @@
+"""GPU check of the prediction-quality analysis: the attention shares the analysis
+computes on the device equal the oracle's, and the analysis runs end to end.
+
+The analysis is measurement code, not the decode path; its predictions come from
+the library's scoring and selection, which test_parity.py holds to the oracle.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+from oracle import ref
+from tests._helpers import f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(msg):
+    print(f"[quality] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("B,H,G,NB,W,lens", [(2, 2, 4, 40, 64, [600, 123]), (1, 3, 1, 20, 0, [320])])
+def test_block_mass_matches_oracle(B, H, G, NB, W, lens):
+    _say(f"block mass B={B} H={H} G={G} NB={NB} W={W}")
+    g = torch.Generator().manual_seed(9 + G)
+    q = torch.randn((B, H, G, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((B, H, NB, 16, 128), generator=g).to(torch.bfloat16)
+    L = torch.tensor(lens, dtype=torch.int32)
+    scale = 1 / math.sqrt(128)
+    got = bench.block_mass_gpu(q.to(DEV), k.to(DEV), L.to(DEV), W, scale, torch)
+    torch.cuda.synchronize()
+    exp = ref.block_attention_mass(f64(q), f64(k), L.numpy(), W, scale)
+    got = f64(got)
+    assert np.array_equal(np.isneginf(got), np.isneginf(exp))
+    fin = np.isfinite(exp)
+    np.testing.assert_allclose(got[fin], exp[fin], rtol=2e-4, atol=1e-9)
+
+
+def test_prediction_quality_runs():
+    """Two layers of the small workload: every figure is a fraction, and the true
+    query's own top-K agrees best with itself among the predictors."""
+    _say("prediction quality, small workload")
+
+    class A:
+        workload, sets = "tiny_4k", 2
+
+    r = bench.prediction_quality(A())
+    assert r["layers"] == 2 and r["top_k"] == 16
+    for name, row in r["predictors"].items():
+        for key in ("top20_accuracy", "topk_agreement", "top20_min_layer", "topk_min_layer",
+                    "agreement_with_true_query_selection"):
+            assert 0.0 <= row[key] <= 1.0, (name, key)
+    assert r["predictors"]["exact"]["agreement_with_true_query_selection"] == 1.0
+    assert r["predictors"]["exact"]["topk_agreement"] >= r["predictors"]["proxy@1.0"]["topk_agreement"]
