@@ -43,7 +43,7 @@ __global__ __launch_bounds__(THREADS) void topk_kernel(const float* __restrict__
   const int bh = blockIdx.x;
   const int len = clamp_len(seq_lens[bh / heads], NB);
   const int n_cand = first_window_block(len, window);
-  const int m = topk_select<THREADS, ITEMS>(scores + (size_t)bh * NB, n_cand, K, sh);
+  const int m = topk_select<THREADS, ITEMS>(scores + (size_t)bh * NB, n_cand, K, sh, NB);
   for (int t = threadIdx.x; t < K; t += THREADS) topk[(size_t)bh * K + t] = t < m ? sh.sorted_idx[t] : -1;
 }
 

@@ -120,24 +120,42 @@ __device__ inline int count_cmp(const uint64_t* v, int n, uint64_t x) {
 // With `bm` (cleared before the call), the selected blocks are marked in bm->sel and
 // this thread's resident block `res_block` (if in [0, NB)) in bm->res, both complete
 // when the call returns a count above zero.
+// Scores per workgroup that fit the bucket array, where they can wait for lookups.
+template <int THREADS, int ITEMS>
+constexpr bool kCanStage = ITEMS * THREADS * sizeof(float) <= sizeof(SelectShared<THREADS, ITEMS>::bucket);
+
+// row holds NB readable scores; every thread's scores are requested before anything
+// waits (the length, and with it n_cand, arrives meanwhile).  With `res_score` (only
+// when kCanStage), the scores also pass through LDS and *res_score receives the score
+// of `res_block` (-inf outside the candidates), so that no second global read
+// depends on the first.
 template <int THREADS, int ITEMS>
 __device__ __attribute__((always_inline)) int topk_select(const float* __restrict__ row, int n_cand, int K,
-                           SelectShared<THREADS, ITEMS>& sh, PlanBitmaps* bm = nullptr,
-                           int res_block = -1, int NB = 0) {
+                           SelectShared<THREADS, ITEMS>& sh, int NB, PlanBitmaps* bm = nullptr,
+                           int res_block = -1, float* res_score = nullptr) {
   constexpr int NW = THREADS / 64;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  float x[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    const int e = i * THREADS + tid;
+    x[i] = row[e < NB ? e : NB - 1];
+  }
+  if (res_score != nullptr) *res_score = -INFINITY;
   const int m = n_cand < K ? n_cand : K;
   if (m <= 0) return 0;  // uniform across the workgroup
 
   uint32_t key[ITEMS];
   uint32_t lmax = 0u, lmin = 0xffffffffu;
+  float* staged = reinterpret_cast<float*>(sh.bucket);
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int e = i * THREADS + tid;
-    key[i] = (e < n_cand) ? order_key(row[e]) : 0u;
+    key[i] = (e < n_cand) ? order_key(x[i]) : 0u;
     if (e < n_cand) {
       lmax = max(lmax, key[i]);
       lmin = min(lmin, key[i]);
+      if (kCanStage<THREADS, ITEMS> && res_score != nullptr) staged[e] = x[i];
     }
   }
   lmax = wave_max_u32(lmax);
@@ -149,6 +167,9 @@ __device__ __attribute__((always_inline)) int topk_select(const float* __restric
   __syncthreads();
   if (bm != nullptr && res_block >= 0 && res_block < NB)   // after the clear, before the last barrier
     atomicOr(&bm->res[res_block >> 5], 1u << (res_block & 31));
+  // The staged scores are overwritten only after the first radix pass's barriers.
+  if (kCanStage<THREADS, ITEMS> && res_score != nullptr && res_block >= 0 && res_block < n_cand)
+    *res_score = staged[res_block];
   uint32_t kmax = 0u, kmin = 0xffffffffu;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -458,9 +479,16 @@ __device__ __attribute__((always_inline)) void topk_plan_wg(int bh, TopkPlanShar
   const int len = clamp_len(a.seq_lens[bh / a.heads], NB);
   const int n_cand = first_window_block(len, a.window);
   const float* srow = a.scores + (size_t)bh * NB;
-  const ResidentSlot rs = load_resident_slot(a.resident + (size_t)bh * K, srow, K, NB);
+  ResidentSlot rs;
+  if (kCanStage<THREADS, ITEMS>) {  // the score comes from the selection's staging
+    rs.block = (int)threadIdx.x < K ? a.resident[(size_t)bh * K + threadIdx.x] : -1;
+    rs.score = -INFINITY;
+  } else {
+    rs = load_resident_slot(a.resident + (size_t)bh * K, srow, K, NB);
+  }
   clear_bitmaps(bm, NB);
-  const int m = topk_select<THREADS, ITEMS>(srow, n_cand, K, sh.t, &bm, rs.block, NB);
+  const int m = topk_select<THREADS, ITEMS>(srow, n_cand, K, sh.t, NB, &bm, rs.block,
+                                            kCanStage<THREADS, ITEMS> ? &rs.score : nullptr);
   if (m == 0) {  // the selection returned at once: mark the resident set here
     __syncthreads();
     if (rs.block >= 0 && rs.block < NB) atomicOr(&bm.res[rs.block >> 5], 1u << (rs.block & 31));
