@@ -825,7 +825,7 @@ def main(argv=None) -> int:
     dom_gbps = dom_bytes / (stage_us[dominant] * 1e-6) / 1e9
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == "qwen3_8b_32k" else METRIC.replace("Qwen3-8B 32K", w.name),
         "value": round(1e3 / ms_per_step, 2),   # one step = one layer
         "unit": "steps/s",
         "n_gpus": 1,
