@@ -814,9 +814,9 @@ def main(argv=None) -> int:
     step_gbps = nb["step"] / (ms_per_step * 1e-3) / 1e9
     if args.order == "overlapped":
         # The first launch: the scoring with the attention gathering (summaries,
-        # scores, K/V blocks); two kernels back to back above 32 query rows per head.
+        # scores, K/V blocks); two kernels back to back above 96 query rows per head.
         dominant = "score_attn_split"
-        kernel = "score_attn_kernel" if w.group * w.queries <= 32 else "score_kernel+attn_split_kernel"
+        kernel = "score_attn_kernel" if w.group * w.queries <= 96 else "score_kernel+attn_split_kernel"
         dom_bytes = nb["score_attn_split"]
     else:
         dominant = max(("score", "attn_split"), key=lambda k: stage_us[k])

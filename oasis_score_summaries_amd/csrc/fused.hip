@@ -13,10 +13,8 @@
 //   launch 2: the selection-and-plan workgroups and the attention merge
 //             workgroups (both latency bound).
 // One grid per phase needs no second stream and no cross-stream event, and the
-// ramp-up and tail of each phase are paid once instead of twice.  (With more than
-// 32 query rows per KV head the scoring workgroup needs more registers than the
-// attention's four waves per SIMD allow; launch 1 is then the two kernels back to
-// back.)  A workgroup's
+// ramp-up and tail of each phase are paid once instead of twice (up to 96 query
+// rows per KV head; see OASIS_FUSED_MAX_RT).  A workgroup's
 // role follows from its index; the scoring and selection workgroups, which run
 // longest, come first so that they start first.
 #include "attention_impl.h"
@@ -26,6 +24,16 @@
 namespace oasis {
 
 static_assert(kScoreWaves == kAttnWaves, "one workgroup size for both roles");
+// Row tiles up to which the scoring shares launch 1 with the attention gather.  From
+// three row tiles on the scoring reads its query fragments step by step, so it fits
+// four waves per SIMD at any row count, but its LDS grows by 8 KB per row tile and
+// the whole grid gets the larger of the two roles' LDS: beyond six row tiles (96
+// query rows) the attention would drop to two workgroups per CU, and the two
+// kernels run back to back instead.  (Measured at 80 rows: 76.5 us per step fused
+// against 81.2 us back to back.)
+#ifndef OASIS_FUSED_MAX_RT
+#define OASIS_FUSED_MAX_RT 6
+#endif
 
 template <int RT, int GP, bool POOL = false>
 __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void score_attn_kernel(ScoreArgs sa, AttnArgs aa,
@@ -82,10 +90,9 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
   const int grid1 = n_score + attn_gx * heads;
   const int rt = (d.group * d.queries + 15) / 16;
   const int gp = d.group <= 4 ? 4 : (d.group <= 8 ? 8 : 16);
-  // Up to two row tiles the scoring work fits the attention's register budget (four
-  // waves per SIMD); with more query rows the two kinds of workgroup keep their own
-  // kernels, back to back.
-  switch (rt <= 2 ? rt * 100 + gp : 0) {
+  // Up to OASIS_FUSED_MAX_RT row tiles the scoring work shares the grid with the
+  // attention's gathering; otherwise the two kernels run back to back.
+  switch (rt <= OASIS_FUSED_MAX_RT ? rt * 100 + gp : 0) {
 #define OASIS_SA_CASE(RT, GP)                                                                  \
   case RT * 100 + GP:                                                                          \
     if (pool)                                                                                  \
@@ -101,6 +108,20 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
     OASIS_SA_CASE(2, 4)
     OASIS_SA_CASE(2, 8)
     OASIS_SA_CASE(2, 16)
+#if OASIS_FUSED_MAX_RT >= 6
+    OASIS_SA_CASE(3, 4)
+    OASIS_SA_CASE(3, 8)
+    OASIS_SA_CASE(3, 16)
+    OASIS_SA_CASE(4, 4)
+    OASIS_SA_CASE(4, 8)
+    OASIS_SA_CASE(4, 16)
+    OASIS_SA_CASE(5, 4)
+    OASIS_SA_CASE(5, 8)
+    OASIS_SA_CASE(5, 16)
+    OASIS_SA_CASE(6, 4)
+    OASIS_SA_CASE(6, 8)
+    OASIS_SA_CASE(6, 16)
+#endif
 #undef OASIS_SA_CASE
     default: {
       hipError_t e = launch_score(d, q, summ, seq_lens, scores, stream);

@@ -109,6 +109,9 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
         acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(afrag[r][s][lane]),
                                                          as_bf16x8(bv[t][s]), acc[r], 0, 0, 0);
       }
+      // With three or more row tiles, holding every step's query fragments at once
+      // would cost more registers than the occupancy allows: read them step by step.
+      if (RT >= 3) __builtin_amdgcn_sched_barrier(0);
     }
     // Lane l holds rows 16r + 4*(l/16) + i of block column l%16: max over its real
     // rows, then across the four lane groups of the column.
