@@ -527,14 +527,15 @@ inline TopkPlanArgs topk_plan_args(const Dims& d, const float* scores, const int
 }
 
 // Workgroup size and scores per thread for a problem: 512 threads while K <= 512
-// and the scores fit 8 per thread (measured fastest for 2048 blocks, K = 128: fewer
-// serial loads and LDS atomics per thread than 256, fewer waves per barrier than
-// 1024), else 1024 (up to 32 per thread).
-#ifndef OASIS_SELECT_SMALL
-#define OASIS_SELECT_SMALL 512
-#endif
+// and the scores fit 8 per thread (measured fastest for 64 heads of 2048 blocks,
+// K = 128: fewer serial loads and LDS atomics per thread than 256, fewer waves per
+// barrier than 1024); with 128 heads or more, 256 threads while K <= 256 and 2048
+// blocks (the selection shares launch 2 with the merge, and smaller workgroups fit
+// more of both per CU: 12 against 20 us at 128 heads, 13.5 against 22.5 at 512);
+// else 1024 (up to 32 per thread).
 inline int select_threads(const Dims& d) {
-  return (d.top_k <= OASIS_SELECT_SMALL && d.max_blocks <= OASIS_SELECT_SMALL * 8) ? OASIS_SELECT_SMALL : 1024;
+  if ((int64_t)d.batch * d.heads >= 128 && d.top_k <= 256 && d.max_blocks <= 256 * 8) return 256;
+  return (d.top_k <= 512 && d.max_blocks <= 512 * 8) ? 512 : 1024;
 }
 inline int select_items(const Dims& d, int threads) {
   int items = 1;
@@ -542,22 +543,27 @@ inline int select_items(const Dims& d, int threads) {
   return items;
 }
 
-#define OASIS_SELECT_DISPATCH(CASE)                      \
-  do {                                                   \
-    const int threads_ = select_threads(d);              \
-    const int items_ = select_items(d, threads_);        \
-    if (threads_ == OASIS_SELECT_SMALL) {                \
-      switch (items_) {                                  \
-        CASE(OASIS_SELECT_SMALL, 1) CASE(OASIS_SELECT_SMALL, 2) \
-        CASE(OASIS_SELECT_SMALL, 4) CASE(OASIS_SELECT_SMALL, 8) \
-        default: return hipErrorInvalidValue;            \
-      }                                                  \
-    } else {                                             \
-      switch (items_) {                                  \
-        CASE(1024, 1) CASE(1024, 2) CASE(1024, 4) CASE(1024, 8) CASE(1024, 16) CASE(1024, 32) \
-        default: return hipErrorInvalidValue;            \
-      }                                                  \
-    }                                                    \
+#define OASIS_SELECT_DISPATCH(CASE)                                                  \
+  do {                                                                               \
+    const int threads_ = select_threads(d);                                          \
+    const int items_ = select_items(d, threads_);                                    \
+    if (threads_ == 256) {                                                           \
+      switch (items_) {                                                              \
+        CASE(256, 1) CASE(256, 2) CASE(256, 4) CASE(256, 8)                          \
+        default: return hipErrorInvalidValue;                                        \
+      }                                                                              \
+    } else if (threads_ == 512) {                                                    \
+      switch (items_) {                                                              \
+        CASE(512, 1) CASE(512, 2) CASE(512, 4) CASE(512, 8)                          \
+        default: return hipErrorInvalidValue;                                        \
+      }                                                                              \
+    } else {                                                                         \
+      switch (items_) {                                                              \
+        CASE(1024, 1) CASE(1024, 2) CASE(1024, 4) CASE(1024, 8) CASE(1024, 16)       \
+        CASE(1024, 32)                                                               \
+        default: return hipErrorInvalidValue;                                        \
+      }                                                                              \
+    }                                                                                \
   } while (0)
 
 

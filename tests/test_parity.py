@@ -305,6 +305,31 @@ def test_decode_step_integer_inputs(lib, ratio, W, lens):
             assert _compare_head(w, got, exp, b, h, resident[b, h].numpy(), robust=True)
 
 
+@pytest.mark.parametrize("NB,ratio", [(100, 0.25), (300, 0.05), (1000, 1.0)])
+def test_decode_step_many_heads(lib, NB, ratio):
+    """128 (sequence, KV head) pairs: the selection runs in 256-thread workgroups
+    (1, 2 and 4 scores per thread); integer inputs, so every decision must agree
+    with the oracle bit for bit."""
+    B, H, G, Q, K, W = 32, 4, 2, 3, 24, 32
+    lens = [int(x) for x in np.random.default_rng(NB).integers(1, NB * 16 + 1, size=B)]
+    _say(f"decode_step many heads NB={NB} ratio={ratio}")
+    q, k, v, L = _small_inputs(23, B, H, G, Q, NB, lens, integer=True)
+    w = synth.Workload(name="many", batch=B, num_kv_heads=H, group=G, ctx=NB * 16, num_drafts=Q - 1,
+                       top_k=K, window=W, fetch_ratio=ratio, planted=0)
+    resident = torch.empty((B, H, K), dtype=torch.int32)
+    for b in range(B):
+        for h in range(H):
+            resident[b, h] = synth.random_resident(K, ref.first_window_block(lens[b], W), h, 7 * b + h)
+    inp_dev = {"q": q.to(DEV), "k": k.to(DEV), "v": v.to(DEV), "seq_lens": L.to(DEV)}
+    got, _ = _run_step(lib, w, inp_dev, resident)
+    for b in range(B):
+        for h in range(H):
+            exp = oracle_head(q, k, v, L, resident[b, h].numpy(), K, W, w.cap, default_scale(), b, h)
+            exp["q64"] = f64(q[b, h])
+            np.testing.assert_array_equal(f64(got["scores"][b, h]), exp["scores"])
+            assert _compare_head(w, got, exp, b, h, resident[b, h].numpy(), robust=True)
+
+
 def test_decode_step_deterministic(lib):
     w = synth.WORKLOADS["tiny_4k"].with_(batch=2, fetch_ratio=0.25)
     inp = {k: v.to(DEV) for k, v in synth.generate(w, "cpu").items()}
