@@ -527,15 +527,18 @@ inline TopkPlanArgs topk_plan_args(const Dims& d, const float* scores, const int
 }
 
 // Workgroup size and scores per thread for a problem: 512 threads while K <= 512
-// and the scores fit 8 per thread (measured fastest for 64 heads of 2048 blocks,
+// and the scores fit 16 per thread (measured fastest for 64 heads of 2048 blocks,
 // K = 128: fewer serial loads and LDS atomics per thread than 256, fewer waves per
-// barrier than 1024); with 128 heads or more, 256 threads while K <= 256 and 2048
+// barrier than 1024; and for 32 heads of 8192 blocks); with 128 heads or more, 256 threads while K <= 256 and 2048
 // blocks (the selection shares launch 2 with the merge, and smaller workgroups fit
 // more of both per CU: 12 against 20 us at 128 heads, 13.5 against 22.5 at 512);
 // else 1024 (up to 32 per thread).
+#ifndef OASIS_SELECT_MID_ITEMS
+#define OASIS_SELECT_MID_ITEMS 16  // 8192 blocks: 12.8 us with 512 threads, 13.5 with 1024
+#endif
 inline int select_threads(const Dims& d) {
   if ((int64_t)d.batch * d.heads >= 128 && d.top_k <= 256 && d.max_blocks <= 256 * 8) return 256;
-  return (d.top_k <= 512 && d.max_blocks <= 512 * 8) ? 512 : 1024;
+  return (d.top_k <= 512 && d.max_blocks <= 512 * OASIS_SELECT_MID_ITEMS) ? 512 : 1024;
 }
 inline int select_items(const Dims& d, int threads) {
   int items = 1;
@@ -554,7 +557,7 @@ inline int select_items(const Dims& d, int threads) {
       }                                                                              \
     } else if (threads_ == 512) {                                                    \
       switch (items_) {                                                              \
-        CASE(512, 1) CASE(512, 2) CASE(512, 4) CASE(512, 8)                          \
+        CASE(512, 1) CASE(512, 2) CASE(512, 4) CASE(512, 8) CASE(512, 16)            \
         default: return hipErrorInvalidValue;                                        \
       }                                                                              \
     } else {                                                                         \
