@@ -134,28 +134,32 @@ __device__ __attribute__((always_inline)) int topk_select(const float* __restric
                            SelectShared<THREADS, ITEMS>& sh, int NB, PlanBitmaps* bm = nullptr,
                            int res_block = -1, float* res_score = nullptr) {
   constexpr int NW = THREADS / 64;
+  constexpr bool kStage = kCanStage<THREADS, ITEMS>;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  float x[ITEMS];
+  uint32_t key[ITEMS];
+  float x[kStage ? ITEMS : 1];  // the raw scores are kept only where they are staged
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int e = i * THREADS + tid;
-    x[i] = row[e < NB ? e : NB - 1];
+    const float xv = row[e < NB ? e : NB - 1];
+    key[i] = order_key(xv);
+    if (kStage) x[i] = xv;
   }
   if (res_score != nullptr) *res_score = -INFINITY;
   const int m = n_cand < K ? n_cand : K;
   if (m <= 0) return 0;  // uniform across the workgroup
 
-  uint32_t key[ITEMS];
   uint32_t lmax = 0u, lmin = 0xffffffffu;
   float* staged = reinterpret_cast<float*>(sh.bucket);
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int e = i * THREADS + tid;
-    key[i] = (e < n_cand) ? order_key(x[i]) : 0u;
     if (e < n_cand) {
       lmax = max(lmax, key[i]);
       lmin = min(lmin, key[i]);
-      if (kCanStage<THREADS, ITEMS> && res_score != nullptr) staged[e] = x[i];
+      if (kStage && res_score != nullptr) staged[e] = x[kStage ? i : 0];
+    } else {
+      key[i] = 0u;
     }
   }
   lmax = wave_max_u32(lmax);

@@ -345,6 +345,44 @@ def test_plan_exhaustive_tiny():
             assert newR == candidates[0]
 
 
+def test_plan_exhaustive_k4_over_12_candidates():
+    """Every slot table of K = 4 slots over 12 candidates (empties included) and every
+    cap 0..4, on scores with ties: the plan equals the rule in words (the best n new
+    blocks of the selection, n = min(cap, new); empties first by slot, then stale slots
+    lowest score first, equal scores higher block first; slots ascending take blocks
+    ascending; everything else unchanged)."""
+    s = np.array([1.0, 3.0, 2.0, 3.0, 0.5, 2.0, 1.0, 4.0, 0.5, 2.0, 1.5, 1.0])
+    W, K = 48, 4
+    L = 16 * 12 + W
+    S = ref.topk_blocks(s[None, None], np.array([L]), K, W)[0, 0].tolist()
+    assert S == [7, 1, 3, 2]                     # 3.0 tie: block 1 before 3; 2.0 tie: 2 first
+    Sset = set(S)
+    n_cfg = 0
+    for R in itertools.product([-1] + list(range(12)), repeat=K):
+        filled = [x for x in R if x >= 0]
+        if len(filled) != len(set(filled)):
+            continue
+        n_cfg += 1
+        new_blocks = [x for x in S if x not in R]
+        empties = [i for i in range(K) if R[i] < 0]
+        stale = sorted([i for i in range(K) if R[i] >= 0 and R[i] not in Sset],
+                       key=lambda i: (s[R[i]], -R[i]))
+        for cap in range(0, 5):
+            p = ref.build_plan(s[None, None], np.array(S)[None, None], np.array(R)[None, None],
+                               np.array([L]), cap, W)
+            n = min(cap, len(new_blocks))
+            slots = sorted((empties + stale)[:n])
+            blocks = sorted(new_blocks[:n])
+            want = list(R)
+            for sl, bl in zip(slots, blocks):
+                want[sl] = bl
+            assert p["resident"][0, 0].tolist() == want, (R, cap)
+            assert int(p["plan_count"][0, 0]) == n
+            rows = [tuple(int(x) for x in p["plan"][0, 0, i]) for i in range(n)]
+            assert rows == [(sl, bl, R[sl]) for sl, bl in zip(slots, blocks)], (R, cap)
+    assert n_cfg == 1 + 4 * 12 + 6 * 132 + 4 * 1320 + 11880
+
+
 # ---------------------------------------------------------------------------
 # O4 attention
 # ---------------------------------------------------------------------------
