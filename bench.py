@@ -262,6 +262,40 @@ def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     return out
 
 
+def layer_pipelined(d, sets, ms_step: float, torch, oa, reps: int = 100) -> dict:
+    """The input sets as the layers of a decode step, each layer's selection and plan
+    riding in the next layer's first launch (oasis_decode_layer_pipelined): the
+    steady-state time per layer of a whole sweep (graph replay; the first layer of a
+    replay selects the previous replay's last layer).  Every layer still does its
+    whole step; only where its selection runs changes."""
+    sweep = oa.PipelinedLayers(d, [(s["q"], s["summ"], s["k"], s["v"], s["seq_lens"], s["resident"])
+                                   for s in sets])
+    for _ in range(3):
+        sweep()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sweep()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sweep()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+    sweep.drain()
+    torch.cuda.synchronize()
+    return {"us_per_layer": round(us, 3), "layers": len(sets), "layers_per_s": round(1e6 / us, 1),
+            "overlapped_step_us": round(ms_step * 1e3, 3)}
+
+
 def layer_pipeline(d, sets, wsets, hosts, torch, oa, steps: int = 20) -> dict:
     """The input sets as the layers of one decode step, the full cache in pinned host
     memory: every layer's step over its working set with the plan's copies on the
@@ -862,6 +896,7 @@ def main(argv=None) -> int:
         "setup_s": round(setup_s, 1),
         "checks": check,
     }
+    result["layer_pipelined"] = layer_pipelined(d, sets, ms_per_step, torch, oa)
     if not args.no_plan_exec:
         result["plan_execution"] = plan_execution(w, d, sets, buffers, res_next, ms_per_step, stage_us,
                                                   torch, oa)

@@ -388,6 +388,53 @@ oasis_status oasis_decode_step_pool_async(
     void* ws, size_t ws_bytes, hipStream_t stream, hipStream_t transfer_stream,
     hipEvent_t plan_ready);
 
+/* ---- Layer-pipelined decode ---------------------------------------------------
+ *
+ * The pages run each layer's background half (look-ahead scoring, selection, plan)
+ * beside the foreground of the layers after it (xllm-io review, section three:
+ * component table, asynchronous pipeline, parallel across layers and serial within
+ * a layer; Eq. (4)).  Here a layer's scoring goes with its own foreground
+ * attention (launch 1) and its selection and plan ride in the next layer's
+ * launch 1; its launch 2 is the attention merge alone, the output the next layer
+ * needs.  One layer's buffers: */
+typedef struct {
+  const void* q;            /* device, bf16 [B, H, G, Q, 128] (row 0 target) */
+  const void* summ;         /* device, bf16 [B, H, NB, 2, 128] */
+  const void* k;            /* device, bf16 [B, H, NB, 16, 128] */
+  const void* v;            /* device, bf16 [B, H, NB, 16, 128] */
+  const int32_t* seq_lens;  /* device, int32 [B] */
+  const int32_t* resident;  /* device, int32 [B, H, K]: the slot table attended now */
+  int32_t* resident_next;   /* device, int32 [B, H, K]: the next slot table (own buffer) */
+  float* scores;            /* device, fp32 [B, H, NB] */
+  int32_t* topk;            /* device, int32 [B, H, K] */
+  int32_t* plan;            /* device, int32 [B, H, C, 3] (NULL allowed when C = 0) */
+  int32_t* plan_count;      /* device, int32 [B, H] */
+  int32_t* table;           /* device, int32 [B, H, oasis_table_stride] */
+  int32_t* table_count;     /* device, int32 [B, H] */
+  float* out;               /* device, fp32 [B, H, G, 128] */
+  float* lse;               /* device, fp32 [B, H, G] or NULL */
+  void* ws;                 /* device workspace of oasis_workspace_bytes(dims) */
+  size_t ws_bytes;
+} oasis_layer_io;
+
+/* Queues, on `stream`: `layer`'s foreground (attention of its target queries over
+ * `resident` and the window into out, lse) and its look-ahead scoring (scores),
+ * and `previous`'s selection and plan (topk, plan, plan_count, table, table_count,
+ * resident_next from previous->scores, previous->seq_lens, previous->resident), as
+ * oasis_decode_step_overlapped computes them for each layer.  Call it for every
+ * layer in order with the layer before as `previous` (for the first layer, the
+ * last layer of the step before, or NULL), and once more with layer = NULL and
+ * previous = the last layer to finish the sweep.  Either argument may be NULL,
+ * not both.  The two must not share scores buffers (one is written while the
+ * other is read), and each resident_next must be its own buffer; a layer's
+ * selection outputs are valid after the next call returns its launches to the
+ * stream order.  Up to K = 256, 2048 blocks per head, 4 query heads and 32 query
+ * rows per KV head, the previous layer's selection shares this layer's first
+ * launch; otherwise it is a launch of its own before it. */
+oasis_status oasis_decode_layer_pipelined(const oasis_dims* dims, const oasis_layer_io* layer,
+                                          const oasis_layer_io* previous, float scale,
+                                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,7 +6,8 @@ attention over the head-wise block table.  The work runs in the HIP kernels of
 liboasis.so (C ABI in include/oasis.h); this package is its Python binding.
 Every call raises if the library has not been built.
 """
-from ._lib import (LIB_PATH, OasisDims, OasisError, PreparedPlanCopy,  # noqa: F401
+from ._lib import (LIB_PATH, LayerIO, OasisDims, OasisError, PipelinedLayers,  # noqa: F401
+                   PreparedPlanCopy,
                    PreparedPoolStep, PreparedStep, StageEvents,
                    StepBuffers, WorkingSet, append_token, build_plan, decode_step_pool,
                    execute_plan, fill_working_set, sparse_decode_attn_pool, window_ring_slots,

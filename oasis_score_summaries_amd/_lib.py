@@ -89,6 +89,7 @@ _SIGNATURES = {
     "oasis_decode_step_pool_async": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                     _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                                                     ctypes.c_size_t, _P, _P, _P]),
+    "oasis_decode_layer_pipelined": (ctypes.c_int, [_DIMS, _P, _P, ctypes.c_float, _P]),
 }
 
 _lib = None
@@ -784,3 +785,67 @@ class PreparedPlanCopy:
 
     def __call__(self, stream=None) -> None:
         _check(self.lib.oasis_execute_plan(*self.args, _stream(stream)), "oasis_execute_plan")
+
+
+class LayerIO(ctypes.Structure):
+    """oasis_layer_io: one layer's buffers for the layer-pipelined decode."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "q", "summ", "k", "v", "seq_lens", "resident", "resident_next", "scores", "topk", "plan",
+        "plan_count", "table", "table_count", "out", "lse", "ws")] + [("ws_bytes", ctypes.c_size_t)]
+
+
+class PipelinedLayers:
+    """A sweep over two or more layers with each layer's selection and plan riding in
+    the next layer's first launch (oasis_decode_layer_pipelined).  ``layers`` holds,
+    per layer, (q, summ, k, v, seq_lens, resident); every layer gets its own step
+    buffers and next slot table.  Calling the object queues one decode step over all
+    layers (the previous step's last layer is selected in the first layer's launch);
+    ``drain()`` queues the last layer's pending selection.  The tensors must stay
+    alive while the object is used."""
+
+    def __init__(self, dims: OasisDims, layers, scale: Optional[float] = None):
+        if len(layers) < 2:
+            raise ValueError("the pipelined sweep needs at least two layers")
+        s = _shapes(dims)
+        self.dims = dims
+        self.scale = 1.0 / math.sqrt(128) if scale is None else float(scale)
+        self.lib = load()
+        self.buffers, self.resident_next, self.ios, self.keep = [], [], [], []
+        for (q, summ, k, v, seq_lens, resident) in layers:
+            _need(q, "q", torch.bfloat16, s["q"], align=16)
+            dev = q.device
+            _need(summ, "summ", torch.bfloat16, s["summ"], dev, align=16)
+            _need(k, "k", torch.bfloat16, s["kv"], dev, align=16)
+            _need(v, "v", torch.bfloat16, s["kv"], dev, align=16)
+            _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+            _need(resident, "resident", torch.int32, s["resident"], dev)
+            b = StepBuffers(dims, dev)
+            rn = torch.empty_like(resident)
+            io = LayerIO(q.data_ptr(), summ.data_ptr(), k.data_ptr(), v.data_ptr(), seq_lens.data_ptr(),
+                         resident.data_ptr(), rn.data_ptr(), b.scores.data_ptr(), b.topk.data_ptr(),
+                         b.plan.data_ptr() if b.plan.numel() else 0, b.plan_count.data_ptr(),
+                         b.table.data_ptr(), b.table_count.data_ptr(), b.out.data_ptr(), b.lse.data_ptr(),
+                         b.ws.data_ptr(), b.ws.numel())
+            self.buffers.append(b)
+            self.resident_next.append(rn)
+            self.ios.append(io)
+            self.keep.append((q, summ, k, v, seq_lens, resident))
+        self.started = False
+
+    def _call(self, layer, previous, stream):
+        _check(self.lib.oasis_decode_layer_pipelined(
+            ctypes.byref(self.dims), ctypes.byref(layer) if layer is not None else None,
+            ctypes.byref(previous) if previous is not None else None, ctypes.c_float(self.scale),
+            _stream(stream)), "oasis_decode_layer_pipelined")
+
+    def __call__(self, stream=None) -> None:
+        L = len(self.ios)
+        for i in range(L):
+            prev = self.ios[i - 1] if (i > 0 or self.started) else None
+            self._call(self.ios[i], prev, stream)
+        self.started = True
+
+    def drain(self, stream=None) -> None:
+        if self.started:
+            self._call(None, self.ios[-1], stream)
+            self.started = False

@@ -586,3 +586,65 @@ oasis_status oasis_decode_step_pool_async(
                                scale, out, lse, ws, ws_bytes, stream, true, transfer_stream,
                                plan_ready);
 }
+
+// ---- layer-pipelined decode ----------------------------------------------------------
+
+oasis_status oasis_decode_layer_pipelined(const oasis_dims* dims, const oasis_layer_io* layer,
+                                          const oasis_layer_io* previous, float scale,
+                                          hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  if (layer == nullptr && previous == nullptr)
+    return fail(OASIS_ERR_INVALID_ARG, "layer and previous are both NULL");
+  if (layer != nullptr) {
+    OASIS_REQUIRE(layer->q);
+    OASIS_REQUIRE(layer->summ);
+    OASIS_REQUIRE(layer->k);
+    OASIS_REQUIRE(layer->v);
+    OASIS_REQUIRE(layer->seq_lens);
+    OASIS_REQUIRE(layer->resident);
+    OASIS_REQUIRE(layer->scores);
+    OASIS_REQUIRE(layer->out);
+    if (!isfinite(scale)) return fail(OASIS_ERR_INVALID_ARG, "scale must be finite");
+    const size_t need = oasis::attn_workspace_bytes(d, d.table_stride);
+    if (layer->ws == nullptr || layer->ws_bytes < need)
+      return fail(OASIS_ERR_WORKSPACE, "layer needs %zu workspace bytes, got %zu", need,
+                  layer->ws == nullptr ? (size_t)0 : layer->ws_bytes);
+  }
+  if (previous != nullptr) {
+    OASIS_REQUIRE(previous->scores);
+    OASIS_REQUIRE(previous->seq_lens);
+    OASIS_REQUIRE(previous->resident);
+    OASIS_REQUIRE(previous->resident_next);
+    OASIS_REQUIRE(previous->topk);
+    if (d.cap > 0) OASIS_REQUIRE(previous->plan);
+    OASIS_REQUIRE(previous->plan_count);
+    OASIS_REQUIRE(previous->table);
+    OASIS_REQUIRE(previous->table_count);
+    const size_t n = (size_t)d.batch * d.heads * d.top_k;
+    if (previous->resident_next < previous->resident + n && previous->resident < previous->resident_next + n)
+      return fail(OASIS_ERR_INVALID_ARG, "previous->resident and previous->resident_next overlap");
+    if (layer != nullptr) {
+      const size_t nsc = (size_t)d.batch * d.heads * d.max_blocks;
+      if (previous->scores < layer->scores + nsc && layer->scores < previous->scores + nsc)
+        return fail(OASIS_ERR_INVALID_ARG, "layer and previous share scores");
+      if (previous->resident_next < layer->resident + n && layer->resident < previous->resident_next + n)
+        return fail(OASIS_ERR_INVALID_ARG, "previous->resident_next overlaps the slot table layer attends");
+    }
+  }
+  oasis::LayerIO cur{}, prev{};
+  if (layer != nullptr)
+    cur = oasis::LayerIO{layer->q, layer->summ, layer->k, layer->v, layer->seq_lens, layer->resident,
+                         layer->resident_next, layer->scores, layer->topk, layer->plan,
+                         layer->plan_count, layer->table, layer->table_count, layer->out,
+                         layer->lse, layer->ws};
+  if (previous != nullptr)
+    prev = oasis::LayerIO{previous->q, previous->summ, previous->k, previous->v, previous->seq_lens,
+                          previous->resident, previous->resident_next, previous->scores,
+                          previous->topk, previous->plan, previous->plan_count, previous->table,
+                          previous->table_count, previous->out, previous->lse, previous->ws};
+  return hip_status(oasis::launch_pipelined_layer(d, layer ? &cur : nullptr, previous ? &prev : nullptr,
+                                                  scale, stream),
+                    "decode_layer_pipelined");
+}

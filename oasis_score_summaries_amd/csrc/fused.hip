@@ -68,6 +68,102 @@ __global__ __launch_bounds__(THREADS) void select_merge_kernel(TopkPlanArgs ta, 
   }
 }
 
+// Layer-pipelined decode: the previous layer's selection and plan (its background
+// half) ride as extra workgroups in this layer's launch 1, next to this layer's
+// scoring and attention gathering; this layer's launch 2 is then the merge alone (its
+// foreground output, which the next layer needs).  The selection workgroups come
+// first, as they run longest, in 256 threads, so K <= 256 and at most 2048 blocks.
+template <int RT, int GP, int ITEMS>
+__global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void select_score_attn_kernel(
+    TopkPlanArgs prev, ScoreArgs sa, AttnArgs aa, int n_sel, int n_score, int score_gx, int attn_gx) {
+  __shared__ union {
+    ScoreShared<RT> s;
+    AttnShared<GP> a;
+    TopkPlanShared<kScoreThreads, ITEMS> t;
+  } sh;
+  __shared__ PlanBitmaps bm;
+  const int b = blockIdx.x;
+  if (b < n_sel) {
+    topk_plan_wg<kScoreThreads, ITEMS>(b, sh.t, bm, prev);
+    return;
+  }
+  const int c = b - n_sel;
+  if (c < n_score) {
+    score_wg<RT>(c % score_gx, c / score_gx, sh.s, sa);
+  } else {
+    const int i = c - n_score;
+    attn_split_wg<GP, true>(i % attn_gx, i / attn_gx, sh.a, aa);
+  }
+}
+
+// The shared launch also needs up to 4 query heads per KV head: the selection's LDS
+// on top of larger attention partials would leave fewer than four workgroups per CU.
+static bool pipelined_fits(const Dims& d) {
+  const int rt = (d.group * d.queries + 15) / 16;
+  return rt <= 2 && d.group <= 4 && d.top_k <= kScoreThreads && d.max_blocks <= 8 * kScoreThreads;
+}
+
+hipError_t launch_pipelined_layer(const Dims& d, const LayerIO* cur, const LayerIO* prev, float scale,
+                                  hipStream_t stream) {
+  const int heads = d.batch * d.heads;
+  TopkPlanArgs ta{};
+  if (prev != nullptr)
+    ta = topk_plan_args(d, prev->scores, prev->seq_lens, prev->topk, prev->resident,
+                        prev->resident_next, prev->plan, prev->plan_count, prev->table,
+                        prev->table_count);
+  if (cur == nullptr) {  // draining the last layer's background half
+    return prev == nullptr ? hipSuccess
+                           : launch_topk_plan(d, prev->scores, prev->seq_lens, prev->topk,
+                                              prev->resident, prev->resident_next, prev->plan,
+                                              prev->plan_count, prev->table, prev->table_count, stream);
+  }
+  const AttnSplit s = attn_split(d, d.table_stride);
+  const ScoreArgs sa = score_args(d, cur->q, cur->summ, cur->seq_lens, cur->scores);
+  const AttnArgs aa = attn_args(d, s, cur->q, cur->k, cur->v, cur->resident, nullptr, d.table_stride,
+                                cur->seq_lens, scale, cur->ws);
+  const int score_gx = score_grid_x(d);
+  const int n_score = score_gx * heads;
+  const int attn_gx = s.num_splits;
+  const int rt = (d.group * d.queries + 15) / 16;
+  hipError_t err;
+  if (pipelined_fits(d)) {
+    const int n_sel = prev != nullptr ? heads : 0;
+    const int grid = n_sel + n_score + attn_gx * heads;
+    const int items = select_items(d, kScoreThreads);
+    switch (rt * 100 + items) {
+#define OASIS_SSA_CASE(RT, I)                                                                  \
+  case RT * 100 + I:                                                                           \
+    select_score_attn_kernel<RT, 4, I><<<dim3(grid), dim3(64 * kAttnWaves), 0, stream>>>(      \
+        ta, sa, aa, n_sel, n_score, score_gx, attn_gx);                                        \
+    break;
+#define OASIS_SSA_ROW(RT) \
+  OASIS_SSA_CASE(RT, 1) OASIS_SSA_CASE(RT, 2) OASIS_SSA_CASE(RT, 4) OASIS_SSA_CASE(RT, 8)
+      OASIS_SSA_ROW(1)
+      OASIS_SSA_ROW(2)
+#undef OASIS_SSA_ROW
+#undef OASIS_SSA_CASE
+      default:
+        return hipErrorInvalidValue;
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  } else {
+    // Larger shapes: the previous layer's selection and plan as their own launch, then
+    // this layer's launch 1.
+    if (prev != nullptr &&
+        (err = launch_topk_plan(d, prev->scores, prev->seq_lens, prev->topk, prev->resident,
+                                prev->resident_next, prev->plan, prev->plan_count, prev->table,
+                                prev->table_count, stream)) != hipSuccess)
+      return err;
+    if ((err = launch_score(d, cur->q, cur->summ, cur->seq_lens, cur->scores, stream)) != hipSuccess)
+      return err;
+    if ((err = launch_attention_split(d, s, cur->q, cur->k, cur->v, cur->resident, nullptr,
+                                      d.table_stride, cur->seq_lens, scale, cur->ws, stream, true)) !=
+        hipSuccess)
+      return err;
+  }
+  return launch_attention_merge(d, s, cur->out, cur->lse, cur->ws, stream);
+}
+
 hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ, const void* k,
                                   const void* v, const int32_t* seq_lens, float* scores,
                                   int32_t* topk, const int32_t* resident, int32_t* resident_next,

@@ -93,4 +93,28 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
                                   void* ws, hipStream_t stream, hipEvent_t after_first = nullptr,
                                   const WorkingSet* pool = nullptr, bool execute_plan = true);
 
+// One layer's buffers for the layer-pipelined decode.
+struct LayerIO {
+  const void* q;
+  const void* summ;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  const int32_t* resident;
+  int32_t* resident_next;
+  float* scores;
+  int32_t* topk;
+  int32_t* plan;
+  int32_t* plan_count;
+  int32_t* table;
+  int32_t* table_count;
+  float* out;
+  float* lse;
+  void* ws;
+};
+// Layer `cur`'s scoring and attention (its merge as launch 2) with the selection and
+// plan of layer `prev` in the same launch 1; either may be NULL.
+hipError_t launch_pipelined_layer(const Dims& d, const LayerIO* cur, const LayerIO* prev, float scale,
+                                  hipStream_t stream);
+
 }  // namespace oasis

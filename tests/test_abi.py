@@ -44,7 +44,7 @@ def _dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.exported_symbols())
@@ -205,3 +205,32 @@ def test_working_set_argument_checks(lib):
                                     P(rv), FAKE, FAKE, FAKE, P(0x30000000), P(0x30000000), FAKE, FAKE,
                                     FAKE, FAKE, 0.1, FAKE, None, FAKE, need, None)
     assert st == INVALID_ARG and b"own buffer" in lib.oasis_last_error()
+
+
+@cpu_only
+def test_layer_pipelined_argument_checks(lib):
+    """Both layers NULL, a shared scores buffer, an overlapping next slot table or a
+    small workspace are rejected before anything is queued."""
+    from oasis_score_summaries_amd import LayerIO
+    d = _dims()
+    need = lib.oasis_workspace_bytes(ctypes.byref(d))
+
+    def io(base, ws_bytes=need):
+        x = LayerIO(*[base + 0x100000 * i for i in range(16)], ws_bytes)
+        return x
+
+    a, b = io(0x10000000), io(0x30000000)
+    call = lambda l, p: lib.oasis_decode_layer_pipelined(ctypes.byref(d), l, p, 0.1, None)
+    assert call(None, None) == INVALID_ARG
+    assert call(ctypes.byref(io(0x10000000, need - 1)), None) == WORKSPACE
+    shared = io(0x30000000)
+    shared.scores = a.scores
+    assert call(ctypes.byref(a), ctypes.byref(shared)) == INVALID_ARG
+    assert b"share scores" in lib.oasis_last_error()
+    bad = io(0x30000000)
+    bad.resident_next = bad.resident + 16
+    assert call(ctypes.byref(a), ctypes.byref(bad)) == INVALID_ARG
+    clash = io(0x30000000)
+    clash.resident_next = a.resident
+    assert call(ctypes.byref(a), ctypes.byref(clash)) == INVALID_ARG
+    assert b"overlaps" in lib.oasis_last_error()

@@ -683,3 +683,40 @@ def test_graph_replay_matches_eager(lib, overlapped):
         got = {**bufs.as_dict(), "resident": rn}
         for key in eager:
             assert torch.equal(eager[key], got[key]), f"replay {rep}: {key}"
+
+
+@pytest.mark.parametrize("group,queries", [(4, 5), (8, 2)])
+def test_layer_pipelined_sweep_matches_the_overlapped_step(lib, group, queries):
+    """Three layers, two decode steps with each layer's selection in the next layer's
+    first launch (group 8: the selection as a launch of its own): every layer's plan
+    outputs equal the overlapped step's bit for bit, its attention equals it up to
+    the merge's summation order and matches the oracle."""
+    w = synth.WORKLOADS["tiny_4k"].with_(batch=2, num_kv_heads=3, group=group, num_drafts=queries - 1,
+                                         fetch_ratio=0.25, ctx=4096 + 40, min_len=1000)
+    _say(f"layer-pipelined sweep group={group}")
+    d = lib.dims_for(w)
+    layers, expected = [], []
+    for layer in range(3):
+        d_, inp, summ, res = _prepared_inputs(lib, w, seed_layer=layer)
+        rn = torch.empty_like(res)
+        ov = lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, rn,
+                                        default_scale())
+        torch.cuda.synchronize()
+        expected.append(({k: v.clone() for k, v in ov.items()}, rn.clone(), inp, res))
+        layers.append((inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res))
+    sweep = lib.PipelinedLayers(d, layers, default_scale())
+    for step in range(2):
+        sweep()
+        sweep.drain()
+        torch.cuda.synchronize()
+        for li, (exp, rn, inp, res) in enumerate(expected):
+            b = sweep.buffers[li]
+            for key in ("scores", "topk", "plan", "plan_count", "table", "table_count"):
+                assert torch.equal(getattr(b, key), exp[key]), f"step {step} layer {li}: {key}"
+            assert torch.equal(sweep.resident_next[li], rn)
+            assert (b.out - exp["out"]).abs().max().item() <= 1e-6
+            lens = inp["seq_lens"].cpu().numpy()
+            table, tc = ref.resident_table(i64(res.cpu()), lens, w.window)
+            eo, _ = ref.sparse_attention(f64(inp["q"].cpu()), f64(inp["k"].cpu()), f64(inp["v"].cpu()),
+                                         table, tc, lens, default_scale())
+            np.testing.assert_allclose(f64(b.out.cpu()), eo, rtol=0, atol=OUT_ATOL)
