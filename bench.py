@@ -296,7 +296,7 @@ def layer_pipelined(d, sets, ms_step: float, torch, oa, reps: int = 100) -> dict
             "overlapped_step_us": round(ms_step * 1e3, 3)}
 
 
-def layer_pipeline(d, sets, wsets, hosts, torch, oa, steps: int = 20) -> dict:
+def transfer_pipeline(d, sets, wsets, hosts, torch, oa, steps: int = 20) -> dict:
     """The input sets as the layers of one decode step, the full cache in pinned host
     memory: every layer's step over its working set with the plan's copies on the
     same stream, against the copies on a transfer stream that each layer's next step
@@ -429,7 +429,7 @@ def plan_execution(w, d, sets, buffers, res_next, ms_step: float, stage_us: dict
     torch.cuda.synchronize()
     bulk = 4 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     out["bulk_h2d_gbps"] = round(bulk, 2)
-    out["layer_pipeline"] = layer_pipeline(d, sets, wsets, hosts, torch, oa)
+    out["transfer_pipeline"] = transfer_pipeline(d, sets, wsets, hosts, torch, oa)
     del src, dst, hosts, host_steps
     # Eq. (3): bytes the link can move while one layer's step computes, at the rate the
     # plan's copies reach; Eq. (4): the slowest background stage against that step.
@@ -522,10 +522,10 @@ def run_sweep(args) -> dict:
                                       buffers=bufs)
             moved += int(bufs.plan_count.sum()) * BLOCK_KV_BYTES
         torch.cuda.synchronize()
-        pipe = layer_pipeline(d, [{**st, "resident": r} for st, r in zip(sets, residents)], wsets, hosts,
+        pipe = transfer_pipeline(d, [{**st, "resident": r} for st, r in zip(sets, residents)], wsets, hosts,
                               torch, oa, steps=10)
         rows.append({"top_k": top_k, "fetch_ratio": ratio, "cap": w.cap,
-                     "layer_pipeline_us_per_layer": {k.replace("_us_per_layer", ""): v
+                     "transfer_pipeline_us_per_layer": {k.replace("_us_per_layer", ""): v
                                                      for k, v in pipe.items() if k.endswith("_us_per_layer")},
                      "overlapped_ms_per_step": round(ms_over, 6),
                      "overlapped_steps_per_s": round(1e3 / ms_over, 1),
