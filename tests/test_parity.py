@@ -720,3 +720,42 @@ def test_layer_pipelined_sweep_matches_the_overlapped_step(lib, group, queries):
             eo, _ = ref.sparse_attention(f64(inp["q"].cpu()), f64(inp["k"].cpu()), f64(inp["v"].cpu()),
                                          table, tc, lens, default_scale())
             np.testing.assert_allclose(f64(b.out.cpu()), eo, rtol=0, atol=OUT_ATOL)
+
+
+def test_pipelined_sweep_graph_replay_matches_eager(lib):
+    """A captured layer-pipelined sweep, replayed several times with eager work and
+    syncs between the replays, gives the eager sweep's outputs bit for bit."""
+    w = synth.WORKLOADS["tiny_4k"].with_(batch=2, num_kv_heads=2, fetch_ratio=0.25)
+    _say("pipelined sweep graph replay")
+    layers = []
+    for layer in range(3):
+        d, inp, summ, res = _prepared_inputs(lib, w, seed_layer=layer)
+        layers.append((inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res))
+    sweep = lib.PipelinedLayers(d, layers, default_scale())
+    sweep()
+    sweep()                          # steady state: the first layer's launch selects the last layer
+    torch.cuda.synchronize()
+    eager = [_step_outputs(b, rn) for b, rn in zip(sweep.buffers, sweep.resident_next)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sweep()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sweep()
+    last = len(layers) - 1
+    for rep in range(3):
+        for li, (b, rn) in enumerate(zip(sweep.buffers, sweep.resident_next)):
+            for key, t in list(b.as_dict().items()) + [("resident", rn)]:
+                if li == last and key == "scores":
+                    continue         # read by the first layer's launch before being rewritten
+                t.fill_(-7 if t.dtype == torch.int32 else float("nan"))   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for li, (b, rn) in enumerate(zip(sweep.buffers, sweep.resident_next)):
+            got = {**b.as_dict(), "resident": rn}
+            for key, val in eager[li].items():
+                assert torch.equal(got[key], val), f"replay {rep} layer {li}: {key}"
