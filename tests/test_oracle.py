@@ -729,3 +729,147 @@ def test_top_overlap_by_hand():
     assert ref.top_overlap(np.array([3, 1, 2, 9]), np.array([7, 5, 3, 9]), 4) == 0.5
     assert ref.top_overlap(np.array([4, -1, -1]), np.array([4, -1, -1]), 3) == 1.0
     assert ref.top_overlap(np.array([-1, -1]), np.array([-1, -1]), 2) == 1.0
+
+
+# ---------------------------------------------------------------------------
+# Block sizes other than 16 (the pages fix 16; 8, 32 and 64 are a sweep variant)
+# ---------------------------------------------------------------------------
+
+def test_summaries_of_merged_blocks():
+    """A block of 2b tokens is two blocks of b tokens: its summary is the elementwise
+    min / max of the halves' summaries over the halves that hold a valid token."""
+    r = _rng(40)
+    B, H, NB16, d = 3, 2, 8, 8
+    k16 = _bf16(r.standard_normal((B, H, NB16, 16, d)))
+    lens = np.array([128, 71, 9])                      # aligned, partial, inside the first half
+    s16 = ref.build_summaries(k16, lens, 16)
+    for small, big in ((8, 16), (16, 32), (32, 64)):
+        ks = k16.reshape(B, H, -1, small, d)
+        kb = k16.reshape(B, H, -1, big, d)
+        ss, sb = ref.build_summaries(ks, lens, small), ref.build_summaries(kb, lens, big)
+        if small == 16:
+            np.testing.assert_array_equal(ss, s16)
+        for b, j in itertools.product(range(B), range(kb.shape[2])):
+            L = int(lens[b])
+            halves = [2 * j + i for i in range(2) if (2 * j + i) * small < L]
+            if not halves:
+                assert not sb[b, :, j].any()
+                continue
+            np.testing.assert_array_equal(sb[b, :, j, 0], np.min([ss[b, :, i, 0] for i in halves], axis=0))
+            np.testing.assert_array_equal(sb[b, :, j, 1], np.max([ss[b, :, i, 1] for i in halves], axis=0))
+
+
+@pytest.mark.parametrize("block", [8, 32, 64])
+def test_score_bounds_every_true_dot_product_other_block_sizes(block):
+    r = _rng(41 + block)
+    B, H, G, Q, d, NB = 2, 2, 2, 3, 8, 5
+    q = _bf16(r.standard_normal((B, H, G, Q, d)))
+    k = _bf16(r.standard_normal((B, H, NB, block, d)))
+    lens = np.array([NB * block, NB * block - block - 3])
+    W = block // 2 + 1
+    s = ref.score_blocks(q, ref.build_summaries(k, lens, block), lens, W, block)
+    for b in range(B):
+        n_cand = (int(lens[b]) - W) // block                 # blocks wholly before the window
+        assert np.all(np.isneginf(s[b, :, n_cand:]))
+        for h, j in itertools.product(range(H), range(n_cand)):
+            dots = q[b, h].reshape(-1, d) @ k[b, h, j].T
+            assert s[b, h, j] >= dots.max() - 1e-12
+            # attained when every row's sign pattern is met by one token: a lone token
+            one = k.copy()
+            one[b, h, j] = k[b, h, j, :1]
+            s1 = ref.score_blocks(q, ref.build_summaries(one, lens, block), lens, W, block)
+            assert s1[b, h, j] == pytest.approx((q[b, h].reshape(-1, d) @ k[b, h, j, 0]).max(), abs=1e-12)
+
+
+@pytest.mark.parametrize("block", [8, 32, 64])
+def test_attention_all_blocks_equals_dense_other_block_sizes(block):
+    r = _rng(50 + block)
+    B, H, G, Q, d = 2, 2, 3, 2, 16
+    NB = 256 // block
+    q = _bf16(r.standard_normal((B, H, G, Q, d)))
+    k = _bf16(r.standard_normal((B, H, NB, block, d)))
+    v = _bf16(r.standard_normal((B, H, NB, block, d)))
+    lens = np.array([256, 211])
+    table = np.tile(np.arange(NB), (B, H, 1))
+    tc = np.full((B, H), NB)
+    scale = 1 / math.sqrt(d)
+    out, lse = ref.sparse_attention(q, k, v, table, tc, lens, scale, block)
+    for b in range(B):
+        L = int(lens[b])
+        kk = torch.from_numpy(k[b].reshape(H, NB * block, d)[:, :L])
+        vv = torch.from_numpy(v[b].reshape(H, NB * block, d)[:, :L])
+        qq = torch.from_numpy(q[b, :, :, 0, :])
+        dense = torch.nn.functional.scaled_dot_product_attention(
+            qq[:, :, None, :], kk[:, None].expand(H, G, L, d), vv[:, None].expand(H, G, L, d), scale=scale)
+        np.testing.assert_allclose(out[b], dense[:, :, 0, :].numpy(), rtol=0, atol=1e-12)
+        z = torch.einsum("hgd,htd->hgt", qq, kk) * scale
+        np.testing.assert_allclose(lse[b], torch.logsumexp(z, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("block", [8, 32, 64])
+def test_window_geometry_other_block_sizes(block):
+    assert ref.num_blocks(100, 32) == 4 and ref.first_window_block(100, 40, 32) == 1
+    assert ref.num_blocks(100, 8) == 13 and ref.first_window_block(100, 40, 8) == 7
+    for L in range(1, 300):
+        for W in (0, 1, block - 1, block, block + 1, 64, 128):
+            w0, nb = ref.first_window_block(L, W, block), ref.num_blocks(L, block)
+            toks = set(range(max(0, L - W), L))
+            covered = set(t for j in range(w0, nb) for t in range(block * j, min(block * j + block, L)))
+            assert toks <= covered
+            assert block * nb >= L > block * (nb - 1)
+            if w0 > 0:
+                assert block * w0 <= L - W
+            assert nb - w0 <= ref.window_ring_slots(W, block) == -(-W // block) + 1
+
+
+@pytest.mark.parametrize("block", [8, 32])
+def test_pool_attention_equals_table_attention_other_block_sizes(block):
+    r = _rng(60 + block)
+    B, H, G, Q, d, K = 2, 2, 2, 2, 8, 5
+    NB = 192 // block
+    q = _bf16(r.standard_normal((B, H, G, Q, d)))
+    k = _bf16(r.standard_normal((B, H, NB, block, d)))
+    v = _bf16(r.standard_normal((B, H, NB, block, d)))
+    lens = np.array([187, 100])
+    R = np.full((B, H, K), -1)
+    for b, h in itertools.product(range(B), range(H)):
+        nb = ref.num_blocks(int(lens[b]), block)
+        R[b, h, : K - 1] = r.choice(nb, size=K - 1, replace=False)
+        r.shuffle(R[b, h])
+    scale = 1 / math.sqrt(d)
+    for window in (0, 40):
+        pk, pv, rk, rv = ref.fill_working_set(k, v, R, lens, window, block)
+        out, lse = ref.pool_attention(q, pk, pv, rk, rv, R, lens, window, scale, block)
+        table, tc = ref.resident_table(R, lens, window, block)
+        eo, el = ref.sparse_attention(q, k, v, table, tc, lens, scale, block)
+        np.testing.assert_allclose(out, eo, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, el, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("block", [8, 32])
+def test_append_token_matches_a_rebuild_other_block_sizes(block):
+    r = _rng(70 + block)
+    B, H, d, W = 2, 2, 8, 24
+    NB = 96 // block
+    k = _bf16(r.standard_normal((B, H, NB, block, d)))
+    v = _bf16(r.standard_normal((B, H, NB, block, d)))
+    lens = np.array([13, 30])
+    summ = ref.build_summaries(k, lens, block)
+    R = np.full((B, H, 2), -1)
+    WB = ref.window_ring_slots(W, block)
+    _, _, rk, rv = ref.fill_working_set(k, v, R, lens, W, block)
+    for step in range(40):
+        kn = _bf16(r.standard_normal((B, H, d)) * (1 + step % 3))
+        vn = _bf16(r.standard_normal((B, H, d)))
+        k, v, summ, rk, rv = ref.append_token(k, v, summ, rk, rv, kn, vn, lens, W, block)
+        for b in range(B):
+            assert np.array_equal(k.reshape(B, H, -1, d)[b, :, int(lens[b])], kn[b])
+        lens = lens + 1
+        rebuilt = ref.build_summaries(k, lens, block)
+        np.testing.assert_array_equal(summ, rebuilt)
+        _, _, ek, ev = ref.fill_working_set(k, v, R, lens, W, block)
+        for b in range(B):
+            L = int(lens[b])
+            for j in range(ref.first_window_block(L, W, block), ref.num_blocks(L, block)):
+                n = min(block, L - block * j)
+                np.testing.assert_array_equal(rk[b, :, j % WB, :n], ek[b, :, j % WB, :n])

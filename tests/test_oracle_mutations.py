@@ -56,6 +56,13 @@ MUTATIONS = {
     "mass_normalised_over_candidates_only": ("p /= p.sum()", "p /= p[: n_cand * bs].sum()"),
     "mass_sums_over_the_group": ("best = np.maximum(best, per_block)",
                                  "best = np.where(np.isinf(best), per_block, best + per_block)"),
+    "window_assumes_16_token_blocks": ("return max(0, (int(seq_len) - int(window)) // block)",
+                                       "return max(0, (int(seq_len) - int(window)) // 16)"),
+    "block_count_assumes_16_tokens": ("return (int(seq_len) + block - 1) // block",
+                                      "return (int(seq_len) + 15) // 16"),
+    "attention_assumes_16_token_blocks": ("for t in range(block) if j * block + t < L]",
+                                          "for t in range(min(block, 16)) if j * block + t < L]"),
+    "summaries_stride_assumes_16": ("n_valid = min(bs, L - j * bs)", "n_valid = min(bs, L - j * 16)"),
     "overlap_divides_by_union": ("return 1.0 if m == 0 else len(a & b) / m",
                                  "return 1.0 if m == 0 else len(a & b) / len(a | b)"),
 }
@@ -78,6 +85,8 @@ def _run_pins(mutant, monkeypatch) -> bool:
             variants = [{"cap": 0}, {"cap": 4}]
         elif "window" in params:
             variants = [{"window": 0}, {"window": 40}, {"window": 64}]
+        elif "block" in params:
+            variants = [{"block": 8}, {"block": 32}]
         else:
             variants = [{}]
         for kw in variants:
