@@ -31,11 +31,12 @@
  *
  * Notation: B sequences, H = num_kv_heads, G = group (query heads per KV
  * head), Q = num_queries (index 0 is the target query, 1..Q-1 the drafts),
- * d = head_dim = 128, bs = block_size = 16, NB = max_blocks, K = top_k,
- * W = window_tokens, C = oasis_fetch_cap(), T = oasis_table_stride().
- * For sequence b with length len_b (1 <= len_b <= 16 * NB):
- *   nblk_b = ceil(len_b / 16)            blocks holding a token,
- *   w0_b   = max(0, floor((len_b - W) / 16))   first local-window block.
+ * d = head_dim = 128, bs = block_size (16 by default; 8, 32 and 64 also),
+ * NB = max_blocks, K = top_k, W = window_tokens, C = oasis_fetch_cap(),
+ * T = oasis_table_stride().
+ * For sequence b with length len_b (1 <= len_b <= bs * NB):
+ *   nblk_b = ceil(len_b / bs)            blocks holding a token,
+ *   w0_b   = max(0, floor((len_b - W) / bs))   first local-window block.
  * Blocks [0, w0_b) are the scoring candidates; blocks [w0_b, nblk_b) form the
  * local window, which is always attended and never scored or evicted.
  */
@@ -62,7 +63,8 @@ typedef enum {
 } oasis_status;
 
 /* Problem sizes of one decode step of one layer.  Host struct, read during the
- * call only.  Supported: head_dim == 128, block_size == 16, 1 <= top_k <= 1024,
+ * call only.  Supported: head_dim == 128, block_size in {8, 16, 32, 64} (the
+ * pages' default is 16, xllm-io review, section six), 1 <= top_k <= 1024,
  * top_k <= max_blocks <= 32768, group * num_queries <= 128, group <= 16,
  * window_tokens >= 0, 0 <= fetch_ratio <= 1. */
 typedef struct {
@@ -70,7 +72,7 @@ typedef struct {
   int32_t num_kv_heads;    /* H */
   int32_t group;           /* G query heads per KV head (GQA group) */
   int32_t head_dim;        /* d, must be 128 */
-  int32_t block_size;      /* tokens per block, must be 16 */
+  int32_t block_size;      /* bs tokens per block: 8, 16, 32 or 64 */
   int32_t max_blocks;      /* NB: block stride of every per-block tensor */
   int32_t num_queries;     /* Q = 1 + drafts per query head */
   int32_t top_k;           /* K blocks selected per KV head */
@@ -94,7 +96,7 @@ const char* oasis_last_error(void);
 int32_t oasis_fetch_cap(const oasis_dims* dims);
 
 /* Row length T of the attention table: K resident slots plus the most local-
- * window blocks any length can produce, ceil(W / 16) + 1.  -1 if invalid. */
+ * window blocks any length can produce, ceil(W / bs) + 1.  -1 if invalid. */
 int32_t oasis_table_stride(const oasis_dims* dims);
 
 /* Device workspace that oasis_decode_step needs (and oasis_sparse_decode_attn
@@ -108,12 +110,12 @@ size_t oasis_attn_workspace_bytes(const oasis_dims* dims, int32_t table_stride);
 
 /* Per-block min/max key summaries ("compressed keys"): for every block j of
  * every (b, h), summ[b,h,j,0,:] = min and summ[b,h,j,1,:] = max over the valid
- * tokens t (16*j + t < len_b) of k[b,h,j,t,:].  Blocks without a valid token
+ * tokens t (bs*j + t < len_b) of k[b,h,j,t,:].  Blocks without a valid token
  * get zeros.  Exact (bf16 min/max).
  * xllm-io review, section three component table (Compressed Key Cache:
  * per-dimension min/max of every logical block, 1/16 of the KV size) and
  * section two (Quest-style min/max pooling).
- *   k        device, bf16 [B, H, NB, 16, 128]
+ *   k        device, bf16 [B, H, NB, bs, 128]
  *   seq_lens device, int32 [B]
  *   summ     device, bf16 [B, H, NB, 2, 128]   (output) */
 oasis_status oasis_build_summaries(const oasis_dims* dims, const void* k, const int32_t* seq_lens,
@@ -187,7 +189,7 @@ oasis_status oasis_build_plan(const oasis_dims* dims, const float* scores, const
  * over the sparse working set) and architecture figure (sparse working set
  * in HBM: selected blocks plus the local window).
  *   q            device, bf16 [B, H, G, Q, 128] (row 0 of each query head is used)
- *   k, v         device, bf16 [B, H, NB, 16, 128]
+ *   k, v         device, bf16 [B, H, NB, bs, 128]
  *   table        device, int32 [B, H, table_stride]; entries distinct, in [0, NB)
  *   table_count  device, int32 [B, H], each in [0, table_stride]
  *   table_stride host, 1 <= table_stride <= 4096
@@ -289,7 +291,7 @@ oasis_status oasis_decode_step_timed(const oasis_dims* dims, const void* q, cons
 
 /* ---- Executing the plan: the working set in HBM -----------------------------
  *
- * The full K/V cache keeps its layout and place ([B, H, max_blocks, 16, 128]
+ * The full K/V cache keeps its layout and place ([B, H, max_blocks, bs, 128]
  * bf16, in HBM or in pinned host memory that the device can address): that is
  * the page table, and it never changes.  HBM holds each KV head's working set:
  * a pool of K block slots, slot s holding the block the resident slot table
@@ -301,16 +303,16 @@ oasis_status oasis_decode_step_timed(const oasis_dims* dims, const void* q, cons
  * an asynchronous transfer; section four, innovations table: only head-wise
  * mapping entries change; section five: compressed-key update and KV
  * transfer.  legiblepapers.com FAQ Q4; lode.cx points 1 and 3.)
- *   pool_k, pool_v  device, bf16 [B, H, K, 16, 128]
- *   ring_k, ring_v  device, bf16 [B, H, WB, 16, 128]
- *   k, v            the full cache, bf16 [B, H, max_blocks, 16, 128]: device
+ *   pool_k, pool_v  device, bf16 [B, H, K, bs, 128]
+ *   ring_k, ring_v  device, bf16 [B, H, WB, bs, 128]
+ *   k, v            the full cache, bf16 [B, H, max_blocks, bs, 128]: device
  *                   memory, or pinned host memory given by its device address
  *                   (hipHostGetDevicePointer); read (and, by append, written)
  *                   by the kernels directly.
  * Buffers are caller-owned and must be pairwise disjoint (checked on the
  * address ranges).  Errors as for the calls above. */
 
-/* Ring slots per KV head, ceil(W / 16) + 1 (== oasis_table_stride - top_k).
+/* Ring slots per KV head, ceil(W / bs) + 1 (== oasis_table_stride - top_k).
  * -1 if dims is invalid. */
 int32_t oasis_window_ring_slots(const oasis_dims* dims);
 
@@ -334,12 +336,12 @@ oasis_status oasis_execute_plan(const oasis_dims* dims, const int32_t* plan,
 /* Appends one decoded token per sequence at position L = seq_lens[b]:
  *   k_new, v_new  device, bf16 [B, H, 128]
  *   k, v          the full cache (both NULL: not written)
- *   ring_k/v      token L % 16 of ring slot (L / 16) % WB
- *   summ          the summary of block L / 16: the new key itself when L % 16
+ *   ring_k/v      token L % bs of ring slot (L / bs) % WB
+ *   summ          the summary of block L / bs: the new key itself when L % bs
  *                 == 0 (the token opens the block), else the elementwise min
  *                 and max with the summary so far (exact in bf16).
  * seq_lens is not changed: the caller counts the token in afterwards.  A
- * sequence with L >= 16 * max_blocks has no room and is skipped. */
+ * sequence with L >= bs * max_blocks has no room and is skipped. */
 oasis_status oasis_append_token(const oasis_dims* dims, const void* k_new, const void* v_new,
                                 const int32_t* seq_lens, void* summ, void* k, void* v,
                                 void* ring_k, void* ring_v, hipStream_t stream);
@@ -400,8 +402,8 @@ oasis_status oasis_decode_step_pool_async(
 typedef struct {
   const void* q;            /* device, bf16 [B, H, G, Q, 128] (row 0 target) */
   const void* summ;         /* device, bf16 [B, H, NB, 2, 128] */
-  const void* k;            /* device, bf16 [B, H, NB, 16, 128] */
-  const void* v;            /* device, bf16 [B, H, NB, 16, 128] */
+  const void* k;            /* device, bf16 [B, H, NB, bs, 128] */
+  const void* v;            /* device, bf16 [B, H, NB, bs, 128] */
   const int32_t* seq_lens;  /* device, int32 [B] */
   const int32_t* resident;  /* device, int32 [B, H, K]: the slot table attended now */
   int32_t* resident_next;   /* device, int32 [B, H, K]: the next slot table (own buffer) */

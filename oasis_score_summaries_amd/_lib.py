@@ -166,7 +166,8 @@ def make_dims(batch: int, num_kv_heads: int, group: int, max_blocks: int, num_qu
 def dims_for(workload) -> OasisDims:
     """Dims of a synthetic workload (any object with the Workload fields)."""
     return make_dims(workload.batch, workload.num_kv_heads, workload.group, workload.max_blocks,
-                     workload.queries, workload.top_k, workload.window, workload.fetch_ratio)
+                     workload.queries, workload.top_k, workload.window, workload.fetch_ratio,
+                     block_size=getattr(workload, "block", 16))
 
 
 def fetch_cap(dims: OasisDims) -> int:
@@ -195,7 +196,7 @@ def workspace_bytes(dims: OasisDims, stride: Optional[int] = None) -> int:
 def _shapes(d: OasisDims):
     B, H, G, Q, NB, K = d.batch, d.num_kv_heads, d.group, d.num_queries, d.max_blocks, d.top_k
     return {
-        "q": (B, H, G, Q, 128), "kv": (B, H, NB, 16, 128), "summ": (B, H, NB, 2, 128),
+        "q": (B, H, G, Q, 128), "kv": (B, H, NB, d.block_size, 128), "summ": (B, H, NB, 2, 128),
         "lens": (B,), "scores": (B, H, NB), "topk": (B, H, K), "resident": (B, H, K),
         "bh": (B, H), "out": (B, H, G, 128), "lse": (B, H, G),
     }
@@ -453,18 +454,19 @@ class WorkingSet:
         dev = _norm_device(device)
         B, H, K, WB = dims.batch, dims.num_kv_heads, dims.top_k, window_ring_slots(dims)
         self.dims = dims
-        self.pool_k = torch.zeros((B, H, K, 16, 128), dtype=torch.bfloat16, device=dev)
+        bs = dims.block_size
+        self.pool_k = torch.zeros((B, H, K, bs, 128), dtype=torch.bfloat16, device=dev)
         self.pool_v = torch.zeros_like(self.pool_k)
-        self.ring_k = torch.zeros((B, H, WB, 16, 128), dtype=torch.bfloat16, device=dev)
+        self.ring_k = torch.zeros((B, H, WB, bs, 128), dtype=torch.bfloat16, device=dev)
         self.ring_v = torch.zeros_like(self.ring_k)
 
     def check(self, device):
         B, H, K = self.dims.batch, self.dims.num_kv_heads, self.dims.top_k
-        WB = window_ring_slots(self.dims)
+        WB, bs = window_ring_slots(self.dims), self.dims.block_size
         for n in ("pool_k", "pool_v"):
-            _need(getattr(self, n), n, torch.bfloat16, (B, H, K, 16, 128), device, align=16)
+            _need(getattr(self, n), n, torch.bfloat16, (B, H, K, bs, 128), device, align=16)
         for n in ("ring_k", "ring_v"):
-            _need(getattr(self, n), n, torch.bfloat16, (B, H, WB, 16, 128), device, align=16)
+            _need(getattr(self, n), n, torch.bfloat16, (B, H, WB, bs, 128), device, align=16)
 
 
 def _cache_ptr(t: torch.Tensor, name: str, shape, device) -> ctypes.c_void_p:

@@ -35,8 +35,12 @@ oasis_status check_dims(const oasis_dims* in, oasis::Dims* out) {
   if (in == nullptr) return fail(OASIS_ERR_INVALID_ARG, "dims is NULL");
   if (in->head_dim != kHeadDim)
     return fail(OASIS_ERR_UNSUPPORTED, "head_dim %d: only %d is implemented", in->head_dim, kHeadDim);
-  if (in->block_size != kBlock)
-    return fail(OASIS_ERR_UNSUPPORTED, "block_size %d: only %d is implemented", in->block_size, kBlock);
+  int bshift = -1;
+  for (int sh = kMinBlockShift; sh <= kMaxBlockShift; ++sh)
+    if (in->block_size == (1 << sh)) bshift = sh;
+  if (bshift < 0)
+    return fail(OASIS_ERR_UNSUPPORTED, "block_size %d: only 8, 16, 32 and 64 are implemented",
+                in->block_size);
   if (in->batch < 1 || in->num_kv_heads < 1 || in->group < 1 || in->num_queries < 1)
     return fail(OASIS_ERR_INVALID_ARG, "batch, num_kv_heads, group and num_queries must be >= 1");
   if (in->max_blocks < 1) return fail(OASIS_ERR_INVALID_ARG, "max_blocks must be >= 1");
@@ -54,8 +58,8 @@ oasis_status check_dims(const oasis_dims* in, oasis::Dims* out) {
   if (in->group > kMaxGroup) return fail(OASIS_ERR_UNSUPPORTED, "group %d exceeds %d", in->group, kMaxGroup);
   if ((int64_t)in->batch * in->num_kv_heads > 65535)
     return fail(OASIS_ERR_UNSUPPORTED, "batch * num_kv_heads exceeds 65535");
-  if (in->window_tokens > kMaxBlocks * kBlock)
-    return fail(OASIS_ERR_UNSUPPORTED, "window_tokens exceeds %d", kMaxBlocks * kBlock);
+  if (in->window_tokens > (kMaxBlocks << bshift))
+    return fail(OASIS_ERR_UNSUPPORTED, "window_tokens exceeds %d", kMaxBlocks << bshift);
   out->batch = in->batch;
   out->heads = in->num_kv_heads;
   out->group = in->group;
@@ -64,7 +68,8 @@ oasis_status check_dims(const oasis_dims* in, oasis::Dims* out) {
   out->top_k = in->top_k;
   out->window = in->window_tokens;
   out->cap = (int)floor(in->fetch_ratio * (double)in->top_k + 1e-9);
-  out->table_stride = in->top_k + (in->window_tokens + kBlock - 1) / kBlock + 1;
+  out->table_stride = in->top_k + num_blocks(in->window_tokens, bshift) + 1;
+  out->bshift = bshift;
   return OASIS_OK;
 }
 
@@ -402,7 +407,7 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 oasis_status check_working_set(const oasis::Dims& d, const void* k, const void* v,
                                const void* pool_k, const void* pool_v, const void* ring_k,
                                const void* ring_v) {
-  const size_t blk = (size_t)oasis::kBlock * oasis::kHeadDim * 2;
+  const size_t blk = ((size_t)oasis::kHeadDim * 2) << d.bshift;
   const size_t heads = (size_t)d.batch * d.heads;
   const size_t full = heads * d.max_blocks * blk, pool = heads * d.top_k * blk;
   const size_t ring = heads * (size_t)(d.table_stride - d.top_k) * blk;

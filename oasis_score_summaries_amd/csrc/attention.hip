@@ -6,11 +6,12 @@
 // legiblepapers.com summary).  Every KV head has its own table of logical
 // block ids (xllm-io review, section four, Head-wise Mapping).
 //
-// The work is a gather of 8 KB per table entry (16 tokens of K and V), and on
-// this part a gather finishes soonest when each wave fetches as little as
-// possible and the whole table is requested at once: one 16-token block per wave
-// and round, four waves per workgroup, a workgroup per four table entries of a
-// head (more rounds only when a head has over 1024 entries).  K is requested
+// The work is a gather of 8 KB per 16 tokens of the table (K and V), and on this
+// part a gather finishes soonest when each wave fetches as little as possible and
+// the whole table is requested at once: 16 tokens per wave and round (one
+// 16-token block, two 8-token blocks, or a 16-token chunk of a larger block), four
+// waves per workgroup, a workgroup per 64 tokens of a head's table (more rounds
+// only when a head has over 1024 units of 16 tokens).  K is requested
 // before V, so the QK product and the softmax run while V is in flight; the
 // waves merge in LDS and each workgroup writes one (max, sum, unnormalised
 // output) partial per query head; a second kernel merges the partials of a
@@ -47,8 +48,9 @@ namespace oasis {
 #endif
 
 AttnSplit attn_split(const Dims& d, int table_stride) {
+  const int units = attn_units(d, table_stride);
   // Rounds per workgroup: enough that no head has more than kAttnMaxSplits partials.
-  const int groups = (table_stride + kAttnWaves - 1) / kAttnWaves;
+  const int groups = (units + kAttnWaves - 1) / kAttnWaves;
   AttnSplit s;
   s.rounds = (groups + kAttnMaxSplits - 1) / kAttnMaxSplits;
   if (s.rounds < 1) s.rounds = 1;
@@ -58,11 +60,11 @@ AttnSplit attn_split(const Dims& d, int table_stride) {
   const int64_t heads = (int64_t)d.batch * d.heads;
   while (s.rounds * 2 <= OASIS_ATTN_MAX_ROUNDS) {
     const int r = s.rounds * 2;
-    const int ns = (table_stride + kAttnWaves * r - 1) / (kAttnWaves * r);
+    const int ns = (units + kAttnWaves * r - 1) / (kAttnWaves * r);
     if (heads * ns < OASIS_ATTN_MIN_WGS) break;
     s.rounds = r;
   }
-  s.num_splits = (table_stride + kAttnWaves * s.rounds - 1) / (kAttnWaves * s.rounds);
+  s.num_splits = (units + kAttnWaves * s.rounds - 1) / (kAttnWaves * s.rounds);
   if (s.num_splits < 1) s.num_splits = 1;
   return s;
 }

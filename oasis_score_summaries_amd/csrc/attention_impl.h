@@ -8,7 +8,7 @@
 
 namespace oasis {
 
-constexpr int kAttnWaves = kWavesPerWG;                 // one table entry per wave and round
+constexpr int kAttnWaves = kWavesPerWG;                 // one 16-token unit per wave and round
 constexpr int kAttnMaxSplits = 256;           // partials per head
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -25,9 +25,14 @@ __device__ inline __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t by
 constexpr uint32_t kOffMasked = 0x80000000u;
 constexpr int kNtAux = 2;  // non-temporal: K and V are read once
 
-// K and V blocks are read with fully contiguous 1 KB wave loads (instruction s of
-// a block covers tokens 4s..4s+3): lane l holds token 4s + l/16, 16-byte chunk
-// l%16.  That is already the layout the PV product wants for V.  For QK, lane l
+// A wave's unit of work is 16 tokens of the table: one 16-token block, two 8-token
+// blocks, or a 16-token chunk of a 32- or 64-token block.  It is taken as two
+// halves of 8 tokens, each resolved on its own to a block and the 8-token
+// sub-block inside it, so every block size runs the same code.
+//
+// K and V units are read with contiguous 1 KB wave loads (instruction s of a unit
+// covers tokens 4s..4s+3, s < 2 in the first half): lane l holds token 4s + l/16,
+// 16-byte chunk l%16.  That is already the layout the PV product wants for V.  For QK, lane l
 // must supply one token's chunks, so K goes through LDS (rows padded to 272
 // bytes, conflict-free) and is read back with MFMA row i holding token
 // 4*(i%4) + i/4; the scores then come out with lane l owning exactly the tokens
@@ -45,7 +50,7 @@ constexpr int kKRow = kHeadDim * 2 / 16 + 1;  // padded LDS row of one K token, 
 // blocks a sequence can have.
 template <int GP>
 struct AttnShared {
-  u32x4 kst[kAttnWaves][kBlock * kKRow];  // per-wave K staging
+  u32x4 kst[kAttnWaves][16 * kKRow];  // per-wave K staging (16 tokens)
   // Per-wave partials: the waves merge without a barrier; the last one to finish
   // combines them and writes the record, the others end as soon as they have
   // published theirs (freeing their slots for waves of other workgroups).
@@ -66,7 +71,7 @@ struct AttnArgs {
   const int32_t* seq_lens;
   float scale_log2;
   float* part;
-  int heads, group, queries, NB, nsplit, rounds, K, window;
+  int heads, group, queries, NB, nsplit, rounds, K, window, bshift;
   // POOL only: the window ring (`k` and `v` are then the pool) and its slots per head.
   const char* ring_k;
   const char* ring_v;
@@ -76,8 +81,8 @@ struct AttnArgs {
 // One workgroup of split `sp` of (sequence, KV head) `bh`; a wave that does not
 // finish last returns early.  Every thread of the workgroup calls it.
 // POOL (with RES): the blocks are read from the working set in HBM instead of the
-// full cache: resident slot e from pool slot e (`k`, `v`: [B, H, K, 16, 128]),
-// window block j from ring slot j % WB (`ring_k`, `ring_v`: [B, H, WB, 16, 128]).
+// full cache: resident slot e from pool slot e (`k`, `v`: [B, H, K, bs, 128]),
+// window block j from ring slot j % WB (`ring_k`, `ring_v`: [B, H, WB, bs, 128]).
 template <int GP, bool RES, bool POOL = false>
 __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, AttnShared<GP>& sh,
                                                              const AttnArgs& a) {
@@ -87,7 +92,8 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
   const char* __restrict__ v = a.v;
   const int32_t* __restrict__ table = a.table;
   const int T = a.T, heads = a.heads, group = a.group, queries = a.queries, NB = a.NB;
-  const int nsplit = a.nsplit, rounds = a.rounds, K = a.K, window = a.window;
+  const int nsplit = a.nsplit, rounds = a.rounds, K = a.K, window = a.window, bshift = a.bshift;
+  const int hs = bshift - 3;  // log2 of the 8-token halves per block
   const float scale_log2 = a.scale_log2;
   float* __restrict__ part = a.part;
   auto& kst = sh.kst;
@@ -99,16 +105,21 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int split_entries = rounds * kAttnWaves;
+  const int split_units = rounds * kAttnWaves;
   const int len_raw = a.seq_lens[bh / heads];
   const int tc_raw = RES ? 0 : a.table_count[bh];
-  // The table entry heads the dependent chain table -> K/V, so it is requested
-  // together with the count, clamped to the row (not to the count).
-  int ent;
+  // The table entries head the dependent chain table -> K/V, so they are requested
+  // together with the count, clamped to the row (not to the count).  Half h of unit
+  // u is 8-token half 2u + h of the table, in entry (2u + h) >> hs (both halves in
+  // one entry unless the blocks hold 8 tokens).
+  auto load_entry = [&](int e) {
+    return RES ? table[(size_t)bh * K + (e < K ? e : K - 1)] : table[(size_t)bh * T + (e < T ? e : T - 1)];
+  };
+  int ent0, ent1 = -1;
   {
-    const int e = sp * split_entries + wave;
-    if (RES) ent = table[(size_t)bh * K + (e < K ? e : K - 1)];
-    else ent = table[(size_t)bh * T + (e < T ? e : T - 1)];
+    const int u = sp * split_units + wave;
+    ent0 = load_entry((2 * u) >> hs);
+    if (hs == 0) ent1 = load_entry(2 * u + 1);
   }
   // Columns past the group repeat the last query head; their results are never read.
   u32x4 qf[4];
@@ -120,18 +131,19 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
   // No early exit for a workgroup past the table count: every entry past it is a
   // masked load (no memory access), the record it writes is never read by the merge,
   // and without the branch the requests above cannot be moved behind the count.
-  const int len = clamp_len(len_raw, NB);
+  const int len = clamp_len(len_raw, NB, bshift);
   const int tc = tc_raw < 0 ? 0 : (tc_raw > T ? T : tc_raw);
-  const int w0 = first_window_block(len, window), nblk = num_blocks(len);
+  const int w0 = first_window_block(len, window, bshift), nblk = num_blocks(len, bshift);
 
-  constexpr uint32_t kBlockBytes = kBlock * kHeadDim * 2;
-  const uint32_t head_bytes = (uint32_t)(POOL ? K : NB) * kBlockBytes;
+  constexpr uint32_t kHalfBytes = 8 * kHeadDim * 2;
+  const uint32_t block_bytes = (uint32_t)(kHeadDim * 2) << bshift;
+  const uint32_t head_bytes = (uint32_t)(POOL ? K : NB) * block_bytes;
   const size_t head_off = (size_t)bh * head_bytes;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc(v + head_off, head_bytes);
   __amdgpu_buffer_rsrc_t rk_ring = rk, rv_ring = rv;
   if (POOL) {
-    const uint32_t ring_bytes = (uint32_t)a.WB * kBlockBytes;
+    const uint32_t ring_bytes = (uint32_t)a.WB * block_bytes;
     rk_ring = head_rsrc(a.ring_k + (size_t)bh * ring_bytes, ring_bytes);
     rv_ring = head_rsrc(a.ring_v + (size_t)bh * ring_bytes, ring_bytes);
   }
@@ -145,41 +157,64 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
 
   int rd = 0;
   do {  // rounds >= 1: a do-while keeps the loads above where they are issued
-    const int e = sp * split_entries + rd * kAttnWaves + wave;
+    const int u = sp * split_units + rd * kAttnWaves + wave;
+    const int e0 = (2 * u) >> hs, e1 = (2 * u + 1) >> hs;
     if (rd > 0) {
-      if (RES) ent = table[(size_t)bh * K + (e < K ? e : K - 1)];
-      else ent = table[(size_t)bh * T + (e < T ? e : T - 1)];
+      ent0 = load_entry(e0);
+      if (hs == 0) ent1 = load_entry(e1);
     }
-    int id = ent;
-    if (RES) {
-      if (e < K) {
-        if (id >= w0) id = -1;  // inside the window: attended as a window block
-      } else {
-        id = e - K < nblk - w0 ? w0 + (e - K) : -1;
+    // Half h: its 8-token sub-block id8[h] in the head's token order (-1: nothing to
+    // read), the byte offset of this lane's first chunk, and the buffers it is in.
+    int id8[2];
+    uint32_t off[2];
+    __amdgpu_buffer_rsrc_t rk_h[2], rv_h[2];
+    auto resolve = [&](int h, int e, int id) {
+      if (RES) {
+        if (e < K) {
+          if (id >= w0) id = -1;  // inside the window: attended as a window block
+        } else {
+          id = e - K < nblk - w0 ? w0 + (e - K) : -1;
+        }
+      } else if (e >= tc) {
+        id = -1;
       }
-    } else if (e >= tc) {
-      id = -1;
-    }
-    if (id < 0 || id >= NB || id * kBlock >= len) id = -1;
-    __amdgpu_buffer_rsrc_t rk_e = rk, rv_e = rv;
-    int phys = id;  // where the block sits: its logical index in the full cache
-    if (POOL) {     // ... or its pool slot, or its ring slot (all wave-uniform)
-      id = __builtin_amdgcn_readfirstlane(id);
-      const bool in_pool = __builtin_amdgcn_readfirstlane(e) < K;
-      phys = in_pool ? e : id % a.WB;
-      if (!in_pool) {
-        rk_e = rk_ring;
-        rv_e = rv_ring;
+      if (id < 0 || id >= NB || (id << bshift) >= len) id = -1;
+      rk_h[h] = rk;
+      rv_h[h] = rv;
+      int phys = id;  // where the block sits: its logical index in the full cache
+      if (POOL) {     // ... or its pool slot, or its ring slot (all wave-uniform)
+        id = __builtin_amdgcn_readfirstlane(id);
+        const bool in_pool = __builtin_amdgcn_readfirstlane(e) < K;
+        phys = in_pool ? e : id % a.WB;
+        if (!in_pool) {
+          rk_h[h] = rk_ring;
+          rv_h[h] = rv_ring;
+        }
       }
+      const int sub = (2 * u + h) & ((1 << hs) - 1);
+      int i8 = id < 0 ? -1 : (id << hs) + sub;
+      if (i8 * 8 >= len) i8 = -1;  // the half lies past the sequence
+      id8[h] = i8;
+      off[h] = i8 < 0 ? kOffMasked : (uint32_t)((phys << hs) + sub) * kHalfBytes + lane * 16;
+    };
+    resolve(0, e0, ent0);
+    if (hs == 0) {  // 8-token blocks: the second half is the next entry
+      resolve(1, e1, ent1);
+    } else {        // the next 8 tokens of the same block
+      int i8 = id8[0] < 0 ? -1 : id8[0] + 1;
+      if (i8 * 8 >= len) i8 = -1;
+      id8[1] = i8;
+      off[1] = i8 < 0 ? kOffMasked : off[0] + kHalfBytes;
+      rk_h[1] = rk_h[0];
+      rv_h[1] = rv_h[0];
     }
-    const uint32_t off = id < 0 ? kOffMasked : (uint32_t)phys * kBlockBytes + lane * 16;
     u32x4 kr[4], vf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      kr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk_e, off + 1024 * s, 0, kNtAux));
+      kr[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk_h[s >> 1], off[s >> 1] + 1024 * (s & 1), 0, kNtAux));
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-      vf[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv_e, off + 1024 * s, 0, kNtAux));
+      vf[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv_h[s >> 1], off[s >> 1] + 1024 * (s & 1), 0, kNtAux));
     // Stage K: token 4s + grp, chunk col.
 #pragma unroll
     for (int s = 0; s < 4; ++s) kst[wave][(4 * s + grp) * kKRow + col] = kr[s];
@@ -197,7 +232,7 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
     float bm = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool ok = id >= 0 && id * kBlock + 4 * r + grp < len;
+      const bool ok = id8[r >> 1] >= 0 && id8[r >> 1] * 8 + 4 * (r & 1) + grp < len;
       p[r] = ok ? st[r] * scale_log2 : -INFINITY;
       bm = fmaxf(bm, p[r]);
     }
@@ -228,7 +263,7 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
     // memory behind them need not hold finite values (masked blocks read zeros).
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (id * kBlock + 4 * s + grp >= len) vf[s] = u32x4{0u, 0u, 0u, 0u};
+      if (id8[s >> 1] * 8 + 4 * (s & 1) + grp >= len) vf[s] = u32x4{0u, 0u, 0u, 0u};
     }
     const bf16x4_bits pb_hi = __builtin_bit_cast(bf16x4_bits, (uint64_t)hw[0] | ((uint64_t)hw[1] << 32));
     const bf16x4_bits pb_lo = __builtin_bit_cast(bf16x4_bits, (uint64_t)lw[0] | ((uint64_t)lw[1] << 32));
@@ -409,6 +444,7 @@ inline AttnArgs attn_args(const Dims& d, const AttnSplit& s, const void* q, cons
   a.rounds = s.rounds;
   a.K = d.top_k;
   a.window = d.window;
+  a.bshift = d.bshift;
   a.ring_k = nullptr;
   a.ring_v = nullptr;
   a.WB = d.table_stride - d.top_k;

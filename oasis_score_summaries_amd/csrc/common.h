@@ -8,7 +8,6 @@
 namespace oasis {
 
 constexpr int kHeadDim = 128;
-constexpr int kBlock = 16;
 constexpr int kMaxBlocks = 32768;   // NB limit (top-K keeps one register slice per thread)
 constexpr int kMaxTopK = 1024;
 constexpr int kMaxRows = 128;       // G * Q limit of the score kernel (8 row tiles of 16)
@@ -26,16 +25,21 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---- sequence geometry (identical on host and device) ----------------------------
-__host__ __device__ inline int clamp_len(int len, int max_blocks) {
-  const int cap = max_blocks * kBlock;
+// Blocks hold 1 << bshift tokens (bshift 3..6: 8 to 64 tokens; 16 is the default).
+constexpr int kMinBlockShift = 3;
+constexpr int kMaxBlockShift = 6;
+__host__ __device__ inline int clamp_len(int len, int max_blocks, int bshift) {
+  const int cap = max_blocks << bshift;
   return len < 0 ? 0 : (len > cap ? cap : len);
 }
 // Blocks that hold at least one token.
-__host__ __device__ inline int num_blocks(int len) { return (len + kBlock - 1) / kBlock; }
+__host__ __device__ inline int num_blocks(int len, int bshift) {
+  return (len + (1 << bshift) - 1) >> bshift;
+}
 // First block overlapping the last `window` tokens; earlier blocks are scoring candidates.
-__host__ __device__ inline int first_window_block(int len, int window) {
+__host__ __device__ inline int first_window_block(int len, int window, int bshift) {
   const int x = len - window;
-  return x > 0 ? x / kBlock : 0;
+  return x > 0 ? x >> bshift : 0;
 }
 
 // ---- bf16 bit helpers -------------------------------------------------------------

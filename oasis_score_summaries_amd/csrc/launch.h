@@ -10,15 +10,22 @@ namespace oasis {
 // Validated problem sizes (see oasis_dims in include/oasis.h).
 struct Dims {
   int batch, heads, group, max_blocks, queries, top_k, window, cap, table_stride;
+  int bshift;  // log2 of the block size in tokens
 };
 
 // Attention split geometry shared by the split kernel, the merge kernel and the
-// workspace layout: workgroup s of a head takes table entries
-// [4 * rounds * s, 4 * rounds * (s + 1)), one per wave and round.
+// workspace layout.  The gather works in units of 16 tokens of a head's table: one
+// entry of 16-token blocks, two entries of 8-token blocks, or one 16-token chunk of
+// a larger block.  Workgroup s of a head takes units [4 * rounds * s,
+// 4 * rounds * (s + 1)), one per wave and round.
 struct AttnSplit {
-  int rounds;      // table entries per wave
-  int num_splits;  // ceil(table_stride / (4 * rounds))
+  int rounds;      // units per wave
+  int num_splits;  // ceil(units / (4 * rounds))
 };
+// Units of a table of `table_stride` entries.
+inline int attn_units(const Dims& d, int table_stride) {
+  return (int)(((int64_t)table_stride << d.bshift) + 15) / 16;
+}
 AttnSplit attn_split(const Dims& d, int table_stride);
 size_t attn_workspace_bytes(const Dims& d, int table_stride);
 
@@ -59,7 +66,7 @@ hipError_t launch_attention(const Dims& d, const void* q, const void* k, const v
                             hipStream_t stream, bool from_resident = false);
 
 // The working set in HBM: per (sequence, KV head) a pool of top_k block slots and a
-// ring of WB = table_stride - top_k window block slots, each slot 16 tokens of K
+// ring of WB = table_stride - top_k window block slots, each slot one block of K
 // (or V) bf16.
 struct WorkingSet {
   void* pool_k;

@@ -29,7 +29,7 @@ struct ScoreArgs {
   const u32x4* summ;
   const int32_t* seq_lens;
   float* scores;
-  int heads, max_blocks, rows, window;
+  int heads, max_blocks, rows, window, bshift;
 };
 
 // One workgroup: block range `bx` (kScoreBlocksPerWG candidate blocks) of (sequence,
@@ -45,8 +45,8 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int jw = bx * kScoreBlocksPerWG + wave * kScoreTilesPerWave * 16;  // this wave's first block
-  const int len = clamp_len(a.seq_lens[b], max_blocks);
-  const int n_cand = first_window_block(len, window);
+  const int len = clamp_len(a.seq_lens[b], max_blocks, a.bshift);
+  const int n_cand = first_window_block(len, window, a.bshift);
   float* out = a.scores + (size_t)bh * max_blocks;
   if ((int)bx * kScoreBlocksPerWG >= n_cand) {  // no candidate in this workgroup's range
     for (int j = threadIdx.x; j < kScoreBlocksPerWG; j += blockDim.x) {
@@ -141,6 +141,7 @@ inline ScoreArgs score_args(const Dims& d, const void* q, const void* summ, cons
   a.max_blocks = d.max_blocks;
   a.rows = d.group * d.queries;
   a.window = d.window;
+  a.bshift = d.bshift;
   return a;
 }
 inline int score_grid_x(const Dims& d) { return (d.max_blocks + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG; }

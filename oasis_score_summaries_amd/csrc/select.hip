@@ -38,11 +38,11 @@ template <int THREADS, int ITEMS>
 __global__ __launch_bounds__(THREADS) void topk_kernel(const float* __restrict__ scores,
                                                        const int32_t* __restrict__ seq_lens,
                                                        int32_t* __restrict__ topk, int heads, int NB,
-                                                       int K, int window) {
+                                                       int K, int window, int bshift) {
   __shared__ SelectShared<THREADS, ITEMS> sh;
   const int bh = blockIdx.x;
-  const int len = clamp_len(seq_lens[bh / heads], NB);
-  const int n_cand = first_window_block(len, window);
+  const int len = clamp_len(seq_lens[bh / heads], NB, bshift);
+  const int n_cand = first_window_block(len, window, bshift);
   const int m = topk_select<THREADS, ITEMS>(scores + (size_t)bh * NB, n_cand, K, sh, NB);
   for (int t = threadIdx.x; t < K; t += THREADS) topk[(size_t)bh * K + t] = t < m ? sh.sorted_idx[t] : -1;
 }
@@ -51,18 +51,19 @@ template <int THREADS>
 __global__ __launch_bounds__(THREADS) void plan_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ topk,
     const int32_t* __restrict__ seq_lens, int32_t* resident, int32_t* plan, int32_t* plan_count,
-    int32_t* table, int32_t* table_count, int heads, int NB, int K, int C, int window, int T) {
+    int32_t* table, int32_t* table_count, int heads, int NB, int K, int C, int window, int T,
+    int bshift) {
   __shared__ PlanShared<THREADS> sh;
   __shared__ PlanBitmaps bm;
   const int bh = blockIdx.x;
-  const int len = clamp_len(seq_lens[bh / heads], NB);
+  const int len = clamp_len(seq_lens[bh / heads], NB, bshift);
   const int s_i = threadIdx.x < K ? topk[(size_t)bh * K + threadIdx.x] : -1;
   const ResidentSlot rs = load_resident_slot(resident + (size_t)bh * K, scores + (size_t)bh * NB, K, NB);
   clear_bitmaps(bm, NB);
   __syncthreads();
   plan_apply<THREADS>(s_i, rs, resident + (size_t)bh * K, plan + (size_t)bh * C * 3,
                       plan_count + bh, table + (size_t)bh * T, table_count + bh, K, C, NB,
-                      first_window_block(len, window), num_blocks(len), T, bm, sh);
+                      first_window_block(len, window, bshift), num_blocks(len, bshift), T, bm, sh);
 }
 
 template <int THREADS, int ITEMS>
@@ -78,7 +79,7 @@ hipError_t launch_topk(const Dims& d, const float* scores, const int32_t* seq_le
   case I:                                                                                           \
     topk_kernel<T, I><<<dim3(d.batch * d.heads), dim3(T), 0, stream>>>(scores, seq_lens, topk,      \
                                                                        d.heads, d.max_blocks,       \
-                                                                       d.top_k, d.window);          \
+                                                                       d.top_k, d.window, d.bshift); \
     break;
   OASIS_SELECT_DISPATCH(OASIS_TOPK_CASE);
 #undef OASIS_TOPK_CASE
@@ -92,11 +93,11 @@ hipError_t launch_plan(const Dims& d, const float* scores, const int32_t* topk,
   if (d.top_k <= 256) {
     plan_kernel<256><<<dim3(d.batch * d.heads), dim3(256), 0, stream>>>(
         scores, topk, seq_lens, resident, plan, plan_count, table, table_count, d.heads,
-        d.max_blocks, d.top_k, d.cap, d.window, d.table_stride);
+        d.max_blocks, d.top_k, d.cap, d.window, d.table_stride, d.bshift);
   } else {
     plan_kernel<1024><<<dim3(d.batch * d.heads), dim3(1024), 0, stream>>>(
         scores, topk, seq_lens, resident, plan, plan_count, table, table_count, d.heads,
-        d.max_blocks, d.top_k, d.cap, d.window, d.table_stride);
+        d.max_blocks, d.top_k, d.cap, d.window, d.table_stride, d.bshift);
   }
   return hipGetLastError();
 }

@@ -471,7 +471,7 @@ struct TopkPlanArgs {
   int32_t* plan_count;
   int32_t* table;
   int32_t* table_count;
-  int heads, NB, K, C, window, T;
+  int heads, NB, K, C, window, T, bshift;
 };
 
 // Selection and plan of (sequence, KV head) `bh` in one workgroup; the bitmaps are
@@ -480,8 +480,8 @@ template <int THREADS, int ITEMS>
 __device__ __attribute__((always_inline)) void topk_plan_wg(int bh, TopkPlanShared<THREADS, ITEMS>& sh,
                                                             PlanBitmaps& bm, const TopkPlanArgs& a) {
   const int NB = a.NB, K = a.K, C = a.C, T = a.T;
-  const int len = clamp_len(a.seq_lens[bh / a.heads], NB);
-  const int n_cand = first_window_block(len, a.window);
+  const int len = clamp_len(a.seq_lens[bh / a.heads], NB, a.bshift);
+  const int n_cand = first_window_block(len, a.window, a.bshift);
   const float* srow = a.scores + (size_t)bh * NB;
   ResidentSlot rs;
   if (kCanStage<THREADS, ITEMS>) {  // the score comes from the selection's staging
@@ -503,7 +503,7 @@ __device__ __attribute__((always_inline)) void topk_plan_wg(int bh, TopkPlanShar
   plan_apply<THREADS, true>(s_i, rs, a.resident_next + (size_t)bh * K,
                       a.plan == nullptr ? nullptr : a.plan + (size_t)bh * C * 3, a.plan_count + bh,
                       a.table + (size_t)bh * T, a.table_count + bh, K, C, NB, n_cand,
-                      num_blocks(len), T, bm, sh.p);
+                      num_blocks(len, a.bshift), T, bm, sh.p);
 }
 
 // Host side: the argument block of the selection-and-plan work for `d`.
@@ -527,6 +527,7 @@ inline TopkPlanArgs topk_plan_args(const Dims& d, const float* scores, const int
   a.C = d.cap;
   a.window = d.window;
   a.T = d.table_stride;
+  a.bshift = d.bshift;
   return a;
 }
 

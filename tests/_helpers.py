@@ -90,28 +90,29 @@ def plan_robust(scores: np.ndarray, sel: np.ndarray, resident: np.ndarray, cap: 
     return True
 
 
-def oracle_head(q, k, v, lens, resident_row, top_k, window, cap, scale, b, h) -> Dict[str, np.ndarray]:
+def oracle_head(q, k, v, lens, resident_row, top_k, window, cap, scale, b, h,
+                block: int = 16) -> Dict[str, np.ndarray]:
     """The whole oracle step for one (sequence b, KV head h); inputs are CPU tensors
     of the full batch (only that head's slices are converted)."""
     qh = f64(q[b:b + 1, h:h + 1])
     kh = f64(k[b:b + 1, h:h + 1])
     vh = f64(v[b:b + 1, h:h + 1])
     L = np.array([int(lens[b])])
-    summ = ref.build_summaries(kh, L)
+    summ = ref.build_summaries(kh, L, block)
     res = ref.decode_step(qh, summ, kh, vh, L, np.asarray(resident_row)[None, None], top_k, window,
-                          cap, scale)
+                          cap, scale, block)
     res["summ"] = summ
     return {key: val[0, 0] if isinstance(val, np.ndarray) and val.ndim >= 2 else val
             for key, val in res.items()}
 
 
-def oracle_selection_head(q, k, lens, top_k, window, b, h) -> np.ndarray:
+def oracle_selection_head(q, k, lens, top_k, window, b, h, block: int = 16) -> np.ndarray:
     """The oracle's top-K for one head (used to build resident sets)."""
     qh = f64(q[b:b + 1, h:h + 1])
     kh = f64(k[b:b + 1, h:h + 1])
     L = np.array([int(lens[b])])
-    s = ref.score_blocks(qh, ref.build_summaries(kh, L), L, window)
-    return ref.topk_blocks(s, L, top_k, window)[0, 0]
+    s = ref.score_blocks(qh, ref.build_summaries(kh, L, block), L, window, block)
+    return ref.topk_blocks(s, L, top_k, window, block)[0, 0]
 
 
 def default_scale() -> float:

@@ -59,7 +59,8 @@ def test_version_and_status_strings(lib):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("head_dim", 64, UNSUPPORTED), ("block_size", 32, UNSUPPORTED), ("batch", 0, INVALID_ARG),
+    ("head_dim", 64, UNSUPPORTED), ("block_size", 24, UNSUPPORTED), ("block_size", 4, UNSUPPORTED),
+    ("block_size", 128, UNSUPPORTED), ("block_size", 0, UNSUPPORTED), ("batch", 0, INVALID_ARG),
     ("num_kv_heads", 0, INVALID_ARG), ("group", 0, INVALID_ARG), ("num_queries", 0, INVALID_ARG),
     ("max_blocks", 0, INVALID_ARG), ("top_k", 0, INVALID_ARG), ("top_k", 65, INVALID_ARG),
     ("window_tokens", -1, INVALID_ARG), ("fetch_ratio", -0.1, INVALID_ARG),
@@ -78,6 +79,20 @@ def test_dims_validation(lib, field, value, status):
     st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
                                FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, FAKE, 1 << 30, None)
     assert st == status
+
+
+@pytest.mark.parametrize("block,W,stride", [(8, 64, 16 + 8 + 1), (16, 64, 16 + 4 + 1),
+                                             (32, 64, 16 + 2 + 1), (64, 64, 16 + 1 + 1),
+                                             (32, 40, 16 + 2 + 1), (64, 0, 16 + 0 + 1)])
+@cpu_only
+def test_block_sizes_accepted(lib, block, W, stride):
+    """8-, 16-, 32- and 64-token blocks: the table holds K slots plus the most window
+    blocks a length has (ceil(W / block) + 1), the ring as many slots."""
+    d = _dims(block_size=block, window_tokens=W)
+    assert lib.oasis_table_stride(ctypes.byref(d)) == stride
+    assert lib.oasis_window_ring_slots(ctypes.byref(d)) == stride - 16
+    assert lib.oasis_workspace_bytes(ctypes.byref(d)) > 0
+    assert lib.oasis_fetch_cap(ctypes.byref(d)) == 0
 
 
 @cpu_only

@@ -374,8 +374,9 @@ def _full_size_case(lib, w, layer=0):
         if w.resident == "prev":
             cpu.setdefault("q_prev", {})[(b, h)] = inp["q_prev"][b:b + 1, h:h + 1].cpu()
         qs = cpu["q_prev" if w.resident == "prev" else "q"][(b, h)]
-        osel = oracle_selection_head(qs, cpu["k"][(b, h)], lens[b:b + 1], w.top_k, w.window, 0, 0)
-        n_cand = ref.first_window_block(int(lens[b]), w.window)
+        osel = oracle_selection_head(qs, cpu["k"][(b, h)], lens[b:b + 1], w.top_k, w.window, 0, 0,
+                                     w.block)
+        n_cand = ref.first_window_block(int(lens[b]), w.window, w.block)
         resident[b, h] = torch.from_numpy(synth.resident_for_head(w, osel, n_cand, b, h, layer).astype(np.int32))
     _say(f"full-size {w.name} layer={layer}: decode_step")
     res_dev = resident.to(DEV)
@@ -387,17 +388,18 @@ def _full_size_case(lib, w, layer=0):
     for (b, h) in heads:
         _say(f"full-size {w.name} layer={layer}: oracle b={b} h={h}")
         exp = oracle_head(cpu["q"][(b, h)], cpu["k"][(b, h)], cpu["v"][(b, h)], lens[b:b + 1],
-                          resident[b, h].numpy(), w.top_k, w.window, w.cap, default_scale(), 0, 0)
+                          resident[b, h].numpy(), w.top_k, w.window, w.cap, default_scale(), 0, 0,
+                          w.block)
         np.testing.assert_array_equal(f64(summ[b, h]), exp["summ"])
         exp["q64"] = f64(cpu["q"][(b, h)][0, 0])
         robust = plan_robust(exp["scores"], exp["topk"], resident[b, h].numpy(), w.cap,
-                             ref.first_window_block(int(lens[b]), w.window))
+                             ref.first_window_block(int(lens[b]), w.window, w.block))
         n_exact += _compare_head(w, got, exp, b, h, resident[b, h].numpy(), robust)
         # whatever the robustness, the GPU's own outputs must be self-consistent
         tc = int(got["table_count"][b, h])
         assert int(got["plan_count"][b, h]) <= w.cap
-        assert tc == int((got["resident"][b, h] >= 0).sum()) + ref.num_blocks(int(lens[b])) - \
-            ref.first_window_block(int(lens[b]), w.window)
+        assert tc == int((got["resident"][b, h] >= 0).sum()) + ref.num_blocks(int(lens[b]), w.block) - \
+            ref.first_window_block(int(lens[b]), w.window, w.block)
         assert torch.isfinite(got["out"][b, h]).all()
     # fp32 scoring error (~1e-7 relative) is far below the 1e-5 tolerance, so nearly
     # every sampled head must reproduce the oracle's plan and table exactly
@@ -415,9 +417,9 @@ def _full_size_case(lib, w, layer=0):
     assert torch.equal(rn.cpu(), got["resident"])
     for (b, h) in heads:
         lb = lens[b:b + 1].numpy()
-        table, tc = ref.resident_table(i64(resident[b:b + 1, h:h + 1]), lb, w.window)
+        table, tc = ref.resident_table(i64(resident[b:b + 1, h:h + 1]), lb, w.window, w.block)
         eo, el = ref.sparse_attention(f64(cpu["q"][(b, h)]), f64(cpu["k"][(b, h)]),
-                                      f64(cpu["v"][(b, h)]), table, tc, lb, default_scale())
+                                      f64(cpu["v"][(b, h)]), table, tc, lb, default_scale(), w.block)
         np.testing.assert_allclose(f64(ov["out"][b, h].cpu()), eo[0, 0], rtol=0, atol=OUT_ATOL)
         np.testing.assert_allclose(f64(ov["lse"][b, h].cpu()), el[0, 0], rtol=0, atol=OUT_ATOL)
     del inp, summ, out, ov

@@ -1,0 +1,323 @@
+"""GPU parity at block sizes other than 16 tokens (8, 32 and 64): every entry point
+against the fp64 oracle, which takes the block size as a parameter.
+
+The pages fix 16-token blocks (xllm-io review, section six, default parameters);
+the other sizes are a sweep variant.  The summaries stay one min and one max row per
+block whatever its size, so the scoring and selection change only through the
+block geometry (candidates, window blocks); the attention, the working set and
+the appended token read and write blocks of 8 to 64 tokens.
+
+All calls go through the C ABI (ctypes binding).  Inputs are seeded synthetic
+tensors; no expected value comes from the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import ref
+from tests._helpers import (OUT_ATOL, check_scores, default_scale, f64, i64, oracle_head,
+                            score_floor)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+BLOCKS = [8, 32, 64]
+PLAN_KEYS = ("topk", "plan", "plan_count", "resident", "table", "table_count")
+
+
+def _say(msg):
+    print(f"[block sizes] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import oasis_score_summaries_amd as oa
+    oa.load()
+    return oa
+
+
+def _inputs(seed, B, H, G, Q, NB, bs, lens, integer=False):
+    g = torch.Generator().manual_seed(seed)
+    if integer:
+        q = torch.randint(-3, 4, (B, H, G, Q, 128), generator=g).to(torch.bfloat16)
+        k = torch.randint(-4, 5, (B, H, NB, bs, 128), generator=g).to(torch.bfloat16)
+    else:
+        q = torch.randn((B, H, G, Q, 128), generator=g).to(torch.bfloat16)
+        k = torch.randn((B, H, NB, bs, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, NB, bs, 128), generator=g).to(torch.bfloat16)
+    return q, k, v, torch.tensor(lens, dtype=torch.int32)
+
+
+def _slot_tables(seed, B, H, K, lens, bs, n_empty_of_h=lambda h: h % 3):
+    """Slot tables with empty slots and with blocks anywhere in the sequence
+    (window blocks included)."""
+    r = np.random.default_rng(seed)
+    R = np.full((B, H, K), -1, dtype=np.int64)
+    for b in range(B):
+        nb = ref.num_blocks(lens[b], bs)
+        for h in range(H):
+            n = min(K - n_empty_of_h(h), nb)
+            R[b, h, :n] = r.choice(nb, size=n, replace=False)
+            r.shuffle(R[b, h])
+    return R
+
+
+@pytest.mark.parametrize("bs", BLOCKS)
+@pytest.mark.parametrize("W", [64, 40])
+def test_decode_step_integer_inputs(lib, bs, W):
+    """Small-integer q and k make every score exact in fp32 and fp64, so the
+    selection, plan and table (ties included) agree bit for bit; lengths ragged at
+    every block size, one shorter than a block."""
+    lens = [4096 + 5, 1000, 3, 777]
+    B, H, G, Q, K = len(lens), 3, 4, 5, 24
+    NB = ref.num_blocks(max(lens), bs) + 2
+    _say(f"integer decode step bs={bs} W={W}")
+    q, k, v, L = _inputs(100 + bs + W, B, H, G, Q, NB, bs, lens, integer=True)
+    d = lib.make_dims(B, H, G, NB, Q, K, W, 0.25, block_size=bs)
+    resident = torch.empty((B, H, K), dtype=torch.int32)
+    for b in range(B):
+        for h in range(H):
+            resident[b, h] = synth.random_resident(K, ref.first_window_block(lens[b], W, bs), [0, 3, K][h],
+                                                   50 * b + h)
+    kd, Ld = k.to(DEV), L.to(DEV)
+    summ = lib.build_summaries(d, kd, Ld)
+    got = lib.decode_step(d, q.to(DEV), summ, kd, v.to(DEV), Ld, resident.to(DEV), default_scale())
+    torch.cuda.synchronize()
+    got = {key: val.cpu() for key, val in got.items()}
+    for b in range(B):
+        for h in range(H):
+            exp = oracle_head(q, k, v, L, resident[b, h].numpy(), K, W, d_cap(d), default_scale(), b, h, bs)
+            assert np.array_equal(f64(summ[b, h]), exp["summ"]), f"summaries b={b} h={h}"
+            np.testing.assert_array_equal(f64(got["scores"][b, h]), exp["scores"])
+            for key in PLAN_KEYS:
+                np.testing.assert_array_equal(i64(got[key][b, h]), exp[key], err_msg=f"{key} b={b} h={h}")
+            np.testing.assert_allclose(f64(got["out"][b, h]), exp["out"], rtol=0, atol=OUT_ATOL)
+            fin = np.isfinite(exp["lse"])
+            np.testing.assert_allclose(f64(got["lse"][b, h])[fin], exp["lse"][fin], rtol=0, atol=OUT_ATOL)
+
+
+def d_cap(d):
+    return ref.fetch_cap(d.fetch_ratio, d.top_k)
+
+
+@pytest.mark.parametrize("bs", BLOCKS)
+def test_overlapped_step(lib, bs):
+    """The overlapped step on N(0,1) data with planted blocks: scores within the
+    tolerance of the oracle's, the selection equal to a full sort of the GPU's own
+    scores, the plan equal to the oracle's plan on the GPU's own scores and
+    selection, and the attention over the slot table as it was within the tolerance."""
+    w = synth.WORKLOADS["tiny_4k"].with_(block=bs, batch=3, num_kv_heads=2, fetch_ratio=0.25,
+                                         ctx=4096 + 40, min_len=1000, top_k=max(8, 256 // bs))
+    _say(f"overlapped step bs={bs} K={w.top_k}")
+    inp = synth.generate(w, "cpu")
+    d = lib.dims_for(w)
+    lens = inp["seq_lens"].numpy()
+    n_cand = [ref.first_window_block(int(x), w.window, bs) for x in lens]
+    R = torch.stack([torch.stack([synth.random_resident(w.top_k, n_cand[b], 2, 7 * b + h)
+                                  for h in range(w.num_kv_heads)]) for b in range(w.batch)])
+    dev = {key: t.to(DEV) for key, t in inp.items()}
+    summ = lib.build_summaries(d, dev["k"], dev["seq_lens"])
+    rn = torch.empty_like(R).to(DEV)
+    ov = lib.decode_step_overlapped(d, dev["q"], summ, dev["k"], dev["v"], dev["seq_lens"], R.to(DEV), rn,
+                                    default_scale())
+    torch.cuda.synchronize()
+    ov = {key: val.cpu() for key, val in ov.items()}
+    q64, k64, v64 = f64(inp["q"]), f64(inp["k"]), f64(inp["v"])
+    summ64 = ref.build_summaries(k64, lens, bs)
+    assert np.array_equal(f64(summ), summ64)
+    escore = ref.score_blocks(q64, summ64, lens, w.window, bs)
+    check_scores(f64(ov["scores"]), escore, score_floor(q64, summ64), f"bs={bs}")
+    gs = ov["scores"].numpy()
+    esel = ref.topk_blocks(gs, lens, w.top_k, w.window, bs)
+    np.testing.assert_array_equal(i64(ov["topk"]), esel)
+    plan = ref.build_plan(gs.astype(np.float64), esel, i64(R), lens, w.cap, w.window, bs)
+    for key in ("plan", "plan_count", "table", "table_count"):
+        np.testing.assert_array_equal(i64(ov[key]), plan[key], err_msg=key)
+    np.testing.assert_array_equal(i64(rn), plan["resident"])
+    assert int(ov["plan_count"].sum()) > 0
+    table, tc = ref.resident_table(i64(R), lens, w.window, bs)
+    eo, el = ref.sparse_attention(q64, k64, v64, table, tc, lens, default_scale(), bs)
+    np.testing.assert_allclose(f64(ov["out"]), eo, rtol=0, atol=OUT_ATOL)
+    np.testing.assert_allclose(f64(ov["lse"]), el, rtol=0, atol=OUT_ATOL)
+
+
+@pytest.mark.parametrize("bs", BLOCKS)
+@pytest.mark.parametrize("G", [4, 16])
+def test_attention_tables(lib, bs, G):
+    """Attention over compacted tables (random subsets in random order, the
+    partial last block included, padded rows past the count) and over slot tables
+    (empty slots, blocks the window has reached)."""
+    lens = [3000 + 7, 70, 1024]
+    B, H, Q, K, W = len(lens), 2, 2, 20, 48
+    NB = ref.num_blocks(max(lens), bs) + 1
+    _say(f"attention tables bs={bs} G={G}")
+    q, k, v, L = _inputs(200 + bs + G, B, H, G, Q, NB, bs, lens)
+    d = lib.make_dims(B, H, G, NB, Q, K, W, 0.05, block_size=bs)
+    T = 40
+    r = np.random.default_rng(bs * G)
+    table = np.full((B, H, T), -1, dtype=np.int64)
+    tc = np.zeros((B, H), dtype=np.int64)
+    for b in range(B):
+        nb = ref.num_blocks(lens[b], bs)
+        for h in range(H):
+            n = min(T - 3, nb) if h == 0 else min(nb, 5)
+            blocks = r.choice(nb, size=n, replace=False)
+            if nb - 1 not in blocks:
+                blocks[0] = nb - 1                      # the partial last block
+            table[b, h, :n] = blocks
+            tc[b, h] = n
+    scale = default_scale()
+    qd, kd, vd, Ld = q.to(DEV), k.to(DEV), v.to(DEV), L.to(DEV)
+    out, lse = lib.sparse_decode_attn(d, qd, kd, vd, torch.from_numpy(table.astype(np.int32)).to(DEV),
+                                      torch.from_numpy(tc.astype(np.int32)).to(DEV), Ld, scale)
+    R = _slot_tables(300 + bs, B, H, K, lens, bs)
+    rout, rlse = lib.sparse_decode_attn_resident(d, qd, kd, vd, torch.from_numpy(R.astype(np.int32)).to(DEV),
+                                                 Ld, scale)
+    torch.cuda.synchronize()
+    q64, k64, v64 = f64(q), f64(k), f64(v)
+    eo, el = ref.sparse_attention(q64, k64, v64, table, tc, L.numpy(), scale, bs)
+    np.testing.assert_allclose(f64(out), eo, rtol=0, atol=OUT_ATOL)
+    np.testing.assert_allclose(f64(lse), el, rtol=0, atol=OUT_ATOL)
+    rt, rtc = ref.resident_table(R, L.numpy(), W, bs)
+    eo, el = ref.sparse_attention(q64, k64, v64, rt, rtc, L.numpy(), scale, bs)
+    np.testing.assert_allclose(f64(rout), eo, rtol=0, atol=OUT_ATOL)
+    np.testing.assert_allclose(f64(rlse), el, rtol=0, atol=OUT_ATOL)
+
+
+@pytest.mark.parametrize("bs", BLOCKS)
+def test_attention_all_blocks_matches_dense(lib, bs):
+    """A table of every block is dense attention over the sequence (the oracle's pin
+    at any block size): the GPU against dense softmax attention in fp64."""
+    lens = [2000 + 3, 129]
+    B, H, G, Q = len(lens), 2, 4, 1
+    NB = ref.num_blocks(max(lens), bs)
+    _say(f"all blocks vs dense bs={bs}")
+    q, k, v, L = _inputs(400 + bs, B, H, G, Q, NB, bs, lens)
+    d = lib.make_dims(B, H, G, NB, Q, 1, 0, 0.0, block_size=bs)
+    table = torch.arange(NB, dtype=torch.int32).repeat(B, H, 1)
+    tc = torch.tensor([[ref.num_blocks(x, bs)] * H for x in lens], dtype=torch.int32)
+    out, _ = lib.sparse_decode_attn(d, q.to(DEV), k.to(DEV), v.to(DEV), table.to(DEV), tc.to(DEV),
+                                    L.to(DEV), default_scale())
+    torch.cuda.synchronize()
+    for b in range(B):
+        kk = k[b].double().reshape(H, NB * bs, 128)[:, : lens[b]]
+        vv = v[b].double().reshape(H, NB * bs, 128)[:, : lens[b]]
+        qq = q[b, :, :, 0].double()
+        dense = torch.nn.functional.scaled_dot_product_attention(
+            qq[:, :, None], kk[:, None].expand(H, G, -1, -1), vv[:, None].expand(H, G, -1, -1),
+            scale=default_scale())[:, :, 0]
+        np.testing.assert_allclose(f64(out[b]), dense.numpy(), rtol=0, atol=OUT_ATOL)
+
+
+@pytest.mark.parametrize("bs", BLOCKS)
+def test_working_set(lib, bs):
+    """The working set gathered from the full cache equals the oracle's bit for bit;
+    attention over it equals the full-cache slot-table attention bit for bit; the
+    plan's copies leave the pool equal to the gather of the next slot table; tokens
+    appended across block boundaries keep cache, ring and summaries equal to the
+    oracle's."""
+    lens = [1500 + 3, 700]
+    B, H, G, Q, W = len(lens), 2, 4, 3, 40
+    K = max(6, 128 // bs)
+    NB = ref.num_blocks(max(lens), bs) + 2
+    _say(f"working set bs={bs} K={K}")
+    q, k, v, L = _inputs(500 + bs, B, H, G, Q, NB, bs, lens)
+    d = lib.make_dims(B, H, G, NB, Q, K, W, 0.5, block_size=bs)
+    R = _slot_tables(600 + bs, B, H, K, lens, bs, lambda h: 1 + h)
+    Rd = torch.from_numpy(R.astype(np.int32)).to(DEV)
+    kd, vd, Ld = k.to(DEV), v.to(DEV), L.to(DEV)
+    wset = lib.fill_working_set(d, Rd, Ld, kd, vd)
+    out, lse = lib.sparse_decode_attn_pool(d, q.to(DEV), wset, Rd, Ld)
+    alone, alone_lse = lib.sparse_decode_attn_resident(d, q.to(DEV), kd, vd, Rd, Ld)
+    torch.cuda.synchronize()
+    pk, pv, rk, rv = ref.fill_working_set(f64(k), f64(v), R, L.numpy(), W, bs)
+    for name, got, exp in (("pool_k", wset.pool_k, pk), ("pool_v", wset.pool_v, pv),
+                           ("ring_k", wset.ring_k, rk), ("ring_v", wset.ring_v, rv)):
+        assert np.array_equal(f64(got), exp), name
+    assert torch.equal(out, alone) and torch.equal(lse, alone_lse)
+    eo, el = ref.pool_attention(f64(q), pk, pv, rk, rv, R, L.numpy(), W, default_scale(), bs)
+    np.testing.assert_allclose(f64(out), eo, rtol=0, atol=OUT_ATOL)
+
+    # A step's plan, executed: the pool becomes the gather of the next slot table.
+    Rc = R.copy()
+    Rc[Rc >= np.array([ref.first_window_block(x, W, bs) for x in lens])[:, None, None]] = -1
+    Rcd = torch.from_numpy(Rc.astype(np.int32)).to(DEV)
+    summ = lib.build_summaries(d, kd, Ld)
+    bufs = lib.StepBuffers(d, DEV)
+    rn = torch.empty_like(Rcd)
+    lib.decode_step(d, q.to(DEV), summ, kd, vd, Ld, Rcd, default_scale(), buffers=bufs, resident_next=rn)
+    wset2 = lib.fill_working_set(d, Rcd, Ld, kd, vd)
+    lib.execute_plan(d, bufs.plan, bufs.plan_count, kd, vd, wset2)
+    expect = lib.fill_working_set(d, rn, Ld, kd, vd)
+    torch.cuda.synchronize()
+    assert int(bufs.plan_count.sum()) > 0
+    assert torch.equal(wset2.pool_k, expect.pool_k) and torch.equal(wset2.pool_v, expect.pool_v)
+    pk2, pv2, _, _ = ref.fill_working_set(f64(k), f64(v), Rc, L.numpy(), W, bs)
+    ek, ev = ref.execute_plan(pk2, pv2, i64(bufs.plan), i64(bufs.plan_count), f64(k), f64(v))
+    assert np.array_equal(f64(wset2.pool_k), ek) and np.array_equal(f64(wset2.pool_v), ev)
+
+    # Appended tokens: more than a block's worth, so that blocks open and close.
+    ok, ov, os_ = f64(kd), f64(vd), f64(summ)
+    _, _, ork, orv = ref.fill_working_set(ok, ov, Rc, L.numpy(), W, bs)
+    wset3 = lib.fill_working_set(d, Rcd, Ld, kd, vd)
+    g = torch.Generator().manual_seed(bs)
+    for step in range(bs + 5):
+        kn = (torch.randn((B, H, 128), generator=g) * (1 + step % 3)).to(torch.bfloat16)
+        vn = torch.randn((B, H, 128), generator=g).to(torch.bfloat16)
+        lib.append_token(d, kn.to(DEV), vn.to(DEV), Ld, summ, wset3, kd, vd)
+        ok, ov, os_, ork, orv = ref.append_token(ok, ov, os_, ork, orv, f64(kn), f64(vn), i64(Ld), W, bs)
+        Ld += 1
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(summ), os_)
+    assert np.array_equal(f64(wset3.ring_k), ork) and np.array_equal(f64(wset3.ring_v), orv)
+    assert np.array_equal(f64(kd), ok) and np.array_equal(f64(vd), ov)
+    rebuilt = lib.build_summaries(d, kd, Ld)
+    torch.cuda.synchronize()
+    for b in range(B):
+        nb = ref.num_blocks(int(Ld[b]), bs)
+        assert torch.equal(summ[b, :, :nb], rebuilt[b, :, :nb])
+
+
+@pytest.mark.parametrize("bs", BLOCKS)
+def test_full_size_fixed_token_budget(lib, bs):
+    """The Qwen3-8B 32K shape (two sequences, two KV heads) at each block size with
+    the pages' 2048-token budget kept: K = 2048 / bs blocks per KV head."""
+    from tests.test_parity import _full_size_case
+    w = synth.WORKLOADS["qwen3_8b_32k"].with_(batch=2, num_kv_heads=2, block=bs, top_k=2048 // bs)
+    _full_size_case(lib, w)
+
+
+def test_layer_pipelined_sweep_32_token_blocks(lib):
+    """The layer-pipelined sweep at 32-token blocks: every layer's outputs equal its
+    overlapped step's (plan outputs bit for bit, attention up to the merge order)."""
+    w = synth.WORKLOADS["tiny_4k"].with_(block=32, batch=2, num_kv_heads=3, fetch_ratio=0.25,
+                                         ctx=4096 + 40, min_len=1000, top_k=12)
+    _say("layer-pipelined sweep bs=32")
+    d = lib.dims_for(w)
+    layers, expected = [], []
+    for layer in range(3):
+        inp = {key: t.to(DEV) for key, t in synth.generate(w, "cpu", layer=layer).items()}
+        summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
+        n_cand = [ref.first_window_block(int(x), w.window, 32) for x in inp["seq_lens"].cpu()]
+        res = torch.stack([torch.stack([synth.random_resident(w.top_k, n_cand[b], 2, 10 * b + h + layer)
+                                        for h in range(w.num_kv_heads)]) for b in range(w.batch)]).to(DEV)
+        rn = torch.empty_like(res)
+        ov = lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, rn,
+                                        default_scale())
+        torch.cuda.synchronize()
+        expected.append(({key: val.clone() for key, val in ov.items()}, rn.clone()))
+        layers.append((inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res))
+    sweep = lib.PipelinedLayers(d, layers, default_scale())
+    sweep()
+    sweep.drain()
+    torch.cuda.synchronize()
+    for li, (exp, rn) in enumerate(expected):
+        b = sweep.buffers[li]
+        for key in ("scores", "topk", "plan", "plan_count", "table", "table_count"):
+            assert torch.equal(getattr(b, key), exp[key]), f"layer {li}: {key}"
+        assert torch.equal(sweep.resident_next[li], rn)
+        assert (b.out - exp["out"]).abs().max().item() <= 1e-6
