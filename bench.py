@@ -39,6 +39,11 @@ if ROOT not in sys.path:
 METRIC = "sparse decode steps/s per layer + achieved HBM GB/s (% peak), Qwen3-8B 32K"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published peak
 BLOCK_KV_BYTES = 16 * 128 * 2 * 2   # K and V of one 16-token block of one KV head, bf16
+
+
+def block_kv_bytes(block: int) -> int:
+    """K and V of one block of ``block`` tokens of one KV head, bf16."""
+    return block * 128 * 2 * 2
 SUMMARY_BYTES = 2 * 128 * 2         # min and max of one block, bf16
 CALIBRATION_BYTES = 512 << 20       # the --calibrate copy: bytes read and bytes written per copy
 
@@ -52,10 +57,11 @@ def working_set_blocks(w, lens, resident) -> int:
     """Blocks the overlapped step's attention reads: per (sequence, KV head) the
     resident blocks before the first window block plus the window blocks."""
     total = 0
+    bs = w.block
     for b in range(w.batch):
         L = int(lens[b])
-        w0 = max(0, (L - w.window) // 16)
-        nblk = (L + 15) // 16
+        w0 = max(0, (L - w.window) // bs)
+        nblk = (L + bs - 1) // bs
         r = resident[b]
         total += int(((r >= 0) & (r < w0)).sum()) + w.num_kv_heads * (nblk - w0)
     return total
@@ -66,20 +72,21 @@ def algorithmic_bytes(w, lens, table_count) -> dict:
     the queries and the output.  Per kernel as well (inputs plus outputs)."""
     import synth
     H, G, Q = w.num_kv_heads, w.group, w.queries
-    cand = sum(synth.first_window_block(int(x), w.window) for x in lens) * H
+    cand = sum(synth.first_window_block(int(x), w.window, w.block) for x in lens) * H
     blocks = int(table_count) if isinstance(table_count, int) else int(table_count.sum())
+    kvb = block_kv_bytes(w.block)
     q_all = w.batch * H * G * Q * 128 * 2
     q_target = w.batch * H * G * 128 * 2
     out = w.batch * H * G * (128 + 1) * 4
     scores = w.batch * H * w.max_blocks * 4
-    step = cand * SUMMARY_BYTES + blocks * BLOCK_KV_BYTES + q_all + out
+    step = cand * SUMMARY_BYTES + blocks * kvb + q_all + out
     return {
         "step": step,
         "score": cand * SUMMARY_BYTES + q_all + scores,
-        "attn_split": blocks * BLOCK_KV_BYTES + q_target,
-        "score_attn_split": cand * SUMMARY_BYTES + q_all + scores + blocks * BLOCK_KV_BYTES,
+        "attn_split": blocks * kvb + q_target,
+        "score_attn_split": cand * SUMMARY_BYTES + q_all + scores + blocks * kvb,
         "summaries": cand * SUMMARY_BYTES,
-        "kv": blocks * BLOCK_KV_BYTES,
+        "kv": blocks * kvb,
         "units": {"candidate_block_heads": cand, "table_blocks": blocks},
     }
 
@@ -198,11 +205,12 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
 
 def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     """The fp64 oracle on the host: the same step (score, top-K, plan, attention) for
-    (sequence, KV head) units of input set 0, until ``budget_s`` seconds have run,
-    in two modes: as written, one unit after another on one core; then the same
-    oracle mapped over the units by a pool of worker threads, one per core up to
-    16 (numpy leaves the interpreter lock while it works on arrays), for at most
-    ``budget_s`` seconds more."""
+    (sequence, KV head) units, taken from the input sets in turn and round again,
+    until ``budget_s`` seconds of oracle work have run, in two modes: as written,
+    one unit after another on one core; then the same oracle mapped over the units
+    by a pool of worker threads, one per core up to 16 (numpy leaves the
+    interpreter lock while it works on arrays), for ``budget_s`` seconds more.
+    Rates are scaled to whole steps (all units of one set)."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -211,53 +219,51 @@ def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
 
     from oracle import ref
 
-    s0 = sets[0]
-    lens = s0["seq_lens"].cpu()
-    res = s0["resident"].cpu()
-    units = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    per_set = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    units = [(i, b, h) for i in range(len(sets)) for (b, h) in per_set]
     f64 = lambda t: t.to(torch.float64).numpy()
     scale = 1.0 / math.sqrt(128)
     step = ref.decode_step_overlapped if overlapped else ref.decode_step
+    host = [{"lens": st["seq_lens"].cpu(), "res": st["resident"].cpu()} for st in sets]
 
-    def unit_inputs(b, h):
-        return (f64(s0["q"][b:b + 1, h:h + 1].cpu()), f64(s0["summ"][b:b + 1, h:h + 1].cpu()),
-                f64(s0["k"][b:b + 1, h:h + 1].cpu()), f64(s0["v"][b:b + 1, h:h + 1].cpu()),
-                lens[b:b + 1].numpy(), res[b:b + 1, h:h + 1].numpy().astype(np.int64))
+    def unit_inputs(u):
+        i, b, h = units[u % len(units)]
+        st = sets[i]
+        return (f64(st["q"][b:b + 1, h:h + 1].cpu()), f64(st["summ"][b:b + 1, h:h + 1].cpu()),
+                f64(st["k"][b:b + 1, h:h + 1].cpu()), f64(st["v"][b:b + 1, h:h + 1].cpu()),
+                host[i]["lens"][b:b + 1].numpy(), host[i]["res"][b:b + 1, h:h + 1].numpy().astype(np.int64))
 
     def run(x):
         step(*x, w.top_k, w.window, w.cap, scale)
 
     done, elapsed = 0, 0.0
     with threadpool_limits(1):
-        for (b, h) in units:
-            x = unit_inputs(b, h)              # conversion to fp64 is not timed
+        while elapsed < budget_s:
+            x = unit_inputs(done)              # conversion to fp64 is not timed
             t = time.perf_counter()
             run(x)
             elapsed += time.perf_counter() - t
             done += 1
-            if elapsed >= budget_s:
-                break
-    per_step = elapsed / done * len(units)
+    per_step = elapsed / done * len(per_set)
     out = {"value": 1.0 / per_step, "unit": "steps/s", "cores": 1, "kind": "oracle",
-           "sample": f"{done} of {len(units)} (sequence, KV head) units of one step, fp64 numpy, "
-                     f"{elapsed:.1f} s, scaled to a whole step",
+           "sample": f"{done} (sequence, KV head) units ({done / len(per_set):.2f} steps of "
+                     f"{len(per_set)} units, from {len(sets)} input sets in turn), fp64 numpy, "
+                     f"{elapsed:.1f} s of oracle time on one core, scaled to steps",
            "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
 
     workers = max(1, min(16, os.cpu_count() or 1))
     done_p, elapsed_p = 0, 0.0
     with threadpool_limits(1), ThreadPoolExecutor(workers) as pool:
-        for c in range(0, len(units), workers):
-            chunk = [unit_inputs(b, h) for (b, h) in units[c:c + workers]]
+        while elapsed_p < budget_s:
+            chunk = [unit_inputs(done_p + j) for j in range(workers)]
             t = time.perf_counter()
             list(pool.map(run, chunk))
             elapsed_p += time.perf_counter() - t
             done_p += len(chunk)
             del chunk
-            if elapsed_p >= budget_s:
-                break
-    out["pool"] = {"value": done_p / elapsed_p / len(units), "unit": "steps/s", "cores": workers,
+    out["pool"] = {"value": done_p / elapsed_p / len(per_set), "unit": "steps/s", "cores": workers,
                    "kind": "oracle",
-                   "sample": f"{done_p} of {len(units)} units of one step over a pool of {workers} "
+                   "sample": f"{done_p} units ({done_p / len(per_set):.2f} steps) over a pool of {workers} "
                              f"threads, {workers} units at a time, {elapsed_p:.1f} s of wall time"}
     return out
 
@@ -395,13 +401,13 @@ def plan_execution(w, d, sets, buffers, res_next, ms_step: float, stage_us: dict
     # One step of set 0 leaves its plan in the buffers: the copies alone, from HBM.
     dev_steps[0]()
     torch.cuda.synchronize()
-    moved = int(buffers.plan_count.sum()) * BLOCK_KV_BYTES
+    moved = int(buffers.plan_count.sum()) * block_kv_bytes(w.block)
     plan = buffers.plan.clone()
     count = buffers.plan_count.clone()
     copy_dev = oa.PreparedPlanCopy(d, plan, count, sets[0]["k"], sets[0]["v"], wsets[0])
     us_dev = launch_us(copy_dev)
     out["plan_bytes_per_step"] = moved
-    out["plan_bytes_cap"] = w.batch * w.num_kv_heads * w.cap * BLOCK_KV_BYTES
+    out["plan_bytes_cap"] = w.batch * w.num_kv_heads * w.cap * block_kv_bytes(w.block)
     out["copy_device_tier_us"] = round(us_dev, 3)
     out["copy_device_tier_gbps"] = round(moved / (us_dev * 1e-6) / 1e9, 1)
     # The full cache in pinned host memory (first host_sets input sets).
@@ -445,15 +451,21 @@ def plan_execution(w, d, sets, buffers, res_next, ms_step: float, stage_us: dict
     return out
 
 
-SWEEP = [(64, 0.05), (128, 0.05), (192, 0.05),
-         (128, 0.01), (128, 0.02), (128, 0.10), (128, 0.20), (128, 1.0)]
+# (top_k, fetch_ratio, block size): the pages' K and fetch-ratio ablations at 16-token
+# blocks, then other block sizes at the same 2048-token budget (K = 2048 / block).
+SWEEP = [(64, 0.05, 16), (128, 0.05, 16), (192, 0.05, 16),
+         (128, 0.01, 16), (128, 0.02, 16), (128, 0.10, 16), (128, 0.20, 16), (128, 1.0, 16),
+         (256, 0.05, 8), (64, 0.05, 32), (32, 0.05, 64)]
 
 
 def run_sweep(args) -> dict:
     """The pages' ablations at kernel level (K and the fetch ratio) on one workload's
-    inputs: per variant the overlapped step from the full cache in HBM, the step over
-    the working set with the full cache in HBM and in pinned host memory (where the
-    fetch ratio sets the bytes crossing the host link), and the plan's bytes."""
+    inputs, and block sizes other than 16 over the same K/V bytes (the tokens are
+    contiguous, so a cache of 16-token blocks is one of 8-, 32- or 64-token blocks;
+    only the summaries are rebuilt): per variant the overlapped step from the full
+    cache in HBM, the step over the working set with the full cache in HBM and in
+    pinned host memory (where the fetch ratio sets the bytes crossing the host
+    link), and the plan's bytes."""
     import torch
 
     import oasis_score_summaries_amd as oa
@@ -495,36 +507,49 @@ def run_sweep(args) -> dict:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (reps * len(step_list))
 
+    def as_blocks(t, bs):
+        return t.view(t.shape[0], t.shape[1], -1, bs, t.shape[-1])
+
     rows = []
-    for top_k, ratio in SWEEP:
-        w = base.with_(top_k=top_k, fetch_ratio=ratio)
+    for top_k, ratio, bs in SWEEP:
+        w = base.with_(top_k=top_k, fetch_ratio=ratio, block=bs)
         d = oa.dims_for(w)
+        if bs == base.block:
+            vsets, vhosts = sets, hosts
+        else:
+            vsets = [{**st, "k": as_blocks(st["k"], bs), "v": as_blocks(st["v"], bs)} for st in sets]
+            for st in vsets:
+                st["summ"] = oa.build_summaries(d, st["k"], st["seq_lens"])
+            vhosts = [(as_blocks(hk, bs), as_blocks(hv, bs)) for hk, hv in hosts]
         residents = []
-        for i, st in enumerate(sets):
+        for i, st in enumerate(vsets):
             sel = oa.topk_blocks(d, oa.score_summaries(d, st["q_sel"], st["summ"], st["seq_lens"]),
                                  st["seq_lens"])
             residents.append(synth.resident_from_selection(w, sel, st["seq_lens"].cpu(), layer=i).to(dev))
         bufs = oa.StepBuffers(d, dev)
         rn = torch.empty_like(residents[0])
         over = [oa.PreparedStep(d, st["q"], st["summ"], st["k"], st["v"], st["seq_lens"], r, bufs,
-                                resident_next=rn, overlapped=True) for st, r in zip(sets, residents)]
+                                resident_next=rn, overlapped=True) for st, r in zip(vsets, residents)]
         ms_over = graph_ms(over)
-        wsets = [oa.fill_working_set(d, r, st["seq_lens"], st["k"], st["v"]) for st, r in zip(sets, residents)]
+        wsets = [oa.fill_working_set(d, r, st["seq_lens"], st["k"], st["v"]) for st, r in zip(vsets, residents)]
         pool_dev = [oa.PreparedPoolStep(d, st["q"], st["summ"], st["k"], st["v"], ws, st["seq_lens"], r,
-                                        bufs, rn) for st, r, ws in zip(sets, residents, wsets)]
+                                        bufs, rn) for st, r, ws in zip(vsets, residents, wsets)]
         ms_pool_dev = graph_ms(pool_dev)
         pool_host = [oa.PreparedPoolStep(d, st["q"], st["summ"], hk, hv, ws, st["seq_lens"], r, bufs, rn)
-                     for st, r, ws, (hk, hv) in zip(sets, residents, wsets, hosts)]
+                     for st, r, ws, (hk, hv) in zip(vsets, residents, wsets, vhosts)]
         ms_pool_host = graph_ms(pool_host, reps=max(3, int(30 * 0.1 / max(ratio, 0.01))))
         moved = 0
-        for st, r in zip(sets, residents):   # the plan bytes of every set's step
+        table_blocks = 0
+        for st, r in zip(vsets, residents):   # the plan bytes of every set's step
             oa.decode_step_overlapped(d, st["q"], st["summ"], st["k"], st["v"], st["seq_lens"], r, rn,
                                       buffers=bufs)
-            moved += int(bufs.plan_count.sum()) * BLOCK_KV_BYTES
+            moved += int(bufs.plan_count.sum()) * block_kv_bytes(bs)
+            table_blocks += working_set_blocks(w, st["seq_lens"].cpu(), r.cpu())
         torch.cuda.synchronize()
-        pipe = transfer_pipeline(d, [{**st, "resident": r} for st, r in zip(sets, residents)], wsets, hosts,
+        step_bytes = algorithmic_bytes(w, vsets[0]["seq_lens"].cpu(), table_blocks // n_sets)["step"]
+        pipe = transfer_pipeline(d, [{**st, "resident": r} for st, r in zip(vsets, residents)], wsets, vhosts,
                               torch, oa, steps=10)
-        rows.append({"top_k": top_k, "fetch_ratio": ratio, "cap": w.cap,
+        rows.append({"top_k": top_k, "fetch_ratio": ratio, "block_size": bs, "cap": w.cap,
                      "transfer_pipeline_us_per_layer": {k.replace("_us_per_layer", ""): v
                                                      for k, v in pipe.items() if k.endswith("_us_per_layer")},
                      "overlapped_ms_per_step": round(ms_over, 6),
@@ -532,13 +557,14 @@ def run_sweep(args) -> dict:
                      "pool_device_tier_ms_per_step": round(ms_pool_dev, 6),
                      "pool_host_tier_ms_per_step": round(ms_pool_host, 6),
                      "plan_bytes_per_step": moved // n_sets,
-                     "table_blocks_per_head": top_k + (w.window + 15) // 16})
-        del over, pool_dev, pool_host, wsets, bufs, residents
+                     "overlapped_step_bytes": step_bytes,
+                     "overlapped_step_gbps": round(step_bytes / (ms_over * 1e-3) / 1e9, 1),
+                     "table_blocks_per_head": top_k + -(-w.window // bs)})
+        del over, pool_dev, pool_host, wsets, bufs, residents, vsets
         torch.cuda.empty_cache()
-    return {"metric": "variant sweep: step time against top-K and fetch ratio", "workload": base.name,
-            "input_sets": n_sets, "host_tier_input_sets": len(hosts), "block_size": 16,
-            "rows": rows, "data": "synthetic",
-            "note": "block sizes other than 16 are not built (the kernels fix 16-token blocks)"}
+    return {"metric": "variant sweep: step time against top-K, fetch ratio and block size",
+            "workload": base.name, "input_sets": n_sets, "host_tier_input_sets": len(hosts),
+            "rows": rows, "data": "synthetic"}
 
 
 def block_mass_gpu(q_true, k, seq_lens, window: int, scale: float, torch):

@@ -77,3 +77,17 @@ def test_analysis_overlap_matches_the_oracle_definition():
         a = np.concatenate([a, -np.ones(3, dtype=int)])
         b = np.concatenate([b, -np.ones(3, dtype=int)])
         assert bench.top_overlap_rows(a, b, n) == ref.top_overlap(a, b, n)
+
+
+def test_block_bytes_at_every_block_size():
+    """K and V of one block is Eq. (1) at one sequence of `block` tokens, one layer, one
+    KV head; the summaries stay two rows whatever the block size."""
+    import synth
+    for block in (8, 16, 32, 64):
+        assert bench.block_kv_bytes(block) == bench.kv_cache_bytes(1, block, 1, 1, 128, 2)
+    w = synth.WORKLOADS["qwen3_8b_32k"].with_(block=32, top_k=64)
+    lens = [32768] * w.batch
+    nb = bench.algorithmic_bytes(w, lens, 10)
+    cand = (32768 - 128) // 32 * w.batch * w.num_kv_heads
+    assert nb["summaries"] == cand * bench.SUMMARY_BYTES
+    assert nb["kv"] == 10 * 32 * 128 * 2 * 2
