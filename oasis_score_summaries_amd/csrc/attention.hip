@@ -39,7 +39,11 @@ namespace oasis {
 
 // Measured at 8 x 8 heads (32K), 4 x 8 (128K), 32 x 4 with 16 query heads (32K) and
 // 64 x 8 (8K-16K): 2048 keeps one block per wave for the first two (64 and 32 heads)
-// and takes 2 and 4 rounds for the last two, 6-7 % faster steps there.
+// and takes 4 rounds for the 64 x 8 heads, 6-7 % faster steps there.  A split's
+// record grows with the group (528 bytes per query head), so with more than 8 query
+// heads per KV head half as many workgroups suffice: the 32 x 4 heads with 16 query
+// heads each then take 4 rounds instead of 2 (69.5 -> 67.1 us per step; the same
+// threshold at 4 query heads costs 35.7 -> 36.3 us).
 #ifndef OASIS_ATTN_MIN_WGS
 #define OASIS_ATTN_MIN_WGS 2048
 #endif
@@ -58,10 +62,11 @@ AttnSplit attn_split(const Dims& d, int table_stride) {
   // many heads fewer, longer splits save bytes, while the grid keeps at least
   // OASIS_ATTN_MIN_WGS workgroups to hide the gather's latency.
   const int64_t heads = (int64_t)d.batch * d.heads;
+  const int64_t min_wgs = d.group > 8 ? OASIS_ATTN_MIN_WGS / 2 : OASIS_ATTN_MIN_WGS;
   while (s.rounds * 2 <= OASIS_ATTN_MAX_ROUNDS) {
     const int r = s.rounds * 2;
     const int ns = (units + kAttnWaves * r - 1) / (kAttnWaves * r);
-    if (heads * ns < OASIS_ATTN_MIN_WGS) break;
+    if (heads * ns < min_wgs) break;
     s.rounds = r;
   }
   s.num_splits = (units + kAttnWaves * s.rounds - 1) / (kAttnWaves * s.rounds);
