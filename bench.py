@@ -203,6 +203,45 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
     return kernel, "\n".join(head + out + body) + "\n"
 
 
+OCCUPANCY_COUNTERS = ("OccupancyPercent", "MeanOccupancyPerCU", "MfmaUtil", "LDSBankConflict", "SQ_WAVES")
+
+
+def summarize_occupancy(dirs, workload: str, command: str) -> str:
+    """Per-kernel means of rocprofv3's occupancy counters (derived: OccupancyPercent,
+    waves resident per CU over the kernel's busy time (MeanOccupancyPerCU), MfmaUtil,
+    LDSBankConflict; raw: SQ_WAVES) from the counter-collection CSVs of one or more
+    ``--pmc`` runs, as a markdown table for the library's kernels."""
+    import csv
+    import re
+
+    vals = {}
+    for d in dirs:
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            name = r["Kernel_Name"]
+            if "oasis::" not in name or r["Counter_Name"] not in OCCUPANCY_COUNTERS:
+                continue
+            name = re.sub(r"\(.*$", "", re.sub(r"^void ", "", name))
+            vals.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = [f"# Occupancy counters per kernel, {workload}",
+             "",
+             f"Command (one run per counter group): `{command}`",
+             "",
+             "OccupancyPercent = 400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CU_NUM / 32 (waves resident as a "
+             "share of 32 per CU); MeanOccupancyPerCU = waves resident per CU, averaged over the kernel's "
+             "busy cycles; MfmaUtil = % of SIMD cycles with the MFMA unit busy; LDSBankConflict = % of CU "
+             "cycles stalled on LDS bank conflicts; SQ_WAVES = waves launched per dispatch. Means over "
+             "the dispatches of each kernel.",
+             "",
+             "| kernel | dispatches | " + " | ".join(OCCUPANCY_COUNTERS) + " |",
+             "|---|---|" + "---|" * len(OCCUPANCY_COUNTERS)]
+    for name in sorted(vals):
+        c = vals[name]
+        n = max(len(v) for v in c.values())
+        cells = [f"{statistics.mean(c[k]):.1f}" if k in c else "" for k in OCCUPANCY_COUNTERS]
+        lines.append(f"| `{name}` | {n} | " + " | ".join(cells) + " |")
+    return "\n".join(lines) + "\n"
+
+
 def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     """The fp64 oracle on the host: the same step (score, top-K, plan, attention) for
     (sequence, KV head) units, taken from the input sets in turn and round again,
@@ -697,6 +736,9 @@ def main(argv=None) -> int:
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic file from two rocprofv3 --pmc runs of "
                          "'bench.py --calibrate' (FETCH_SIZE, then WRITE_SIZE) and exit")
+    ap.add_argument("--summarize-occupancy", nargs="+", metavar="PMC_DIR",
+                    help="write profiles/occupancy_<workload>.md from rocprofv3 --pmc runs of the "
+                         "occupancy counters")
     ap.add_argument("--counter-command", default="", help="the command recorded in the traffic file")
     ap.add_argument("--quality", action="store_true",
                     help="print one JSON line with the prediction-quality analogue instead of the benchmark")
@@ -705,6 +747,13 @@ def main(argv=None) -> int:
     ap.add_argument("--no-plan-exec", action="store_true",
                     help="skip the working-set measurements (step over the pool, plan copies, host tier)")
     args = ap.parse_args(argv)
+    if args.summarize_occupancy:
+        text = summarize_occupancy(args.summarize_occupancy, args.workload, args.counter_command)
+        path = os.path.join(ROOT, "profiles", f"occupancy_{args.workload}.md")
+        with open(path, "w") as f:
+            f.write(text)
+        print(text)
+        return 0
     if args.summarize_counters:
         kernel, text = summarize_counters(*args.summarize_counters, args.workload, args.counter_command)
         with open(traffic_file(kernel, args.workload), "w") as f:
