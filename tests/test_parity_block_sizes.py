@@ -321,3 +321,65 @@ def test_layer_pipelined_sweep_32_token_blocks(lib):
             assert torch.equal(getattr(b, key), exp[key]), f"layer {li}: {key}"
         assert torch.equal(sweep.resident_next[li], rn)
         assert (b.out - exp["out"]).abs().max().item() <= 1e-6
+
+
+def test_largest_supported_sizes_64_token_blocks(lib):
+    """max_blocks = 32768 at 64-token blocks (a 2M-token context, 512 MiB of K per
+    head: the largest byte offsets the gather forms), K = 1024, a 4096-token window,
+    16 query heads, a cap of 512 and a ragged last block, both step orders.  Scores
+    are checked on sampled blocks, selection, plan and attention on the GPU's own
+    scores and tables."""
+    bs = 64
+    B, H, G, Q, NB, K, W, ratio = 1, 1, 16, 2, 32768, 1024, 4096, 0.5
+    L = NB * bs - 5
+    _say("largest sizes bs=64: generating")
+    g = torch.Generator().manual_seed(78)
+    q = torch.randn((B, H, G, Q, 128), generator=g).to(torch.bfloat16)
+    k = torch.randn((B, H, NB, bs, 128), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, H, NB, bs, 128), generator=g).to(torch.bfloat16)
+    lens = torch.tensor([L], dtype=torch.int32)
+    d = lib.make_dims(B, H, G, NB, Q, K, W, ratio, block_size=bs)
+    C = lib.fetch_cap(d)
+    assert C == 512
+    n_cand = ref.first_window_block(L, W, bs)
+    res = synth.random_resident(K, n_cand, 100, 6).reshape(1, 1, K)
+    qd, kd, vd, ld = q.to(DEV), k.to(DEV), v.to(DEV), lens.to(DEV)
+    summ = lib.build_summaries(d, kd, ld)
+    _say("largest sizes bs=64: serial and overlapped steps")
+    ser = lib.decode_step(d, qd, summ, kd, vd, ld, res.to(DEV).clone(), default_scale())
+    ser = {key: val.cpu() for key, val in ser.items()}
+    rn = torch.empty_like(res).to(DEV)
+    ov = lib.decode_step_overlapped(d, qd, summ, kd, vd, ld, res.to(DEV), rn, default_scale())
+    ov = {key: val.cpu() for key, val in ov.items()}
+    torch.cuda.synchronize()
+    del qd, kd, vd
+    rng = np.random.default_rng(4)
+    blocks = np.sort(rng.choice(n_cand, size=256, replace=False))
+    summ_s = f64(summ[:, :, blocks].cpu())
+    exp_s = ref.score_blocks(f64(q), summ_s, np.array([len(blocks) * bs]), 0, bs)
+    check_scores(f64(ser["scores"][:, :, blocks]), exp_s, score_floor(f64(q), summ_s), "sampled scores")
+    np.testing.assert_array_equal(f64(summ[:, :, blocks[:8]].cpu()),
+                                  ref.build_summaries(f64(k[:, :, blocks[:8]]), np.array([8 * bs]), bs)[:, :, :8])
+    sc = f64(ser["scores"])
+    np.testing.assert_array_equal(f64(ov["scores"]), sc)
+    sel = ref.topk_blocks(sc, lens.numpy(), K, W, bs)
+    np.testing.assert_array_equal(i64(ser["topk"]), sel)
+    plan = ref.build_plan(sc, sel, i64(res), lens.numpy(), C, W, bs)
+    for key in ("plan", "plan_count", "resident", "table", "table_count"):
+        np.testing.assert_array_equal(i64(ser[key]), plan[key], err_msg=key)
+        np.testing.assert_array_equal(i64(ov[key]), plan[key], err_msg=key)
+    assert int(ser["plan_count"][0, 0]) == C
+    _say("largest sizes bs=64: oracle attention")
+    # Only the blocks some table names are widened to fp64; the others stay zero (never read).
+    used = np.union1d(plan["table"][plan["table"] >= 0], ref.resident_table(i64(res), lens.numpy(), W, bs)[0])
+    used = used[used >= 0]
+    kf = np.zeros((B, H, NB, bs, 128))
+    vf = np.zeros((B, H, NB, bs, 128))
+    kf[:, :, used] = f64(k[:, :, used])
+    vf[:, :, used] = f64(v[:, :, used])
+    eo, _ = ref.sparse_attention(f64(q), kf, vf, plan["table"], plan["table_count"], lens.numpy(),
+                                 default_scale(), bs)
+    np.testing.assert_allclose(f64(ser["out"]), eo, rtol=0, atol=OUT_ATOL)
+    table, tc = ref.resident_table(i64(res), lens.numpy(), W, bs)
+    eo2, _ = ref.sparse_attention(f64(q), kf, vf, table, tc, lens.numpy(), default_scale(), bs)
+    np.testing.assert_allclose(f64(ov["out"]), eo2, rtol=0, atol=OUT_ATOL)
