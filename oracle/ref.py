@@ -351,6 +351,45 @@ def block_attention_mass(q_true: np.ndarray, k: np.ndarray, seq_lens: np.ndarray
     return out
 
 
+def captured_attention(q_true: np.ndarray, k: np.ndarray, seq_lens: np.ndarray, window: int,
+                       scale: float, selection: np.ndarray, block: int = 16) -> np.ndarray:
+    """Share of the true query's attention over the candidate blocks that a
+    selection holds, per KV head, averaged over the query heads of the group.
+
+    For query head g of (b, h): the softmax of scale * q_true[b,h,g] . k_t over
+    every valid token t, summed over the tokens of the selected candidate blocks,
+    divided by the same sum over all candidate blocks (the window is attended in
+    any case).  Unlike a block overlap it counts tokens, so selections of equal
+    token budget made at different block sizes compare on one scale.  [xllm]
+    section four, Figures 4 and 6 measure how well the look-ahead finds the
+    blocks the next token needs; this is the attention those blocks carry.
+    Reading: a head with no candidate block counts as fully captured (1.0).
+
+    q_true: [B, H, G, d]; k: [B, H, NB, block, d]; selection: [B, H, K] block
+    ids (-1 and ids outside the candidates are ignored).  Returns [B, H].
+    """
+    B, H, NB, bs, d = k.shape
+    G = q_true.shape[2]
+    out = np.ones((B, H))
+    for b in range(B):
+        L = int(seq_lens[b])
+        n_cand = first_window_block(L, window, block)
+        if L <= 0 or n_cand == 0:
+            continue
+        flat = k[b].reshape(H, NB * bs, d)[:, :L]
+        for h in range(H):
+            sel = np.unique([int(j) for j in selection[b, h] if 0 <= j < n_cand]).astype(np.int64)
+            fractions = []
+            for g in range(G):
+                z = flat[h] @ q_true[b, h, g] * scale
+                p = np.exp(z - z.max())
+                p /= p.sum()
+                per_block = np.add.reduceat(p, np.arange(0, L, bs))[:n_cand]
+                fractions.append(per_block[sel].sum() / per_block.sum())
+            out[b, h] = float(np.mean(fractions))
+    return out
+
+
 def top_overlap(pred: np.ndarray, true: np.ndarray, n: int) -> float:
     """|first n of pred & first n of true| / n for two rankings (block ids, best
     first, -1 padded); 1.0 when both are empty."""

@@ -873,3 +873,69 @@ def test_append_token_matches_a_rebuild_other_block_sizes(block):
             for j in range(ref.first_window_block(L, W, block), ref.num_blocks(L, block)):
                 n = min(block, L - block * j)
                 np.testing.assert_array_equal(rk[b, :, j % WB, :n], ek[b, :, j % WB, :n])
+
+
+# ---------------------------------------------------------------------------
+# Captured attention (the quality figure compared across block sizes)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("block", [8, 16, 32, 64])
+def test_captured_attention_pins(block):
+    """All candidates capture everything, none capture nothing, disjoint selections
+    add, and identical keys spread the attention evenly over the tokens; with one
+    query head it is the block shares of block_attention_mass, normalised."""
+    r = _rng(80 + block)
+    B, H, G, d = 2, 2, 3, 16
+    NB = 512 // block
+    q = _bf16(r.standard_normal((B, H, G, d)))
+    k = _bf16(r.standard_normal((B, H, NB, block, d)))
+    lens = np.array([512, 300])
+    W, scale = 40, 1 / math.sqrt(d)
+    n_cand = [ref.first_window_block(int(x), W, block) for x in lens]
+    everything = np.full((B, H, NB), -1)
+    for b in range(B):
+        everything[b, :, :n_cand[b]] = np.arange(n_cand[b])
+    np.testing.assert_allclose(ref.captured_attention(q, k, lens, W, scale, everything, block), 1.0,
+                               rtol=0, atol=1e-12)
+    nothing = np.full((B, H, 4), -1)
+    assert np.all(ref.captured_attention(q, k, lens, W, scale, nothing, block) == 0.0)
+    # ids outside the candidates (window, past the sequence) are ignored
+    beyond = np.full((B, H, 2), NB + 3)
+    beyond[:, :, 0] = [[n_cand[0]] * H, [n_cand[1]] * H]
+    assert np.all(ref.captured_attention(q, k, lens, W, scale, beyond, block) == 0.0)
+    for b in range(B):
+        perm = r.permutation(n_cand[b])
+        a, c = perm[: len(perm) // 3], perm[len(perm) // 3:]
+        sa = np.full((B, H, len(perm)), -1)
+        sc = np.full((B, H, len(perm)), -1)
+        sa[b, :, :len(a)] = a
+        sc[b, :, :len(c)] = c
+        fa = ref.captured_attention(q, k, lens, W, scale, sa, block)[b]
+        fc = ref.captured_attention(q, k, lens, W, scale, sc, block)[b]
+        np.testing.assert_allclose(fa + fc, 1.0, rtol=0, atol=1e-12)
+    same = np.broadcast_to(k[:, :, :1, :1], k.shape).copy()         # one key everywhere
+    sel = np.full((B, H, 3), -1)
+    sel[:, :, :3] = [0, 2, 3]
+    got = ref.captured_attention(q, same, lens, W, scale, sel, block)
+    for b in range(B):
+        np.testing.assert_allclose(got[b], 3 * block / (n_cand[b] * block), rtol=0, atol=1e-12)
+    q1 = q[:, :, :1]
+    mass = ref.block_attention_mass(q1, k, lens, W, scale, block)
+    got1 = ref.captured_attention(q1, k, lens, W, scale, sel, block)
+    for b in range(B):
+        for h in range(H):
+            m = mass[b, h, :n_cand[b]]
+            np.testing.assert_allclose(got1[b, h], m[[0, 2, 3]].sum() / m.sum(), rtol=1e-12)
+
+
+def test_captured_attention_by_hand():
+    """Two blocks of two tokens, one query head: the shares come from the softmax
+    written out by hand."""
+    q = np.array([[[[1.0, 0.0]]]])                        # [1, 1, 1, 2]
+    k = np.array([[[[[0.0, 0.0], [1.0, 0.0]], [[2.0, 0.0], [0.0, 5.0]], [[9.0, 9.0], [9.0, 9.0]]]]])
+    lens = np.array([5])                                  # window 1 token: block 2 is the window
+    e = np.exp([0.0, 1.0, 2.0, 0.0, 9.0])
+    p = e / e.sum()
+    cand = p[0] + p[1] + p[2] + p[3]
+    got = ref.captured_attention(q, k, lens, 1, 1.0, np.array([[[1, -1]]]), 2)
+    np.testing.assert_allclose(got[0, 0], (p[2] + p[3]) / cand, rtol=1e-14)

@@ -63,6 +63,11 @@ MUTATIONS = {
     "attention_assumes_16_token_blocks": ("for t in range(block) if j * block + t < L]",
                                           "for t in range(min(block, 16)) if j * block + t < L]"),
     "summaries_stride_assumes_16": ("n_valid = min(bs, L - j * bs)", "n_valid = min(bs, L - j * 16)"),
+    "captured_over_all_attention": ("fractions.append(per_block[sel].sum() / per_block.sum())",
+                                    "fractions.append(per_block[sel].sum())"),
+    "captured_best_of_the_group": ("out[b, h] = float(np.mean(fractions))", "out[b, h] = float(np.max(fractions))"),
+    "captured_counts_window_blocks": ("for j in selection[b, h] if 0 <= j < n_cand]",
+                                      "for j in selection[b, h] if 0 <= j < NB]"),
     "overlap_divides_by_union": ("return 1.0 if m == 0 else len(a & b) / m",
                                  "return 1.0 if m == 0 else len(a & b) / len(a | b)"),
 }
