@@ -606,30 +606,56 @@ def run_sweep(args) -> dict:
             "rows": rows, "data": "synthetic"}
 
 
-def block_mass_gpu(q_true, k, seq_lens, window: int, scale: float, torch):
+def block_shares_gpu(q_true, k, seq_lens, window: int, scale: float, torch):
     """Analysis, not the decode path: each candidate block's share of the true
-    query's softmax over all valid tokens, largest over the group ([B, H, NB] fp32,
-    -inf outside the candidates); the definition of the oracle's block_attention_mass,
-    in fp32 torch on the device."""
-    B, H, NB = k.shape[:3]
-    T = NB * 16
+    query's softmax over all valid tokens, per query head ([B, H, G, NB] fp32, 0
+    outside the candidates), in fp32 torch on the device; k is [B, H, NB, bs, 128]."""
+    B, H, NB, bs = k.shape[:4]
+    G = q_true.shape[2]
+    T = NB * bs
     lens = seq_lens.to(torch.int64)
     tok = torch.arange(T, device=k.device)
     blk = torch.arange(NB, device=k.device)
-    out = torch.empty((B, H, NB), dtype=torch.float32, device=k.device)
+    out = torch.empty((B, H, G, NB), dtype=torch.float32, device=k.device)
     for b in range(B):
         kf = k[b].reshape(H, T, 128).float()                                # [H, T, d]
         qt = q_true[b].float().transpose(-1, -2).contiguous()               # [H, d, G]
         z = torch.matmul(kf, qt).transpose(-1, -2) * scale                  # [H, G, T]
         z = z.masked_fill(tok >= lens[b], float("-inf"))
         p = torch.softmax(z, dim=-1)
-        share = p.reshape(H, -1, NB, 16).sum(-1).amax(1)                    # [H, NB]
-        n_cand = max(0, (int(lens[b]) - window) // 16)
-        out[b] = share.masked_fill(blk >= n_cand, float("-inf"))
+        share = p.reshape(H, G, NB, bs).sum(-1)                             # [H, G, NB]
+        n_cand = max(0, (int(lens[b]) - window) // bs)
+        out[b] = share.masked_fill(blk >= n_cand, 0.0)
     return out
 
 
+def block_mass_gpu(q_true, k, seq_lens, window: int, scale: float, torch):
+    """Each candidate block's share, largest over the group ([B, H, NB] fp32, -inf
+    outside the candidates): the definition of the oracle's block_attention_mass."""
+    bs = k.shape[3]
+    shares = block_shares_gpu(q_true, k, seq_lens, window, scale, torch).amax(2)
+    n_cand = ((seq_lens.to(torch.int64) - window).clamp(min=0) // bs)[:, None, None]
+    blk = torch.arange(k.shape[2], device=k.device)
+    return shares.masked_fill(blk >= n_cand, float("-inf"))
+
+
+def captured_gpu(shares, selection, seq_lens, window: int, torch):
+    """Share of each query head's candidate attention held by the selected blocks,
+    averaged over the group ([B, H]): the definition of the oracle's
+    captured_attention on shares from block_shares_gpu (block size from the shares'
+    candidates: ids past them carry 0)."""
+    NB = shares.shape[-1]
+    sel = selection.to(torch.int64)
+    ok = (sel >= 0) & (sel < NB)
+    idx = sel.clamp(0, NB - 1)[:, :, None, :].expand(-1, -1, shares.shape[2], -1)
+    got = (torch.gather(shares, -1, idx) * ok[:, :, None, :]).sum(-1)     # [B, H, G]
+    tot = shares.sum(-1)
+    frac = torch.where(tot > 0, got / torch.where(tot > 0, tot, torch.ones_like(tot)), torch.ones_like(tot))
+    return frac.mean(2)
+
+
 QUALITY_NOISE = (0.1, 0.3, 0.6, 1.0)
+QUALITY_BLOCKS = (8, 16, 32, 64)
 
 
 def prediction_quality(args) -> dict:
@@ -643,7 +669,12 @@ def prediction_quality(args) -> dict:
     Reported per noise level s: top-20 accuracy against the 20 largest attention
     shares, top-K agreement with the K largest, and top-K agreement with the set the
     true query itself selects (the same selection fed the true query), averaged over
-    heads and layers (the input sets)."""
+    heads and layers (the input sets).  Then, per block size at the workload's token
+    budget (K = K_16 * 16 / bs, the same K/V bytes viewed as blocks of bs tokens, the
+    same noisy rows at s = 0.3): the share of each query head's attention over the
+    candidates that the selected blocks hold (captured attention), for the same
+    predictors and for the best selection the true shares allow (the K blocks of
+    largest share, largest over the group)."""
     import torch
 
     import oasis_score_summaries_amd as oa
@@ -653,8 +684,11 @@ def prediction_quality(args) -> dict:
     w = synth.WORKLOADS[args.workload]
     scale = 1.0 / math.sqrt(128)
     K, D = w.top_k, 4
+    budget = K * w.block
     gen = torch.Generator(device=dev).manual_seed(20260)
+    gen_b = torch.Generator(device=dev).manual_seed(20261)   # the block-size rows' own draws
     acc = {}
+    by_block = {}
 
     def predict(rows, inp, summ):
         Q = rows.shape[3]
@@ -673,9 +707,9 @@ def prediction_quality(args) -> dict:
         valid = torch.isfinite(torch.gather(mass, -1, true_rank.long()))
         true_rank = torch.where(valid, true_rank, torch.full_like(true_rank, -1)).cpu().numpy()
 
-        def noisy(n, s):
+        def noisy(n, s, g=gen):
             x = q_true.float().unsqueeze(3).expand(-1, -1, -1, n, -1)
-            return (x + s * torch.randn(x.shape, generator=gen, device=dev)).to(torch.bfloat16)
+            return (x + s * torch.randn(x.shape, generator=g, device=dev)).to(torch.bfloat16)
 
         preds = {"exact": predict(q_true.unsqueeze(3), inp, summ)}
         for s in QUALITY_NOISE:
@@ -683,6 +717,31 @@ def prediction_quality(args) -> dict:
             preds[f"lookahead@{s}"] = predict(drafts, inp, summ)
             preds[f"proxy@{s}"] = predict(proxy, inp, summ)
             preds[f"proxy+lookahead@{s}"] = predict(torch.cat([proxy, drafts], dim=3), inp, summ)
+        # Block sizes at one token budget, one set of noisy rows.
+        s_b = 0.3
+        drafts_b, proxy_b = noisy(D, s_b, gen_b), noisy(1, s_b, gen_b)
+        rows_b = {"exact": q_true.unsqueeze(3), f"lookahead@{s_b}": drafts_b, f"proxy@{s_b}": proxy_b,
+                  f"proxy+lookahead@{s_b}": torch.cat([proxy_b, drafts_b], dim=3)}
+        for bs in QUALITY_BLOCKS:
+            Kb = budget // bs
+            kb = inp["k"].view(w.batch, w.num_kv_heads, -1, bs, 128)
+            db = oa.make_dims(w.batch, w.num_kv_heads, w.group, kb.shape[2], 1, Kb, w.window,
+                              w.fetch_ratio, block_size=bs)
+            summ_b = oa.build_summaries(db, kb, inp["seq_lens"])
+            shares = block_shares_gpu(q_true, kb, inp["seq_lens"], w.window, scale, torch)
+            best = block_mass_gpu(q_true, kb, inp["seq_lens"], w.window, scale, torch)
+            top = torch.topk(best, Kb, dim=-1)
+            sels = {"best possible": torch.where(torch.isfinite(top.values), top.indices,
+                                                 torch.full_like(top.indices, -1))}
+            for name, rows in rows_b.items():
+                dq = oa.make_dims(w.batch, w.num_kv_heads, w.group, kb.shape[2], rows.shape[3], Kb,
+                                  w.window, w.fetch_ratio, block_size=bs)
+                sc = oa.score_summaries(dq, rows.contiguous(), summ_b, inp["seq_lens"])
+                sels[name] = oa.topk_blocks(dq, sc, inp["seq_lens"])
+            for name, sel in sels.items():
+                frac = captured_gpu(shares, sel, inp["seq_lens"], w.window, torch)
+                by_block.setdefault(bs, {}).setdefault(name, []).append(float(frac.mean()))
+            del summ_b, shares, best
         exact_sel = preds["exact"].cpu().numpy()
         for name, sel in preds.items():
             sel = sel.cpu().numpy()
@@ -702,9 +761,14 @@ def prediction_quality(args) -> dict:
                    "topk_min_layer": round(min(v["topk"]), 4),
                    "agreement_with_true_query_selection": round(statistics.mean(v["sel"]), 4),
                    "selection_min_layer": round(min(v["sel"]), 4)} for name, v in acc.items()}
+    captured = {str(bs): {"top_k": budget // bs,
+                          "captured_attention": {name: round(statistics.mean(v), 4) for name, v in c.items()},
+                          "captured_min_layer": {name: round(min(v), 4) for name, v in c.items()}}
+                for bs, c in by_block.items()}
     return {"metric": "look-ahead prediction quality (synthetic analogue)", "workload": w.name,
             "layers": layers, "top_k": K, "drafts": D, "noise_levels": list(QUALITY_NOISE),
-            "predictors": rows, "data": "synthetic"}
+            "predictors": rows, "token_budget": budget, "captured_attention_by_block_size": captured,
+            "data": "synthetic"}
 
 
 def top_overlap_rows(pred, true, n: int) -> float:
