@@ -432,7 +432,7 @@ typedef struct {
  * selection outputs are valid after the next call returns its launches to the
  * stream order.  Up to K = 256, 2048 blocks per head, 4 query heads and 32 query
  * rows per KV head, the previous layer's selection shares this layer's first
- * launch; otherwise it is a launch of its own before it. */
+ * launch; otherwise it shares this layer's second launch, with the merge. */
 oasis_status oasis_decode_layer_pipelined(const oasis_dims* dims, const oasis_layer_io* layer,
                                           const oasis_layer_io* previous, float scale,
                                           hipStream_t stream);

@@ -96,6 +96,13 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void select_
   }
 }
 
+static hipError_t launch_first_half(const Dims& d, const AttnSplit& s, const void* q, const void* summ,
+                                    const void* k, const void* v, const int32_t* seq_lens,
+                                    float* scores, const int32_t* resident, float scale, void* ws,
+                                    hipStream_t stream, const WorkingSet* pool);
+static hipError_t launch_second_half(const Dims& d, const AttnSplit& s, const TopkPlanArgs& sel,
+                                     const void* ws, float* out, float* lse, hipStream_t stream);
+
 // The shared launch also needs up to 4 query heads per KV head: the selection's LDS
 // on top of larger attention partials would leave fewer than four workgroups per CU.
 static bool pipelined_fits(const Dims& d) {
@@ -147,32 +154,25 @@ hipError_t launch_pipelined_layer(const Dims& d, const LayerIO* cur, const Layer
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   } else {
-    // Larger shapes: the previous layer's selection and plan as their own launch, then
-    // this layer's launch 1.
-    if (prev != nullptr &&
-        (err = launch_topk_plan(d, prev->scores, prev->seq_lens, prev->topk, prev->resident,
-                                prev->resident_next, prev->plan, prev->plan_count, prev->table,
-                                prev->table_count, stream)) != hipSuccess)
+    // Larger shapes: this layer's launch 1 as in the overlapped step, and the previous
+    // layer's selection and plan (its scores are complete) with this layer's merge as
+    // launch 2 -- two launches per layer, as in the overlapped step.
+    if ((err = launch_first_half(d, s, cur->q, cur->summ, cur->k, cur->v, cur->seq_lens, cur->scores,
+                                 cur->resident, scale, cur->ws, stream, nullptr)) != hipSuccess)
       return err;
-    if ((err = launch_score(d, cur->q, cur->summ, cur->seq_lens, cur->scores, stream)) != hipSuccess)
-      return err;
-    if ((err = launch_attention_split(d, s, cur->q, cur->k, cur->v, cur->resident, nullptr,
-                                      d.table_stride, cur->seq_lens, scale, cur->ws, stream, true)) !=
-        hipSuccess)
-      return err;
+    if (prev != nullptr) return launch_second_half(d, s, ta, cur->ws, cur->out, cur->lse, stream);
   }
   return launch_attention_merge(d, s, cur->out, cur->lse, cur->ws, stream);
 }
 
-hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ, const void* k,
-                                  const void* v, const int32_t* seq_lens, float* scores,
-                                  int32_t* topk, const int32_t* resident, int32_t* resident_next,
-                                  int32_t* plan, int32_t* plan_count, int32_t* table,
-                                  int32_t* table_count, float scale, float* out, float* lse,
-                                  void* ws, hipStream_t stream, hipEvent_t after_first,
-                                  const WorkingSet* pool, bool execute_plan) {
+// Launch 1 of a step: the scoring of every candidate block into `scores` and the
+// attention's split partials over `resident` and the window into `ws`, in one grid
+// up to OASIS_FUSED_MAX_RT row tiles, else back to back.
+static hipError_t launch_first_half(const Dims& d, const AttnSplit& s, const void* q, const void* summ,
+                                    const void* k, const void* v, const int32_t* seq_lens,
+                                    float* scores, const int32_t* resident, float scale, void* ws,
+                                    hipStream_t stream, const WorkingSet* pool) {
   const int heads = d.batch * d.heads;
-  const AttnSplit s = attn_split(d, d.table_stride);
   const ScoreArgs sa = score_args(d, q, summ, seq_lens, scores);
   AttnArgs aa = attn_args(d, s, q, pool ? pool->pool_k : k, pool ? pool->pool_v : v, resident,
                           nullptr, d.table_stride, seq_lens, scale, ws);
@@ -231,22 +231,41 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
       if (e != hipSuccess) return e;
     }
   }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (after_first != nullptr && (err = hipEventRecord(after_first, stream)) != hipSuccess) return err;
+  return hipGetLastError();
+}
 
-  const TopkPlanArgs ta = topk_plan_args(d, scores, seq_lens, topk, resident, resident_next, plan,
-                                         plan_count, table, table_count);
+// Launch 2 of a step: the selection and plan of `sel` (any layer whose scores are
+// complete) and the merge of the partials in `ws` into out, lse, in one grid.
+static hipError_t launch_second_half(const Dims& d, const AttnSplit& s, const TopkPlanArgs& sel,
+                                     const void* ws, float* out, float* lse, hipStream_t stream) {
+  const int heads = d.batch * d.heads;
   const int grid2 = heads + heads * d.group;
 #define OASIS_SM_CASE(T, I)                                                                    \
   case I:                                                                                      \
-    select_merge_kernel<T, I><<<dim3(grid2), dim3(T), 0, stream>>>(ta, (const float*)ws,       \
+    select_merge_kernel<T, I><<<dim3(grid2), dim3(T), 0, stream>>>(sel, (const float*)ws,      \
                                                                    d.group, s.num_splits, out, \
                                                                    lse, heads);                \
     break;
   OASIS_SELECT_DISPATCH(OASIS_SM_CASE);
 #undef OASIS_SM_CASE
-  hipError_t err2 = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ, const void* k,
+                                  const void* v, const int32_t* seq_lens, float* scores,
+                                  int32_t* topk, const int32_t* resident, int32_t* resident_next,
+                                  int32_t* plan, int32_t* plan_count, int32_t* table,
+                                  int32_t* table_count, float scale, float* out, float* lse,
+                                  void* ws, hipStream_t stream, hipEvent_t after_first,
+                                  const WorkingSet* pool, bool execute_plan) {
+  const AttnSplit s = attn_split(d, d.table_stride);
+  hipError_t err = launch_first_half(d, s, q, summ, k, v, seq_lens, scores, resident, scale, ws, stream,
+                                     pool);
+  if (err != hipSuccess) return err;
+  if (after_first != nullptr && (err = hipEventRecord(after_first, stream)) != hipSuccess) return err;
+  const TopkPlanArgs ta = topk_plan_args(d, scores, seq_lens, topk, resident, resident_next, plan,
+                                         plan_count, table, table_count);
+  hipError_t err2 = launch_second_half(d, s, ta, ws, out, lse, stream);
   if (err2 != hipSuccess || pool == nullptr || !execute_plan) return err2;
   // The attention has read the pool (launch 1), so the admitted blocks can take
   // their slots now.

@@ -690,7 +690,7 @@ def test_graph_replay_matches_eager(lib, overlapped):
 @pytest.mark.parametrize("group,queries", [(4, 5), (8, 2)])
 def test_layer_pipelined_sweep_matches_the_overlapped_step(lib, group, queries):
     """Three layers, two decode steps with each layer's selection in the next layer's
-    first launch (group 8: the selection as a launch of its own): every layer's plan
+    first launch (group 8: in the second launch, with the merge): every layer's plan
     outputs equal the overlapped step's bit for bit, its attention equals it up to
     the merge's summation order and matches the oracle."""
     w = synth.WORKLOADS["tiny_4k"].with_(batch=2, num_kv_heads=3, group=group, num_drafts=queries - 1,
