@@ -131,7 +131,8 @@ def traffic_file(kernel: str, workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
 
 
-KERNEL_SOURCES = ("fused.hip", "score_impl.h", "attention_impl.h", "select_impl.h", "common.h", "launch.h")
+KERNEL_SOURCES = ("fused.hip", "attention.hip", "score_impl.h", "attention_impl.h", "select_impl.h", "common.h",
+                  "launch.h")
 
 
 def kernel_sources_sha256() -> str:
