@@ -42,6 +42,27 @@ __host__ __device__ inline int first_window_block(int len, int window, int bshif
   return x > 0 ? x >> bshift : 0;
 }
 
+// ---- workgroup placement ---------------------------------------------------------
+// The dispatcher deals workgroups to the eight XCDs in turn (workgroup i to XCD
+// i % 8), each XCD with its own L2.  Item i of a role with gx items per head and nh
+// heads maps to (x, head): head-major in the plain order, or, with `by_xcd` and nh a
+// multiple of 8 (and the role's first workgroup index too), with every item of a
+// head on one XCD, so that the head's queries are fetched into one L2 instead of
+// eight.  Measured: 2 % faster steps at 80 query rows per KV head (20 KB of queries
+// per head), 0.5 % slower at 20 rows and 32 x 8 heads, 14 % slower at 20 rows and
+// 4 x 8 heads of 8192 blocks; the host asks for it from 64 query rows on.
+__device__ inline void xcd_item(int i, int gx, int nh, bool by_xcd, int& x, int& head) {
+  if (by_xcd && (nh & 7) == 0) {
+    const int j = i >> 3;
+    head = (j / gx) * 8 + (i & 7);
+    x = j % gx;
+    return;
+  }
+  x = i % gx;
+  head = i / gx;
+}
+__host__ inline bool place_by_xcd(int query_rows) { return query_rows >= 64; }
+
 // ---- bf16 bit helpers -------------------------------------------------------------
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -38,17 +38,20 @@ static_assert(kScoreWaves == kAttnWaves, "one workgroup size for both roles");
 template <int RT, int GP, bool POOL = false>
 __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void score_attn_kernel(ScoreArgs sa, AttnArgs aa,
                                                                              int n_score, int score_gx,
-                                                                             int attn_gx) {
+                                                                             int attn_gx, int by_xcd) {
   __shared__ union {
     ScoreShared<RT> s;
     AttnShared<GP> a;
   } sh;
   const int b = blockIdx.x;
+  const int nh = n_score / score_gx;  // (sequence, KV head) pairs
+  int x, head;
   if (b < n_score) {
-    score_wg<RT>(b % score_gx, b / score_gx, sh.s, sa);
+    xcd_item(b, score_gx, nh, by_xcd, x, head);
+    score_wg<RT>(x, head, sh.s, sa);
   } else {
-    const int i = b - n_score;
-    attn_split_wg<GP, true, POOL>(i % attn_gx, i / attn_gx, sh.a, aa);
+    xcd_item(b - n_score, attn_gx, nh, by_xcd, x, head);
+    attn_split_wg<GP, true, POOL>(x, head, sh.a, aa);
   }
 }
 
@@ -75,7 +78,8 @@ __global__ __launch_bounds__(THREADS) void select_merge_kernel(TopkPlanArgs ta, 
 // first, as they run longest, in 256 threads, so K <= 256 and at most 2048 blocks.
 template <int RT, int GP, int ITEMS>
 __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void select_score_attn_kernel(
-    TopkPlanArgs prev, ScoreArgs sa, AttnArgs aa, int n_sel, int n_score, int score_gx, int attn_gx) {
+    TopkPlanArgs prev, ScoreArgs sa, AttnArgs aa, int n_sel, int n_score, int score_gx, int attn_gx,
+    int by_xcd) {
   __shared__ union {
     ScoreShared<RT> s;
     AttnShared<GP> a;
@@ -87,12 +91,15 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void select_
     topk_plan_wg<kScoreThreads, ITEMS>(b, sh.t, bm, prev);
     return;
   }
-  const int c = b - n_sel;
+  const int c = b - n_sel;  // n_sel is 0 or the number of heads
+  const int nh = n_score / score_gx;
+  int x, head;
   if (c < n_score) {
-    score_wg<RT>(c % score_gx, c / score_gx, sh.s, sa);
+    xcd_item(c, score_gx, nh, by_xcd, x, head);
+    score_wg<RT>(x, head, sh.s, sa);
   } else {
-    const int i = c - n_score;
-    attn_split_wg<GP, true>(i % attn_gx, i / attn_gx, sh.a, aa);
+    xcd_item(c - n_score, attn_gx, nh, by_xcd, x, head);
+    attn_split_wg<GP, true>(x, head, sh.a, aa);
   }
 }
 
@@ -141,7 +148,7 @@ hipError_t launch_pipelined_layer(const Dims& d, const LayerIO* cur, const Layer
 #define OASIS_SSA_CASE(RT, I)                                                                  \
   case RT * 100 + I:                                                                           \
     select_score_attn_kernel<RT, 4, I><<<dim3(grid), dim3(64 * kAttnWaves), 0, stream>>>(      \
-        ta, sa, aa, n_sel, n_score, score_gx, attn_gx);                                        \
+        ta, sa, aa, n_sel, n_score, score_gx, attn_gx, place_by_xcd(d.group * d.queries));     \
     break;
 #define OASIS_SSA_ROW(RT) \
   OASIS_SSA_CASE(RT, 1) OASIS_SSA_CASE(RT, 2) OASIS_SSA_CASE(RT, 4) OASIS_SSA_CASE(RT, 8)
@@ -186,6 +193,7 @@ static hipError_t launch_first_half(const Dims& d, const AttnSplit& s, const voi
   const int grid1 = n_score + attn_gx * heads;
   const int rt = (d.group * d.queries + 15) / 16;
   const int gp = d.group <= 4 ? 4 : (d.group <= 8 ? 8 : 16);
+  const int xcd = place_by_xcd(d.group * d.queries);
   // Up to OASIS_FUSED_MAX_RT row tiles the scoring work shares the grid with the
   // attention's gathering; otherwise the two kernels run back to back.
   switch (rt <= OASIS_FUSED_MAX_RT ? rt * 100 + gp : 0) {
@@ -193,10 +201,10 @@ static hipError_t launch_first_half(const Dims& d, const AttnSplit& s, const voi
   case RT * 100 + GP:                                                                          \
     if (pool)                                                                                  \
       score_attn_kernel<RT, GP, true><<<dim3(grid1), dim3(64 * kAttnWaves), 0, stream>>>(     \
-          sa, aa, n_score, score_gx, attn_gx);                                                 \
+          sa, aa, n_score, score_gx, attn_gx, xcd);                                            \
     else                                                                                       \
       score_attn_kernel<RT, GP><<<dim3(grid1), dim3(64 * kAttnWaves), 0, stream>>>(           \
-          sa, aa, n_score, score_gx, attn_gx);                                                 \
+          sa, aa, n_score, score_gx, attn_gx, xcd);                                            \
     break;
     OASIS_SA_CASE(1, 4)
     OASIS_SA_CASE(1, 8)
