@@ -342,13 +342,14 @@ def layer_pipelined(d, sets, ms_step: float, torch, oa, reps: int = 100) -> dict
             "overlapped_step_us": round(ms_step * 1e3, 3)}
 
 
-def transfer_pipeline(d, sets, wsets, hosts, torch, oa, steps: int = 20) -> dict:
+def transfer_pipeline(d, sets, wsets, hosts, torch, oa, steps: int = 20, streams=None) -> dict:
     """The input sets as the layers of one decode step, the full cache in pinned host
     memory: every layer's step over its working set with the plan's copies on the
     same stream, against the copies on a transfer stream that each layer's next step
     waits for (the pages' per-layer background transfer), and the foreground alone
     (no copies).  Eager launches; per-layer buffers; layer i copies from host buffer
-    i mod 2 (the same bytes)."""
+    i mod 2 (the same bytes).  ``streams`` = (foreground, transfer) to reuse across calls
+    (new ones otherwise)."""
     dev = torch.device("cuda:0")
     L = len(sets)
     per = []
@@ -360,7 +361,7 @@ def transfer_pipeline(d, sets, wsets, hosts, torch, oa, steps: int = 20) -> dict
                                         st["resident"], bufs, rn),
                     oa.PreparedStep(d, st["q"], st["summ"], st["k"], st["v"], st["seq_lens"],
                                     st["resident"], bufs, resident_next=rn, overlapped=True)))
-    fg, tr = torch.cuda.Stream(), torch.cuda.Stream()
+    fg, tr = streams if streams is not None else (torch.cuda.Stream(), torch.cuda.Stream())
     done = [torch.cuda.Event() for _ in range(L)]
 
     def run(mode):
@@ -551,6 +552,7 @@ def run_sweep(args) -> dict:
         return t.view(t.shape[0], t.shape[1], -1, bs, t.shape[-1])
 
     rows = []
+    pipe_streams = (torch.cuda.Stream(), torch.cuda.Stream())   # one pair for every variant
     for top_k, ratio, bs in SWEEP:
         w = base.with_(top_k=top_k, fetch_ratio=ratio, block=bs)
         d = oa.dims_for(w)
@@ -588,7 +590,7 @@ def run_sweep(args) -> dict:
         torch.cuda.synchronize()
         step_bytes = algorithmic_bytes(w, vsets[0]["seq_lens"].cpu(), table_blocks // n_sets)["step"]
         pipe = transfer_pipeline(d, [{**st, "resident": r} for st, r in zip(vsets, residents)], wsets, vhosts,
-                              torch, oa, steps=10)
+                                 torch, oa, steps=10, streams=pipe_streams)
         rows.append({"top_k": top_k, "fetch_ratio": ratio, "block_size": bs, "cap": w.cap,
                      "transfer_pipeline_us_per_layer": {k.replace("_us_per_layer", ""): v
                                                      for k, v in pipe.items() if k.endswith("_us_per_layer")},

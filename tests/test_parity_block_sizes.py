@@ -383,3 +383,78 @@ def test_largest_supported_sizes_64_token_blocks(lib):
     table, tc = ref.resident_table(i64(res), lens.numpy(), W, bs)
     eo2, _ = ref.sparse_attention(f64(q), kf, vf, table, tc, lens.numpy(), default_scale(), bs)
     np.testing.assert_allclose(f64(ov["out"]), eo2, rtol=0, atol=OUT_ATOL)
+
+
+@pytest.mark.parametrize("bs,tier", [(8, "device"), (32, "host"), (64, "device")])
+def test_decode_loop_over_the_working_set(lib, bs, tier):
+    """Four decode steps over the working set, each followed by an appended token:
+    every output equals the full-cache overlapped step's bit for bit and the pool
+    holds the next slot table's blocks afterwards; then a captured step over the
+    working set replays bit-exactly."""
+    w = synth.WORKLOADS["tiny_4k"].with_(block=bs, batch=3, num_kv_heads=2, fetch_ratio=0.25,
+                                         ctx=4096 + 40, min_len=1000, top_k=max(8, 256 // bs))
+    _say(f"decode loop over the working set bs={bs} {tier}")
+    inp = {key: t.to(DEV) for key, t in synth.generate(w, "cpu").items()}
+    d = lib.dims_for(w)
+    kd, vd, Ld = inp["k"].clone(), inp["v"].clone(), inp["seq_lens"].clone()
+    summ = lib.build_summaries(d, kd, Ld)
+    n_cand = [ref.first_window_block(int(x), w.window, bs) for x in Ld.cpu()]
+    R = torch.stack([torch.stack([synth.random_resident(w.top_k, n_cand[b], 2, 9 * b + h)
+                                  for h in range(w.num_kv_heads)]) for b in range(w.batch)]).to(DEV)
+    if tier == "host":
+        hk, hv = kd.cpu().pin_memory(), vd.cpu().pin_memory()
+        src_k, src_v = hk, hv
+    else:
+        src_k, src_v = kd, vd
+    wset = lib.fill_working_set(d, R, Ld, src_k, src_v)
+    g = torch.Generator().manual_seed(bs)
+    for step in range(4):
+        rn_pool, rn_full = torch.empty_like(R), torch.empty_like(R)
+        pool_out = {key: t.clone() for key, t in
+                    lib.decode_step_pool(d, inp["q"], summ, src_k, src_v, wset, Ld, R, rn_pool).items()}
+        full_out = lib.decode_step_overlapped(d, inp["q"], summ, kd, vd, Ld, R, rn_full)
+        torch.cuda.synchronize()
+        for key in ("scores", "topk", "plan", "plan_count", "table", "table_count", "out", "lse"):
+            assert torch.equal(pool_out[key], full_out[key]), f"step {step}: {key}"
+        assert torch.equal(rn_pool, rn_full)
+        expect = lib.fill_working_set(d, rn_full, Ld, kd, vd)
+        torch.cuda.synchronize()
+        assert torch.equal(wset.pool_k, expect.pool_k) and torch.equal(wset.pool_v, expect.pool_v)
+        kn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.bfloat16).to(DEV)
+        vn = torch.randn((w.batch, w.num_kv_heads, 128), generator=g).to(torch.bfloat16).to(DEV)
+        lib.append_token(d, kn, vn, Ld, summ, wset, kd, vd)
+        if tier == "host":
+            lib.append_token(d, kn, vn, Ld, summ.clone(), lib.WorkingSet(d, DEV), hk, hv)
+        torch.cuda.synchronize()
+        Ld += 1
+        R = rn_full
+    # A captured step over the working set: before the eager step and before every
+    # replay the working set is gathered again for R (the step's copies move the
+    # admitted blocks into it), so every replay must equal the eager step, pool included.
+    bufs = lib.StepBuffers(d, DEV)
+    rn = torch.empty_like(R)
+    st = lib.PreparedPoolStep(d, inp["q"], summ, src_k, src_v, wset, Ld, R, bufs, rn)
+    lib.fill_working_set(d, R, Ld, src_k, src_v, wset)
+    st()
+    torch.cuda.synchronize()
+    eager = {**{key: t.clone() for key, t in bufs.as_dict().items()}, "resident": rn.clone(),
+             "pool_k": wset.pool_k.clone(), "pool_v": wset.pool_v.clone()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st()
+    for rep in range(3):
+        for t in list(bufs.as_dict().values()) + [rn]:
+            t.fill_(-7 if t.dtype == torch.int32 else float("nan"))
+        lib.fill_working_set(d, R, Ld, src_k, src_v, wset)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {**bufs.as_dict(), "resident": rn, "pool_k": wset.pool_k, "pool_v": wset.pool_v}
+        for key in eager:
+            assert torch.equal(eager[key], got[key]), f"replay {rep}: {key}"
