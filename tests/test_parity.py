@@ -440,7 +440,7 @@ def test_variant_sweep_shapes(lib, top_k, ratio):
     _full_size_case(lib, w)
 
 
-@pytest.mark.parametrize("layer", [0, 35])
+@pytest.mark.parametrize("layer", [0, 17, 35])
 def test_full_size_reasoning_layer(lib, layer):
     _full_size_case(lib, synth.WORKLOADS["reasoning_36l"], layer=layer)
 
