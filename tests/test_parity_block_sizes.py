@@ -458,3 +458,41 @@ def test_decode_loop_over_the_working_set(lib, bs, tier):
         got = {**bufs.as_dict(), "resident": rn, "pool_k": wset.pool_k, "pool_v": wset.pool_v}
         for key in eager:
             assert torch.equal(eager[key], got[key]), f"replay {rep}: {key}"
+
+
+@pytest.mark.parametrize("bs", BLOCKS)
+def test_no_candidates_and_short_sequences(lib, bs):
+    """Lengths at or below the window, a single token, a length one past a block
+    boundary and zero window tokens: nothing (or one block) to score; the table is
+    the window alone (or the partial last block), both step orders."""
+    for W, lens in ((128, [100, 1, 128]), (0, [1, bs + 1, 3 * bs])):
+        B, H, G, Q, K = len(lens), 2, 4, 2, 4
+        NB = max(ref.num_blocks(max(lens), bs) + 1, K)
+        _say(f"short sequences bs={bs} W={W} lens={lens}")
+        q, k, v, L = _inputs(90 + bs + W, B, H, G, Q, NB, bs, lens)
+        d = lib.make_dims(B, H, G, NB, Q, K, W, 1.0, block_size=bs)
+        resident = torch.full((B, H, K), -1, dtype=torch.int32)
+        kd, Ld = k.to(DEV), L.to(DEV)
+        summ = lib.build_summaries(d, kd, Ld)
+        got = lib.decode_step(d, q.to(DEV), summ, kd, v.to(DEV), Ld, resident.to(DEV), default_scale())
+        rn = torch.empty_like(resident).to(DEV)
+        ov = lib.decode_step_overlapped(d, q.to(DEV), summ, kd, v.to(DEV), Ld, resident.to(DEV), rn,
+                                        default_scale())
+        torch.cuda.synchronize()
+        got = {key: val.cpu() for key, val in got.items()}
+        ov = {key: val.cpu() for key, val in ov.items()}
+        for b in range(B):
+            for h in range(H):
+                exp = oracle_head(q, k, v, L, resident[b, h].numpy(), K, W, d_cap(d), default_scale(),
+                                  b, h, bs)
+                for key in PLAN_KEYS:
+                    np.testing.assert_array_equal(i64(got[key][b, h]), exp[key], err_msg=f"{key} b={b}")
+                    if key != "resident":
+                        np.testing.assert_array_equal(i64(ov[key][b, h]), exp[key], err_msg=f"{key} b={b}")
+                np.testing.assert_allclose(f64(got["out"][b, h]), exp["out"], rtol=0, atol=OUT_ATOL)
+                # with an empty slot table the overlapped step attends over the window alone
+                table, tc = ref.resident_table(resident[b:b + 1, h:h + 1].numpy(), L[b:b + 1].numpy(), W, bs)
+                eo, _ = ref.sparse_attention(f64(q[b:b + 1, h:h + 1]), f64(k[b:b + 1, h:h + 1]),
+                                             f64(v[b:b + 1, h:h + 1]), table, tc, L[b:b + 1].numpy(),
+                                             default_scale(), bs)
+                np.testing.assert_allclose(f64(ov["out"][b, h]), eo[0, 0], rtol=0, atol=OUT_ATOL)
