@@ -21,7 +21,7 @@
 // per-head resource whose range check turns a masked load (past the table, an
 // invalid id, a block past the sequence) into zeros without a memory access.
 //
-// Per block, per wave (G <= 16 query heads padded to 16 MFMA columns):
+// Per 16-token unit, per wave (G <= 16 query heads padded to 16 MFMA columns):
 //   S^T = K (16 tokens x 128) . q^T           4 x v_mfma_f32_16x16x32_bf16
 //   O^T += V^T (128 x 16 tokens) . P^T        2 x 8 x v_mfma_f32_16x16x16_bf16
 // bf16 K and q multiply exactly.  Each fp32 probability p enters the PV product
@@ -38,7 +38,7 @@
 namespace oasis {
 
 // Measured at 8 x 8 heads (32K), 4 x 8 (128K), 32 x 4 with 16 query heads (32K) and
-// 64 x 8 (8K-16K): 2048 keeps one block per wave for the first two (64 and 32 heads)
+// 64 x 8 (8K-16K): 2048 keeps one 16-token unit per wave for the first two (64 and 32 heads)
 // and takes 4 rounds for the 64 x 8 heads, 6-7 % faster steps there.  A split's
 // record grows with the group (528 bytes per query head), so with more than 8 query
 // heads per KV head half as many workgroups suffice: the 32 x 4 heads with 16 query
