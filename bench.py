@@ -243,6 +243,18 @@ def summarize_occupancy(dirs, workload: str, command: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo where there is one)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     """The fp64 oracle on the host: the same step (score, top-K, plan, attention) for
     (sequence, KV head) units, taken from the input sets in turn and round again,
@@ -289,7 +301,7 @@ def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
            "sample": f"{done} (sequence, KV head) units ({done / len(per_set):.2f} steps of "
                      f"{len(per_set)} units, from {len(sets)} input sets in turn), fp64 numpy, "
                      f"{elapsed:.1f} s of oracle time on one core, scaled to steps",
-           "cpu": platform.processor() or platform.machine(), "host_cpus": os.cpu_count()}
+           "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 
     workers = max(1, min(16, os.cpu_count() or 1))
     done_p, elapsed_p = 0, 0.0
