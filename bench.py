@@ -320,12 +320,13 @@ def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     return out
 
 
-def layer_pipelined(d, sets, ms_step: float, torch, oa, reps: int = 100) -> dict:
+def layer_pipelined(d, sets, ms_step: float, torch, oa, reps: int = 100, step_bytes: int = 0) -> dict:
     """The input sets as the layers of a decode step, each layer's selection and plan
     riding in the next layer's first launch (oasis_decode_layer_pipelined): the
     steady-state time per layer of a whole sweep (graph replay; the first layer of a
     replay selects the previous replay's last layer).  Every layer still does its
-    whole step; only where its selection runs changes."""
+    whole step; only where its selection runs changes.  With ``step_bytes`` (one
+    layer's algorithmic bytes) also the per-layer rate against the HBM peak."""
     sweep = oa.PipelinedLayers(d, [(s["q"], s["summ"], s["k"], s["v"], s["seq_lens"], s["resident"])
                                    for s in sets])
     for _ in range(3):
@@ -350,8 +351,13 @@ def layer_pipelined(d, sets, ms_step: float, torch, oa, reps: int = 100) -> dict
     us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
     sweep.drain()
     torch.cuda.synchronize()
-    return {"us_per_layer": round(us, 3), "layers": len(sets), "layers_per_s": round(1e6 / us, 1),
-            "overlapped_step_us": round(ms_step * 1e3, 3)}
+    out = {"us_per_layer": round(us, 3), "layers": len(sets), "layers_per_s": round(1e6 / us, 1),
+           "overlapped_step_us": round(ms_step * 1e3, 3)}
+    if step_bytes:
+        gbps = step_bytes / (us * 1e-6) / 1e9
+        out["hbm"] = {"achieved": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                      "bytes_per_layer": step_bytes}
+    return out
 
 
 def transfer_pipeline(d, sets, wsets, hosts, torch, oa, steps: int = 20, streams=None) -> dict:
@@ -1050,7 +1056,7 @@ def main(argv=None) -> int:
         "setup_s": round(setup_s, 1),
         "checks": check,
     }
-    result["layer_pipelined"] = layer_pipelined(d, sets, ms_per_step, torch, oa)
+    result["layer_pipelined"] = layer_pipelined(d, sets, ms_per_step, torch, oa, step_bytes=nb["step"])
     if not args.no_plan_exec:
         result["plan_execution"] = plan_execution(w, d, sets, buffers, res_next, ms_per_step, stage_us,
                                                   torch, oa)
