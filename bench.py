@@ -703,6 +703,9 @@ def prediction_quality(args) -> dict:
 
     dev = torch.device("cuda:0")
     w = synth.WORKLOADS[args.workload]
+    boost = getattr(args, "boost", None)
+    if boost is not None:   # sensitivity: a stronger planted shift concentrates the attention
+        w = w.with_(boost=float(boost))
     scale = 1.0 / math.sqrt(128)
     K, D = w.top_k, 4
     budget = K * w.block
@@ -787,7 +790,7 @@ def prediction_quality(args) -> dict:
                           "captured_min_layer": {name: round(min(v), 4) for name, v in c.items()}}
                 for bs, c in by_block.items()}
     return {"metric": "look-ahead prediction quality (synthetic analogue)", "workload": w.name,
-            "layers": layers, "top_k": K, "drafts": D, "noise_levels": list(QUALITY_NOISE),
+            "planted_boost": w.boost, "layers": layers, "top_k": K, "drafts": D, "noise_levels": list(QUALITY_NOISE),
             "predictors": rows, "token_budget": budget, "captured_attention_by_block_size": captured,
             "data": "synthetic"}
 
@@ -825,6 +828,8 @@ def main(argv=None) -> int:
                     help="write profiles/occupancy_<workload>.md from rocprofv3 --pmc runs of the "
                          "occupancy counters")
     ap.add_argument("--counter-command", default="", help="the command recorded in the traffic file")
+    ap.add_argument("--boost", type=float, default=None,
+                    help="with --quality: the planted blocks' key shift in place of the workload's")
     ap.add_argument("--quality", action="store_true",
                     help="print one JSON line with the prediction-quality analogue instead of the benchmark")
     ap.add_argument("--sweep", action="store_true",
