@@ -146,7 +146,7 @@ def test_overlapped_step(lib, bs):
 
 
 @pytest.mark.parametrize("bs", BLOCKS)
-@pytest.mark.parametrize("G", [4, 16])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_attention_tables(lib, bs, G):
     """Attention over compacted tables (random subsets in random order, the
     partial last block included, padded rows past the count) and over slot tables
@@ -496,3 +496,39 @@ def test_no_candidates_and_short_sequences(lib, bs):
                                              f64(v[b:b + 1, h:h + 1]), table, tc, L[b:b + 1].numpy(),
                                              default_scale(), bs)
                 np.testing.assert_allclose(f64(ov["out"][b, h]), eo[0, 0], rtol=0, atol=OUT_ATOL)
+
+
+@pytest.mark.parametrize("bs", [8, 64])
+def test_copy_and_append_edge_cases(lib, bs):
+    """Plan rows out of range are skipped and the rest copied (whole blocks of bs
+    tokens); with a cap of 0 the copy is a no-op; a sequence at capacity takes no
+    appended token while the other takes it at its position."""
+    B, H, G, Q, NB, K, W = 2, 2, 4, 1, 8, 4, 2 * bs
+    q, k, v, L = _inputs(61 + bs, B, H, G, Q, NB, bs, [NB * bs, 3 * bs + 2])
+    kd, vd, Ld = k.to(DEV), v.to(DEV), L.to(DEV)
+    d = lib.make_dims(B, H, G, NB, Q, K, W, 0.5, block_size=bs)                    # cap 2
+    R = torch.tensor([[[0, 1, 2, -1]] * H] * B, dtype=torch.int32, device=DEV)
+    wset = lib.fill_working_set(d, R, Ld, kd, vd)
+    before_k, before_v = wset.pool_k.clone(), wset.pool_v.clone()
+    plan = torch.tensor([[[[3, 5, -1], [9, 6, 0]], [[0, 99, 0], [1, -4, 1]]],
+                         [[[2, 7, 2], [-1, 4, 1]], [[3, 2, -1], [3, 3, -1]]]], dtype=torch.int32, device=DEV)
+    count = torch.tensor([[2, 2], [1, 2]], dtype=torch.int32, device=DEV)
+    lib.execute_plan(d, plan, count, kd, vd, wset)
+    torch.cuda.synchronize()
+    exp_k, exp_v = before_k.clone(), before_v.clone()
+    for (b, h, slot, blk) in [(0, 0, 3, 5), (1, 0, 2, 7), (1, 1, 3, 2), (1, 1, 3, 3)]:
+        exp_k[b, h, slot], exp_v[b, h, slot] = kd[b, h, blk], vd[b, h, blk]
+    assert torch.equal(wset.pool_k, exp_k) and torch.equal(wset.pool_v, exp_v)
+    d0 = lib.make_dims(B, H, G, NB, Q, K, W, 0.1, block_size=bs)                   # cap 0
+    lib.execute_plan(d0, torch.empty((B, H, 0, 3), dtype=torch.int32, device=DEV), count, kd, vd, wset)
+    summ = lib.build_summaries(d, kd, Ld)
+    s0, r0, k0 = summ.clone(), wset.ring_k.clone(), kd.clone()
+    kn = torch.randn((B, H, 128)).to(torch.bfloat16).to(DEV)
+    lib.append_token(d, kn, kn, Ld, summ, wset, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(wset.pool_k, exp_k)
+    assert torch.equal(summ[0], s0[0]) and torch.equal(kd[0], k0[0]) and torch.equal(wset.ring_k[0], r0[0])
+    pos = 3 * bs + 2
+    assert torch.equal(kd[1, :, pos // bs, pos % bs], kn[1])             # the other sequence took it
+    WB = lib.window_ring_slots(d)
+    assert torch.equal(wset.ring_k[1, :, (pos // bs) % WB, pos % bs], kn[1])
