@@ -687,15 +687,15 @@ def test_graph_replay_matches_eager(lib, overlapped):
             assert torch.equal(eager[key], got[key]), f"replay {rep}: {key}"
 
 
-@pytest.mark.parametrize("group,queries", [(4, 5), (8, 2)])
-def test_layer_pipelined_sweep_matches_the_overlapped_step(lib, group, queries):
+@pytest.mark.parametrize("group,queries,ctx", [(4, 5, 4096 + 40), (8, 2, 4096 + 40), (4, 5, 2048 * 16 + 40)])
+def test_layer_pipelined_sweep_matches_the_overlapped_step(lib, group, queries, ctx):
     """Three layers, two decode steps with each layer's selection in the next layer's
-    first launch (group 8: in the second launch, with the merge): every layer's plan
-    outputs equal the overlapped step's bit for bit, its attention equals it up to
-    the merge's summation order and matches the oracle."""
+    first launch (group 8, or more than 2048 blocks: in its second launch, with the
+    merge): every layer's plan outputs equal the overlapped step's bit for bit, its
+    attention equals it up to the merge's summation order and matches the oracle."""
     w = synth.WORKLOADS["tiny_4k"].with_(batch=2, num_kv_heads=3, group=group, num_drafts=queries - 1,
-                                         fetch_ratio=0.25, ctx=4096 + 40, min_len=1000)
-    _say(f"layer-pipelined sweep group={group}")
+                                         fetch_ratio=0.25, ctx=ctx, min_len=1000)
+    _say(f"layer-pipelined sweep group={group} ctx={ctx}")
     d = lib.dims_for(w)
     layers, expected = [], []
     for layer in range(3):
