@@ -77,3 +77,33 @@ def test_resident_from_selection_recipes():
 def test_random_scores_distinct():
     s = synth.random_scores((4, 2048), seed=3)
     assert s.dtype == torch.float32 and torch.unique(s).numel() == s.numel()
+
+
+def test_block_sizes_shapes_planting_and_resident_sets():
+    """At 8-, 32- and 64-token blocks: K/V carry blocks of that size, planted blocks sit
+    among that size's candidates, and a resident set built from a selection holds
+    distinct candidate blocks only."""
+    for bs in (8, 32, 64):
+        w = synth.WORKLOADS["tiny_4k"].with_(block=bs, batch=2, ctx=2048 + 40, min_len=1000,
+                                             top_k=max(4, 256 // bs), planted=6)
+        inp = synth.generate(w, "cpu")
+        NB = w.max_blocks
+        assert NB == -(-(2048 + 40) // bs)
+        assert inp["k"].shape == (2, w.num_kv_heads, NB, bs, 128)
+        assert inp["v"].shape == inp["k"].shape
+        assert w.table_stride == w.top_k + -(-w.window // bs) + 1
+        for b in range(2):
+            n_cand = synth.first_window_block(int(inp["seq_lens"][b]), w.window, bs)
+            assert not inp["planted"][b, :, n_cand:].any()
+            assert torch.all(inp["planted"][b].sum(-1) == min(w.planted, n_cand))
+        sel = torch.stack([torch.stack([torch.arange(w.top_k, dtype=torch.int32) * 2
+                                        for _ in range(w.num_kv_heads)]) for _ in range(2)])
+        res = synth.resident_from_selection(w.with_(resident="swap", resident_swaps=1), sel,
+                                            inp["seq_lens"])
+        for b in range(2):
+            n_cand = synth.first_window_block(int(inp["seq_lens"][b]), w.window, bs)
+            r = res[b]
+            assert torch.all((r == -1) | ((r >= 0) & (r < n_cand)))
+            for h in range(w.num_kv_heads):
+                vals = [int(x) for x in r[h] if x >= 0]
+                assert len(vals) == len(set(vals))
