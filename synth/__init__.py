@@ -8,13 +8,14 @@ plan, no attention -- so that the CPU oracle and the HIP path can both take
 their inputs from here without sharing any computation.
 
 Shapes follow the decode-step problem statement of the OasisKV pages (batch B,
-context L, N_kv KV heads, GQA group G, head dim d_h = 128, 16-token blocks,
+context L, N_kv KV heads, GQA group G, head dim d_h = 128, blocks of bs tokens
+(16 by default; 8, 32 and 64 as a variant),
 top-K blocks per KV head, fetch ratio); see the xllm-io paper review,
 section six (default parameters: block size 16, K = 128 blocks per KV head).
 
 Layouts (all contiguous, head-major):
   q, q_prev : bf16 [B, N_kv, G, Q, 128]   Q = 1 + drafts; index 0 is the target
-  k, v      : bf16 [B, N_kv, NB, 16, 128] NB = ceil(L / 16) blocks per sequence
+  k, v      : bf16 [B, N_kv, NB, bs, 128] NB = ceil(L / bs) blocks per sequence
   seq_lens  : int32 [B]
   planted   : bool [B, N_kv, NB]          blocks that received a key boost
 """
