@@ -59,7 +59,7 @@ def test_cpu_baseline_both_modes_on_the_tiny_workload():
     resident = torch.full((w.batch, w.num_kv_heads, w.top_k), -1, dtype=torch.int32)
     sets = [{"q": inp["q"], "k": inp["k"], "v": inp["v"], "seq_lens": inp["seq_lens"],
              "summ": torch.from_numpy(summ).to(torch.bfloat16), "resident": resident}]
-    out = bench.cpu_baseline(w, sets, budget_s=5.0, overlapped=True)
+    out = bench.cpu_baseline(w, sets, budget_s=1.0, overlapped=True)
     assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
     assert out["pool"]["value"] > 0 and 1 <= out["pool"]["cores"] <= 16
     assert np.isfinite(out["pool"]["value"])
@@ -91,3 +91,50 @@ def test_block_bytes_at_every_block_size():
     cand = (32768 - 128) // 32 * w.batch * w.num_kv_heads
     assert nb["summaries"] == cand * bench.SUMMARY_BYTES
     assert nb["kv"] == 10 * 32 * 128 * 2 * 2
+
+
+def _counter_csv(path, rows):
+    import csv
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        wr.writeheader()
+        for i, (kernel, counter, value) in enumerate(rows):
+            wr.writerow({"Dispatch_Id": i, "Kernel_Name": kernel, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_summarize_counters_scales_by_the_calibration_copy(tmp_path):
+    """Bytes per launch = the counter's mean (KiB) x 1024 x the scale that makes the
+    512 MiB calibration copy read (write) 512 MiB; the file carries the sources' hash."""
+    launch = "void oasis::score_attn_kernel<2, 4, false>(oasis::ScoreArgs, oasis::AttnArgs, int, int, int, int)"
+    copy = "__amd_rocclr_copyBuffer"
+    fetch_dir, write_dir = str(tmp_path / "f"), str(tmp_path / "w")
+    _counter_csv(fetch_dir, [(copy, "FETCH_SIZE", 262144.0)] * 3 + [(copy, "FETCH_SIZE", 4.0)]
+                 + [(launch, "FETCH_SIZE", 1000.0), (launch, "FETCH_SIZE", 3000.0)])
+    _counter_csv(write_dir, [(copy, "WRITE_SIZE", 524288.0)] * 3
+                 + [(launch, "WRITE_SIZE", 10.0), (launch, "WRITE_SIZE", 30.0)])
+    kernel, text = bench.summarize_counters(fetch_dir, write_dir, "qwen3_8b_32k", "cmd")
+    assert kernel == "score_attn_kernel"
+    kv = dict(line.split(" = ", 1) for line in text.splitlines() if " = " in line and not line.startswith("#"))
+    assert int(kv["fetch_bytes_per_launch"]) == 2000 * 1024 * 2       # mean 2000 KiB, scale 2
+    assert int(kv["write_bytes_per_launch"]) == 20 * 1024             # mean 20 KiB, scale 1
+    assert int(kv["traffic_bytes_per_launch"]) == 2000 * 1024 * 2 + 20 * 1024
+    assert kv["sources_sha256"] == bench.kernel_sources_sha256() and kv["workload"] == "qwen3_8b_32k"
+
+
+def test_summarize_occupancy_means_per_kernel(tmp_path):
+    a, b = str(tmp_path / "a"), str(tmp_path / "b")
+    k1 = "void oasis::score_attn_kernel<2, 4, false>(oasis::ScoreArgs, oasis::AttnArgs, int, int, int, int)"
+    k2 = "oasis::attn_merge_kernel(float const*, int, int, float*, float*)"
+    _counter_csv(a, [(k1, "OccupancyPercent", 20.0), (k1, "OccupancyPercent", 30.0),
+                     (k1, "MeanOccupancyPerCU", 8.0), (k2, "OccupancyPercent", 3.0),
+                     ("other_kernel", "OccupancyPercent", 99.0)])
+    _counter_csv(b, [(k1, "SQ_WAVES", 13056.0), (k2, "MfmaUtil", 0.0)])
+    text = bench.summarize_occupancy([a, b], "qwen3_8b_32k", "cmd")
+    rows = {line.split("|")[1].strip(): [c.strip() for c in line.split("|")[2:-1]]
+            for line in text.splitlines() if line.startswith("| `")}
+    assert set(rows) == {"`oasis::score_attn_kernel<2, 4, false>`", "`oasis::attn_merge_kernel`"}
+    r1 = rows["`oasis::score_attn_kernel<2, 4, false>`"]
+    assert r1[0] == "2" and r1[1] == "25.0" and r1[2] == "8.0" and r1[5] == "13056.0"
+    r2 = rows["`oasis::attn_merge_kernel`"]
+    assert r2[1] == "3.0" and r2[3] == "0.0"
