@@ -138,3 +138,12 @@ def test_summarize_occupancy_means_per_kernel(tmp_path):
     assert r1[0] == "2" and r1[1] == "25.0" and r1[2] == "8.0" and r1[5] == "13056.0"
     r2 = rows["`oasis::attn_merge_kernel`"]
     assert r2[1] == "3.0" and r2[3] == "0.0"
+
+
+def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
+    """--gpus above 1 (or a multi-rank launch) ends with a message and status 2 before any
+    device work: no multi-GPU path is built."""
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "exactly one GPU" in capsys.readouterr().err
+    monkeypatch.setenv("WORLD_SIZE", "8")
+    assert bench.main([]) == 2
