@@ -41,9 +41,10 @@ namespace oasis {
 // 64 x 8 (8K-16K): 2048 keeps one 16-token unit per wave for the first two (64 and 32 heads)
 // and takes 4 rounds for the 64 x 8 heads, 6-7 % faster steps there.  A split's
 // record grows with the group (528 bytes per query head), so with more than 8 query
-// heads per KV head half as many workgroups suffice: the 32 x 4 heads with 16 query
-// heads each then take 4 rounds instead of 2 (69.5 -> 67.1 us per step; the same
-// threshold at 4 query heads costs 35.7 -> 36.3 us).
+// heads per KV head a quarter of the workgroups suffice and splits run up to 8 rounds:
+// the 32 x 4 heads with 16 query heads each take 8 rounds instead of 2 (step 69.5 ->
+// 67.1 us at 4 rounds, 66.3-66.8 -> 65.8-66.1 us at 8; the gathering alone 36.0 ->
+// 33.0 us).  Half the threshold at 4 query heads made that step slower (35.7 -> 36.3 us).
 #ifndef OASIS_ATTN_MIN_WGS
 #define OASIS_ATTN_MIN_WGS 2048
 #endif
@@ -62,8 +63,10 @@ AttnSplit attn_split(const Dims& d, int table_stride) {
   // many heads fewer, longer splits save bytes, while the grid keeps at least
   // OASIS_ATTN_MIN_WGS workgroups to hide the gather's latency.
   const int64_t heads = (int64_t)d.batch * d.heads;
-  const int64_t min_wgs = d.group > 8 ? OASIS_ATTN_MIN_WGS / 2 : OASIS_ATTN_MIN_WGS;
-  while (s.rounds * 2 <= OASIS_ATTN_MAX_ROUNDS) {
+  const bool big_group = d.group > 8;
+  const int64_t min_wgs = big_group ? OASIS_ATTN_MIN_WGS / 4 : OASIS_ATTN_MIN_WGS;
+  const int max_rounds = big_group ? 2 * OASIS_ATTN_MAX_ROUNDS : OASIS_ATTN_MAX_ROUNDS;
+  while (s.rounds * 2 <= max_rounds) {
     const int r = s.rounds * 2;
     const int ns = (units + kAttnWaves * r - 1) / (kAttnWaves * r);
     if (heads * ns < min_wgs) break;
