@@ -761,3 +761,38 @@ def test_pipelined_sweep_graph_replay_matches_eager(lib):
             got = {**b.as_dict(), "resident": rn}
             for key, val in eager[li].items():
                 assert torch.equal(got[key], val), f"replay {rep} layer {li}: {key}"
+
+
+def test_layer_pipelined_sweep_at_the_qwen3_8b_shape(lib):
+    """Three layers of the Qwen3-8B 32K shape (four sequences, all eight KV heads: the
+    selection shares the next layer's first launch at K = 128 and 2048 blocks), two
+    sweeps: every layer's plan outputs and next slot table equal its overlapped step's
+    bit for bit and its attention equals it up to the merge's summation order."""
+    w = synth.WORKLOADS["qwen3_8b_32k"].with_(batch=4)
+    _say("layer-pipelined sweep at the Qwen3-8B shape")
+    d = lib.dims_for(w)
+    layers, expected = [], []
+    for layer in range(3):
+        inp = synth.generate(w, DEV, layer=layer)
+        summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
+        sel = lib.topk_blocks(d, lib.score_summaries(d, inp["q_prev"], summ, inp["seq_lens"]), inp["seq_lens"])
+        res = synth.resident_from_selection(w, sel, inp["seq_lens"].cpu(), layer=layer).to(DEV)
+        rn = torch.empty_like(res)
+        ov = lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, rn,
+                                        default_scale())
+        torch.cuda.synchronize()
+        expected.append(({k: v.clone() for k, v in ov.items()}, rn.clone()))
+        layers.append((inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res))
+    sweep = lib.PipelinedLayers(d, layers, default_scale())
+    for step in range(2):
+        sweep()
+        sweep.drain()
+        torch.cuda.synchronize()
+        for li, (exp, rn) in enumerate(expected):
+            b = sweep.buffers[li]
+            for key in ("scores", "topk", "plan", "plan_count", "table", "table_count"):
+                assert torch.equal(getattr(b, key), exp[key]), f"step {step} layer {li}: {key}"
+            assert torch.equal(sweep.resident_next[li], rn)
+            assert (b.out - exp["out"]).abs().max().item() <= 1e-6
+    del layers, expected, sweep
+    torch.cuda.empty_cache()
