@@ -282,3 +282,36 @@ def test_copy_and_append_edge_cases(lib):
     assert torch.equal(wset.pool_k, exp_k)
     assert torch.equal(summ[0], s0[0]) and torch.equal(kd[0], k0[0]) and torch.equal(wset.ring_k[0], r0[0])
     assert torch.equal(kd[1, :, 50 // 16, 50 % 16], kn[1])             # the other sequence took it
+
+
+@pytest.mark.parametrize("tier", ["device", "host"])
+def test_step_over_the_working_set_at_the_qwen3_8b_shape(lib, tier):
+    """The Qwen3-8B 32K shape (two sequences, all eight KV heads, K = 128, cap 6): the
+    step over the working set gives the full-cache overlapped step's outputs bit for
+    bit, and its copies leave the pool equal to the gather of the next slot table."""
+    w = synth.WORKLOADS["qwen3_8b_32k"].with_(batch=2)
+    _say(f"step over the working set at the Qwen3-8B shape, {tier} tier")
+    inp = synth.generate(w, DEV)
+    d = lib.dims_for(w)
+    summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
+    sel = lib.topk_blocks(d, lib.score_summaries(d, inp["q_prev"], summ, inp["seq_lens"]), inp["seq_lens"])
+    R = synth.resident_from_selection(w, sel, inp["seq_lens"].cpu()).to(DEV)
+    if tier == "host":
+        src_k, src_v = inp["k"].cpu().pin_memory(), inp["v"].cpu().pin_memory()
+    else:
+        src_k, src_v = inp["k"], inp["v"]
+    wset = lib.fill_working_set(d, R, inp["seq_lens"], src_k, src_v)
+    rn_pool, rn_full = torch.empty_like(R), torch.empty_like(R)
+    pool_out = {key: t.clone() for key, t in
+                lib.decode_step_pool(d, inp["q"], summ, src_k, src_v, wset, inp["seq_lens"], R, rn_pool).items()}
+    full_out = lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], R, rn_full)
+    torch.cuda.synchronize()
+    for key in ("scores", "topk", "plan", "plan_count", "table", "table_count", "out", "lse"):
+        assert torch.equal(pool_out[key], full_out[key]), key
+    assert torch.equal(rn_pool, rn_full)
+    assert int(full_out["plan_count"].sum()) > 0
+    expect = lib.fill_working_set(d, rn_full, inp["seq_lens"], inp["k"], inp["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(wset.pool_k, expect.pool_k) and torch.equal(wset.pool_v, expect.pool_v)
+    del inp, summ, wset, expect
+    torch.cuda.empty_cache()
