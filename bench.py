@@ -834,6 +834,8 @@ def main(argv=None) -> int:
                     help="print one JSON line with the prediction-quality analogue instead of the benchmark")
     ap.add_argument("--sweep", action="store_true",
                     help="print one JSON line with the K and fetch-ratio sweep instead of the benchmark")
+    ap.add_argument("--pipeline-reps", type=int, default=100,
+                    help="graph replays of the layer-pipelined sweep (each runs every input set)")
     ap.add_argument("--no-plan-exec", action="store_true",
                     help="skip the working-set measurements (step over the pool, plan copies, host tier)")
     args = ap.parse_args(argv)
@@ -887,6 +889,10 @@ def main(argv=None) -> int:
     t_setup = time.perf_counter()
     sets = []
     for i in range(n_sets):
+        if n_sets > 1:
+            # Progress on stderr (stdout carries only the JSON line): under a counter
+            # profiler the set-up of many layers takes minutes.
+            print(f"bench: set-up of input set {i + 1}/{n_sets}", file=sys.stderr, flush=True)
         inp = synth.generate(w, dev, layer=i)
         summ = oa.build_summaries(d, inp["k"], inp["seq_lens"])
         q_sel = inp["q_prev"] if w.resident == "prev" else inp["q"]
@@ -960,6 +966,7 @@ def main(argv=None) -> int:
         return ms, n, wall, graph, spread
 
     # ---- the timed region (the chosen order), then the other order for reference ------
+    print(f"bench: set-up done in {setup_s:.1f} s; timing", file=sys.stderr, flush=True)
     ms_per_step, n_timed, wall_s, graph, spread = timed(steps)
     check = {}
     if graph is not None:
@@ -994,6 +1001,7 @@ def main(argv=None) -> int:
             done += n
         return {k: [1e3 * x for x in v] for k, v in acc.items()}
 
+    print("bench: per-launch events", file=sys.stderr, flush=True)
     stage_samples = evented(serial_steps, False)
     stage_samples.update(evented(over_steps, True))
     stage_us = {k: statistics.mean(v) for k, v in stage_samples.items()}
@@ -1061,11 +1069,15 @@ def main(argv=None) -> int:
         "setup_s": round(setup_s, 1),
         "checks": check,
     }
-    result["layer_pipelined"] = layer_pipelined(d, sets, ms_per_step, torch, oa, step_bytes=nb["step"])
+    print("bench: layer-pipelined sweep", file=sys.stderr, flush=True)
+    result["layer_pipelined"] = layer_pipelined(d, sets, ms_per_step, torch, oa, reps=max(1, args.pipeline_reps),
+                                                step_bytes=nb["step"])
     if not args.no_plan_exec:
+        print("bench: plan execution", file=sys.stderr, flush=True)
         result["plan_execution"] = plan_execution(w, d, sets, buffers, res_next, ms_per_step, stage_us,
                                                   torch, oa)
     if args.cpu_budget > 0:
+        print("bench: oracle on the host cores", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(w, sets, args.cpu_budget, args.order == "overlapped")
     print(json.dumps(result), flush=True)
     return 0
