@@ -82,8 +82,14 @@ __global__ __launch_bounds__(kCopyThreads) void fill_working_set_kernel(
 // 8 x 8 heads is 384) goes out in one round from HBM, larger plans fill the host link
 // in several, and the copies hold at most one workgroup's slots per CU, so that they
 // can run beside another stream's kernels.
-constexpr int kCopyRows = 4;
-constexpr int kCopyGrid = 256;
+#ifndef OASIS_COPY_ROWS
+#define OASIS_COPY_ROWS 4
+#endif
+#ifndef OASIS_COPY_GRID
+#define OASIS_COPY_GRID 256
+#endif
+constexpr int kCopyRows = OASIS_COPY_ROWS;
+constexpr int kCopyGrid = OASIS_COPY_GRID;
 __global__ __launch_bounds__(kCopyThreads) void execute_plan_kernel(
     const int32_t* __restrict__ plan, const int32_t* __restrict__ plan_count,
     const u32x4* __restrict__ k, const u32x4* __restrict__ v, u32x4* __restrict__ pool_k,
