@@ -531,13 +531,27 @@ def plan_execution(w, d, sets, buffers, res_next, ms_step: float, stage_us: dict
     del src, dst, hosts, host_steps
     # Eq. (3): bytes the link can move while one layer's step computes, at the rate the
     # plan's copies reach; Eq. (4): the slowest background stage against that step.
+    # Reading of the two equations: the pages' T_decode is the compute time of a whole
+    # decode step (every layer) and their per-layer stage budget is T_step / N_layer.
+    # This path is one layer, so the layer's own measured step stands for both: the
+    # plan's copies for a layer must cross the link within that layer's step.
     t_step = ms_step * 1e-3
-    out["eq3"] = {"link_gbps": round(link_gbps, 2), "t_step_us": round(ms_step * 1e3, 3),
-                  "c_token_bytes": int(link_gbps * 1e9 * t_step),
+    heads = w.batch * w.num_kv_heads
+    per_cap_bytes = heads * block_kv_bytes(w.block)          # one more admitted block per head
+    budget = link_gbps * 1e9 * t_step
+    reading = ("T_decode and the per-layer budget T_step / N_layer are both taken as this one "
+               "layer's measured step; the plan's copies of a layer must cross the host link "
+               "within it")
+    out["eq3"] = {"reading": reading, "link_gbps": round(link_gbps, 2), "t_step_us": round(ms_step * 1e3, 3),
+                  "c_token_bytes": int(budget),
                   "plan_bytes_per_step": moved,
-                  "fits": bool(moved <= link_gbps * 1e9 * t_step)}
+                  "fits": bool(moved <= budget),
+                  "break_even_layer_us": round(moved / (link_gbps * 1e9) * 1e6, 3),
+                  "largest_cap_fitting": int(min(w.top_k, budget // per_cap_bytes)),
+                  "cap": w.cap}
     t_pipe = max(stage_us["score"], stage_us["select_plan"], us_host)
-    out["eq4"] = {"t_pred_us": round(stage_us["score"], 3), "t_select_us": round(stage_us["select_plan"], 3),
+    out["eq4"] = {"reading": reading, "t_pred_us": round(stage_us["score"], 3),
+                  "t_select_us": round(stage_us["select_plan"], 3),
                   "t_transfer_us": round(us_host, 3), "t_pipe_us": round(t_pipe, 3),
                   "delta_prefetch_us": round(ms_step * 1e3, 3)}
     return out
@@ -945,29 +959,39 @@ def main(argv=None) -> int:
     setup_s = time.perf_counter() - t_setup
 
     def timed(step_list):
-        """Warm-up, then exactly the timed steps; returns (ms per step, steps, wall s,
-        graph or None)."""
+        """Warm-up, then exactly args.steps timed steps; returns (ms per step, steps,
+        wall s, graph or None, per-step spread)."""
         for i in range(args.warmup):
             step_list[i % n_sets]()
         torch.cuda.synchronize()
-        graph = None
+        graph = rest = None
+        reps, n_rest = divmod(args.steps, n_sets)
+
+        def capture(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for st in step_list[:n]:
+                    st()
+            return g
+
         if args.mode == "graph":
             # One graph holds one step per input set; replaying it walks the rotation.
+            # A second graph holds the first n_rest steps, so that exactly args.steps
+            # steps are timed whatever their number.
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
                 step_list[0]()
             torch.cuda.current_stream().wait_stream(side)
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                for st in step_list:
-                    st()
+            graph = capture(n_sets)
+            rest = capture(n_rest) if n_rest else None
             torch.cuda.synchronize()
             for _ in range(max(1, args.warmup // n_sets)):
                 graph.replay()
+            if rest is not None:
+                rest.replay()
             torch.cuda.synchronize()
-        reps = max(1, args.steps // n_sets)
-        n = reps * n_sets if graph is not None else args.steps
+        n = args.steps
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -975,6 +999,8 @@ def main(argv=None) -> int:
         if graph is not None:
             for _ in range(reps):
                 graph.replay()
+            if rest is not None:
+                rest.replay()
         else:
             for i in range(n):
                 step_list[i % n_sets]()
@@ -982,9 +1008,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         ms = ev0.elapsed_time(ev1) / n
         wall = time.perf_counter() - t0
-        # Spread: the same work again with an event after every graph replay (one
-        # rotation through the input sets) or every eager step; per-step ms of each.
-        n_samples = min(reps if graph is not None else n, 300)
+        # Spread: 300 more replays (one rotation through the input sets each) or eager
+        # steps, whatever args.steps is, with an event after each; per-step ms of each.
+        n_samples = 300
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_samples + 1)]
         evs[0].record()
         for i in range(n_samples):

@@ -158,8 +158,8 @@ oasis_status oasis_topk_blocks(const oasis_dims* dims, const float* scores, cons
  *   order receive the admitted blocks in ascending block order.
  *   plan[b,h,r,:] = (slot, new block, old block or -1) for r < n by ascending
  *   slot, rows r >= n are -1; plan_count[b,h] = n; resident is updated in
- *   place.  table[b,h,:] = the updated resident entries != -1 in slot order,
- *   then the window blocks w0_b .. nblk_b - 1, then -1 up to T entries;
+ *   place.  table[b,h,:] = the updated resident entries in [0, w0_b) in slot
+ *   order, then the window blocks w0_b .. nblk_b - 1, then -1 up to T entries;
  *   table_count[b,h] = number of entries.
  * xllm-io review, section three training flow step 3 (compare with the
  * resident set, build the transfer plan) and component table (Capped
@@ -170,7 +170,10 @@ oasis_status oasis_topk_blocks(const oasis_dims* dims, const float* scores, cons
  *   scores      device, fp32 [B, H, NB]  (ranks stale slots)
  *   topk        device, int32 [B, H, K]  (oasis_topk_blocks output)
  *   seq_lens    device, int32 [B]
- *   resident    device, int32 [B, H, K]  in/out; entries distinct, in [0, w0_b) or -1
+ *   resident    device, int32 [B, H, K]  in/out; entries distinct, in [0, nblk_b) or -1.
+ *               A resident block at or past w0_b (one the local window has reached) is
+ *               not a candidate: its score is -inf, so it is the first stale slot to be
+ *               freed, and while it stays it is listed once, among the window blocks.
  *   plan        device, int32 [B, H, C, 3] (output; may be NULL when C == 0)
  *   plan_count  device, int32 [B, H]       (output)
  *   table       device, int32 [B, H, T]    (output)
@@ -224,7 +227,11 @@ oasis_status oasis_sparse_decode_attn_resident(const oasis_dims* dims, const voi
 /* The whole step on one stream: oasis_score_summaries, then the selection and
  * the plan (one kernel doing oasis_topk_blocks and oasis_build_plan), then
  * oasis_sparse_decode_attn over the updated table (table_stride =
- * oasis_table_stride(dims)).  Arguments as above, except:
+ * oasis_table_stride(dims)).  This is the order of the xllm-io review, section
+ * three, training flow step 3, read as one stream: the look-ahead prediction
+ * of the top-K blocks, the comparison with the resident set that yields the
+ * capped transfer plan, and attention over the working set that results.
+ * Arguments as above, except:
  *   resident_next  device, int32 [B, H, K] or NULL.  NULL: `resident` is
  *                  updated in place.  Otherwise `resident` is only read and the
  *                  updated slot table is written here (a double-buffered slot

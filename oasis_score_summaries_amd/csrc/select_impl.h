@@ -42,7 +42,7 @@ struct PlanBitmaps {
   // Per-wave counts of the plan's compactions (up to 16 waves).  Outside the LDS the
   // plan shares with the selection, so the plan can write them before its first
   // barrier while other waves still read the selection's output.
-  int w_new[16], w_empty[16], w_stale[16], w_vict[16];
+  int w_new[16], w_empty[16], w_stale[16], w_vict[16], w_tab[16];
 };
 __device__ inline void clear_bitmaps(PlanBitmaps& bm, int NB) {
   for (int w = threadIdx.x; w < (NB + 31) >> 5; w += blockDim.x) {
@@ -412,10 +412,20 @@ __device__ __attribute__((always_inline)) void plan_apply(
   }
   int c_vict;
   const int rk_vict = wave_flag_rank(victim, &c_vict);
-  if (lane == 0) bm.w_vict[wave] = c_vict;
+  // Table entries: a victim takes an admitted block (a candidate); a kept slot is listed
+  // if its block lies before the first window block.  A block the window has reached
+  // stays resident but is attended once, as a window block.
+  const bool tabled = tid < K && (victim || (r_i >= 0 && r_i < w0));
+  int c_tab;
+  const int rk_tab = wave_flag_rank(tabled, &c_tab);
+  if (lane == 0) {
+    bm.w_vict[wave] = c_vict;
+    bm.w_tab[wave] = c_tab;
+  }
   __syncthreads();
-  int n_vict;
+  int n_vict, n_res;
   const int pos_vict = waves_before<NW>(bm.w_vict, &n_vict) + rk_vict;
+  const int pos_tab = waves_before<NW>(bm.w_tab, &n_res) + rk_tab;
   // Empty plus stale slots number K - |R and S| >= |S without R| >= n, so every one
   // of the n victims takes an admitted block.
   const int n_placed = n < n_vict ? n : n_vict;
@@ -437,14 +447,10 @@ __device__ __attribute__((always_inline)) void plan_apply(
   }
   if (tid == 0) *plan_count = n_placed;
 
-  // Table: updated resident entries in slot order, then the window blocks.  The
-  // updated set is empty exactly at the empty slots that were not filled, which
-  // are the empty slots of rank n and above (empty slots are filled in slot order);
-  // so slot t moves forward by the unfilled empty slots before it (pos_empty is the
-  // number of empty slots before t, for every thread).
-  const int unfilled_before = pos_empty > n_placed ? pos_empty - n_placed : 0;
-  const int n_res = K - (n_empty > n_placed ? n_empty - n_placed : 0);
-  if (tid < K && new_r >= 0) table_row[tid - unfilled_before] = new_r;
+  // Table: the listed resident entries in slot order, then the window blocks.  Every
+  // victim takes an admitted block (there are n of each), so a victim's entry is its
+  // new block.
+  if (tabled) table_row[pos_tab] = new_r;
   const int nwin = nblk - w0;
   for (int i = tid; i < nwin; i += THREADS) table_row[n_res + i] = w0 + i;
   for (int i = n_res + nwin + tid; i < T; i += THREADS) table_row[i] = -1;

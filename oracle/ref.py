@@ -210,7 +210,10 @@ def build_plan(scores: np.ndarray, topk: np.ndarray, resident: np.ndarray, seq_l
       * the attention table is the updated resident entries in slot order
         (empty slots skipped) followed by the local-window blocks
         [first_window_block, num_blocks) ([xllm] section three, training
-        flow step 2: selected historical blocks plus the local window).
+        flow step 2: selected historical blocks plus the local window); a
+        resident block that the window has reached (the window moves as the
+        sequence grows) is listed once, as a window block, as in
+        resident_table.
 
     scores: [B, H, NB]; topk: [B, H, K]; resident: [B, H, K] (-1 = empty).
     Returns dict with plan [B, H, C, 3], plan_count [B, H], resident [B, H, K],
@@ -229,7 +232,7 @@ def build_plan(scores: np.ndarray, topk: np.ndarray, resident: np.ndarray, seq_l
         for h in range(H):
             p, n, r = _plan_one(scores[b, h], topk[b, h], resident[b, h], cap)
             plan[b, h], plan_count[b, h], new_res[b, h] = p, n, r
-            entries = [int(x) for x in r if x >= 0] + list(range(w0, nb))
+            entries = [int(x) for x in r if 0 <= x < w0] + list(range(w0, nb))
             table[b, h, : len(entries)] = entries
             table_count[b, h] = len(entries)
     return {"plan": plan, "plan_count": plan_count, "resident": new_res,

@@ -102,8 +102,10 @@ def oracle_head(q, k, v, lens, resident_row, top_k, window, cap, scale, b, h,
     res = ref.decode_step(qh, summ, kh, vh, L, np.asarray(resident_row)[None, None], top_k, window,
                           cap, scale, block)
     res["summ"] = summ
-    return {key: val[0, 0] if isinstance(val, np.ndarray) and val.ndim >= 2 else val
-            for key, val in res.items()}
+    out = {key: val[0, 0] if isinstance(val, np.ndarray) and val.ndim >= 2 else val
+           for key, val in res.items()}
+    out["head_inputs"] = (qh, kh, vh, L, block)   # for attention over another table
+    return out
 
 
 def oracle_selection_head(q, k, lens, top_k, window, b, h, block: int = 16) -> np.ndarray:

@@ -518,6 +518,42 @@ def test_resident_table_hand_example():
     assert np.all(table[0, 0, 7:] == -1) and table.shape[-1] == 4 + 4 + 1
 
 
+def test_plan_table_lists_a_window_reached_block_once():
+    """Hand example: len 700, W 64, so the first window block is floor(636 / 16) = 39
+    and the blocks run to ceil(700 / 16) = 44.  Slots hold [5, -1, 40, 2]: slot 1 is
+    empty and block 40 lies in the window.  The selection is [5, 2, 10, 11]."""
+    NB, K, W = 48, 4, 64
+    lens = np.array([700])
+    scores = np.full((1, 1, NB), -np.inf)
+    scores[0, 0, :39] = np.linspace(1.0, 0.5, 39)   # candidates only; 40 is not one
+    scores[0, 0, [5, 2, 10, 11]] = [9.0, 8.0, 7.0, 6.0]
+    sel = ref.topk_blocks(scores, lens, K, W)
+    assert sel[0, 0].tolist() == [5, 2, 10, 11]
+    R = np.array([[[5, -1, 40, 2]]])
+    # cap 0: nothing moves; block 40 is attended once, as a window block
+    p = ref.build_plan(scores, sel, R, lens, 0, W)
+    assert p["resident"][0, 0].tolist() == [5, -1, 40, 2]
+    assert p["table_count"].tolist() == [[7]]
+    assert p["table"][0, 0, :7].tolist() == [5, 2, 39, 40, 41, 42, 43]
+    # cap 1: the best new block (10) fills the empty slot; 40 stays resident, listed once
+    p = ref.build_plan(scores, sel, R, lens, 1, W)
+    assert p["resident"][0, 0].tolist() == [5, 10, 40, 2]
+    assert p["table"][0, 0, :8].tolist() == [5, 10, 2, 39, 40, 41, 42, 43]
+    # cap 4: both new blocks; the empty slot, then the window-reached block (score -inf,
+    # the worst stale one) are freed, and slots 1, 2 take blocks 10, 11 in order
+    p = ref.build_plan(scores, sel, R, lens, 4, W)
+    assert p["plan_count"].tolist() == [[2]]
+    assert p["plan"][0, 0, :2].tolist() == [[1, 10, -1], [2, 11, 40]]
+    assert p["resident"][0, 0].tolist() == [5, 10, 11, 2]
+    assert p["table"][0, 0, :9].tolist() == [5, 10, 11, 2, 39, 40, 41, 42, 43]
+    # either way the table is the resident-slot table of the updated set
+    for cap in (0, 1, 4):
+        p = ref.build_plan(scores, sel, R, lens, cap, W)
+        table, count = ref.resident_table(p["resident"], lens, W)
+        np.testing.assert_array_equal(table, p["table"])
+        np.testing.assert_array_equal(count, p["table_count"])
+
+
 def test_resident_table_of_planned_set_is_the_plan_table():
     r = _rng(11)
     B, H, NB, K, W = 2, 3, 64, 12, 40
@@ -530,7 +566,8 @@ def test_resident_table_of_planned_set_is_the_plan_table():
             n_cand = ref.first_window_block(int(lens[b]), W)
             for h in range(H):
                 m = min(K - trial, n_cand)
-                res[b, h, :m] = r.choice(n_cand, size=m, replace=False)
+                nb = ref.num_blocks(int(lens[b]))
+                res[b, h, :m] = r.choice(nb, size=m, replace=False)   # window blocks too
                 r.shuffle(res[b, h])
         p = ref.build_plan(scores, sel, res, lens, 3, W)
         table, count = ref.resident_table(p["resident"], lens, W)

@@ -29,8 +29,10 @@ MUTATIONS = {
     "attention_drops_scale": ("z = (kt @ q[b, h, g, 0, :]) * scale", "z = (kt @ q[b, h, g, 0, :])"),
     "attention_uses_a_draft": ("z = (kt @ q[b, h, g, 0, :]) * scale", "z = (kt @ q[b, h, g, 1, :]) * scale"),
     "attention_ignores_length": ("if j * block + t < L]", "if True]"),
-    "table_drops_window": ("entries = [int(x) for x in r if x >= 0] + list(range(w0, nb))",
-                           "entries = [int(x) for x in r if x >= 0]"),
+    "table_drops_window": ("entries = [int(x) for x in r if 0 <= x < w0] + list(range(w0, nb))",
+                           "entries = [int(x) for x in r if 0 <= x < w0]"),
+    "plan_table_keeps_window_blocks": ("entries = [int(x) for x in r if 0 <= x < w0] + list(range(w0, nb))",
+                                       "entries = [int(x) for x in r if x >= 0] + list(range(w0, nb))"),
     "cap_rounds_to_nearest": ("return int(math.floor(float(fetch_ratio) * int(top_k) + 1e-9))",
                               "return int(round(float(fetch_ratio) * int(top_k)))"),
     "resident_table_keeps_window_blocks": (

@@ -247,7 +247,8 @@ def _compare_head(w, got, exp, b, h, resident_row, robust: bool) -> bool:
     """Scores within tolerance and the selection equal up to near-ties, always.  If the
     GPU's selection, plan and table equal the oracle's, the attention output is
     compared too (returns True); otherwise the head must have a near-tie in a
-    deciding comparison and its plan must still obey the rule (returns False)."""
+    deciding comparison, its plan must still obey the rule, and its attention must
+    equal the oracle's over the GPU's own table (returns False)."""
     floor = score_floor(exp["q64"][None, None], exp["summ"][None, None])[0, 0]
     check_scores(f64(got["scores"][b, h]), exp["scores"], floor, f"scores b={b} h={h}")
     gsel, esel = i64(got["topk"][b, h]), exp["topk"]
@@ -257,6 +258,12 @@ def _compare_head(w, got, exp, b, h, resident_row, robust: bool) -> bool:
         assert not robust, f"b={b} h={h}: the plan differs although no decision is a near-tie"
         fin = exp["scores"][np.isfinite(exp["scores"])]
         _plan_valid(got, exp, b, h, resident_row, w.cap, 1e-5 * float(np.abs(fin).max()))
+        qh, kh, vh, L, block = exp["head_inputs"]
+        eo, el = ref.sparse_attention(qh, kh, vh, i64(got["table"][b, h])[None, None],
+                                      i64(got["table_count"][b, h]).reshape(1, 1), L,
+                                      default_scale(), block)
+        np.testing.assert_allclose(f64(got["out"][b, h]), eo[0, 0], rtol=0, atol=OUT_ATOL)
+        np.testing.assert_allclose(f64(got["lse"][b, h]), el[0, 0], rtol=0, atol=OUT_ATOL)
         return False
     np.testing.assert_allclose(f64(got["out"][b, h]), exp["out"], rtol=0, atol=OUT_ATOL)
     fin = np.isfinite(exp["lse"])
@@ -398,8 +405,9 @@ def _full_size_case(lib, w, layer=0):
         # whatever the robustness, the GPU's own outputs must be self-consistent
         tc = int(got["table_count"][b, h])
         assert int(got["plan_count"][b, h]) <= w.cap
-        assert tc == int((got["resident"][b, h] >= 0).sum()) + ref.num_blocks(int(lens[b]), w.block) - \
-            ref.first_window_block(int(lens[b]), w.window, w.block)
+        w0 = ref.first_window_block(int(lens[b]), w.window, w.block)
+        rb = got["resident"][b, h]
+        assert tc == int(((rb >= 0) & (rb < w0)).sum()) + ref.num_blocks(int(lens[b]), w.block) - w0
         assert torch.isfinite(got["out"][b, h]).all()
     # fp32 scoring error (~1e-7 relative) is far below the 1e-5 tolerance, so nearly
     # every sampled head must reproduce the oracle's plan and table exactly
@@ -429,6 +437,57 @@ def _full_size_case(lib, w, layer=0):
 @pytest.mark.parametrize("name", ["qwen3_8b_32k", "long_128k", "qwen3_235b_32k"])
 def test_full_size_workload(lib, name):
     _full_size_case(lib, synth.WORKLOADS[name])
+
+
+def _zero_scale_check(w, v, lens, table, table_count, out, lse, where):
+    """With scale 0 every attended token weighs the same: exp(lse) is the number of
+    tokens of the head's table below the length, and out is the mean of their V rows
+    (fp64 on the device).  Every head is checked."""
+    bs = w.block
+    for b in range(w.batch):
+        L = int(lens[b])
+        for h in range(w.num_kv_heads):
+            blocks = [int(x) for x in table[b, h, : int(table_count[b, h])]]
+            count = sum(min(bs, L - bs * j) for j in blocks if 0 <= j and bs * j < L)
+            got_n = np.exp(f64(lse[b, h]))
+            assert np.all(np.abs(got_n - count) <= 1e-6 * count), f"{where} b={b} h={h}: exp(lse) {got_n} vs {count}"
+            idx = torch.tensor(blocks, dtype=torch.int64, device=v.device)
+            vb = v[b, h].index_select(0, idx).to(torch.float64)               # [n, bs, 128]
+            tok = torch.arange(bs, device=v.device)[None, :] + bs * idx[:, None]
+            mean = (vb * (tok < L)[:, :, None]).sum(dim=(0, 1)) / count
+            err = (out[b, h].to(v.device).to(torch.float64) - mean[None, :]).abs().max().item()
+            assert err <= 1e-5, f"{where} b={b} h={h}: out differs from the mean of V by {err:.3g}"
+
+
+@pytest.mark.parametrize("name,layer", [("qwen3_235b_32k", 0), ("reasoning_36l", 17), ("qwen3_8b_32k", 0)])
+def test_full_size_zero_scale_every_head(lib, name, layer):
+    """At full size, in the benchmark's launch configuration (Qwen3-235B: eight-round
+    attention splits; 36 layers: four rounds), both step orders with scale 0, on every
+    head: the merged log-sum-exp counts the attended tokens exactly and the output is
+    the mean of their V rows.  A dropped or doubled token moves exp(lse) by one count
+    (above 1e-6 relative up to a million tokens) and the output by about 1/count."""
+    w = synth.WORKLOADS[name]
+    _say(f"zero-scale full size {name} layer={layer}: generating")
+    inp = synth.generate(w, DEV, layer=layer)
+    d = lib.dims_for(w)
+    summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
+    sel = lib.topk_blocks(d, lib.score_summaries(d, inp["q"], summ, inp["seq_lens"]), inp["seq_lens"])
+    lens = inp["seq_lens"].cpu().numpy()
+    resident = synth.resident_from_selection(w, sel, torch.from_numpy(lens), layer=layer).to(DEV)
+    res_cpu = i64(resident)
+    _say(f"zero-scale full size {name}: serial step")
+    ser = lib.decode_step(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], resident.clone(), 0.0)
+    ser = {key: val.detach().cpu() for key, val in ser.items()}
+    _zero_scale_check(w, inp["v"], lens, i64(ser["table"]), i64(ser["table_count"]), ser["out"], ser["lse"],
+                      f"{name} serial")
+    _say(f"zero-scale full size {name}: overlapped step")
+    rn = torch.empty_like(resident)
+    ov = lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], resident, rn, 0.0)
+    ov = {key: val.detach().cpu() for key, val in ov.items()}
+    table, tc = ref.resident_table(res_cpu, lens, w.window, w.block)
+    _zero_scale_check(w, inp["v"], lens, table, tc, ov["out"], ov["lse"], f"{name} overlapped")
+    del inp, summ
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("top_k,ratio", [(64, 0.05), (192, 0.05), (128, 0.01), (128, 0.02),
@@ -650,6 +709,106 @@ def test_attention_over_resident_slots(lib, G, lens, NB, K):
     fin = np.isfinite(el)
     assert np.array_equal(np.isneginf(f64(lse)), ~fin)
     np.testing.assert_allclose(f64(lse)[fin], el[fin], rtol=0, atol=OUT_ATOL)
+
+
+@pytest.mark.parametrize("ratio", [0.0, 0.25, 1.0])
+def test_serial_step_with_window_reached_slots(lib, ratio):
+    """oasis_decode_step over slot tables that hold blocks the window has reached, empty
+    slots and historical blocks: the plan, the updated slots and the table equal the
+    oracle's given the GPU's own scores and selection (a window-reached block is listed
+    once, as a window block), and the attention equals the oracle's over the GPU's table."""
+    _say(f"serial step, window-reached slots, ratio={ratio}")
+    B, H, G, Q, NB, K, W = 3, 2, 4, 5, 64, 12, 64
+    lens = [1000, 700, 300]
+    q, k, v, L = _small_inputs(77, B, H, G, Q, NB, lens)
+    d = _dims(lib, B, H, G, NB, Q, K, W, ratio)
+    cap = ref.fetch_cap(ratio, K)
+    rng = np.random.default_rng(17)
+    R = np.full((B, H, K), -1, dtype=np.int64)
+    for b in range(B):
+        nb, w0 = ref.num_blocks(lens[b]), ref.first_window_block(lens[b], W)
+        for h in range(H):
+            win = list(range(w0, nb))[: 2 + h]                     # blocks the window has reached
+            hist = rng.choice(w0, size=K - len(win) - 2, replace=False).tolist()
+            row = np.array(win + hist + [-1, -1])
+            rng.shuffle(row)
+            R[b, h] = row
+    R_dev = torch.from_numpy(R.astype(np.int32)).to(DEV)
+    got = lib.decode_step(d, q.to(DEV), lib.build_summaries(d, k.to(DEV), L.to(DEV)), k.to(DEV),
+                          v.to(DEV), L.to(DEV), R_dev, default_scale())
+    torch.cuda.synchronize()
+    got = {key: val.detach().cpu() for key, val in got.items()}
+    summ = ref.build_summaries(f64(k), L.numpy())
+    check_scores(f64(got["scores"]), ref.score_blocks(f64(q), summ, L.numpy(), W),
+                 score_floor(f64(q), summ), "scores")
+    gs = f64(got["scores"])
+    np.testing.assert_array_equal(i64(got["topk"]), ref.topk_blocks(gs, L.numpy(), K, W))
+    exp = ref.build_plan(gs, i64(got["topk"]), R, L.numpy(), cap, W)
+    for key in ("plan", "plan_count", "table", "table_count"):
+        if key == "plan" and cap == 0:
+            continue
+        np.testing.assert_array_equal(i64(got[key]), exp[key], err_msg=key)
+    np.testing.assert_array_equal(i64(got["resident"]), exp["resident"])
+    assert (i64(got["table_count"]) > 0).all()
+    eo, el = ref.sparse_attention(f64(q), f64(k), f64(v), i64(got["table"]), i64(got["table_count"]),
+                                  L.numpy(), default_scale())
+    np.testing.assert_allclose(f64(got["out"]), eo, rtol=0, atol=OUT_ATOL)
+    np.testing.assert_allclose(f64(got["lse"]), el, rtol=0, atol=OUT_ATOL)
+
+
+def test_append_then_step_loop_both_step_orders_agree(lib):
+    """A decode loop at cap 0 (the plan never moves a block) over slot tables that hold
+    blocks of the local window: each step appends one token, so the window moves on
+    and those blocks turn into historical ones.  The serial step (attention over its
+    table) and the overlapped step (attention over the slot table) attend the same
+    tokens at every step (a block is listed once, as a window block while the window
+    covers it), and both equal the oracle."""
+    B, H, G, Q, NB, K, W = 2, 2, 4, 3, 40, 8, 32
+    lens = [500, 263]
+    _say("append-then-step loop, both step orders")
+    q, k, v, L = _small_inputs(91, B, H, G, Q, NB, lens)
+    d = _dims(lib, B, H, G, NB, Q, K, W, 0.0)
+    kd, vd, Ld = k.to(DEV), v.to(DEV), L.to(DEV)
+    summ = lib.build_summaries(d, kd, Ld)
+    # slot tables holding the first three window blocks and some historical ones
+    R = np.full((B, H, K), -1, dtype=np.int64)
+    w0_start = [ref.first_window_block(x, W) for x in lens]
+    for b in range(B):
+        for h in range(H):
+            R[b, h, :K - 1] = list(range(w0_start[b], w0_start[b] + 3)) + list(range(h, h + K - 4))
+    R_serial = torch.from_numpy(R.astype(np.int32)).to(DEV)
+    R_over = R_serial.clone()
+    wset = lib.WorkingSet(d, DEV)
+    g = torch.Generator().manual_seed(3)
+    qd = q.to(DEV)
+    reached = 0
+    for step in range(40):
+        a = lib.decode_step(d, qd, summ, kd, vd, Ld, R_serial, default_scale())
+        a = {key: val.clone() for key, val in a.items()}
+        rn = torch.empty_like(R_over)
+        o = lib.decode_step_overlapped(d, qd, summ, kd, vd, Ld, R_over, rn, default_scale())
+        torch.cuda.synchronize()
+        assert torch.equal(rn, R_over) and torch.equal(a["resident"], R_serial)   # cap 0: nothing moves
+        Lh = Ld.cpu().numpy()
+        table, tc = ref.resident_table(i64(R_serial), Lh, W)
+        np.testing.assert_array_equal(i64(a["table"]), table, err_msg=f"step {step}: table")
+        np.testing.assert_array_equal(i64(a["table_count"]), tc, err_msg=f"step {step}: table_count")
+        assert (o["out"] - a["out"]).abs().max().item() <= 1e-5, f"step {step}: out"
+        assert (o["lse"] - a["lse"]).abs().max().item() <= 1e-5, f"step {step}: lse"
+        if step % 13 == 0 or step == 39:
+            eo, el = ref.sparse_attention(f64(qd), f64(kd), f64(vd), table, tc, Lh, default_scale())
+            np.testing.assert_allclose(f64(a["out"]), eo, rtol=0, atol=OUT_ATOL)
+            np.testing.assert_allclose(f64(a["lse"]), el, rtol=0, atol=OUT_ATOL)
+        reached += int(sum(int((i64(R_serial)[b] >= ref.first_window_block(int(Lh[b]), W)).sum())
+                           for b in range(B)))
+        kn = torch.randn((B, H, 128), generator=g).to(torch.bfloat16).to(DEV)
+        vn = torch.randn((B, H, 128), generator=g).to(torch.bfloat16).to(DEV)
+        lib.append_token(d, kn, vn, Ld, summ, wset, kd, vd)
+        torch.cuda.synchronize()
+        Ld += 1
+    assert reached > 0, "no resident block lay in the window"
+    # the window moved past some of them: they are historical blocks now
+    assert any(ref.first_window_block(int(Ld[b]), W) > w0_start[b] for b in range(B))
 
 
 @pytest.mark.parametrize("overlapped", [False, True])
