@@ -99,10 +99,34 @@ int32_t oasis_fetch_cap(const oasis_dims* dims);
  * window blocks any length can produce, ceil(W / bs) + 1.  -1 if invalid. */
 int32_t oasis_table_stride(const oasis_dims* dims);
 
-/* Device workspace that oasis_decode_step needs (and oasis_sparse_decode_attn
- * with table_stride == oasis_table_stride(dims)), in bytes, a multiple of 256.
- * It holds the per-split attention partials.  0 if dims is invalid. */
+/* Device workspace of the decode steps (oasis_decode_step, _overlapped, _pool,
+ * oasis_decode_layer_pipelined), in bytes, a multiple of 256; it also serves
+ * oasis_sparse_decode_attn with table_stride == oasis_table_stride(dims).  It
+ * holds the per-split attention partials and, after them, the hand-off region
+ * through which the workgroups of the one-launch step (see
+ * oasis_decode_step_overlapped) pass scores and partials to each other.
+ * The hand-off region must be zero before the workspace first serves a step:
+ * allocate it zero-filled or call oasis_workspace_clear once.  Every step leaves
+ * it zero again, so the workspace can serve any number of steps and layers of
+ * the same dims in turn (one at a time).  Before it serves steps of other dims
+ * (whose regions lie elsewhere), call oasis_workspace_clear with the new dims.
+ * 0 if dims is invalid. */
 size_t oasis_workspace_bytes(const oasis_dims* dims);
+
+/* Zero-fills the hand-off region of a step workspace for `dims` on `stream` (a
+ * fill kernel, so the call can be captured in a graph).  Needed once after
+ * allocation unless the memory is allocated zero-filled, when the workspace
+ * moves to other dims, and after a step whose status word (below) is non-zero.
+ * ws_bytes >= oasis_workspace_bytes(dims), else OASIS_ERR_WORKSPACE. */
+oasis_status oasis_workspace_clear(const oasis_dims* dims, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* Byte offset, inside the step workspace, of the hand-off status word (uint32).
+ * It stays 0 unless a workgroup of a one-launch step waited past its bound (about
+ * 10 ms) for the scores or partials it needs; it then holds bit 1 (scores) or bit
+ * 2 (partials), the outputs of that step are unspecified and the workspace must
+ * be cleared.  A wait never hangs the device.  0 if dims is invalid. */
+size_t oasis_workspace_status_offset(const oasis_dims* dims);
 
 /* Device workspace that oasis_sparse_decode_attn needs for a given table
  * stride, in bytes, a multiple of 256.  0 if an argument is invalid. */
@@ -256,10 +280,16 @@ oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void
  *   background: oasis_score_summaries, then the selection and the plan, reading
  *     `resident` and writing the next slot table to `resident_next` (and plan,
  *     table, table_count for it), as oasis_decode_step does.
- * The halves share only inputs; they are queued on `stream` as two launches that
- * each hold work of both halves (scoring with the attention's block gathering,
- * then the selection and plan with the attention's merge), so the
- * latency-bound parts of one half run under the other's streaming.
+ * The halves share only inputs, so their work items sit in the same grids.  Up
+ * to 32 query rows (G * Q), 4 query heads per KV head, K = 256 and 2048 blocks
+ * per KV head, the step is ONE launch: scoring workgroups, one selection-and-plan
+ * workgroup per KV head that takes its head's scores over from the scoring
+ * workgroups, the attention split workgroups, and one merge workgroup per query
+ * head that takes the splits' partials over, through the hand-off region of the
+ * workspace (it must be zero before the first step; see oasis_workspace_bytes).
+ * The selection then runs while the attention still streams K and V.  Larger
+ * shapes take two launches: scoring with the attention's block gathering, then
+ * the selection and plan with the attention's merge.
  * resident_next is required and must not overlap `resident`; the caller swaps
  * the two between steps.  Other arguments as for oasis_decode_step. */
 oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q, const void* summ,
@@ -273,9 +303,9 @@ oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q,
 
 /* oasis_decode_step_overlapped with timing markers, for measurement:
  * events[0..2] (created by the caller with hipEventCreate) are recorded on
- * `stream` before the first launch (scoring with the attention's block
- * gathering), between the two launches, and after the second (selection and
- * plan with the attention merge).  The kernels queued are the same. */
+ * `stream` before the first launch, after it, and after the second launch (the
+ * selection and plan with the attention merge; when the step is one launch,
+ * events[1] and events[2] both follow it).  The kernels queued are the same. */
 oasis_status oasis_decode_step_overlapped_timed(
     const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
     const int32_t* seq_lens, float* scores, int32_t* topk, const int32_t* resident,

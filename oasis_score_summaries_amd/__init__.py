@@ -13,5 +13,5 @@ from ._lib import (LIB_PATH, LayerIO, OasisDims, OasisError, PipelinedLayers,  #
                    execute_plan, fill_working_set, sparse_decode_attn_pool, window_ring_slots,
                    build_summaries, decode_step, decode_step_overlapped, dims_for,
                    exported_symbols, fetch_cap, load, make_dims, score_summaries,
-                   sparse_decode_attn, sparse_decode_attn_resident, table_stride, topk_blocks,
-                   workspace_bytes)
+                   sparse_decode_attn, sparse_decode_attn_resident, step_workspace, table_stride,
+                   topk_blocks, workspace_bytes, workspace_clear, workspace_status)

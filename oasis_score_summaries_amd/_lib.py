@@ -56,6 +56,8 @@ _SIGNATURES = {
     "oasis_fetch_cap": (ctypes.c_int32, [_DIMS]),
     "oasis_table_stride": (ctypes.c_int32, [_DIMS]),
     "oasis_workspace_bytes": (ctypes.c_size_t, [_DIMS]),
+    "oasis_workspace_clear": (ctypes.c_int, [_DIMS, _P, ctypes.c_size_t, _P]),
+    "oasis_workspace_status_offset": (ctypes.c_size_t, [_DIMS]),
     "oasis_attn_workspace_bytes": (ctypes.c_size_t, [_DIMS, ctypes.c_int32]),
     "oasis_build_summaries": (ctypes.c_int, [_DIMS, _P, _P, _P, _P]),
     "oasis_score_summaries": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P]),
@@ -346,6 +348,27 @@ def sparse_decode_attn_resident(dims: OasisDims, q: torch.Tensor, k: torch.Tenso
     return out, lse
 
 
+def step_workspace(dims: OasisDims, device) -> torch.Tensor:
+    """A workspace for the decode steps, zero-filled as the one-launch step requires
+    before its first use (each step leaves it zero)."""
+    return torch.zeros(workspace_bytes(dims), dtype=torch.uint8, device=_norm_device(device))
+
+
+def workspace_clear(dims: OasisDims, ws: torch.Tensor, stream=None) -> None:
+    """Zero-fills the hand-off region of a step workspace (oasis_workspace_clear)."""
+    _check(load().oasis_workspace_clear(ctypes.byref(dims), _ptr(ws), ws.numel(), _stream(stream)),
+           "oasis_workspace_clear")
+
+
+def workspace_status(dims: OasisDims, ws: torch.Tensor) -> int:
+    """The hand-off status word of a step workspace (0 unless a wait of a one-launch
+    step timed out); reads it after the work queued so far."""
+    off = int(load().oasis_workspace_status_offset(ctypes.byref(dims)))
+    if off == 0 or off + 4 > ws.numel():
+        raise ValueError("the workspace is not a step workspace for these dims")
+    return int(ws[off:off + 4].view(torch.int32).item())
+
+
 class StepBuffers:
     """Outputs and workspace of oasis_decode_step, allocated once and reused."""
 
@@ -358,7 +381,12 @@ class StepBuffers:
             dims, dev, None, None, None, None)
         self.out = torch.empty(s["out"], dtype=torch.float32, device=dev)
         self.lse = torch.empty(s["lse"], dtype=torch.float32, device=dev)
-        self.ws = torch.empty(workspace_bytes(dims), dtype=torch.uint8, device=dev)
+        self.ws = step_workspace(dims, dev)
+        self.dims = dims
+
+    def status(self) -> int:
+        """The workspace's hand-off status word (0 unless a wait timed out)."""
+        return workspace_status(self.dims, self.ws)
 
     def as_dict(self) -> Dict[str, torch.Tensor]:
         return {n: getattr(self, n) for n in ("scores", "topk", "plan", "plan_count", "table",

@@ -120,7 +120,24 @@ int32_t oasis_table_stride(const oasis_dims* dims) {
 size_t oasis_workspace_bytes(const oasis_dims* dims) {
   oasis::Dims d;
   if (check_dims(dims, &d) != OASIS_OK) return 0;
-  return oasis::attn_workspace_bytes(d, d.table_stride);
+  return oasis::step_workspace_bytes(d);
+}
+
+size_t oasis_workspace_status_offset(const oasis_dims* dims) {
+  oasis::Dims d;
+  if (check_dims(dims, &d) != OASIS_OK) return 0;
+  return oasis::handoff_status_offset(d);
+}
+
+oasis_status oasis_workspace_clear(const oasis_dims* dims, void* ws, size_t ws_bytes, hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  const size_t need = oasis::step_workspace_bytes(d);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(OASIS_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                ws == nullptr ? (size_t)0 : ws_bytes);
+  return hip_status(oasis::launch_clear_handoff(d, ws, stream), "workspace_clear");
 }
 
 size_t oasis_attn_workspace_bytes(const oasis_dims* dims, int32_t table_stride) {
@@ -261,7 +278,7 @@ static oasis_status check_step_args(const oasis_dims* dims, oasis::Dims& d, cons
   OASIS_REQUIRE(table_count);
   OASIS_REQUIRE(out);
   if (!isfinite(scale)) return fail(OASIS_ERR_INVALID_ARG, "scale must be finite");
-  const size_t need = oasis::attn_workspace_bytes(d, d.table_stride);
+  const size_t need = oasis::step_workspace_bytes(d);
   if (ws == nullptr || ws_bytes < need)
     return fail(OASIS_ERR_WORKSPACE, "decode step needs %zu workspace bytes, got %zu", need,
                 ws == nullptr ? (size_t)0 : ws_bytes);
@@ -612,7 +629,7 @@ oasis_status oasis_decode_layer_pipelined(const oasis_dims* dims, const oasis_la
     OASIS_REQUIRE(layer->scores);
     OASIS_REQUIRE(layer->out);
     if (!isfinite(scale)) return fail(OASIS_ERR_INVALID_ARG, "scale must be finite");
-    const size_t need = oasis::attn_workspace_bytes(d, d.table_stride);
+    const size_t need = oasis::step_workspace_bytes(d);
     if (layer->ws == nullptr || layer->ws_bytes < need)
       return fail(OASIS_ERR_WORKSPACE, "layer needs %zu workspace bytes, got %zu", need,
                   layer->ws == nullptr ? (size_t)0 : layer->ws_bytes);

@@ -23,6 +23,7 @@ constexpr int kWavesPerWG = OASIS_WAVES_PER_WG;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
 // ---- sequence geometry (identical on host and device) ----------------------------
 // Blocks hold 1 << bshift tokens (bshift 3..6: 8 to 64 tokens; 16 is the default).
@@ -62,6 +63,96 @@ __device__ inline void xcd_item(int i, int gx, int nh, bool by_xcd, int& x, int&
   head = i / gx;
 }
 __host__ inline bool place_by_xcd(int query_rows) { return query_rows >= 64; }
+
+// ---- hand-offs between workgroups of one launch -----------------------------------
+// Producers write their data with device-scope stores (written through to where every
+// XCD reads them), then store a flag word of their own (1 = "my stores are issued");
+// no producer waits, and no two producers write one word (an arrival counter shared
+// by many producers serializes their atomics).  A consumer wave polls the flags of its
+// producers, one per lane, then reads the data with device-scope loads.  As nothing
+// orders a producer's data before its flag, the data carry their own validity: zero
+// means "not written yet", and a consumer reads again until every word it needs is
+// non-zero.  Consumers write zeros back over what they read (flags and data), so that
+// every region is zero again when the launch ends.  All waits are bounded by the
+// constant-rate clock (100 MHz): past kSpinTicks the consumer raises a bit in the
+// status word and goes on, so no launch can hang.
+constexpr uint64_t kSpinTicks = 1000000;  // 10 ms
+constexpr uint32_t kStatusScoreWait = 1u, kStatusAttnWait = 2u;
+constexpr int kDevScopeAux = 0x10;  // buffer-instruction cache policy: device scope (sc1)
+
+__device__ inline uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void raise_status(uint32_t* status, uint32_t bit) {
+  (void)__hip_atomic_fetch_or(status, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// One wave waits until flags[0 .. n) are all non-zero (lane i polls flags i, i + 64,
+// ...; n <= 256), then clears them.  False (and the status bit raised) on time-out.
+// Every lane of the wave must call it.
+__device__ inline bool wait_flags(uint32_t* flags, int n, uint32_t* status, uint32_t bit) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  bool ok = true;
+  for (;;) {
+    bool mine = true;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = c * 64 + lane;
+      if (i < n && ld_dev(flags + i) == 0u) mine = false;
+    }
+    if (__ballot(!mine) == 0ull) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+      if (lane == 0) raise_status(status, bit);
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (ok) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = c * 64 + lane;
+      if (i < n) st_dev(flags + i, 0u);
+    }
+  }
+  return ok;
+}
+// Reads a device-scope word until it is non-zero (bounded as above; on time-out the
+// zero is returned and the status bit raised).
+__device__ inline uint32_t ld_dev_nonzero(const uint32_t* p, uint32_t* status, uint32_t bit) {
+  uint32_t w = ld_dev(p);
+  if (w != 0u) return w;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while ((w = ld_dev(p)) == 0u) {
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+      raise_status(status, bit);
+      return 0u;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return w;
+}
+// A float as a non-zero word and back: the bits inverted, NaNs made the canonical
+// quiet NaN first (its inverse is not zero), so every value, -inf and 0 included,
+// travels as a non-zero word.
+__device__ inline uint32_t enc_f32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return ~((x != x) ? 0x7fc00000u : u);
+}
+__device__ inline float dec_f32(uint32_t w) { return __uint_as_float(~w); }
+
+// The hand-off region of the one-launch step (inside the caller's workspace).
+struct Handoff {
+  uint32_t* flag_score;  // [B*H, score_waves]: one flag per scoring wave
+  uint32_t* flag_attn;   // [B*H*G, nsplit]: one flag per split and query head
+  uint32_t* status;      // stays 0 unless a wait timed out
+  uint32_t* mbox;        // [B*H, NB]: order keys of the candidate scores (never 0)
+  uint32_t* part;        // [B*H, nsplit, G, kRec]: encoded split records
+  int score_waves;       // scoring waves per (sequence, KV head), <= 64
+};
 
 // ---- bf16 bit helpers -------------------------------------------------------------
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

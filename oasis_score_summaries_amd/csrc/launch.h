@@ -28,6 +28,15 @@ inline int attn_units(const Dims& d, int table_stride) {
 }
 AttnSplit attn_split(const Dims& d, int table_stride);
 size_t attn_workspace_bytes(const Dims& d, int table_stride);
+// Workspace of the decode steps: the split records, then the hand-off region of the
+// one-launch step (which must be zero before the first such step; each leaves it zero).
+size_t step_workspace_bytes(const Dims& d);
+// Byte offset of the hand-off status word (non-zero after a wait that timed out).
+size_t handoff_status_offset(const Dims& d);
+// Whether the overlapped step runs as one launch for these sizes.
+bool one_launch_fits(const Dims& d);
+// Zero-fills the hand-off region of a step workspace.
+hipError_t launch_clear_handoff(const Dims& d, void* ws, hipStream_t stream);
 
 hipError_t launch_build_summaries(const Dims& d, const void* k, const int32_t* seq_lens, void* summ,
                                   hipStream_t stream);

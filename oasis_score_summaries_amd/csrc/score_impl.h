@@ -33,10 +33,14 @@ struct ScoreArgs {
 };
 
 // One workgroup: block range `bx` (kScoreBlocksPerWG candidate blocks) of (sequence,
-// KV head) `bh`.  Every thread of the workgroup calls it.
-template <int RT>
+// KV head) `bh`.  Every thread of the workgroup calls it.  With HANDOFF, each
+// candidate's order key also goes to the mailbox of `ho` (device-scope stores) and
+// every wave then sets its flag, so that a selection workgroup of the same launch can
+// take the scores over.
+template <int RT, bool HANDOFF = false>
 __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreShared<RT>& sh,
-                                                        const ScoreArgs& a) {
+                                                        const ScoreArgs& a,
+                                                        const Handoff* ho = nullptr) {
   const u32x4* __restrict__ q = a.q;
   const u32x4* __restrict__ summ = a.summ;
   const int heads = a.heads, max_blocks = a.max_blocks, rows = a.rows, window = a.window;
@@ -53,6 +57,8 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
       const int jb = bx * kScoreBlocksPerWG + j;
       if (jb < max_blocks) out[jb] = -INFINITY;
     }
+    if (HANDOFF && (threadIdx.x & 63) == 0)
+      st_dev(ho->flag_score + (size_t)bh * ho->score_waves + bx * kScoreWaves + (threadIdx.x >> 6), 1u);
     return;
   }
 
@@ -126,7 +132,12 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
     if (grp == 0 && jb < max_blocks) out[jb] = (jb < n_cand) ? m : -INFINITY;
+    if (HANDOFF && grp == 0 && jb < n_cand) {
+      const uint32_t key = order_key(m);
+      st_dev(ho->mbox + (size_t)bh * max_blocks + jb, key != 0u ? key : 1u);  // 0 marks "not written"
+    }
   }
+  if (HANDOFF && lane == 0) st_dev(ho->flag_score + (size_t)bh * ho->score_waves + bx * kScoreWaves + wave, 1u);
 }
 
 // Host side: the argument block of the scoring work for `d`.

@@ -125,39 +125,57 @@ template <int THREADS, int ITEMS>
 constexpr bool kCanStage = ITEMS * THREADS * sizeof(float) <= sizeof(SelectShared<THREADS, ITEMS>::bucket);
 
 // row holds NB readable scores; every thread's scores are requested before anything
-// waits (the length, and with it n_cand, arrives meanwhile).  With `res_score` (only
-// when kCanStage), the scores also pass through LDS and *res_score receives the score
-// of `res_block` (-inf outside the candidates), so that no second global read
-// depends on the first.
-template <int THREADS, int ITEMS>
+// waits (the length, and with it n_cand, arrives meanwhile).  With `res_key` (only
+// when kCanStage), the keys also pass through LDS and *res_key receives the order key
+// of the score of `res_block` (that of -inf outside the candidates), so that no second
+// global read depends on the first.
+// MBOX: the keys come from the mailbox row `mrow` of a hand-off instead (the caller has
+// waited for the head's arrivals): each candidate's key is read until it is non-zero
+// and then cleared, leaving the row zero.
+template <int THREADS, int ITEMS, bool MBOX = false>
 __device__ __attribute__((always_inline)) int topk_select(const float* __restrict__ row, int n_cand, int K,
                            SelectShared<THREADS, ITEMS>& sh, int NB, PlanBitmaps* bm = nullptr,
-                           int res_block = -1, float* res_score = nullptr) {
+                           int res_block = -1, uint32_t* res_key = nullptr,
+                           uint32_t* mrow = nullptr, uint32_t* status = nullptr) {
   constexpr int NW = THREADS / 64;
   constexpr bool kStage = kCanStage<THREADS, ITEMS>;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   uint32_t key[ITEMS];
-  float x[kStage ? ITEMS : 1];  // the raw scores are kept only where they are staged
+  // MBOX: the row through a buffer resource (device-scope loads issued together).
+  const __amdgpu_buffer_rsrc_t mr =
+      __builtin_amdgcn_make_buffer_rsrc(MBOX ? (void*)mrow : (void*)row, (short)0, MBOX ? NB * 4 : 0, 0x00020000);
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int e = i * THREADS + tid;
-    const float xv = row[e < NB ? e : NB - 1];
-    key[i] = order_key(xv);
-    if (kStage) x[i] = xv;
+    const int ec = e < NB ? e : NB - 1;
+    key[i] = MBOX ? __builtin_amdgcn_raw_buffer_load_b32(mr, (uint32_t)ec * 4u, 0, kDevScopeAux)
+                  : order_key(row[ec]);
   }
-  if (res_score != nullptr) *res_score = -INFINITY;
+  if (res_key != nullptr) *res_key = order_key(-INFINITY);
   const int m = n_cand < K ? n_cand : K;
   if (m <= 0) return 0;  // uniform across the workgroup
+  if (MBOX) {
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {  // a key still zero has not arrived yet: read it again
+      const int e = i * THREADS + tid;
+      if (e < n_cand && key[i] == 0u) key[i] = ld_dev_nonzero(mrow + e, status, kStatusScoreWait);
+    }
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const int e = i * THREADS + tid;
+      if (e < n_cand) __builtin_amdgcn_raw_buffer_store_b32(0u, mr, (uint32_t)e * 4u, 0, kDevScopeAux);
+    }
+  }
 
   uint32_t lmax = 0u, lmin = 0xffffffffu;
-  float* staged = reinterpret_cast<float*>(sh.bucket);
+  uint32_t* staged = reinterpret_cast<uint32_t*>(sh.bucket);
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
     const int e = i * THREADS + tid;
     if (e < n_cand) {
       lmax = max(lmax, key[i]);
       lmin = min(lmin, key[i]);
-      if (kStage && res_score != nullptr) staged[e] = x[kStage ? i : 0];
+      if (kStage && res_key != nullptr) staged[e] = key[i];
     } else {
       key[i] = 0u;
     }
@@ -171,9 +189,9 @@ __device__ __attribute__((always_inline)) int topk_select(const float* __restric
   __syncthreads();
   if (bm != nullptr && res_block >= 0 && res_block < NB)   // after the clear, before the last barrier
     atomicOr(&bm->res[res_block >> 5], 1u << (res_block & 31));
-  // The staged scores are overwritten only after the first radix pass's barriers.
-  if (kCanStage<THREADS, ITEMS> && res_score != nullptr && res_block >= 0 && res_block < n_cand)
-    *res_score = staged[res_block];
+  // The staged keys are overwritten only after the first radix pass's barriers.
+  if (kCanStage<THREADS, ITEMS> && res_key != nullptr && res_block >= 0 && res_block < n_cand)
+    *res_key = staged[res_block];
   uint32_t kmax = 0u, kmin = 0xffffffffu;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -325,19 +343,21 @@ __device__ __attribute__((always_inline)) int topk_select(const float* __restric
   return m;
 }
 
-// The resident slot a thread t < K owns (-1 for the other threads) and that block's
-// score (-inf when the block is out of range).  Loaded by the caller before the
-// selection so that the latency overlaps it.
+// The resident slot a thread t < K owns (-1 for the other threads) and the order key
+// of that block's score (that of -inf when the block is out of range or not a
+// candidate).  Loaded by the caller before the selection so that the latency
+// overlaps it.
 struct ResidentSlot {
   int block;
-  float score;
+  uint32_t key;
 };
 __device__ inline ResidentSlot load_resident_slot(const int32_t* res, const float* __restrict__ srow,
                                                   int K, int NB) {
   const int tid = threadIdx.x;
   const int r = tid < K ? res[tid] : -1;
   const bool ok = r >= 0 && r < NB;
-  return ResidentSlot{r, srow[ok ? r : 0]};
+  const float sc = srow[ok ? r : 0];
+  return ResidentSlot{r, order_key(ok ? sc : -INFINITY)};
 }
 
 // Applies the capped-eviction rule for one (sequence, KV head).  Thread t < K passes
@@ -377,7 +397,7 @@ __device__ __attribute__((always_inline)) void plan_apply(
   }
   // Worst-first order of stale slots: ascending score, equal scores higher block first.
   const uint64_t st_me =
-      stale ? (((uint64_t)order_key(r_ok ? rs.score : -INFINITY) << 32) | (uint32_t)(~(uint32_t)r_i))
+      stale ? (((uint64_t)(r_ok ? rs.key : order_key(-INFINITY)) << 32) | (uint32_t)(~(uint32_t)r_i))
             : ~0ull;
   __syncthreads();
   int n_new, n_empty, n_stale;
@@ -482,23 +502,35 @@ struct TopkPlanArgs {
 
 // Selection and plan of (sequence, KV head) `bh` in one workgroup; the bitmaps are
 // cleared while the selection runs.  Every thread of the workgroup calls it.
-template <int THREADS, int ITEMS>
+// MBOX: the scores are handed over by the scoring workgroups of the same launch
+// through `ho` (wave 0 waits for the flags of the head's scoring waves and clears
+// them, then every thread reads its keys from the mailbox).
+template <int THREADS, int ITEMS, bool MBOX = false>
 __device__ __attribute__((always_inline)) void topk_plan_wg(int bh, TopkPlanShared<THREADS, ITEMS>& sh,
-                                                            PlanBitmaps& bm, const TopkPlanArgs& a) {
+                                                            PlanBitmaps& bm, const TopkPlanArgs& a,
+                                                            const Handoff* ho = nullptr) {
+  static_assert(!MBOX || kCanStage<THREADS, ITEMS>, "mailbox keys are staged for the resident lookup");
   const int NB = a.NB, K = a.K, C = a.C, T = a.T;
   const int len = clamp_len(a.seq_lens[bh / a.heads], NB, a.bshift);
   const int n_cand = first_window_block(len, a.window, a.bshift);
   const float* srow = a.scores + (size_t)bh * NB;
   ResidentSlot rs;
-  if (kCanStage<THREADS, ITEMS>) {  // the score comes from the selection's staging
+  if (kCanStage<THREADS, ITEMS>) {  // the key comes from the selection's staging
     rs.block = (int)threadIdx.x < K ? a.resident[(size_t)bh * K + threadIdx.x] : -1;
-    rs.score = -INFINITY;
+    rs.key = order_key(-INFINITY);
   } else {
     rs = load_resident_slot(a.resident + (size_t)bh * K, srow, K, NB);
   }
   clear_bitmaps(bm, NB);
-  const int m = topk_select<THREADS, ITEMS>(srow, n_cand, K, sh.t, NB, &bm, rs.block,
-                                            kCanStage<THREADS, ITEMS> ? &rs.score : nullptr);
+  if (MBOX) {
+    if (threadIdx.x < 64)
+      wait_flags(ho->flag_score + (size_t)bh * ho->score_waves, ho->score_waves, ho->status, kStatusScoreWait);
+    __syncthreads();
+  }
+  const int m = topk_select<THREADS, ITEMS, MBOX>(srow, n_cand, K, sh.t, NB, &bm, rs.block,
+                                                  kCanStage<THREADS, ITEMS> ? &rs.key : nullptr,
+                                                  MBOX ? ho->mbox + (size_t)bh * NB : nullptr,
+                                                  MBOX ? ho->status : nullptr);
   if (m == 0) {  // the selection returned at once: mark the resident set here
     __syncthreads();
     if (rs.block >= 0 && rs.block < NB) atomicOr(&bm.res[rs.block >> 5], 1u << (rs.block & 31));

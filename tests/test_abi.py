@@ -44,7 +44,7 @@ def _dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 25
+    assert len(names) == 27
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.exported_symbols())
@@ -120,11 +120,17 @@ def test_null_pointers_rejected(lib):
 @cpu_only
 def test_workspace_and_table_stride_checks(lib):
     d = _dims()
-    need = lib.oasis_workspace_bytes(ctypes.byref(d))
-    assert need > 0 and need % 256 == 0
+    step_need = lib.oasis_workspace_bytes(ctypes.byref(d))
+    assert step_need > 0 and step_need % 256 == 0
     T = lib.oasis_table_stride(ctypes.byref(d))
     assert T == 16 + 4 + 1
-    assert lib.oasis_attn_workspace_bytes(ctypes.byref(d), T) == need
+    need = lib.oasis_attn_workspace_bytes(ctypes.byref(d), T)
+    assert need > 0 and need % 256 == 0
+    # the step workspace: the split records, then the hand-off region (counters, status
+    # word, a score mailbox of B*H*NB words, a second region of split records)
+    assert step_need >= 2 * need + 2 * 2 * 64 * 4
+    off = lib.oasis_workspace_status_offset(ctypes.byref(d))
+    assert need <= off < step_need and off % 4 == 0
     assert lib.oasis_attn_workspace_bytes(ctypes.byref(d), 0) == 0
     st = lib.oasis_sparse_decode_attn(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, T, FAKE, 0.1,
                                       FAKE, None, FAKE, need - 1, None)
@@ -136,13 +142,18 @@ def test_workspace_and_table_stride_checks(lib):
                                       float("inf"), FAKE, None, FAKE, need, None)
     assert st == INVALID_ARG
     st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
-                               FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, None, need, None)
+                               FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, None, step_need, None)
     assert st == WORKSPACE
+    st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, FAKE, step_need - 1, None)
+    assert st == WORKSPACE
+    assert lib.oasis_workspace_clear(ctypes.byref(d), None, step_need, None) == WORKSPACE
+    assert lib.oasis_workspace_clear(ctypes.byref(d), FAKE, step_need - 1, None) == WORKSPACE
     # overlapping double-buffered slot tables are rejected
     res = ctypes.c_void_p(0x10000)
     st = lib.oasis_decode_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, res,
                                ctypes.c_void_p(0x10000 + 64), FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None,
-                               FAKE, need, None)
+                               FAKE, step_need, None)
     assert st == INVALID_ARG and b"overlap" in lib.oasis_last_error()
 
 
@@ -179,8 +190,11 @@ def test_overlapped_step_argument_checks(lib):
     st = lib.oasis_sparse_decode_attn_resident(ctypes.byref(d), FAKE, FAKE, FAKE, None, FAKE, 0.1,
                                                FAKE, None, FAKE, need, None)
     assert st == INVALID_ARG
+    # the attention over slot tables needs the split records only
+    attn_need = lib.oasis_attn_workspace_bytes(ctypes.byref(d), lib.oasis_table_stride(ctypes.byref(d)))
+    assert attn_need < need
     st = lib.oasis_sparse_decode_attn_resident(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1,
-                                               FAKE, None, FAKE, need - 1, None)
+                                               FAKE, None, FAKE, attn_need - 1, None)
     assert st == WORKSPACE
 
 
@@ -214,8 +228,9 @@ def test_working_set_argument_checks(lib):
     assert lib.oasis_append_token(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, P(k), None, P(rk), P(rv),
                                   None) == INVALID_ARG                            # k without v
     need = lib.oasis_workspace_bytes(ctypes.byref(d))
+    attn_need = lib.oasis_attn_workspace_bytes(ctypes.byref(d), lib.oasis_table_stride(ctypes.byref(d)))
     assert lib.oasis_sparse_decode_attn_pool(ctypes.byref(d), FAKE, P(pk), P(pv), P(rk), P(rv), FAKE,
-                                             FAKE, 0.1, FAKE, None, FAKE, need - 1, None) == WORKSPACE
+                                             FAKE, 0.1, FAKE, None, FAKE, attn_need - 1, None) == WORKSPACE
     st = lib.oasis_decode_step_pool(ctypes.byref(d), FAKE, FAKE, P(k), P(v), P(pk), P(pv), P(rk),
                                     P(rv), FAKE, FAKE, FAKE, P(0x30000000), P(0x30000000), FAKE, FAKE,
                                     FAKE, FAKE, 0.1, FAKE, None, FAKE, need, None)

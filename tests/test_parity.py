@@ -674,6 +674,7 @@ def test_overlapped_step_repeated_over_rotating_inputs(lib):
                                    default_scale(), buffers=bufs)
         runs.append((bufs, rn))
     torch.cuda.synchronize()
+    assert lib.workspace_status(sets[0][0], shared_ws) == 0, "a hand-off wait timed out"
     for i, (bufs, rn) in enumerate(runs):
         _, _, _, _, ref_out, alone = sets[i % n_sets]
         got = _step_outputs(bufs, rn)
@@ -809,6 +810,74 @@ def test_append_then_step_loop_both_step_orders_agree(lib):
     assert reached > 0, "no resident block lay in the window"
     # the window moved past some of them: they are historical blocks now
     assert any(ref.first_window_block(int(Ld[b]), W) > w0_start[b] for b in range(B))
+
+
+@pytest.mark.parametrize("shape", ["tiny", "qwen3_8b_2x2", "short"])
+def test_one_launch_step_leaves_the_handoff_region_zero(lib, shape):
+    """The overlapped step at sizes it runs as one launch: after every step the
+    hand-off region of the workspace (counters, status word, score mailbox, second
+    record region) is zero again and the status word never records a timed-out wait;
+    the step's outputs equal the oracle's, and consecutive steps with different sizes
+    share the workspace."""
+    if shape == "tiny":
+        w = synth.WORKLOADS["tiny_4k"].with_(batch=2, fetch_ratio=0.25)
+    elif shape == "qwen3_8b_2x2":
+        w = synth.WORKLOADS["qwen3_8b_32k"].with_(batch=2, num_kv_heads=2)
+    else:
+        w = synth.WORKLOADS["tiny_4k"].with_(batch=3, ctx=1024, min_len=60, fetch_ratio=1.0)
+    _say(f"one-launch hand-off region, {shape}")
+    d = lib.dims_for(w)
+    inp = {kk: t.to(DEV) for kk, t in synth.generate(w, "cpu").items()}
+    summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
+    sel = lib.topk_blocks(d, lib.score_summaries(d, inp["q"], summ, inp["seq_lens"]), inp["seq_lens"])
+    lens = inp["seq_lens"].cpu()
+    resident = synth.resident_from_selection(w, sel, lens).to(DEV)
+    bufs = lib.StepBuffers(d, DEV)
+    attn_need = lib.workspace_bytes(d, lib.table_stride(d))
+    for step in range(3):
+        rn = torch.empty_like(resident)
+        got = lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], resident, rn,
+                                         buffers=bufs)
+        torch.cuda.synchronize()
+        assert lib.workspace_status(d, bufs.ws) == 0
+        tail = bufs.ws[attn_need:]
+        assert int(torch.count_nonzero(tail)) == 0, f"step {step}: hand-off region not left zero"
+        if step == 0:
+            exp = ref.decode_step_overlapped(f64(inp["q"]), f64(summ), f64(inp["k"]), f64(inp["v"]),
+                                             lens.numpy(), i64(resident), w.top_k, w.window, w.cap,
+                                             default_scale(), w.block)
+            gs = f64(got["scores"])
+            check_scores(gs, exp["scores"], score_floor(f64(inp["q"]), f64(summ)), "scores")
+            np.testing.assert_array_equal(i64(got["topk"]), ref.topk_blocks(gs, lens.numpy(), w.top_k,
+                                                                             w.window, w.block))
+            pl = ref.build_plan(gs, i64(got["topk"]), i64(resident), lens.numpy(), w.cap, w.window, w.block)
+            for key in ("plan_count", "table", "table_count"):
+                np.testing.assert_array_equal(i64(got[key]), pl[key], err_msg=key)
+            np.testing.assert_array_equal(i64(rn), pl["resident"])
+            np.testing.assert_allclose(f64(got["out"]), exp["out"], rtol=0, atol=OUT_ATOL)
+            np.testing.assert_allclose(f64(got["lse"]), exp["lse"], rtol=0, atol=OUT_ATOL)
+        resident = rn
+    # the same workspace then serves steps of other sizes (fewer heads, other cap), once
+    # cleared for them
+    w2 = w.with_(num_kv_heads=1, fetch_ratio=0.5)
+    d2 = lib.dims_for(w2)
+    if lib.workspace_bytes(d2) <= bufs.ws.numel():
+        inp2 = {kk: t.to(DEV) for kk, t in synth.generate(w2, "cpu").items()}
+        summ2 = lib.build_summaries(d2, inp2["k"], inp2["seq_lens"])
+        b2 = lib.StepBuffers(d2, DEV)
+        b2.ws = bufs.ws
+        lib.workspace_clear(d2, bufs.ws)
+        r2 = resident[:, :1].contiguous()
+        rn2 = torch.empty_like(r2)
+        got2 = lib.decode_step_overlapped(d2, inp2["q"], summ2, inp2["k"], inp2["v"], inp2["seq_lens"], r2,
+                                          rn2, buffers=b2)
+        torch.cuda.synchronize()
+        assert lib.workspace_status(d2, bufs.ws) == 0
+        assert int(torch.count_nonzero(bufs.ws[lib.workspace_bytes(d2, lib.table_stride(d2)):])) == 0
+        table, tc = ref.resident_table(i64(r2), inp2["seq_lens"].cpu().numpy(), w2.window, w2.block)
+        eo, el = ref.sparse_attention(f64(inp2["q"]), f64(inp2["k"]), f64(inp2["v"]), table, tc,
+                                      inp2["seq_lens"].cpu().numpy(), default_scale(), w2.block)
+        np.testing.assert_allclose(f64(got2["out"]), eo, rtol=0, atol=OUT_ATOL)
 
 
 @pytest.mark.parametrize("overlapped", [False, True])
