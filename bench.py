@@ -78,13 +78,15 @@ def algorithmic_bytes(w, lens, table_count) -> dict:
     q_all = w.batch * H * G * Q * 128 * 2
     q_target = w.batch * H * G * 128 * 2
     out = w.batch * H * G * (128 + 1) * 4
-    scores = w.batch * H * w.max_blocks * 4
     step = cand * SUMMARY_BYTES + blocks * kvb + q_all + out
+    # Algorithmic bytes only: the scores, the split partials and the plan's tables are
+    # intermediates of the implementation, not of the method, and count as overhead.
     return {
         "step": step,
-        "score": cand * SUMMARY_BYTES + q_all + scores,
+        "score": cand * SUMMARY_BYTES + q_all,
         "attn_split": blocks * kvb + q_target,
-        "score_attn_split": cand * SUMMARY_BYTES + q_all + scores + blocks * kvb,
+        "launch1": cand * SUMMARY_BYTES + q_all + blocks * kvb,
+        "launch2": out,
         "summaries": cand * SUMMARY_BYTES,
         "kv": blocks * kvb,
         "units": {"candidate_block_heads": cand, "table_blocks": blocks},
@@ -119,16 +121,23 @@ def copy_bandwidth(torch, dev, nbytes: int = 1 << 30, reps: int = 20) -> float:
     return gbps
 
 
-# HBM traffic of the dominant kernel, measured offline with rocprofv3 byte counters
+# HBM traffic of the overlapped step, measured offline with rocprofv3 byte counters
 # (FETCH_SIZE and WRITE_SIZE, one run each, scaled by what they read for the
-# --calibrate copy) and kept under profiles/ with a hash of the kernel's sources.
-# bench.py reports it only while those sources are unchanged.  The dominant kernel
-# is the overlapped step's first launch, scoring with attention gathering.
-LAUNCH1_KERNELS = ("score_attn_kernel",)
+# --calibrate copy) and kept under profiles/ with a hash of the kernel sources.
+# bench.py reports it only while those sources are unchanged.
 
 
-def traffic_file(kernel: str, workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+def step_kernels(oa, d, w) -> tuple:
+    """The kernels of the overlapped step's two launches for dims d (launch 1, launch 2)."""
+    if oa.overlapped_selects_in_launch1(d):
+        return ("step_kernel", "attn_merge_kernel")
+    if w.group * w.queries <= 96:
+        return ("score_attn_kernel", "select_merge_kernel")
+    return ("score_kernel+attn_split_kernel", "select_merge_kernel")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"overlapped_step_{workload}_traffic.txt")
 
 
 KERNEL_SOURCES = ("fused.hip", "attention.hip", "score_impl.h", "attention_impl.h", "select_impl.h", "common.h",
@@ -144,24 +153,35 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(kernel: str, workload: str):
-    """Bytes per launch from the traffic file, or None if absent, for another
-    workload, or taken on other kernel sources."""
+def measured_traffic(workload: str, kernels: tuple):
+    """HBM bytes per launch of each of the step's kernels and per step, from the
+    traffic file; None if it is absent, for another workload or other kernels, or
+    taken on other kernel sources."""
     try:
-        with open(traffic_file(kernel, workload)) as f:
+        with open(traffic_file(workload)) as f:
             kv = dict(line.split("=", 1) for line in f.read().splitlines()
                       if "=" in line and not line.startswith("#"))
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("workload") != workload or kv.get("sources_sha256") != kernel_sources_sha256():
+    if (kv.get("workload") != workload or kv.get("sources_sha256") != kernel_sources_sha256()
+            or kv.get("kernels") != ",".join(kernels)):
         return None
-    return int(kv["traffic_bytes_per_launch"])
+    out = {k: int(kv[f"{k}.traffic_bytes_per_launch"]) for k in kernels}
+    out["per_step"] = int(kv["traffic_bytes_per_step"])
+    return out
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str):
-    """(kernel, traffic file text) from the counter-collection CSVs of a FETCH_SIZE
-    run and a WRITE_SIZE run of ``bench.py --calibrate``."""
+def kernel_matches(full_name: str, kernel: str) -> bool:
+    """Whether a demangled dispatch name is liboasis's kernel ``kernel``."""
+    import re
+    return re.search(rf"(^|\s)oasis::{re.escape(kernel)}[<(]", full_name) is not None
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: str, kernels: tuple) -> str:
+    """Traffic file text from the counter-collection CSVs of a FETCH_SIZE run and a
+    WRITE_SIZE run of ``bench.py --calibrate``: bytes per launch of each of the
+    overlapped step's kernels, read plus written, and their sum per step."""
     import csv
 
     def per_kernel(d, counter):
@@ -171,37 +191,31 @@ def summarize_counters(fetch_dir: str, write_dir: str, workload: str, command: s
                 vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return vals
 
-    out = []
-    scale = {}
-    mean = {}
+    notes, body = [], []
+    per_launch = {k: 0.0 for k in kernels}
     for counter, d, direction in (("FETCH_SIZE", fetch_dir, "read"), ("WRITE_SIZE", write_dir, "written")):
         vals = per_kernel(d, counter)
         copy = [v for v in vals.get("__amd_rocclr_copyBuffer", []) if v > CALIBRATION_BYTES / 1024 / 8]
         if not copy:
             raise SystemExit(f"no calibration copy found in {d}")
-        scale[counter] = (CALIBRATION_BYTES / 1024) / statistics.mean(copy[:3])
-        kernel, fused = None, []
-        for name in LAUNCH1_KERNELS:
-            fused = [v for k, v in vals.items() if k.startswith(f"void oasis::{name}<")]
-            if fused:
-                kernel = name
-                break
-        if not fused:
-            raise SystemExit(f"no dispatch of {' or '.join(LAUNCH1_KERNELS)} in {d}")
-        mean[counter] = statistics.mean(fused[0])
-        out.append(f"# {counter}: {statistics.mean(copy[:3]):.1f} KiB for the calibration copy "
-                   f"({CALIBRATION_BYTES >> 20} MiB {direction}) -> scale {scale[counter]:.4f}; "
-                   f"{kernel}: {mean[counter]:.1f} KiB per launch over {len(fused[0])} launches")
-    fetch = mean["FETCH_SIZE"] * 1024 * scale["FETCH_SIZE"]
-    write = mean["WRITE_SIZE"] * 1024 * scale["WRITE_SIZE"]
-    head = [f"# HBM traffic per launch of {kernel} (the fused scoring + attention-gather launch)",
+        scale = (CALIBRATION_BYTES / 1024) / statistics.mean(copy[:3])
+        notes.append(f"# {counter}: {statistics.mean(copy[:3]):.1f} KiB for the calibration copy "
+                     f"({CALIBRATION_BYTES >> 20} MiB {direction}) -> scale {scale:.4f}")
+        for kernel in kernels:
+            xs = [v for name, v_list in vals.items() if kernel_matches(name, kernel) for v in v_list]
+            if not xs:
+                raise SystemExit(f"no dispatch of {kernel} in {d}")
+            per_launch[kernel] += statistics.mean(xs) * 1024 * scale
+            notes.append(f"#   {kernel}: {statistics.mean(xs):.1f} KiB per launch over {len(xs)} launches")
+            body.append(f"{kernel}.{counter.split('_')[0].lower()}_bytes_per_launch = "
+                        f"{int(round(statistics.mean(xs) * 1024 * scale))}")
+    head = [f"# HBM traffic of the overlapped step's kernels ({', '.join(kernels)}), per launch and per step",
             f"# command (one run per counter): {command}"]
-    body = [f"kernel = {kernel}", f"workload = {workload}",
-            f"sources_sha256 = {kernel_sources_sha256()}",
-            f"fetch_bytes_per_launch = {int(round(fetch))}",
-            f"write_bytes_per_launch = {int(round(write))}",
-            f"traffic_bytes_per_launch = {int(round(fetch + write))}"]
-    return kernel, "\n".join(head + out + body) + "\n"
+    body = ([f"kernels = {','.join(kernels)}", f"workload = {workload}",
+             f"sources_sha256 = {kernel_sources_sha256()}"] + body +
+            [f"{k}.traffic_bytes_per_launch = {int(round(v))}" for k, v in per_launch.items()] +
+            [f"traffic_bytes_per_step = {int(round(sum(per_launch.values())))}"])
+    return "\n".join(head + notes + body) + "\n"
 
 
 OCCUPANCY_COUNTERS = ("OccupancyPercent", "MeanOccupancyPerCU", "MfmaUtil", "LDSBankConflict", "SQ_WAVES")
@@ -894,8 +908,12 @@ def main(argv=None) -> int:
         print(text)
         return 0
     if args.summarize_counters:
-        kernel, text = summarize_counters(*args.summarize_counters, args.workload, args.counter_command)
-        with open(traffic_file(kernel, args.workload), "w") as f:
+        import oasis_score_summaries_amd as oa
+        import synth
+        w = synth.WORKLOADS[args.workload]
+        text = summarize_counters(*args.summarize_counters, args.workload, args.counter_command,
+                                  step_kernels(oa, oa.dims_for(w), w))
+        with open(traffic_file(args.workload), "w") as f:
             f.write(text)
         print(text, end="")
         return 0
@@ -1078,17 +1096,29 @@ def main(argv=None) -> int:
         blocks = int(buffers.table_count.sum())
     nb = algorithmic_bytes(w, s0["seq_lens"].cpu(), blocks)
     step_gbps = nb["step"] / (ms_per_step * 1e-3) / 1e9
+    kernels = step_kernels(oa, d, w)
     if args.order == "overlapped":
-        # The first launch: the scoring with the attention gathering (summaries,
-        # scores, K/V blocks); two kernels back to back above 96 query rows per head.
-        dominant = "score_attn_split"
-        kernel = "score_attn_kernel" if w.group * w.queries <= 96 else "score_kernel+attn_split_kernel"
-        dom_bytes = nb["score_attn_split"]
+        launches = {"launch1": kernels[0], "launch2": kernels[1]}
+        traffic = measured_traffic(w.name, kernels)
     else:
-        dominant = max(("score", "attn_split"), key=lambda k: stage_us[k])
-        kernel = {"score": "score_kernel", "attn_split": "attn_split_kernel"}[dominant]
-        dom_bytes = nb[dominant]
-    dom_gbps = dom_bytes / (stage_us[dominant] * 1e-6) / 1e9
+        launches = {"score": "score_kernel", "select_plan": "topk_plan_kernel",
+                    "attn_split": "attn_split_kernel", "attn_merge": "attn_merge_kernel"}
+        traffic = None
+    per_launch = {}
+    for stage, kernel in launches.items():
+        us = stage_us[stage]
+        e = {"kernel": kernel, "avg_launch_us": round(us, 3),
+             "launch_us": {k: round(v, 3) if isinstance(v, float) else v
+                           for k, v in percentiles(stage_samples[stage]).items()}}
+        if nb.get(stage):
+            gbps = nb[stage] / (us * 1e-6) / 1e9
+            e.update({"bytes_per_launch": nb[stage], "achieved_gbps": round(gbps, 1),
+                      "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        if traffic is not None and kernel in traffic:
+            e["traffic"] = traffic[kernel]
+        per_launch[stage] = e
+    dominant = max(per_launch, key=lambda k: per_launch[k]["avg_launch_us"])
+    check["handoff_status_zero"] = oa.workspace_status(d, buffers.ws) == 0
 
     result = {
         "metric": METRIC if w.name == "qwen3_8b_32k" else METRIC.replace("Qwen3-8B 32K", w.name),
@@ -1107,20 +1137,21 @@ def main(argv=None) -> int:
                    "context": w.ctx, "queries_per_head": w.queries, "top_k": w.top_k,
                    "window_tokens": w.window, "fetch_ratio": w.fetch_ratio, "cap": w.cap,
                    "input_sets": n_sets, "mode": args.mode, "order": args.order},
-        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(dom_gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(kernel, w.name),
-                     "bytes_per_launch": dom_bytes,
-                     "avg_launch_us": round(stage_us[dominant], 3),
-                     "launch_us": {k: round(v, 3) if isinstance(v, float) else v
-                                   for k, v in percentiles(stage_samples[dominant]).items()},
+        # The whole timed step against HBM: the method's bytes (candidate summaries,
+        # the K/V blocks of every table entry, queries, outputs) over the step time.
+        "roofline": {"bound": "hbm", "scope": "whole step",
+                     "kernels": list(launches.values()),
+                     "achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic["per_step"] if traffic is not None else None,
+                     "bytes_per_step": nb["step"], "units": nb["units"],
                      "copy_gbps": round(copy_gbps, 1),
-                     "frac_of_copy": round(dom_gbps / copy_gbps, 4)},
+                     "frac_of_copy": round(step_gbps / copy_gbps, 4)},
+        "dominant_kernel": dict(per_launch[dominant], stage=dominant),
+        "launches": per_launch,
         "step_ms": {k: round(v, 6) if isinstance(v, float) else v for k, v in percentiles(spread).items()},
         "step_ms_sample": ("per graph replay (one step of each input set), divided by the sets"
                            if graph_mode else "per eager step"),
-        "step_hbm": {"achieved": round(step_gbps, 1), "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
-                     "bytes_per_step": nb["step"], "units": nb["units"]},
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
         "stage_timing": stage_method,
         f"{other}_ms_per_step": round(ms_other, 6),

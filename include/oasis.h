@@ -99,12 +99,19 @@ int32_t oasis_fetch_cap(const oasis_dims* dims);
  * window blocks any length can produce, ceil(W / bs) + 1.  -1 if invalid. */
 int32_t oasis_table_stride(const oasis_dims* dims);
 
+/* Whether oasis_decode_step_overlapped runs the selection and plan inside its
+ * first launch (1: launch 1 = scoring, selection and plan, attention splits;
+ * launch 2 = attention merge) or after it (0: launch 2 = selection and plan with
+ * the merge); see oasis_decode_step_overlapped for the limits.  -1 if dims is
+ * invalid. */
+int32_t oasis_overlapped_selects_in_launch1(const oasis_dims* dims);
+
 /* Device workspace of the decode steps (oasis_decode_step, _overlapped, _pool,
  * oasis_decode_layer_pipelined), in bytes, a multiple of 256; it also serves
  * oasis_sparse_decode_attn with table_stride == oasis_table_stride(dims).  It
  * holds the per-split attention partials and, after them, the hand-off region
- * through which the workgroups of the one-launch step (see
- * oasis_decode_step_overlapped) pass scores and partials to each other.
+ * through which the scoring workgroups of oasis_decode_step_overlapped's first
+ * launch pass the scores to the selection workgroups of the same launch.
  * The hand-off region must be zero before the workspace first serves a step:
  * allocate it zero-filled or call oasis_workspace_clear once.  Every step leaves
  * it zero again, so the workspace can serve any number of steps and layers of
@@ -122,9 +129,10 @@ oasis_status oasis_workspace_clear(const oasis_dims* dims, void* ws, size_t ws_b
                                    hipStream_t stream);
 
 /* Byte offset, inside the step workspace, of the hand-off status word (uint32).
- * It stays 0 unless a workgroup of a one-launch step waited past its bound (about
- * 10 ms) for the scores or partials it needs; it then holds bit 1 (scores) or bit
- * 2 (partials), the outputs of that step are unspecified and the workspace must
+ * It stays 0 unless a selection workgroup in the first launch of
+ * oasis_decode_step_overlapped waited past its bound (about 10 ms) for the
+ * scores it needs; it then holds bit 1, the selection outputs of
+ * that step (topk, plan, table, resident_next) are unspecified and the workspace must
  * be cleared.  A wait never hangs the device.  0 if dims is invalid. */
 size_t oasis_workspace_status_offset(const oasis_dims* dims);
 
@@ -282,14 +290,14 @@ oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void
  *     table, table_count for it), as oasis_decode_step does.
  * The halves share only inputs, so their work items sit in the same grids.  Up
  * to 32 query rows (G * Q), 4 query heads per KV head, K = 256 and 2048 blocks
- * per KV head, the step is ONE launch: scoring workgroups, one selection-and-plan
+ * per KV head, launch 1 holds the scoring workgroups, one selection-and-plan
  * workgroup per KV head that takes its head's scores over from the scoring
- * workgroups, the attention split workgroups, and one merge workgroup per query
- * head that takes the splits' partials over, through the hand-off region of the
- * workspace (it must be zero before the first step; see oasis_workspace_bytes).
- * The selection then runs while the attention still streams K and V.  Larger
- * shapes take two launches: scoring with the attention's block gathering, then
- * the selection and plan with the attention's merge.
+ * workgroups through the hand-off region of the workspace (it must be zero
+ * before the first step; see oasis_workspace_bytes), and the attention split
+ * workgroups; the selection then runs while the attention still streams K and
+ * V.  Launch 2 is the attention merge.  Larger shapes keep the selection out of
+ * launch 1: scoring with the attention's block gathering, then the selection
+ * and plan with the attention's merge.
  * resident_next is required and must not overlap `resident`; the caller swaps
  * the two between steps.  Other arguments as for oasis_decode_step. */
 oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q, const void* summ,
@@ -304,8 +312,8 @@ oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q,
 /* oasis_decode_step_overlapped with timing markers, for measurement:
  * events[0..2] (created by the caller with hipEventCreate) are recorded on
  * `stream` before the first launch, after it, and after the second launch (the
- * selection and plan with the attention merge; when the step is one launch,
- * events[1] and events[2] both follow it).  The kernels queued are the same. */
+ * attention merge, with the selection and plan when those are not in launch 1).
+ * The kernels queued are the same. */
 oasis_status oasis_decode_step_overlapped_timed(
     const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
     const int32_t* seq_lens, float* scores, int32_t* topk, const int32_t* resident,
@@ -433,9 +441,11 @@ oasis_status oasis_decode_step_pool_async(
  * beside the foreground of the layers after it (xllm-io review, section three:
  * component table, asynchronous pipeline, parallel across layers and serial within
  * a layer; Eq. (4)).  Here a layer's scoring goes with its own foreground
- * attention (launch 1) and its selection and plan ride in the next layer's
- * launch 1; its launch 2 is the attention merge alone, the output the next layer
- * needs.  One layer's buffers: */
+ * attention (launch 1); its launch 2 is the attention merge, the output the next
+ * layer needs.  Up to the one-launch limits of oasis_decode_step_overlapped the
+ * layer's selection and plan run inside its own launch 1, fed by the hand-off
+ * region; above them they ride in the next layer's launch 1 (or, for the
+ * largest shapes, its launch 2).  One layer's buffers: */
 typedef struct {
   const void* q;            /* device, bf16 [B, H, G, Q, 128] (row 0 target) */
   const void* summ;         /* device, bf16 [B, H, NB, 2, 128] */
@@ -467,9 +477,9 @@ typedef struct {
  * not both.  The two must not share scores buffers (one is written while the
  * other is read), and each resident_next must be its own buffer; a layer's
  * selection outputs are valid after the next call returns its launches to the
- * stream order.  Up to K = 256, 2048 blocks per head, 4 query heads and 32 query
- * rows per KV head, the previous layer's selection shares this layer's first
- * launch; otherwise it shares this layer's second launch, with the merge. */
+ * stream order (within the one-launch limits, as soon as this call's own
+ * launches are done; `previous` then has nothing left to run and the final call
+ * with layer = NULL queues nothing). */
 oasis_status oasis_decode_layer_pipelined(const oasis_dims* dims, const oasis_layer_io* layer,
                                           const oasis_layer_io* previous, float scale,
                                           hipStream_t stream);

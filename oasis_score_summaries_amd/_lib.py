@@ -58,6 +58,7 @@ _SIGNATURES = {
     "oasis_workspace_bytes": (ctypes.c_size_t, [_DIMS]),
     "oasis_workspace_clear": (ctypes.c_int, [_DIMS, _P, ctypes.c_size_t, _P]),
     "oasis_workspace_status_offset": (ctypes.c_size_t, [_DIMS]),
+    "oasis_overlapped_selects_in_launch1": (ctypes.c_int32, [_DIMS]),
     "oasis_attn_workspace_bytes": (ctypes.c_size_t, [_DIMS, ctypes.c_int32]),
     "oasis_build_summaries": (ctypes.c_int, [_DIMS, _P, _P, _P, _P]),
     "oasis_score_summaries": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P]),
@@ -349,9 +350,18 @@ def sparse_decode_attn_resident(dims: OasisDims, q: torch.Tensor, k: torch.Tenso
 
 
 def step_workspace(dims: OasisDims, device) -> torch.Tensor:
-    """A workspace for the decode steps, zero-filled as the one-launch step requires
-    before its first use (each step leaves it zero)."""
+    """A workspace for the decode steps, zero-filled as the overlapped step's hand-off
+    region requires before its first use (each step leaves it zero)."""
     return torch.zeros(workspace_bytes(dims), dtype=torch.uint8, device=_norm_device(device))
+
+
+def overlapped_selects_in_launch1(dims: OasisDims) -> bool:
+    """Whether the overlapped step's first launch holds the selection and plan
+    (oasis_overlapped_selects_in_launch1)."""
+    r = int(load().oasis_overlapped_selects_in_launch1(ctypes.byref(dims)))
+    if r < 0:
+        _check(1, "oasis_overlapped_selects_in_launch1")
+    return r == 1
 
 
 def workspace_clear(dims: OasisDims, ws: torch.Tensor, stream=None) -> None:
@@ -361,8 +371,9 @@ def workspace_clear(dims: OasisDims, ws: torch.Tensor, stream=None) -> None:
 
 
 def workspace_status(dims: OasisDims, ws: torch.Tensor) -> int:
-    """The hand-off status word of a step workspace (0 unless a wait of a one-launch
-    step timed out); reads it after the work queued so far."""
+    """The hand-off status word of a step workspace (0 unless a selection workgroup
+    of the overlapped step timed out waiting for its scores); reads it after the work
+    queued so far."""
     off = int(load().oasis_workspace_status_offset(ctypes.byref(dims)))
     if off == 0 or off + 4 > ws.numel():
         raise ValueError("the workspace is not a step workspace for these dims")
@@ -645,7 +656,7 @@ class StageEvents:
     (oasis_decode_step_overlapped_timed)."""
 
     SERIAL_STAGES = ("score", "select_plan", "attn_split", "attn_merge")
-    OVERLAPPED_STAGES = ("score_attn_split", "select_plan_merge")
+    OVERLAPPED_STAGES = ("launch1", "launch2")
 
     def __init__(self, overlapped: bool = False):
         self.STAGES = self.OVERLAPPED_STAGES if overlapped else self.SERIAL_STAGES

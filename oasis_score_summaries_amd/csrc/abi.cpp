@@ -117,6 +117,12 @@ int32_t oasis_table_stride(const oasis_dims* dims) {
   return d.table_stride;
 }
 
+int32_t oasis_overlapped_selects_in_launch1(const oasis_dims* dims) {
+  oasis::Dims d;
+  if (check_dims(dims, &d) != OASIS_OK) return -1;
+  return oasis::handoff_step_fits(d) ? 1 : 0;
+}
+
 size_t oasis_workspace_bytes(const oasis_dims* dims) {
   oasis::Dims d;
   if (check_dims(dims, &d) != OASIS_OK) return 0;

@@ -83,13 +83,9 @@ struct AttnArgs {
 // POOL (with RES): the blocks are read from the working set in HBM instead of the
 // full cache: resident slot e from pool slot e (`k`, `v`: [B, H, K, bs, 128]),
 // window block j from ring slot j % WB (`ring_k`, `ring_v`: [B, H, WB, bs, 128]).
-// HANDOFF: the record goes to the hand-off region of `ho` as encoded device-scope
-// words, and the split then sets its flag of each query head, for the merge workgroups
-// of the same launch.
-template <int GP, bool RES, bool POOL = false, bool HANDOFF = false>
+template <int GP, bool RES, bool POOL = false>
 __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, AttnShared<GP>& sh,
-                                                             const AttnArgs& a,
-                                                             const Handoff* ho = nullptr) {
+                                                             const AttnArgs& a) {
   static_assert(RES || !POOL, "the pool is addressed through the resident slots");
   const u32x4* __restrict__ q = a.q;
   const char* __restrict__ k = a.k;
@@ -307,10 +303,6 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
 
   // Last wave: combine the four partials into the split's record.
   float* rec0 = part + ((size_t)bh * nsplit + sp) * group * kRec;
-  // HANDOFF: the head's records through a buffer resource, for device-scope stores.
-  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
-      HANDOFF ? (void*)(ho->part + (size_t)bh * nsplit * group * kRec) : (void*)rec0, (short)0,
-      HANDOFF ? nsplit * group * kRec * 4 : 0, 0x00020000);
   for (int idx = lane; idx < group * (kHeadDim / 4); idx += 64) {
     const int g = idx / (kHeadDim / 4), d4 = idx % (kHeadDim / 4);
     float mx = -INFINITY;
@@ -326,24 +318,13 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
         lsum += f * sm_l[w][g];
       }
     }
-    if (HANDOFF) {
-      const uint32_t off = (uint32_t)(((sp * group + g) * kRec + 4 * d4) * 4);
-      const u32x4 wv = {enc_f32(acc.x), enc_f32(acc.y), enc_f32(acc.z), enc_f32(acc.w)};
-      __builtin_amdgcn_raw_buffer_store_b128(wv, hr, off, 0, kDevScopeAux);
-      if (d4 == 0) {
-        __builtin_amdgcn_raw_buffer_store_b32(enc_f32(mx), hr, off + kHeadDim * 4, 0, kDevScopeAux);
-        __builtin_amdgcn_raw_buffer_store_b32(enc_f32(lsum), hr, off + kHeadDim * 4 + 4, 0, kDevScopeAux);
-      }
-    } else {
-      float* rec = rec0 + g * kRec;
-      *(floatx4*)(rec + 4 * d4) = acc;
-      if (d4 == 0) {
-        rec[kHeadDim + 0] = mx;
-        rec[kHeadDim + 1] = lsum;
-      }
+    float* rec = rec0 + g * kRec;
+    *(floatx4*)(rec + 4 * d4) = acc;
+    if (d4 == 0) {
+      rec[kHeadDim + 0] = mx;
+      rec[kHeadDim + 1] = lsum;
     }
   }
-  if (HANDOFF && lane < group) st_dev(ho->flag_attn + ((size_t)bh * group + lane) * nsplit + sp, 1u);
 }
 
 // One workgroup per (sequence, KV head, query head).  Every wave
@@ -359,101 +340,38 @@ struct MergeShared {
   float2v acc[NWV][64];
 };
 
-// HANDOFF reads of the records (device scope), issued together as buffer loads; a word
-// still zero (its store not yet arrived) is read again by rec_fix.
-__device__ inline uint32_t rec_fix(uint32_t w, const uint32_t* p, uint32_t* status) {
-  return w != 0u ? w : ld_dev_nonzero(p, status, kStatusAttnWait);
-}
-
 // Query head `bhg` = (sequence, KV head) * group + g, merged by the NWV waves of the
-// calling workgroup.  Every thread of the workgroup calls it.  HANDOFF: the records
-// are those the split workgroups of the same launch hand over through `ho` (`part` is
-// then the hand-off region): wave 0 waits for the query head's split flags (and clears
-// them), then the workgroup reads the records with device-scope loads and writes zeros
-// back over them.
-template <int NWV, bool HANDOFF = false>
+// calling workgroup.  Every thread of the workgroup calls it.
+template <int NWV>
 __device__ __attribute__((always_inline)) void attn_merge_wg(int bhg, MergeShared<NWV>& sh,
                                                              const float* __restrict__ part,
                                                              int group, int nsplit,
                                                              float* __restrict__ out,
-                                                             float* __restrict__ lse,
-                                                             const Handoff* ho = nullptr) {
+                                                             float* __restrict__ lse) {
   constexpr int kMergeWaves = NWV;
   auto& sm_acc = sh.acc;
   const int bh = bhg / group, g = bhg % group;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint32_t* status = HANDOFF ? ho->status : nullptr;
-  if (HANDOFF) {
-    if (threadIdx.x < 64) wait_flags(ho->flag_attn + (size_t)bhg * nsplit, nsplit, status, kStatusAttnWait);
-    __syncthreads();
-  }
   // Every split writes its record; splits past the table hold max -inf, sum 0 and a
   // zero output, so the merge takes all of them and needs no table count.
   const float* rec = part + ((size_t)bh * nsplit * group + g) * kRec;  // split s: + s * stride
   const size_t stride = (size_t)group * kRec;
   const size_t stride2 = stride / 2;
   const float2v* po = (const float2v*)rec + lane;
-  // HANDOFF: the query head's records through a buffer resource (offsets in words from
-  // `rec`); a lane past the splits reads nothing (offset past the range: zeros, no
-  // access), so that no split is read after its owner has cleared it.
-  const uint32_t* ru = reinterpret_cast<const uint32_t*>(rec);
-  const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(rec), (short)0, HANDOFF ? (int)(((nsplit - 1) * stride + kRec) * 4) : 0, 0x00020000);
-  auto word_off = [&](int s, int i) -> uint32_t {
-    return s < nsplit ? (uint32_t)((s * stride + i) * 4) : 0x80000000u;
-  };
 
   float mloc[kAttnMaxSplits / 64], lloc[kAttnMaxSplits / 64];
+#pragma unroll
+  for (int c = 0; c < kAttnMaxSplits / 64; ++c) {
+    const int s = c * 64 + lane;
+    const int sc = s < nsplit ? s : 0;
+    mloc[c] = rec[sc * stride + kHeadDim + 0];
+    lloc[c] = rec[sc * stride + kHeadDim + 1];
+  }
   float2v x[kMergeBatch];
-  if (HANDOFF) {
-    uint32_t mw[kAttnMaxSplits / 64], lw[kAttnMaxSplits / 64];
-    uint64_t xw[kMergeBatch];
 #pragma unroll
-    for (int c = 0; c < kAttnMaxSplits / 64; ++c) {
-      const int s = c * 64 + lane;
-      mw[c] = __builtin_amdgcn_raw_buffer_load_b32(rr, word_off(s, kHeadDim), 0, kDevScopeAux);
-      lw[c] = __builtin_amdgcn_raw_buffer_load_b32(rr, word_off(s, kHeadDim + 1), 0, kDevScopeAux);
-    }
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int s = wave + kMergeWaves * u;
-      xw[u] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr, word_off(s, 2 * lane), 0, kDevScopeAux));
-    }
-#pragma unroll
-    for (int c = 0; c < kAttnMaxSplits / 64; ++c) {
-      const int s = c * 64 + lane;
-      if (s < nsplit) {
-        mloc[c] = dec_f32(rec_fix(mw[c], ru + s * stride + kHeadDim, status));
-        lloc[c] = dec_f32(rec_fix(lw[c], ru + s * stride + kHeadDim + 1, status));
-      } else {
-        mloc[c] = -INFINITY;
-        lloc[c] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int s = wave + kMergeWaves * u;
-      if (s < nsplit) {
-        const uint32_t* p = ru + s * stride + 2 * lane;
-        x[u] = float2v{dec_f32(rec_fix((uint32_t)xw[u], p, status)),
-                       dec_f32(rec_fix((uint32_t)(xw[u] >> 32), p + 1, status))};
-      } else {
-        x[u] = float2v{0.f, 0.f};
-      }
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < kAttnMaxSplits / 64; ++c) {
-      const int s = c * 64 + lane;
-      const int sc = s < nsplit ? s : 0;
-      mloc[c] = rec[sc * stride + kHeadDim + 0];
-      lloc[c] = rec[sc * stride + kHeadDim + 1];
-    }
-#pragma unroll
-    for (int u = 0; u < kMergeBatch; ++u) {
-      const int s = wave + kMergeWaves * u;
-      x[u] = po[(size_t)(s < nsplit ? s : 0) * stride2];
-    }
+  for (int u = 0; u < kMergeBatch; ++u) {
+    const int s = wave + kMergeWaves * u;
+    x[u] = po[(size_t)(s < nsplit ? s : 0) * stride2];
   }
   const int nvalid = nsplit;  // <= kAttnMaxSplits
 
@@ -485,50 +403,17 @@ __device__ __attribute__((always_inline)) void attn_merge_wg(int bhg, MergeShare
       const int s = s0 + kMergeWaves * u;
       if (s < nvalid) acc += weight(s) * x[u];
     }
-    if (HANDOFF) {  // this wave's outputs of the batch are read: clear them
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const int s = s0 + kMergeWaves * u;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, (uint64_t)0), rr, word_off(s, 2 * lane), 0,
-                                              kDevScopeAux);
-      }
-    }
     const int s1 = s0 + kMergeWaves * kMergeBatch;
     if (s1 >= nvalid) break;
-    if (HANDOFF) {
-      uint64_t xw[kMergeBatch];
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const int s = s1 + kMergeWaves * u;
-        xw[u] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(rr, word_off(s, 2 * lane), 0, kDevScopeAux));
-      }
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const int s = s1 + kMergeWaves * u;
-        const uint32_t* p = ru + (s < nsplit ? s : 0) * stride + 2 * lane;
-        x[u] = s < nsplit ? float2v{dec_f32(rec_fix((uint32_t)xw[u], p, status)),
-                                    dec_f32(rec_fix((uint32_t)(xw[u] >> 32), p + 1, status))}
-                          : float2v{0.f, 0.f};
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
-        const int s = s1 + kMergeWaves * u;
-        x[u] = po[(size_t)(s < nsplit ? s : 0) * stride2];
-      }
+    for (int u = 0; u < kMergeBatch; ++u) {
+      const int s = s1 + kMergeWaves * u;
+      x[u] = po[(size_t)(s < nsplit ? s : 0) * stride2];
     }
   }
   sm_acc[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
-  if (HANDOFF) {  // every wave has read the maxima and sums: clear them
-#pragma unroll
-    for (int c = 0; c < kAttnMaxSplits / 64; ++c) {
-      const int s = c * 64 + lane;
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(uint2v, (uint64_t)0), rr, word_off(s, kHeadDim), 0,
-                                            kDevScopeAux);
-    }
-  }
 #pragma unroll
   for (int w = 1; w < kMergeWaves; ++w) acc += sm_acc[w][lane];
   const bool any = mx != -INFINITY && sum > 0.f;

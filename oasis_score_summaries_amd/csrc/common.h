@@ -23,7 +23,6 @@ constexpr int kWavesPerWG = OASIS_WAVES_PER_WG;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
 // ---- sequence geometry (identical on host and device) ----------------------------
 // Blocks hold 1 << bshift tokens (bshift 3..6: 8 to 64 tokens; 16 is the default).
@@ -77,7 +76,7 @@ __host__ inline bool place_by_xcd(int query_rows) { return query_rows >= 64; }
 // constant-rate clock (100 MHz): past kSpinTicks the consumer raises a bit in the
 // status word and goes on, so no launch can hang.
 constexpr uint64_t kSpinTicks = 1000000;  // 10 ms
-constexpr uint32_t kStatusScoreWait = 1u, kStatusAttnWait = 2u;
+constexpr uint32_t kStatusScoreWait = 1u;
 constexpr int kDevScopeAux = 0x10;  // buffer-instruction cache policy: device scope (sc1)
 
 __device__ inline uint32_t ld_dev(const uint32_t* p) {
@@ -135,22 +134,11 @@ __device__ inline uint32_t ld_dev_nonzero(const uint32_t* p, uint32_t* status, u
   }
   return w;
 }
-// A float as a non-zero word and back: the bits inverted, NaNs made the canonical
-// quiet NaN first (its inverse is not zero), so every value, -inf and 0 included,
-// travels as a non-zero word.
-__device__ inline uint32_t enc_f32(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return ~((x != x) ? 0x7fc00000u : u);
-}
-__device__ inline float dec_f32(uint32_t w) { return __uint_as_float(~w); }
-
-// The hand-off region of the one-launch step (inside the caller's workspace).
+// The hand-off region of step_kernel (inside the caller's workspace).
 struct Handoff {
   uint32_t* flag_score;  // [B*H, score_waves]: one flag per scoring wave
-  uint32_t* flag_attn;   // [B*H*G, nsplit]: one flag per split and query head
   uint32_t* status;      // stays 0 unless a wait timed out
   uint32_t* mbox;        // [B*H, NB]: order keys of the candidate scores (never 0)
-  uint32_t* part;        // [B*H, nsplit, G, kRec]: encoded split records
   int score_waves;       // scoring waves per (sequence, KV head), <= 64
 };
 

@@ -57,26 +57,22 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void score_a
 
 // The overlapped step with its background half inside launch 1: the scoring
 // workgroups, then one selection-and-plan workgroup per (sequence, KV head), then
-// the attention split workgroups (and, with MERGE, one merge workgroup per query
-// head).  A selection workgroup takes its head's scores over from the scoring
-// workgroups through the hand-off region `ho` (device-scope stores, per-wave flags,
-// words that carry their own validity; see common.h), so the selection and plan run
-// while the attention still streams K and V instead of after a kernel boundary.  With
-// MERGE a merge workgroup likewise takes its query head's split records over and the
-// step is one launch; without it the splits write plain records and the merge is a
-// second, small launch (the kernel boundary makes the records visible).  Every
-// workgroup comes after the ones it waits for in the grid, and every wait is bounded.
-// Up to 32 query rows, 4 query heads, K = 256 and 2048 blocks per KV head (the
-// selection in 256 threads).
-template <int RT, int GP, int ITEMS, bool POOL, bool MERGE>
+// the attention split workgroups.  A selection workgroup takes its head's scores
+// over from the scoring workgroups through the hand-off region `ho` (device-scope
+// stores, per-wave flags, words that carry their own validity; see common.h), so the
+// selection and plan run while the attention still streams K and V instead of after
+// a kernel boundary.  The splits write plain records and the merge is a second,
+// small launch (the kernel boundary makes the records visible).  Every selection
+// workgroup comes after the scoring workgroups it waits for in the grid, and every
+// wait is bounded.  Up to 32 query rows, 4 query heads, K = 256 and 2048 blocks per
+// KV head (the selection in 256 threads).
+template <int RT, int GP, int ITEMS, bool POOL>
 __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void step_kernel(
-    ScoreArgs sa, TopkPlanArgs ta, AttnArgs aa, Handoff ho, int n_score, int score_gx, int attn_gx,
-    float* out, float* lse) {
+    ScoreArgs sa, TopkPlanArgs ta, AttnArgs aa, Handoff ho, int n_score, int score_gx, int attn_gx) {
   __shared__ union {
     ScoreShared<RT> s;
     AttnShared<GP> a;
     TopkPlanShared<kScoreThreads, ITEMS> t;
-    MergeShared<kAttnWaves> m;
   } sh;
   __shared__ PlanBitmaps bm;
   const int heads = n_score / score_gx;
@@ -91,15 +87,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void step_ke
     return;
   }
   b -= heads;
-  if (b < attn_gx * heads) {
-    attn_split_wg<GP, true, POOL, MERGE>(b % attn_gx, b / attn_gx, sh.a, aa, &ho);
-    return;
-  }
-  if (MERGE) {
-    b -= attn_gx * heads;
-    attn_merge_wg<kAttnWaves, true>(b, sh.m, reinterpret_cast<const float*>(ho.part), aa.group, aa.nsplit,
-                                    out, lse, &ho);
-  }
+  if (b < attn_gx * heads) attn_split_wg<GP, true, POOL>(b % attn_gx, b / attn_gx, sh.a, aa);
 }
 
 template <int THREADS, int ITEMS>
@@ -166,10 +154,10 @@ static bool pipelined_fits(const Dims& d) {
 
 hipError_t launch_pipelined_layer(const Dims& d, const LayerIO* cur, const LayerIO* prev, float scale,
                                   hipStream_t stream) {
-  if (one_launch_fits(d)) {
-    // Each layer's step is one launch that already holds its selection, plan and
-    // merge (the background half runs under the layer's own streaming), so the
-    // previous layer has nothing left to do.
+  if (handoff_step_fits(d)) {
+    // Each layer's launch 1 already holds its own selection and plan (the background
+    // half runs under the layer's own streaming), so the previous layer has nothing
+    // left to do.
     if (cur == nullptr) return hipSuccess;
     return launch_overlapped_step(d, cur->q, cur->summ, cur->k, cur->v, cur->seq_lens, cur->scores,
                                   cur->topk, cur->resident, cur->resident_next, cur->plan,
@@ -318,26 +306,22 @@ static hipError_t launch_second_half(const Dims& d, const AttnSplit& s, const To
 
 // ---- the hand-off region of the workspace -------------------------------------------
 // After the split records (the layout of attn_workspace_bytes): the flags (one per
-// scoring wave, one per split and query head), the status word, the score mailbox
-// [B*H, NB], and a second region of split records, used only by the one-launch step
-// (so that no other entry point leaves values in it).  Zero before the first
-// one-launch step; every one-launch step leaves it zero.
+// scoring wave), the status word and the score mailbox [B*H, NB].  Only
+// step_kernel touches it.  Zero before the first such launch; every one leaves it
+// zero.
 struct HandoffLayout {
-  size_t flag_score, flag_attn, status, mbox, part, total;
+  size_t flag_score, status, mbox, total;
 };
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static HandoffLayout handoff_layout(const Dims& d) {
   const size_t heads = (size_t)d.batch * d.heads;
   const size_t recs = attn_workspace_bytes(d, d.table_stride);
   const size_t score_waves = (size_t)score_grid_x(d) * kScoreWaves;
-  const size_t nsplit = (size_t)attn_split(d, d.table_stride).num_splits;
   HandoffLayout L;
   L.flag_score = recs;
-  L.flag_attn = L.flag_score + heads * score_waves * sizeof(uint32_t);
-  L.status = L.flag_attn + heads * d.group * nsplit * sizeof(uint32_t);
+  L.status = L.flag_score + heads * score_waves * sizeof(uint32_t);
   L.mbox = align256(L.status + sizeof(uint32_t));
-  L.part = align256(L.mbox + heads * d.max_blocks * sizeof(uint32_t));
-  L.total = align256(L.part + recs);
+  L.total = align256(L.mbox + heads * d.max_blocks * sizeof(uint32_t));
   return L;
 }
 size_t step_workspace_bytes(const Dims& d) { return handoff_layout(d).total; }
@@ -358,16 +342,11 @@ hipError_t launch_clear_handoff(const Dims& d, void* ws, hipStream_t stream) {
   return hipGetLastError();
 }
 
-bool one_launch_fits(const Dims& d) {
+bool handoff_step_fits(const Dims& d) {
   const int rt = (d.group * d.queries + 15) / 16;
   return rt <= 2 && d.group <= 4 && d.top_k <= kScoreThreads && d.max_blocks <= 8 * kScoreThreads &&
          score_grid_x(d) * kScoreWaves <= 64 && attn_split(d, d.table_stride).num_splits <= 256;
 }
-
-// Whether the merge runs inside the step's launch (one launch) or as a second launch.
-#ifndef OASIS_MERGE_IN_STEP
-#define OASIS_MERGE_IN_STEP 0
-#endif
 
 static hipError_t launch_one_step(const Dims& d, const AttnSplit& s, const void* q, const void* summ,
                                   const void* k, const void* v, const int32_t* seq_lens, float* scores,
@@ -379,30 +358,27 @@ static hipError_t launch_one_step(const Dims& d, const AttnSplit& s, const void*
   char* base = static_cast<char*>(ws);
   Handoff ho;
   ho.flag_score = reinterpret_cast<uint32_t*>(base + L.flag_score);
-  ho.flag_attn = reinterpret_cast<uint32_t*>(base + L.flag_attn);
   ho.status = reinterpret_cast<uint32_t*>(base + L.status);
   ho.mbox = reinterpret_cast<uint32_t*>(base + L.mbox);
-  ho.part = reinterpret_cast<uint32_t*>(base + L.part);
   const int score_gx = score_grid_x(d);
   ho.score_waves = score_gx * kScoreWaves;
   const ScoreArgs sa = score_args(d, q, summ, seq_lens, scores);
   AttnArgs aa = attn_args(d, s, q, pool ? pool->pool_k : k, pool ? pool->pool_v : v, resident, nullptr,
-                          d.table_stride, seq_lens, scale, nullptr);
+                          d.table_stride, seq_lens, scale, static_cast<float*>(ws));
   if (pool) {
     aa.ring_k = (const char*)pool->ring_k;
     aa.ring_v = (const char*)pool->ring_v;
   }
   const int n_score = score_gx * heads;
   const int attn_gx = s.num_splits;
-  if (!OASIS_MERGE_IN_STEP) aa.part = static_cast<float*>(ws);  // plain records for the merge launch
-  const int grid = n_score + heads + attn_gx * heads + (OASIS_MERGE_IN_STEP ? heads * d.group : 0);
+  const int grid = n_score + heads + attn_gx * heads;
   const int rt = (d.group * d.queries + 15) / 16;
   const int items = select_items(d, kScoreThreads);
   switch ((rt * 100 + items) * 2 + (pool ? 1 : 0)) {
 #define OASIS_STEP_CASE(RT, I, P)                                                               \
   case (RT * 100 + I) * 2 + P:                                                                  \
-    step_kernel<RT, 4, I, P, OASIS_MERGE_IN_STEP><<<dim3(grid), dim3(64 * kAttnWaves), 0, stream>>>( \
-        sa, ta, aa, ho, n_score, score_gx, attn_gx, out, lse);                                  \
+    step_kernel<RT, 4, I, P><<<dim3(grid), dim3(64 * kAttnWaves), 0, stream>>>(                \
+        sa, ta, aa, ho, n_score, score_gx, attn_gx);                                            \
     break;
 #define OASIS_STEP_ROW(RT)                                                                      \
   OASIS_STEP_CASE(RT, 1, 0) OASIS_STEP_CASE(RT, 2, 0) OASIS_STEP_CASE(RT, 4, 0)                 \
@@ -426,15 +402,14 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
                                   void* ws, hipStream_t stream, hipEvent_t after_first,
                                   const WorkingSet* pool, bool execute_plan) {
   const AttnSplit s = attn_split(d, d.table_stride);
-  if (one_launch_fits(d)) {
+  if (handoff_step_fits(d)) {
     const TopkPlanArgs ta = topk_plan_args(d, scores, seq_lens, topk, resident, resident_next, plan,
                                            plan_count, table, table_count);
     hipError_t err = launch_one_step(d, s, q, summ, k, v, seq_lens, scores, resident, ta, scale, out, lse,
                                      ws, stream, pool);
     if (err != hipSuccess) return err;
     if (after_first != nullptr && (err = hipEventRecord(after_first, stream)) != hipSuccess) return err;
-    if (!OASIS_MERGE_IN_STEP && (err = launch_attention_merge(d, s, out, lse, ws, stream)) != hipSuccess)
-      return err;
+    if ((err = launch_attention_merge(d, s, out, lse, ws, stream)) != hipSuccess) return err;
     if (pool == nullptr || !execute_plan) return hipSuccess;
     return launch_execute_plan(d, plan, plan_count, k, v, pool->pool_k, pool->pool_v, stream);
   }

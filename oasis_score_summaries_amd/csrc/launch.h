@@ -29,12 +29,13 @@ inline int attn_units(const Dims& d, int table_stride) {
 AttnSplit attn_split(const Dims& d, int table_stride);
 size_t attn_workspace_bytes(const Dims& d, int table_stride);
 // Workspace of the decode steps: the split records, then the hand-off region of the
-// one-launch step (which must be zero before the first such step; each leaves it zero).
+// overlapped step's launch 1 (zero before the first such step; each leaves it zero).
 size_t step_workspace_bytes(const Dims& d);
 // Byte offset of the hand-off status word (non-zero after a wait that timed out).
 size_t handoff_status_offset(const Dims& d);
-// Whether the overlapped step runs as one launch for these sizes.
-bool one_launch_fits(const Dims& d);
+// Whether the overlapped step runs its selection and plan inside launch 1 (scores
+// handed over in the launch) for these sizes.
+bool handoff_step_fits(const Dims& d);
 // Zero-fills the hand-off region of a step workspace.
 hipError_t launch_clear_handoff(const Dims& d, void* ws, hipStream_t stream);
 

@@ -44,7 +44,7 @@ def _dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 27
+    assert len(names) == 28
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.exported_symbols())
@@ -126,9 +126,12 @@ def test_workspace_and_table_stride_checks(lib):
     assert T == 16 + 4 + 1
     need = lib.oasis_attn_workspace_bytes(ctypes.byref(d), T)
     assert need > 0 and need % 256 == 0
-    # the step workspace: the split records, then the hand-off region (counters, status
-    # word, a score mailbox of B*H*NB words, a second region of split records)
-    assert step_need >= 2 * need + 2 * 2 * 64 * 4
+    # the step workspace: the split records, then the hand-off region (flags, status
+    # word, a score mailbox of B*H*NB words)
+    assert step_need >= need + 2 * 2 * 64 * 4
+    assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(d)) == 1
+    assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=8))) == 0
+    assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=0))) == -1
     off = lib.oasis_workspace_status_offset(ctypes.byref(d))
     assert need <= off < step_need and off % 4 == 0
     assert lib.oasis_attn_workspace_bytes(ctypes.byref(d), 0) == 0

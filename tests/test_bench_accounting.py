@@ -104,22 +104,48 @@ def _counter_csv(path, rows):
 
 
 def test_summarize_counters_scales_by_the_calibration_copy(tmp_path):
-    """Bytes per launch = the counter's mean (KiB) x 1024 x the scale that makes the
-    512 MiB calibration copy read (write) 512 MiB; the file carries the sources' hash."""
-    launch = "void oasis::score_attn_kernel<2, 4, false>(oasis::ScoreArgs, oasis::AttnArgs, int, int, int, int)"
+    """Bytes per launch of each step kernel = the counter's mean (KiB) x 1024 x the scale
+    that makes the 512 MiB calibration copy read (write) 512 MiB; the step's bytes are
+    the sum over its kernels; the file carries the sources' hash and reads back."""
+    l1 = "void oasis::step_kernel<2, 4, 2, false>(oasis::ScoreArgs, oasis::TopkPlanArgs, oasis::AttnArgs)"
+    l2 = "oasis::attn_merge_kernel(float const*, int, int, float*, float*)"
+    other = "void oasis::score_kernel<2>(oasis::ScoreArgs)"
     copy = "__amd_rocclr_copyBuffer"
     fetch_dir, write_dir = str(tmp_path / "f"), str(tmp_path / "w")
     _counter_csv(fetch_dir, [(copy, "FETCH_SIZE", 262144.0)] * 3 + [(copy, "FETCH_SIZE", 4.0)]
-                 + [(launch, "FETCH_SIZE", 1000.0), (launch, "FETCH_SIZE", 3000.0)])
+                 + [(l1, "FETCH_SIZE", 1000.0), (l1, "FETCH_SIZE", 3000.0), (l2, "FETCH_SIZE", 50.0),
+                    (other, "FETCH_SIZE", 9e9)])
     _counter_csv(write_dir, [(copy, "WRITE_SIZE", 524288.0)] * 3
-                 + [(launch, "WRITE_SIZE", 10.0), (launch, "WRITE_SIZE", 30.0)])
-    kernel, text = bench.summarize_counters(fetch_dir, write_dir, "qwen3_8b_32k", "cmd")
-    assert kernel == "score_attn_kernel"
+                 + [(l1, "WRITE_SIZE", 10.0), (l1, "WRITE_SIZE", 30.0), (l2, "WRITE_SIZE", 4.0)])
+    kernels = ("step_kernel", "attn_merge_kernel")
+    text = bench.summarize_counters(fetch_dir, write_dir, "qwen3_8b_32k", "cmd", kernels)
     kv = dict(line.split(" = ", 1) for line in text.splitlines() if " = " in line and not line.startswith("#"))
-    assert int(kv["fetch_bytes_per_launch"]) == 2000 * 1024 * 2       # mean 2000 KiB, scale 2
-    assert int(kv["write_bytes_per_launch"]) == 20 * 1024             # mean 20 KiB, scale 1
-    assert int(kv["traffic_bytes_per_launch"]) == 2000 * 1024 * 2 + 20 * 1024
+    assert int(kv["step_kernel.fetch_bytes_per_launch"]) == 2000 * 1024 * 2    # mean 2000 KiB, scale 2
+    assert int(kv["step_kernel.write_bytes_per_launch"]) == 20 * 1024          # mean 20 KiB, scale 1
+    assert int(kv["step_kernel.traffic_bytes_per_launch"]) == 2000 * 1024 * 2 + 20 * 1024
+    assert int(kv["attn_merge_kernel.traffic_bytes_per_launch"]) == 50 * 1024 * 2 + 4 * 1024
+    assert int(kv["traffic_bytes_per_step"]) == 2000 * 1024 * 2 + 20 * 1024 + 50 * 1024 * 2 + 4 * 1024
     assert kv["sources_sha256"] == bench.kernel_sources_sha256() and kv["workload"] == "qwen3_8b_32k"
+    assert kv["kernels"] == "step_kernel,attn_merge_kernel"
+    # read back through measured_traffic (the file is written where bench.py looks, then removed)
+    path = bench.traffic_file("unit_test_workload")
+    assert not os.path.exists(path)
+    try:
+        with open(path, "w") as f:
+            f.write(text.replace("workload = qwen3_8b_32k", "workload = unit_test_workload"))
+        got = bench.measured_traffic("unit_test_workload", kernels)
+        assert got == {"step_kernel": 2000 * 1024 * 2 + 20 * 1024, "attn_merge_kernel": 50 * 1024 * 2 + 4 * 1024,
+                       "per_step": int(kv["traffic_bytes_per_step"])}
+        assert bench.measured_traffic("unit_test_workload", ("score_attn_kernel", "select_merge_kernel")) is None
+    finally:
+        os.remove(path)
+
+
+def test_kernel_name_matching():
+    assert bench.kernel_matches("void oasis::step_kernel<1, 4, 2, true>(oasis::ScoreArgs)", "step_kernel")
+    assert bench.kernel_matches("oasis::attn_merge_kernel(float const*, int)", "attn_merge_kernel")
+    assert not bench.kernel_matches("void oasis::select_score_attn_kernel<1, 4, 2>(int)", "score_attn_kernel")
+    assert not bench.kernel_matches("void oasis::attn_merge_kernel_x<1>(int)", "attn_merge_kernel")
 
 
 def test_summarize_occupancy_means_per_kernel(tmp_path):

@@ -813,10 +813,10 @@ def test_append_then_step_loop_both_step_orders_agree(lib):
 
 
 @pytest.mark.parametrize("shape", ["tiny", "qwen3_8b_2x2", "short"])
-def test_one_launch_step_leaves_the_handoff_region_zero(lib, shape):
-    """The overlapped step at sizes it runs as one launch: after every step the
-    hand-off region of the workspace (counters, status word, score mailbox, second
-    record region) is zero again and the status word never records a timed-out wait;
+def test_overlapped_step_leaves_the_handoff_region_zero(lib, shape):
+    """The overlapped step at sizes whose selection runs in launch 1: after every
+    step the hand-off region of the workspace (flags, status word, score mailbox) is
+    zero again and the status word never records a timed-out wait;
     the step's outputs equal the oracle's, and consecutive steps with different sizes
     share the workspace."""
     if shape == "tiny":
@@ -825,7 +825,7 @@ def test_one_launch_step_leaves_the_handoff_region_zero(lib, shape):
         w = synth.WORKLOADS["qwen3_8b_32k"].with_(batch=2, num_kv_heads=2)
     else:
         w = synth.WORKLOADS["tiny_4k"].with_(batch=3, ctx=1024, min_len=60, fetch_ratio=1.0)
-    _say(f"one-launch hand-off region, {shape}")
+    _say(f"hand-off region, {shape}")
     d = lib.dims_for(w)
     inp = {kk: t.to(DEV) for kk, t in synth.generate(w, "cpu").items()}
     summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
@@ -873,7 +873,8 @@ def test_one_launch_step_leaves_the_handoff_region_zero(lib, shape):
                                           rn2, buffers=b2)
         torch.cuda.synchronize()
         assert lib.workspace_status(d2, bufs.ws) == 0
-        assert int(torch.count_nonzero(bufs.ws[lib.workspace_bytes(d2, lib.table_stride(d2)):])) == 0
+        lo2, hi2 = lib.workspace_bytes(d2, lib.table_stride(d2)), lib.workspace_bytes(d2)
+        assert int(torch.count_nonzero(bufs.ws[lo2:hi2])) == 0
         table, tc = ref.resident_table(i64(r2), inp2["seq_lens"].cpu().numpy(), w2.window, w2.block)
         eo, el = ref.sparse_attention(f64(inp2["q"]), f64(inp2["k"]), f64(inp2["v"]), table, tc,
                                       inp2["seq_lens"].cpu().numpy(), default_scale(), w2.block)

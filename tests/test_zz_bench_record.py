@@ -1,5 +1,5 @@
 """bench.py end to end on the GPU at the small workload: one JSON line with every field
-of the benchmark record (throughput, roofline of the dominant launch, the oracle's
+of the benchmark record (throughput, roofline of the whole step, per-launch times, the oracle's
 CPU baseline), produced through the C ABI."""
 import json
 
@@ -38,9 +38,15 @@ def test_bench_record_fields(capsys):
         assert key in roof, key
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert roof["achieved"] > 0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
-    assert roof["bytes_per_launch"] > 0 and roof["avg_launch_us"] > 0
+    assert roof["scope"] == "whole step" and roof["bytes_per_step"] > 0
+    assert abs(roof["achieved"] - roof["bytes_per_step"] / (r["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * roof["achieved"] + 0.2
+    dom = r["dominant_kernel"]
+    assert dom["avg_launch_us"] > 0 and dom["kernel"] in roof["kernels"]
+    assert set(r["launches"]) == {"launch1", "launch2"}
+    assert r["launches"]["launch1"]["bytes_per_launch"] > 0
     cpu = r["cpu_baseline"]
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in cpu, key
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
     assert r["checks"].get("graph_matches_eager", True) is True
+    assert r["checks"]["handoff_status_zero"] is True
