@@ -309,6 +309,24 @@ oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q,
                                           float* lse, void* ws, size_t ws_bytes,
                                           hipStream_t stream);
 
+/* oasis_decode_step_overlapped without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is a 16 MiB device
+ * array of the library (one copy per GPU, held from the library's load until
+ * the process ends); dims whose oasis_workspace_bytes exceeds it are rejected
+ * with OASIS_ERR_WORKSPACE before anything is queued.  The call queues a fill
+ * kernel that clears the array's hand-off region for `dims`, then the kernels of
+ * oasis_decode_step_overlapped; it allocates nothing and calls no allocating
+ * routine.  All calls on one GPU share its array: calls whose work overlaps on
+ * that GPU (other streams, other threads) race and their results are undefined;
+ * calls ordered on one stream are safe.  Arguments and outputs as for
+ * oasis_decode_step_overlapped. */
+oasis_status oasis_decode_step_overlapped_noalloc(
+    const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
+    const int32_t* seq_lens, float* scores, int32_t* topk, const int32_t* resident,
+    int32_t* resident_next, int32_t* plan, int32_t* plan_count, int32_t* table,
+    int32_t* table_count, float scale, float* out, float* lse, hipStream_t stream);
+
 /* oasis_decode_step_overlapped with timing markers, for measurement:
  * events[0..2] (created by the caller with hipEventCreate) are recorded on
  * `stream` before the first launch, after it, and after the second launch (the

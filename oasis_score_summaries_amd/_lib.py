@@ -76,6 +76,8 @@ _SIGNATURES = {
     "oasis_decode_step_overlapped": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                     _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_size_t,
                                                     _P]),
+    "oasis_decode_step_overlapped_noalloc": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                            _P, _P, _P, ctypes.c_float, _P, _P, _P]),
     "oasis_decode_step_overlapped_timed": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                                           _P, _P, _P, ctypes.c_float, _P, _P, _P,
                                                           ctypes.c_size_t, _P,
@@ -463,6 +465,37 @@ def decode_step_overlapped(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor,
         _ptr(b.plan if b.plan.numel() else None), _ptr(b.plan_count),
         _ptr(b.table), _ptr(b.table_count), float(scale), _ptr(b.out), _ptr(b.lse), _ptr(b.ws),
         b.ws.numel(), _stream(stream)), "oasis_decode_step_overlapped")
+    res = b.as_dict()
+    res["resident"] = resident_next
+    return res
+
+
+def decode_step_overlapped_noalloc(dims: OasisDims, q: torch.Tensor, summ: torch.Tensor, k: torch.Tensor,
+                                   v: torch.Tensor, seq_lens: torch.Tensor, resident: torch.Tensor,
+                                   resident_next: torch.Tensor, scale: Optional[float] = None,
+                                   outputs: Optional[StepBuffers] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """decode_step_overlapped with the library's own scratch array as the workspace
+    (oasis_decode_step_overlapped_noalloc); ``outputs``' workspace is not used."""
+    s = _shapes(dims)
+    _need(q, "q", torch.bfloat16, s["q"], align=16)
+    dev = q.device
+    _need(summ, "summ", torch.bfloat16, s["summ"], dev, align=16)
+    _need(k, "k", torch.bfloat16, s["kv"], dev, align=16)
+    _need(v, "v", torch.bfloat16, s["kv"], dev, align=16)
+    _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
+    _need(resident, "resident", torch.int32, s["resident"], dev)
+    _need(resident_next, "resident_next", torch.int32, s["resident"], dev)
+    if outputs is None:
+        outputs = StepBuffers(dims, dev)
+    b = outputs
+    if scale is None:
+        scale = 1.0 / math.sqrt(128)
+    _check(load().oasis_decode_step_overlapped_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(summ), _ptr(k), _ptr(v), _ptr(seq_lens), _ptr(b.scores),
+        _ptr(b.topk), _ptr(resident), _ptr(resident_next),
+        _ptr(b.plan if b.plan.numel() else None), _ptr(b.plan_count),
+        _ptr(b.table), _ptr(b.table_count), float(scale), _ptr(b.out), _ptr(b.lse),
+        _stream(stream)), "oasis_decode_step_overlapped_noalloc")
     res = b.as_dict()
     res["resident"] = resident_next
     return res

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liboasis.so")
 SOURCES = ["abi.cpp", "summaries.hip", "score.hip", "select.hip", "attention.hip", "fused.hip",
-           "working_set.hip"]
+           "working_set.hip", "noalloc.hip"]
 ARCH = os.environ.get("OASIS_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions are kept out of the device code: ordinary float code

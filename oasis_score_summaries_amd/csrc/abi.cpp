@@ -378,6 +378,42 @@ oasis_status oasis_decode_step_overlapped(const oasis_dims* dims, const void* q,
                                      out, lse, ws, ws_bytes, stream, nullptr);
 }
 
+oasis_status oasis_decode_step_overlapped_noalloc(
+    const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
+    const int32_t* seq_lens, float* scores, int32_t* topk, const int32_t* resident,
+    int32_t* resident_next, int32_t* plan, int32_t* plan_count, int32_t* table,
+    int32_t* table_count, float scale, float* out, float* lse, hipStream_t stream) {
+  oasis::Dims d;
+  oasis_status st = check_dims(dims, &d);
+  if (st != OASIS_OK) return st;
+  const size_t need = oasis::step_workspace_bytes(d), have = oasis::noalloc_scratch_bytes();
+  if (need > have)
+    return fail(OASIS_ERR_WORKSPACE,
+                "decode_step_overlapped_noalloc: these dims need %zu workspace bytes, the library's "
+                "scratch array holds %zu; use oasis_decode_step_overlapped with a workspace",
+                need, have);
+  void* ws = nullptr;
+  if ((st = hip_status(oasis::noalloc_scratch(&ws), "decode_step_overlapped_noalloc/scratch")) != OASIS_OK)
+    return st;
+  // Every argument checked before anything is queued.
+  int32_t* rn = resident_next;
+  OASIS_REQUIRE(resident_next);
+  if ((st = check_step_args(dims, d, q, summ, k, v, seq_lens, scores, topk, resident, &rn, plan,
+                            plan_count, table, table_count, scale, out, ws, have)) != OASIS_OK)
+    return st;
+  if (resident_next == resident)
+    return fail(OASIS_ERR_INVALID_ARG,
+                "resident_next must be its own buffer: the attention reads resident meanwhile");
+  // The array keeps whatever the last call on this device left (other dims, or a step
+  // whose wait timed out): its hand-off region is cleared for these dims first.
+  if ((st = hip_status(oasis::launch_clear_handoff(d, ws, stream), "decode_step_overlapped_noalloc/clear")) !=
+      OASIS_OK)
+    return st;
+  return decode_step_overlapped_impl(dims, q, summ, k, v, seq_lens, scores, topk, resident,
+                                     resident_next, plan, plan_count, table, table_count, scale,
+                                     out, lse, ws, have, stream, nullptr);
+}
+
 oasis_status oasis_decode_step_overlapped_timed(
     const oasis_dims* dims, const void* q, const void* summ, const void* k, const void* v,
     const int32_t* seq_lens, float* scores, int32_t* topk, const int32_t* resident,

@@ -38,6 +38,10 @@ size_t handoff_status_offset(const Dims& d);
 bool handoff_step_fits(const Dims& d);
 // Zero-fills the hand-off region of a step workspace.
 hipError_t launch_clear_handoff(const Dims& d, void* ws, hipStream_t stream);
+// The library's own step workspace on the current device (a device array, no
+// allocation): its size, and its device address (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
 
 hipError_t launch_build_summaries(const Dims& d, const void* k, const int32_t* seq_lens, void* summ,
                                   hipStream_t stream);

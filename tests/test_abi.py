@@ -44,7 +44,7 @@ def _dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 28
+    assert len(names) == 29
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.exported_symbols())
@@ -115,6 +115,20 @@ def test_null_pointers_rejected(lib):
     assert lib.oasis_fetch_cap(ctypes.byref(d0)) == 0
     assert lib.oasis_build_plan(ctypes.byref(d0), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
                                 None) == INVALID_ARG          # plan_count is still required
+
+
+@cpu_only
+def test_noalloc_step_rejects_dims_beyond_its_array(lib):
+    """The step on the library's own scratch array refuses dims whose workspace exceeds
+    the array (16 MiB), before any HIP call, and names the reason."""
+    big = _dims(batch=256, num_kv_heads=8, max_blocks=2048, top_k=128)
+    assert lib.oasis_workspace_bytes(ctypes.byref(big)) > 16 << 20
+    st = lib.oasis_decode_step_overlapped_noalloc(ctypes.byref(big), *([FAKE] * 13), 0.1, FAKE, FAKE, None)
+    assert st == WORKSPACE
+    assert b"scratch array" in lib.oasis_last_error()
+    bad = _dims(group=0)
+    assert lib.oasis_decode_step_overlapped_noalloc(ctypes.byref(bad), *([FAKE] * 13), 0.1, FAKE, FAKE,
+                                                    None) == INVALID_ARG
 
 
 @cpu_only
