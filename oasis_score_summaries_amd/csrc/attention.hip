@@ -101,7 +101,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(const floa
                                                                       float* __restrict__ out,
                                                                       float* __restrict__ lse) {
   __shared__ MergeShared<kMergeWaves> sh;
-  attn_merge_wg<kMergeWaves>(blockIdx.x, sh, part, group, nsplit, out, lse);
+  // Query heads of KV head h on XCD h % 8, the XCD its splits ran on when they were
+  // placed by XCD (a multiple of 8 heads); otherwise in order.
+  int x, head;
+  xcd_item(blockIdx.x, group, gridDim.x / group, true, x, head);
+  attn_merge_wg<kMergeWaves>(head * group + x, sh, part, group, nsplit, out, lse);
 }
 
 hipError_t launch_attention_split(const Dims& d, const AttnSplit& s, const void* q, const void* k,

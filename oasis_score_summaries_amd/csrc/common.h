@@ -48,9 +48,12 @@ __host__ __device__ inline int first_window_block(int len, int window, int bshif
 // heads maps to (x, head): head-major in the plain order, or, with `by_xcd` and nh a
 // multiple of 8 (and the role's first workgroup index too), with every item of a
 // head on one XCD, so that the head's queries are fetched into one L2 instead of
-// eight.  Measured: 2 % faster steps at 80 query rows per KV head (20 KB of queries
-// per head), 0.5 % slower at 20 rows and 32 x 8 heads, 14 % slower at 20 rows and
-// 4 x 8 heads of 8192 blocks; the host asks for it from 64 query rows on.
+// eight.  Measured for the kernels that place both their scoring and their
+// attention this way: 2 % faster steps at 80 query rows per KV head (20 KB of
+// queries per head), 0.5 % slower at 20 rows and 32 x 8 heads, 14 % slower at 20
+// rows and 4 x 8 heads of 8192 blocks; the host asks for it from 64 query rows on.
+// The overlapped step's first launch places only its attention splits (and the merge)
+// by XCD, always: 1 % faster at 20 rows and 8 x 8 heads.
 __device__ inline void xcd_item(int i, int gx, int nh, bool by_xcd, int& x, int& head) {
   if (by_xcd && (nh & 7) == 0) {
     const int j = i >> 3;
@@ -139,7 +142,7 @@ struct Handoff {
   uint32_t* flag_score;  // [B*H, score_waves]: one flag per scoring wave
   uint32_t* status;      // stays 0 unless a wait timed out
   uint32_t* mbox;        // [B*H, NB]: order keys of the candidate scores (never 0)
-  int score_waves;       // scoring waves per (sequence, KV head), <= 64
+  int score_waves;       // scoring waves per (sequence, KV head), <= 256
 };
 
 // ---- bf16 bit helpers -------------------------------------------------------------

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void step_ke
   const int heads = n_score / score_gx;
   int b = blockIdx.x;
   if (b < n_score) {
-    score_wg<RT, true>(b % score_gx, b / score_gx, sh.s, sa, &ho);
+    score_wg<RT, true, kStepScoreTiles>(b % score_gx, b / score_gx, sh.s, sa, &ho);
     return;
   }
   b -= n_score;
@@ -87,7 +87,11 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void step_ke
     return;
   }
   b -= heads;
-  if (b < attn_gx * heads) attn_split_wg<GP, true, POOL>(b % attn_gx, b / attn_gx, sh.a, aa);
+  // The attention splits of a head share one XCD (its L2 fetches the head's queries
+  // once); the role starts at a multiple of 8 when the head count is one.
+  int x, head;
+  xcd_item(b, attn_gx, heads, true, x, head);
+  if (head < heads) attn_split_wg<GP, true, POOL>(x, head, sh.a, aa);
 }
 
 template <int THREADS, int ITEMS>
@@ -316,7 +320,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static HandoffLayout handoff_layout(const Dims& d) {
   const size_t heads = (size_t)d.batch * d.heads;
   const size_t recs = attn_workspace_bytes(d, d.table_stride);
-  const size_t score_waves = (size_t)score_grid_x(d) * kScoreWaves;
+  const size_t score_waves = (size_t)score_grid_x(d, kStepScoreTiles) * kScoreWaves;
   HandoffLayout L;
   L.flag_score = recs;
   L.status = L.flag_score + heads * score_waves * sizeof(uint32_t);
@@ -345,7 +349,8 @@ hipError_t launch_clear_handoff(const Dims& d, void* ws, hipStream_t stream) {
 bool handoff_step_fits(const Dims& d) {
   const int rt = (d.group * d.queries + 15) / 16;
   return rt <= 2 && d.group <= 4 && d.top_k <= kScoreThreads && d.max_blocks <= 8 * kScoreThreads &&
-         score_grid_x(d) * kScoreWaves <= 64 && attn_split(d, d.table_stride).num_splits <= 256;
+         score_grid_x(d, kStepScoreTiles) * kScoreWaves <= 256 &&
+         attn_split(d, d.table_stride).num_splits <= 256;
 }
 
 static hipError_t launch_one_step(const Dims& d, const AttnSplit& s, const void* q, const void* summ,
@@ -360,7 +365,7 @@ static hipError_t launch_one_step(const Dims& d, const AttnSplit& s, const void*
   ho.flag_score = reinterpret_cast<uint32_t*>(base + L.flag_score);
   ho.status = reinterpret_cast<uint32_t*>(base + L.status);
   ho.mbox = reinterpret_cast<uint32_t*>(base + L.mbox);
-  const int score_gx = score_grid_x(d);
+  const int score_gx = score_grid_x(d, kStepScoreTiles);
   ho.score_waves = score_gx * kScoreWaves;
   const ScoreArgs sa = score_args(d, q, summ, seq_lens, scores);
   AttnArgs aa = attn_args(d, s, q, pool ? pool->pool_k : k, pool ? pool->pool_v : v, resident, nullptr,

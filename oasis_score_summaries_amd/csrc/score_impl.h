@@ -14,7 +14,10 @@ namespace oasis {
 constexpr int kScoreWaves = kWavesPerWG;                         // waves per workgroup
 constexpr int kScoreThreads = 64 * kScoreWaves;
 constexpr int kScoreTilesPerWave = OASIS_SCORE_TILES_PER_WAVE;   // 16-block MFMA tiles per wave
-constexpr int kScoreBlocksPerWG = kScoreWaves * kScoreTilesPerWave * 16;
+// The overlapped step's first launch scores one tile per wave: twice the workgroups of
+// half the size, which retire sooner and let its attention workgroups in earlier.
+constexpr int kStepScoreTiles = 1;
+__host__ __device__ constexpr int score_blocks_per_wg(int tiles) { return kScoreWaves * tiles * 16; }
 
 // The query fragments do not depend on the block, so the workgroup builds them once
 // in LDS (sign-split, in MFMA lane order) and every wave reads them from there.
@@ -32,12 +35,12 @@ struct ScoreArgs {
   int heads, max_blocks, rows, window, bshift;
 };
 
-// One workgroup: block range `bx` (kScoreBlocksPerWG candidate blocks) of (sequence,
+// One workgroup: block range `bx` (score_blocks_per_wg(TILES) candidate blocks) of (sequence,
 // KV head) `bh`.  Every thread of the workgroup calls it.  With HANDOFF, each
 // candidate's order key also goes to the mailbox of `ho` (device-scope stores) and
 // every wave then sets its flag, so that a selection workgroup of the same launch can
 // take the scores over.
-template <int RT, bool HANDOFF = false>
+template <int RT, bool HANDOFF = false, int TILES = kScoreTilesPerWave>
 __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreShared<RT>& sh,
                                                         const ScoreArgs& a,
                                                         const Handoff* ho = nullptr) {
@@ -48,13 +51,14 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
   const int b = bh / heads;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int jw = bx * kScoreBlocksPerWG + wave * kScoreTilesPerWave * 16;  // this wave's first block
+  constexpr int kBlocksPerWG = score_blocks_per_wg(TILES);
+  const int jw = bx * kBlocksPerWG + wave * TILES * 16;  // this wave's first block
   const int len = clamp_len(a.seq_lens[b], max_blocks, a.bshift);
   const int n_cand = first_window_block(len, window, a.bshift);
   float* out = a.scores + (size_t)bh * max_blocks;
-  if ((int)bx * kScoreBlocksPerWG >= n_cand) {  // no candidate in this workgroup's range
-    for (int j = threadIdx.x; j < kScoreBlocksPerWG; j += blockDim.x) {
-      const int jb = bx * kScoreBlocksPerWG + j;
+  if ((int)bx * kBlocksPerWG >= n_cand) {  // no candidate in this workgroup's range
+    for (int j = threadIdx.x; j < kBlocksPerWG; j += blockDim.x) {
+      const int jb = bx * kBlocksPerWG + j;
       if (jb < max_blocks) out[jb] = -INFINITY;
     }
     if (HANDOFF && (threadIdx.x & 63) == 0)
@@ -76,9 +80,9 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
     const int c = 4 * ((f / 64) % 8) + ((f & 63) >> 4);
     qv[u] = qb[(row < rows ? row : rows - 1) * 16 + (c & 15)];
   }
-  u32x4 bv[kScoreTilesPerWave][8];
+  u32x4 bv[TILES][8];
 #pragma unroll
-  for (int t = 0; t < kScoreTilesPerWave; ++t) {
+  for (int t = 0; t < TILES; ++t) {
     int jb = jw + 16 * t + col;
     jb = jb < n_cand ? jb : n_cand - 1;  // n_cand >= 1 here; columns past it are masked below
     const size_t base = ((size_t)bh * max_blocks + jb) * 32 + grp;
@@ -102,7 +106,7 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
   __syncthreads();
 
 #pragma unroll
-  for (int t = 0; t < kScoreTilesPerWave; ++t) {
+  for (int t = 0; t < TILES; ++t) {
     const int jb = jw + 16 * t + col;
     if (jw + 16 * t >= max_blocks) break;  // uniform across the wave
     floatx4 acc[RT];
@@ -155,6 +159,8 @@ inline ScoreArgs score_args(const Dims& d, const void* q, const void* summ, cons
   a.bshift = d.bshift;
   return a;
 }
-inline int score_grid_x(const Dims& d) { return (d.max_blocks + kScoreBlocksPerWG - 1) / kScoreBlocksPerWG; }
+inline int score_grid_x(const Dims& d, int tiles = kScoreTilesPerWave) {
+  return (d.max_blocks + score_blocks_per_wg(tiles) - 1) / score_blocks_per_wg(tiles);
+}
 
 }  // namespace oasis
