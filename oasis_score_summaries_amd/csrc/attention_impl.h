@@ -112,8 +112,14 @@ __device__ __attribute__((always_inline)) void attn_split_wg(int sp, int bh, Att
   // together with the count, clamped to the row (not to the count).  Half h of unit
   // u is 8-token half 2u + h of the table, in entry (2u + h) >> hs (both halves in
   // one entry unless the blocks hold 8 tokens).
+  // The entry is wave-uniform: a scalar load (through the scalar cache) keeps it out of
+  // the vector memory queues that the streaming loads fill.  The table is never written
+  // by the launch that reads it.
   auto load_entry = [&](int e) {
-    return RES ? table[(size_t)bh * K + (e < K ? e : K - 1)] : table[(size_t)bh * T + (e < T ? e : T - 1)];
+    e = __builtin_amdgcn_readfirstlane(e);
+    const size_t idx = RES ? (size_t)bh * K + (e < K ? e : K - 1) : (size_t)bh * T + (e < T ? e : T - 1);
+    return reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+        reinterpret_cast<uintptr_t>(table))[idx];
   };
   int ent0, ent1 = -1;
   {

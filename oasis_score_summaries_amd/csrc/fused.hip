@@ -56,8 +56,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void score_a
 }
 
 // The overlapped step with its background half inside launch 1: the scoring
-// workgroups, then one selection-and-plan workgroup per (sequence, KV head), then
-// the attention split workgroups.  A selection workgroup takes its head's scores
+// workgroups, then the attention split workgroups with one selection-and-plan
+// workgroup per (sequence, KV head) among them.  A selection workgroup takes its head's scores
 // over from the scoring workgroups through the hand-off region `ho` (device-scope
 // stores, per-wave flags, words that carry their own validity; see common.h), so the
 // selection and plan run while the attention still streams K and V instead of after
@@ -66,6 +66,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void score_a
 // workgroup comes after the scoring workgroups it waits for in the grid, and every
 // wait is bounded.  Up to 32 query rows, 4 query heads, K = 256 and 2048 blocks per
 // KV head (the selection in 256 threads).
+constexpr int kStepAttnBeforeSelect = 512;  // measured at Qwen3-8B 32K: 256-768 alike, 1024 late
 template <int RT, int GP, int ITEMS, bool POOL>
 __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void step_kernel(
     ScoreArgs sa, TopkPlanArgs ta, AttnArgs aa, Handoff ho, int n_score, int score_gx, int attn_gx) {
@@ -82,11 +83,15 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void step_ke
     return;
   }
   b -= n_score;
-  if (b < heads) {
-    topk_plan_wg<kScoreThreads, ITEMS, true>(b, sh.t, bm, ta, &ho);
+  // The selection workgroups follow the first kStepAttnBeforeSelect attention
+  // workgroups, so that they are dispatched about when the scores they wait for are
+  // done rather than holding slots while the scoring still streams.
+  const int k_pre = min(kStepAttnBeforeSelect, attn_gx * heads) & ~7;
+  if (b >= k_pre && b < k_pre + heads) {
+    topk_plan_wg<kScoreThreads, ITEMS, true>(b - k_pre, sh.t, bm, ta, &ho);
     return;
   }
-  b -= heads;
+  if (b >= k_pre) b -= heads;
   // The attention splits of a head share one XCD (its L2 fetches the head's queries
   // once); the role starts at a multiple of 8 when the head count is one.
   int x, head;
