@@ -142,6 +142,7 @@ struct Handoff {
   uint32_t* flag_score;  // [B*H, score_waves]: one flag per scoring wave
   uint32_t* status;      // stays 0 unless a wait timed out
   uint32_t* mbox;        // [B*H, NB]: order keys of the candidate scores (never 0)
+  float* scores;         // [B*H, NB]: the scores output, written by the selection workgroups
   int score_waves;       // scoring waves per (sequence, KV head), <= 256
 };
 
@@ -169,6 +170,10 @@ __device__ inline uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// The float of an order key (-0.0 comes back as +0.0).
+__device__ inline float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 // ---- wave64 cross-lane primitives on DPP (no LDS traffic) ---------------------------

@@ -370,6 +370,7 @@ static hipError_t launch_one_step(const Dims& d, const AttnSplit& s, const void*
   ho.flag_score = reinterpret_cast<uint32_t*>(base + L.flag_score);
   ho.status = reinterpret_cast<uint32_t*>(base + L.status);
   ho.mbox = reinterpret_cast<uint32_t*>(base + L.mbox);
+  ho.scores = scores;
   const int score_gx = score_grid_x(d, kStepScoreTiles);
   ho.score_waves = score_gx * kScoreWaves;
   const ScoreArgs sa = score_args(d, q, summ, seq_lens, scores);

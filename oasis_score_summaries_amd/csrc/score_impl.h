@@ -36,10 +36,11 @@ struct ScoreArgs {
 };
 
 // One workgroup: block range `bx` (score_blocks_per_wg(TILES) candidate blocks) of (sequence,
-// KV head) `bh`.  Every thread of the workgroup calls it.  With HANDOFF, each
-// candidate's order key also goes to the mailbox of `ho` (device-scope stores) and
-// every wave then sets its flag, so that a selection workgroup of the same launch can
-// take the scores over.
+// KV head) `bh`.  Every thread of the workgroup calls it.  With HANDOFF, the scores
+// go to the selection workgroup of the same launch instead of `a.scores`: each
+// candidate's order key goes to the mailbox of `ho` (device-scope stores) and every
+// wave then sets its flag; the selection writes the scores output, a head's row at a
+// time (whole lines, where the scoring waves would write 64-byte pieces).
 template <int RT, bool HANDOFF = false, int TILES = kScoreTilesPerWave>
 __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreShared<RT>& sh,
                                                         const ScoreArgs& a,
@@ -57,7 +58,7 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
   const int n_cand = first_window_block(len, window, a.bshift);
   float* out = a.scores + (size_t)bh * max_blocks;
   if ((int)bx * kBlocksPerWG >= n_cand) {  // no candidate in this workgroup's range
-    for (int j = threadIdx.x; j < kBlocksPerWG; j += blockDim.x) {
+    for (int j = threadIdx.x; !HANDOFF && j < kBlocksPerWG; j += blockDim.x) {
       const int jb = bx * kBlocksPerWG + j;
       if (jb < max_blocks) out[jb] = -INFINITY;
     }
@@ -135,7 +136,7 @@ __device__ __attribute__((always_inline)) void score_wg(int bx, int bh, ScoreSha
     }
     m = fmaxf(m, __shfl_xor(m, 16, 64));
     m = fmaxf(m, __shfl_xor(m, 32, 64));
-    if (grp == 0 && jb < max_blocks) out[jb] = (jb < n_cand) ? m : -INFINITY;
+    if (!HANDOFF && grp == 0 && jb < max_blocks) out[jb] = (jb < n_cand) ? m : -INFINITY;
     if (HANDOFF && grp == 0 && jb < n_cand) {
       const uint32_t key = order_key(m);
       st_dev(ho->mbox + (size_t)bh * max_blocks + jb, key != 0u ? key : 1u);  // 0 marks "not written"

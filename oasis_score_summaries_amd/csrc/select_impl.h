@@ -131,12 +131,14 @@ constexpr bool kCanStage = ITEMS * THREADS * sizeof(float) <= sizeof(SelectShare
 // global read depends on the first.
 // MBOX: the keys come from the mailbox row `mrow` of a hand-off instead (the caller has
 // waited for the head's arrivals): each candidate's key is read until it is non-zero
-// and then cleared, leaving the row zero.
+// and then cleared, leaving the row zero; the row's scores then go to `score_out`
+// (-inf past the candidates), whole lines at a time.
 template <int THREADS, int ITEMS, bool MBOX = false>
 __device__ __attribute__((always_inline)) int topk_select(const float* __restrict__ row, int n_cand, int K,
                            SelectShared<THREADS, ITEMS>& sh, int NB, PlanBitmaps* bm = nullptr,
                            int res_block = -1, uint32_t* res_key = nullptr,
-                           uint32_t* mrow = nullptr, uint32_t* status = nullptr) {
+                           uint32_t* mrow = nullptr, uint32_t* status = nullptr,
+                           float* score_out = nullptr) {
   constexpr int NW = THREADS / 64;
   constexpr bool kStage = kCanStage<THREADS, ITEMS>;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -153,7 +155,6 @@ __device__ __attribute__((always_inline)) int topk_select(const float* __restric
   }
   if (res_key != nullptr) *res_key = order_key(-INFINITY);
   const int m = n_cand < K ? n_cand : K;
-  if (m <= 0) return 0;  // uniform across the workgroup
   if (MBOX) {
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {  // a key still zero has not arrived yet: read it again
@@ -164,8 +165,10 @@ __device__ __attribute__((always_inline)) int topk_select(const float* __restric
     for (int i = 0; i < ITEMS; ++i) {
       const int e = i * THREADS + tid;
       if (e < n_cand) __builtin_amdgcn_raw_buffer_store_b32(0u, mr, (uint32_t)e * 4u, 0, kDevScopeAux);
+      if (e < NB) score_out[e] = e < n_cand ? key_float(key[i]) : -INFINITY;
     }
   }
+  if (m <= 0) return 0;  // uniform across the workgroup
 
   uint32_t lmax = 0u, lmin = 0xffffffffu;
   uint32_t* staged = reinterpret_cast<uint32_t*>(sh.bucket);
@@ -504,7 +507,8 @@ struct TopkPlanArgs {
 // cleared while the selection runs.  Every thread of the workgroup calls it.
 // MBOX: the scores are handed over by the scoring workgroups of the same launch
 // through `ho` (wave 0 waits for the flags of the head's scoring waves and clears
-// them, then every thread reads its keys from the mailbox).
+// them, then every thread reads its keys from the mailbox), and the workgroup writes
+// the head's row of the scores output from them.
 template <int THREADS, int ITEMS, bool MBOX = false>
 __device__ __attribute__((always_inline)) void topk_plan_wg(int bh, TopkPlanShared<THREADS, ITEMS>& sh,
                                                             PlanBitmaps& bm, const TopkPlanArgs& a,
@@ -530,7 +534,8 @@ __device__ __attribute__((always_inline)) void topk_plan_wg(int bh, TopkPlanShar
   const int m = topk_select<THREADS, ITEMS, MBOX>(srow, n_cand, K, sh.t, NB, &bm, rs.block,
                                                   kCanStage<THREADS, ITEMS> ? &rs.key : nullptr,
                                                   MBOX ? ho->mbox + (size_t)bh * NB : nullptr,
-                                                  MBOX ? ho->status : nullptr);
+                                                  MBOX ? ho->status : nullptr,
+                                                  MBOX ? ho->scores + (size_t)bh * NB : nullptr);
   if (m == 0) {  // the selection returned at once: mark the resident set here
     __syncthreads();
     if (rs.block >= 0 && rs.block < NB) atomicOr(&bm.res[rs.block >> 5], 1u << (rs.block & 31));
