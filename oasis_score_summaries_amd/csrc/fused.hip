@@ -351,10 +351,16 @@ hipError_t launch_clear_handoff(const Dims& d, void* ws, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The selection workgroups of launch 1 hold a workgroup slot each for most of the
+// launch, so past a few hundred heads the selection is better off in launch 2.
+// Measured per step at 20 query rows (Qwen3-8B layer shape): 64 heads 31.5 against
+// 35.9 us, 128 heads 55.5 against 58.7, 256 heads 104.1 against 103.5, and 512 heads
+// of 1024 blocks (36-layer shape) 152.9 against 143.7.
+constexpr int kHandoffMaxHeads = 256;
 bool handoff_step_fits(const Dims& d) {
   const int rt = (d.group * d.queries + 15) / 16;
   return rt <= 2 && d.group <= 4 && d.top_k <= kScoreThreads && d.max_blocks <= 8 * kScoreThreads &&
-         score_grid_x(d, kStepScoreTiles) * kScoreWaves <= 256 &&
+         d.batch * d.heads <= kHandoffMaxHeads && score_grid_x(d, kStepScoreTiles) * kScoreWaves <= 256 &&
          attn_split(d, d.table_stride).num_splits <= 256;
 }
 

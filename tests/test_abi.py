@@ -145,6 +145,8 @@ def test_workspace_and_table_stride_checks(lib):
     assert step_need >= need + 2 * 2 * 64 * 4
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(d)) == 1
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=8))) == 0
+    assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(batch=32, num_kv_heads=8))) == 1
+    assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(batch=64, num_kv_heads=8))) == 0
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=0))) == -1
     off = lib.oasis_workspace_status_offset(ctypes.byref(d))
     assert need <= off < step_need and off % 4 == 0
