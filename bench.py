@@ -287,17 +287,28 @@ def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
 
     per_set = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
     units = [(i, b, h) for i in range(len(sets)) for (b, h) in per_set]
-    f64 = lambda t: t.to(torch.float64).numpy()
     scale = 1.0 / math.sqrt(128)
     step = ref.decode_step_overlapped if overlapped else ref.decode_step
     host = [{"lens": st["seq_lens"].cpu(), "res": st["resident"].cpu()} for st in sets]
+    workers = max(1, min(16, os.cpu_count() or 1))
+    # A unit's device inputs reach the oracle through host buffers allocated once per
+    # worker (the copy, then its fp64 form): fresh host arrays for every unit made the
+    # process's resident memory grow by about their size per unit with device inputs.
+    names = ("q", "summ", "k", "v")
+    slots = [[(torch.empty(tuple(sets[0][n][0:1, 0:1].shape), dtype=sets[0][n].dtype),
+               torch.empty(tuple(sets[0][n][0:1, 0:1].shape), dtype=torch.float64)) for n in names]
+             for _ in range(workers)]
 
-    def unit_inputs(u):
+    def unit_inputs(u, slot=0):
         i, b, h = units[u % len(units)]
         st = sets[i]
-        return (f64(st["q"][b:b + 1, h:h + 1].cpu()), f64(st["summ"][b:b + 1, h:h + 1].cpu()),
-                f64(st["k"][b:b + 1, h:h + 1].cpu()), f64(st["v"][b:b + 1, h:h + 1].cpu()),
-                host[i]["lens"][b:b + 1].numpy(), host[i]["res"][b:b + 1, h:h + 1].numpy().astype(np.int64))
+        xs = []
+        for n, (copy, wide) in zip(names, slots[slot]):
+            copy.copy_(st[n][b:b + 1, h:h + 1])
+            wide.copy_(copy)
+            xs.append(wide.numpy())
+        return (*xs, host[i]["lens"][b:b + 1].numpy(),
+                host[i]["res"][b:b + 1, h:h + 1].numpy().astype(np.int64))
 
     def run(x):
         step(*x, w.top_k, w.window, w.cap, scale)
@@ -317,11 +328,10 @@ def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
                      f"{elapsed:.1f} s of oracle time on one core, scaled to steps",
            "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 
-    workers = max(1, min(16, os.cpu_count() or 1))
     done_p, elapsed_p = 0, 0.0
     with threadpool_limits(1), ThreadPoolExecutor(workers) as pool:
         while elapsed_p < budget_s:
-            chunk = [unit_inputs(done_p + j) for j in range(workers)]
+            chunk = [unit_inputs(done_p + j, j) for j in range(workers)]
             t = time.perf_counter()
             list(pool.map(run, chunk))
             elapsed_p += time.perf_counter() - t
