@@ -99,8 +99,13 @@ constexpr int kMergeWaves = 4;
 __global__ __launch_bounds__(64 * kMergeWaves) void attn_merge_kernel(const float* __restrict__ part,
                                                                       int group, int nsplit,
                                                                       float* __restrict__ out,
-                                                                      float* __restrict__ lse) {
+                                                                      float* __restrict__ lse, int n_qh) {
   __shared__ MergeShared<kMergeWaves> sh;
+  if (nsplit <= kMergeWaveSplits) {  // a query head per wave
+    const int bhg = merge_wave_head(blockIdx.x, threadIdx.x >> 6, kMergeWaves, group, n_qh);
+    if (bhg >= 0) attn_merge_wave(bhg, part, group, nsplit, out, lse);
+    return;
+  }
   // Query heads of KV head h on XCD h % 8, the XCD its splits ran on when they were
   // placed by XCD (a multiple of 8 heads); otherwise in order.
   int x, head;
@@ -149,8 +154,9 @@ hipError_t launch_attention_split_pool(const Dims& d, const AttnSplit& s, const 
 
 hipError_t launch_attention_merge(const Dims& d, const AttnSplit& s, float* out, float* lse,
                                   const void* ws, hipStream_t stream) {
-  attn_merge_kernel<<<dim3(d.batch * d.heads * d.group), dim3(64 * kMergeWaves), 0, stream>>>(
-      (const float*)ws, d.group, s.num_splits, out, lse);
+  const int n_qh = d.batch * d.heads * d.group;
+  attn_merge_kernel<<<dim3(merge_workgroups(n_qh, s.num_splits, kMergeWaves)), dim3(64 * kMergeWaves), 0,
+                      stream>>>((const float*)ws, d.group, s.num_splits, out, lse, n_qh);
   return hipGetLastError();
 }
 

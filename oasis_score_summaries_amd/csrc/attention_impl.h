@@ -428,6 +428,59 @@ __device__ __attribute__((always_inline)) void attn_merge_wg(int bhg, MergeShare
   if (lse != nullptr && lane == 0) lse[(size_t)bh * group + g] = any ? (mx + __log2f(sum)) * kLn2 : -INFINITY;
 }
 
+// Query head `bhg` merged by the calling wave alone, for at most kMergeBatch splits:
+// every split's (max, sum) and output requested at once, no LDS.  With few splits per
+// head (many heads), a workgroup's waves take one query head each, instead of all
+// the waves sharing one head's few splits.  Every lane of the wave calls it.
+constexpr int kMergeWaveSplits = kMergeBatch;
+__device__ __attribute__((always_inline)) void attn_merge_wave(int bhg, const float* __restrict__ part,
+                                                               int group, int nsplit,
+                                                               float* __restrict__ out,
+                                                               float* __restrict__ lse) {
+  const int bh = bhg / group, g = bhg % group;
+  const int lane = threadIdx.x & 63;
+  const float* rec = part + ((size_t)bh * nsplit * group + g) * kRec;  // split s: + s * stride
+  const size_t stride = (size_t)group * kRec;
+  const int sl = lane < nsplit ? lane : 0;
+  const float m_l = rec[sl * stride + kHeadDim + 0];
+  const float l_l = rec[sl * stride + kHeadDim + 1];
+  float2v x[kMergeWaveSplits];
+#pragma unroll
+  for (int u = 0; u < kMergeWaveSplits; ++u)
+    x[u] = *((const float2v*)(rec + (size_t)(u < nsplit ? u : 0) * stride) + lane);
+  const float mx = wave_max_f32(lane < nsplit ? m_l : -INFINITY);
+  const float w = (mx == -INFINITY || lane >= nsplit) ? 0.f : __builtin_amdgcn_exp2f(m_l - mx);
+  const float sum = wave_sum_f32(w * (lane < nsplit ? l_l : 0.f));
+  float2v acc = {0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < kMergeWaveSplits; ++u) {
+    if (u < nsplit) acc += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u)) * x[u];
+  }
+  const bool any = mx != -INFINITY && sum > 0.f;
+  float2v* o2 = (float2v*)(out + ((size_t)bh * group + g) * kHeadDim) + lane;
+  *o2 = any ? acc / sum : float2v{0.f, 0.f};
+  if (lse != nullptr && lane == 0) lse[(size_t)bh * group + g] = any ? (mx + __log2f(sum)) * kLn2 : -INFINITY;
+}
+
+// Workgroups of the merge for `n_qh` query heads: one per query head, or, with at most
+// kMergeWaveSplits splits, one per `waves` query heads.
+__host__ __device__ inline int merge_workgroups(int n_qh, int nsplit, int waves) {
+  return nsplit <= kMergeWaveSplits ? (n_qh + waves - 1) / waves : n_qh;
+}
+
+// Query head of wave `wave` in merge workgroup `wg` of the one-head-per-wave merge
+// (-1: none).  When a KV head's query heads fill whole workgroups, those of KV head h
+// run on XCD h % 8, where its splits ran when they were placed by XCD.
+__device__ inline int merge_wave_head(int wg, int wave, int waves, int group, int n_qh) {
+  if (group % waves == 0) {
+    int x, head;
+    xcd_item(wg, group / waves, n_qh / group, true, x, head);
+    return head * group + x * waves + wave;
+  }
+  const int bhg = wg * waves + wave;
+  return bhg < n_qh ? bhg : -1;
+}
+
 // Host side: the argument block of the split kernels for `d` and split `s`.
 inline AttnArgs attn_args(const Dims& d, const AttnSplit& s, const void* q, const void* k, const void* v,
                    const int32_t* table, const int32_t* table_count, int table_stride,

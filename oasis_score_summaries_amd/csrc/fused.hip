@@ -110,6 +110,10 @@ __global__ __launch_bounds__(THREADS) void select_merge_kernel(TopkPlanArgs ta, 
   __shared__ PlanBitmaps bm;
   if ((int)blockIdx.x < n_select) {
     topk_plan_wg<THREADS, ITEMS>(blockIdx.x, sh.t, bm, ta);
+  } else if (nsplit <= kMergeWaveSplits) {  // a query head per wave
+    const int bhg = merge_wave_head((int)blockIdx.x - n_select, threadIdx.x >> 6, THREADS / 64, group,
+                                    n_select * group);
+    if (bhg >= 0) attn_merge_wave(bhg, part, group, nsplit, out, lse);
   } else {
     attn_merge_wg<THREADS / 64>(blockIdx.x - n_select, sh.m, part, group, nsplit, out, lse);
   }
@@ -301,10 +305,10 @@ static hipError_t launch_first_half(const Dims& d, const AttnSplit& s, const voi
 static hipError_t launch_second_half(const Dims& d, const AttnSplit& s, const TopkPlanArgs& sel,
                                      const void* ws, float* out, float* lse, hipStream_t stream) {
   const int heads = d.batch * d.heads;
-  const int grid2 = heads + heads * d.group;
 #define OASIS_SM_CASE(T, I)                                                                    \
   case I:                                                                                      \
-    select_merge_kernel<T, I><<<dim3(grid2), dim3(T), 0, stream>>>(sel, (const float*)ws,      \
+    select_merge_kernel<T, I><<<dim3(heads + merge_workgroups(heads * d.group, s.num_splits, T / 64)), \
+                                dim3(T), 0, stream>>>(sel, (const float*)ws,                   \
                                                                    d.group, s.num_splits, out, \
                                                                    lse, heads);                \
     break;
