@@ -170,6 +170,45 @@ def test_attention_on_given_tables(lib, G, lens, NB):
     np.testing.assert_allclose(f64(lse)[fin], el[fin], rtol=0, atol=OUT_ATOL)
 
 
+@pytest.mark.parametrize("B,H,G,K,nsplit", [(2, 3, 1, 56, 16), (2, 3, 3, 52, 15), (2, 3, 2, 60, 17),
+                                             (2, 4, 4, 56, 16), (1, 8, 8, 56, 16), (2, 4, 16, 56, 16),
+                                             (2, 4, 16, 60, 17)])
+def test_attention_merge_forms(lib, B, H, G, K, nsplit):
+    """The merge's two forms on either side of 16 splits per head: one wave per query head
+    (query-head counts that do not fill the last workgroup, KV heads placed by XCD or in
+    order) and one workgroup per query head; full, short and empty tables."""
+    _say(f"attention merge B={B} H={H} G={G} K={K}")
+    NB, W, Q = 128, 64, 2
+    lens = [2048, 1500][:B]
+    q, k, v, L = _small_inputs(40 + G + K, B, H, G, Q, NB, lens)
+    d = _dims(lib, B, H, G, NB, Q, K, W, 0.05)
+    T = lib.table_stride(d)
+    assert (T + 3) // 4 == nsplit           # one 16-token unit per wave, four waves per split
+    rng = np.random.default_rng(K * 100 + G)
+    table = np.full((B, H, T), -1, dtype=np.int64)
+    tc = np.zeros((B, H), dtype=np.int64)
+    for b in range(B):
+        nb = ref.num_blocks(lens[b])
+        for h in range(H):
+            n = [min(T, nb), min(T, nb), min(5, nb), 0][(b * H + h) % 4]
+            table[b, h, :n] = rng.choice(nb, size=n, replace=False)
+            tc[b, h] = n
+    scale = default_scale()
+    out, lse = lib.sparse_decode_attn(d, q.to(DEV), k.to(DEV), v.to(DEV),
+                                      torch.from_numpy(table.astype(np.int32)).to(DEV),
+                                      torch.from_numpy(tc.astype(np.int32)).to(DEV), L.to(DEV), scale)
+    torch.cuda.synchronize()
+    eo, el = ref.sparse_attention(f64(q), f64(k), f64(v), table, tc, L.numpy(), scale)
+    np.testing.assert_allclose(f64(out), eo, rtol=0, atol=OUT_ATOL)
+    fin = np.isfinite(el)
+    assert np.array_equal(np.isneginf(f64(lse)), ~fin)
+    np.testing.assert_allclose(f64(lse)[fin], el[fin], rtol=0, atol=OUT_ATOL)
+    # The merge adds fp32 partials: a dropped, doubled or misweighted split, or a query
+    # head's record taken for another's, moves the output far more than this.
+    assert np.abs(f64(out) - eo).max() <= 1e-4
+    assert np.abs(f64(lse)[fin] - el[fin]).max() <= 1e-4
+
+
 def test_attention_all_blocks_matches_dense(lib):
     """Table = every block: the sparse path reduces to dense decode attention."""
     B, H, G, Q, NB = 2, 2, 4, 1, 64
