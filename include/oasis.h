@@ -289,8 +289,8 @@ oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void
  *     `resident` and writing the next slot table to `resident_next` (and plan,
  *     table, table_count for it), as oasis_decode_step does.
  * The halves share only inputs, so their work items sit in the same grids.  Up
- * to 32 query rows (G * Q), 4 query heads per KV head, K = 256, 2048 blocks per
- * KV head and 256 (sequence, KV head) pairs, launch 1 holds the scoring
+ * to 96 query rows (G * Q), K = 256, 2048 blocks per KV head and 256
+ * (sequence, KV head) pairs, launch 1 holds the scoring
  * workgroups, one selection-and-plan workgroup per KV head that takes its
  * head's scores over from the scoring workgroups through the hand-off region of
  * the workspace (it must be zero before the first step; see

@@ -34,6 +34,8 @@ static_assert(kScoreWaves == kAttnWaves, "one workgroup size for both roles");
 #ifndef OASIS_FUSED_MAX_RT
 #define OASIS_FUSED_MAX_RT 6
 #endif
+// 16-row tiles of the query rows (group x queries) of one KV head.
+static inline int fused_rt(const Dims& d) { return (d.group * d.queries + 15) / 16; }
 
 template <int RT, int GP, bool POOL = false>
 __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void score_attn_kernel(ScoreArgs sa, AttnArgs aa,
@@ -64,22 +66,32 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void score_a
 // a kernel boundary.  The splits write plain records and the merge is a second,
 // small launch (the kernel boundary makes the records visible).  Every selection
 // workgroup comes after the scoring workgroups it waits for in the grid, and every
-// wait is bounded.  Up to 32 query rows, 4 query heads, K = 256 and 2048 blocks per
-// KV head (the selection in 256 threads).
+// wait is bounded.  Up to K = 256 and 2048 blocks per KV head (the selection in 256
+// threads) and as many query rows as launch 1 fuses.  The selection's LDS, plan
+// bitmaps included, shares the union with the other roles', so the grid keeps the
+// occupancy of the scoring and attention roles.  With `by_xcd` (many query rows per KV
+// head) a head's scoring workgroups share an XCD, whose L2 then fetches its queries once.
 constexpr int kStepAttnBeforeSelect = 512;  // measured at Qwen3-8B 32K: 256-768 alike, 1024 late
 template <int RT, int GP, int ITEMS, bool POOL>
 __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void step_kernel(
-    ScoreArgs sa, TopkPlanArgs ta, AttnArgs aa, Handoff ho, int n_score, int score_gx, int attn_gx) {
+    ScoreArgs sa, TopkPlanArgs ta, AttnArgs aa, Handoff ho, int n_score, int score_gx, int attn_gx,
+    int by_xcd) {
   __shared__ union {
     ScoreShared<RT> s;
     AttnShared<GP> a;
-    TopkPlanShared<kScoreThreads, ITEMS> t;
+    struct {
+      TopkPlanShared<kScoreThreads, ITEMS> t;
+      PlanBitmaps bm;
+    } sel;
   } sh;
-  __shared__ PlanBitmaps bm;
   const int heads = n_score / score_gx;
   int b = blockIdx.x;
   if (b < n_score) {
-    score_wg<RT, true, kStepScoreTiles>(b % score_gx, b / score_gx, sh.s, sa, &ho);
+    // (The placement is resolved at run time only where it can apply: at 20 query rows
+    // the extra index arithmetic measured 0.2 us per step.)
+    int x = b % score_gx, head = b / score_gx;
+    if (RT >= 4) xcd_item(b, score_gx, heads, by_xcd, x, head);
+    score_wg<RT, true, step_score_tiles(RT)>(x, head, sh.s, sa, &ho);
     return;
   }
   b -= n_score;
@@ -88,7 +100,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, OASIS_ATTN_MIN_WAVES) void step_ke
   // done rather than holding slots while the scoring still streams.
   const int k_pre = min(kStepAttnBeforeSelect, attn_gx * heads) & ~7;
   if (b >= k_pre && b < k_pre + heads) {
-    topk_plan_wg<kScoreThreads, ITEMS, true>(b - k_pre, sh.t, bm, ta, &ho);
+    topk_plan_wg<kScoreThreads, ITEMS, true>(b - k_pre, sh.sel.t, sh.sel.bm, ta, &ho);
     return;
   }
   if (b >= k_pre) b -= heads;
@@ -161,7 +173,7 @@ static hipError_t launch_second_half(const Dims& d, const AttnSplit& s, const To
 // The shared launch also needs up to 4 query heads per KV head: the selection's LDS
 // on top of larger attention partials would leave fewer than four workgroups per CU.
 static bool pipelined_fits(const Dims& d) {
-  const int rt = (d.group * d.queries + 15) / 16;
+  const int rt = fused_rt(d);
   return rt <= 2 && d.group <= 4 && d.top_k <= kScoreThreads && d.max_blocks <= 8 * kScoreThreads;
 }
 
@@ -196,7 +208,7 @@ hipError_t launch_pipelined_layer(const Dims& d, const LayerIO* cur, const Layer
   const int score_gx = score_grid_x(d);
   const int n_score = score_gx * heads;
   const int attn_gx = s.num_splits;
-  const int rt = (d.group * d.queries + 15) / 16;
+  const int rt = fused_rt(d);
   hipError_t err;
   if (pipelined_fits(d)) {
     const int n_sel = prev != nullptr ? heads : 0;
@@ -249,7 +261,7 @@ static hipError_t launch_first_half(const Dims& d, const AttnSplit& s, const voi
   const int n_score = score_gx * heads;
   const int attn_gx = s.num_splits;
   const int grid1 = n_score + attn_gx * heads;
-  const int rt = (d.group * d.queries + 15) / 16;
+  const int rt = fused_rt(d);
   const int gp = d.group <= 4 ? 4 : (d.group <= 8 ? 8 : 16);
   const int xcd = place_by_xcd(d.group * d.queries);
   // Up to OASIS_FUSED_MAX_RT row tiles the scoring work shares the grid with the
@@ -329,7 +341,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static HandoffLayout handoff_layout(const Dims& d) {
   const size_t heads = (size_t)d.batch * d.heads;
   const size_t recs = attn_workspace_bytes(d, d.table_stride);
-  const size_t score_waves = (size_t)score_grid_x(d, kStepScoreTiles) * kScoreWaves;
+  const size_t score_waves = (size_t)score_grid_x(d, step_score_tiles(fused_rt(d))) * kScoreWaves;
   HandoffLayout L;
   L.flag_score = recs;
   L.status = L.flag_score + heads * score_waves * sizeof(uint32_t);
@@ -359,12 +371,14 @@ hipError_t launch_clear_handoff(const Dims& d, void* ws, hipStream_t stream) {
 // launch, so past a few hundred heads the selection is better off in launch 2.
 // Measured per step at 20 query rows (Qwen3-8B layer shape): 64 heads 31.5 against
 // 35.9 us, 128 heads 55.5 against 58.7, 256 heads 104.1 against 103.5, and 512 heads
-// of 1024 blocks (36-layer shape) 152.9 against 143.7.
+// of 1024 blocks (36-layer shape) 152.9 against 143.7; at 80 query rows (Qwen3-235B,
+// 128 heads) 63.0 against 64.4.
 constexpr int kHandoffMaxHeads = 256;
 bool handoff_step_fits(const Dims& d) {
-  const int rt = (d.group * d.queries + 15) / 16;
-  return rt <= 2 && d.group <= 4 && d.top_k <= kScoreThreads && d.max_blocks <= 8 * kScoreThreads &&
-         d.batch * d.heads <= kHandoffMaxHeads && score_grid_x(d, kStepScoreTiles) * kScoreWaves <= 256 &&
+  const int rt = fused_rt(d);
+  return rt <= OASIS_FUSED_MAX_RT && d.top_k <= kScoreThreads && d.max_blocks <= 8 * kScoreThreads &&
+         d.batch * d.heads <= kHandoffMaxHeads &&
+         score_grid_x(d, step_score_tiles(rt)) * kScoreWaves <= 256 &&
          attn_split(d, d.table_stride).num_splits <= 256;
 }
 
@@ -381,7 +395,8 @@ static hipError_t launch_one_step(const Dims& d, const AttnSplit& s, const void*
   ho.status = reinterpret_cast<uint32_t*>(base + L.status);
   ho.mbox = reinterpret_cast<uint32_t*>(base + L.mbox);
   ho.scores = scores;
-  const int score_gx = score_grid_x(d, kStepScoreTiles);
+  const int rt = fused_rt(d);
+  const int score_gx = score_grid_x(d, step_score_tiles(rt));
   ho.score_waves = score_gx * kScoreWaves;
   const ScoreArgs sa = score_args(d, q, summ, seq_lens, scores);
   AttnArgs aa = attn_args(d, s, q, pool ? pool->pool_k : k, pool ? pool->pool_v : v, resident, nullptr,
@@ -393,21 +408,42 @@ static hipError_t launch_one_step(const Dims& d, const AttnSplit& s, const void*
   const int n_score = score_gx * heads;
   const int attn_gx = s.num_splits;
   const int grid = n_score + heads + attn_gx * heads;
-  const int rt = (d.group * d.queries + 15) / 16;
-  const int items = select_items(d, kScoreThreads);
-  switch ((rt * 100 + items) * 2 + (pool ? 1 : 0)) {
-#define OASIS_STEP_CASE(RT, I, P)                                                               \
-  case (RT * 100 + I) * 2 + P:                                                                  \
-    step_kernel<RT, 4, I, P><<<dim3(grid), dim3(64 * kAttnWaves), 0, stream>>>(                \
-        sa, ta, aa, ho, n_score, score_gx, attn_gx);                                            \
+  const int gp = d.group <= 4 ? 4 : (d.group <= 8 ? 8 : 16);
+  const int xcd = place_by_xcd(d.group * d.queries);
+  // Up to two row tiles and four query heads every selection width has its instance;
+  // the other shapes take 8 scores per thread (any count up to 2048 blocks).
+  const int items = (rt <= 2 && gp == 4) ? select_items(d, kScoreThreads) : 8;
+  switch (((rt * 100 + gp) * 10 + items) * 2 + (pool ? 1 : 0)) {
+#define OASIS_STEP_CASE(RT, GP, I, P)                                                           \
+  case ((RT * 100 + GP) * 10 + I) * 2 + P:                                                      \
+    step_kernel<RT, GP, I, P><<<dim3(grid), dim3(64 * kAttnWaves), 0, stream>>>(               \
+        sa, ta, aa, ho, n_score, score_gx, attn_gx, xcd);                                       \
     break;
-#define OASIS_STEP_ROW(RT)                                                                      \
-  OASIS_STEP_CASE(RT, 1, 0) OASIS_STEP_CASE(RT, 2, 0) OASIS_STEP_CASE(RT, 4, 0)                 \
-  OASIS_STEP_CASE(RT, 8, 0) OASIS_STEP_CASE(RT, 1, 1) OASIS_STEP_CASE(RT, 2, 1)                 \
-  OASIS_STEP_CASE(RT, 4, 1) OASIS_STEP_CASE(RT, 8, 1)
-    OASIS_STEP_ROW(1)
-    OASIS_STEP_ROW(2)
-#undef OASIS_STEP_ROW
+#define OASIS_STEP_G4(RT)                                                                       \
+  OASIS_STEP_CASE(RT, 4, 1, 0) OASIS_STEP_CASE(RT, 4, 2, 0) OASIS_STEP_CASE(RT, 4, 4, 0)        \
+  OASIS_STEP_CASE(RT, 4, 8, 0) OASIS_STEP_CASE(RT, 4, 1, 1) OASIS_STEP_CASE(RT, 4, 2, 1)        \
+  OASIS_STEP_CASE(RT, 4, 4, 1) OASIS_STEP_CASE(RT, 4, 8, 1)
+#define OASIS_STEP_G4_8(RT) OASIS_STEP_CASE(RT, 4, 8, 0) OASIS_STEP_CASE(RT, 4, 8, 1)
+#define OASIS_STEP_G8_16(RT)                                                                    \
+  OASIS_STEP_CASE(RT, 8, 8, 0) OASIS_STEP_CASE(RT, 8, 8, 1) OASIS_STEP_CASE(RT, 16, 8, 0)       \
+  OASIS_STEP_CASE(RT, 16, 8, 1)
+    OASIS_STEP_G4(1)
+    OASIS_STEP_G8_16(1)
+    OASIS_STEP_G4(2)
+    OASIS_STEP_G8_16(2)
+#if OASIS_FUSED_MAX_RT >= 6
+    OASIS_STEP_G4_8(3)
+    OASIS_STEP_G8_16(3)
+    OASIS_STEP_G4_8(4)
+    OASIS_STEP_G8_16(4)
+    OASIS_STEP_G4_8(5)
+    OASIS_STEP_G8_16(5)
+    OASIS_STEP_G4_8(6)
+    OASIS_STEP_G8_16(6)
+#endif
+#undef OASIS_STEP_G8_16
+#undef OASIS_STEP_G4_8
+#undef OASIS_STEP_G4
 #undef OASIS_STEP_CASE
     default:
       return hipErrorInvalidValue;

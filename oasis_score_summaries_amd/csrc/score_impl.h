@@ -14,9 +14,11 @@ namespace oasis {
 constexpr int kScoreWaves = kWavesPerWG;                         // waves per workgroup
 constexpr int kScoreThreads = 64 * kScoreWaves;
 constexpr int kScoreTilesPerWave = OASIS_SCORE_TILES_PER_WAVE;   // 16-block MFMA tiles per wave
-// The overlapped step's first launch scores one tile per wave: twice the workgroups of
-// half the size, which retire sooner and let its attention workgroups in earlier.
-constexpr int kStepScoreTiles = 1;
+// Tiles per wave of the scoring in the overlapped step's first launch, by row tiles:
+// one up to two row tiles (twice the workgroups of half the size, which retire sooner
+// and let the attention workgroups in earlier), two from three on (a workgroup's query
+// fragments, built once in LDS, then serve twice the summaries).
+__host__ __device__ constexpr int step_score_tiles(int rt) { return rt <= 2 ? 1 : 2; }
 __host__ __device__ constexpr int score_blocks_per_wg(int tiles) { return kScoreWaves * tiles * 16; }
 
 // The query fragments do not depend on the block, so the workgroup builds them once

@@ -144,7 +144,11 @@ def test_workspace_and_table_stride_checks(lib):
     # word, a score mailbox of B*H*NB words)
     assert step_need >= need + 2 * 2 * 64 * 4
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(d)) == 1
-    assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=8))) == 0
+    # every row count launch 1 fuses (up to 96 query rows per KV head), none beyond
+    assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=8))) == 1
+    assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=16, num_queries=6))) == 1
+    assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=16, num_queries=7))) == 0
+    assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(max_blocks=4096, top_k=16))) == 0
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(batch=32, num_kv_heads=8))) == 1
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(batch=64, num_kv_heads=8))) == 0
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=0))) == -1

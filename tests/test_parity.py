@@ -646,7 +646,12 @@ def _step_outputs(bufs, rn):
     {"group": 8, "num_drafts": 1},                     # 8 query heads per KV head
     {"top_k": 300, "ctx": 8192 + 40},                  # K above 256 (1024-thread selection)
     {"ctx": 2048 * 16 + 40, "min_len": 30000, "top_k": 64},   # 2051 blocks
-    {"group": 8, "num_drafts": 4},                     # 40 query rows: scoring in its own kernel
+    {"group": 8, "num_drafts": 4},                     # 40 query rows, 8 query heads
+    {"group": 16, "num_drafts": 1},                    # 32 query rows, 16 query heads
+    {"group": 4, "num_drafts": 11},                    # 48 query rows, 4 query heads
+    {"group": 16, "num_drafts": 4},                    # 80 query rows (Qwen3-235B's 16 x 5)
+    {"group": 16, "num_drafts": 5},                    # 96 query rows: the fused launch's widest
+    {"group": 16, "num_drafts": 6},                    # 112 query rows: scoring in its own kernel
 ])
 def test_overlapped_step_matches_its_parts(lib, shape):
     """The overlapped step is the serial step's background half plus the attention
@@ -851,7 +856,7 @@ def test_append_then_step_loop_both_step_orders_agree(lib):
     assert any(ref.first_window_block(int(Ld[b]), W) > w0_start[b] for b in range(B))
 
 
-@pytest.mark.parametrize("shape", ["tiny", "qwen3_8b_2x2", "short"])
+@pytest.mark.parametrize("shape", ["tiny", "qwen3_8b_2x2", "short", "g16x5"])
 def test_overlapped_step_leaves_the_handoff_region_zero(lib, shape):
     """The overlapped step at sizes whose selection runs in launch 1: after every
     step the hand-off region of the workspace (flags, status word, score mailbox) is
@@ -862,6 +867,8 @@ def test_overlapped_step_leaves_the_handoff_region_zero(lib, shape):
         w = synth.WORKLOADS["tiny_4k"].with_(batch=2, fetch_ratio=0.25)
     elif shape == "qwen3_8b_2x2":
         w = synth.WORKLOADS["qwen3_8b_32k"].with_(batch=2, num_kv_heads=2)
+    elif shape == "g16x5":       # 16 query heads x 5 queries: 80 rows, scoring placed by XCD
+        w = synth.WORKLOADS["qwen3_235b_32k"].with_(batch=2, num_kv_heads=4, ctx=8192 + 40)
     else:
         w = synth.WORKLOADS["tiny_4k"].with_(batch=3, ctx=1024, min_len=60, fetch_ratio=1.0)
     _say(f"hand-off region, {shape}")
