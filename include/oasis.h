@@ -498,7 +498,9 @@ typedef struct {
  * selection outputs are valid after the next call returns its launches to the
  * stream order (within the one-launch limits, as soon as this call's own
  * launches are done; `previous` then has nothing left to run and the final call
- * with layer = NULL queues nothing). */
+ * with layer = NULL queues nothing).  Calls ordered on one stream may all pass
+ * the same workspace: a call reads back its split records within its own
+ * launches and leaves the hand-off region zero. */
 oasis_status oasis_decode_layer_pipelined(const oasis_dims* dims, const oasis_layer_io* layer,
                                           const oasis_layer_io* previous, float scale,
                                           hipStream_t stream);

@@ -871,8 +871,10 @@ class LayerIO(ctypes.Structure):
 class PipelinedLayers:
     """A sweep over two or more layers with each layer's selection and plan riding in
     the next layer's first launch (oasis_decode_layer_pipelined).  ``layers`` holds,
-    per layer, (q, summ, k, v, seq_lens, resident); every layer gets its own step
-    buffers and next slot table.  Calling the object queues one decode step over all
+    per layer, (q, summ, k, v, seq_lens, resident); every layer gets its own outputs
+    and next slot table, and all layers share one workspace (their launches run in
+    stream order; one workspace also stays warm in the caches from layer to layer:
+    0.8 us per layer at the Qwen3-8B shape).  Calling the object queues one decode step over all
     layers (the previous step's last layer is selected in the first layer's launch);
     ``drain()`` queues the last layer's pending selection.  The tensors must stay
     alive while the object is used."""
@@ -885,6 +887,7 @@ class PipelinedLayers:
         self.scale = 1.0 / math.sqrt(128) if scale is None else float(scale)
         self.lib = load()
         self.buffers, self.resident_next, self.ios, self.keep = [], [], [], []
+        self.ws = None
         for (q, summ, k, v, seq_lens, resident) in layers:
             _need(q, "q", torch.bfloat16, s["q"], align=16)
             dev = q.device
@@ -894,6 +897,10 @@ class PipelinedLayers:
             _need(seq_lens, "seq_lens", torch.int32, s["lens"], dev)
             _need(resident, "resident", torch.int32, s["resident"], dev)
             b = StepBuffers(dims, dev)
+            if self.ws is None:
+                self.ws = b.ws
+            else:
+                b.ws = self.ws
             rn = torch.empty_like(resident)
             io = LayerIO(q.data_ptr(), summ.data_ptr(), k.data_ptr(), v.data_ptr(), seq_lens.data_ptr(),
                          resident.data_ptr(), rn.data_ptr(), b.scores.data_ptr(), b.topk.data_ptr(),
