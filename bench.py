@@ -344,13 +344,16 @@ def cpu_baseline(w, sets, budget_s: float, overlapped: bool) -> dict:
     return out
 
 
-def layer_pipelined(d, sets, ms_step: float, torch, oa, reps: int = 100, step_bytes: int = 0) -> dict:
+def layer_pipelined(d, sets, ms_step: float, torch, oa, reps: int = 100, step_bytes: int = 0,
+                    sweeps: int = 1) -> dict:
     """The input sets as the layers of a decode step, each layer's selection and plan
     riding in the next layer's first launch (oasis_decode_layer_pipelined): the
     steady-state time per layer of a whole sweep (graph replay; the first layer of a
-    replay selects the previous replay's last layer).  Every layer still does its
-    whole step; only where its selection runs changes.  With ``step_bytes`` (one
-    layer's algorithmic bytes) also the per-layer rate against the HBM peak."""
+    replay selects the previous replay's last layer; a graph holds ``sweeps`` sweeps, and
+    about ``reps`` sweeps are timed, in whole graphs).  Every layer still does its whole
+    step; only where its selection runs changes.  With ``step_bytes`` (one layer's
+    algorithmic bytes) also the per-layer rate against the HBM peak."""
+    replays = max(1, reps // sweeps)
     sweep = oa.PipelinedLayers(d, [(s["q"], s["summ"], s["k"], s["v"], s["seq_lens"], s["resident"])
                                    for s in sets])
     for _ in range(3):
@@ -363,19 +366,20 @@ def layer_pipelined(d, sets, ms_step: float, torch, oa, reps: int = 100, step_by
     torch.cuda.current_stream().wait_stream(side)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        sweep()
+        for _ in range(sweeps):
+            sweep()
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(reps):
+    for _ in range(replays):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+    us = e0.elapsed_time(e1) * 1e3 / (replays * len(sets) * sweeps)
     sweep.drain()
     torch.cuda.synchronize()
-    out = {"us_per_layer": round(us, 3), "layers": len(sets), "layers_per_s": round(1e6 / us, 1),
+    out = {"us_per_layer": round(us, 3), "layers": len(sets), "sweeps_per_graph": sweeps, "layers_per_s": round(1e6 / us, 1),
            "overlapped_step_us": round(ms_step * 1e3, 3)}
     if step_bytes:
         gbps = step_bytes / (us * 1e-6) / 1e9
@@ -882,6 +886,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="qwen3_8b_32k")
     ap.add_argument("--sets", type=int, default=6, help="independent input sets rotated per step")
+    ap.add_argument("--graph-steps", type=int, default=36,
+                    help="steps per captured graph, in whole rotations through the input sets (at least "
+                         "one): 36, the layers of one decode token of Qwen3-8B")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--stage-steps", type=int, default=300, help="evented steps for per-kernel times")
@@ -906,7 +913,7 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="print one JSON line with the K and fetch-ratio sweep instead of the benchmark")
     ap.add_argument("--pipeline-reps", type=int, default=100,
-                    help="graph replays of the layer-pipelined sweep (each runs every input set)")
+                    help="layer-pipelined sweeps timed (each runs every input set), in whole graphs")
     ap.add_argument("--no-plan-exec", action="store_true",
                     help="skip the working-set measurements (step over the pool, plan copies, host tier)")
     args = ap.parse_args(argv)
@@ -952,6 +959,7 @@ def main(argv=None) -> int:
     w = synth.WORKLOADS[args.workload]
     d = oa.dims_for(w)
     n_sets = w.layers if w.layers > 1 else args.sets
+    graph_rotations = max(1, args.graph_steps // n_sets)
     if args.calibrate:
         src = torch.ones(CALIBRATION_BYTES // 2, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
@@ -993,28 +1001,30 @@ def main(argv=None) -> int:
             step_list[i % n_sets]()
         torch.cuda.synchronize()
         graph = rest = None
-        reps, n_rest = divmod(args.steps, n_sets)
+        n_graph = n_sets * graph_rotations
+        reps, n_rest = divmod(args.steps, n_graph)
 
         def capture(n):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for st in step_list[:n]:
-                    st()
+                for i in range(n):
+                    step_list[i % n_sets]()
             return g
 
         if args.mode == "graph":
-            # One graph holds one step per input set; replaying it walks the rotation.
-            # A second graph holds the first n_rest steps, so that exactly args.steps
-            # steps are timed whatever their number.
+            # One graph holds graph_rotations rotations through the input sets (one step
+            # per set each); replaying it walks the rotation.  A second graph holds the
+            # first n_rest steps, so that exactly args.steps steps are timed whatever
+            # their number.
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(side):
                 step_list[0]()
             torch.cuda.current_stream().wait_stream(side)
-            graph = capture(n_sets)
+            graph = capture(n_graph)
             rest = capture(n_rest) if n_rest else None
             torch.cuda.synchronize()
-            for _ in range(max(1, args.warmup // n_sets)):
+            for _ in range(max(1, args.warmup // n_graph)):
                 graph.replay()
             if rest is not None:
                 rest.replay()
@@ -1036,8 +1046,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         ms = ev0.elapsed_time(ev1) / n
         wall = time.perf_counter() - t0
-        # Spread: 300 more replays (one rotation through the input sets each) or eager
-        # steps, whatever args.steps is, with an event after each; per-step ms of each.
+        # Spread: 300 more replays (graph_rotations rotations through the input sets
+        # each) or eager steps, whatever args.steps is, with an event after each; per-step
+        # ms of each.
         n_samples = 300
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_samples + 1)]
         evs[0].record()
@@ -1048,7 +1059,7 @@ def main(argv=None) -> int:
                 step_list[i % n_sets]()
             evs[i + 1].record()
         torch.cuda.synchronize()
-        per = n_sets if graph is not None else 1
+        per = n_graph if graph is not None else 1
         spread = [evs[i].elapsed_time(evs[i + 1]) / per for i in range(n_samples)]
         return ms, n, wall, graph, spread
 
@@ -1146,7 +1157,8 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "batch": w.batch, "kv_heads": w.num_kv_heads, "group": w.group,
                    "context": w.ctx, "queries_per_head": w.queries, "top_k": w.top_k,
                    "window_tokens": w.window, "fetch_ratio": w.fetch_ratio, "cap": w.cap,
-                   "input_sets": n_sets, "mode": args.mode, "order": args.order},
+                   "input_sets": n_sets, "mode": args.mode, "order": args.order,
+                   "graph_steps": n_sets * graph_rotations if args.mode == "graph" else None},
         # The whole timed step against HBM: the method's bytes (candidate summaries,
         # the K/V blocks of every table entry, queries, outputs) over the step time.
         "roofline": {"bound": "hbm", "scope": "whole step",
@@ -1160,7 +1172,7 @@ def main(argv=None) -> int:
         "dominant_kernel": dict(per_launch[dominant], stage=dominant),
         "launches": per_launch,
         "step_ms": {k: round(v, 6) if isinstance(v, float) else v for k, v in percentiles(spread).items()},
-        "step_ms_sample": ("per graph replay (one step of each input set), divided by the sets"
+        "step_ms_sample": (f"per graph replay ({graph_rotations} rotation(s) through the input sets), divided by its steps"
                            if graph_mode else "per eager step"),
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
         "stage_timing": stage_method,
@@ -1171,7 +1183,7 @@ def main(argv=None) -> int:
     }
     print("bench: layer-pipelined sweep", file=sys.stderr, flush=True)
     result["layer_pipelined"] = layer_pipelined(d, sets, ms_per_step, torch, oa, reps=max(1, args.pipeline_reps),
-                                                step_bytes=nb["step"])
+                                                step_bytes=nb["step"], sweeps=graph_rotations)
     if not args.no_plan_exec:
         print("bench: plan execution", file=sys.stderr, flush=True)
         result["plan_execution"] = plan_execution(w, d, sets, buffers, res_next, ms_per_step, stage_us,

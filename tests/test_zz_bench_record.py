@@ -30,7 +30,8 @@ def test_bench_record_fields(capsys):
                 "roofline", "cpu_baseline", "layer_pipelined"):
         assert key in r, key
     assert r["n_gpus"] == 1 and r["unit"] == "steps/s" and r["higher_is_better"] is True
-    assert r["config"]["workload"] == "tiny_4k"
+    assert r["config"]["workload"] == "tiny_4k" and r["config"]["graph_steps"] == 36
+    assert r["steps"] == 12 and r["step_ms"]["n"] == 300
     assert r["value"] > 0 and r["ms_per_step"] > 0
     assert abs(r["value"] - 1.0 / r["ms_per_step"] * 1e3) <= 0.01 * r["value"] + 0.01
     roof = r["roofline"]
