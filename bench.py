@@ -935,6 +935,9 @@ def main(argv=None) -> int:
         print(text, end="")
         return 0
 
+    if args.steps < 1 or args.warmup < 0 or args.graph_steps < 1:
+        print("bench.py needs --steps >= 1, --warmup >= 0 and --graph-steps >= 1", file=sys.stderr)
+        return 2
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the decode step of one layer is measured on a single "
               "MI355X and no multi-GPU path is built", file=sys.stderr)

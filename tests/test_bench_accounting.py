@@ -166,6 +166,14 @@ def test_summarize_occupancy_means_per_kernel(tmp_path):
     assert r2[1] == "3.0" and r2[3] == "0.0"
 
 
+def test_empty_timed_region_is_refused(capsys):
+    """No timed step (or a negative warm-up, or an empty graph) ends with a message and
+    status 2 before any device work."""
+    for argv in (["--steps", "0"], ["--warmup", "-1"], ["--graph-steps", "0"]):
+        assert bench.main(argv) == 2
+        assert "--steps >= 1" in capsys.readouterr().err
+
+
 def test_more_than_one_gpu_is_refused(capsys, monkeypatch):
     """--gpus above 1 (or a multi-rank launch) ends with a message and status 2 before any
     device work: no multi-GPU path is built."""
