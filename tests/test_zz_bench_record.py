@@ -19,7 +19,8 @@ def _need_gpu():
 def test_bench_record_fields(capsys):
     import bench
 
-    rc = bench.main(["--workload", "tiny_4k", "--steps", "12", "--warmup", "2", "--stage-steps", "4",
+    # 40 steps: one replay of the 36-step graph and a remainder graph of 4
+    rc = bench.main(["--workload", "tiny_4k", "--steps", "40", "--warmup", "2", "--stage-steps", "4",
                      "--cpu-budget", "0.3", "--no-plan-exec", "--pipeline-reps", "2"])
     assert rc == 0
     lines = [ln for ln in capsys.readouterr().out.splitlines() if ln.strip()]
@@ -31,7 +32,7 @@ def test_bench_record_fields(capsys):
         assert key in r, key
     assert r["n_gpus"] == 1 and r["unit"] == "steps/s" and r["higher_is_better"] is True
     assert r["config"]["workload"] == "tiny_4k" and r["config"]["graph_steps"] == 36
-    assert r["steps"] == 12 and r["step_ms"]["n"] == 300
+    assert r["steps"] == 40 and r["step_ms"]["n"] == 300
     assert r["value"] > 0 and r["ms_per_step"] > 0
     assert abs(r["value"] - 1.0 / r["ms_per_step"] * 1e3) <= 0.01 * r["value"] + 0.01
     roof = r["roofline"]
