@@ -315,3 +315,33 @@ def test_step_over_the_working_set_at_the_qwen3_8b_shape(lib, tier):
     assert torch.equal(wset.pool_k, expect.pool_k) and torch.equal(wset.pool_v, expect.pool_v)
     del inp, summ, wset, expect
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("shape", [{"group": 16, "num_drafts": 4},   # 80 query rows, 16 query heads
+                                   {"group": 8, "num_drafts": 1}])   # 16 query rows, 8 query heads
+def test_step_over_the_working_set_at_wider_groups(lib, shape):
+    """Wider GQA groups, whose overlapped step also selects inside its first launch: the
+    step over the working set (device tier) gives the full-cache step's outputs bit for
+    bit, and its copies leave the pool equal to the gather of the next slot table."""
+    w = synth.WORKLOADS["qwen3_235b_32k"].with_(batch=2, num_kv_heads=4, ctx=8192 + 40, **shape)
+    _say(f"step over the working set, {shape}")
+    inp = {kk: t.to(DEV) for kk, t in synth.generate(w, "cpu").items()}
+    d = lib.dims_for(w)
+    assert lib.overlapped_selects_in_launch1(d)
+    summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
+    sel = lib.topk_blocks(d, lib.score_summaries(d, inp["q"], summ, inp["seq_lens"]), inp["seq_lens"])
+    R = synth.resident_from_selection(w, sel, inp["seq_lens"].cpu()).to(DEV)
+    wset = lib.fill_working_set(d, R, inp["seq_lens"], inp["k"], inp["v"])
+    rn_pool, rn_full = torch.empty_like(R), torch.empty_like(R)
+    pool_out = {key: t.clone() for key, t in
+                lib.decode_step_pool(d, inp["q"], summ, inp["k"], inp["v"], wset, inp["seq_lens"], R,
+                                     rn_pool).items()}
+    full_out = lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], R, rn_full)
+    torch.cuda.synchronize()
+    for key in ("scores", "topk", "plan", "plan_count", "table", "table_count", "out", "lse"):
+        assert torch.equal(pool_out[key], full_out[key]), key
+    assert torch.equal(rn_pool, rn_full)
+    assert int(full_out["plan_count"].sum()) > 0
+    expect = lib.fill_working_set(d, rn_full, inp["seq_lens"], inp["k"], inp["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(wset.pool_k, expect.pool_k) and torch.equal(wset.pool_v, expect.pool_v)
