@@ -962,13 +962,19 @@ def test_graph_replay_matches_eager(lib, overlapped):
             assert torch.equal(eager[key], got[key]), f"replay {rep}: {key}"
 
 
-@pytest.mark.parametrize("group,queries,ctx", [(4, 5, 4096 + 40), (8, 2, 4096 + 40), (4, 5, 2048 * 16 + 40)])
-def test_layer_pipelined_sweep_matches_the_overlapped_step(lib, group, queries, ctx):
-    """Three layers, two decode steps with each layer's selection in the next layer's
-    first launch (group 8, or more than 2048 blocks: in its second launch, with the
-    merge): every layer's plan outputs equal the overlapped step's bit for bit, its
-    attention equals it up to the merge's summation order and matches the oracle."""
-    w = synth.WORKLOADS["tiny_4k"].with_(batch=2, num_kv_heads=3, group=group, num_drafts=queries - 1,
+@pytest.mark.parametrize("group,queries,ctx,batch,heads", [
+    (4, 5, 4096 + 40, 2, 3),            # each layer selects in its own first launch
+    (8, 2, 4096 + 40, 2, 3),            # the same at 8 query heads
+    (4, 5, 2048 * 16 + 40, 2, 3),       # 2051 blocks: in the next layer's second launch
+    (4, 5, 4096 + 40, 33, 8),           # 264 pairs: in the next layer's first launch
+])
+def test_layer_pipelined_sweep_matches_the_overlapped_step(lib, group, queries, ctx, batch, heads):
+    """Three layers, two decode steps of the layer-pipelined sweep, whose selections run
+    in the layer's own first launch, the next layer's first launch, or the next layer's
+    second launch with its merge, by size: every layer's plan outputs equal the
+    overlapped step's bit for bit, its attention equals it up to the merge's summation
+    order and matches the oracle."""
+    w = synth.WORKLOADS["tiny_4k"].with_(batch=batch, num_kv_heads=heads, group=group, num_drafts=queries - 1,
                                          fetch_ratio=0.25, ctx=ctx, min_len=1000)
     _say(f"layer-pipelined sweep group={group} ctx={ctx}")
     d = lib.dims_for(w)
