@@ -1045,10 +1045,10 @@ def test_pipelined_sweep_graph_replay_matches_eager(lib):
 
 
 def test_layer_pipelined_sweep_at_the_qwen3_8b_shape(lib):
-    """Three layers of the Qwen3-8B 32K shape (four sequences, all eight KV heads: the
-    selection shares the next layer's first launch at K = 128 and 2048 blocks), two
-    sweeps: every layer's plan outputs and next slot table equal its overlapped step's
-    bit for bit and its attention equals it up to the merge's summation order."""
+    """Three layers of the Qwen3-8B 32K shape (four sequences, all eight KV heads: each
+    layer selects in its own first launch at K = 128 and 2048 blocks), two sweeps:
+    every layer's plan outputs and next slot table equal its overlapped step's bit for
+    bit and its attention equals it up to the merge's summation order."""
     w = synth.WORKLOADS["qwen3_8b_32k"].with_(batch=4)
     _say("layer-pipelined sweep at the Qwen3-8B shape")
     d = lib.dims_for(w)
