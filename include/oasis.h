@@ -106,12 +106,19 @@ int32_t oasis_table_stride(const oasis_dims* dims);
  * invalid. */
 int32_t oasis_overlapped_selects_in_launch1(const oasis_dims* dims);
 
+/* 1 if oasis_decode_step, called with its own resident_next buffer, runs for these
+ * dims as the first launch of oasis_decode_step_overlapped, a launch that redoes
+ * the attention splits holding a slot the plan changed over the updated slot
+ * table, and the merge (see oasis_decode_step); 0 if it runs as four kernels.
+ * -1 if dims is invalid. */
+int32_t oasis_decode_step_redoes_touched_splits(const oasis_dims* dims);
+
 /* Device workspace of the decode steps (oasis_decode_step, _overlapped, _pool,
  * oasis_decode_layer_pipelined), in bytes, a multiple of 256; it also serves
  * oasis_sparse_decode_attn with table_stride == oasis_table_stride(dims).  It
  * holds the per-split attention partials and, after them, the hand-off region
- * through which the scoring workgroups of oasis_decode_step_overlapped's first
- * launch pass the scores to the selection workgroups of the same launch.
+ * through which the scoring workgroups of the overlapped step's first launch
+ * pass the scores to the selection workgroups of the same launch.
  * The hand-off region must be zero before the workspace first serves a step:
  * allocate it zero-filled or call oasis_workspace_clear once.  Every step leaves
  * it zero again, so the workspace can serve any number of steps and layers of
@@ -268,7 +275,18 @@ oasis_status oasis_sparse_decode_attn_resident(const oasis_dims* dims, const voi
  *                  updated in place.  Otherwise `resident` is only read and the
  *                  updated slot table is written here (a double-buffered slot
  *                  table: step t reads one buffer and writes the other); the
- *                  two buffers must not overlap. */
+ *                  two buffers must not overlap.
+ * The attention is the same set as oasis_sparse_decode_attn_resident over the
+ * updated slot table.  With resident_next given and
+ * oasis_decode_step_redoes_touched_splits(dims) == 1, the step runs as three
+ * launches: the first launch of oasis_decode_step_overlapped (its attention
+ * splits over `resident`, its selection and plan writing resident_next), one
+ * that redoes, over resident_next, only the splits holding a slot that a plan
+ * row changed (the other splits read the same blocks either way), and the
+ * merge of each head's partials.  That form uses the hand-off region of the
+ * workspace (zero before the first step, left zero; see
+ * oasis_workspace_bytes); the results differ from the four-kernel form's only
+ * in the order of the fp32 additions. */
 oasis_status oasis_decode_step(const oasis_dims* dims, const void* q, const void* summ,
                                const void* k, const void* v, const int32_t* seq_lens,
                                float* scores, int32_t* topk, int32_t* resident,

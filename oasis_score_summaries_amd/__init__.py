@@ -15,4 +15,5 @@ from ._lib import (LIB_PATH, LayerIO, OasisDims, OasisError, PipelinedLayers,  #
                    exported_symbols, fetch_cap, load, make_dims, score_summaries,
                    sparse_decode_attn, sparse_decode_attn_resident, step_workspace, table_stride,
                    topk_blocks, workspace_bytes, workspace_clear, workspace_status,
-                   overlapped_selects_in_launch1, decode_step_overlapped_noalloc)
+                   overlapped_selects_in_launch1, decode_step_overlapped_noalloc,
+                   decode_step_redoes_touched_splits)

@@ -59,6 +59,7 @@ _SIGNATURES = {
     "oasis_workspace_clear": (ctypes.c_int, [_DIMS, _P, ctypes.c_size_t, _P]),
     "oasis_workspace_status_offset": (ctypes.c_size_t, [_DIMS]),
     "oasis_overlapped_selects_in_launch1": (ctypes.c_int32, [_DIMS]),
+    "oasis_decode_step_redoes_touched_splits": (ctypes.c_int32, [_DIMS]),
     "oasis_attn_workspace_bytes": (ctypes.c_size_t, [_DIMS, ctypes.c_int32]),
     "oasis_build_summaries": (ctypes.c_int, [_DIMS, _P, _P, _P, _P]),
     "oasis_score_summaries": (ctypes.c_int, [_DIMS, _P, _P, _P, _P, _P]),
@@ -363,6 +364,16 @@ def overlapped_selects_in_launch1(dims: OasisDims) -> bool:
     r = int(load().oasis_overlapped_selects_in_launch1(ctypes.byref(dims)))
     if r < 0:
         _check(1, "oasis_overlapped_selects_in_launch1")
+    return r == 1
+
+
+def decode_step_redoes_touched_splits(dims: OasisDims) -> bool:
+    """Whether decode_step with its own ``resident_next`` runs as the overlapped
+    step's first launch plus a launch that redoes only the splits the plan touched
+    (oasis_decode_step_redoes_touched_splits)."""
+    r = int(load().oasis_decode_step_redoes_touched_splits(ctypes.byref(dims)))
+    if r < 0:
+        _check(1, "oasis_decode_step_redoes_touched_splits")
     return r == 1
 
 

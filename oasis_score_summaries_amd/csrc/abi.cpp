@@ -123,6 +123,12 @@ int32_t oasis_overlapped_selects_in_launch1(const oasis_dims* dims) {
   return oasis::handoff_step_fits(d) ? 1 : 0;
 }
 
+int32_t oasis_decode_step_redoes_touched_splits(const oasis_dims* dims) {
+  oasis::Dims d;
+  if (check_dims(dims, &d) != OASIS_OK) return -1;
+  return oasis::post_plan_reuse_fits(d) ? 1 : 0;
+}
+
 size_t oasis_workspace_bytes(const oasis_dims* dims) {
   oasis::Dims d;
   if (check_dims(dims, &d) != OASIS_OK) return 0;
@@ -298,7 +304,11 @@ static oasis_status check_step_args(const oasis_dims* dims, oasis::Dims& d, cons
   return OASIS_OK;
 }
 
-// The fused step; with `events` non-NULL, markers are recorded between its kernels.
+// The step in order: scoring, selection and plan, then the attention over the updated
+// slot table.  Untimed, with a separate resident_next and sizes whose selection fits
+// launch 1, it is the overlapped step's launch 1, a launch that redoes only the splits
+// the plan touched, and the merge; otherwise four kernels, and with `events` non-NULL
+// markers are recorded between them.
 static oasis_status decode_step_impl(const oasis_dims* dims, const void* q, const void* summ,
                                      const void* k, const void* v, const int32_t* seq_lens,
                                      float* scores, int32_t* topk, int32_t* resident,
@@ -311,6 +321,11 @@ static oasis_status decode_step_impl(const oasis_dims* dims, const void* q, cons
                                     &resident_next, plan, plan_count, table, table_count, scale,
                                     out, ws, ws_bytes);
   if (st != OASIS_OK) return st;
+  if (events == nullptr && resident_next != resident && oasis::post_plan_reuse_fits(d))
+    return hip_status(oasis::launch_post_plan_step(d, q, summ, k, v, seq_lens, scores, topk, resident,
+                                                   resident_next, plan, plan_count, table, table_count,
+                                                   scale, out, lse, ws, stream),
+                      "decode_step");
   if (events != nullptr) {
     for (int i = 0; i < 5; ++i) OASIS_REQUIRE(events[i]);
   }

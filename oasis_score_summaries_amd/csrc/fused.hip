@@ -451,6 +451,108 @@ static hipError_t launch_one_step(const Dims& d, const AttnSplit& s, const void*
   return hipGetLastError();
 }
 
+// ---- the step with the attention after the plan, from the overlapped step ----------
+// oasis_decode_step attends over the slot table that the plan produces.  Launch 1 of
+// the overlapped step already attends over the slot table as it was, split by split,
+// and the plan changes at most C slots per (sequence, KV head): only the splits that
+// hold a changed slot differ from those over the updated table (the same split
+// geometry, the same blocks elsewhere).  post_plan_redo_kernel redoes those splits
+// over `resident_next`, one workgroup each, writing their records over the old ones;
+// the merge then runs as in the overlapped step.  `per_head` workgroups per head, at
+// least as many as the splits a plan can touch.
+// (Merging in the same launch, with the head's last workgroup found by an arrival
+// counter, needs a device-scope release and acquire around every record: measured at
+// Qwen3-8B 32K, that launch took 24.5 us against 7.4 + 4.9 us for the two.)
+constexpr int kPostPlanMaxSplits = 16;
+template <int GP>
+__global__ __launch_bounds__(64 * kAttnWaves) void post_plan_redo_kernel(AttnArgs aa, const int32_t* __restrict__ plan,
+                                                                         const int32_t* __restrict__ plan_count,
+                                                                         int cap, int per_head) {
+  __shared__ AttnShared<GP> sh;
+  const int bh = (int)blockIdx.x / per_head, i = (int)blockIdx.x % per_head;
+  const int nsplit = aa.nsplit, units_per_split = kAttnWaves * aa.rounds;
+  // The plan's rows (cap <= 64), one per lane, requested together with the count.
+  const int lane = threadIdx.x & 63;
+  int slot = -1;
+  if (lane < cap) slot = plan[((size_t)bh * cap + lane) * 3];
+  const int pc = plan_count[bh];
+  const int rows = pc < 0 ? 0 : (pc > cap ? cap : pc);
+  // The splits holding those slots, as a mask over at most 256 splits (wave-uniform).
+  uint64_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+  for (int r = 0; r < rows; ++r) {
+    const int t = __builtin_amdgcn_readlane(slot, r);
+    if (t < 0 || t >= aa.K) continue;
+    const int lo = ((t << aa.bshift) >> 4) / units_per_split;
+    int hi = ((((t + 1) << aa.bshift) - 1) >> 4) / units_per_split;
+    hi = hi < nsplit - 1 ? hi : nsplit - 1;
+    for (int sp = lo; sp <= hi; ++sp) {
+      const uint64_t bit = 1ull << (sp & 63);
+      const int w = sp >> 6;
+      m0 |= w == 0 ? bit : 0ull;
+      m1 |= w == 1 ? bit : 0ull;
+      m2 |= w == 2 ? bit : 0ull;
+      m3 |= w == 3 ? bit : 0ull;
+    }
+  }
+  const int c0 = __builtin_popcountll(m0), c1 = __builtin_popcountll(m1), c2 = __builtin_popcountll(m2);
+  if (i >= c0 + c1 + c2 + __builtin_popcountll(m3)) return;
+  // Split i of the mask, in ascending order.
+  int k = i, base;
+  uint64_t w;
+  if (k < c0) {
+    w = m0, base = 0;
+  } else if ((k -= c0) < c1) {
+    w = m1, base = 64;
+  } else if ((k -= c1) < c2) {
+    w = m2, base = 128;
+  } else {
+    k -= c2, w = m3, base = 192;
+  }
+  for (; k > 0; --k) w &= w - 1;
+  attn_split_wg<GP, true>(base + __builtin_ctzll(w), bh, sh, aa);
+}
+
+// The most splits that one plan row's slot lies in: one, or a few for blocks of more
+// than 16 tokens (a slot spans 1 << (bshift - 4) units).
+static int post_plan_row_span(const Dims& d, const AttnSplit& s) {
+  const int units_per_split = kAttnWaves * s.rounds;
+  const int units_per_entry = d.bshift >= 4 ? 1 << (d.bshift - 4) : 1;
+  return (units_per_entry + units_per_split - 2) / units_per_split + 1;
+}
+
+bool post_plan_reuse_fits(const Dims& d) {
+  return handoff_step_fits(d) && d.cap * post_plan_row_span(d, attn_split(d, d.table_stride)) <= kPostPlanMaxSplits;
+}
+
+hipError_t launch_post_plan_step(const Dims& d, const void* q, const void* summ, const void* k,
+                                 const void* v, const int32_t* seq_lens, float* scores, int32_t* topk,
+                                 const int32_t* resident, int32_t* resident_next, int32_t* plan,
+                                 int32_t* plan_count, int32_t* table, int32_t* table_count, float scale,
+                                 float* out, float* lse, void* ws, hipStream_t stream) {
+  if (!post_plan_reuse_fits(d) || resident_next == resident) return hipErrorInvalidValue;
+  const AttnSplit s = attn_split(d, d.table_stride);
+  const TopkPlanArgs ta = topk_plan_args(d, scores, seq_lens, topk, resident, resident_next, plan,
+                                         plan_count, table, table_count);
+  hipError_t err = launch_one_step(d, s, q, summ, k, v, seq_lens, scores, resident, ta, scale, out, lse,
+                                   ws, stream, nullptr);
+  if (err != hipSuccess) return err;
+  const AttnArgs aa = attn_args(d, s, q, k, v, resident_next, nullptr, d.table_stride, seq_lens, scale, ws);
+  // Workgroups per head: the splits that the C rows of a plan can touch, at most all.
+  int per = d.cap * post_plan_row_span(d, s);
+  if (per > s.num_splits) per = s.num_splits;
+  const dim3 grid((unsigned)(d.batch * d.heads * per)), block(64 * kAttnWaves);
+  if (per > 0) {  // (cap 0: the plan changes nothing)
+    if (d.group <= 4)
+      post_plan_redo_kernel<4><<<grid, block, 0, stream>>>(aa, plan, plan_count, d.cap, per);
+    else if (d.group <= 8)
+      post_plan_redo_kernel<8><<<grid, block, 0, stream>>>(aa, plan, plan_count, d.cap, per);
+    else
+      post_plan_redo_kernel<16><<<grid, block, 0, stream>>>(aa, plan, plan_count, d.cap, per);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return launch_attention_merge(d, s, out, lse, ws, stream);
+}
+
 hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ, const void* k,
                                   const void* v, const int32_t* seq_lens, float* scores,
                                   int32_t* topk, const int32_t* resident, int32_t* resident_next,

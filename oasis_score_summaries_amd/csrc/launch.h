@@ -36,6 +36,9 @@ size_t handoff_status_offset(const Dims& d);
 // Whether the overlapped step runs its selection and plan inside launch 1 (scores
 // handed over in the launch) for these sizes.
 bool handoff_step_fits(const Dims& d);
+// Whether oasis_decode_step can take its attention from the overlapped step's launch 1
+// (redoing only the splits that the plan touched) for these sizes.
+bool post_plan_reuse_fits(const Dims& d);
 // Zero-fills the hand-off region of a step workspace.
 hipError_t launch_clear_handoff(const Dims& d, void* ws, hipStream_t stream);
 // The library's own step workspace on the current device (a device array, no
@@ -113,6 +116,16 @@ hipError_t launch_overlapped_step(const Dims& d, const void* q, const void* summ
                                   int32_t* table_count, float scale, float* out, float* lse,
                                   void* ws, hipStream_t stream, hipEvent_t after_first = nullptr,
                                   const WorkingSet* pool = nullptr, bool execute_plan = true);
+
+// The step with the attention over the updated slot table (oasis_decode_step) as the
+// overlapped step's launch 1, a launch that redoes the splits holding a changed slot
+// over `resident_next`, and the merge; only where post_plan_reuse_fits(d) and
+// `resident_next` is its own buffer (hipErrorInvalidValue otherwise).
+hipError_t launch_post_plan_step(const Dims& d, const void* q, const void* summ, const void* k,
+                                 const void* v, const int32_t* seq_lens, float* scores, int32_t* topk,
+                                 const int32_t* resident, int32_t* resident_next, int32_t* plan,
+                                 int32_t* plan_count, int32_t* table, int32_t* table_count, float scale,
+                                 float* out, float* lse, void* ws, hipStream_t stream);
 
 // One layer's buffers for the layer-pipelined decode.
 struct LayerIO {

@@ -44,7 +44,7 @@ def _dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 29
+    assert len(names) == 30
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.exported_symbols())
@@ -72,6 +72,7 @@ def test_dims_validation(lib, field, value, status):
     d = _dims(**{field: value})
     assert lib.oasis_fetch_cap(ctypes.byref(d)) == -1
     assert lib.oasis_table_stride(ctypes.byref(d)) == -1
+    assert lib.oasis_decode_step_redoes_touched_splits(ctypes.byref(d)) == -1
     assert lib.oasis_workspace_bytes(ctypes.byref(d)) == 0
     st = lib.oasis_score_summaries(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None)
     assert st == status
@@ -149,6 +150,12 @@ def test_workspace_and_table_stride_checks(lib):
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=16, num_queries=6))) == 1
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=16, num_queries=7))) == 0
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(max_blocks=4096, top_k=16))) == 0
+    # the serial step redoes the touched splits where the selection fits launch 1 and
+    # a plan touches at most 16 splits (cap 6 of K = 128 here), else four kernels
+    assert lib.oasis_decode_step_redoes_touched_splits(ctypes.byref(_dims(max_blocks=2048, top_k=128))) == 1
+    assert lib.oasis_decode_step_redoes_touched_splits(ctypes.byref(_dims(max_blocks=2048, top_k=128,
+                                                                          fetch_ratio=0.25))) == 0
+    assert lib.oasis_decode_step_redoes_touched_splits(ctypes.byref(_dims(group=16, num_queries=7))) == 0
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(batch=32, num_kv_heads=8))) == 1
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(batch=64, num_kv_heads=8))) == 0
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=0))) == -1

@@ -689,6 +689,68 @@ def test_overlapped_step_matches_its_parts(lib, shape):
     np.testing.assert_allclose(f64(o["lse"].cpu()), el, rtol=0, atol=OUT_ATOL)
 
 
+@pytest.mark.parametrize("shape", [
+    {},                                                   # K = 16, cap 4, 6 splits
+    {"group": 8, "num_drafts": 1},                        # 8 query heads per KV head
+    {"group": 16, "num_drafts": 4},                       # 16 query heads, 80 query rows
+    {"fetch_ratio": 0.0},                                 # cap 0: nothing to redo, the merge alone
+    {"fetch_ratio": 1.0, "ctx": 1024, "min_len": 60},     # cap 16 = K; rows the window covers
+    {"block": 8}, {"block": 32}, {"block": 64},           # a slot in half a unit .. four units
+    {"top_k": 128, "fetch_ratio": 0.05, "ctx": 8192 + 40, "batch": 32, "num_kv_heads": 8},  # 256 heads: 4 rounds
+    {"workload": "qwen3_8b_32k", "batch": 2, "num_kv_heads": 2},   # 35 splits
+])
+def test_serial_step_redoes_the_touched_splits(lib, shape):
+    """oasis_decode_step with its own resident_next: launch 1 of the overlapped step,
+    then only the splits holding a slot that the plan changed, redone over the updated
+    slot table, and the merge.  Three steps in a row on one workspace, each: the plan
+    outputs equal the oracle's on the step's own scores; the attention equals
+    oasis_sparse_decode_attn_resident over the updated slot table bit for bit (the
+    same split records, merged by the same kernel: a split left out or redone over
+    the wrong slots would differ) and the oracle's attention over the updated table;
+    the hand-off region is zero again afterwards."""
+    shape = dict(shape)
+    base = dict(batch=5, num_kv_heads=3, fetch_ratio=0.25, ctx=4096 + 40, min_len=1000)
+    w = synth.WORKLOADS[shape.pop("workload", "tiny_4k")]
+    w = w.with_(**({**base, **shape} if w.name == "tiny_4k" else shape))
+    _say(f"serial step redoing the touched splits {shape}")
+    inp = {kk: t.to(DEV) for kk, t in synth.generate(w, "cpu").items()}
+    d = lib.dims_for(w)
+    assert lib.decode_step_redoes_touched_splits(d)
+    summ = lib.build_summaries(d, inp["k"], inp["seq_lens"])
+    lens = inp["seq_lens"].cpu().numpy()
+    n_cand = [ref.first_window_block(int(x), w.window, w.block) for x in lens]
+    res = torch.stack([torch.stack([synth.random_resident(w.top_k, n_cand[b], 3, 10 * b + h)
+                                    for h in range(w.num_kv_heads)]) for b in range(w.batch)]).to(DEV)
+    bufs = lib.StepBuffers(d, DEV)
+    attn_need = lib.workspace_bytes(d, lib.table_stride(d))
+    scale = default_scale()
+    qf, kf, vf = f64(inp["q"]), f64(inp["k"]), f64(inp["v"])
+    for step in range(3):
+        rn = torch.empty_like(res)
+        got = lib.decode_step(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, scale,
+                              buffers=bufs, resident_next=rn)
+        out, lse = got["out"].clone(), got["lse"].clone()
+        alone, alone_lse = lib.sparse_decode_attn_resident(d, inp["q"], inp["k"], inp["v"], rn,
+                                                           inp["seq_lens"], scale)
+        torch.cuda.synchronize()
+        assert lib.workspace_status(d, bufs.ws) == 0
+        assert int(torch.count_nonzero(bufs.ws[attn_need:])) == 0, f"step {step}: hand-off region"
+        gs = f64(got["scores"])
+        sel = ref.topk_blocks(gs, lens, w.top_k, w.window, w.block)
+        np.testing.assert_array_equal(i64(got["topk"]), sel)
+        pl = ref.build_plan(gs, sel, i64(res), lens, w.cap, w.window, w.block)
+        for key in ("plan", "plan_count", "table", "table_count"):
+            np.testing.assert_array_equal(i64(got[key]), pl[key], err_msg=key)
+        np.testing.assert_array_equal(i64(rn), pl["resident"])
+        if w.cap > 0 and step == 0:
+            assert int(got["plan_count"].sum()) > 0
+        assert torch.equal(out, alone) and torch.equal(lse, alone_lse), f"step {step}"
+        eo, el = ref.sparse_attention(qf, kf, vf, pl["table"], pl["table_count"], lens, scale, w.block)
+        np.testing.assert_allclose(f64(out), eo, rtol=0, atol=OUT_ATOL)
+        np.testing.assert_allclose(f64(lse), el, rtol=0, atol=OUT_ATOL)
+        res = rn
+
+
 def test_overlapped_step_repeated_over_rotating_inputs(lib):
     """Steps queued back to back over rotating input sets, sharing one workspace:
     every step must give its own set's results (the scores handed from the scoring
