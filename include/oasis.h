@@ -109,7 +109,9 @@ int32_t oasis_overlapped_selects_in_launch1(const oasis_dims* dims);
 /* 1 if oasis_decode_step, called with its own resident_next buffer, runs for these
  * dims as the first launch of oasis_decode_step_overlapped, a launch that redoes
  * the attention splits holding a slot the plan changed over the updated slot
- * table, and the merge (see oasis_decode_step); 0 if it runs as four kernels.
+ * table, and the merge (see oasis_decode_step): where the selection runs in that
+ * first launch and the C rows of a plan can touch at most 16 of a head's
+ * attention splits and at most half of them.  0 if it runs as four kernels.
  * -1 if dims is invalid. */
 int32_t oasis_decode_step_redoes_touched_splits(const oasis_dims* dims);
 

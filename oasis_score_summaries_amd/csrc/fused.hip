@@ -520,8 +520,15 @@ static int post_plan_row_span(const Dims& d, const AttnSplit& s) {
   return (units_per_entry + units_per_split - 2) / units_per_split + 1;
 }
 
+// The redo pays off while a plan touches at most half of a head's splits: at Qwen3-8B
+// 32K (6 of 35 splits) the step takes 38.8 us against 42.3 us as four kernels; at
+// Qwen3-235B 32K, whose 128 heads of 16 query heads run 5 splits of 8 rounds each, the
+// redo is nearly the whole attention again (29.0 us against 30.7 us for all of it).
 bool post_plan_reuse_fits(const Dims& d) {
-  return handoff_step_fits(d) && d.cap * post_plan_row_span(d, attn_split(d, d.table_stride)) <= kPostPlanMaxSplits;
+  if (!handoff_step_fits(d)) return false;
+  const AttnSplit s = attn_split(d, d.table_stride);
+  const int touched = d.cap * post_plan_row_span(d, s);
+  return touched <= kPostPlanMaxSplits && 2 * touched <= s.num_splits;
 }
 
 hipError_t launch_post_plan_step(const Dims& d, const void* q, const void* summ, const void* k,

@@ -151,10 +151,13 @@ def test_workspace_and_table_stride_checks(lib):
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(group=16, num_queries=7))) == 0
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(max_blocks=4096, top_k=16))) == 0
     # the serial step redoes the touched splits where the selection fits launch 1 and
-    # a plan touches at most 16 splits (cap 6 of K = 128 here), else four kernels
+    # a plan touches at most 16 splits and half of them (cap 6 of 35 here), else four
+    # kernels: more new blocks per step, or Qwen3-235B's shape (5 splits of 8 rounds)
     assert lib.oasis_decode_step_redoes_touched_splits(ctypes.byref(_dims(max_blocks=2048, top_k=128))) == 1
     assert lib.oasis_decode_step_redoes_touched_splits(ctypes.byref(_dims(max_blocks=2048, top_k=128,
                                                                           fetch_ratio=0.25))) == 0
+    assert lib.oasis_decode_step_redoes_touched_splits(ctypes.byref(_dims(batch=32, num_kv_heads=4, group=16,
+                                                                          max_blocks=2048, top_k=128))) == 0
     assert lib.oasis_decode_step_redoes_touched_splits(ctypes.byref(_dims(group=16, num_queries=7))) == 0
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(batch=32, num_kv_heads=8))) == 1
     assert lib.oasis_overlapped_selects_in_launch1(ctypes.byref(_dims(batch=64, num_kv_heads=8))) == 0

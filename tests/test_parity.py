@@ -690,13 +690,13 @@ def test_overlapped_step_matches_its_parts(lib, shape):
 
 
 @pytest.mark.parametrize("shape", [
-    {},                                                   # K = 16, cap 4, 6 splits
+    {},                                                   # K = 64, cap 4, 18 splits
     {"group": 8, "num_drafts": 1},                        # 8 query heads per KV head
     {"group": 16, "num_drafts": 4},                       # 16 query heads, 80 query rows
     {"fetch_ratio": 0.0},                                 # cap 0: nothing to redo, the merge alone
-    {"fetch_ratio": 1.0, "ctx": 1024, "min_len": 60},     # cap 16 = K; rows the window covers
-    {"block": 8}, {"block": 32}, {"block": 64},           # a slot in half a unit .. four units
-    {"top_k": 128, "fetch_ratio": 0.05, "ctx": 8192 + 40, "batch": 32, "num_kv_heads": 8},  # 256 heads: 4 rounds
+    {"ctx": 2048, "min_len": 60},                         # rows the window covers, empty slot tables
+    {"block": 8}, {"block": 32}, {"block": 64, "top_k": 32},   # a slot in half a unit .. four units
+    {"top_k": 128, "fetch_ratio": 0.03, "ctx": 8192 + 40, "batch": 32, "num_kv_heads": 8},  # 256 heads: 4 rounds
     {"workload": "qwen3_8b_32k", "batch": 2, "num_kv_heads": 2},   # 35 splits
 ])
 def test_serial_step_redoes_the_touched_splits(lib, shape):
@@ -709,7 +709,7 @@ def test_serial_step_redoes_the_touched_splits(lib, shape):
     the wrong slots would differ) and the oracle's attention over the updated table;
     the hand-off region is zero again afterwards."""
     shape = dict(shape)
-    base = dict(batch=5, num_kv_heads=3, fetch_ratio=0.25, ctx=4096 + 40, min_len=1000)
+    base = dict(batch=5, num_kv_heads=3, top_k=64, fetch_ratio=0.0625, ctx=4096 + 40, min_len=1000)
     w = synth.WORKLOADS[shape.pop("workload", "tiny_4k")]
     w = w.with_(**({**base, **shape} if w.name == "tiny_4k" else shape))
     _say(f"serial step redoing the touched splits {shape}")
