@@ -469,7 +469,23 @@ def _full_size_case(lib, w, layer=0):
                                       f64(cpu["v"][(b, h)]), table, tc, lb, default_scale(), w.block)
         np.testing.assert_allclose(f64(ov["out"][b, h].cpu()), eo[0, 0], rtol=0, atol=OUT_ATOL)
         np.testing.assert_allclose(f64(ov["lse"][b, h].cpu()), el[0, 0], rtol=0, atol=OUT_ATOL)
-    del inp, summ, out, ov
+    # The serial step with its own resident_next (where it applies, the overlapped launch
+    # 1 plus the touched splits redone): the same plan outputs, and on every head the
+    # attention of the in-place step up to the order of the fp32 additions (its splits
+    # cut the same tokens differently); a split redone over the wrong slots would move
+    # the output by about a block's share of the softmax mass, far above 1e-4.
+    _say(f"full-size {w.name} layer={layer}: serial step into resident_next "
+         f"(touched splits redone: {lib.decode_step_redoes_touched_splits(d)})")
+    rn2 = torch.empty_like(res0)
+    s2 = lib.decode_step(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], resident.to(DEV),
+                         default_scale(), resident_next=rn2)
+    torch.cuda.synchronize()
+    for key in ("scores", "topk", "plan", "plan_count", "table", "table_count"):
+        assert torch.equal(s2[key].cpu(), got[key]), key
+    assert torch.equal(rn2.cpu(), got["resident"])
+    np.testing.assert_allclose(f64(s2["out"].cpu()), f64(got["out"]), rtol=0, atol=1e-4)
+    np.testing.assert_allclose(f64(s2["lse"].cpu()), f64(got["lse"]), rtol=0, atol=1e-4)
+    del inp, summ, out, ov, s2
     torch.cuda.empty_cache()
 
 
@@ -501,8 +517,9 @@ def _zero_scale_check(w, v, lens, table, table_count, out, lse, where):
 @pytest.mark.parametrize("name,layer", [("qwen3_235b_32k", 0), ("reasoning_36l", 17), ("qwen3_8b_32k", 0)])
 def test_full_size_zero_scale_every_head(lib, name, layer):
     """At full size, in the benchmark's launch configuration (Qwen3-235B: eight-round
-    attention splits; 36 layers: four rounds), both step orders with scale 0, on every
-    head: the merged log-sum-exp counts the attended tokens exactly and the output is
+    attention splits; 36 layers: four rounds), both step orders with scale 0 (the serial
+    one in place and into resident_next, at Qwen3-8B the form that redoes the touched
+    splits), on every head: the merged log-sum-exp counts the attended tokens exactly and the output is
     the mean of their V rows.  A dropped or doubled token moves exp(lse) by one count
     (above 1e-6 relative up to a million tokens) and the output by about 1/count."""
     w = synth.WORKLOADS[name]
@@ -519,6 +536,14 @@ def test_full_size_zero_scale_every_head(lib, name, layer):
     ser = {key: val.detach().cpu() for key, val in ser.items()}
     _zero_scale_check(w, inp["v"], lens, i64(ser["table"]), i64(ser["table_count"]), ser["out"], ser["lse"],
                       f"{name} serial")
+    _say(f"zero-scale full size {name}: serial step into resident_next")
+    rn_s = torch.empty_like(resident)
+    ser2 = lib.decode_step(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], resident, 0.0,
+                           resident_next=rn_s)
+    ser2 = {key: val.detach().cpu() for key, val in ser2.items()}
+    assert torch.equal(ser2["table"], ser["table"]) and torch.equal(ser2["table_count"], ser["table_count"])
+    _zero_scale_check(w, inp["v"], lens, i64(ser2["table"]), i64(ser2["table_count"]), ser2["out"],
+                      ser2["lse"], f"{name} serial into resident_next")
     _say(f"zero-scale full size {name}: overlapped step")
     rn = torch.empty_like(resident)
     ov = lib.decode_step_overlapped(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], resident, rn, 0.0)
