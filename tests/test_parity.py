@@ -843,13 +843,16 @@ def test_attention_over_resident_slots(lib, G, lens, NB, K):
     np.testing.assert_allclose(f64(lse)[fin], el[fin], rtol=0, atol=OUT_ATOL)
 
 
-@pytest.mark.parametrize("ratio", [0.0, 0.25, 1.0])
-def test_serial_step_with_window_reached_slots(lib, ratio):
+@pytest.mark.parametrize("into_next", [False, True])
+@pytest.mark.parametrize("ratio", [0.0, 0.125, 0.25, 1.0])
+def test_serial_step_with_window_reached_slots(lib, ratio, into_next):
     """oasis_decode_step over slot tables that hold blocks the window has reached, empty
     slots and historical blocks: the plan, the updated slots and the table equal the
     oracle's given the GPU's own scores and selection (a window-reached block is listed
-    once, as a window block), and the attention equals the oracle's over the GPU's table."""
-    _say(f"serial step, window-reached slots, ratio={ratio}")
+    once, as a window block), and the attention equals the oracle's over the GPU's table.
+    In place and into resident_next (at caps 0 and 1 the form that redoes the touched
+    splits: a plan row may replace a slot whose block the window has reached)."""
+    _say(f"serial step, window-reached slots, ratio={ratio}, into_next={into_next}")
     B, H, G, Q, NB, K, W = 3, 2, 4, 5, 64, 12, 64
     lens = [1000, 700, 300]
     q, k, v, L = _small_inputs(77, B, H, G, Q, NB, lens)
@@ -866,8 +869,11 @@ def test_serial_step_with_window_reached_slots(lib, ratio):
             rng.shuffle(row)
             R[b, h] = row
     R_dev = torch.from_numpy(R.astype(np.int32)).to(DEV)
+    rn = torch.empty_like(R_dev) if into_next else None
+    if into_next:
+        assert lib.decode_step_redoes_touched_splits(d) == (cap <= 1)
     got = lib.decode_step(d, q.to(DEV), lib.build_summaries(d, k.to(DEV), L.to(DEV)), k.to(DEV),
-                          v.to(DEV), L.to(DEV), R_dev, default_scale())
+                          v.to(DEV), L.to(DEV), R_dev, default_scale(), resident_next=rn)
     torch.cuda.synchronize()
     got = {key: val.detach().cpu() for key, val in got.items()}
     summ = ref.build_summaries(f64(k), L.numpy())
