@@ -25,6 +25,9 @@ MUTATIONS = {
     "plan_evicts_best_stale": ("stale.sort(key=lambda i: (s[int(res[i])], -int(res[i])))",
                                "stale.sort(key=lambda i: (-s[int(res[i])], -int(res[i])))"),
     "plan_pairs_unsorted": ("zip(sorted(victims), sorted(admit))", "zip(victims, admit)"),
+    "plan_ignores_cap": ("n = min(cap, len(admit))", "n = len(admit)"),
+    "plan_frees_stale_before_empty": ("victims = (empty + stale)[:n]", "victims = (stale + empty)[:n]"),
+    "attention_lse_drops_max": ("lse[b, h, g] = m + math.log(den)", "lse[b, h, g] = math.log(den)"),
     "summaries_read_past_length": ("n_valid = min(bs, L - j * bs)", "n_valid = bs"),
     "attention_drops_scale": ("z = (kt @ q[b, h, g, 0, :]) * scale", "z = (kt @ q[b, h, g, 0, :])"),
     "attention_uses_a_draft": ("z = (kt @ q[b, h, g, 0, :]) * scale", "z = (kt @ q[b, h, g, 1, :]) * scale"),
