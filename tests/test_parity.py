@@ -236,12 +236,13 @@ def test_attention_all_blocks_matches_dense(lib):
 # The fused step
 # ---------------------------------------------------------------------------
 
-def _run_step(lib, w, inp_dev, resident_cpu):
+def _run_step(lib, w, inp_dev, resident_cpu, into_next=False):
     d = lib.dims_for(w)
     summ = lib.build_summaries(d, inp_dev["k"], inp_dev["seq_lens"])
     res_dev = resident_cpu.to(DEV)
     out = lib.decode_step(d, inp_dev["q"], summ, inp_dev["k"], inp_dev["v"], inp_dev["seq_lens"],
-                          res_dev, default_scale())
+                          res_dev, default_scale(),
+                          resident_next=torch.empty_like(res_dev) if into_next else None)
     torch.cuda.synchronize()
     return {key: val.detach().cpu() for key, val in out.items()}, summ
 
@@ -327,12 +328,14 @@ def test_decode_step_tiny_workload(lib):
             assert _compare_head(w, got, exp, b, h, resident[b, h].numpy(), robust=True)
 
 
+@pytest.mark.parametrize("into_next", [False, True])
 @pytest.mark.parametrize("ratio,W,lens", [(0.05, 64, [4096, 1000, 70]), (0.25, 0, [4096, 1024, 16]),
                                           (1.0, 128, [4000, 2222, 130])])
-def test_decode_step_integer_inputs(lib, ratio, W, lens):
+def test_decode_step_integer_inputs(lib, ratio, W, lens, into_next):
     """Small-integer q and k make every score exact in fp32 and fp64, so every
-    selection and plan decision (exact ties included) must agree bit for bit."""
-    _say(f"decode_step integer ratio={ratio} W={W} lens={lens}")
+    selection and plan decision (exact ties included) must agree bit for bit.  In
+    place and into resident_next (at cap 1 the form that redoes the touched splits)."""
+    _say(f"decode_step integer ratio={ratio} W={W} lens={lens} into_next={into_next}")
     B, H, G, Q, NB, K = len(lens), 3, 4, 5, 256, 24
     q, k, v, L = _small_inputs(21, B, H, G, Q, NB, lens, integer=True)
     w = synth.Workload(name="int", batch=B, num_kv_heads=H, group=G, ctx=NB * 16, num_drafts=Q - 1,
@@ -342,7 +345,7 @@ def test_decode_step_integer_inputs(lib, ratio, W, lens):
         for h in range(H):
             resident[b, h] = synth.random_resident(K, ref.first_window_block(lens[b], W), [0, 3, K][h], 50 * b + h)
     inp_dev = {"q": q.to(DEV), "k": k.to(DEV), "v": v.to(DEV), "seq_lens": L.to(DEV)}
-    got, _ = _run_step(lib, w, inp_dev, resident)
+    got, _ = _run_step(lib, w, inp_dev, resident, into_next)
     for b in range(B):
         for h in range(H):
             exp = oracle_head(q, k, v, L, resident[b, h].numpy(), K, W, w.cap, default_scale(), b, h)
@@ -630,16 +633,21 @@ def test_largest_supported_sizes(lib):
 # Degenerate cases
 # ---------------------------------------------------------------------------
 
-def test_no_candidates_and_short_sequences(lib):
-    """len < W: nothing to score or select; the table is the window alone."""
+@pytest.mark.parametrize("ratio,into_next", [(1.0, False), (0.25, True)])
+def test_no_candidates_and_short_sequences(lib, ratio, into_next):
+    """len < W: nothing to score or select; the table is the window alone.  In place,
+    and into resident_next at cap 1 (the form that redoes the touched splits, with
+    nothing to redo)."""
     B, H, G, Q, NB, K, W = 3, 2, 4, 2, 16, 4, 128
     lens = [100, 1, 128]
     q, k, v, L = _small_inputs(2, B, H, G, Q, NB, lens)
     w = synth.Workload(name="short", batch=B, num_kv_heads=H, group=G, ctx=NB * 16, num_drafts=Q - 1,
-                       top_k=K, window=W, fetch_ratio=1.0, planted=0)
+                       top_k=K, window=W, fetch_ratio=ratio, planted=0)
+    if into_next:
+        assert lib.decode_step_redoes_touched_splits(lib.dims_for(w))
     resident = torch.full((B, H, K), -1, dtype=torch.int32)
     got, _ = _run_step(lib, w, {"q": q.to(DEV), "k": k.to(DEV), "v": v.to(DEV), "seq_lens": L.to(DEV)},
-                       resident)
+                       resident, into_next)
     assert torch.all(got["topk"] == -1) and torch.all(got["plan_count"] == 0)
     for b in range(B):
         for h in range(H):
