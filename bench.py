@@ -1180,6 +1180,8 @@ def main(argv=None) -> int:
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
         "stage_timing": stage_method,
         f"{other}_ms_per_step": round(ms_other, 6),
+        "serial_form": ("overlapped launch 1, touched splits redone, merge"
+                        if oa.decode_step_redoes_touched_splits(d) else "four kernels"),
         "wall_s": round(wall_s, 3),
         "setup_s": round(setup_s, 1),
         "checks": check,

@@ -52,3 +52,5 @@ def test_bench_record_fields(capsys):
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
     assert r["checks"].get("graph_matches_eager", True) is True
     assert r["checks"]["handoff_status_zero"] is True
+    # the serial step at this shape (cap 0) takes the overlapped launch 1 and the merge
+    assert r["serial_form"] == "overlapped launch 1, touched splits redone, merge"
