@@ -1028,14 +1028,18 @@ def test_overlapped_step_leaves_the_handoff_region_zero(lib, shape):
         np.testing.assert_allclose(f64(got2["out"]), eo, rtol=0, atol=OUT_ATOL)
 
 
-@pytest.mark.parametrize("overlapped", [False, True])
-def test_graph_replay_matches_eager(lib, overlapped):
-    """Every replay of a captured step (the overlapped one forks a second stream
-    inside the capture), with eager work and syncs between replays, gives the
-    eager result bit for bit."""
+@pytest.mark.parametrize("overlapped,redo", [(False, False), (False, True), (True, False)])
+def test_graph_replay_matches_eager(lib, overlapped, redo):
+    """Every replay of a captured step, with eager work and syncs between replays,
+    gives the eager result bit for bit: the serial step as four kernels and in the form
+    that redoes the touched splits, and the overlapped step."""
     w = synth.WORKLOADS["tiny_4k"].with_(batch=4, fetch_ratio=0.25)
-    _say(f"graph replay overlapped={overlapped}")
+    if redo:   # K = 64, cap 4: a plan touches at most 4 of 18 splits
+        w = w.with_(top_k=64, fetch_ratio=0.0625)
+    _say(f"graph replay overlapped={overlapped} redo={redo}")
     d, inp, summ, res = _prepared_inputs(lib, w, seed_layer=3)
+    if not overlapped:
+        assert lib.decode_step_redoes_touched_splits(d) == redo
     bufs = lib.StepBuffers(d, DEV)
     rn = torch.empty_like(res)
     st = lib.PreparedStep(d, inp["q"], summ, inp["k"], inp["v"], inp["seq_lens"], res, bufs,
