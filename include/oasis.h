@@ -140,9 +140,10 @@ oasis_status oasis_workspace_clear(const oasis_dims* dims, void* ws, size_t ws_b
 /* Byte offset, inside the step workspace, of the hand-off status word (uint32).
  * It stays 0 unless a selection workgroup in the first launch of
  * oasis_decode_step_overlapped waited past its bound (about 10 ms) for the
- * scores it needs; it then holds bit 1, the selection outputs of
- * that step (topk, plan, table, resident_next) are unspecified and the workspace must
- * be cleared.  A wait never hangs the device.  0 if dims is invalid. */
+ * scores it needs (the first launch of oasis_decode_step too, in the form that
+ * redoes the touched splits); it then holds bit 1, the selection outputs of
+ * that step (topk, plan, table, resident_next; in that form of oasis_decode_step
+ * also out and lse) are unspecified and the workspace must be cleared.  A wait never hangs the device.  0 if dims is invalid. */
 size_t oasis_workspace_status_offset(const oasis_dims* dims);
 
 /* Device workspace that oasis_sparse_decode_attn needs for a given table
